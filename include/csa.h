@@ -1,0 +1,284 @@
+/*
+ * csa.h -- C ABI of the MI355X (gfx950) CSA / HCA hybrid-attention hot path.
+ *
+ * The method is DeepSeek-V4's hybrid attention layer as described in
+ *   [book]  "DeepSeek-V4" (slop-6tp.pages.dev/papers-html/dsv4), ch. 5-8, 13;
+ *   [note]  "2026 DeepSeek-V4" (awesome.papernotes.org), "Method Deep Dive",
+ *           "Key design 1" (CSA) and "Key design 2" (HCA) with their equations.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers, row-major and contiguous, with
+ *   the shapes given per argument.  The caller owns every buffer (inputs,
+ *   outputs, caches, state, workspace); the library never allocates, frees or
+ *   keeps a pointer after the call returns.
+ * - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *   void*; NULL = the default stream).  Buffers must stay alive until the
+ *   caller synchronises that stream.
+ * - Every entry point returns a csa_status.  All argument checks run on the
+ *   host before anything is enqueued, so an error has no side effects.
+ *   csa_last_error() returns a thread-local message about the last failure.
+ *   Nothing is printed; no C++ exception crosses the ABI.
+ * - Positions are 0-based token positions (int64).  Entry ids are int32.
+ * - Workspaces ("ws") are caller-allocated device memory of at least the size
+ *   the matching *_workspace() function returns.  A workspace must be
+ *   zero-filled once when first allocated; every call returns the counters it
+ *   uses to zero before it completes.  Calls that share a workspace must be
+ *   ordered on one stream.
+ * - Supported shapes: c in {64, 128, 256, 512}; d_I in {32, 64, 128};
+ *   H <= 128; H_I <= 64; 1 <= m <= 128; k <= 2048; n_win <= 256.  Other
+ *   shapes return CSA_ERR_UNSUPPORTED (there is no slow fallback).
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_ARG = 1,         /* null pointer, bad size, inconsistent arguments  */
+  CSA_ERR_UNSUPPORTED = 2, /* valid but outside the supported shapes / dtypes */
+  CSA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required      */
+  CSA_ERR_DEVICE = 4       /* the HIP runtime reported an error on launch     */
+} csa_status;
+
+typedef enum {
+  CSA_F32 = 0,  /* IEEE binary32                                            */
+  CSA_BF16 = 1, /* bfloat16                                                 */
+  CSA_E4M3 = 2  /* OCP FP8 E4M3FN, one float32 scale per vector (v = q * s) */
+} csa_dtype;
+
+/* Which compressed entries a query at position t may read ([book] ch. 5 "When
+ * an entry becomes available"; the printed condition is garbled).  The
+ * default admits only blocks that end before the query's own block. */
+typedef enum {
+  CSA_VIS_PRIOR_BLOCKS = 0, /* entry s visible iff s < floor(t / m)       */
+  CSA_VIS_COMPLETED = 1     /* entry s visible iff s < floor((t + 1) / m) */
+} csa_visibility;
+
+/* Thread-local text of the last error, or "" after a successful call. */
+const char* csa_last_error(void);
+
+/* ABI version of this header (bumped on incompatible change). */
+int csa_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * a1. Compressor: fold token streams into compressed entries.
+ *
+ * [note] "Key design 1" equation (CSA, two branches with overlap) and "Key
+ * design 2" equation (HCA, one branch); [book] ch. 5 "One weight distribution
+ * per coordinate", "Which positions enter a compressed block", and the
+ * start-of-sequence rule.
+ *
+ * For chunk entry i (0 <= i < T/m) and coordinate r, the logits
+ *   Za[m*i+j, r] + Ba[j, r]        (j < m, current block, branch a)
+ *   Zb[m*(i-1)+j, r] + Bb[j, r]    (j < m, previous block, branch b)
+ * go through one softmax across the source positions and the entry is the
+ * weighted sum of Ca / Cb.  For i = 0 the previous block is prev_content_b /
+ * prev_logits_b; if those are NULL the chunk starts the sequence and entry 0
+ * has no branch-b sources.  With content_b == NULL the compressor has one
+ * branch (HCA form).
+ *
+ *   dtype          F32 or BF16: dtype of every content / logit input.
+ *   content_a      [B][T][c]
+ *   logits_a       [B][T][logit_width]; logit_width is c (per coordinate) or
+ *                  1 (one scalar per token, shared by all coordinates).  May
+ *                  be NULL when score_w is given.
+ *   score_w        [c] float32 or NULL: when logits_a is NULL the scalar
+ *                  logit of a token is score_w . content_a[token] (one-branch
+ *                  form only).
+ *   bias_a         [m][c] float32 or NULL (= 0).
+ *   content_b, logits_b, bias_b   branch b, same shapes, or NULL (no overlap).
+ *   prev_content_b, prev_logits_b [B][m][c] / [B][m][logit_width] or NULL.
+ *   B, T, c, m     T % m == 0.
+ *   out            [B][E_cap][c] in out_dtype; entry i of sequence b goes to
+ *                  row out_first_entry + i.  out_first_entry + T/m <= E_cap.
+ *   out_dtype      F32, BF16, or E4M3 (then out_scale [B][E_cap] receives
+ *                  scale = max|entry| / 448 and the codes round to nearest
+ *                  even; an all-zero entry gets scale 1).
+ * ------------------------------------------------------------------------ */
+csa_status csa_compress(csa_dtype dtype, const void* content_a, const void* logits_a,
+                        int logit_width, const float* score_w, const float* bias_a,
+                        const void* content_b, const void* logits_b, const float* bias_b,
+                        const void* prev_content_b, const void* prev_logits_b, int B, int T,
+                        int c, int m, void* out, csa_dtype out_dtype, float* out_scale,
+                        int E_cap, int64_t out_first_entry, void* stream);
+
+/* ------------------------------------------------------------------------
+ * a2 + a3. Lightning indexer and per-query top-k.
+ *
+ * I[t, s] = sum_h w[t, h] * ReLU(q[t, h] . K[s])   ([note] "Key design 1"
+ * indexer equation; [book] ch. 6 "The index score": w may be negative), over
+ * the entries visible to the query (vis, m, q_pos, n_entries), followed by
+ * C_t = TopK_k(I[t, :]) ([note] same equation; [book] ch. 6 "Top-k is a budget
+ * over compressed entries": all visible entries are kept when fewer than k).
+ * Ties between equal float32 scores go to the lower entry id.
+ *
+ *   idx_dtype  F32, BF16 or E4M3 for q_idx and k_idx.
+ *   q_idx      [B][Tq][H_I][d_I];  q_scale [B][Tq][H_I] float32 iff E4M3.
+ *   w_idx      [B][Tq][H_I] float32 head weights.
+ *   k_idx      [B][E_cap][d_I];    k_scale [B][E_cap] float32 iff E4M3.
+ *   q_pos      [B][Tq] int64 query positions.
+ *   n_entries  [B] int32 entries present in the cache.
+ *   topk_idx   [B][Tq][k] int32 out: selected ids ascending, -1 padded.
+ *   topk_cnt   [B][Tq] int32 out: number selected (= min(k, visible)).
+ *   scores     [B][Tq][E_cap] float32 out, or NULL.  Only the visible prefix
+ *              of each row is written.
+ *   ws         workspace of csa_index_topk_workspace(B, Tq, E_cap, k) bytes.
+ * ------------------------------------------------------------------------ */
+size_t csa_index_topk_workspace(int B, int Tq, int E_cap, int k);
+csa_status csa_index_topk(csa_dtype idx_dtype, const void* q_idx, const float* q_scale,
+                          const float* w_idx, const void* k_idx, const float* k_scale,
+                          const int64_t* q_pos, const int32_t* n_entries, int B, int Tq, int H_I,
+                          int d_I, int E_cap, int m, int k, csa_visibility vis, int32_t* topk_idx,
+                          int32_t* topk_cnt, float* scores, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* ------------------------------------------------------------------------
+ * a4 + a6. Sparse attention over the selected entries, the window and the
+ * sink, merged in one softmax.
+ *
+ * Every row serves as both key and value for all H heads (shared-KV MQA,
+ * [book] ch. 6 "Shared key-value MQA").  For query (b, t) with position
+ * p = q_pos[b][t] the rows are kv[b][topk_idx[b][t][0 .. topk_cnt-1]] and the
+ * window rows of positions max(0, p-n_win+1) .. p ([book] ch. 7 "The sliding
+ * window"), all in one softmax ([note] concat(selected, local_kv)) whose
+ * denominator also holds exp(sink[h]) ([book] ch. 7 "Attention sinks"):
+ *   o_h = sum_j exp(l_j - M) row_j / (sum_j exp(l_j - M) + exp(z'_h - M)),
+ *   l_j = scale * q_h . row_j.
+ *
+ *   dtype      F32 or BF16 for q, kv, win and out (float32 accumulation).
+ *   q          [B][Tq][H][c]
+ *   kv         [B][E_cap][c] compressed entries
+ *   topk_idx, topk_cnt   as produced by csa_index_topk (ids must be < E_cap).
+ *   win        [B][W_cap][c]: the row of position p is row
+ *              (p - win_pos0[b]) mod W_cap (a ring buffer uses win_pos0 = 0; a
+ *              linear buffer uses its first position).  All window positions
+ *              of every query must be present.
+ *   sink       [H] float32 logits, or NULL (no sink).
+ *   q_pos      [B][Tq] int64.
+ *   out        [B][Tq][H][c];  lse [B][Tq][H] float32 out or NULL
+ *              (lse = log of the full softmax denominator incl. the sink).
+ *   ws         workspace of csa_attend_workspace(B, Tq, H, c, k + n_win).
+ * ------------------------------------------------------------------------ */
+size_t csa_attend_workspace(int B, int Tq, int H, int c, int rows_max);
+csa_status csa_attend(csa_dtype dtype, const void* q, const void* kv, int E_cap,
+                      const int32_t* topk_idx, const int32_t* topk_cnt, int k, const void* win,
+                      int W_cap, const int64_t* win_pos0, int n_win, const float* sink,
+                      const int64_t* q_pos, float scale, int B, int Tq, int H, int c, void* out,
+                      float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* a5 + a6. Dense HCA attention: as csa_attend, with the rows being every
+ * visible compressed entry s < min(n_entries[b], vis-limit(q_pos)) plus the
+ * window and the sink ([note] "Key design 2"; [book] ch. 7 "Dense attention
+ * over compressed history").  ws: csa_attend_workspace(B, Tq, H, c, E_cap +
+ * n_win). */
+csa_status hca_attend(csa_dtype dtype, const void* q, const void* kv, int E_cap,
+                      const int32_t* n_entries, int m, csa_visibility vis, const void* win,
+                      int W_cap, const int64_t* win_pos0, int n_win, const float* sink,
+                      const int64_t* q_pos, float scale, int B, int Tq, int H, int c, void* out,
+                      float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * a7 + the whole layer.  A layer is described by csa_layer_desc and keeps its
+ * cache and bounded state in csa_layer_state ([book] ch. 5 "What is retained
+ * during decode": a classical cache of completed entries plus state for the
+ * window and the compression tail; ch. 13 heterogeneous KV cache).
+ * ------------------------------------------------------------------------ */
+typedef enum { CSA_LAYER_CSA = 1, CSA_LAYER_HCA = 2 } csa_layer_kind;
+
+typedef struct {
+  int kind;          /* csa_layer_kind                                        */
+  int H, c;          /* query heads, entry / head dim                         */
+  int H_I, d_I;      /* indexer heads and dim (CSA)                           */
+  int m;             /* compression rate (4 for CSA, 128 for HCA)             */
+  int overlap;       /* 1: two-branch overlapping compressor (CSA); 0: one    */
+  int k;             /* top-k budget (CSA)                                    */
+  int n_win;         /* sliding-window width                                  */
+  int vis;           /* csa_visibility                                        */
+  int kv_dtype;      /* F32 or BF16: activations, caches, outputs             */
+  int idx_dtype;     /* F32, BF16 or E4M3: indexer queries and keys (CSA)     */
+  float scale;       /* attention logit scale (1/sqrt(c) for the pages)       */
+} csa_layer_desc;
+
+/* Number of compressor streams per token: 4 (ca, za, cb, zb) with overlap,
+ * else 2 (ca, za); tail ring depth R = 3m with overlap, else 2m. */
+typedef struct {
+  int B, E_cap;
+  void* kv_cache;        /* [B][E_cap][c] kv_dtype                             */
+  void* idx_cache;       /* [B][E_cap][d_I] idx_dtype (CSA)                    */
+  float* idx_scale;      /* [B][E_cap] (E4M3 only)                             */
+  int32_t* n_entries;    /* [B] completed entries in the cache                 */
+  void* win_ring;        /* [B][n_win][c]: position p lives in slot p % n_win  */
+  void* tail;            /* [B][streams][R][c]: position p in slot p % R       */
+  void* idx_tail;        /* [B][4][R][d_I] (CSA): the indexer-key streams      */
+  const float* bias_a;   /* [m][c] positional biases of branch a (or NULL)     */
+  const float* bias_b;   /* [m][c] branch b (or NULL)                          */
+  const float* ibias_a;  /* [m][d_I] indexer-key biases (CSA, or NULL)         */
+  const float* ibias_b;
+  const float* sink;     /* [H] sink logits or NULL                            */
+} csa_layer_state;
+
+/* One decode step: one new token per sequence at position pos[b]. */
+typedef struct {
+  const int64_t* pos;       /* [B]                                             */
+  const void* q;            /* [B][H][c]                                       */
+  const void* q_idx;        /* [B][H_I][d_I] (CSA)                             */
+  const float* q_scale;     /* [B][H_I] (E4M3)                                 */
+  const float* w_idx;       /* [B][H_I] (CSA)                                  */
+  const void* x_new;        /* [B][c] the new token's window row               */
+  const void* streams;      /* [B][streams][c] the new token's compressor rows */
+  const void* idx_streams;  /* [B][4][d_I] (CSA)                               */
+  void* out;                /* [B][H][c]                                       */
+  float* lse;               /* [B][H] or NULL                                  */
+  int32_t* topk_idx;        /* [B][k] out (CSA)                                */
+  int32_t* topk_cnt;        /* [B] out (CSA)                                   */
+} csa_decode_io;
+
+/* A prefill chunk of T tokens per sequence starting at position pos0 (all
+ * sequences aligned); pos0 % m == 0 and T % m == 0. */
+typedef struct {
+  int64_t pos0;
+  int T;
+  const void* q;            /* [B][T][H][c]                                    */
+  const void* q_idx;        /* [B][T][H_I][d_I] (CSA)                          */
+  const float* q_scale;     /* [B][T][H_I] (E4M3)                              */
+  const float* w_idx;       /* [B][T][H_I] (CSA)                               */
+  const void* win;          /* [B][n_win-1+T][c]: rows of positions
+                               pos0-n_win+1 .. pos0+T-1                        */
+  const void* streams;      /* [B][streams][T][c] the chunk's compressor rows  */
+  const void* idx_streams;  /* [B][4][T][d_I] (CSA)                            */
+  void* out;                /* [B][T][H][c]                                    */
+  float* lse;               /* [B][T][H] or NULL                               */
+  int32_t* topk_idx;        /* [B][T][k] out (CSA)                             */
+  int32_t* topk_cnt;        /* [B][T] out (CSA)                                */
+} csa_prefill_io;
+
+/* Workspace for hybrid_layer_decode / hybrid_layer_prefill (T = 1 for decode). */
+size_t hybrid_layer_workspace(const csa_layer_desc* desc, int B, int T, int E_cap);
+
+/* Decode step ([note] csa() / hca() in "Key design 1" / "Key design 2"):
+ * append the new token to the window ring and the tail; fold the block whose
+ * entry becomes visible at this position (at most one per step; the caller
+ * steps every position); CSA: score the visible entries, keep the top-k and
+ * attend over them + window + sink; HCA: attend over all visible entries +
+ * window + sink.  n_entries is updated on the device. */
+csa_status hybrid_layer_decode(const csa_layer_desc* desc, csa_layer_state* state,
+                               const csa_decode_io* io, void* ws, size_t ws_bytes, void* stream);
+
+/* Prefill chunk: compress the chunk's blocks into the cache (the first uses
+ * the previous block's branch b from the tail unless pos0 == 0), answer all T
+ * queries causally, then leave the window ring and the tail holding the
+ * chunk's last tokens so that decode can continue at pos0 + T. */
+csa_status hybrid_layer_prefill(const csa_layer_desc* desc, csa_layer_state* state,
+                                const csa_prefill_io* io, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */

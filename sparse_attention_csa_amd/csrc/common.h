@@ -1,0 +1,90 @@
+// Device helpers shared by the HIP kernels of the CSA/HCA hot path (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define CSA_DEV __device__ __forceinline__
+
+namespace csa {
+
+// ---------------------------------------------------------------- bfloat16
+struct bf16 {
+  uint16_t bits;
+};
+
+CSA_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// round to nearest even; NaN stays NaN
+CSA_DEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// element load / store for the two activation dtypes
+CSA_DEV float ld(const float* p, size_t i) { return p[i]; }
+CSA_DEV float ld(const bf16* p, size_t i) { return bf16_to_f32(p[i].bits); }
+CSA_DEV void st(float* p, size_t i, float v) { p[i] = v; }
+CSA_DEV void st(bf16* p, size_t i, float v) { p[i].bits = f32_to_bf16(v); }
+
+// ---------------------------------------------------------------- OCP e4m3fn
+// 1 sign, 4 exponent (bias 7), 3 fraction bits; S.1111.111 is NaN; max 448.
+CSA_DEV float e4m3_to_f32(uint8_t c) {
+  const uint32_t e = (c >> 3) & 0xf, f = c & 7;
+  float mag;
+  if (e == 0)
+    mag = ldexpf((float)f * 0.125f, -6);
+  else if (e == 15 && f == 7)
+    mag = __builtin_nanf("");
+  else
+    mag = ldexpf(1.0f + (float)f * 0.125f, (int)e - 7);
+  return (c & 0x80) ? -mag : mag;
+}
+
+// nearest e4m3fn code of y (|y| clamped to 448), ties to even.
+CSA_DEV uint8_t f32_to_e4m3(float y) {
+  const uint8_t sign = (y < 0.f) ? 0x80 : 0;
+  float a = fminf(fabsf(y), 448.0f);
+  if (!(a > 0.f)) return sign;
+  int e;
+  frexpf(a, &e);                   // a = mant * 2^e, mant in [0.5, 1)
+  int sp = e - 4;                  // 4 significant bits
+  if (sp < -9) sp = -9;            // subnormal spacing 2^-9
+  float r = rintf(ldexpf(a, -sp)); // multiples of the spacing, ties to even
+  r = ldexpf(r, sp);
+  if (r > 448.f) r = 448.f;
+  if (r < ldexpf(1.0f, -6)) {      // subnormal: field 0
+    return sign | (uint8_t)(int)rintf(ldexpf(r, 9));
+  }
+  int er;
+  float mr = frexpf(r, &er);       // r = mr * 2^er, mr in [0.5, 1)
+  int E = er - 1;                  // r = (2 mr) * 2^E, 2 mr in [1, 2)
+  int f = (int)rintf((2.f * mr - 1.f) * 8.f);
+  return sign | (uint8_t)(((E + 7) << 3) | f);
+}
+
+// ---------------------------------------------------------------- top-k keys
+// order-preserving map float -> uint32 (larger float -> larger key)
+CSA_DEV uint32_t f32_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- reductions
+CSA_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+CSA_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// visible-entry limit for a query at position t
+CSA_DEV int64_t vis_limit(int64_t t, int m, int vis) { return vis == 0 ? t / m : (t + 1) / m; }
+
+}  // namespace csa

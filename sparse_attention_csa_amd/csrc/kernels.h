@@ -1,0 +1,121 @@
+// Internal launch interface between the C-ABI host layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace csa {
+
+enum Dt { F32 = 0, BF16 = 1, E4M3 = 2 };
+
+// ------------------------------------------------------------ compressor
+struct CompressArgs {
+  int dtype;  // input dtype (F32 / BF16)
+  const void *ca, *za, *cb, *zb, *prev_cb, *prev_zb;
+  int logit_width;
+  const float *score_w, *bias_a, *bias_b;
+  int B, T, c, m;
+  void* out;
+  int out_dtype;
+  float* out_scale;
+  int E_cap;
+  int64_t first;
+  size_t seq_stride;       // elements between sequences of ca/za/cb/zb (0: T*c or T*lw)
+  size_t prev_seq_stride;  // elements between sequences of prev_cb/prev_zb (0: m*c or m*lw)
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+
+// decode-step fold of the pending block + append of the new token
+struct FoldArgs {
+  int dtype;      // kv dtype (F32 / BF16) of streams, tails, caches
+  int idx_dtype;  // indexer-cache dtype (F32 / BF16 / E4M3) or -1 (no indexer)
+  int B, c, d_I, m, R, n_win, vis, overlap;
+  const int64_t* pos;
+  int32_t* n_entries;
+  const void* streams;      // [B][S][c]
+  const void* idx_streams;  // [B][4][d_I]
+  const void* x_new;        // [B][c]
+  void* tail;               // [B][S][R][c]
+  void* idx_tail;           // [B][4][R][d_I]
+  void* win_ring;           // [B][n_win][c]
+  void* kv_cache;           // [B][E_cap][c]
+  void* idx_cache;          // [B][E_cap][d_I]
+  float* idx_scale;         // [B][E_cap]
+  int E_cap;
+  const float *bias_a, *bias_b, *ibias_a, *ibias_b;
+  int32_t* counters;        // [B] workspace, zero between calls
+};
+hipError_t launch_fold_append(const FoldArgs& a, hipStream_t s);
+
+// prefill epilogue: copy the chunk's last tokens into the window ring / tail
+struct PrefillStateArgs {
+  int dtype, B, T, c, d_I, R, n_win, S;
+  int64_t pos0;
+  const void* win;          // [B][n_win-1+T][c]
+  const void* streams;      // [B][S][T][c]
+  const void* idx_streams;  // [B][4][T][d_I] or null
+  void* win_ring;
+  void* tail;
+  void* idx_tail;
+  int32_t* n_entries;
+  int new_entries;
+};
+hipError_t launch_prefill_state(const PrefillStateArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------ indexer + top-k
+struct IndexArgs {
+  int idx_dtype;
+  const void* q;        // [B][Tq][H_I][d_I]
+  const float* q_scale; // [B][Tq][H_I]
+  const float* w;       // [B][Tq][H_I]
+  const void* keys;     // [B][E_cap][d_I]
+  const float* k_scale; // [B][E_cap]
+  const int64_t* q_pos; // [B][Tq], or null: query tq is at q_pos0 + tq
+  int64_t q_pos0;
+  const int32_t* n_entries;
+  int n_add;            // entries appended earlier in the same step
+  int B, Tq, H_I, d_I, E_cap, m, k, vis;
+  float* scores;        // [B][Tq][E_cap]
+  int32_t* topk_idx;    // [B][Tq][k]
+  int32_t* topk_cnt;    // [B][Tq]
+  void* ws;             // topk scratch
+};
+size_t index_topk_ws_bytes(int B, int Tq, int E_cap, int k);
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s);
+
+// ------------------------------------------------------------ attention
+struct AttendArgs {
+  int dtype;
+  const void* q;        // [B][Tq][H][c]
+  const void* kv;       // [B][E_cap][c]
+  int E_cap;
+  // sparse (CSA) rows
+  const int32_t* topk_idx;
+  const int32_t* topk_cnt;
+  int k;
+  // dense (HCA) rows
+  const int32_t* n_entries;
+  int n_add;
+  int m, vis;
+  int dense;
+  // window
+  const void* win;
+  int W_cap;
+  const int64_t* win_pos0;  // [B] or null (= 0)
+  int64_t win_pos0_const;   // used when win_pos0 is null
+  int n_win;
+  const float* sink;
+  const int64_t* q_pos;  // [B][Tq], or null: query tq is at q_pos0 + tq
+  int64_t q_pos0;
+  float scale;
+  int B, Tq, H, c;
+  void* out;
+  float* lse;
+  void* ws;
+  size_t ws_bytes;
+};
+size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+
+}  // namespace csa
