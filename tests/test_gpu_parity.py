@@ -56,11 +56,14 @@ def _check_folded_key(g, sess, b, e0, ref_row, label):
         codes = sess.state.idx_cache[b, e0].cpu().numpy()
         scale = sess.state.idx_scale[b, e0].cpu().numpy()
         got = Stored(codes[None], "e4m3", np.array([scale])).all()[0]
-        # codes may differ by one quantum where the value sits on a rounding tie
+        # The scale may differ by float32 rounding (amax of a float32 vs a float64
+        # fold); a code may differ by one quantum where the value sits on a
+        # rounding tie.  Anything beyond float32 rounding counts as a code flip.
         q = np.abs(got - ref_row)
         step = np.abs(ref_row) / 8 + float(scale) * 2.0 ** -9
         assert np.all(q <= step * 1.0001), f"{label} e4m3 key b={b}"
-        assert (q > 0).mean() <= 0.02, f"{label} e4m3 key b={b}: {(q > 0).mean():.3f} codes differ"
+        flips = q > 1e-5 * np.abs(ref_row).max()
+        assert flips.mean() <= 0.02, f"{label} e4m3 key b={b}: {flips.mean():.3f} codes differ"
     else:
         gk = f64(sess.state.idx_cache[b, e0])
         assert_close(gk[None], ref_row[None], g["idx_dtype"], f"{label} folded key b={b}")
