@@ -278,6 +278,22 @@ csa_status hybrid_layer_decode(const csa_layer_desc* desc, csa_layer_state* stat
 csa_status hybrid_layer_prefill(const csa_layer_desc* desc, csa_layer_state* state,
                                 const csa_prefill_io* io, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Kernel timing (diagnostics, not part of the method).  While enabled, every
+ * kernel the library launches is bracketed by two hipEvents recorded on its
+ * stream.  csa_profile_collect waits for the recorded events, fills up to
+ * max_entries per-kernel totals (launch count, summed GPU milliseconds) since
+ * the previous collect, clears them, and returns the number of kernels seen.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} csa_kernel_time;
+
+csa_status csa_profile_enable(int on);
+int csa_profile_collect(csa_kernel_time* out, int max_entries);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,7 @@ EXPORTS = [
     "csa_last_error", "csa_abi_version", "csa_compress", "csa_index_topk_workspace",
     "csa_index_topk", "csa_attend_workspace", "csa_attend", "hca_attend",
     "hybrid_layer_workspace", "hybrid_layer_decode", "hybrid_layer_prefill",
+    "csa_profile_enable", "csa_profile_collect",
 ]
 
 
@@ -61,6 +62,10 @@ class PrefillIO(C.Structure):
                 ("lse", C.c_void_p), ("topk_idx", C.c_void_p), ("topk_cnt", C.c_void_p)]
 
 
+class KernelTime(C.Structure):
+    _fields_ = [("name", C.c_char * 48), ("launches", C.c_int64), ("total_ms", C.c_double)]
+
+
 _LIB = None
 
 P = C.c_void_p
@@ -85,6 +90,8 @@ def _declare(lib):
                                     C.POINTER(DecodeIO), P, SZ, P]),
         "hybrid_layer_prefill": (I, [C.POINTER(LayerDesc), C.POINTER(LayerState),
                                      C.POINTER(PrefillIO), P, SZ, P]),
+        "csa_profile_enable": (I, [I]),
+        "csa_profile_collect": (I, [C.POINTER(KernelTime), I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -233,3 +240,14 @@ def hybrid_layer_decode(desc, state, io, ws, stream=None):
 def hybrid_layer_prefill(desc, state, io, ws, stream=None):
     check(lib().hybrid_layer_prefill(C.byref(desc), C.byref(state), C.byref(io), ptr(ws),
                                      ws.numel(), stream_handle(stream)))
+
+
+def profile_enable(on=True):
+    check(lib().csa_profile_enable(1 if on else 0))
+
+
+def profile_collect():
+    """{kernel name: (launches, total_ms)} since the previous collect."""
+    buf = (KernelTime * 64)()
+    n = lib().csa_profile_collect(buf, 64)
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].total_ms) for i in range(min(n, 64))}

@@ -167,9 +167,9 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   dim3 grid(a.B * a.Tq, (a.H + kHG - 1) / kHG), block(256);
   const size_t sh = sizeof(float) * ((size_t)kHG * a.c + (size_t)kTile * (a.c + 1) + kHG * kTile + kHG + kTile);
   if (a.dtype == F32)
-    hipLaunchKernelGGL(attend_generic_kernel<float>, grid, block, sh, s, a);
+    CSA_LAUNCH(a.dense ? "attend_dense" : "attend_sparse", attend_generic_kernel<float>, grid, block, sh, s, a);
   else
-    hipLaunchKernelGGL(attend_generic_kernel<bf16>, grid, block, sh, s, a);
+    CSA_LAUNCH(a.dense ? "attend_dense" : "attend_sparse", attend_generic_kernel<bf16>, grid, block, sh, s, a);
   return hipGetLastError();
 }
 

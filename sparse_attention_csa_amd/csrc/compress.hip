@@ -138,18 +138,18 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   dim3 grid(a.T / a.m, a.B), block(256);
   if (a.dtype == F32) {
     if (a.out_dtype == F32)
-      hipLaunchKernelGGL((compress_chunk_kernel<float, float>), grid, block, 0, s, a);
+      CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<float, float>), grid, block, 0, s, a);
     else if (a.out_dtype == BF16)
-      hipLaunchKernelGGL((compress_chunk_kernel<float, bf16>), grid, block, 0, s, a);
+      CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<float, bf16>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((compress_chunk_kernel<float, uint8_t>), grid, block, 0, s, a);
+      CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<float, uint8_t>), grid, block, 0, s, a);
   } else {
     if (a.out_dtype == F32)
-      hipLaunchKernelGGL((compress_chunk_kernel<bf16, float>), grid, block, 0, s, a);
+      CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<bf16, float>), grid, block, 0, s, a);
     else if (a.out_dtype == BF16)
-      hipLaunchKernelGGL((compress_chunk_kernel<bf16, bf16>), grid, block, 0, s, a);
+      CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<bf16, bf16>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((compress_chunk_kernel<bf16, uint8_t>), grid, block, 0, s, a);
+      CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<bf16, uint8_t>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -273,18 +273,18 @@ hipError_t launch_fold_append(const FoldArgs& a, hipStream_t s) {
   dim3 grid(a.B, n_main + (a.idx_dtype >= 0 ? 1 : 0)), block(256);
   if (a.dtype == F32) {
     if (a.idx_dtype == E4M3)
-      hipLaunchKernelGGL((fold_append_kernel<float, uint8_t>), grid, block, 0, s, a);
+      CSA_LAUNCH("fold_append", (fold_append_kernel<float, uint8_t>), grid, block, 0, s, a);
     else if (a.idx_dtype == BF16)
-      hipLaunchKernelGGL((fold_append_kernel<float, bf16>), grid, block, 0, s, a);
+      CSA_LAUNCH("fold_append", (fold_append_kernel<float, bf16>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((fold_append_kernel<float, float>), grid, block, 0, s, a);
+      CSA_LAUNCH("fold_append", (fold_append_kernel<float, float>), grid, block, 0, s, a);
   } else {
     if (a.idx_dtype == E4M3)
-      hipLaunchKernelGGL((fold_append_kernel<bf16, uint8_t>), grid, block, 0, s, a);
+      CSA_LAUNCH("fold_append", (fold_append_kernel<bf16, uint8_t>), grid, block, 0, s, a);
     else if (a.idx_dtype == F32)
-      hipLaunchKernelGGL((fold_append_kernel<bf16, float>), grid, block, 0, s, a);
+      CSA_LAUNCH("fold_append", (fold_append_kernel<bf16, float>), grid, block, 0, s, a);
     else
-      hipLaunchKernelGGL((fold_append_kernel<bf16, bf16>), grid, block, 0, s, a);
+      CSA_LAUNCH("fold_append", (fold_append_kernel<bf16, bf16>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -332,9 +332,9 @@ hipError_t launch_prefill_state(const PrefillStateArgs& a, hipStream_t s) {
   const int n_t = a.R < a.T ? a.R : a.T;
   dim3 grid(a.B, n_w + n_t + 1), block(256);
   if (a.dtype == F32)
-    hipLaunchKernelGGL(prefill_state_kernel<float>, grid, block, 0, s, a);
+    CSA_LAUNCH("prefill_state", prefill_state_kernel<float>, grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL(prefill_state_kernel<bf16>, grid, block, 0, s, a);
+    CSA_LAUNCH("prefill_state", prefill_state_kernel<bf16>, grid, block, 0, s, a);
   return hipGetLastError();
 }
 

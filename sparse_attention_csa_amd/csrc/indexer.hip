@@ -189,14 +189,14 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t s) {
   if (!a.scores) a.scores = reinterpret_cast<float*>(a.ws);
   dim3 g1((a.E_cap + 255) / 256, a.B * a.Tq), blk(256);
   if (a.idx_dtype == F32)
-    hipLaunchKernelGGL(index_score_kernel<float>, g1, blk, 0, s, a);
+    CSA_LAUNCH("index_score", index_score_kernel<float>, g1, blk, 0, s, a);
   else if (a.idx_dtype == BF16)
-    hipLaunchKernelGGL(index_score_kernel<bf16>, g1, blk, 0, s, a);
+    CSA_LAUNCH("index_score", index_score_kernel<bf16>, g1, blk, 0, s, a);
   else
-    hipLaunchKernelGGL(index_score_kernel<uint8_t>, g1, blk, 0, s, a);
+    CSA_LAUNCH("index_score", index_score_kernel<uint8_t>, g1, blk, 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_row_kernel, dim3(a.B * a.Tq), blk, 0, s, a);
+  CSA_LAUNCH("topk_row", topk_row_kernel, dim3(a.B * a.Tq), blk, 0, s, a);
   return hipGetLastError();
 }
 

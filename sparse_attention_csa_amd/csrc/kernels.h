@@ -7,6 +7,24 @@
 
 namespace csa {
 
+// kernel timing hook (profile.cpp): records events around a launch when enabled
+class ProfScope {
+ public:
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+
+ private:
+  const char* name_;
+  hipStream_t s_;
+  void* a_;
+};
+
+#define CSA_LAUNCH(name, kern, grid, block, shm, stream, ...)           \
+  do {                                                                  \
+    ::csa::ProfScope csa_prof_scope_(name, stream);                     \
+    hipLaunchKernelGGL(kern, grid, block, shm, stream, __VA_ARGS__);    \
+  } while (0)
+
 enum Dt { F32 = 0, BF16 = 1, E4M3 = 2 };
 
 // ------------------------------------------------------------ compressor
