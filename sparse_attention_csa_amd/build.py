@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
 
-SOURCES = ["api.cpp", "profile.cpp", "compress.hip", "indexer.hip", "attend.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "compress.hip", "indexer.hip", "attend.hip", "attend_mfma.hip"]
 
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 
@@ -39,9 +39,6 @@ def hipcc():
 def _compile(src, verbose):
     obj = os.path.join(BUILD, src + ".o")
     cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
-    if src.endswith(".cpp"):
-        cmd = [hipcc(), *[f for f in FLAGS if not f.startswith("--offload-arch")], "-c",
-               os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -158,12 +158,21 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
   }
 }
 
+bool attend_mfma_supported(const AttendArgs& a);
+size_t attend_mfma_ws_bytes(int BT, int H, int rows_max);
+hipError_t launch_attend_mfma(const AttendArgs& a, int rows_max, hipStream_t s);
+
 size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max) {
-  (void)B; (void)Tq; (void)H; (void)c; (void)rows_max;
-  return 256;
+  size_t n = 256;
+  if (c == 512 && H % 32 == 0) n += attend_mfma_ws_bytes(B * Tq, H, rows_max);
+  return n;
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
+  if (attend_mfma_supported(a)) {
+    const int rows_max = (a.dense ? a.E_cap : a.k) + a.n_win;
+    return launch_attend_mfma(a, rows_max, s);
+  }
   dim3 grid(a.B * a.Tq, (a.H + kHG - 1) / kHG), block(256);
   const size_t sh = sizeof(float) * ((size_t)kHG * a.c + (size_t)kTile * (a.c + 1) + kHG * kTile + kHG + kTile);
   if (a.dtype == F32)

@@ -116,20 +116,24 @@ def test_decode_csa_bf16_small(gpu_lib, vis):
     _check_decode(g, sess, f"csa-bf16-vis{vis}")
 
 
-def test_decode_hca_bf16_small(gpu_lib):
+@pytest.mark.parametrize("H,c", [(16, 128), (64, 512)])
+def test_decode_hca_bf16_small(gpu_lib, H, c):
+    """c = 512 with H % 32 == 0 runs the MFMA kernel with several row splits
+    (200 entries + 128 window rows: a ragged last tile) and the merge."""
     from sparse_attention_csa_amd.harness import DecodeSession
-    g = workloads.flash_hca_decode(seed=32, B=3, n=128 * 200, H=16, c=128)
+    g = workloads.flash_hca_decode(seed=32, B=3, n=128 * 200, H=H, c=c)
     sess = DecodeSession(g)
     sess.run()
-    _check_decode(g, sess, "hca-bf16")
+    _check_decode(g, sess, f"hca-bf16-c{c}")
 
 
-def test_decode_csa_fp8_indexer_small(gpu_lib):
+@pytest.mark.parametrize("H,c", [(16, 128), (128, 512)])
+def test_decode_csa_fp8_indexer_small(gpu_lib, H, c):
     from sparse_attention_csa_amd.harness import DecodeSession
-    g = workloads.pro_csa_decode(seed=33, B=2, n=4 * 3000, H=16, c=128, H_I=8, d_I=64, k=128)
+    g = workloads.pro_csa_decode(seed=33, B=2, n=4 * 3000, H=H, c=c, H_I=8, d_I=64, k=128)
     sess = DecodeSession(g)
     sess.run()
-    _check_decode(g, sess, "csa-fp8")
+    _check_decode(g, sess, f"csa-fp8-c{c}")
 
 
 def _check_prefill(g, sess, label, queries=None):
@@ -157,9 +161,10 @@ def _check_prefill(g, sess, label, queries=None):
         assert np.abs(lse[0, i] - ref["lse"]).max() < 1e-3
 
 
-def test_prefill_csa_and_hca_small(gpu_lib):
+@pytest.mark.parametrize("H,c", [(8, 64), (64, 512)])
+def test_prefill_csa_and_hca_small(gpu_lib, H, c):
     from sparse_attention_csa_amd.harness import PrefillSession
-    a, h = workloads.flash_prefill(seed=34, T=256, n0=1024, H=8, c=64, H_I=8, d_I=32, k=32,
+    a, h = workloads.flash_prefill(seed=34, T=256, n0=1024, H=H, c=c, H_I=8, d_I=32, k=32,
                                    m_hca=128)
     for g, label in ((a, "prefill-csa"), (h, "prefill-hca")):
         sess = PrefillSession(g)
