@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
 
-SOURCES = ["api.cpp", "profile.cpp", "compress.hip", "indexer.hip", "attend.hip", "attend_mfma.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "compress.hip", "indexer.hip", "attend.hip", "attend_mfma.hip", "indexer_mfma.hip", "topk.hip"]
 
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 

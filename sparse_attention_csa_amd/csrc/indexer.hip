@@ -14,6 +14,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace csa {
 
@@ -86,118 +87,48 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
 }
 
 // --------------------------------------------------------------------------
-// top-k: grid (B*Tq), 256 threads, one row per WG
+// scoring + selection
 // --------------------------------------------------------------------------
-// exclusive prefix count of `flag` over the WG in thread order; returns the
-// WG total through *total.  s_w holds 4 per-wave counts.
-CSA_DEV int block_excl_scan(bool flag, int* s_w, int* total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const unsigned long long mask = __ballot(flag);
-  const int in_wave = __popcll(mask & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-  if (lane == 0) s_w[wave] = __popcll(mask);
-  __syncthreads();
-  int off = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int c = s_w[w];
-    if (w < wave) off += c;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return off + in_wave;
-}
-
-__global__ __launch_bounds__(256) void topk_row_kernel(IndexArgs a) {
-  const int row = blockIdx.x, b = row / a.Tq, tq = row % a.Tq;
-  const int tid = threadIdx.x;
-  const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
-  const int nv = (int)n_visible(a, b, t);
-  const float* sc = a.scores + (size_t)row * a.E_cap;
-  int32_t* out = a.topk_idx + (size_t)row * a.k;
-  const int k = a.k;
-
-  __shared__ int hist[256];
-  __shared__ int s_w[4];
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_krem;
-
-  if (nv <= k) {
-    for (int i = tid; i < k; i += 256) out[i] = i < nv ? i : -1;
-    if (tid == 0) a.topk_cnt[row] = nv;
-    return;
-  }
-  // radix select of the k-th largest key
-  uint32_t prefix = 0;
-  int krem = k;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    hist[tid] = 0;
-    __syncthreads();
-    for (int s = tid; s < nv; s += 256) {
-      const uint32_t key = f32_key(sc[s]);
-      const bool match = pass == 0 || (key >> (shift + 8)) == prefix;
-      if (match) atomicAdd(&hist[(key >> shift) & 255], 1);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int above = 0, dsel = 0;
-      for (int dgt = 255; dgt >= 0; --dgt) {
-        const int h = hist[dgt];
-        if (above + h >= krem) {
-          dsel = dgt;
-          break;
-        }
-        above += h;
-      }
-      s_prefix = (prefix << 8) | (uint32_t)dsel;
-      s_krem = krem - above;
-    }
-    __syncthreads();
-    prefix = s_prefix;
-    krem = s_krem;
-    __syncthreads();
-  }
-  const uint32_t tau = prefix;  // exact key of the k-th largest; take krem ties
-  // in-order emission
-  int n_out = 0, n_eq = 0;
-  for (int base = 0; base < nv; base += 256) {
-    const int s = base + tid;
-    uint32_t key = 0;
-    if (s < nv) key = f32_key(sc[s]);
-    const bool eq = s < nv && key == tau;
-    int tot_eq;
-    const int eq_rank = block_excl_scan(eq, s_w, &tot_eq);
-    const bool sel = s < nv && (key > tau || (eq && n_eq + eq_rank < krem));
-    int tot_sel;
-    const int pos = block_excl_scan(sel, s_w, &tot_sel);
-    if (sel) out[n_out + pos] = s;
-    n_out += tot_sel;
-    n_eq += tot_eq;
-  }
-  for (int i = n_out + tid; i < k; i += 256) out[i] = -1;
-  if (tid == 0) a.topk_cnt[row] = n_out;
+namespace {
+constexpr int kSplitRows = 64;  // at most this many rows: split-mode selection
 }
 
 size_t index_topk_ws_bytes(int B, int Tq, int E_cap, int k) {
   (void)k;
-  return (size_t)B * Tq * E_cap * sizeof(float) + 256;
+  const int rows = B * Tq;
+  const size_t sc = ((size_t)rows * E_cap * sizeof(float) + 255) / 256 * 256;
+  return sc + topk_ws_bytes(rows, E_cap, rows <= kSplitRows);
 }
 
 hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t s) {
   IndexArgs a = a0;
-  if (!a.scores) a.scores = reinterpret_cast<float*>(a.ws);
-  dim3 g1((a.E_cap + 255) / 256, a.B * a.Tq), blk(256);
-  if (a.idx_dtype == F32)
-    CSA_LAUNCH("index_score", index_score_kernel<float>, g1, blk, 0, s, a);
-  else if (a.idx_dtype == BF16)
-    CSA_LAUNCH("index_score", index_score_kernel<bf16>, g1, blk, 0, s, a);
-  else
-    CSA_LAUNCH("index_score", index_score_kernel<uint8_t>, g1, blk, 0, s, a);
-  hipError_t e = hipGetLastError();
+  const int rows = a.B * a.Tq;
+  char* ws = reinterpret_cast<char*>(a.ws);
+  const size_t sc_bytes = ((size_t)rows * a.E_cap * sizeof(float) + 255) / 256 * 256;
+  if (!a.scores) a.scores = reinterpret_cast<float*>(ws);
+  const bool split = rows <= kSplitRows;
+  TopkWs tw = topk_ws_carve(ws + sc_bytes, rows, a.E_cap, split);
+  const bool mfma = index_mfma_supported(a) && split;
+  hipError_t e;
+  if (mfma) {
+    e = launch_index_score_mfma(a, tw, 1, s);
+  } else {
+    dim3 g1((a.E_cap + 255) / 256, rows), blk(256);
+    if (a.idx_dtype == F32)
+      CSA_LAUNCH("index_score", index_score_kernel<float>, g1, blk, 0, s, a);
+    else if (a.idx_dtype == BF16)
+      CSA_LAUNCH("index_score", index_score_kernel<bf16>, g1, blk, 0, s, a);
+    else
+      CSA_LAUNCH("index_score", index_score_kernel<uint8_t>, g1, blk, 0, s, a);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
-  CSA_LAUNCH("topk_row", topk_row_kernel, dim3(a.B * a.Tq), blk, 0, s, a);
-  return hipGetLastError();
+  if (mfma) {
+    const int slice_len = 4096;
+    const int slices = (a.E_cap + slice_len - 1) / slice_len;
+    return launch_topk_collect(a, tw, slices, slice_len, s);
+  }
+  return launch_topk_rows(a, tw, s);
 }
 
 }  // namespace csa
