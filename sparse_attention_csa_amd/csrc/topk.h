@@ -14,15 +14,16 @@ constexpr int kTopkCandCap = 8192;   // threshold-bin candidates resolved in LDS
 
 // per-row scratch, zero between calls (the finishing workgroup re-zeroes it)
 struct TopkWs {
-  int* hist;         // [rows][kTopkBins]
-  int* ctr;          // [rows][4]: candidates, finished workgroups
-  uint32_t* bitmap;  // [rows][bitmap_words]
-  uint2* cand;       // [rows][kTopkCandCap] (key, id), split mode
-  int bitmap_words;
+  int* hist;          // [rows][kTopkBins]
+  int* ctr;           // [rows][4]: candidates, finished workgroups
+  uint32_t* bitmap;   // [rows][bitmap_words]: selected entries
+  uint32_t* summary;  // [rows][summary_words]: nonzero bitmap words
+  uint2* cand;        // [rows][kTopkCandCap] (key, id), split mode
+  int bitmap_words, summary_words;
 };
 
 __device__ void topk_resolve_from_row(const float* sc, int nv, int b1, int want, uint32_t* bitmap,
-                                      uint32_t* s_flag_key, int* s_scan, int* s_hist, int* s_misc);
+                                      uint32_t* summary, int* s_scan, int* s_hist, int* s_misc);
 
 size_t topk_ws_bytes(int rows, int E_cap, bool with_cand);
 TopkWs topk_ws_carve(void* base, int rows, int E_cap, bool with_cand);

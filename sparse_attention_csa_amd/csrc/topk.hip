@@ -8,16 +8,18 @@
 // stages:
 //  1. coarse: a histogram of the top 11 key bits locates the bin b1 holding
 //     the k-th largest key; every entry in a higher bin is selected and is
-//     marked in a per-row bitmap; entries in bin b1 are candidates.
+//     marked in a two-level per-row bitmap; entries in bin b1 are candidates.
 //  2. exact: one workgroup resolves the candidates by radix select on the
 //     remaining 21 key bits (and, among equal keys, on the entry id), marks
-//     the winners, and emits the marked ids in order from the bitmap while
-//     clearing it.
+//     the winners, and emits the marked ids in order while clearing the
+//     bitmap.  The summary level (one bit per nonzero bitmap word) lets the
+//     emitter touch only nonzero words in a single prefix pass.
 // Split mode (few long rows, decode): the histogram is accumulated by the
 // scoring kernel, many workgroups scan slices of a row, and the last one to
-// finish resolves the row.  Row mode (many rows, prefill): one workgroup per
-// row does everything.  Counters, histograms and bitmaps are returned to zero
-// by the workgroup that finishes a row.
+// finish resolves the row.  Candidate slots are reserved with one atomic per
+// workgroup.  Row mode (many rows, prefill): one workgroup per row does
+// everything.  Counters, histograms and bitmaps are returned to zero by the
+// workgroup that finishes a row.
 
 #include "common.h"
 #include "kernels.h"
@@ -28,57 +30,79 @@ namespace csa {
 namespace {
 
 constexpr int kT = 256;  // threads per workgroup
+constexpr int kW = kT / 64;
 
 CSA_DEV uint32_t bin_of(uint32_t key) { return key >> kTopkShift; }
 
-// Locate the bin holding the k-th largest key.  hist: kTopkBins counters.
-// Returns b1 and `above` = number of keys in bins > b1 (< k).  kT threads.
-CSA_DEV void find_bin(const int* hist, int k, int* s_red, int* b1_out, int* above_out) {
-  // each thread owns 8 consecutive bins, counted from the top
-  const int tid = threadIdx.x;
-  const int hi = kTopkBins - 1 - 8 * tid;  // bins hi, hi-1, ..., hi-7
-  int c[8], tot = 0;
+CSA_DEV int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    c[i] = hist[hi - i];
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(v, o, 64);
+    if (lane >= o) v += x;
+  }
+  return v;
+}
+
+// exclusive prefix of v over the workgroup in thread order; *total = sum.
+// s_w: kW ints of scratch.  Contains two barriers.
+CSA_DEV int block_excl_scan(int v, int* s_w, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int inc = wave_incl_scan(v);
+  if (lane == 63) s_w[wave] = inc;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    const int c = s_w[w];
+    if (w < wave) off += c;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + inc - v;
+}
+
+// In a histogram of nb bins (nb = 64 * per), find the bin where the count,
+// accumulated from the top (descending) or the bottom, first reaches `want`.
+// Executed by wave 0 only; returns (bin, count before it) in s_out[0..1].
+template <int PER, bool DESC>
+CSA_DEV void wave_find(const int* hist, int want, int* s_out) {
+  const int lane = threadIdx.x & 63;
+  int c[PER], tot = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int bin = DESC ? (64 * PER - 1 - (PER * lane + i)) : (PER * lane + i);
+    c[i] = hist[bin];
     tot += c[i];
   }
-  // exclusive prefix over threads (bins above this thread's range)
-  s_red[tid] = tot;
-  __syncthreads();
-  for (int off = 1; off < kT; off <<= 1) {
-    const int v = tid >= off ? s_red[tid - off] : 0;
-    __syncthreads();
-    s_red[tid] += v;
-    __syncthreads();
-  }
-  int before = s_red[tid] - tot;
-  __syncthreads();
-  if (before < k && before + tot >= k) {
+  const int inc = wave_incl_scan(tot);
+  const int before = inc - tot;
+  if (before < want && inc >= want) {
     int acc = before;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      if (acc + c[i] >= k) {
-        s_red[0] = hi - i;
-        s_red[1] = acc;
+    for (int i = 0; i < PER; ++i) {
+      if (acc + c[i] >= want) {
+        s_out[0] = DESC ? (64 * PER - 1 - (PER * lane + i)) : (PER * lane + i);
+        s_out[1] = acc;
         break;
       }
       acc += c[i];
     }
   }
-  __syncthreads();
-  *b1_out = s_red[0];
-  *above_out = s_red[1];
-  __syncthreads();
 }
 
-// Radix select among n (key, id) pairs in LDS: the `want` largest by key with
-// ties to the lower id.  Marks winners in the row bitmap.  kT threads.
+CSA_DEV void mark(uint32_t* bitmap, uint32_t* summary, int id) {
+  const uint32_t old = atomicOr(&bitmap[id >> 5], 1u << (id & 31));
+  if (old == 0u) atomicOr(&summary[id >> 10], 1u << ((id >> 5) & 31));
+}
+
+// Radix select among n (key, id) pairs in LDS (all in one top-11-bit bin):
+// the `want` largest keys, ties to the lower id; winners are marked.
 CSA_DEV void select_candidates(const uint32_t* ckey, const int* cid, int n, int want,
-                               uint32_t* bitmap, int* s_hist, int* s_misc) {
+                               uint32_t* bitmap, uint32_t* summary, int* s_hist, int* s_misc) {
   const int tid = threadIdx.x;
-  // refine the key on bits 20..0 (bin bits already equal): passes of 7 bits
-  uint32_t prefix = ckey[0] >> kTopkShift;  // all candidates share the bin
+  uint32_t prefix = ckey[0] >> kTopkShift;
   int rem = want;
   int shift = kTopkShift;
   for (int pass = 0; pass < 3; ++pass) {
@@ -90,104 +114,79 @@ CSA_DEV void select_candidates(const uint32_t* ckey, const int* cid, int n, int 
       if ((key >> (shift + 7)) == prefix) atomicAdd(&s_hist[(key >> shift) & 127], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int acc = 0, d = 0;
-      for (d = 127; d >= 0; --d) {
-        if (acc + s_hist[d] >= rem) break;
-        acc += s_hist[d];
-      }
-      s_misc[0] = d;
-      s_misc[1] = rem - acc;
-    }
+    if (tid < 64) wave_find<2, true>(s_hist, rem, s_misc);
     __syncthreads();
     prefix = (prefix << 7) | (uint32_t)s_misc[0];
-    rem = s_misc[1];
+    rem -= s_misc[1];
     __syncthreads();
   }
-  const uint32_t tau = prefix;  // exact key of the last winner; `rem` ties at tau win
-  // count ties; if more than rem, pick the rem lowest ids by radix on the id
-  if (tid == 0) s_misc[2] = 0;
-  __syncthreads();
-  for (int i = tid; i < n; i += kT)
-    if (ckey[i] == tau) atomicAdd(&s_misc[2], 1);
-  __syncthreads();
-  const int n_tie = s_misc[2];
+  const uint32_t tau = prefix;  // key of the last winner; `rem` keys equal to tau win
+  int nt = 0;
+  for (int i = tid; i < n; i += kT) nt += ckey[i] == tau;
+  int n_tie;
+  block_excl_scan(nt, s_misc + 4, &n_tie);
   int id_lim = 0x7fffffff;  // ties with id <= id_lim win
   if (n_tie > rem) {
-    // rem smallest ids among the ties: 3 passes of 10 bits over a 30-bit id
+    // the rem lowest ids among the ties: 3 passes of 10 bits over a 30-bit id
     uint32_t ipref = 0;
-    int r2 = rem;
     for (int pass = 0; pass < 3; ++pass) {
       const int sh = 20 - 10 * pass;
       for (int i = tid; i < 1024; i += kT) s_hist[i] = 0;
       __syncthreads();
       for (int i = tid; i < n; i += kT) {
         const uint32_t id = (uint32_t)cid[i];
-        if (ckey[i] == tau && (pass == 0 || (id >> (sh + 10)) == ipref)) atomicAdd(&s_hist[(id >> sh) & 1023], 1);
+        if (ckey[i] == tau && (pass == 0 || (id >> (sh + 10)) == ipref))
+          atomicAdd(&s_hist[(id >> sh) & 1023], 1);
       }
       __syncthreads();
-      if (tid == 0) {
-        int acc = 0, d = 0;
-        for (d = 0; d < 1024; ++d) {
-          if (acc + s_hist[d] >= r2) break;
-          acc += s_hist[d];
-        }
-        s_misc[0] = d;
-        s_misc[1] = r2 - acc;
-      }
+      if (tid < 64) wave_find<16, false>(s_hist, rem, s_misc);
       __syncthreads();
       ipref = (ipref << 10) | (uint32_t)s_misc[0];
-      r2 = s_misc[1];
+      rem -= s_misc[1];
       __syncthreads();
     }
-    id_lim = (int)ipref;  // ids are distinct, so exactly rem ties have id <= ipref
+    id_lim = (int)ipref;  // ids are distinct: exactly the wanted ties have id <= ipref
   }
   for (int i = tid; i < n; i += kT) {
     const uint32_t key = ckey[i];
-    if (key > tau || (key == tau && cid[i] <= id_lim)) atomicOr(&bitmap[cid[i] >> 5], 1u << (cid[i] & 31));
+    if (key > tau || (key == tau && cid[i] <= id_lim)) mark(bitmap, summary, cid[i]);
   }
-  __syncthreads();
 }
 
-// Emit the ids marked in the bitmap in ascending order, clear the bitmap,
-// pad with -1 to k.  kT threads; each thread owns 32-word groups in order.
-CSA_DEV void emit_bitmap(uint32_t* bitmap, int nwords, int32_t* out, int k, int32_t* cnt_out,
-                         int* s_red) {
+// Emit the marked ids in ascending order, clear both bitmap levels, pad with
+// -1 to k.  Thread i owns summary words i, i + kT, ... in order.
+CSA_DEV void emit_bitmap(uint32_t* bitmap, uint32_t* summary, int nwords, int32_t* out, int k,
+                         int32_t* cnt_out, int* s_w) {
   const int tid = threadIdx.x;
+  const int nsum = (nwords + 31) >> 5;
   int base = 0;
-  for (int w0 = 0; w0 < nwords; w0 += kT * 4) {
-    // thread owns words w0 + 4 tid .. +3
-    uint32_t v[4];
+  for (int s0 = 0; s0 < nsum; s0 += kT) {
+    const int si = s0 + tid;
+    const uint32_t sw = si < nsum ? summary[si] : 0u;
     int c = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int wi = w0 + 4 * tid + i;
-      v[i] = wi < nwords ? bitmap[wi] : 0u;
-      c += __popc(v[i]);
+    uint32_t bits = sw;
+    while (bits) {
+      const int j = __ffs(bits) - 1;
+      bits &= bits - 1;
+      c += __popc(bitmap[32 * si + j]);
     }
-    s_red[tid] = c;
-    __syncthreads();
-    for (int off = 1; off < kT; off <<= 1) {
-      const int x = tid >= off ? s_red[tid - off] : 0;
-      __syncthreads();
-      s_red[tid] += x;
-      __syncthreads();
-    }
-    int pos = base + s_red[tid] - c;
-    const int total = s_red[kT - 1];
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int wi = w0 + 4 * tid + i;
-      uint32_t bits = v[i];
-      while (bits) {
-        const int bpos = __ffs(bits) - 1;
-        bits &= bits - 1;
-        if (pos < k) out[pos] = wi * 32 + bpos;
+    int total;
+    int pos = base + block_excl_scan(c, s_w, &total);
+    bits = sw;
+    while (bits) {
+      const int j = __ffs(bits) - 1;
+      bits &= bits - 1;
+      const int wi = 32 * si + j;
+      uint32_t v = bitmap[wi];
+      bitmap[wi] = 0u;
+      while (v) {
+        const int b = __ffs(v) - 1;
+        v &= v - 1;
+        if (pos < k) out[pos] = wi * 32 + b;
         ++pos;
       }
-      if (wi < nwords && v[i]) bitmap[wi] = 0u;
     }
+    if (sw) summary[si] = 0u;
     base += total;
   }
   for (int i = base + tid; i < k; i += kT) out[i] = -1;
@@ -202,13 +201,51 @@ CSA_DEV int64_t visible(const IndexArgs& a, int b, int64_t t) {
   return n < 0 ? 0 : n;
 }
 
+// b1 and the count above it, from a kTopkBins histogram; all threads get them
+CSA_DEV void find_bin(const int* hist, int k, int* s_w, int* s_out, int* b1, int* above) {
+  const int tid = threadIdx.x;
+  constexpr int PER = kTopkBins / kT;  // 8
+  int c[PER], tot = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    c[i] = hist[kTopkBins - 1 - (PER * tid + i)];
+    tot += c[i];
+  }
+  int all;
+  const int before = block_excl_scan(tot, s_w, &all);
+  if (before < k && before + tot >= k) {
+    int acc = before;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (acc + c[i] >= k) {
+        s_out[0] = kTopkBins - 1 - (PER * tid + i);
+        s_out[1] = acc;
+        break;
+      }
+      acc += c[i];
+    }
+  }
+  __syncthreads();
+  *b1 = s_out[0];
+  *above = s_out[1];
+  __syncthreads();
+}
+
+struct Lds {
+  uint32_t ckey[kTopkCandCap];
+  int cid[kTopkCandCap];
+  int hist[kTopkBins];
+  int misc[16];
+};
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
 // split mode: grid (n_slices, rows), kT threads.  hist filled by the scorer.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT) void topk_collect_kernel(IndexArgs a, TopkWs ws, int slice_len) {
-  __shared__ int s_red[kT];
+  extern __shared__ unsigned char dyn[];
+  Lds& L = *reinterpret_cast<Lds*>(dyn);
   __shared__ int s_flag;
   const int row = blockIdx.y, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x;
   const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
@@ -217,26 +254,39 @@ __global__ __launch_bounds__(kT) void topk_collect_kernel(IndexArgs a, TopkWs ws
   int* hist = ws.hist + (size_t)row * kTopkBins;
   int* ctr = ws.ctr + (size_t)row * 4;
   uint32_t* bitmap = ws.bitmap + (size_t)row * ws.bitmap_words;
+  uint32_t* summary = ws.summary + (size_t)row * ws.summary_words;
   uint2* cand = ws.cand + (size_t)row * kTopkCandCap;
   const float* sc = a.scores + (size_t)row * a.E_cap;
 
   int b1 = -1, above = 0;
-  if (nv > k) find_bin(hist, k, s_red, &b1, &above);
-  const int s0 = blockIdx.x * slice_len;
-  const int s1 = min(nv, s0 + slice_len);
   if (nv > k) {
+    find_bin(hist, k, L.misc, L.misc + 8, &b1, &above);
+    const int s0 = blockIdx.x * slice_len;
+    const int s1 = min(nv, s0 + slice_len);
+    // pass 1: mark winners above the bin, count candidates
+    int nc = 0;
     for (int s = s0 + tid; s < s1; s += kT) {
-      const uint32_t key = f32_key(sc[s]);
-      const int bin = (int)bin_of(key);
-      if (bin > b1) {
-        atomicOr(&bitmap[s >> 5], 1u << (s & 31));
-      } else if (bin == b1) {
-        const int slot = atomicAdd(&ctr[0], 1);
-        if (slot < kTopkCandCap) cand[slot] = make_uint2(key, (uint32_t)s);
+      const int bin = (int)bin_of(f32_key(sc[s]));
+      if (bin > b1) mark(bitmap, summary, s);
+      nc += bin == b1;
+    }
+    int total;
+    int off = block_excl_scan(nc, L.misc, &total);
+    if (tid == 0) L.misc[4] = total ? atomicAdd(&ctr[0], total) : 0;
+    __syncthreads();
+    off += L.misc[4];
+    // pass 2: write candidates into the reserved slots
+    if (nc) {
+      for (int s = s0 + tid; s < s1; s += kT) {
+        const uint32_t key = f32_key(sc[s]);
+        if ((int)bin_of(key) == b1) {
+          if (off < kTopkCandCap) cand[off] = make_uint2(key, (uint32_t)s);
+          ++off;
+        }
       }
     }
   }
-  // last workgroup of the row resolves it
+  // the last workgroup of the row resolves it
   __threadfence();
   __syncthreads();
   if (tid == 0) s_flag = (atomicAdd(&ctr[1], 1) == (int)gridDim.x - 1);
@@ -248,30 +298,22 @@ __global__ __launch_bounds__(kT) void topk_collect_kernel(IndexArgs a, TopkWs ws
     for (int i = tid; i < k; i += kT) out[i] = i < nv ? i : -1;
     if (tid == 0) a.topk_cnt[row] = nv;
   } else {
-    extern __shared__ unsigned char dyn[];
-    uint32_t* ckey = reinterpret_cast<uint32_t*>(dyn);
-    int* cid = reinterpret_cast<int*>(ckey + kTopkCandCap);
-    int* s_hist = cid + kTopkCandCap;  // 1024
-    int* s_misc = s_hist + 1024;       // 4
     const int n_cand = atomicAdd(&ctr[0], 0);
     if (n_cand <= kTopkCandCap) {
       for (int i = tid; i < n_cand; i += kT) {
         const uint2 v = cand[i];
-        ckey[i] = v.x;
-        cid[i] = (int)v.y;
+        L.ckey[i] = v.x;
+        L.cid[i] = (int)v.y;
       }
       __syncthreads();
-      select_candidates(ckey, cid, n_cand, k - above, bitmap, s_hist, s_misc);
+      select_candidates(L.ckey, L.cid, n_cand, k - above, bitmap, summary, L.hist, L.misc);
     } else {
-      // too many keys share the threshold bin: resolve from the row itself,
-      // scanning it in chunks of kTopkCandCap candidates in id order
-      topk_resolve_from_row(sc, nv, b1, k - above, bitmap, ckey, cid, s_hist, s_misc);
+      topk_resolve_from_row(sc, nv, b1, k - above, bitmap, summary, L.cid, L.hist, L.misc);
     }
     __threadfence();
     __syncthreads();
-    emit_bitmap(bitmap, (nv + 31) >> 5, out, k, &a.topk_cnt[row], s_red);
+    emit_bitmap(bitmap, summary, (nv + 31) >> 5, out, k, &a.topk_cnt[row], L.misc);
   }
-  // reset the row's scratch for the next call
   for (int i = tid; i < kTopkBins; i += kT) hist[i] = 0;
   if (tid == 0) {
     ctr[0] = 0;
@@ -284,16 +326,13 @@ __global__ __launch_bounds__(kT) void topk_collect_kernel(IndexArgs a, TopkWs ws
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT) void topk_rowsel_kernel(IndexArgs a, TopkWs ws) {
   extern __shared__ unsigned char dyn[];
-  uint32_t* ckey = reinterpret_cast<uint32_t*>(dyn);
-  int* cid = reinterpret_cast<int*>(ckey + kTopkCandCap);
-  int* s_hist = cid + kTopkCandCap;  // max(1024, kTopkBins) ints
-  int* s_misc = s_hist + kTopkBins;  // 4
-  int* s_red = s_misc + 4;           // kT
+  Lds& L = *reinterpret_cast<Lds*>(dyn);
   const int row = blockIdx.x, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x;
   const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
   const int nv = (int)visible(a, b, t);
   const int k = a.k;
   uint32_t* bitmap = ws.bitmap + (size_t)row * ws.bitmap_words;
+  uint32_t* summary = ws.summary + (size_t)row * ws.summary_words;
   const float* sc = a.scores + (size_t)row * a.E_cap;
   int32_t* out = a.topk_idx + (size_t)row * k;
   if (nv <= k) {
@@ -301,37 +340,39 @@ __global__ __launch_bounds__(kT) void topk_rowsel_kernel(IndexArgs a, TopkWs ws)
     if (tid == 0) a.topk_cnt[row] = nv;
     return;
   }
-  for (int i = tid; i < kTopkBins; i += kT) s_hist[i] = 0;
+  for (int i = tid; i < kTopkBins; i += kT) L.hist[i] = 0;
   __syncthreads();
-  for (int s = tid; s < nv; s += kT) atomicAdd(&s_hist[bin_of(f32_key(sc[s]))], 1);
+  for (int s = tid; s < nv; s += kT) atomicAdd(&L.hist[bin_of(f32_key(sc[s]))], 1);
   __syncthreads();
   int b1, above;
-  find_bin(s_hist, k, s_red, &b1, &above);
-  if (tid == 0) s_misc[3] = 0;
-  __syncthreads();
+  find_bin(L.hist, k, L.misc, L.misc + 8, &b1, &above);
+  int nc = 0;
   for (int s = tid; s < nv; s += kT) {
-    const uint32_t key = f32_key(sc[s]);
-    const int bin = (int)bin_of(key);
-    if (bin > b1) {
-      atomicOr(&bitmap[s >> 5], 1u << (s & 31));
-    } else if (bin == b1) {
-      const int slot = atomicAdd(&s_misc[3], 1);
-      if (slot < kTopkCandCap) {
-        ckey[slot] = key;
-        cid[slot] = s;
+    const int bin = (int)bin_of(f32_key(sc[s]));
+    if (bin > b1) mark(bitmap, summary, s);
+    nc += bin == b1;
+  }
+  int n_cand;
+  int off = block_excl_scan(nc, L.misc, &n_cand);
+  if (n_cand <= kTopkCandCap) {
+    if (nc) {
+      for (int s = tid; s < nv; s += kT) {
+        const uint32_t key = f32_key(sc[s]);
+        if ((int)bin_of(key) == b1) {
+          L.ckey[off] = key;
+          L.cid[off] = s;
+          ++off;
+        }
       }
     }
+    __syncthreads();
+    select_candidates(L.ckey, L.cid, n_cand, k - above, bitmap, summary, L.hist, L.misc);
+  } else {
+    topk_resolve_from_row(sc, nv, b1, k - above, bitmap, summary, L.cid, L.hist, L.misc);
   }
-  __syncthreads();
-  const int n_cand = s_misc[3];
-  __syncthreads();
-  if (n_cand <= kTopkCandCap)
-    select_candidates(ckey, cid, n_cand, k - above, bitmap, s_hist, s_misc);
-  else
-    topk_resolve_from_row(sc, nv, b1, k - above, bitmap, ckey, cid, s_hist, s_misc);
   __threadfence();
   __syncthreads();
-  emit_bitmap(bitmap, (nv + 31) >> 5, out, k, &a.topk_cnt[row], s_red);
+  emit_bitmap(bitmap, summary, (nv + 31) >> 5, out, k, &a.topk_cnt[row], L.misc);
 }
 
 // Exact resolution when the threshold bin holds more than kTopkCandCap keys:
@@ -339,7 +380,7 @@ __global__ __launch_bounds__(kT) void topk_rowsel_kernel(IndexArgs a, TopkWs ws)
 // then one in-order pass marks keys above the threshold and the lowest-id
 // ties (the row is scanned in id order, chunk by chunk).
 __device__ void topk_resolve_from_row(const float* sc, int nv, int b1, int want, uint32_t* bitmap,
-                                      uint32_t* s_flag_key, int* s_scan, int* s_hist, int* s_misc) {
+                                      uint32_t* summary, int* s_scan, int* s_hist, int* s_misc) {
   const int tid = threadIdx.x;
   uint32_t prefix = (uint32_t)b1;
   int rem = want;
@@ -353,67 +394,54 @@ __device__ void topk_resolve_from_row(const float* sc, int nv, int b1, int want,
       if ((key >> (shift + 7)) == prefix) atomicAdd(&s_hist[(key >> shift) & 127], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int acc = 0, d = 0;
-      for (d = 127; d >= 0; --d) {
-        if (acc + s_hist[d] >= rem) break;
-        acc += s_hist[d];
-      }
-      s_misc[0] = d;
-      s_misc[1] = rem - acc;
-    }
+    if (tid < 64) wave_find<2, true>(s_hist, rem, s_misc);
     __syncthreads();
     prefix = (prefix << 7) | (uint32_t)s_misc[0];
-    rem = s_misc[1];
+    rem -= s_misc[1];
     __syncthreads();
   }
   const uint32_t tau = prefix;
-  // in-order pass: ties taken while fewer than rem have been taken
   int taken = 0;
   for (int base = 0; base < nv; base += kT) {
     const int s = base + tid;
     const uint32_t key = s < nv ? f32_key(sc[s]) : 0u;
     const bool bin_ok = s < nv && (int)(key >> kTopkShift) == b1;
     const bool eq = bin_ok && key == tau;
-    s_scan[tid] = eq ? 1 : 0;
-    __syncthreads();
-    for (int off = 1; off < kT; off <<= 1) {
-      const int x = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += x;
-      __syncthreads();
-    }
-    const int rank = taken + s_scan[tid] - (eq ? 1 : 0);
-    const int tot = s_scan[kT - 1];
-    __syncthreads();
-    if (bin_ok && (key > tau || (eq && rank < rem))) atomicOr(&bitmap[s >> 5], 1u << (s & 31));
+    int tot;
+    const int rank = taken + block_excl_scan(eq ? 1 : 0, s_scan, &tot);
+    if (bin_ok && (key > tau || (eq && rank < rem))) mark(bitmap, summary, s);
     taken += tot;
   }
-  (void)s_flag_key;
   __syncthreads();
 }
 
 size_t topk_ws_bytes(int rows, int E_cap, bool with_cand) {
   const size_t words = ((size_t)E_cap + 31) / 32;
-  return (size_t)rows * (kTopkBins * 4 + 16 + words * 4 + (with_cand ? (size_t)kTopkCandCap * 8 : 0)) + 1024;
+  const size_t swords = (words + 31) / 32;
+  return (size_t)rows * (kTopkBins * 4 + 16 + (words + swords) * 4 +
+                         (with_cand ? (size_t)kTopkCandCap * 8 : 0)) +
+         1024;
 }
 
 TopkWs topk_ws_carve(void* base, int rows, int E_cap, bool with_cand) {
   TopkWs w;
   char* p = reinterpret_cast<char*>(base);
   w.bitmap_words = (int)(((size_t)E_cap + 31) / 32);
+  w.summary_words = (w.bitmap_words + 31) / 32;
   w.hist = reinterpret_cast<int*>(p);
   p += (size_t)rows * kTopkBins * 4;
   w.ctr = reinterpret_cast<int*>(p);
   p += (size_t)rows * 16;
   w.bitmap = reinterpret_cast<uint32_t*>(p);
   p += (size_t)rows * w.bitmap_words * 4;
+  w.summary = reinterpret_cast<uint32_t*>(p);
+  p += (size_t)rows * w.summary_words * 4;
   p = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(p) + 15) & ~uintptr_t(15));
   w.cand = with_cand ? reinterpret_cast<uint2*>(p) : nullptr;
   return w;
 }
 
-size_t topk_lds_bytes() { return (size_t)kTopkCandCap * 8 + (kTopkBins + 4 + kT) * 4; }
+static size_t topk_lds_bytes() { return sizeof(Lds); }
 
 hipError_t launch_topk_collect(const IndexArgs& a, const TopkWs& ws, int slices, int slice_len,
                                hipStream_t s) {
