@@ -26,7 +26,8 @@
  *   uses to zero before it completes.  Calls that share a workspace must be
  *   ordered on one stream.
  * - Supported shapes: c in {64, 128, 256, 512}; d_I in {32, 64, 128};
- *   H <= 128; H_I <= 64; 1 <= m <= 128; k <= 2048; n_win <= 256.  Other
+ *   H <= 128; H_I <= 64; 1 <= m <= 128; k <= 2048; n_win <= 256; at most
+ *   2^19 indexer entries per sequence (a 2M-token context at m = 4).  Other
  *   shapes return CSA_ERR_UNSUPPORTED (there is no slow fallback).
  */
 #ifndef CSA_H

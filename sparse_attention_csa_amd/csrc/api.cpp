@@ -38,6 +38,7 @@ csa_status from_hip(hipError_t e, const char* what) {
 bool is_pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxIndexEntries = 1 << 19;  // top-k keeps a row's selection bitmap in LDS
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 #define REQUIRE(cond, status, ...)                      \
@@ -129,6 +130,8 @@ static csa_status check_index(csa_dtype idx_dtype, const void* q_idx, const floa
   REQUIRE(k <= 2048, CSA_ERR_UNSUPPORTED, "k <= 2048 supported (got %d)", k);
   REQUIRE(m <= 128, CSA_ERR_UNSUPPORTED, "m <= 128 supported");
   REQUIRE(vis == 0 || vis == 1, CSA_ERR_ARG, "bad visibility");
+  REQUIRE(E_cap <= kMaxIndexEntries, CSA_ERR_UNSUPPORTED, "E_cap <= %d supported (got %d)",
+          kMaxIndexEntries, E_cap);
   return CSA_OK;
 }
 
@@ -249,6 +252,8 @@ static csa_status check_state(const csa_layer_desc* d, const csa_layer_state* s)
   REQ_PTR(s->kv_cache); REQ_PTR(s->n_entries); REQ_PTR(s->win_ring); REQ_PTR(s->tail);
   if (d->kind == CSA_LAYER_CSA) {
     REQ_PTR(s->idx_cache); REQ_PTR(s->idx_tail);
+    REQUIRE(s->E_cap <= kMaxIndexEntries, CSA_ERR_UNSUPPORTED, "E_cap <= %d supported for CSA layers",
+            kMaxIndexEntries);
     REQUIRE(d->idx_dtype != CSA_E4M3 || s->idx_scale != nullptr, CSA_ERR_ARG, "E4M3 indexer cache needs idx_scale");
   }
   return CSA_OK;
@@ -285,7 +290,6 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
   REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
   hipStream_t hs = (hipStream_t)stream;
   char* w = (char*)ws;
-  int32_t* counters = (int32_t*)w;
   w += align_up((size_t)B * sizeof(int32_t));
 
   csa::FoldArgs f{};
@@ -296,7 +300,6 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
   f.x_new = io->x_new; f.tail = s->tail; f.idx_tail = s->idx_tail; f.win_ring = s->win_ring;
   f.kv_cache = s->kv_cache; f.idx_cache = s->idx_cache; f.idx_scale = s->idx_scale; f.E_cap = s->E_cap;
   f.bias_a = s->bias_a; f.bias_b = s->bias_b; f.ibias_a = s->ibias_a; f.ibias_b = s->ibias_b;
-  f.counters = counters;
   hipError_t e = csa::launch_fold_append(f, hs);
   if (e != hipSuccess) return from_hip(e, "hybrid_layer_decode/fold");
 

@@ -84,6 +84,31 @@ CSA_DEV float wave_max(float v) {
   return v;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global access of the wave (vmcnt(0)), which would drain
+// asynchronous global-to-LDS prefetches; callers that need those complete
+// wait for them explicitly.
+CSA_DEV void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Workgroup barrier for LDS written by ordinary LDS stores only, while
+// global-to-LDS DMAs may still be in flight: waits for this wave's LDS
+// operations (lgkmcnt = 0; vmcnt and expcnt are not waited), then s_barrier.
+// The empty asm statements keep the compiler from moving memory accesses
+// across.  (An LDS-scoped release fence would also wait for the in-flight
+// DMAs, since they write LDS.)  DMA'd data is published by waiting for its
+// vmcnt explicitly before this barrier.
+constexpr int kWaitLgkm0 = 0xC07F;  // gfx9 s_waitcnt: vmcnt 63, expcnt 7, lgkmcnt 0
+CSA_DEV void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
 // visible-entry limit for a query at position t
 CSA_DEV int64_t vis_limit(int64_t t, int m, int vis) { return vis == 0 ? t / m : (t + 1) / m; }
 

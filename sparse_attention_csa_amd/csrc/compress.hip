@@ -158,119 +158,148 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
 // Decode step: fold the block whose entry becomes visible at this position,
 // and append the new token to the tail ring and the window ring.
 //
-// grid (B, S): S-1 (or S) slices of 64 main coordinates, plus one indexer
-// slice of d_I coordinates for CSA.  256 threads = CS coordinates x G token
-// groups.  Every WG reads its sources before it overwrites the tail slot of
-// the new token (same coordinates, same WG), and the last WG of a sequence to
-// finish publishes n_entries[b] (all WGs of b have read it by then).
+// One 1024-thread workgroup per sequence: thread = (coordinate, source
+// group); every group folds an interleaved subset of the block's source
+// tokens with an online softmax per coordinate, the groups merge through LDS.
+// The workgroup reads all its sources before it overwrites the tail slot of
+// the new token, and publishes n_entries[b] itself (no other workgroup reads
+// it), so no cross-workgroup ordering is needed.
 // --------------------------------------------------------------------------
-template <typename T, typename TI>
-__global__ __launch_bounds__(256) void fold_append_kernel(FoldArgs a) {
-  const int b = blockIdx.x, slice = blockIdx.y, tid = threadIdx.x;
-  const int n_main = (a.c + 63) / 64;
-  const bool idx_slice = slice >= n_main;
-  const int d = idx_slice ? a.d_I : a.c;        // row width of this slice's arrays
-  const int CS = idx_slice ? a.d_I : 64;        // coordinates per slice
-  const int G = 256 / CS;                       // token groups
-  const int coord = tid % CS, grp = tid / CS;
-  const int r = (idx_slice ? 0 : slice * 64) + coord;
-  const bool active = r < d && grp < G;
-  const int nstr = idx_slice ? 4 : (a.overlap ? 4 : 2);
-  const int m = a.m, R = a.R;
+constexpr int kFoldT = 1024;
 
+// Sources of entry e for coordinate r, split over G groups: group g takes
+// source slots g, g+G, ... (branch a: tokens e*m + j; branch b: (e-1)*m + j).
+// Ring slots are computed in 32 bits from one 64-bit remainder.  All loads of
+// a group are issued before the softmax chain consumes them.
+template <typename T>
+CSA_DEV Soft fold_sources(const T* tail, const T* io, int d, int r, int grp, int G, int m, int R,
+                          int64_t t, int64_t e, bool use_b, const float* ba, const float* bb) {
+  Soft st{-INFINITY, 0.f, 0.f};
+  const int nsrc = use_b ? 2 * m : m;
+  const int64_t p_first = use_b ? (e - 1) * m : e * m;  // earliest source token
+  const int slot_first = (int)(p_first % R);
+  const int t_off = (int)(t - p_first);                 // new token's offset (may be > 2m)
+  // source slot j: a-branch j < m is token e*m + j, b-branch j >= m is (e-1)*m + (j - m)
+  auto tok_off = [&](int j) -> int { return use_b ? (j < m ? m + j : j - m) : j; };
+  float lgv[16], vv[16];
+  for (int j0 = grp; j0 < nsrc; j0 += 16 * G) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int j = j0 + u * G;
+      lgv[u] = -INFINITY;
+      vv[u] = 0.f;
+      if (j < nsrc) {
+        const int off = tok_off(j);
+        const bool a_branch = j < m;
+        const int sc = a_branch ? 0 : 2;
+        const int jj = a_branch ? j : j - m;
+        float z, v;
+        if (off == t_off) {
+          z = ld(io, (size_t)(sc + 1) * d + r);
+          v = ld(io, (size_t)sc * d + r);
+        } else {
+          int slot = slot_first + off;
+          while (slot >= R) slot -= R;
+          z = ld(tail, ((size_t)(sc + 1) * R + slot) * d + r);
+          v = ld(tail, ((size_t)sc * R + slot) * d + r);
+        }
+        const float* bias = a_branch ? ba : bb;
+        lgv[u] = z + (bias ? bias[jj * d + r] : 0.f);
+        vv[u] = v;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (lgv[u] != -INFINITY) soft_push(st, lgv[u], vv[u]);
+  }
+  return st;
+}
+
+// merge the G partial states of each coordinate (LDS), result in group 0
+CSA_DEV float fold_merge(Soft st, Soft* s_part, int d, int r, int grp, int G) {
+  const int tid = threadIdx.x;
+  s_part[tid] = st;
+  __syncthreads();
+  float val = 0.f;
+  if (grp == 0 && r < d) {
+    Soft acc = s_part[tid];
+    for (int g2 = 1; g2 < G; ++g2) acc = soft_merge(acc, s_part[g2 * d + r]);
+    val = acc.acc / acc.l;
+  }
+  __syncthreads();
+  return val;
+}
+
+template <typename T, typename TI>
+__global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
+  __shared__ Soft s_part[kFoldT];
+  __shared__ float s_red[kFoldT / 64];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int m = a.m, R = a.R, c = a.c;
   const int64_t t = a.pos[b];
   const int n_have = a.n_entries[b];
   const int64_t lim = vis_limit(t, m, a.vis);
   const bool fold = (lim == (int64_t)n_have + 1) && (int64_t)n_have < (int64_t)a.E_cap;
   const int64_t e = n_have;
-  const bool use_b = (a.overlap || idx_slice) && e > 0;
+  const bool has_idx = a.idx_dtype >= 0;
+  const int nstr = a.overlap ? 4 : 2;
+  const T* tail = reinterpret_cast<const T*>(a.tail) + (size_t)b * nstr * R * c;
+  const T* io = reinterpret_cast<const T*>(a.streams) + (size_t)b * nstr * c;
 
-  const T* tail = cptr<T>(idx_slice ? a.idx_tail : a.tail) + (size_t)b * nstr * R * d;
-  const T* io = cptr<T>(idx_slice ? a.idx_streams : a.streams) + (size_t)b * nstr * d;
-  const float* ba = idx_slice ? a.ibias_a : a.bias_a;
-  const float* bb = idx_slice ? a.ibias_b : a.bias_b;
-
-  __shared__ Soft s_part[256];
-  __shared__ float s_red[4];
-  Soft st_{-INFINITY, 0.f, 0.f};
-  if (fold && active) {
-    // source token p through stream pair (content, logit) = (0,1) for a, (2,3) for b
-    auto src = [&](int64_t p, int sc) -> float {
-      if (p == t) return ld(io, (size_t)sc * d + r);
-      return ld(tail, ((size_t)sc * R + (size_t)(p % R)) * d + r);
-    };
-    const int nsrc = use_b ? 2 * m : m;
-    for (int j = grp; j < nsrc; j += G) {
-      float lg, v;
-      if (j < m) {
-        const int64_t p = e * m + j;
-        lg = src(p, 1) + (ba ? ba[j * d + r] : 0.f);
-        v = src(p, 0);
-      } else {
-        const int64_t p = (e - 1) * m + (j - m);
-        lg = src(p, 3) + (bb ? bb[(j - m) * d + r] : 0.f);
-        v = src(p, 2);
-      }
-      soft_push(st_, lg, v);
-    }
-  }
-  s_part[tid] = st_;
-  __syncthreads();
-  float val = 0.f;
-  if (fold && active && grp == 0) {
-    Soft acc = s_part[tid];
-    for (int g2 = 1; g2 < G; ++g2) acc = soft_merge(acc, s_part[g2 * CS + coord]);
-    val = acc.acc / acc.l;
-  }
-  // append the new token's streams (reads above are complete for this WG)
-  if (active && grp == 0) {
-    T* tw = const_cast<T*>(tail);
-    const size_t slot = (size_t)(t % R);
-    for (int sc = 0; sc < nstr; ++sc) tw[((size_t)sc * R + slot) * d + r] = cptr<T>(io)[(size_t)sc * d + r];
-    if (!idx_slice) {
-      T* ring = reinterpret_cast<T*>(a.win_ring) + (size_t)b * a.n_win * a.c;
-      ring[(size_t)(t % a.n_win) * a.c + r] = cptr<T>(a.x_new)[(size_t)b * a.c + r];
-    }
-  }
   if (fold) {
-    if (!idx_slice) {
-      if (active && grp == 0) {
-        T* kv = reinterpret_cast<T*>(a.kv_cache);
-        st(kv, ((size_t)b * a.E_cap + e) * a.c + r, val);
+    // main entry: coordinates r = tid % c, groups of kFoldT / c
+    const int G = kFoldT / c, r = tid % c, grp = tid / c;
+    Soft part = fold_sources(tail, io, c, r, grp, G, m, R, t, e, a.overlap && e > 0, a.bias_a, a.bias_b);
+    const float val = fold_merge(part, s_part, c, r, grp, G);
+    if (grp == 0) st(reinterpret_cast<T*>(a.kv_cache), ((size_t)b * a.E_cap + e) * c + r, val);
+    if (has_idx) {
+      const int d = a.d_I, Gi = kFoldT / d, ri = tid % d, gi = tid / d;
+      const T* itail = reinterpret_cast<const T*>(a.idx_tail) + (size_t)b * 4 * R * d;
+      const T* iio = reinterpret_cast<const T*>(a.idx_streams) + (size_t)b * 4 * d;
+      Soft si = fold_sources(itail, iio, d, ri, gi, Gi, m, R, t, e, e > 0, a.ibias_a, a.ibias_b);
+      const float iv = fold_merge(si, s_part, d, ri, gi, Gi);
+      if constexpr (sizeof(TI) == 1) {
+        float am = gi == 0 ? fabsf(iv) : 0.f;
+        am = wave_max(am);
+        if ((tid & 63) == 0) s_red[tid >> 6] = am;
+        __syncthreads();
+        am = 0.f;
+        for (int i = 0; i < kFoldT / 64; ++i) am = fmaxf(am, s_red[i]);
+        float scale = am / 448.0f;
+        if (!(scale > 0.f)) scale = 1.f;
+        if (gi == 0)
+          reinterpret_cast<uint8_t*>(a.idx_cache)[((size_t)b * a.E_cap + e) * d + ri] = f32_to_e4m3(iv / scale);
+        if (tid == 0) a.idx_scale[(size_t)b * a.E_cap + e] = scale;
+      } else {
+        if (gi == 0) st(reinterpret_cast<TI*>(a.idx_cache), ((size_t)b * a.E_cap + e) * d + ri, iv);
       }
-    } else if constexpr (sizeof(TI) == 1) {
-      float am = (active && grp == 0) ? fabsf(val) : 0.f;
-      am = wave_max(am);
-      if ((tid & 63) == 0) s_red[tid >> 6] = am;
-      __syncthreads();
-      am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-      float scale = am / 448.0f;
-      if (!(scale > 0.f)) scale = 1.f;
-      if (active && grp == 0)
-        reinterpret_cast<uint8_t*>(a.idx_cache)[((size_t)b * a.E_cap + e) * a.d_I + r] =
-            f32_to_e4m3(val / scale);
-      if (tid == 0) a.idx_scale[(size_t)b * a.E_cap + e] = scale;
-    } else {
-      if (active && grp == 0) st(reinterpret_cast<TI*>(a.idx_cache), ((size_t)b * a.E_cap + e) * a.d_I + r, val);
     }
   }
-  // publish n_entries once every WG of this sequence is done reading it
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int total = gridDim.y;
-    const int old = atomicAdd(&a.counters[b], 1);
-    if (old == total - 1) {
-      if (fold) a.n_entries[b] = n_have + 1;
-      a.counters[b] = 0;
-      __threadfence();
+  __syncthreads();  // every source read of this sequence is done
+  // append the new token: tail slot t % R of every stream, window ring slot
+  const size_t slot = (size_t)(t % R);
+  T* tw = const_cast<T*>(tail);
+  for (int i = tid; i < nstr * c; i += kFoldT) {
+    const int sc = i / c, r = i % c;
+    tw[((size_t)sc * R + slot) * c + r] = io[(size_t)sc * c + r];
+  }
+  if (has_idx) {
+    const int d = a.d_I;
+    T* itw = reinterpret_cast<T*>(a.idx_tail) + (size_t)b * 4 * R * d;
+    const T* iio = reinterpret_cast<const T*>(a.idx_streams) + (size_t)b * 4 * d;
+    for (int i = tid; i < 4 * d; i += kFoldT) {
+      const int sc = i / d, r = i % d;
+      itw[((size_t)sc * R + slot) * d + r] = iio[(size_t)sc * d + r];
     }
   }
+  T* ring = reinterpret_cast<T*>(a.win_ring) + (size_t)b * a.n_win * c;
+  for (int r = tid; r < c; r += kFoldT)
+    ring[(size_t)(t % a.n_win) * c + r] = reinterpret_cast<const T*>(a.x_new)[(size_t)b * c + r];
+  if (fold && tid == 0) a.n_entries[b] = n_have + 1;
 }
 
 hipError_t launch_fold_append(const FoldArgs& a, hipStream_t s) {
-  const int n_main = (a.c + 63) / 64;
-  dim3 grid(a.B, n_main + (a.idx_dtype >= 0 ? 1 : 0)), block(256);
+  dim3 grid(a.B), block(kFoldT);
   if (a.dtype == F32) {
     if (a.idx_dtype == E4M3)
       CSA_LAUNCH("fold_append", (fold_append_kernel<float, uint8_t>), grid, block, 0, s, a);

@@ -124,7 +124,7 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t s) {
   }
   if (e != hipSuccess) return e;
   if (mfma) {
-    const int slice_len = 4096;
+    const int slice_len = kTopkCollectSlice;
     const int slices = (a.E_cap + slice_len - 1) / slice_len;
     return launch_topk_collect(a, tw, slices, slice_len, s);
   }

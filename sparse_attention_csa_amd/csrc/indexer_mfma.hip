@@ -12,8 +12,9 @@
 // accumulator holds 4 heads x 1 key per lane, so ReLU, the head weights and
 // the head sum are in-lane, then two cross-lane adds.  For e4m3 the per-head
 // query scale is folded into w and the per-key scale multiplies the sum (both
-// positive, so they commute with ReLU).  The next tile's keys are loaded
-// before the current tile's MFMAs.  With use_hist the wave also counts the
+// positive, so they commute with ReLU).  Each wave scores a contiguous run of
+// tiles in batches of four, loading the next batch before scoring the current
+// one, so eight tiles' keys are in flight per wave.  With use_hist the wave also counts the
 // top 11 bits of each score's order-preserving key into an LDS histogram that
 // is added to the row's global histogram at the end (stage 1 of the top-k).
 
@@ -45,13 +46,17 @@ struct KeyOp<0> {  // bf16 keys: 4 x 16 B per lane
   }
 };
 
+// e4m3 keys: 2 x 16 B per lane.  The reduction index is permuted so that one
+// load instruction covers bytes 0..63 (then 64..127) of each key contiguously:
+// lane group g supplies d = 16g..16g+15 and 64+16g..64+16g+15 as its 32
+// k-slots; the query operand uses the same permutation.
 template <>
-struct KeyOp<1> {  // e4m3 keys: 2 x 16 B per lane (32 consecutive codes)
+struct KeyOp<1> {
   uint4 v[2];
   CSA_DEV void load(const uint8_t* row, int lg, bool ok) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      v[i] = ok ? *reinterpret_cast<const uint4*>(row + 32 * lg + 16 * i) : make_uint4(0, 0, 0, 0);
+      v[i] = ok ? *reinterpret_cast<const uint4*>(row + 64 * i + 16 * lg) : make_uint4(0, 0, 0, 0);
   }
 };
 
@@ -86,8 +91,8 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   for (int ht = 0; ht < HT; ++ht) {
     const int h = 16 * ht + li;
     if constexpr (FP8) {
-      const uint8_t* q = reinterpret_cast<const uint8_t*>(a.q) + ((size_t)row * H + h) * kD + 32 * lg;
-      const uint4 v0 = *reinterpret_cast<const uint4*>(q), v1 = *reinterpret_cast<const uint4*>(q + 16);
+      const uint8_t* q = reinterpret_cast<const uint8_t*>(a.q) + ((size_t)row * H + h) * kD + 16 * lg;
+      const uint4 v0 = *reinterpret_cast<const uint4*>(q), v1 = *reinterpret_cast<const uint4*>(q + 64);
       q8[ht] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
     } else {
       const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)row * H + h) * kD;
@@ -107,47 +112,58 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   const float* ksc = a.k_scale ? a.k_scale + (size_t)b * a.E_cap : nullptr;
   float* out = a.scores + (size_t)row * a.E_cap;
 
+  // each wave scores a contiguous range of 16-key tiles, U tiles per batch,
+  // with the next batch's loads in flight while the current one is scored
+  constexpr int U = 4;
   const int64_t ntile = (nv + 15) / 16;
-  const int64_t stride = (int64_t)gridDim.x * 4;
-  int64_t tile = (int64_t)blockIdx.x * 4 + w;
-  KeyOp<FP8> cur, nxt;
-  {
-    const int64_t e = tile * 16 + li;
-    cur.load(keys + (size_t)(e < nv ? e : 0) * kD, lg, tile < ntile && e < nv);
-  }
-  for (; tile < ntile; tile += stride) {
-    const int64_t e = tile * 16 + li;
-    const bool ok = e < nv;
-    {
-      const int64_t en = (tile + stride) * 16 + li;
-      const bool okn = tile + stride < ntile && en < nv;
-      nxt.load(keys + (size_t)(okn ? en : 0) * kD, lg, okn);
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t per = ((ntile + nwaves - 1) / nwaves + U - 1) / U * U;
+  const int64_t t0 = ((int64_t)blockIdx.x * 4 + w) * per;
+  const int64_t t1 = t0 + per < ntile ? t0 + per : ntile;
+  auto load_batch = [&](KeyOp<FP8>* kb, int64_t tb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = (tb + u) * 16 + li;
+      const bool ok = tb + u < t1 && e < nv;
+      kb[u].load(keys + (size_t)(ok ? e : 0) * kD, lg, ok);
     }
-    float part = 0.f;
+  };
+  KeyOp<FP8> cur[U], nxt[U];
+  if (t0 < t1) load_batch(cur, t0);
+  for (int64_t tb = t0; tb < t1; tb += U) {
+    if (tb + U < t1) load_batch(nxt, tb + U);
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (FP8) {
-        const i32x8_t kb = i32x8_t{(int)cur.v[0].x, (int)cur.v[0].y, (int)cur.v[0].z, (int)cur.v[0].w,
-                                   (int)cur.v[1].x, (int)cur.v[1].y, (int)cur.v[1].z, (int)cur.v[1].w};
-        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q8[ht], kb, c, 0, 0, 0, 127, 0, 127);
-      } else {
+    for (int u = 0; u < U; ++u) {
+      const int64_t e = (tb + u) * 16 + li;
+      const bool ok = tb + u < t1 && e < nv;
+      float part = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[ht][ks], __builtin_bit_cast(bf16x8_t, cur.v[ks]), c,
-                                                      0, 0, 0);
+      for (int ht = 0; ht < HT; ++ht) {
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (FP8) {
+          const i32x8_t kb = i32x8_t{(int)cur[u].v[0].x, (int)cur[u].v[0].y, (int)cur[u].v[0].z,
+                                     (int)cur[u].v[0].w, (int)cur[u].v[1].x, (int)cur[u].v[1].y,
+                                     (int)cur[u].v[1].z, (int)cur[u].v[1].w};
+          c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q8[ht], kb, c, 0, 0, 0, 127, 0, 127);
+        } else {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[ht][ks], __builtin_bit_cast(bf16x8_t, cur[u].v[ks]),
+                                                        c, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) part += wr[ht][r] * fmaxf(c[r], 0.f);
       }
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      if (ok && lg == 0) {
+        if (ksc) part *= ksc[e];
+        out[e] = part;
+        if (use_hist) atomicAdd(&s_hist[f32_key(part) >> kTopkShift], 1);
+      }
+    }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part += wr[ht][r] * fmaxf(c[r], 0.f);
-    }
-    part += __shfl_xor(part, 16, 64);
-    part += __shfl_xor(part, 32, 64);
-    if (ok && lg == 0) {
-      if (ksc) part *= ksc[e];
-      out[e] = part;
-      if (use_hist) atomicAdd(&s_hist[f32_key(part) >> kTopkShift], 1);
-    }
-    cur = nxt;
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
   }
   if (use_hist) {
     __syncthreads();
@@ -165,9 +181,9 @@ bool index_mfma_supported(const IndexArgs& a) {
 
 hipError_t launch_index_score_mfma(const IndexArgs& a, const TopkWs& ws, int use_hist, hipStream_t s) {
   const int rows = a.B * a.Tq;
-  // about 1024 workgroups in total, at most one tile per wave beyond the row
+  // about 1024 workgroups in total, at least 4 tiles (one batch) per wave
   int per_row = (1024 + rows - 1) / rows;
-  const int max_wg = (int)((((int64_t)a.E_cap + 15) / 16 + 3) / 4);
+  const int max_wg = (int)((((int64_t)a.E_cap + 15) / 16 + 15) / 16);
   if (per_row > max_wg) per_row = max_wg;
   if (per_row < 1) per_row = 1;
   dim3 grid(per_row, rows), block(256);

@@ -62,7 +62,6 @@ struct FoldArgs {
   float* idx_scale;         // [B][E_cap]
   int E_cap;
   const float *bias_a, *bias_b, *ibias_a, *ibias_b;
-  int32_t* counters;        // [B] workspace, zero between calls
 };
 hipError_t launch_fold_append(const FoldArgs& a, hipStream_t s);
 

@@ -26,6 +26,9 @@ __device__ void topk_resolve_from_row(const float* sc, int nv, int b1, int want,
                                       uint32_t* summary, int* s_scan, int* s_hist, int* s_misc);
 
 size_t topk_ws_bytes(int rows, int E_cap, bool with_cand);
+// LDS of the split-mode resolve kernel; it must fit one workgroup (160 KB)
+size_t topk_split_lds_bytes(int E_cap);
+constexpr int kTopkCollectSlice = 4096;  // entries per collect workgroup
 TopkWs topk_ws_carve(void* base, int rows, int E_cap, bool with_cand);
 hipError_t launch_topk_collect(const IndexArgs& a, const TopkWs& ws, int slices, int slice_len,
                                hipStream_t s);

@@ -11,13 +11,13 @@
 //     marked in a two-level per-row bitmap; entries in bin b1 are candidates.
 //  2. exact: one workgroup resolves the candidates by radix select on the
 //     remaining 21 key bits (and, among equal keys, on the entry id), marks
-//     the winners, and emits the marked ids in order while clearing the
-//     bitmap.  The summary level (one bit per nonzero bitmap word) lets the
+//     the winners in an LDS copy of the bitmap, and emits the marked ids in
+//     order.  The summary level (one bit per nonzero bitmap word) lets the
 //     emitter touch only nonzero words in a single prefix pass.
 // Split mode (few long rows, decode): the histogram is accumulated by the
-// scoring kernel, many workgroups scan slices of a row, and the last one to
-// finish resolves the row.  Candidate slots are reserved with one atomic per
-// workgroup.  Row mode (many rows, prefill): one workgroup per row does
+// scoring kernel, many workgroups scan slices of a row (candidate slots are
+// reserved with one atomic per workgroup), then a second kernel resolves each
+// row with one workgroup.  No workgroup waits on another.  Row mode (many rows, prefill): one workgroup per row does
 // everything.  Counters, histograms and bitmaps are returned to zero by the
 // workgroup that finishes a row.
 
@@ -31,6 +31,8 @@ namespace {
 
 constexpr int kT = 256;  // threads per workgroup
 constexpr int kW = kT / 64;
+constexpr int kCollectPer = 16;  // keys per thread in a collect slice
+static_assert(kCollectPer * kT == kTopkCollectSlice, "collect slice");
 
 CSA_DEV uint32_t bin_of(uint32_t key) { return key >> kTopkShift; }
 
@@ -92,9 +94,10 @@ CSA_DEV void wave_find(const int* hist, int want, int* s_out) {
   }
 }
 
+// mark an id in a two-level bitmap (global or LDS); results are not awaited
 CSA_DEV void mark(uint32_t* bitmap, uint32_t* summary, int id) {
-  const uint32_t old = atomicOr(&bitmap[id >> 5], 1u << (id & 31));
-  if (old == 0u) atomicOr(&summary[id >> 10], 1u << ((id >> 5) & 31));
+  atomicOr(&bitmap[id >> 5], 1u << (id & 31));
+  atomicOr(&summary[id >> 10], 1u << ((id >> 5) & 31));
 }
 
 // Radix select among n (key, id) pairs in LDS (all in one top-11-bit bin):
@@ -244,9 +247,7 @@ struct Lds {
 // split mode: grid (n_slices, rows), kT threads.  hist filled by the scorer.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kT) void topk_collect_kernel(IndexArgs a, TopkWs ws, int slice_len) {
-  extern __shared__ unsigned char dyn[];
-  Lds& L = *reinterpret_cast<Lds*>(dyn);
-  __shared__ int s_flag;
+  __shared__ int s_misc[16];
   const int row = blockIdx.y, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x;
   const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
   const int nv = (int)visible(a, b, t);
@@ -260,45 +261,77 @@ __global__ __launch_bounds__(kT) void topk_collect_kernel(IndexArgs a, TopkWs ws
 
   int b1 = -1, above = 0;
   if (nv > k) {
-    find_bin(hist, k, L.misc, L.misc + 8, &b1, &above);
+    find_bin(hist, k, s_misc, s_misc + 8, &b1, &above);
     const int s0 = blockIdx.x * slice_len;
     const int s1 = min(nv, s0 + slice_len);
-    // pass 1: mark winners above the bin, count candidates
+    // pass 1: mark winners above the bin, count candidates (keys stay in
+    // registers for pass 2; slices are at most kCollectPer * kT long)
+    uint32_t keys[kCollectPer];
     int nc = 0;
-    for (int s = s0 + tid; s < s1; s += kT) {
-      const int bin = (int)bin_of(f32_key(sc[s]));
-      if (bin > b1) mark(bitmap, summary, s);
-      nc += bin == b1;
+#pragma unroll
+    for (int i = 0; i < kCollectPer; ++i) {
+      const int s = s0 + tid + i * kT;
+      keys[i] = s < s1 ? f32_key(sc[s]) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < kCollectPer; ++i) {
+      const int s = s0 + tid + i * kT;
+      if (s < s1) {
+        const int bin = (int)bin_of(keys[i]);
+        if (bin > b1) mark(bitmap, summary, s);
+        nc += bin == b1;
+      }
     }
     int total;
-    int off = block_excl_scan(nc, L.misc, &total);
-    if (tid == 0) L.misc[4] = total ? atomicAdd(&ctr[0], total) : 0;
+    int off = block_excl_scan(nc, s_misc, &total);
+    if (tid == 0) s_misc[4] = total ? atomicAdd(&ctr[0], total) : 0;
     __syncthreads();
-    off += L.misc[4];
+    off += s_misc[4];
     // pass 2: write candidates into the reserved slots
     if (nc) {
-      for (int s = s0 + tid; s < s1; s += kT) {
-        const uint32_t key = f32_key(sc[s]);
-        if ((int)bin_of(key) == b1) {
-          if (off < kTopkCandCap) cand[off] = make_uint2(key, (uint32_t)s);
+#pragma unroll
+      for (int i = 0; i < kCollectPer; ++i) {
+        const int s = s0 + tid + i * kT;
+        if (s < s1 && (int)bin_of(keys[i]) == b1) {
+          if (off < kTopkCandCap) cand[off] = make_uint2(keys[i], (uint32_t)s);
           ++off;
         }
       }
     }
   }
-  // the last workgroup of the row resolves it
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_flag = (atomicAdd(&ctr[1], 1) == (int)gridDim.x - 1);
-  __syncthreads();
-  if (!s_flag) return;
-  __threadfence();
+}
+
+// ---------------------------------------------------------------------------
+// split mode, stage 2: grid (rows), one workgroup resolves a row's
+// candidates, emits its ids and clears the row's scratch.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kT) void topk_resolve_kernel(IndexArgs a, TopkWs ws) {
+  extern __shared__ unsigned char dyn[];
+  Lds& L = *reinterpret_cast<Lds*>(dyn);
+  uint32_t* lbit = reinterpret_cast<uint32_t*>(dyn + sizeof(Lds));  // [bitmap_words]
+  uint32_t* lsum = lbit + ws.bitmap_words;                           // [summary_words]
+  const int row = blockIdx.x, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x;
+  const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
+  const int nv = (int)visible(a, b, t);
+  const int k = a.k;
+  int* hist = ws.hist + (size_t)row * kTopkBins;
+  int* ctr = ws.ctr + (size_t)row * 4;
+  uint32_t* bitmap = ws.bitmap + (size_t)row * ws.bitmap_words;
+  uint32_t* summary = ws.summary + (size_t)row * ws.summary_words;
+  const uint2* cand = ws.cand + (size_t)row * kTopkCandCap;
+  const float* sc = a.scores + (size_t)row * a.E_cap;
   int32_t* out = a.topk_idx + (size_t)row * k;
   if (nv <= k) {
     for (int i = tid; i < k; i += kT) out[i] = i < nv ? i : -1;
     if (tid == 0) a.topk_cnt[row] = nv;
   } else {
-    const int n_cand = atomicAdd(&ctr[0], 0);
+    const int nwords = (nv + 31) >> 5, nsum = (nwords + 31) >> 5;
+    // the row's winners so far (marked by the collect pass) move to LDS
+    for (int i = tid; i < nwords; i += kT) lbit[i] = bitmap[i];
+    for (int i = tid; i < nsum; i += kT) lsum[i] = summary[i];
+    int b1, above;
+    find_bin(hist, k, L.misc, L.misc + 8, &b1, &above);
+    const int n_cand = ctr[0];
     if (n_cand <= kTopkCandCap) {
       for (int i = tid; i < n_cand; i += kT) {
         const uint2 v = cand[i];
@@ -306,19 +339,26 @@ __global__ __launch_bounds__(kT) void topk_collect_kernel(IndexArgs a, TopkWs ws
         L.cid[i] = (int)v.y;
       }
       __syncthreads();
-      select_candidates(L.ckey, L.cid, n_cand, k - above, bitmap, summary, L.hist, L.misc);
+      select_candidates(L.ckey, L.cid, n_cand, k - above, lbit, lsum, L.hist, L.misc);
     } else {
-      topk_resolve_from_row(sc, nv, b1, k - above, bitmap, summary, L.cid, L.hist, L.misc);
+      topk_resolve_from_row(sc, nv, b1, k - above, lbit, lsum, L.cid, L.hist, L.misc);
     }
-    __threadfence();
     __syncthreads();
-    emit_bitmap(bitmap, summary, (nv + 31) >> 5, out, k, &a.topk_cnt[row], L.misc);
+    // clear the global bitmap words the collect pass may have set
+    for (int i = tid; i < nsum; i += kT) {
+      uint32_t sw = lsum[i];
+      if (sw) summary[i] = 0u;
+      while (sw) {
+        const int j = __ffs(sw) - 1;
+        sw &= sw - 1;
+        bitmap[32 * i + j] = 0u;
+      }
+    }
+    emit_bitmap(lbit, lsum, nwords, out, k, &a.topk_cnt[row], L.misc);
   }
+  __syncthreads();
   for (int i = tid; i < kTopkBins; i += kT) hist[i] = 0;
-  if (tid == 0) {
-    ctr[0] = 0;
-    ctr[1] = 0;
-  }
+  if (tid == 0) ctr[0] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -327,12 +367,12 @@ __global__ __launch_bounds__(kT) void topk_collect_kernel(IndexArgs a, TopkWs ws
 __global__ __launch_bounds__(kT) void topk_rowsel_kernel(IndexArgs a, TopkWs ws) {
   extern __shared__ unsigned char dyn[];
   Lds& L = *reinterpret_cast<Lds*>(dyn);
+  uint32_t* lbit = reinterpret_cast<uint32_t*>(dyn + sizeof(Lds));  // [bitmap_words]
+  uint32_t* lsum = lbit + ws.bitmap_words;                           // [summary_words]
   const int row = blockIdx.x, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x;
   const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
   const int nv = (int)visible(a, b, t);
   const int k = a.k;
-  uint32_t* bitmap = ws.bitmap + (size_t)row * ws.bitmap_words;
-  uint32_t* summary = ws.summary + (size_t)row * ws.summary_words;
   const float* sc = a.scores + (size_t)row * a.E_cap;
   int32_t* out = a.topk_idx + (size_t)row * k;
   if (nv <= k) {
@@ -340,7 +380,10 @@ __global__ __launch_bounds__(kT) void topk_rowsel_kernel(IndexArgs a, TopkWs ws)
     if (tid == 0) a.topk_cnt[row] = nv;
     return;
   }
+  const int nwords = (nv + 31) >> 5, nsum = (nwords + 31) >> 5;
   for (int i = tid; i < kTopkBins; i += kT) L.hist[i] = 0;
+  for (int i = tid; i < nwords; i += kT) lbit[i] = 0u;
+  for (int i = tid; i < nsum; i += kT) lsum[i] = 0u;
   __syncthreads();
   for (int s = tid; s < nv; s += kT) atomicAdd(&L.hist[bin_of(f32_key(sc[s]))], 1);
   __syncthreads();
@@ -349,7 +392,7 @@ __global__ __launch_bounds__(kT) void topk_rowsel_kernel(IndexArgs a, TopkWs ws)
   int nc = 0;
   for (int s = tid; s < nv; s += kT) {
     const int bin = (int)bin_of(f32_key(sc[s]));
-    if (bin > b1) mark(bitmap, summary, s);
+    if (bin > b1) mark(lbit, lsum, s);
     nc += bin == b1;
   }
   int n_cand;
@@ -366,13 +409,12 @@ __global__ __launch_bounds__(kT) void topk_rowsel_kernel(IndexArgs a, TopkWs ws)
       }
     }
     __syncthreads();
-    select_candidates(L.ckey, L.cid, n_cand, k - above, bitmap, summary, L.hist, L.misc);
+    select_candidates(L.ckey, L.cid, n_cand, k - above, lbit, lsum, L.hist, L.misc);
   } else {
-    topk_resolve_from_row(sc, nv, b1, k - above, bitmap, summary, L.cid, L.hist, L.misc);
+    topk_resolve_from_row(sc, nv, b1, k - above, lbit, lsum, L.cid, L.hist, L.misc);
   }
-  __threadfence();
   __syncthreads();
-  emit_bitmap(bitmap, summary, (nv + 31) >> 5, out, k, &a.topk_cnt[row], L.misc);
+  emit_bitmap(lbit, lsum, nwords, out, k, &a.topk_cnt[row], L.misc);
 }
 
 // Exact resolution when the threshold bin holds more than kTopkCandCap keys:
@@ -415,6 +457,11 @@ __device__ void topk_resolve_from_row(const float* sc, int nv, int b1, int want,
   __syncthreads();
 }
 
+size_t topk_split_lds_bytes(int E_cap) {
+  const size_t words = ((size_t)E_cap + 31) / 32;
+  return sizeof(Lds) + (words + (words + 31) / 32) * 4;
+}
+
 size_t topk_ws_bytes(int rows, int E_cap, bool with_cand) {
   const size_t words = ((size_t)E_cap + 31) / 32;
   const size_t swords = (words + 31) / 32;
@@ -445,27 +492,32 @@ static size_t topk_lds_bytes() { return sizeof(Lds); }
 
 hipError_t launch_topk_collect(const IndexArgs& a, const TopkWs& ws, int slices, int slice_len,
                                hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_collect_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)topk_lds_bytes());
+  CSA_LAUNCH("topk_collect", topk_collect_kernel, dim3(slices, a.B * a.Tq), dim3(kT), 0, s, a, ws,
+             slice_len);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = topk_lds_bytes() + (size_t)(ws.bitmap_words + ws.summary_words) * 4;
+  static int attr2 = 0;
+  if (attr2 < (int)lds) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_resolve_kernel),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr2 = (int)lds;
   }
-  CSA_LAUNCH("topk_collect", topk_collect_kernel, dim3(slices, a.B * a.Tq), dim3(kT), topk_lds_bytes(), s,
-             a, ws, slice_len);
+  CSA_LAUNCH("topk_resolve", topk_resolve_kernel, dim3(a.B * a.Tq), dim3(kT), lds, s, a, ws);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_rows(const IndexArgs& a, const TopkWs& ws, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
+  const size_t lds = topk_split_lds_bytes(a.E_cap);
+  static int attr_set = 0;
+  if (attr_set < (int)lds) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_rowsel_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)topk_lds_bytes());
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_set = (int)lds;
   }
-  CSA_LAUNCH("topk_rows", topk_rowsel_kernel, dim3(a.B * a.Tq), dim3(kT), topk_lds_bytes(), s, a, ws);
+  CSA_LAUNCH("topk_rows", topk_rowsel_kernel, dim3(a.B * a.Tq), dim3(kT), lds, s, a, ws);
   return hipGetLastError();
 }
 
