@@ -9,7 +9,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All tensor pointers are DEVICE pointers, row-major and contiguous, with
- *   the shapes given per argument.  The caller owns every buffer (inputs,
+ *   the shapes given per argument, and 16-byte aligned (kernels load rows in
+ *   16-byte pieces); a misaligned pointer is CSA_ERR_ARG.  The caller owns every buffer (inputs,
  *   outputs, caches, state, workspace); the library never allocates, frees or
  *   keeps a pointer after the call returns.
  * - Work is enqueued asynchronously on `stream` (a hipStream_t passed as

@@ -46,7 +46,14 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
     if (!(cond)) return fail(status, __VA_ARGS__);      \
   } while (0)
 
-#define REQ_PTR(p) REQUIRE((p) != nullptr, CSA_ERR_ARG, "%s must not be NULL", #p)
+#define REQ_PTR(p)                                                                  \
+  do {                                                                              \
+    REQUIRE((p) != nullptr, CSA_ERR_ARG, "%s must not be NULL", #p);                \
+    REQUIRE(((uintptr_t)(p) & 15) == 0, CSA_ERR_ARG, "%s must be 16-byte aligned", #p); \
+  } while (0)
+// optional pointers: NULL or 16-byte aligned
+#define REQ_ALIGNED(p) \
+  REQUIRE(((uintptr_t)(p) & 15) == 0, CSA_ERR_ARG, "%s must be 16-byte aligned", #p)
 
 csa_status check_main_dims(int H, int c) {
   REQUIRE(H >= 1, CSA_ERR_ARG, "H must be >= 1 (got %d)", H);
@@ -250,6 +257,8 @@ static csa_status check_state(const csa_layer_desc* d, const csa_layer_state* s)
   REQ_PTR(s);
   REQUIRE(s->B >= 1 && s->E_cap >= 1, CSA_ERR_ARG, "state B and E_cap must be >= 1");
   REQ_PTR(s->kv_cache); REQ_PTR(s->n_entries); REQ_PTR(s->win_ring); REQ_PTR(s->tail);
+  REQ_ALIGNED(s->bias_a); REQ_ALIGNED(s->bias_b); REQ_ALIGNED(s->ibias_a); REQ_ALIGNED(s->ibias_b);
+  REQ_ALIGNED(s->sink); REQ_ALIGNED(s->idx_scale);
   if (d->kind == CSA_LAYER_CSA) {
     REQ_PTR(s->idx_cache); REQ_PTR(s->idx_tail);
     REQUIRE(s->E_cap <= kMaxIndexEntries, CSA_ERR_UNSUPPORTED, "E_cap <= %d supported for CSA layers",
@@ -290,9 +299,11 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
   REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
   hipStream_t hs = (hipStream_t)stream;
   char* w = (char*)ws;
+  int32_t* fold_counters = (int32_t*)w;
   w += align_up((size_t)B * sizeof(int32_t));
 
   csa::FoldArgs f{};
+  f.counters = fold_counters;
   f.dtype = d->kv_dtype; f.idx_dtype = is_csa ? d->idx_dtype : -1;
   f.B = B; f.c = d->c; f.d_I = d->d_I; f.m = d->m; f.R = tail_depth(d); f.n_win = d->n_win;
   f.vis = d->vis; f.overlap = d->overlap;

@@ -159,12 +159,13 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
 }
 
 bool attend_mfma_supported(const AttendArgs& a);
+bool attend_mfma_shape_ok(int H, int c);
 size_t attend_mfma_ws_bytes(int BT, int H, int rows_max);
 hipError_t launch_attend_mfma(const AttendArgs& a, int rows_max, hipStream_t s);
 
 size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max) {
   size_t n = 256;
-  if (c == 512 && H % 32 == 0) n += attend_mfma_ws_bytes(B * Tq, H, rows_max);
+  if (attend_mfma_shape_ok(H, c)) n += attend_mfma_ws_bytes(B * Tq, H, rows_max);
   return n;
 }
 

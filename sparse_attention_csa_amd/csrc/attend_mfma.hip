@@ -8,28 +8,30 @@
 // local_kv)).  Every row is both key and value.
 //
 // Work split.  A workgroup (4 wavefronts, one per SIMD, the whole register
-// file) owns one query, 32 heads and a contiguous range of its rows
-// ("split"); several splits of one query are merged by attend_merge_kernel
-// with the online-softmax rule.  Row tiles of 64 rows are fetched into LDS by
+// file) owns one query, 64 heads (16 per wavefront) and a contiguous range of
+// its rows ("split"); the splits of one query are merged by
+// attend_merge_kernel with the online-softmax rule.  Every wavefront consumes
+// every row of a tile, so a row crosses HBM / L2 into LDS once per split, not
+// once per head group.  Row tiles of 64 rows (64 KB) are fetched into LDS by
 // direct global-to-LDS DMA (one 1 KB row per wave instruction), double
-// buffered so that tile i+1 is in flight while tile i is computed; the LDS
-// row stride is 520 elements so 16-byte reads of 16 different rows hit
-// distinct banks.  Block order is XCD-aware: the head groups of one split run
-// on the same XCD and share its L2.
+// buffered: tile i+1 is in flight while tile i is computed.
+//
+// LDS layout.  Rows are unpadded (1 KB); the 16-byte chunk g of tile row r is
+// stored at chunk position g ^ swz(r % 16).  The DMA applies the permutation
+// by choosing which global chunk each lane fetches.  swz makes both LDS read
+// patterns below free of bank conflicts (checked for 32 and 64 banks).
 //
 // Tied K = V on MFMA.  The score product is computed transposed,
 //   S^T[rows x heads] = K[rows x d] . Q^T[d x heads]   (v_mfma 16x16x32 bf16),
-// with Q^T held in registers and K read row-major from LDS; wave w scores
-// rows 16w..16w+15 of the tile.  The accumulator layout of S^T (lane = head,
-// 4 consecutive rows per lane group) is, after exp2 and a bf16 cast, exactly
-// the B operand of
-//   O^T[d x heads] += V^T[d x rows] . P^T[rows x heads],
-// once the 32-row reduction slots are permuted consistently (slot 8g+t is row
-// 4g+t of one 16-row half for t < 4 and of the other half for t >= 4).  V^T is
-// fetched from the same LDS tile with the gfx950 transpose read
-// (ds_read_b64_tr_b16), whose per-lane addresses implement that permutation.
-// Wave w accumulates O^T for d = 128w..128w+127 and all 32 heads, so only P^T
-// (4 KB) and per-head maxima cross wavefronts.  Softmax runs in base 2.
+// with Q^T held in registers and K read row-major from LDS.  The accumulator
+// layout of S^T (lane = head, 4 consecutive rows per lane group) is, after
+// exp2 and a bf16 cast, the B operand of
+//   O^T[d x heads] += V^T[d x rows] . P^T[rows x heads]  (16x16x32 bf16)
+// once the 32 reduction slots of a row pair (two 16-row blocks) are permuted
+// consistently: slot 8g+i is row 4g+i of the first block for i < 4 and of
+// the second for i >= 4.  V^T comes from the same LDS tile through the gfx950
+// transpose read (ds_read_b64_tr_b16), whose per-lane addresses implement
+// that permutation.  Softmax runs in base 2.
 
 #include "common.h"
 #include "kernels.h"
@@ -45,27 +47,25 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int kC = 512;        // entry / head dim
-constexpr int kHT = 1;         // MFMA head tiles per workgroup
-constexpr int kHW = 16 * kHT;  // heads per workgroup
+constexpr int kHW = 64;        // heads per workgroup (16 per wavefront)
 constexpr int kTN = 64;        // rows per LDS tile
-constexpr int kLD = kC + 8;    // padded LDS row stride (elements)
+constexpr int kRowB = kC * 2;  // bytes per row
 constexpr int kMaxSparseRows = 2304;  // k + n_win <= 2048 + 256
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 8.f;  // log2 headroom before the running max is moved
 
-// s_waitcnt with vmcnt = 16, lgkmcnt / expcnt not waited (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-constexpr int kWaitVm16 = 0x4F70;
+// s_waitcnt vmcnt(0), lgkmcnt / expcnt not waited (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
 constexpr int kWaitVm0 = 0x0F70;
 
 CSA_DEV f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-CSA_DEV bf16x8_t ld8(const uint16_t* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
+CSA_DEV bf16x8_t lds8(const char* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
 
-CSA_DEV i16x4_t ld_tr(const uint16_t* p) {
+CSA_DEV i16x4_t ld_tr(const char* p) {
   typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
@@ -75,10 +75,17 @@ CSA_DEV bf16x8_t cat8(i16x4_t a, i16x4_t b) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// one lane's 16 bytes of a 1 KB row, DMA'd to LDS at lds_row + 16 * lane
-CSA_DEV void dma_row(const uint16_t* src_row, uint16_t* lds_row, int lane) {
+// chunk permutation of a tile row (r % 16): a bijection on 0..15 with
+//   bits 0..3 = r2, r0, r1, r2 ^ r3
+CSA_DEV int swz(int r) {
+  return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) | ((((r >> 2) ^ (r >> 3)) & 1) << 3);
+}
+
+// one lane's 16 bytes of a 1 KB row: global chunk (lane ^ sw) lands at LDS
+// chunk lane of the row
+CSA_DEV void dma_row(const uint16_t* src_row, char* lds_row, int lane, int sw) {
   __builtin_amdgcn_global_load_lds(
-      (const void __attribute__((address_space(1)))*)(src_row + 8 * lane),
+      (const void __attribute__((address_space(1)))*)(src_row + 8 * (lane ^ sw)),
       (void __attribute__((address_space(3)))*)(lds_row), 16, 0, 0);
 }
 
@@ -97,12 +104,9 @@ CSA_DEV int64_t rows_compressed(const AttendArgs& a, int b, int qrow, int64_t t)
 // split) are blocks L, L + 8, ... so they share that XCD's L2.
 __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n_split,
                                                              int rows_per_split) {
-  __shared__ uint16_t tile0[kTN * kLD];
-  __shared__ uint16_t tile1[kTN * kLD];
-  __shared__ float wmax[4][kHW];
-  __shared__ float wsum[4][kHW];
+  __shared__ __attribute__((aligned(1024))) char tiles[2][kTN * kRowB];
   __shared__ int rsrc[kMaxSparseRows];  // sparse: cache entry per row of the split (-1: none)
-  __shared__ unsigned char rvalid[2][kTN];
+  __shared__ uint32_t rvalid[2][kTN / 4];  // byte r % 4 of word r / 4: row r is a real row
 
   const int n_hg = a.H / kHW;
   const int L = blockIdx.x;
@@ -115,7 +119,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   const int b = qrow / a.Tq;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int H = a.H;
-  const int h0 = hg * kHW;
+  const int h0 = hg * kHW + 16 * w;  // this wavefront's first head
   const int64_t t = a.q_pos ? a.q_pos[qrow] : a.q_pos0 + qrow % a.Tq;
   const int64_t n_c = rows_compressed(a, b, qrow, t);
   const int64_t n_w = (t + 1) < a.n_win ? (t + 1) : a.n_win;
@@ -149,16 +153,6 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
       rsrc[j - r_begin] = e;
     }
   }
-
-  // Q^T operands for the 32 heads: lane (head li, d group lg)
-  bf16x8_t qf[kHT][16];
-  {
-    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)qrow * H + h0) * kC;
-#pragma unroll
-    for (int ht = 0; ht < kHT; ++ht)
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) qf[ht][ks] = ld8(q + (size_t)(16 * ht + li) * kC + 32 * ks + 8 * lg);
-  }
   __syncthreads();  // rsrc ready
 
   auto row_src = [&](int j, bool* ok) -> const uint16_t* {
@@ -179,298 +173,254 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     *ok = true;
     return win + (size_t)wr * kC;
   };
-  // wave w fetches (and later consumes) rows 16w .. 16w+15 of a tile
-  auto issue_tile = [&](int r0, uint16_t* __restrict__ tile, int buf) {
+  // wave w fetches rows 16w .. 16w+15 of a tile; every wave reads all rows
+  auto issue_tile = [&](int r0, int buf) {
+    uint32_t vw = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 16 * w + i;
       bool ok;
       const uint16_t* src = row_src(r0 + r, &ok);
-      dma_row(src, tile + r * kLD, l);
-      if (l == 0) rvalid[buf][r] = ok;
-    }
-  };
-
-  // this wave's running softmax state and O^T[512 d x 32 heads] over its rows
-  f32x4_t acc[32][kHT];
-#pragma unroll
-  for (int dt = 0; dt < 32; ++dt)
-#pragma unroll
-    for (int ht = 0; ht < kHT; ++ht) acc[dt][ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run[kHT], l_run[kHT];
-#pragma unroll
-  for (int ht = 0; ht < kHT; ++ht) {
-    m_run[ht] = -INFINITY;
-    l_run[ht] = 0.f;
-  }
-
-  auto compute_tile = [&](const uint16_t* __restrict__ tile, int buf) {
-    const uint16_t* rows = tile + 16 * w * kLD;  // this wave's 16 rows
-    // S^T[16 rows x 32 heads] = K . Q^T
-    f32x4_t s[kHT];
-#pragma unroll
-    for (int ht = 0; ht < kHT; ++ht) s[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const bf16x8_t kf = ld8(&rows[li * kLD + 32 * ks + 8 * lg]);
-#pragma unroll
-      for (int ht = 0; ht < kHT; ++ht) s[ht] = mfma(kf, qf[ht][ks], s[ht]);
-    }
-    // online softmax per head over this wave's rows; lane holds rows 4lg..4lg+3.
-    // The reference max m_run only moves when a head's tile max exceeds it by
-    // more than kSlack (log2 units), so unnormalised weights stay <= 2^kSlack
-    // and the accumulator rescale is a rare, wave-uniform branch.
-    bf16x4_t pb[kHT];
-    float x[kHT][4], tmax[kHT];
-#pragma unroll
-    for (int ht = 0; ht < kHT; ++ht) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[ht][r] = rvalid[buf][16 * w + 4 * lg + r] ? s[ht][r] * sc2 : -INFINITY;
-        mx = fmaxf(mx, x[ht][r]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      tmax[ht] = mx;
-    }
-    bool grow = false;
-#pragma unroll
-    for (int ht = 0; ht < kHT; ++ht) grow = grow || (tmax[ht] > m_run[ht] + kSlack);
-    if (__builtin_amdgcn_ballot_w64(grow) != 0ull) {
-#pragma unroll
-      for (int ht = 0; ht < kHT; ++ht) {
-        const float m_new = fmaxf(m_run[ht], tmax[ht]);
-        const float alpha = (m_run[ht] == -INFINITY) ? 0.f : exp2f(m_run[ht] - m_new);
-        l_run[ht] *= alpha;
-        m_run[ht] = m_new;
-#pragma unroll
-        for (int dt = 0; dt < 32; ++dt) acc[dt][ht] *= alpha;
+      dma_row(src, tiles[buf] + r * kRowB, l, swz(i));
+      vw |= (uint32_t)ok << (8 * (i & 3));
+      if ((i & 3) == 3) {
+        if (l == 0) rvalid[buf][4 * w + (i >> 2)] = vw;
+        vw = 0;
       }
     }
+  };
+
+  // DMA of the first tile goes out before the Q loads
+  if (r_begin < r_end) issue_tile(r_begin, 0);
+
+  // Q^T operands for this wavefront's 16 heads: lane (head li, d group lg)
+  bf16x8_t qf[16];
+  {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)qrow * H + h0 + li) * kC + 8 * lg;
 #pragma unroll
-    for (int ht = 0; ht < kHT; ++ht) {
-      float p[4], ps = 0.f;
+    for (int ks = 0; ks < 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(q + 32 * ks);
+  }
+
+  // running softmax state (per head, identical in the 4 lane groups; the sum
+  // is kept per lane over its own rows) and O^T[512 d x 16 heads]
+  f32x4_t acc[32];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = (x[ht][r] == -INFINITY) ? 0.f : exp2f(x[ht][r] - m_run[ht]);
-        ps += p[r];
+  for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_lane = 0.f;
+
+  // per-lane LDS byte offsets: score reads (row li of a 16-row block, chunk
+  // 4ks + lg) and transpose reads (row 4lg + li/4, d 16dt + 4(li%4))
+  const int s_off = li * kRowB;
+  const int s_x = 16 * (lg ^ swz(li));
+  const int tr_row = 4 * lg + (li >> 2);
+  const int t_off = tr_row * kRowB + 8 * (li & 1);
+  const int t_x = 16 * (((li >> 1) & 1) ^ swz(tr_row));
+
+  auto compute_tile = [&](int buf) {
+    const char* T = tiles[buf];
+    // S^T[64 rows x 16 heads] = K . Q^T as four 16-row blocks
+    f32x4_t s[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      s[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const char* rp = T + rb * 16 * kRowB + s_off;
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) s[rb] = mfma(lds8(rp + ((64 * ks) ^ s_x)), qf[ks], s[rb]);
+    }
+    // online softmax; lane holds rows 16rb + 4lg + i of head li.  The
+    // reference max only moves when the tile max exceeds it by more than
+    // kSlack (log2 units), so unnormalised weights stay <= 2^kSlack and the
+    // accumulator rescale is a rare, wave-uniform branch.
+    float x[4][4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      const uint32_t fl = rvalid[buf][4 * rb + lg];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[rb][i] = ((fl >> (8 * i)) & 1u) ? s[rb][i] * sc2 : -INFINITY;
+        mx = fmaxf(mx, x[rb][i]);
       }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
-      l_run[ht] += ps;
-      pb[ht] = bf16x4_t{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
     }
-    // O^T[d x heads] += V^T[d x 16 rows] . P^T[16 rows x heads] (16x16x16):
-    // the P^T operand is this lane's own S^T values; V^T comes from one
-    // transpose read (lane j of group g addresses row 4g + j/4, d 4(j%4)).
-    const uint16_t* vb = &rows[(4 * lg + (li >> 2)) * kLD + 4 * (li & 3)];
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0ull) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+      l_lane *= alpha;
+      m_run = m_new;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const bf16x4_t vf = __builtin_bit_cast(bf16x4_t, ld_tr(vb + 16 * dt));
-#pragma unroll
-      for (int ht = 0; ht < kHT; ++ht)
-        acc[dt][ht] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pb[ht], acc[dt][ht], 0, 0, 0);
+      for (int dt = 0; dt < 32; ++dt) acc[dt] *= alpha;
     }
-  };
-
-  // double-buffered loop: tile i computes while tile i+1 is in flight.  Each
-  // wave only reads the rows it fetched itself, so waiting for its own DMAs
-  // (vmcnt <= 16 leaves the next tile's 16 in flight) suffices before
-  // computing; one barrier per tile keeps a buffer from being refilled while
-  // another wave could still... (waves never touch each other's rows, the
-  // barrier only bounds how far waves drift apart).
-  int r0 = r_begin;
-  if (r0 < r_end) issue_tile(r0, tile0, 0);
-  while (r0 < r_end) {
-    const int r1 = r0 + kTN;
-    if (r1 < r_end) {
-      issue_tile(r1, tile1, 1);
-      __builtin_amdgcn_s_waitcnt(kWaitVm16);
-    } else {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    bf16x4_t pb[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = (x[rb][i] == -INFINITY) ? 0.f : exp2f(x[rb][i] - m_run);
+        l_lane += p[i];
+      }
+      pb[rb] = bf16x4_t{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
     }
-    lds_barrier();
-    compute_tile(tile0, 0);
-    r0 = r1;
-    if (r0 >= r_end) break;
-    const int r2 = r0 + kTN;
-    if (r2 < r_end) {
-      issue_tile(r2, tile0, 0);
-      __builtin_amdgcn_s_waitcnt(kWaitVm16);
-    } else {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    }
-    lds_barrier();
-    compute_tile(tile1, 1);
-    r0 = r2;
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
-
-  // merge the four wavefronts: common max, rescale, tree-sum O through LDS
-  if (lg == 0) {
+    // O^T[d x heads] += V^T[d x 32 rows] . P^T[32 rows x heads] per row pair
 #pragma unroll
-    for (int ht = 0; ht < kHT; ++ht) wmax[w][16 * ht + li] = m_run[ht];
-  }
-  __syncthreads();
-  float Lh[kHT], Mh[kHT];
-#pragma unroll
-  for (int ht = 0; ht < kHT; ++ht) {
-    const int c = 16 * ht + li;
-    const float M = fmaxf(fmaxf(wmax[0][c], wmax[1][c]), fmaxf(wmax[2][c], wmax[3][c]));
-    const float f = (m_run[ht] == -INFINITY) ? 0.f : exp2f(m_run[ht] - M);
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) acc[dt][ht] *= f;
-    Mh[ht] = M;
-    Lh[ht] = l_run[ht] * f;
-  }
-  if (lg == 0) {
-#pragma unroll
-    for (int ht = 0; ht < kHT; ++ht) wsum[w][16 * ht + li] = Lh[ht];
-  }
-  f32x4_t* red0 = reinterpret_cast<f32x4_t*>(tile0);  // [32][kHT][64] f32x4
-  f32x4_t* red1 = reinterpret_cast<f32x4_t*>(tile1);
-  auto put = [&](f32x4_t* R) {
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt)
-#pragma unroll
-      for (int ht = 0; ht < kHT; ++ht) R[(dt * kHT + ht) * 64 + l] = acc[dt][ht];
-  };
-  auto add = [&](const f32x4_t* R) {
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt)
-#pragma unroll
-      for (int ht = 0; ht < kHT; ++ht) acc[dt][ht] += R[(dt * kHT + ht) * 64 + l];
-  };
-  if (w == 1) put(red0);
-  if (w == 3) put(red1);
-  __syncthreads();
-  if (w == 0) add(red0);
-  if (w == 2) add(red1);
-  __syncthreads();
-  if (w == 2) put(red0);
-  __syncthreads();
-  if (w != 0) return;
-  add(red0);
-#pragma unroll
-  for (int ht = 0; ht < kHT; ++ht)
-    Lh[ht] = wsum[0][16 * ht + li] + wsum[1][16 * ht + li] + wsum[2][16 * ht + li] + wsum[3][16 * ht + li];
-
-  // wave 0 writes: lane (head li, d rows 4lg..4lg+3 of each 16-wide d tile)
-  if (n_split == 1) {
-#pragma unroll
-    for (int ht = 0; ht < kHT; ++ht) {
-      const int h = h0 + 16 * ht + li;
-      const float z2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
-      const float M = fmaxf(Mh[ht], z2);
-      const float em = exp2f(Mh[ht] - M);
-      const float den = Lh[ht] * em + (z2 == -INFINITY ? 0.f : exp2f(z2 - M));
-      const float f = em / den;
-      if (a.lse && lg == 0) a.lse[(size_t)qrow * H + h] = (M + log2f(den)) * kLn2;
-      uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * H + h) * kC + 4 * lg;
+    for (int pr = 0; pr < 2; ++pr) {
+      const bf16x8_t pB = __builtin_shufflevector(pb[2 * pr], pb[2 * pr + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+      const char* vp = T + pr * 32 * kRowB + t_off;
 #pragma unroll
       for (int dt = 0; dt < 32; ++dt) {
-        ushort4 v;
-        v.x = f32_to_bf16(acc[dt][ht][0] * f);
-        v.y = f32_to_bf16(acc[dt][ht][1] * f);
-        v.z = f32_to_bf16(acc[dt][ht][2] * f);
-        v.w = f32_to_bf16(acc[dt][ht][3] * f);
-        *reinterpret_cast<ushort4*>(o + 16 * dt) = v;
+        const int o = (32 * dt) ^ t_x;
+        const bf16x8_t vA = cat8(ld_tr(vp + o), ld_tr(vp + 16 * kRowB + o));
+        acc[dt] = mfma(vA, pB, acc[dt]);
       }
+    }
+  };
+
+  // double-buffered loop, one barrier per tile: after the barrier every
+  // wave's DMAs of tile i have landed and every wave has finished tile i-1,
+  // so tile i+1 may be fetched into that buffer while tile i is computed.
+  int buf = 0;
+  for (int r0 = r_begin; r0 < r_end; r0 += kTN) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    lds_barrier();
+    if (r0 + kTN < r_end) issue_tile(r0 + kTN, buf ^ 1);
+    compute_tile(buf);
+    buf ^= 1;
+  }
+
+  // per-head sum over the four lane groups
+  float Lh = l_lane;
+  Lh += __shfl_xor(Lh, 16, 64);
+  Lh += __shfl_xor(Lh, 32, 64);
+  const int h = h0 + li;
+
+  // lane (head li) holds d = 16dt + 4lg + i
+  if (n_split == 1) {
+    const float z2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+    const float M = fmaxf(m_run, z2);
+    const float em = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
+    const float den = Lh * em + (z2 == -INFINITY ? 0.f : exp2f(z2 - M));
+    const float f = em / den;
+    if (a.lse && lg == 0) a.lse[(size_t)qrow * H + h] = (M + log2f(den)) * kLn2;
+    uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * H + h) * kC + 4 * lg;
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) {
+      ushort4 v;
+      v.x = f32_to_bf16(acc[dt][0] * f);
+      v.y = f32_to_bf16(acc[dt][1] * f);
+      v.z = f32_to_bf16(acc[dt][2] * f);
+      v.w = f32_to_bf16(acc[dt][3] * f);
+      *reinterpret_cast<ushort4*>(o + 16 * dt) = v;
     }
     return;
   }
   // partial: (m, L) and O / L in bf16
   float* pml = reinterpret_cast<float*>(a.ws);
   uint16_t* po = reinterpret_cast<uint16_t*>(pml + (size_t)a.B * a.Tq * n_split * H * 2);
+  const size_t slot = ((size_t)qrow * n_split + split) * H + h;
+  if (lg == 0) {
+    pml[2 * slot] = m_run;
+    pml[2 * slot + 1] = Lh;
+  }
+  const float f = Lh > 0.f ? 1.f / Lh : 0.f;
+  uint16_t* o = po + slot * kC + 4 * lg;
 #pragma unroll
-  for (int ht = 0; ht < kHT; ++ht) {
-    const int h = h0 + 16 * ht + li;
-    const size_t slot = ((size_t)qrow * n_split + split) * H + h;
-    if (lg == 0) {
-      pml[2 * slot] = Mh[ht];
-      pml[2 * slot + 1] = Lh[ht];
-    }
-    const float f = Lh[ht] > 0.f ? 1.f / Lh[ht] : 0.f;
-    uint16_t* o = po + slot * kC + 4 * lg;
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      ushort4 v;
-      v.x = f32_to_bf16(acc[dt][ht][0] * f);
-      v.y = f32_to_bf16(acc[dt][ht][1] * f);
-      v.z = f32_to_bf16(acc[dt][ht][2] * f);
-      v.w = f32_to_bf16(acc[dt][ht][3] * f);
-      *reinterpret_cast<ushort4*>(o + 16 * dt) = v;
-    }
+  for (int dt = 0; dt < 32; ++dt) {
+    ushort4 v;
+    v.x = f32_to_bf16(acc[dt][0] * f);
+    v.y = f32_to_bf16(acc[dt][1] * f);
+    v.z = f32_to_bf16(acc[dt][2] * f);
+    v.w = f32_to_bf16(acc[dt][3] * f);
+    *reinterpret_cast<ushort4*>(o + 16 * dt) = v;
   }
 }
 
-// grid (B*Tq, H), 64 threads: each lane merges 8 coordinates of one head.
-// All split statistics are loaded first, then all partial rows (independent
-// loads in flight together).
+// grid (B*Tq, H), 256 threads: wavefront w merges splits w, w+4, ... of one
+// head (lane = 8 coordinates), the four wavefronts add up through LDS.
 constexpr int kMaxSplit = 64;
+constexpr int kMergeU = kMaxSplit / 4;
 
-__global__ __launch_bounds__(64) void attend_merge_kernel(AttendArgs a, int n_split) {
-  const int qrow = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
+__global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_split) {
+  __shared__ float s_o[4][64 * 8];
+  __shared__ float s_den;
+  const int qrow = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, w = tid >> 6, l = tid & 63;
   const int H = a.H;
   const float* pml = reinterpret_cast<const float*>(a.ws);
   const uint16_t* po = reinterpret_cast<const uint16_t*>(pml + (size_t)a.B * a.Tq * n_split * H * 2);
   const float z2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
-  float ms[kMaxSplit], Ls[kMaxSplit];
-  float M = z2;
-#pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s) {
-    if (s < n_split) {
-      const float2 v = *reinterpret_cast<const float2*>(pml + 2 * (((size_t)qrow * n_split + s) * H + h));
-      ms[s] = v.x;
-      Ls[s] = v.y;
-      M = fmaxf(M, v.x);
-    }
+  // lane s holds split s's statistics
+  float ms = -INFINITY, Ls = 0.f;
+  if (l < n_split) {
+    const float2 v = *reinterpret_cast<const float2*>(pml + 2 * (((size_t)qrow * n_split + l) * H + h));
+    ms = v.x;
+    Ls = v.y;
   }
-  float den = z2 == -INFINITY ? 0.f : exp2f(z2 - M);
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int s = 0; s < kMaxSplit; ++s) {
+  const float M = fmaxf(wave_max(ms), z2);
+  const float wgt = (ms == -INFINITY || Ls == 0.f) ? 0.f : exp2f(ms - M) * Ls;
+  // this wavefront's splits: all loads first
+  uint4 raw[kMergeU];
+#pragma unroll
+  for (int u = 0; u < kMergeU; ++u) {
+    const int s = w + 4 * u;
+    raw[u] = uint4{0, 0, 0, 0};
     if (s < n_split) {
       const size_t slot = ((size_t)qrow * n_split + s) * H + h;
-      const float wgt = (ms[s] == -INFINITY || Ls[s] == 0.f) ? 0.f : exp2f(ms[s] - M) * Ls[s];
-      den += wgt;
-      const uint4 raw = *reinterpret_cast<const uint4*>(po + slot * kC + 8 * l);
-      const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
+      raw[u] = *reinterpret_cast<const uint4*>(po + slot * kC + 8 * l);
+    }
+  }
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < kMergeU; ++u) {
+    const int s = w + 4 * u;  // < kMaxSplit = 64
+    const float ws = __shfl(wgt, s, 64);
+    if (s < n_split) {
+      const uint32_t v[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        o[2 * i] += wgt * bf16_to_f32((uint16_t)(u[i] & 0xffff));
-        o[2 * i + 1] += wgt * bf16_to_f32((uint16_t)(u[i] >> 16));
+        o[2 * i] += ws * bf16_to_f32((uint16_t)(v[i] & 0xffff));
+        o[2 * i + 1] += ws * bf16_to_f32((uint16_t)(v[i] >> 16));
       }
     }
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s_o[w][8 * l + i] = o[i];
+  if (w == 0) {
+    const float den = wave_sum(wgt) + (z2 == -INFINITY ? 0.f : exp2f(z2 - M));
+    if (l == 0) s_den = den;
+  }
+  __syncthreads();
+  if (w != 0) return;
+  const float den = s_den;
   const float inv = 1.f / den;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    o[i] = (s_o[0][8 * l + i] + s_o[1][8 * l + i] + s_o[2][8 * l + i] + s_o[3][8 * l + i]) * inv;
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * H + h) * kC + 8 * l;
   uint4 r;
-  r.x = (uint32_t)f32_to_bf16(o[0] * inv) | ((uint32_t)f32_to_bf16(o[1] * inv) << 16);
-  r.y = (uint32_t)f32_to_bf16(o[2] * inv) | ((uint32_t)f32_to_bf16(o[3] * inv) << 16);
-  r.z = (uint32_t)f32_to_bf16(o[4] * inv) | ((uint32_t)f32_to_bf16(o[5] * inv) << 16);
-  r.w = (uint32_t)f32_to_bf16(o[6] * inv) | ((uint32_t)f32_to_bf16(o[7] * inv) << 16);
+  r.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+  r.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+  r.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
+  r.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
   *reinterpret_cast<uint4*>(out) = r;
   if (a.lse && l == 0) a.lse[(size_t)qrow * H + h] = (M + log2f(den)) * kLn2;
 }
 
-bool attend_mfma_supported(const AttendArgs& a) {
-  return a.dtype == BF16 && a.c == kC && a.H % kHW == 0;
-}
+bool attend_mfma_shape_ok(int H, int c) { return c == kC && H % kHW == 0; }
 
-// number of row splits per (query, head group) and rows per split
+bool attend_mfma_supported(const AttendArgs& a) { return a.dtype == BF16 && attend_mfma_shape_ok(a.H, a.c); }
+
+// Row splits per (query, head group): about one workgroup per CU (256), each
+// split a multiple of 16 rows, at most kMaxSplit splits.
 void attend_mfma_plan(int BT, int H, int rows_max, int* n_split, int* rows_per_split) {
   const int cols = BT * (H / kHW);
-  const int tiles = (rows_max + kTN - 1) / kTN;
-  int want = (256 + cols - 1) / cols;
+  int want = 256 / cols;
   if (want < 1) want = 1;
   if (want > kMaxSplit) want = kMaxSplit;
-  if (want > tiles) want = tiles;
-  const int tiles_per = (tiles + want - 1) / want;
-  *rows_per_split = tiles_per * kTN;
-  *n_split = (rows_max + *rows_per_split - 1) / *rows_per_split;
+  int rps = (rows_max + want - 1) / want;
+  rps = (rps + 15) / 16 * 16;
+  *rows_per_split = rps;
+  *n_split = (rows_max + rps - 1) / rps;
 }
 
 size_t attend_mfma_ws_bytes(int BT, int H, int rows_max) {
@@ -483,6 +433,7 @@ size_t attend_mfma_ws_bytes(int BT, int H, int rows_max) {
 hipError_t launch_attend_mfma(const AttendArgs& a, int rows_max, hipStream_t s) {
   int ns, rps;
   attend_mfma_plan(a.B * a.Tq, a.H, rows_max, &ns, &rps);
+  if (!a.dense && rps > kMaxSparseRows) return hipErrorInvalidValue;
   const int n_hg = a.H / kHW;
   const long long units = (long long)ns * a.B * a.Tq;       // (query, split) pairs
   const long long blocks = (units + 7) / 8 * 8 * n_hg;      // padded to whole XCD rounds
@@ -491,7 +442,7 @@ hipError_t launch_attend_mfma(const AttendArgs& a, int rows_max, hipStream_t s) 
   if (ns > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    CSA_LAUNCH("attend_merge", attend_merge_kernel, dim3(a.B * a.Tq, a.H), dim3(64), 0, s, a, ns);
+    CSA_LAUNCH("attend_merge", attend_merge_kernel, dim3(a.B * a.Tq, a.H), dim3(256), 0, s, a, ns);
   }
   return hipGetLastError();
 }

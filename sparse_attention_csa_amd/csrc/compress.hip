@@ -158,72 +158,118 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
 // Decode step: fold the block whose entry becomes visible at this position,
 // and append the new token to the tail ring and the window ring.
 //
-// One 1024-thread workgroup per sequence: thread = (coordinate, source
-// group); every group folds an interleaved subset of the block's source
-// tokens with an online softmax per coordinate, the groups merge through LDS.
-// The workgroup reads all its sources before it overwrites the tail slot of
-// the new token, and publishes n_entries[b] itself (no other workgroup reads
-// it), so no cross-workgroup ordering is needed.
+// grid (jobs, B), 256 threads.  Job j < c/64 owns coordinates [64j, 64j+64)
+// of the main entry and of the new token's appended rows; the last job of a
+// CSA layer owns the whole indexer key (its e4m3 scale needs the row
+// maximum).  A thread loads 16 contiguous bytes (V coordinates) of each of
+// its source rows: the TR = W/V threads of a row cover the job's W
+// coordinates, the G = 256/TR thread groups take interleaved source tokens,
+// and the per-coordinate online softmaxes of the groups merge through LDS.
+//
+// The ring holds the last 2m tokens (3m with overlap) and a fold reads at
+// most the 2m tokens before t (the new token itself from the step's inputs),
+// so the new token's slot is never a source and the appends need no
+// ordering against the reads.  Every workgroup of a sequence reads
+// n_entries[b]; the last one to finish (a per-sequence counter in the
+// workspace, returned to zero) publishes the new count.
 // --------------------------------------------------------------------------
-constexpr int kFoldT = 1024;
+constexpr int kFoldT = 256;
+constexpr int kFoldCW = 64;  // main-entry coordinates per workgroup
 
-// Sources of entry e for coordinate r, split over G groups: group g takes
-// source slots g, g+G, ... (branch a: tokens e*m + j; branch b: (e-1)*m + j).
-// Ring slots are computed in 32 bits from one 64-bit remainder.  All loads of
-// a group are issued before the softmax chain consumes them.
 template <typename T>
-CSA_DEV Soft fold_sources(const T* tail, const T* io, int d, int r, int grp, int G, int m, int R,
-                          int64_t t, int64_t e, bool use_b, const float* ba, const float* bb) {
-  Soft st{-INFINITY, 0.f, 0.f};
+struct Vec16 {
+  static constexpr int V = 16 / (int)sizeof(T);
+};
+
+// V consecutive elements (16 bytes) of T as floats
+CSA_DEV void unpack16(const uint4 u, const bf16*, float* o) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = __uint_as_float(w[i] << 16);
+    o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+CSA_DEV void unpack16(const uint4 u, const float*, float* o) {
+  o[0] = __uint_as_float(u.x); o[1] = __uint_as_float(u.y);
+  o[2] = __uint_as_float(u.z); o[3] = __uint_as_float(u.w);
+}
+
+// Folds coordinates [r0, r0 + W) of entry e from rows of length d; returns
+// the value of coordinate r0 + tid for tid < W.  Sources: branch a is tokens
+// e*m .. e*m+m-1 (streams 0, 1), branch b (use_b) tokens (e-1)*m .. e*m-1
+// (streams 2, 3); token p is ring slot p % R, the new token t comes from io.
+template <typename T>
+CSA_DEV float fold_job(const T* tail, const T* io, int d, int r0, int W, int m, int R, int64_t t,
+                       int64_t e, bool use_b, const float* ba, const float* bb, Soft* s_part) {
+  constexpr int V = Vec16<T>::V;
+  constexpr int U = 4;  // sources in flight per thread
+  const int tid = threadIdx.x;
+  const int TR = W / V, G = kFoldT / TR;
+  const int o = tid % TR, grp = tid / TR;
+  const int rr = r0 + o * V;
   const int nsrc = use_b ? 2 * m : m;
   const int64_t p_first = use_b ? (e - 1) * m : e * m;  // earliest source token
   const int slot_first = (int)(p_first % R);
-  const int t_off = (int)(t - p_first);                 // new token's offset (may be > 2m)
-  // source slot j: a-branch j < m is token e*m + j, b-branch j >= m is (e-1)*m + (j - m)
-  auto tok_off = [&](int j) -> int { return use_b ? (j < m ? m + j : j - m) : j; };
-  float lgv[16], vv[16];
-  for (int j0 = grp; j0 < nsrc; j0 += 16 * G) {
+  const int t_off = (int)(t - p_first);
+  Soft st[V];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+  for (int v = 0; v < V; ++v) st[v] = Soft{-INFINITY, 0.f, 0.f};
+  for (int j0 = grp; j0 < nsrc; j0 += U * G) {
+    uint4 zr[U], xr[U];
+    float bz[U][V];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
       const int j = j0 + u * G;
-      lgv[u] = -INFINITY;
-      vv[u] = 0.f;
+      zr[u] = xr[u] = uint4{0, 0, 0, 0};
+#pragma unroll
+      for (int v = 0; v < V; ++v) bz[u][v] = 0.f;
       if (j < nsrc) {
-        const int off = tok_off(j);
-        const bool a_branch = j < m;
-        const int sc = a_branch ? 0 : 2;
-        const int jj = a_branch ? j : j - m;
-        float z, v;
+        const bool a_br = j < m;
+        const int jj = a_br ? j : j - m;                 // index within the branch
+        const int off = use_b ? (a_br ? m + j : j - m) : j;  // token - p_first
+        const int sc = a_br ? 0 : 2;
+        const T *pz, *px;
         if (off == t_off) {
-          z = ld(io, (size_t)(sc + 1) * d + r);
-          v = ld(io, (size_t)sc * d + r);
+          pz = io + (size_t)(sc + 1) * d + rr;
+          px = io + (size_t)sc * d + rr;
         } else {
           int slot = slot_first + off;
           while (slot >= R) slot -= R;
-          z = ld(tail, ((size_t)(sc + 1) * R + slot) * d + r);
-          v = ld(tail, ((size_t)sc * R + slot) * d + r);
+          pz = tail + ((size_t)(sc + 1) * R + slot) * d + rr;
+          px = tail + ((size_t)sc * R + slot) * d + rr;
         }
-        const float* bias = a_branch ? ba : bb;
-        lgv[u] = z + (bias ? bias[jj * d + r] : 0.f);
-        vv[u] = v;
+        zr[u] = *reinterpret_cast<const uint4*>(pz);
+        xr[u] = *reinterpret_cast<const uint4*>(px);
+        const float* bias = a_br ? ba : bb;
+        if (bias) {
+#pragma unroll
+          for (int v = 0; v < V; v += 4) {
+            const float4 f = *reinterpret_cast<const float4*>(bias + (size_t)jj * d + rr + v);
+            bz[u][v] = f.x; bz[u][v + 1] = f.y; bz[u][v + 2] = f.z; bz[u][v + 3] = f.w;
+          }
+        }
       }
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      if (lgv[u] != -INFINITY) soft_push(st, lgv[u], vv[u]);
+    for (int u = 0; u < U; ++u) {
+      if (j0 + u * G < nsrc) {
+        float z[V], x[V];
+        unpack16(zr[u], (const T*)nullptr, z);
+        unpack16(xr[u], (const T*)nullptr, x);
+#pragma unroll
+        for (int v = 0; v < V; ++v) soft_push(st[v], z[v] + bz[u][v], x[v]);
+      }
+    }
   }
-  return st;
-}
-
-// merge the G partial states of each coordinate (LDS), result in group 0
-CSA_DEV float fold_merge(Soft st, Soft* s_part, int d, int r, int grp, int G) {
-  const int tid = threadIdx.x;
-  s_part[tid] = st;
+  // merge the G groups of every coordinate: s_part[g][w]
+#pragma unroll
+  for (int v = 0; v < V; ++v) s_part[grp * W + o * V + v] = st[v];
   __syncthreads();
   float val = 0.f;
-  if (grp == 0 && r < d) {
+  if (tid < W) {
     Soft acc = s_part[tid];
-    for (int g2 = 1; g2 < G; ++g2) acc = soft_merge(acc, s_part[g2 * d + r]);
+    for (int g = 1; g < G; ++g) acc = soft_merge(acc, s_part[g * W + tid]);
     val = acc.acc / acc.l;
   }
   __syncthreads();
@@ -232,74 +278,74 @@ CSA_DEV float fold_merge(Soft st, Soft* s_part, int d, int r, int grp, int G) {
 
 template <typename T, typename TI>
 __global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
-  __shared__ Soft s_part[kFoldT];
+  __shared__ Soft s_part[kFoldT * Vec16<T>::V];
   __shared__ float s_red[kFoldT / 64];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int job = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int m = a.m, R = a.R, c = a.c;
   const int64_t t = a.pos[b];
   const int n_have = a.n_entries[b];
   const int64_t lim = vis_limit(t, m, a.vis);
-  const bool fold = (lim == (int64_t)n_have + 1) && (int64_t)n_have < (int64_t)a.E_cap;
+  const bool fold = (lim == (int64_t)n_have + 1) && n_have < a.E_cap;
   const int64_t e = n_have;
-  const bool has_idx = a.idx_dtype >= 0;
   const int nstr = a.overlap ? 4 : 2;
-  const T* tail = reinterpret_cast<const T*>(a.tail) + (size_t)b * nstr * R * c;
-  const T* io = reinterpret_cast<const T*>(a.streams) + (size_t)b * nstr * c;
+  const int slot = (int)(t % R);
 
-  if (fold) {
-    // main entry: coordinates r = tid % c, groups of kFoldT / c
-    const int G = kFoldT / c, r = tid % c, grp = tid / c;
-    Soft part = fold_sources(tail, io, c, r, grp, G, m, R, t, e, a.overlap && e > 0, a.bias_a, a.bias_b);
-    const float val = fold_merge(part, s_part, c, r, grp, G);
-    if (grp == 0) st(reinterpret_cast<T*>(a.kv_cache), ((size_t)b * a.E_cap + e) * c + r, val);
-    if (has_idx) {
-      const int d = a.d_I, Gi = kFoldT / d, ri = tid % d, gi = tid / d;
-      const T* itail = reinterpret_cast<const T*>(a.idx_tail) + (size_t)b * 4 * R * d;
-      const T* iio = reinterpret_cast<const T*>(a.idx_streams) + (size_t)b * 4 * d;
-      Soft si = fold_sources(itail, iio, d, ri, gi, Gi, m, R, t, e, e > 0, a.ibias_a, a.ibias_b);
-      const float iv = fold_merge(si, s_part, d, ri, gi, Gi);
+  if (job < c / kFoldCW) {
+    const int r0 = job * kFoldCW;
+    T* tail = reinterpret_cast<T*>(a.tail) + (size_t)b * nstr * R * c;
+    const T* io = reinterpret_cast<const T*>(a.streams) + (size_t)b * nstr * c;
+    if (fold) {
+      const float val = fold_job<T>(tail, io, c, r0, kFoldCW, m, R, t, e, a.overlap && e > 0, a.bias_a,
+                                    a.bias_b, s_part);
+      if (tid < kFoldCW) st(reinterpret_cast<T*>(a.kv_cache), ((size_t)b * a.E_cap + e) * c + r0 + tid, val);
+    }
+    for (int i = tid; i < nstr * kFoldCW; i += kFoldT) {
+      const int sc = i / kFoldCW, r = r0 + i % kFoldCW;
+      tail[((size_t)sc * R + slot) * c + r] = io[(size_t)sc * c + r];
+    }
+    if (tid < kFoldCW) {
+      T* ring = reinterpret_cast<T*>(a.win_ring) + (size_t)b * a.n_win * c;
+      ring[(size_t)(t % a.n_win) * c + r0 + tid] = reinterpret_cast<const T*>(a.x_new)[(size_t)b * c + r0 + tid];
+    }
+  } else {
+    const int d = a.d_I;
+    T* itail = reinterpret_cast<T*>(a.idx_tail) + (size_t)b * 4 * R * d;
+    const T* iio = reinterpret_cast<const T*>(a.idx_streams) + (size_t)b * 4 * d;
+    if (fold) {
+      const float iv = fold_job<T>(itail, iio, d, 0, d, m, R, t, e, e > 0, a.ibias_a, a.ibias_b, s_part);
+      const size_t row = (size_t)b * a.E_cap + e;
       if constexpr (sizeof(TI) == 1) {
-        float am = gi == 0 ? fabsf(iv) : 0.f;
-        am = wave_max(am);
+        float am = wave_max(tid < d ? fabsf(iv) : 0.f);
         if ((tid & 63) == 0) s_red[tid >> 6] = am;
         __syncthreads();
-        am = 0.f;
-        for (int i = 0; i < kFoldT / 64; ++i) am = fmaxf(am, s_red[i]);
+        am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
         float scale = am / 448.0f;
         if (!(scale > 0.f)) scale = 1.f;
-        if (gi == 0)
-          reinterpret_cast<uint8_t*>(a.idx_cache)[((size_t)b * a.E_cap + e) * d + ri] = f32_to_e4m3(iv / scale);
-        if (tid == 0) a.idx_scale[(size_t)b * a.E_cap + e] = scale;
+        if (tid < d) reinterpret_cast<uint8_t*>(a.idx_cache)[row * d + tid] = f32_to_e4m3(iv / scale);
+        if (tid == 0) a.idx_scale[row] = scale;
       } else {
-        if (gi == 0) st(reinterpret_cast<TI*>(a.idx_cache), ((size_t)b * a.E_cap + e) * d + ri, iv);
+        if (tid < d) st(reinterpret_cast<TI*>(a.idx_cache), row * d + tid, iv);
       }
     }
-  }
-  __syncthreads();  // every source read of this sequence is done
-  // append the new token: tail slot t % R of every stream, window ring slot
-  const size_t slot = (size_t)(t % R);
-  T* tw = const_cast<T*>(tail);
-  for (int i = tid; i < nstr * c; i += kFoldT) {
-    const int sc = i / c, r = i % c;
-    tw[((size_t)sc * R + slot) * c + r] = io[(size_t)sc * c + r];
-  }
-  if (has_idx) {
-    const int d = a.d_I;
-    T* itw = reinterpret_cast<T*>(a.idx_tail) + (size_t)b * 4 * R * d;
-    const T* iio = reinterpret_cast<const T*>(a.idx_streams) + (size_t)b * 4 * d;
     for (int i = tid; i < 4 * d; i += kFoldT) {
       const int sc = i / d, r = i % d;
-      itw[((size_t)sc * R + slot) * d + r] = iio[(size_t)sc * d + r];
+      itail[((size_t)sc * R + slot) * d + r] = iio[(size_t)sc * d + r];
     }
   }
-  T* ring = reinterpret_cast<T*>(a.win_ring) + (size_t)b * a.n_win * c;
-  for (int r = tid; r < c; r += kFoldT)
-    ring[(size_t)(t % a.n_win) * c + r] = reinterpret_cast<const T*>(a.x_new)[(size_t)b * c + r];
-  if (fold && tid == 0) a.n_entries[b] = n_have + 1;
+  // the last workgroup of the sequence publishes the count; every
+  // workgroup's read of n_entries[b] completed before its increment
+  __syncthreads();
+  if (tid == 0) {
+    const int done = atomicAdd(&a.counters[b], 1);
+    if (done == (int)gridDim.x - 1) {
+      a.counters[b] = 0;
+      if (fold) a.n_entries[b] = n_have + 1;
+    }
+  }
 }
 
 hipError_t launch_fold_append(const FoldArgs& a, hipStream_t s) {
-  dim3 grid(a.B), block(kFoldT);
+  dim3 grid(a.c / kFoldCW + (a.idx_dtype >= 0 ? 1 : 0), a.B), block(kFoldT);
   if (a.dtype == F32) {
     if (a.idx_dtype == E4M3)
       CSA_LAUNCH("fold_append", (fold_append_kernel<float, uint8_t>), grid, block, 0, s, a);

@@ -51,6 +51,7 @@ struct FoldArgs {
   int B, c, d_I, m, R, n_win, vis, overlap;
   const int64_t* pos;
   int32_t* n_entries;
+  int32_t* counters;        // [B] workspace, zero between calls
   const void* streams;      // [B][S][c]
   const void* idx_streams;  // [B][4][d_I]
   const void* x_new;        // [B][c]
