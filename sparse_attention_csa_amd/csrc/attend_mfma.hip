@@ -53,7 +53,7 @@ constexpr int kRowB = kC * 2;  // bytes per row
 constexpr int kMaxSparseRows = 2304;  // k + n_win <= 2048 + 256
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kSlack = 8.f;  // log2 headroom before the running max is moved
+constexpr float kSlack = 20.f;  // log2 headroom of the weights over the reference max
 
 // s_waitcnt vmcnt(0), lgkmcnt / expcnt not waited (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
@@ -102,11 +102,13 @@ CSA_DEV int64_t rows_compressed(const AttendArgs& a, int b, int qrow, int64_t t)
 
 // 1-D grid: block L runs on XCD L % 8; the n_hg head groups of one (query,
 // split) are blocks L, L + 8, ... so they share that XCD's L2.
+template <bool kDense>
 __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n_split,
                                                              int rows_per_split) {
   __shared__ __attribute__((aligned(1024))) char tiles[2][kTN * kRowB];
   __shared__ int rsrc[kMaxSparseRows];  // sparse: cache entry per row of the split (-1: none)
   __shared__ uint32_t rvalid[2][kTN / 4];  // byte r % 4 of word r / 4: row r is a real row
+  __shared__ int s_restart;                // a wavefront asks the split to be recomputed
 
   const int n_hg = a.H / kHW;
   const int L = blockIdx.x;
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   if (own >= wcap) own -= wcap;
   const uint16_t* pad_row = win + (size_t)own * kC;
 
-  if (!a.dense) {
+  if (!kDense) {
     const int32_t* ids = a.topk_idx + (size_t)qrow * a.k;
     for (int j = r_begin + tid; j < r_end; j += 256) {
       int e = -1;
@@ -153,13 +155,14 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
       rsrc[j - r_begin] = e;
     }
   }
-  __syncthreads();  // rsrc ready
+  if (tid == 0) s_restart = 0;
+  __syncthreads();  // rsrc, s_restart ready
 
   auto row_src = [&](int j, bool* ok) -> const uint16_t* {
     *ok = false;
     if (j >= r_end) return pad_row;
     if (j < nc32) {
-      if (a.dense) {
+      if (kDense) {
         *ok = true;
         return kv + (size_t)j * kC;
       }
@@ -201,36 +204,54 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     for (int ks = 0; ks < 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(q + 32 * ks);
   }
 
-  // running softmax state (per head, identical in the 4 lane groups; the sum
-  // is kept per lane over its own rows) and O^T[512 d x 16 heads]
+  // running softmax state: the reference max per head (identical in the 4
+  // lane groups), the sum per lane over its own rows, O^T[512 d x 16 heads]
   f32x4_t acc[32];
 #pragma unroll
   for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_lane = 0.f;
 
-  // per-lane LDS byte offsets: score reads (row li of a 16-row block, chunk
-  // 4ks + lg) and transpose reads (row 4lg + li/4, d 16dt + 4(li%4))
-  const int s_off = li * kRowB;
+  // per-lane LDS byte offsets.  Score reads: row li of a 16-row block,
+  // chunk 4ks + lg, i.e. byte (64 ks) ^ s_x with s_x < 256, which is
+  // 256 (ks / 4) + ((64 (ks % 4)) ^ s_x): four per-lane bases, the rest is an
+  // immediate offset.  Transpose reads: row 4lg + li/4, d 16dt + 4(li%4),
+  // byte (32 dt) ^ t_x = 256 (dt / 8) + ((32 (dt % 8)) ^ t_x): eight bases.
   const int s_x = 16 * (lg ^ swz(li));
   const int tr_row = 4 * lg + (li >> 2);
-  const int t_off = tr_row * kRowB + 8 * (li & 1);
   const int t_x = 16 * (((li >> 1) & 1) ^ swz(tr_row));
+  int s_base[4], t_base[8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) s_base[u] = li * kRowB + ((64 * u) ^ s_x);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) t_base[u] = tr_row * kRowB + 8 * (li & 1) + ((32 * u) ^ t_x);
 
   auto compute_tile = [&](int buf) {
     const char* T = tiles[buf];
     // S^T[64 rows x 16 heads] = K . Q^T as four 16-row blocks
+    // (the four block chains interleave, so consecutive MFMAs are independent)
     f32x4_t s[4];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      s[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const char* rp = T + rb * 16 * kRowB + s_off;
+    for (int rb = 0; rb < 4; ++rb) s[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) s[rb] = mfma(lds8(rp + ((64 * ks) ^ s_x)), qf[ks], s[rb]);
+    for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        s[rb] = mfma(lds8(T + s_base[ks & 3] + rb * 16 * kRowB + 256 * (ks >> 2)), qf[ks], s[rb]);
+    // keep 12 fragment reads in flight ahead of the MFMAs (lgkmcnt counts 15)
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 1);
+#pragma unroll
+    for (int i = 0; i < 52; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
     }
-    // online softmax; lane holds rows 16rb + 4lg + i of head li.  The
-    // reference max only moves when the tile max exceeds it by more than
-    // kSlack (log2 units), so unnormalised weights stay <= 2^kSlack and the
-    // accumulator rescale is a rare, wave-uniform branch.
+    __builtin_amdgcn_sched_group_barrier(0x008, 12, 1);
+    // softmax weights against a fixed reference max per head; lane holds
+    // rows 16rb + 4lg + i of head li.  The reference is the first tile's max
+    // and stays put while tile maxima exceed it by at most kSlack (log2
+    // units), so weights stay <= 2^kSlack and the accumulator is never
+    // rescaled.  A larger jump raises the reference and asks for the split
+    // to be recomputed from its first row (at most once: the second pass
+    // starts from the largest max of the first).
     float x[4][4];
     float mx = -INFINITY;
 #pragma unroll
@@ -244,21 +265,16 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    if (__builtin_amdgcn_ballot_w64(mx > m_run + kSlack) != 0ull) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-      l_lane *= alpha;
-      m_run = m_new;
-#pragma unroll
-      for (int dt = 0; dt < 32; ++dt) acc[dt] *= alpha;
-    }
+    const bool jump = m_run != -INFINITY && mx > m_run + kSlack;
+    if (__builtin_amdgcn_ballot_w64(jump) != 0ull && l == 0) s_restart = 1;
+    if (m_run == -INFINITY || jump) m_run = mx;  // no weight so far, or a pass to be redone
     bf16x4_t pb[4];
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[i] = (x[rb][i] == -INFINITY) ? 0.f : exp2f(x[rb][i] - m_run);
+        p[i] = (x[rb][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x[rb][i] - m_run);
         l_lane += p[i];
       }
       pb[rb] = bf16x4_t{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
@@ -267,26 +283,45 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
       const bf16x8_t pB = __builtin_shufflevector(pb[2 * pr], pb[2 * pr + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-      const char* vp = T + pr * 32 * kRowB + t_off;
+      const char* vp = T + pr * 32 * kRowB;
 #pragma unroll
       for (int dt = 0; dt < 32; ++dt) {
-        const int o = (32 * dt) ^ t_x;
-        const bf16x8_t vA = cat8(ld_tr(vp + o), ld_tr(vp + 16 * kRowB + o));
-        acc[dt] = mfma(vA, pB, acc[dt]);
+        const char* v0 = vp + t_base[dt & 7] + 256 * (dt >> 3);
+        acc[dt] = mfma(cat8(ld_tr(v0), ld_tr(v0 + 16 * kRowB)), pB, acc[dt]);
       }
     }
+    // keep 7 MFMAs' worth of transpose reads in flight
+    __builtin_amdgcn_sched_group_barrier(0x100, 14, 2);
+#pragma unroll
+    for (int i = 0; i < 57; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 7, 2);
   };
 
   // double-buffered loop, one barrier per tile: after the barrier every
   // wave's DMAs of tile i have landed and every wave has finished tile i-1,
   // so tile i+1 may be fetched into that buffer while tile i is computed.
-  int buf = 0;
-  for (int r0 = r_begin; r0 < r_end; r0 += kTN) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  for (;;) {
+    int buf = 0;
+    for (int r0 = r_begin; r0 < r_end; r0 += kTN) {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      lds_barrier();
+      if (r0 + kTN < r_end) issue_tile(r0 + kTN, buf ^ 1);
+      compute_tile(buf);
+      buf ^= 1;
+    }
     lds_barrier();
-    if (r0 + kTN < r_end) issue_tile(r0 + kTN, buf ^ 1);
-    compute_tile(buf);
-    buf ^= 1;
+    const int again = s_restart;
+    if (!again) break;
+    // recompute the split against the raised reference maxima
+    lds_barrier();
+    if (tid == 0) s_restart = 0;
+#pragma unroll
+    for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    l_lane = 0.f;
+    issue_tile(r_begin, 0);
   }
 
   // per-head sum over the four lane groups
@@ -437,8 +472,10 @@ hipError_t launch_attend_mfma(const AttendArgs& a, int rows_max, hipStream_t s) 
   const int n_hg = a.H / kHW;
   const long long units = (long long)ns * a.B * a.Tq;       // (query, split) pairs
   const long long blocks = (units + 7) / 8 * 8 * n_hg;      // padded to whole XCD rounds
-  CSA_LAUNCH(a.dense ? "attend_dense_mfma" : "attend_sparse_mfma", attend_mfma_kernel, dim3((unsigned)blocks),
-             dim3(256), 0, s, a, ns, rps);
+  if (a.dense)
+    CSA_LAUNCH("attend_dense_mfma", attend_mfma_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+  else
+    CSA_LAUNCH("attend_sparse_mfma", attend_mfma_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
   if (ns > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
