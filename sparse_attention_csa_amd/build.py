@@ -29,6 +29,12 @@ FLAGS = [
 ]
 
 
+# per-source extra flags: the indexer scan keeps its MFMA results in VGPRs
+# (its in-lane epilogue reads every result; accumulation registers would
+# need a copy per value)
+EXTRA = {"indexer_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc():
     p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(p):
@@ -38,7 +44,7 @@ def hipcc():
 
 def _compile(src, verbose):
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

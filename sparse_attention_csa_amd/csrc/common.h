@@ -84,6 +84,15 @@ CSA_DEV float wave_max(float v) {
   return v;
 }
 
+// v + the values of lanes l^16, l^32 and l^48 (the four 16-lane rows), with
+// the gfx950 lane-swap instructions instead of LDS permutes
+CSA_DEV float lane_sum_xor16_32(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 // Workgroup barrier that orders LDS only.  __syncthreads() also waits for
 // every outstanding global access of the wave (vmcnt(0)), which would drain
 // asynchronous global-to-LDS prefetches; callers that need those complete
@@ -107,6 +116,18 @@ CSA_DEV void lds_barrier() {
   __asm__ __volatile__("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   __asm__ __volatile__("" ::: "memory");
+}
+
+// LDS atomic add without return.  Issued as inline asm so that the
+// compiler's wait insertion does not treat it as possibly overlapping
+// in-flight global-to-LDS DMAs into other LDS arrays (it would otherwise
+// wait for every outstanding DMA first).  Callers guarantee that p is not in
+// any region still being filled by DMA.  No result register, so nothing is
+// read before the add completes; later LDS reads wait for it through lgkmcnt
+// as usual (LDS operations complete in order).
+CSA_DEV void lds_add_noret(int* p, int v) {
+  const uint32_t addr = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) int*)p);
+  __asm__ __volatile__("ds_add_u32 %0, %1" ::"v"(addr), "v"(v) : "memory");
 }
 
 // visible-entry limit for a query at position t

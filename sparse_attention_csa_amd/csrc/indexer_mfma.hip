@@ -4,19 +4,28 @@
 // score"), for d_I = 128 and H_I a multiple of 16 (<= 64).
 //
 // The scan over the visible keys is the HBM stream of a CSA decode step.  A
-// wavefront scores 16 keys per step: C[heads x keys] = Q[heads x d] .
-// K^T[d x keys] with Q in registers (loaded once) and each lane loading its
-// key's 16- or 32-byte slices straight from HBM into the B operand
-// (v_mfma_f32_16x16x32_bf16 for bf16 keys, 4 k-steps; the scaled f8f6f4
-// v_mfma 16x16x128 with unit scales for e4m3 keys, one step).  The
-// accumulator holds 4 heads x 1 key per lane, so ReLU, the head weights and
-// the head sum are in-lane, then two cross-lane adds.  For e4m3 the per-head
-// query scale is folded into w and the per-key scale multiplies the sum (both
-// positive, so they commute with ReLU).  Each wave scores a contiguous run of
-// tiles in batches of four, loading the next batch before scoring the current
-// one, so eight tiles' keys are in flight per wave.  With use_hist the wave also counts the
-// top 11 bits of each score's order-preserving key into an LDS histogram that
-// is added to the row's global histogram at the end (stage 1 of the top-k).
+// wavefront owns a contiguous run of 16-key tiles and streams them in
+// batches of kU tiles: every load instruction reads 1 KB of consecutive rows
+// (full cache lines) into registers, and the next batch is in flight while
+// the current one is scored, so a wavefront keeps up to 2 kU tiles of reads
+// outstanding (registers hold far more in-flight data per CU than LDS
+// could).  A batch is transposed to the MFMA operand layout through a
+// per-wavefront LDS buffer (private to the wavefront, so only its own LDS
+// counter is waited on); the 16-byte chunks of each key are stored XOR
+// swizzled so that both the writes and the MFMA-layout reads hit distinct
+// LDS banks.
+//
+// Scoring: C[heads x keys] = Q[heads x d] . K^T[d x keys] with Q in
+// registers (v_mfma_f32_16x16x32_bf16, 4 k-steps, for bf16 keys; the scaled
+// f8f6f4 v_mfma 16x16x128 with unit scales for e4m3 keys, one step, with the
+// reduction index permuted so a lane takes bytes 16g.. and 64+16g.. of its
+// key; the query operand uses the same permutation).  The accumulator holds 4
+// heads x 1 key per lane, so ReLU, the head weights and the head sum are
+// in-lane, then two cross-lane adds.  For e4m3 the per-head query scale is
+// folded into w and the per-key scale multiplies the sum (both positive, so
+// they commute with ReLU).  With use_hist the wave also counts the top 11
+// bits of each score's order-preserving key into an LDS histogram that is
+// added to the row's global histogram at the end (stage 1 of the top-k).
 
 #include <type_traits>
 
@@ -28,62 +37,103 @@ namespace csa {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// ReLU as one integer max on the bit pattern: non-negative floats order
+// like their bits, negative ones (sign bit set) are negative integers
+CSA_DEV float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 namespace {
 
 constexpr int kD = 128;
 
+// Tile geometry.  e4m3: 16 keys x 128 B = 2 KB, read as two 1 KB pieces of
+// 8 keys; bf16: 16 keys x 256 B = 4 KB, four pieces of 4 keys.  In LDS, chunk
+// q of key (piece j, key-in-piece k) sits at chunk position kCpk*k + (q ^ s)
+// of piece j, s = k ^ j (e4m3) or k + 4j (bf16).
 template <int FP8>
-struct KeyOp;
-
-template <>
-struct KeyOp<0> {  // bf16 keys: 4 x 16 B per lane
-  uint4 v[4];
-  CSA_DEV void load(const uint16_t* row, int lg, bool ok) {
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      v[ks] = ok ? *reinterpret_cast<const uint4*>(row + 32 * ks + 8 * lg) : make_uint4(0, 0, 0, 0);
+struct Geo {
+  static constexpr int kKeyB = FP8 ? 128 : 256;
+  static constexpr int kTileB = 16 * kKeyB;
+  static constexpr int kPieces = kTileB / 1024;
+  static constexpr int kKpp = 16 / kPieces;  // keys per piece
+  static constexpr int kCpk = kKeyB / 16;    // 16-byte chunks per key
+  static constexpr int kU = FP8 ? 6 : 4;     // tiles per batch (even)
+  CSA_DEV static int sw(int k, int j) { return FP8 ? (k ^ j) : (k + 4 * j); }
+  // LDS byte offset of chunk q of key c within a tile
+  CSA_DEV static int lds_off(int c, int q) {
+    const int j = c / kKpp, k = c % kKpp;
+    return 1024 * j + 16 * (kCpk * k + (q ^ sw(k, j)));
   }
 };
-
-// e4m3 keys: 2 x 16 B per lane.  The reduction index is permuted so that one
-// load instruction covers bytes 0..63 (then 64..127) of each key contiguously:
-// lane group g supplies d = 16g..16g+15 and 64+16g..64+16g+15 as its 32
-// k-slots; the query operand uses the same permutation.
-template <>
-struct KeyOp<1> {
-  uint4 v[2];
-  CSA_DEV void load(const uint8_t* row, int lg, bool ok) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      v[i] = ok ? *reinterpret_cast<const uint4*>(row + 64 * i + 16 * lg) : make_uint4(0, 0, 0, 0);
-  }
-};
-
-CSA_DEV int64_t n_vis(const IndexArgs& a, int b, int64_t t) {
-  const int64_t lim = vis_limit(t, a.m, a.vis);
-  const int64_t have = (int64_t)a.n_entries[b] + a.n_add;
-  int64_t n = lim < have ? lim : have;
-  if (n > a.E_cap) n = a.E_cap;
-  return n < 0 ? 0 : n;
-}
 
 }  // namespace
 
 // grid (n_wg, rows), 256 threads
 template <int FP8, int HT>
 __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, TopkWs ws, int use_hist) {
+  typedef Geo<FP8> G;
+  constexpr int kU = G::kU;
+  __shared__ __attribute__((aligned(1024))) char s_tr[4][kU * G::kTileB];  // per-wave transpose buffer
   __shared__ int s_hist[kTopkBins];
   const int row = blockIdx.y, b = row / a.Tq, tq = row % a.Tq;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
-  const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
-  const int64_t nv = n_vis(a, b, t);
   const int H = a.H_I;
-  if (use_hist) {
-    for (int i = tid; i < kTopkBins; i += 256) s_hist[i] = 0;
-    __syncthreads();
+
+  // the visible-entry count first (scalar loads), so the first key batch can
+  // be issued before the query operands and head weights are fetched
+  const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
+  const int32_t n_have = a.n_entries[b];
+  int64_t nv = vis_limit(t, a.m, a.vis);
+  {
+    const int64_t have = (int64_t)n_have + a.n_add;
+    if (have < nv) nv = have;
+    if (nv > a.E_cap) nv = a.E_cap;
+    if (nv < 0) nv = 0;
   }
-  // query operands and effective head weights for this lane's C rows
+  const char* keys = reinterpret_cast<const char*>(a.keys) + (size_t)b * a.E_cap * G::kKeyB;
+  const float* ksc = a.k_scale ? a.k_scale + (size_t)b * a.E_cap : nullptr;
+  float* out = a.scores + (size_t)row * a.E_cap;
+
+  // this wave's tiles [t0, t1), in batches of kU
+  const int64_t ntile = (nv + 15) / 16;
+  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t per = (ntile + nwaves - 1) / nwaves;
+  const int64_t t0 = ((int64_t)blockIdx.x * 4 + w) * per;
+  const int64_t t1 = t0 + per < ntile ? t0 + per : ntile;
+  const int n = t1 > t0 ? (int)(t1 - t0) : 0;
+  const int nbatch = (n + kU - 1) / kU;
+
+  // piece j of a tile: lane l reads bytes [16 l, 16 l + 16) of the piece,
+  // i.e. chunk (l % kCpk) of key kKpp*j + l / kCpk
+  typedef u32x4_t KBatch[kU][G::kPieces];
+  typedef float SBatch[kU];
+  const int ld_key = l / G::kCpk, ld_chunk = l % G::kCpk;
+  // the last row of this wave's run: loads past it (the tail of the run and
+  // the batches after it) all re-read that row, which stays in cache
+  const int64_t e_last = (t1 * 16 < nv ? t1 * 16 : nv) - 1;
+  auto load_batch = [&](KBatch& kreg, SBatch& sreg, int bi) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t e0 = (t0 + (int64_t)bi * kU + u) * 16;
+#pragma unroll
+      for (int j = 0; j < G::kPieces; ++j) {
+        int64_t e = e0 + G::kKpp * j + ld_key;
+        if (e > e_last) e = e_last;
+        kreg[u][j] = *reinterpret_cast<const u32x4_t*>(keys + (size_t)e * G::kKeyB + 16 * ld_chunk);
+      }
+      if constexpr (FP8) {
+        int64_t e = e0 + li;
+        if (e > e_last) e = e_last;
+        sreg[u] = ksc[e];
+      }
+    }
+  };
+  KBatch kA, kB;
+  SBatch sA, sB;
+  if (nbatch > 0) load_batch(kA, sA, 0);
+  __builtin_amdgcn_sched_barrier(0);
+
   bf16x8_t qb[HT][4];
   i32x8_t q8[HT];
   float wr[HT][4];
@@ -99,71 +149,129 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) qb[ht][ks] = *reinterpret_cast<const bf16x8_t*>(q + 32 * ks + 8 * lg);
     }
+    // heads 16 ht + 4 lg + r: one 16-byte load
+    const float4 wv = *reinterpret_cast<const float4*>(a.w + (size_t)row * H + 16 * ht + 4 * lg);
+    wr[ht][0] = wv.x; wr[ht][1] = wv.y; wr[ht][2] = wv.z; wr[ht][3] = wv.w;
+  }
+  // the per-head query scale (e4m3) folds into the head weight; one uniform
+  // branch around all its loads
+  if (a.q_scale) {
+    float4 qs[HT];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int hh = 16 * ht + 4 * lg + r;
-      float wv = a.w[(size_t)row * H + hh];
-      if (a.q_scale) wv *= a.q_scale[(size_t)row * H + hh];
-      wr[ht][r] = wv;
+    for (int ht = 0; ht < HT; ++ht)
+      qs[ht] = *reinterpret_cast<const float4*>(a.q_scale + (size_t)row * H + 16 * ht + 4 * lg);
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      wr[ht][0] *= qs[ht].x; wr[ht][1] *= qs[ht].y; wr[ht][2] *= qs[ht].z; wr[ht][3] *= qs[ht].w;
     }
   }
-  typedef typename std::conditional<FP8, uint8_t, uint16_t>::type KT;
-  const KT* keys = reinterpret_cast<const KT*>(a.keys) + (size_t)b * a.E_cap * kD;
-  const float* ksc = a.k_scale ? a.k_scale + (size_t)b * a.E_cap : nullptr;
-  float* out = a.scores + (size_t)row * a.E_cap;
+  if (use_hist) {
+    for (int i = tid; i < kTopkBins; i += 256) s_hist[i] = 0;
+    lds_barrier();  // LDS only: the key loads in flight are not waited for
+  }
 
-  // each wave scores a contiguous range of 16-key tiles, U tiles per batch,
-  // with the next batch's loads in flight while the current one is scored
-  constexpr int U = 4;
-  const int64_t ntile = (nv + 15) / 16;
-  const int64_t nwaves = (int64_t)gridDim.x * 4;
-  const int64_t per = ((ntile + nwaves - 1) / nwaves + U - 1) / U * U;
-  const int64_t t0 = ((int64_t)blockIdx.x * 4 + w) * per;
-  const int64_t t1 = t0 + per < ntile ? t0 + per : ntile;
-  auto load_batch = [&](KeyOp<FP8>* kb, int64_t tb) {
+  // LDS positions: where this lane writes its chunk of piece j, where it
+  // reads its MFMA operand chunks
+  char* tr = s_tr[w];
+  int wr_off[G::kPieces];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t e = (tb + u) * 16 + li;
-      const bool ok = tb + u < t1 && e < nv;
-      kb[u].load(keys + (size_t)(ok ? e : 0) * kD, lg, ok);
+  for (int j = 0; j < G::kPieces; ++j) wr_off[j] = G::lds_off(G::kKpp * j + ld_key, ld_chunk);
+  constexpr int kReads = FP8 ? 2 : 4;
+  int rd_off[kReads];
+#pragma unroll
+  for (int r = 0; r < kReads; ++r) rd_off[r] = G::lds_off(li, FP8 ? lg + 4 * r : 4 * r + lg);
+
+  // score tiles u, u+1 of the batch in the transpose buffer (interleaved so
+  // the two latency chains overlap)
+  constexpr int kG = 2;
+  auto score = [&](const SBatch& sreg, int bi, int u) __attribute__((always_inline)) {
+    float part[kG];
+#pragma unroll
+    for (int g = 0; g < kG; ++g) part[g] = 0.f;
+    if constexpr (FP8) {
+      i32x8_t kb[kG];
+#pragma unroll
+      for (int g = 0; g < kG; ++g) {
+        const char* src = tr + (u + g) * G::kTileB;
+        const uint4 v0 = *reinterpret_cast<const uint4*>(src + rd_off[0]);
+        const uint4 v1 = *reinterpret_cast<const uint4*>(src + rd_off[1]);
+        kb[g] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+      }
+      f32x4_t c[HT][kG];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int g = 0; g < kG; ++g)
+          c[ht][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q8[ht], kb[g], f32x4_t{0.f, 0.f, 0.f, 0.f},
+                                                                      0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int g = 0; g < kG; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part[g] += wr[ht][r] * relu(c[ht][g][r]);
+    } else {
+      bf16x8_t kf[kG][4];
+#pragma unroll
+      for (int g = 0; g < kG; ++g)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          kf[g][ks] = *reinterpret_cast<const bf16x8_t*>(tr + (u + g) * G::kTileB + rd_off[ks]);
+      f32x4_t c[HT][kG];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int g = 0; g < kG; ++g) c[ht][g] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+          for (int g = 0; g < kG; ++g)
+            c[ht][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[ht][ks], kf[g][ks], c[ht][g], 0, 0, 0);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int g = 0; g < kG; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part[g] += wr[ht][r] * relu(c[ht][g][r]);
+    }
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      // head sum over the four lane groups: lanes l, l^16, l^32, l^48
+      part[g] = lane_sum_xor16_32(part[g]);
+      if (FP8) part[g] *= sreg[u + g];
+      const int i = bi * kU + u + g;
+      const int64_t e = (t0 + i) * 16 + li;
+      if (e < nv && i < n && lg == 0) {
+        out[e] = part[g];
+        if (use_hist) atomicAdd(&s_hist[f32_key(part[g]) >> kTopkShift], 1);
+      }
     }
   };
-  KeyOp<FP8> cur[U], nxt[U];
-  if (t0 < t1) load_batch(cur, t0);
-  for (int64_t tb = t0; tb < t1; tb += U) {
-    if (tb + U < t1) load_batch(nxt, tb + U);
+
+  // transpose a batch through this wavefront's LDS buffer and score it; the
+  // writes land before the reads (the wavefront's own LDS operations, in order)
+  auto run_batch = [&](KBatch& kcur, SBatch& scur, int bi) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t e = (tb + u) * 16 + li;
-      const bool ok = tb + u < t1 && e < nv;
-      float part = 0.f;
+    for (int u = 0; u < kU; ++u)
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) {
-        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (FP8) {
-          const i32x8_t kb = i32x8_t{(int)cur[u].v[0].x, (int)cur[u].v[0].y, (int)cur[u].v[0].z,
-                                     (int)cur[u].v[0].w, (int)cur[u].v[1].x, (int)cur[u].v[1].y,
-                                     (int)cur[u].v[1].z, (int)cur[u].v[1].w};
-          c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q8[ht], kb, c, 0, 0, 0, 127, 0, 127);
-        } else {
+      for (int j = 0; j < G::kPieces; ++j)
+        *reinterpret_cast<u32x4_t*>(tr + u * G::kTileB + wr_off[j]) = kcur[u][j];
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[ht][ks], __builtin_bit_cast(bf16x8_t, cur[u].v[ks]),
-                                                        c, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part += wr[ht][r] * fmaxf(c[r], 0.f);
-      }
-      part += __shfl_xor(part, 16, 64);
-      part += __shfl_xor(part, 32, 64);
-      if (ok && lg == 0) {
-        if (ksc) part *= ksc[e];
-        out[e] = part;
-        if (use_hist) atomicAdd(&s_hist[f32_key(part) >> kTopkShift], 1);
-      }
+    for (int u = 0; u < kU; u += kG) score(scur, bi, u);
+  };
+  // two register batches alternate; loads are unconditional (past the run
+  // they hit one cached row), so the compiler's wait bookkeeping sees the
+  // same outstanding loads on every path and only waits for the batch that
+  // is about to be used
+  if (nbatch > 0) {
+    for (int bi = 0; bi < nbatch; bi += 2) {
+      load_batch(kB, sB, bi + 1);
+      run_batch(kA, sA, bi);
+      load_batch(kA, sA, bi + 2);
+      if (bi + 1 < nbatch) run_batch(kB, sB, bi + 1);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
   }
   if (use_hist) {
     __syncthreads();
@@ -179,26 +287,45 @@ bool index_mfma_supported(const IndexArgs& a) {
   return (a.idx_dtype == BF16 || a.idx_dtype == E4M3) && a.d_I == kD && a.H_I % 16 == 0 && a.H_I <= 64;
 }
 
-hipError_t launch_index_score_mfma(const IndexArgs& a, const TopkWs& ws, int use_hist, hipStream_t s) {
+// workgroups that fit on the device at once for a kernel of 256 threads
+template <typename K>
+static int resident_wgs(K kernel) {
+  int dev = 0, n_cu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1024;
+  if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 1024;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  return n_cu * per_cu;
+}
+
+template <int FP8, int HT>
+static hipError_t launch_scorer(const IndexArgs& a, const TopkWs& ws, int use_hist, hipStream_t s) {
+  // one round of resident workgroups (the scan is a single pass over the
+  // keys), at most one workgroup per 16 tiles of a row
+  static int resident = 0;
+  if (!resident) resident = resident_wgs(index_score_mfma_kernel<FP8, HT>);
   const int rows = a.B * a.Tq;
-  // about 1024 workgroups in total, at least 4 tiles (one batch) per wave
-  int per_row = (1024 + rows - 1) / rows;
+  int per_row = (resident + rows - 1) / rows;
   const int max_wg = (int)((((int64_t)a.E_cap + 15) / 16 + 15) / 16);
   if (per_row > max_wg) per_row = max_wg;
   if (per_row < 1) per_row = 1;
   dim3 grid(per_row, rows), block(256);
-  const int HT = a.H_I / 16;
-#define CSA_IDX_LAUNCH(F, N)                                                                       \
-  CSA_LAUNCH("index_score_mfma", (index_score_mfma_kernel<F, N>), grid, block, 0, s, a, ws, use_hist)
-  if (a.idx_dtype == E4M3) {
-    if (HT == 4) CSA_IDX_LAUNCH(1, 4); else if (HT == 3) CSA_IDX_LAUNCH(1, 3);
-    else if (HT == 2) CSA_IDX_LAUNCH(1, 2); else CSA_IDX_LAUNCH(1, 1);
-  } else {
-    if (HT == 4) CSA_IDX_LAUNCH(0, 4); else if (HT == 3) CSA_IDX_LAUNCH(0, 3);
-    else if (HT == 2) CSA_IDX_LAUNCH(0, 2); else CSA_IDX_LAUNCH(0, 1);
-  }
-#undef CSA_IDX_LAUNCH
+  CSA_LAUNCH("index_score_mfma", (index_score_mfma_kernel<FP8, HT>), grid, block, 0, s, a, ws, use_hist);
   return hipGetLastError();
+}
+
+hipError_t launch_index_score_mfma(const IndexArgs& a, const TopkWs& ws, int use_hist, hipStream_t s) {
+  const int HT = a.H_I / 16;
+  if (a.idx_dtype == E4M3) {
+    if (HT == 4) return launch_scorer<1, 4>(a, ws, use_hist, s);
+    if (HT == 3) return launch_scorer<1, 3>(a, ws, use_hist, s);
+    if (HT == 2) return launch_scorer<1, 2>(a, ws, use_hist, s);
+    return launch_scorer<1, 1>(a, ws, use_hist, s);
+  }
+  if (HT == 4) return launch_scorer<0, 4>(a, ws, use_hist, s);
+  if (HT == 3) return launch_scorer<0, 3>(a, ws, use_hist, s);
+  if (HT == 2) return launch_scorer<0, 2>(a, ws, use_hist, s);
+  return launch_scorer<0, 1>(a, ws, use_hist, s);
 }
 
 }  // namespace csa
