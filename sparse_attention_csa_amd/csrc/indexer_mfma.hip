@@ -80,8 +80,37 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int H = a.H_I;
 
-  // the visible-entry count first (scalar loads), so the first key batch can
-  // be issued before the query operands and head weights are fetched
+  // query operands and head weights first: small, their loads go out
+  // before the key stream so they do not queue behind it
+  bf16x8_t qb[HT][4];
+  i32x8_t q8[HT];
+  float wr[HT][4];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int h = 16 * ht + li;
+    if constexpr (FP8) {
+      const uint8_t* q = reinterpret_cast<const uint8_t*>(a.q) + ((size_t)row * H + h) * kD + 16 * lg;
+      const uint4 v0 = *reinterpret_cast<const uint4*>(q), v1 = *reinterpret_cast<const uint4*>(q + 64);
+      q8[ht] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+    } else {
+      const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)row * H + h) * kD;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qb[ht][ks] = *reinterpret_cast<const bf16x8_t*>(q + 32 * ks + 8 * lg);
+    }
+    // heads 16 ht + 4 lg + r: one 16-byte load
+    const float4 wv = *reinterpret_cast<const float4*>(a.w + (size_t)row * H + 16 * ht + 4 * lg);
+    wr[ht][0] = wv.x; wr[ht][1] = wv.y; wr[ht][2] = wv.z; wr[ht][3] = wv.w;
+  }
+  // e4m3 always comes with its per-head query scale (bf16 never has one)
+  float4 qs[HT];
+  if constexpr (FP8) {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+      qs[ht] = *reinterpret_cast<const float4*>(a.q_scale + (size_t)row * H + 16 * ht + 4 * lg);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // the visible-entry count (scalar loads), then the first two key batches
   const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
   const int32_t n_have = a.n_entries[b];
   int64_t nv = vis_limit(t, a.m, a.vis);
@@ -132,34 +161,11 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   KBatch kA, kB;
   SBatch sA, sB;
   if (nbatch > 0) load_batch(kA, sA, 0);
+  if (nbatch > 1) load_batch(kB, sB, 1);
   __builtin_amdgcn_sched_barrier(0);
 
-  bf16x8_t qb[HT][4];
-  i32x8_t q8[HT];
-  float wr[HT][4];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) {
-    const int h = 16 * ht + li;
-    if constexpr (FP8) {
-      const uint8_t* q = reinterpret_cast<const uint8_t*>(a.q) + ((size_t)row * H + h) * kD + 16 * lg;
-      const uint4 v0 = *reinterpret_cast<const uint4*>(q), v1 = *reinterpret_cast<const uint4*>(q + 64);
-      q8[ht] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-    } else {
-      const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)row * H + h) * kD;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) qb[ht][ks] = *reinterpret_cast<const bf16x8_t*>(q + 32 * ks + 8 * lg);
-    }
-    // heads 16 ht + 4 lg + r: one 16-byte load
-    const float4 wv = *reinterpret_cast<const float4*>(a.w + (size_t)row * H + 16 * ht + 4 * lg);
-    wr[ht][0] = wv.x; wr[ht][1] = wv.y; wr[ht][2] = wv.z; wr[ht][3] = wv.w;
-  }
-  // the per-head query scale (e4m3) folds into the head weight; one uniform
-  // branch around all its loads
-  if (a.q_scale) {
-    float4 qs[HT];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-      qs[ht] = *reinterpret_cast<const float4*>(a.q_scale + (size_t)row * H + 16 * ht + 4 * lg);
+  // the per-head query scale (e4m3) folds into the head weight
+  if constexpr (FP8) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       wr[ht][0] *= qs[ht].x; wr[ht][1] *= qs[ht].y; wr[ht][2] *= qs[ht].z; wr[ht][3] *= qs[ht].w;
@@ -265,12 +271,16 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   // they hit one cached row), so the compiler's wait bookkeeping sees the
   // same outstanding loads on every path and only waits for the batch that
   // is about to be used
+  // batches bi, bi+1 are in flight when step bi starts; a register batch is
+  // refilled (batch bi+2) as soon as its data has gone to LDS
   if (nbatch > 0) {
     for (int bi = 0; bi < nbatch; bi += 2) {
-      load_batch(kB, sB, bi + 1);
       run_batch(kA, sA, bi);
       load_batch(kA, sA, bi + 2);
-      if (bi + 1 < nbatch) run_batch(kB, sB, bi + 1);
+      if (bi + 1 < nbatch) {
+        run_batch(kB, sB, bi + 1);
+        load_batch(kB, sB, bi + 3);
+      }
     }
   }
   if (use_hist) {
