@@ -11,25 +11,20 @@ namespace csa {
 constexpr int kTopkBins = 2048;      // histogram of the top 11 key bits
 constexpr int kTopkShift = 21;       // key >> 21 = bin
 constexpr int kTopkCandCap = 8192;   // threshold-bin candidates resolved in LDS
+constexpr int kTopkMaxK = 2048;      // largest k
+constexpr int kTopkCollectSlice = 4096;  // entries per collect workgroup
 
-// per-row scratch, zero between calls (the finishing workgroup re-zeroes it)
+// per-row scratch; hist and ctr are zero between calls (the resolving
+// workgroup returns them to zero)
 struct TopkWs {
-  int* hist;          // [rows][kTopkBins]
-  int* ctr;           // [rows][4]: candidates, finished workgroups
-  uint32_t* bitmap;   // [rows][bitmap_words]: selected entries
-  uint32_t* summary;  // [rows][summary_words]: nonzero bitmap words
-  uint2* cand;        // [rows][kTopkCandCap] (key, id), split mode
-  int bitmap_words, summary_words;
+  int* hist;   // [rows][kTopkBins]
+  int* ctr;    // [rows][4]: candidates, certain winners
+  uint2* cand; // [rows][kTopkCandCap] (key, id) of threshold-bin entries (split mode)
+  int* sure;   // [rows][kTopkMaxK] ids above the threshold bin (split mode)
 };
 
-__device__ void topk_resolve_from_row(const float* sc, int nv, int b1, int want, uint32_t* bitmap,
-                                      uint32_t* summary, int* s_scan, int* s_hist, int* s_misc);
-
-size_t topk_ws_bytes(int rows, int E_cap, bool with_cand);
-// LDS of the split-mode resolve kernel; it must fit one workgroup (160 KB)
-size_t topk_split_lds_bytes(int E_cap);
-constexpr int kTopkCollectSlice = 4096;  // entries per collect workgroup
-TopkWs topk_ws_carve(void* base, int rows, int E_cap, bool with_cand);
+size_t topk_ws_bytes(int rows, int E_cap, bool split);
+TopkWs topk_ws_carve(void* base, int rows, int E_cap, bool split);
 hipError_t launch_topk_collect(const IndexArgs& a, const TopkWs& ws, int slices, int slice_len,
                                hipStream_t s);
 hipError_t launch_topk_rows(const IndexArgs& a, const TopkWs& ws, hipStream_t s);

@@ -7,19 +7,22 @@
 // Scores are compared as order-preserving 32-bit keys.  Selection runs in two
 // stages:
 //  1. coarse: a histogram of the top 11 key bits locates the bin b1 holding
-//     the k-th largest key; every entry in a higher bin is selected and is
-//     marked in a two-level per-row bitmap; entries in bin b1 are candidates.
-//  2. exact: one workgroup resolves the candidates by radix select on the
-//     remaining 21 key bits (and, among equal keys, on the entry id), marks
-//     the winners in an LDS copy of the bitmap, and emits the marked ids in
-//     order.  The summary level (one bit per nonzero bitmap word) lets the
-//     emitter touch only nonzero words in a single prefix pass.
+//     the k-th largest key.  Every entry in a higher bin is a certain winner
+//     (there are fewer than k of them); entries in bin b1 are candidates.
+//  2. exact: the (k - #certain) largest candidates are found by radix select
+//     on the remaining 21 key bits and, among equal keys, on the entry id.
+//     Certain winners and selected candidates (exactly k ids) are sorted
+//     ascending by a bitonic sort in LDS and written out.
+// If bin b1 holds more candidates than fit in LDS, the threshold is refined
+// over the whole row instead and the winners are emitted by one in-order
+// scan of the row (no sort needed).
+//
 // Split mode (few long rows, decode): the histogram is accumulated by the
-// scoring kernel, many workgroups scan slices of a row (candidate slots are
-// reserved with one atomic per workgroup), then a second kernel resolves each
-// row with one workgroup.  No workgroup waits on another.  Row mode (many rows, prefill): one workgroup per row does
-// everything.  Counters, histograms and bitmaps are returned to zero by the
-// workgroup that finishes a row.
+// scoring kernel; many workgroups scan slices of a row and append certain
+// winners and candidates to two per-row lists (one atomic reservation per
+// list and workgroup); then one workgroup per row resolves.  No workgroup
+// waits on another.  Row mode (many rows, prefill): one workgroup per row
+// does everything from the row's scores.
 
 #include "common.h"
 #include "kernels.h"
@@ -29,10 +32,9 @@ namespace csa {
 
 namespace {
 
-constexpr int kT = 256;  // threads per workgroup
-constexpr int kW = kT / 64;
-constexpr int kCollectPer = 16;  // keys per thread in a collect slice
-static_assert(kCollectPer * kT == kTopkCollectSlice, "collect slice");
+constexpr int kCT = 256;   // collect workgroup
+constexpr int kRT = 1024;  // resolve / row workgroup
+constexpr int kCollectPer = kTopkCollectSlice / kCT;  // 16 keys per thread
 
 CSA_DEV uint32_t bin_of(uint32_t key) { return key >> kTopkShift; }
 
@@ -46,8 +48,9 @@ CSA_DEV int wave_incl_scan(int v) {
   return v;
 }
 
-// exclusive prefix of v over the workgroup in thread order; *total = sum.
-// s_w: kW ints of scratch.  Contains two barriers.
+// exclusive prefix of v over the NT threads in thread order; *total = sum.
+// s_w: NT/64 ints of scratch.  Contains two barriers.
+template <int NT>
 CSA_DEV int block_excl_scan(int v, int* s_w, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int inc = wave_incl_scan(v);
@@ -55,7 +58,7 @@ CSA_DEV int block_excl_scan(int v, int* s_w, int* total) {
   __syncthreads();
   int off = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kW; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const int c = s_w[w];
     if (w < wave) off += c;
     tot += c;
@@ -65,9 +68,9 @@ CSA_DEV int block_excl_scan(int v, int* s_w, int* total) {
   return off + inc - v;
 }
 
-// In a histogram of nb bins (nb = 64 * per), find the bin where the count,
-// accumulated from the top (descending) or the bottom, first reaches `want`.
-// Executed by wave 0 only; returns (bin, count before it) in s_out[0..1].
+// In a histogram of 64 * PER bins, the bin where the count accumulated from
+// the top (DESC) or the bottom first reaches `want`.  Executed by one
+// wavefront; writes (bin, count before it) to s_out[0..1].
 template <int PER, bool DESC>
 CSA_DEV void wave_find(const int* hist, int want, int* s_out) {
   const int lane = threadIdx.x & 63;
@@ -94,120 +97,13 @@ CSA_DEV void wave_find(const int* hist, int want, int* s_out) {
   }
 }
 
-// mark an id in a two-level bitmap (global or LDS); results are not awaited
-CSA_DEV void mark(uint32_t* bitmap, uint32_t* summary, int id) {
-  atomicOr(&bitmap[id >> 5], 1u << (id & 31));
-  atomicOr(&summary[id >> 10], 1u << ((id >> 5) & 31));
-}
-
-// Radix select among n (key, id) pairs in LDS (all in one top-11-bit bin):
-// the `want` largest keys, ties to the lower id; winners are marked.
-CSA_DEV void select_candidates(const uint32_t* ckey, const int* cid, int n, int want,
-                               uint32_t* bitmap, uint32_t* summary, int* s_hist, int* s_misc) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = ckey[0] >> kTopkShift;
-  int rem = want;
-  int shift = kTopkShift;
-  for (int pass = 0; pass < 3; ++pass) {
-    shift -= 7;
-    if (tid < 128) s_hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < n; i += kT) {
-      const uint32_t key = ckey[i];
-      if ((key >> (shift + 7)) == prefix) atomicAdd(&s_hist[(key >> shift) & 127], 1);
-    }
-    __syncthreads();
-    if (tid < 64) wave_find<2, true>(s_hist, rem, s_misc);
-    __syncthreads();
-    prefix = (prefix << 7) | (uint32_t)s_misc[0];
-    rem -= s_misc[1];
-    __syncthreads();
-  }
-  const uint32_t tau = prefix;  // key of the last winner; `rem` keys equal to tau win
-  int nt = 0;
-  for (int i = tid; i < n; i += kT) nt += ckey[i] == tau;
-  int n_tie;
-  block_excl_scan(nt, s_misc + 4, &n_tie);
-  int id_lim = 0x7fffffff;  // ties with id <= id_lim win
-  if (n_tie > rem) {
-    // the rem lowest ids among the ties: 3 passes of 10 bits over a 30-bit id
-    uint32_t ipref = 0;
-    for (int pass = 0; pass < 3; ++pass) {
-      const int sh = 20 - 10 * pass;
-      for (int i = tid; i < 1024; i += kT) s_hist[i] = 0;
-      __syncthreads();
-      for (int i = tid; i < n; i += kT) {
-        const uint32_t id = (uint32_t)cid[i];
-        if (ckey[i] == tau && (pass == 0 || (id >> (sh + 10)) == ipref))
-          atomicAdd(&s_hist[(id >> sh) & 1023], 1);
-      }
-      __syncthreads();
-      if (tid < 64) wave_find<16, false>(s_hist, rem, s_misc);
-      __syncthreads();
-      ipref = (ipref << 10) | (uint32_t)s_misc[0];
-      rem -= s_misc[1];
-      __syncthreads();
-    }
-    id_lim = (int)ipref;  // ids are distinct: exactly the wanted ties have id <= ipref
-  }
-  for (int i = tid; i < n; i += kT) {
-    const uint32_t key = ckey[i];
-    if (key > tau || (key == tau && cid[i] <= id_lim)) mark(bitmap, summary, cid[i]);
-  }
-}
-
-// Emit the marked ids in ascending order, clear both bitmap levels, pad with
-// -1 to k.  Thread i owns summary words i, i + kT, ... in order.
-CSA_DEV void emit_bitmap(uint32_t* bitmap, uint32_t* summary, int nwords, int32_t* out, int k,
-                         int32_t* cnt_out, int* s_w) {
-  const int tid = threadIdx.x;
-  const int nsum = (nwords + 31) >> 5;
-  int base = 0;
-  for (int s0 = 0; s0 < nsum; s0 += kT) {
-    const int si = s0 + tid;
-    const uint32_t sw = si < nsum ? summary[si] : 0u;
-    int c = 0;
-    uint32_t bits = sw;
-    while (bits) {
-      const int j = __ffs(bits) - 1;
-      bits &= bits - 1;
-      c += __popc(bitmap[32 * si + j]);
-    }
-    int total;
-    int pos = base + block_excl_scan(c, s_w, &total);
-    bits = sw;
-    while (bits) {
-      const int j = __ffs(bits) - 1;
-      bits &= bits - 1;
-      const int wi = 32 * si + j;
-      uint32_t v = bitmap[wi];
-      bitmap[wi] = 0u;
-      while (v) {
-        const int b = __ffs(v) - 1;
-        v &= v - 1;
-        if (pos < k) out[pos] = wi * 32 + b;
-        ++pos;
-      }
-    }
-    if (sw) summary[si] = 0u;
-    base += total;
-  }
-  for (int i = base + tid; i < k; i += kT) out[i] = -1;
-  if (tid == 0) *cnt_out = base < k ? base : k;
-}
-
-CSA_DEV int64_t visible(const IndexArgs& a, int b, int64_t t) {
-  const int64_t lim = vis_limit(t, a.m, a.vis);
-  const int64_t have = (int64_t)a.n_entries[b] + a.n_add;
-  int64_t n = lim < have ? lim : have;
-  if (n > a.E_cap) n = a.E_cap;
-  return n < 0 ? 0 : n;
-}
-
-// b1 and the count above it, from a kTopkBins histogram; all threads get them
+// b1 (bin of the k-th largest key) and the count above it from a kTopkBins
+// histogram (global or LDS); every thread gets both.  s_w: NT/64 ints,
+// s_out: 2 ints.
+template <int NT>
 CSA_DEV void find_bin(const int* hist, int k, int* s_w, int* s_out, int* b1, int* above) {
   const int tid = threadIdx.x;
-  constexpr int PER = kTopkBins / kT;  // 8
+  constexpr int PER = kTopkBins / NT;
   int c[PER], tot = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -215,7 +111,7 @@ CSA_DEV void find_bin(const int* hist, int k, int* s_w, int* s_out, int* b1, int
     tot += c[i];
   }
   int all;
-  const int before = block_excl_scan(tot, s_w, &all);
+  const int before = block_excl_scan<NT>(tot, s_w, &all);
   if (before < k && before + tot >= k) {
     int acc = before;
 #pragma unroll
@@ -234,290 +130,416 @@ CSA_DEV void find_bin(const int* hist, int k, int* s_w, int* s_out, int* b1, int
   __syncthreads();
 }
 
+CSA_DEV int64_t visible(const IndexArgs& a, int b, int64_t t) {
+  const int64_t lim = vis_limit(t, a.m, a.vis);
+  const int64_t have = (int64_t)a.n_entries[b] + a.n_add;
+  int64_t n = lim < have ? lim : have;
+  if (n > a.E_cap) n = a.E_cap;
+  return n < 0 ? 0 : n;
+}
+
+// LDS of a resolving workgroup.  misc: [0..1] wave_find result, [8..23] and
+// [24..39] scan scratch, [40..41] find_bin result, [48..49] list counters.
 struct Lds {
   uint32_t ckey[kTopkCandCap];
   int cid[kTopkCandCap];
-  int hist[kTopkBins];
-  int misc[16];
+  int win[kTopkMaxK];   // winner ids (sorted in place)
+  int hist[kTopkBins];  // radix histograms / the row histogram
+  int misc[64];
 };
 
-}  // namespace
-
-// ---------------------------------------------------------------------------
-// split mode: grid (n_slices, rows), kT threads.  hist filled by the scorer.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kT) void topk_collect_kernel(IndexArgs a, TopkWs ws, int slice_len) {
-  __shared__ int s_misc[16];
-  const int row = blockIdx.y, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x;
-  const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
-  const int nv = (int)visible(a, b, t);
-  const int k = a.k;
-  int* hist = ws.hist + (size_t)row * kTopkBins;
-  int* ctr = ws.ctr + (size_t)row * 4;
-  uint32_t* bitmap = ws.bitmap + (size_t)row * ws.bitmap_words;
-  uint32_t* summary = ws.summary + (size_t)row * ws.summary_words;
-  uint2* cand = ws.cand + (size_t)row * kTopkCandCap;
-  const float* sc = a.scores + (size_t)row * a.E_cap;
-
-  int b1 = -1, above = 0;
-  if (nv > k) {
-    find_bin(hist, k, s_misc, s_misc + 8, &b1, &above);
-    const int s0 = blockIdx.x * slice_len;
-    const int s1 = min(nv, s0 + slice_len);
-    // pass 1: mark winners above the bin, count candidates (keys stay in
-    // registers for pass 2; slices are at most kCollectPer * kT long)
-    uint32_t keys[kCollectPer];
-    int nc = 0;
-#pragma unroll
-    for (int i = 0; i < kCollectPer; ++i) {
-      const int s = s0 + tid + i * kT;
-      keys[i] = s < s1 ? f32_key(sc[s]) : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < kCollectPer; ++i) {
-      const int s = s0 + tid + i * kT;
-      if (s < s1) {
-        const int bin = (int)bin_of(keys[i]);
-        if (bin > b1) mark(bitmap, summary, s);
-        nc += bin == b1;
-      }
-    }
-    int total;
-    int off = block_excl_scan(nc, s_misc, &total);
-    if (tid == 0) s_misc[4] = total ? atomicAdd(&ctr[0], total) : 0;
+// Radix select among n candidates (keys all in bin b1): the `want` largest,
+// ties to the lower id.  Appends the winners' ids to win[*n_win ...].
+CSA_DEV void select_candidates(Lds& L, int n, uint32_t b1, int want, int* n_win) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = b1;
+  int rem = want;
+  int shift = kTopkShift;
+  for (int pass = 0; pass < 3; ++pass) {  // bits 20..14, 13..7, 6..0
+    shift -= 7;
+    if (tid < 128) L.hist[tid] = 0;
     __syncthreads();
-    off += s_misc[4];
-    // pass 2: write candidates into the reserved slots
-    if (nc) {
-#pragma unroll
-      for (int i = 0; i < kCollectPer; ++i) {
-        const int s = s0 + tid + i * kT;
-        if (s < s1 && (int)bin_of(keys[i]) == b1) {
-          if (off < kTopkCandCap) cand[off] = make_uint2(keys[i], (uint32_t)s);
-          ++off;
-        }
-      }
+    for (int i = tid; i < n; i += kRT) {
+      const uint32_t key = L.ckey[i];
+      if ((key >> (shift + 7)) == prefix) atomicAdd(&L.hist[(key >> shift) & 127], 1);
     }
+    __syncthreads();
+    if (tid < 64) wave_find<2, true>(L.hist, rem, L.misc);
+    __syncthreads();
+    prefix = (prefix << 7) | (uint32_t)L.misc[0];
+    rem -= L.misc[1];
+    __syncthreads();
   }
-}
-
-// ---------------------------------------------------------------------------
-// split mode, stage 2: grid (rows), one workgroup resolves a row's
-// candidates, emits its ids and clears the row's scratch.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kT) void topk_resolve_kernel(IndexArgs a, TopkWs ws) {
-  extern __shared__ unsigned char dyn[];
-  Lds& L = *reinterpret_cast<Lds*>(dyn);
-  uint32_t* lbit = reinterpret_cast<uint32_t*>(dyn + sizeof(Lds));  // [bitmap_words]
-  uint32_t* lsum = lbit + ws.bitmap_words;                           // [summary_words]
-  const int row = blockIdx.x, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x;
-  const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
-  const int nv = (int)visible(a, b, t);
-  const int k = a.k;
-  int* hist = ws.hist + (size_t)row * kTopkBins;
-  int* ctr = ws.ctr + (size_t)row * 4;
-  uint32_t* bitmap = ws.bitmap + (size_t)row * ws.bitmap_words;
-  uint32_t* summary = ws.summary + (size_t)row * ws.summary_words;
-  const uint2* cand = ws.cand + (size_t)row * kTopkCandCap;
-  const float* sc = a.scores + (size_t)row * a.E_cap;
-  int32_t* out = a.topk_idx + (size_t)row * k;
-  if (nv <= k) {
-    for (int i = tid; i < k; i += kT) out[i] = i < nv ? i : -1;
-    if (tid == 0) a.topk_cnt[row] = nv;
-  } else {
-    const int nwords = (nv + 31) >> 5, nsum = (nwords + 31) >> 5;
-    // the row's winners so far (marked by the collect pass) move to LDS
-    for (int i = tid; i < nwords; i += kT) lbit[i] = bitmap[i];
-    for (int i = tid; i < nsum; i += kT) lsum[i] = summary[i];
-    int b1, above;
-    find_bin(hist, k, L.misc, L.misc + 8, &b1, &above);
-    const int n_cand = ctr[0];
-    if (n_cand <= kTopkCandCap) {
-      for (int i = tid; i < n_cand; i += kT) {
-        const uint2 v = cand[i];
-        L.ckey[i] = v.x;
-        L.cid[i] = (int)v.y;
+  const uint32_t tau = prefix;  // key of the last winner; `rem` keys equal to tau win
+  int nt = 0;
+  for (int i = tid; i < n; i += kRT) nt += L.ckey[i] == tau;
+  int n_tie;
+  block_excl_scan<kRT>(nt, L.misc + 8, &n_tie);
+  int id_lim = 0x7fffffff;  // ties with id <= id_lim win
+  if (n_tie > rem) {
+    // the rem lowest ids among the ties: 2 passes of 10 bits (ids < 2^20)
+    uint32_t ipref = 0;
+    for (int pass = 0; pass < 2; ++pass) {
+      const int sh = 10 - 10 * pass;
+      for (int i = tid; i < 1024; i += kRT) L.hist[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += kRT) {
+        const uint32_t id = (uint32_t)L.cid[i];
+        if (L.ckey[i] == tau && (pass == 0 || (id >> (sh + 10)) == ipref))
+          atomicAdd(&L.hist[(id >> sh) & 1023], 1);
       }
       __syncthreads();
-      select_candidates(L.ckey, L.cid, n_cand, k - above, lbit, lsum, L.hist, L.misc);
-    } else {
-      topk_resolve_from_row(sc, nv, b1, k - above, lbit, lsum, L.cid, L.hist, L.misc);
+      if (tid < 64) wave_find<16, false>(L.hist, rem, L.misc);
+      __syncthreads();
+      ipref = (ipref << 10) | (uint32_t)L.misc[0];
+      rem -= L.misc[1];
+      __syncthreads();
     }
-    __syncthreads();
-    // clear the global bitmap words the collect pass may have set
-    for (int i = tid; i < nsum; i += kT) {
-      uint32_t sw = lsum[i];
-      if (sw) summary[i] = 0u;
-      while (sw) {
-        const int j = __ffs(sw) - 1;
-        sw &= sw - 1;
-        bitmap[32 * i + j] = 0u;
-      }
+    id_lim = (int)ipref;  // ids are distinct: exactly the wanted ties have id <= ipref
+  }
+  if (tid == 0) L.misc[48] = *n_win;
+  __syncthreads();
+  for (int i = tid; i < n; i += kRT) {
+    const uint32_t key = L.ckey[i];
+    if (key > tau || (key == tau && L.cid[i] <= id_lim)) {
+      const int o = atomicAdd(&L.misc[48], 1);
+      if (o < kTopkMaxK) L.win[o] = L.cid[i];
     }
-    emit_bitmap(lbit, lsum, nwords, out, k, &a.topk_cnt[row], L.misc);
   }
   __syncthreads();
-  for (int i = tid; i < kTopkBins; i += kT) hist[i] = 0;
-  if (tid == 0) ctr[0] = 0;
+  *n_win = min(L.misc[48], kTopkMaxK);
+  __syncthreads();
 }
 
-// ---------------------------------------------------------------------------
-// row mode: grid (rows), one workgroup per row, scores already written.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kT) void topk_rowsel_kernel(IndexArgs a, TopkWs ws) {
-  extern __shared__ unsigned char dyn[];
-  Lds& L = *reinterpret_cast<Lds*>(dyn);
-  uint32_t* lbit = reinterpret_cast<uint32_t*>(dyn + sizeof(Lds));  // [bitmap_words]
-  uint32_t* lsum = lbit + ws.bitmap_words;                           // [summary_words]
-  const int row = blockIdx.x, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x;
-  const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
-  const int nv = (int)visible(a, b, t);
-  const int k = a.k;
-  const float* sc = a.scores + (size_t)row * a.E_cap;
-  int32_t* out = a.topk_idx + (size_t)row * k;
-  if (nv <= k) {
-    for (int i = tid; i < k; i += kT) out[i] = i < nv ? i : -1;
-    if (tid == 0) a.topk_cnt[row] = nv;
-    return;
-  }
-  const int nwords = (nv + 31) >> 5, nsum = (nwords + 31) >> 5;
-  for (int i = tid; i < kTopkBins; i += kT) L.hist[i] = 0;
-  for (int i = tid; i < nwords; i += kT) lbit[i] = 0u;
-  for (int i = tid; i < nsum; i += kT) lsum[i] = 0u;
+// Ascending sort of the n (<= kTopkMaxK) distinct ids in win[], by buckets
+// of the id range [0, nv): bucket counts, their exclusive prefix, a scatter
+// into ckey/cid storage (free after the selection), then each thread orders
+// its own buckets (about one id per bucket on average) by insertion sort.
+// The sorted ids end in L.cid[0..n).
+constexpr int kSortBuckets = 2048;
+CSA_DEV void sort_ids(Lds& L, int n, int nv) {
+  const int tid = threadIdx.x;
+  int* cnt = L.hist;                                    // [kSortBuckets]
+  int* start = reinterpret_cast<int*>(L.ckey);          // [kSortBuckets] bucket starts
+  int* fill = reinterpret_cast<int*>(L.ckey) + kSortBuckets;
+  int* dst = L.cid;
+  auto bucket = [&](int id) { return (int)(((uint64_t)(uint32_t)id * kSortBuckets) / (uint32_t)nv); };
+  for (int i = tid; i < kSortBuckets; i += kRT) cnt[i] = 0;
   __syncthreads();
-  for (int s = tid; s < nv; s += kT) atomicAdd(&L.hist[bin_of(f32_key(sc[s]))], 1);
+  for (int i = tid; i < n; i += kRT) atomicAdd(&cnt[bucket(L.win[i])], 1);
   __syncthreads();
-  int b1, above;
-  find_bin(L.hist, k, L.misc, L.misc + 8, &b1, &above);
-  int nc = 0;
-  for (int s = tid; s < nv; s += kT) {
-    const int bin = (int)bin_of(f32_key(sc[s]));
-    if (bin > b1) mark(lbit, lsum, s);
-    nc += bin == b1;
+  constexpr int PER = kSortBuckets / kRT;
+  int c[PER], tot = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    c[j] = cnt[PER * tid + j];
+    tot += c[j];
   }
-  int n_cand;
-  int off = block_excl_scan(nc, L.misc, &n_cand);
-  if (n_cand <= kTopkCandCap) {
-    if (nc) {
-      for (int s = tid; s < nv; s += kT) {
-        const uint32_t key = f32_key(sc[s]);
-        if ((int)bin_of(key) == b1) {
-          L.ckey[off] = key;
-          L.cid[off] = s;
-          ++off;
-        }
+  int all;
+  int off = block_excl_scan<kRT>(tot, L.misc + 8, &all);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    start[PER * tid + j] = off;
+    fill[PER * tid + j] = off;
+    off += c[j];
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += kRT) {
+    const int id = L.win[i];
+    dst[atomicAdd(&fill[bucket(id)], 1)] = id;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int bk = PER * tid + j, b0 = start[bk], b1 = b0 + c[j];
+    for (int x = b0 + 1; x < b1; ++x) {
+      const int v = dst[x];
+      int y = x - 1;
+      while (y >= b0 && dst[y] > v) {
+        dst[y + 1] = dst[y];
+        --y;
       }
+      dst[y + 1] = v;
     }
-    __syncthreads();
-    select_candidates(L.ckey, L.cid, n_cand, k - above, lbit, lsum, L.hist, L.misc);
-  } else {
-    topk_resolve_from_row(sc, nv, b1, k - above, lbit, lsum, L.cid, L.hist, L.misc);
   }
   __syncthreads();
-  emit_bitmap(lbit, lsum, nwords, out, k, &a.topk_cnt[row], L.misc);
 }
 
-// Exact resolution when the threshold bin holds more than kTopkCandCap keys:
-// radix refine over the row on bits 20..0 restricted to bin b1 (3 passes),
-// then one in-order pass marks keys above the threshold and the lowest-id
-// ties (the row is scanned in id order, chunk by chunk).
-__device__ void topk_resolve_from_row(const float* sc, int nv, int b1, int want, uint32_t* bitmap,
-                                      uint32_t* summary, int* s_scan, int* s_hist, int* s_misc) {
+// Threshold over the whole row (bin b1 too large for LDS): radix refine on
+// bits 20..0 restricted to b1, then one in-order pass writes every winner
+// (key above the threshold, or equal to it among the first `rem` in id
+// order) to out in ascending id order.  Returns the count written.
+CSA_DEV int resolve_from_row(Lds& L, const float* sc, int nv, int b1, int want, int32_t* out) {
   const int tid = threadIdx.x;
   uint32_t prefix = (uint32_t)b1;
   int rem = want;
   int shift = kTopkShift;
   for (int pass = 0; pass < 3; ++pass) {
     shift -= 7;
-    if (tid < 128) s_hist[tid] = 0;
+    if (tid < 128) L.hist[tid] = 0;
     __syncthreads();
-    for (int s = tid; s < nv; s += kT) {
+    for (int s = tid; s < nv; s += kRT) {
       const uint32_t key = f32_key(sc[s]);
-      if ((key >> (shift + 7)) == prefix) atomicAdd(&s_hist[(key >> shift) & 127], 1);
+      if ((key >> (shift + 7)) == prefix) atomicAdd(&L.hist[(key >> shift) & 127], 1);
     }
     __syncthreads();
-    if (tid < 64) wave_find<2, true>(s_hist, rem, s_misc);
+    if (tid < 64) wave_find<2, true>(L.hist, rem, L.misc);
     __syncthreads();
-    prefix = (prefix << 7) | (uint32_t)s_misc[0];
-    rem -= s_misc[1];
+    prefix = (prefix << 7) | (uint32_t)L.misc[0];
+    rem -= L.misc[1];
     __syncthreads();
   }
   const uint32_t tau = prefix;
-  int taken = 0;
-  for (int base = 0; base < nv; base += kT) {
+  int taken = 0, pos = 0;
+  for (int base = 0; base < nv; base += kRT) {
     const int s = base + tid;
     const uint32_t key = s < nv ? f32_key(sc[s]) : 0u;
-    const bool bin_ok = s < nv && (int)(key >> kTopkShift) == b1;
-    const bool eq = bin_ok && key == tau;
-    int tot;
-    const int rank = taken + block_excl_scan(eq ? 1 : 0, s_scan, &tot);
-    if (bin_ok && (key > tau || (eq && rank < rem))) mark(bitmap, summary, s);
-    taken += tot;
+    const bool eq = s < nv && key == tau;
+    int n_eq;
+    const int rank = taken + block_excl_scan<kRT>(eq ? 1 : 0, L.misc + 8, &n_eq);
+    const bool win = s < nv && (key > tau || (eq && rank < rem));
+    int n_w;
+    const int off = block_excl_scan<kRT>(win ? 1 : 0, L.misc + 24, &n_w);
+    if (win) out[pos + off] = s;
+    taken += n_eq;
+    pos += n_w;
+  }
+  return pos;
+}
+
+// write the sorted winners (L.cid) and the -1 padding, and the count
+CSA_DEV void emit(const Lds& L, int n, int k, int32_t* out, int32_t* cnt) {
+  const int tid = threadIdx.x;
+  for (int i = tid; i < k; i += kRT) out[i] = i < n ? L.cid[i] : -1;
+  if (tid == 0) *cnt = n < k ? n : k;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// split mode, stage 1: grid (n_slices, rows), kCT threads.  The row's
+// histogram was filled by the scorer.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kCT) void topk_collect_kernel(IndexArgs a, TopkWs ws, int slice_len) {
+  __shared__ int s_misc[32];
+  const int row = blockIdx.y, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x;
+  const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
+  const int nv = (int)visible(a, b, t);
+  const int k = a.k;
+  if (nv <= k) return;
+  const int s0 = blockIdx.x * slice_len;
+  if (s0 >= nv) return;
+  const int s1 = min(nv, s0 + slice_len);
+  const float* sc = a.scores + (size_t)row * a.E_cap;
+  // the slice's scores first (independent of the threshold bin)
+  uint32_t keys[kCollectPer];
+#pragma unroll
+  for (int i = 0; i < kCollectPer; ++i) {
+    const int s = s0 + tid + i * kCT;
+    keys[i] = s < s1 ? f32_key(sc[s]) : 0u;
+  }
+  int b1, above;
+  find_bin<kCT>(ws.hist + (size_t)row * kTopkBins, k, s_misc, s_misc + 8, &b1, &above);
+  // per thread: certain winners in the low half, candidates in the high half
+  // (at most kCollectPer each, so one scan carries both counts)
+  int cnt = 0;
+#pragma unroll
+  for (int i = 0; i < kCollectPer; ++i) {
+    const int s = s0 + tid + i * kCT;
+    if (s < s1) {
+      const int bin = (int)bin_of(keys[i]);
+      cnt += (bin > b1 ? 1 : 0) + (bin == b1 ? 1 << 16 : 0);
+    }
+  }
+  int total;
+  const int off = block_excl_scan<kCT>(cnt, s_misc, &total);
+  // one 64-bit reservation for both lists: candidates in the low word,
+  // certain winners in the high word
+  unsigned long long* ctr = reinterpret_cast<unsigned long long*>(ws.ctr + (size_t)row * 4);
+  if (tid == 0) {
+    const unsigned long long ts = total & 0xffff, tc = (unsigned)total >> 16;
+    const unsigned long long old = total ? atomicAdd(ctr, tc | (ts << 32)) : 0ull;
+    s_misc[16] = (int)(old >> 32);
+    s_misc[17] = (int)(old & 0xffffffffull);
   }
   __syncthreads();
+  if (cnt == 0) return;
+  int os = s_misc[16] + (off & 0xffff), oc = s_misc[17] + (off >> 16);
+  int* sure = ws.sure + (size_t)row * kTopkMaxK;
+  uint2* cand = ws.cand + (size_t)row * kTopkCandCap;
+#pragma unroll
+  for (int i = 0; i < kCollectPer; ++i) {
+    const int s = s0 + tid + i * kCT;
+    if (s < s1) {
+      const int bin = (int)bin_of(keys[i]);
+      if (bin > b1) {  // fewer than k of them in the row
+        if (os < kTopkMaxK) sure[os] = s;
+        ++os;
+      }
+      if (bin == b1) {
+        if (oc < kTopkCandCap) cand[oc] = make_uint2(keys[i], (uint32_t)s);
+        ++oc;
+      }
+    }
+  }
 }
 
-size_t topk_split_lds_bytes(int E_cap) {
-  const size_t words = ((size_t)E_cap + 31) / 32;
-  return sizeof(Lds) + (words + (words + 31) / 32) * 4;
+// ---------------------------------------------------------------------------
+// split mode, stage 2: grid (rows), kRT threads; resolves a row and returns
+// its histogram and counters to zero.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRT) void topk_resolve_kernel(IndexArgs a, TopkWs ws) {
+  extern __shared__ unsigned char dyn[];
+  Lds& L = *reinterpret_cast<Lds*>(dyn);
+  const int row = blockIdx.x, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x;
+  const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
+  const int nv = (int)visible(a, b, t);
+  const int k = a.k;
+  int* hist = ws.hist + (size_t)row * kTopkBins;
+  int* ctr = ws.ctr + (size_t)row * 4;
+  int32_t* out = a.topk_idx + (size_t)row * k;
+  if (nv <= k) {
+    for (int i = tid; i < k; i += kRT) out[i] = i < nv ? i : -1;
+    if (tid == 0) a.topk_cnt[row] = nv;
+  } else {
+    const int n_cand = ctr[0], n_sure = min(ctr[1], kTopkMaxK);
+    int b1, above;
+    find_bin<kRT>(hist, k, L.misc + 8, L.misc + 40, &b1, &above);
+    if (n_cand <= kTopkCandCap) {
+      const uint2* cand = ws.cand + (size_t)row * kTopkCandCap;
+      const int* sure = ws.sure + (size_t)row * kTopkMaxK;
+      for (int i = tid; i < n_cand; i += kRT) {
+        const uint2 v = cand[i];
+        L.ckey[i] = v.x;
+        L.cid[i] = (int)v.y;
+      }
+      for (int i = tid; i < n_sure; i += kRT) L.win[i] = sure[i];
+      __syncthreads();
+      int n_win = n_sure;  // == above
+      select_candidates(L, n_cand, (uint32_t)b1, k - above, &n_win);
+      sort_ids(L, n_win, nv);
+      emit(L, n_win, k, out, &a.topk_cnt[row]);
+    } else {
+      const int n = resolve_from_row(L, a.scores + (size_t)row * a.E_cap, nv, b1, k - above, out);
+      if (tid == 0) a.topk_cnt[row] = n;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kTopkBins; i += kRT) hist[i] = 0;
+  if (tid == 0) {
+    ctr[0] = 0;
+    ctr[1] = 0;
+  }
 }
 
-size_t topk_ws_bytes(int rows, int E_cap, bool with_cand) {
-  const size_t words = ((size_t)E_cap + 31) / 32;
-  const size_t swords = (words + 31) / 32;
-  return (size_t)rows * (kTopkBins * 4 + 16 + (words + swords) * 4 +
-                         (with_cand ? (size_t)kTopkCandCap * 8 : 0)) +
-         1024;
+// ---------------------------------------------------------------------------
+// row mode: grid (rows), kRT threads, one workgroup per row, scores already
+// written.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRT) void topk_rowsel_kernel(IndexArgs a, TopkWs ws) {
+  extern __shared__ unsigned char dyn[];
+  Lds& L = *reinterpret_cast<Lds*>(dyn);
+  (void)ws;
+  const int row = blockIdx.x, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x;
+  const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
+  const int nv = (int)visible(a, b, t);
+  const int k = a.k;
+  const float* sc = a.scores + (size_t)row * a.E_cap;
+  int32_t* out = a.topk_idx + (size_t)row * k;
+  if (nv <= k) {
+    for (int i = tid; i < k; i += kRT) out[i] = i < nv ? i : -1;
+    if (tid == 0) a.topk_cnt[row] = nv;
+    return;
+  }
+  for (int i = tid; i < kTopkBins; i += kRT) L.hist[i] = 0;
+  if (tid == 0) {
+    L.misc[48] = 0;
+    L.misc[49] = 0;
+  }
+  __syncthreads();
+  for (int s = tid; s < nv; s += kRT) atomicAdd(&L.hist[bin_of(f32_key(sc[s]))], 1);
+  __syncthreads();
+  int b1, above;
+  find_bin<kRT>(L.hist, k, L.misc + 8, L.misc + 40, &b1, &above);
+  // certain winners to win[], candidates to ckey/cid (counted past the cap)
+  for (int s = tid; s < nv; s += kRT) {
+    const uint32_t key = f32_key(sc[s]);
+    const int bin = (int)bin_of(key);
+    if (bin > b1) {
+      const int o = atomicAdd(&L.misc[48], 1);
+      if (o < kTopkMaxK) L.win[o] = s;
+    }
+    if (bin == b1) {
+      const int o = atomicAdd(&L.misc[49], 1);
+      if (o < kTopkCandCap) {
+        L.ckey[o] = key;
+        L.cid[o] = s;
+      }
+    }
+  }
+  __syncthreads();
+  const int n_sure = min(L.misc[48], kTopkMaxK), n_cand = L.misc[49];
+  __syncthreads();
+  if (n_cand <= kTopkCandCap) {
+    int n_win = n_sure;
+    select_candidates(L, n_cand, (uint32_t)b1, k - above, &n_win);
+    sort_ids(L, n_win, nv);
+    emit(L, n_win, k, out, &a.topk_cnt[row]);
+  } else {
+    const int n = resolve_from_row(L, sc, nv, b1, k - above, out);
+    if (tid == 0) a.topk_cnt[row] = n;
+  }
 }
 
-TopkWs topk_ws_carve(void* base, int rows, int E_cap, bool with_cand) {
+size_t topk_ws_bytes(int rows, int E_cap, bool split) {
+  (void)E_cap;
+  size_t per = kTopkBins * 4 + 16;
+  if (split) per += (size_t)kTopkCandCap * 8 + (size_t)kTopkMaxK * 4;
+  return (size_t)rows * per + 1024;
+}
+
+TopkWs topk_ws_carve(void* base, int rows, int E_cap, bool split) {
+  (void)E_cap;
   TopkWs w;
   char* p = reinterpret_cast<char*>(base);
-  w.bitmap_words = (int)(((size_t)E_cap + 31) / 32);
-  w.summary_words = (w.bitmap_words + 31) / 32;
   w.hist = reinterpret_cast<int*>(p);
   p += (size_t)rows * kTopkBins * 4;
   w.ctr = reinterpret_cast<int*>(p);
   p += (size_t)rows * 16;
-  w.bitmap = reinterpret_cast<uint32_t*>(p);
-  p += (size_t)rows * w.bitmap_words * 4;
-  w.summary = reinterpret_cast<uint32_t*>(p);
-  p += (size_t)rows * w.summary_words * 4;
   p = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(p) + 15) & ~uintptr_t(15));
-  w.cand = with_cand ? reinterpret_cast<uint2*>(p) : nullptr;
+  w.cand = split ? reinterpret_cast<uint2*>(p) : nullptr;
+  if (split) p += (size_t)rows * kTopkCandCap * 8;
+  w.sure = split ? reinterpret_cast<int*>(p) : nullptr;
   return w;
 }
 
-static size_t topk_lds_bytes() { return sizeof(Lds); }
+template <typename K>
+static hipError_t allow_lds(K kernel, size_t bytes, size_t* done) {
+  if (*done >= bytes) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) *done = bytes;
+  return e;
+}
 
 hipError_t launch_topk_collect(const IndexArgs& a, const TopkWs& ws, int slices, int slice_len,
                                hipStream_t s) {
-  CSA_LAUNCH("topk_collect", topk_collect_kernel, dim3(slices, a.B * a.Tq), dim3(kT), 0, s, a, ws,
+  CSA_LAUNCH("topk_collect", topk_collect_kernel, dim3(slices, a.B * a.Tq), dim3(kCT), 0, s, a, ws,
              slice_len);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = topk_lds_bytes() + (size_t)(ws.bitmap_words + ws.summary_words) * 4;
-  static int attr2 = 0;
-  if (attr2 < (int)lds) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_resolve_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr2 = (int)lds;
-  }
-  CSA_LAUNCH("topk_resolve", topk_resolve_kernel, dim3(a.B * a.Tq), dim3(kT), lds, s, a, ws);
+  static size_t lds_set = 0;
+  e = allow_lds(topk_resolve_kernel, sizeof(Lds), &lds_set);
+  if (e != hipSuccess) return e;
+  CSA_LAUNCH("topk_resolve", topk_resolve_kernel, dim3(a.B * a.Tq), dim3(kRT), sizeof(Lds), s, a, ws);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_rows(const IndexArgs& a, const TopkWs& ws, hipStream_t s) {
-  const size_t lds = topk_split_lds_bytes(a.E_cap);
-  static int attr_set = 0;
-  if (attr_set < (int)lds) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&topk_rowsel_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr_set = (int)lds;
-  }
-  CSA_LAUNCH("topk_rows", topk_rowsel_kernel, dim3(a.B * a.Tq), dim3(kT), lds, s, a, ws);
+  static size_t lds_set = 0;
+  hipError_t e = allow_lds(topk_rowsel_kernel, sizeof(Lds), &lds_set);
+  if (e != hipSuccess) return e;
+  CSA_LAUNCH("topk_rows", topk_rowsel_kernel, dim3(a.B * a.Tq), dim3(kRT), sizeof(Lds), s, a, ws);
   return hipGetLastError();
 }
 
