@@ -48,16 +48,18 @@ namespace {
 
 constexpr int kC = 512;        // entry / head dim
 constexpr int kHW = 64;        // heads per workgroup (16 per wavefront)
-constexpr int kTN = 64;        // rows per LDS tile
+constexpr int kTN = 32;        // rows per LDS tile
+constexpr int kRing = 4;       // LDS tile slots: kRing - 1 tiles in flight while one is computed
 constexpr int kRowB = kC * 2;  // bytes per row
 constexpr int kMaxSparseRows = 2304;  // k + n_win <= 2048 + 256
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSlack = 20.f;  // log2 headroom of the weights over the reference max
 
-// s_waitcnt vmcnt(0), lgkmcnt / expcnt not waited (gfx9 encoding: vmcnt in
+// s_waitcnt vmcnt(N), lgkmcnt / expcnt not waited (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-constexpr int kWaitVm0 = 0x0F70;
+constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kRowsPerWave = kTN / 4;  // DMA instructions per wave and tile
 
 CSA_DEV f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -89,14 +91,6 @@ CSA_DEV void dma_row(const uint16_t* src_row, char* lds_row, int lane, int sw) {
       (void __attribute__((address_space(3)))*)(lds_row), 16, 0, 0);
 }
 
-CSA_DEV int64_t rows_compressed(const AttendArgs& a, int b, int qrow, int64_t t) {
-  if (!a.dense) return a.topk_cnt[qrow];
-  const int64_t lim = vis_limit(t, a.m, a.vis);
-  const int64_t have = (int64_t)a.n_entries[b] + a.n_add;
-  int64_t n = lim < have ? lim : have;
-  if (n > a.E_cap) n = a.E_cap;
-  return n < 0 ? 0 : n;
-}
 
 }  // namespace
 
@@ -105,9 +99,9 @@ CSA_DEV int64_t rows_compressed(const AttendArgs& a, int b, int qrow, int64_t t)
 template <bool kDense>
 __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n_split,
                                                              int rows_per_split) {
-  __shared__ __attribute__((aligned(1024))) char tiles[2][kTN * kRowB];
+  __shared__ __attribute__((aligned(1024))) char tiles[kRing][kTN * kRowB];
   __shared__ int rsrc[kMaxSparseRows];  // sparse: cache entry per row of the split (-1: none)
-  __shared__ uint32_t rvalid[2][kTN / 4];  // byte r % 4 of word r / 4: row r is a real row
+  __shared__ uint32_t rvalid[kRing][kTN / 4];  // byte r % 4 of word r / 4: row r is a real row
   __shared__ int s_restart;                // a wavefront asks the split to be recomputed
 
   const int n_hg = a.H / kHW;
@@ -122,22 +116,60 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int H = a.H;
   const int h0 = hg * kHW + 16 * w;  // this wavefront's first head
-  const int64_t t = a.q_pos ? a.q_pos[qrow] : a.q_pos0 + qrow % a.Tq;
-  const int64_t n_c = rows_compressed(a, b, qrow, t);
+
+  // Everything that depends only on the block index is requested at once:
+  // the query operands (vector loads) and the position, row count and window
+  // base (scalar loads), so the start-up costs one memory round trip.
+  // Q^T operands for this wavefront's 16 heads: lane (head li, d group lg).
+  bf16x8_t qf[16];
+  {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)qrow * H + h0 + li) * kC + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(q + 32 * ks);
+  }
+  // (unconditional loads: an absent optional array is replaced by a valid
+  // dummy address and the value discarded, so the three loads are in flight
+  // together instead of one branch and wait each)
+  const int64_t* dummy64 = reinterpret_cast<const int64_t*>(a.kv);
+  const int64_t t_ld = (a.q_pos ? a.q_pos + qrow : dummy64)[0];
+  const int64_t w_ld = (a.win_pos0 ? a.win_pos0 + b : dummy64)[0];
+  const int32_t cnt = kDense ? a.n_entries[b] : a.topk_cnt[qrow];
+  // all three are needed right away; one wait covers them (the empty asm
+  // keeps the compiler from sinking a load below later arithmetic)
+  __asm__ __volatile__("" ::"s"(t_ld), "s"(w_ld), "s"(cnt));
+  const int64_t t = a.q_pos ? t_ld : a.q_pos0 + qrow % a.Tq;
+  const int64_t wpos0 = a.win_pos0 ? w_ld : a.win_pos0_const;
+  int64_t n_c;
+  if (kDense) {
+    const int64_t lim = vis_limit(t, a.m, a.vis);
+    const int64_t have = (int64_t)cnt + a.n_add;
+    n_c = lim < have ? lim : have;
+    if (n_c > a.E_cap) n_c = a.E_cap;
+    if (n_c < 0) n_c = 0;
+  } else {
+    n_c = cnt;
+  }
   const int64_t n_w = (t + 1) < a.n_win ? (t + 1) : a.n_win;
   const int64_t n_rows = n_c + n_w;
   const int r_begin = split * rows_per_split;
   const int r_end = (int)((int64_t)r_begin + rows_per_split < n_rows ? r_begin + rows_per_split : n_rows);
   const int nc32 = (int)n_c;
-  const int64_t wpos0 = a.win_pos0 ? a.win_pos0[b] : a.win_pos0_const;
   const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv) + (size_t)b * a.E_cap * kC;
   const uint16_t* win = reinterpret_cast<const uint16_t*>(a.win) + (size_t)b * a.W_cap * kC;
   const float sc2 = a.scale * kLog2e;
   // ring row of the first window position; later window rows follow with
-  // one conditional wrap (n_win <= W_cap)
-  int64_t wb = (t - n_w + 1 - wpos0) % a.W_cap;
-  if (wb < 0) wb += a.W_cap;
-  const int wbase = (int)wb, wcap = a.W_cap;
+  // one conditional wrap (n_win <= W_cap).  32-bit remainder when the
+  // offset fits (always, for positions below 2^31).
+  const int64_t wofs = t - n_w + 1 - wpos0;
+  int wbase;
+  if (wofs >= 0 && wofs < 0x7fffffff) {
+    wbase = (int)((uint32_t)wofs % (uint32_t)a.W_cap);
+  } else {
+    int64_t wb = wofs % a.W_cap;
+    if (wb < 0) wb += a.W_cap;
+    wbase = (int)wb;
+  }
+  const int wcap = a.W_cap;
   // the query's own window row: always present, the source of padding rows
   // (their logits are masked)
   int own = wbase + (int)n_w - 1;
@@ -176,33 +208,31 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     *ok = true;
     return win + (size_t)wr * kC;
   };
-  // wave w fetches rows 16w .. 16w+15 of a tile; every wave reads all rows
+  // wave w fetches rows kRowsPerWave * w .. of a tile; every wave reads all rows
   auto issue_tile = [&](int r0, int buf) {
     uint32_t vw = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 16 * w + i;
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int r = kRowsPerWave * w + i;
       bool ok;
       const uint16_t* src = row_src(r0 + r, &ok);
-      dma_row(src, tiles[buf] + r * kRowB, l, swz(i));
+      dma_row(src, tiles[buf] + r * kRowB, l, swz(r & 15));
       vw |= (uint32_t)ok << (8 * (i & 3));
       if ((i & 3) == 3) {
-        if (l == 0) rvalid[buf][4 * w + (i >> 2)] = vw;
+        if (l == 0) rvalid[buf][r >> 2] = vw;
         vw = 0;
       }
     }
   };
 
-  // DMA of the first tile goes out before the Q loads
-  if (r_begin < r_end) issue_tile(r_begin, 0);
-
-  // Q^T operands for this wavefront's 16 heads: lane (head li, d group lg)
-  bf16x8_t qf[16];
-  {
-    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)qrow * H + h0 + li) * kC + 8 * lg;
+  // the first kRing - 1 tiles (the query operands, loaded earlier, are
+  // older, so waiting for a tile also covers them)
+  auto prologue = [&]() {
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(q + 32 * ks);
-  }
+    for (int j = 0; j < kRing - 1; ++j)
+      if (r_begin + j * kTN < r_end) issue_tile(r_begin + j * kTN, j);
+  };
+  prologue();
 
   // running softmax state: the reference max per head (identical in the 4
   // lane groups), the sum per lane over its own rows, O^T[512 d x 16 heads]
@@ -227,20 +257,21 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
 
   auto compute_tile = [&](int buf) {
     const char* T = tiles[buf];
-    // S^T[64 rows x 16 heads] = K . Q^T as four 16-row blocks
-    // (the four block chains interleave, so consecutive MFMAs are independent)
-    f32x4_t s[4];
+    // S^T[32 rows x 16 heads] = K . Q^T as two 16-row blocks
+    // (the block chains interleave, so consecutive MFMAs are independent)
+    constexpr int kRB = kTN / 16;
+    f32x4_t s[kRB];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) s[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < kRB; ++rb) s[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks)
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+      for (int rb = 0; rb < kRB; ++rb)
         s[rb] = mfma(lds8(T + s_base[ks & 3] + rb * 16 * kRowB + 256 * (ks >> 2)), qf[ks], s[rb]);
     // keep 12 fragment reads in flight ahead of the MFMAs (lgkmcnt counts 15)
     __builtin_amdgcn_sched_group_barrier(0x100, 12, 1);
 #pragma unroll
-    for (int i = 0; i < 52; ++i) {
+    for (int i = 0; i < 16 * kRB - 12; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
     }
@@ -252,10 +283,10 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     // rescaled.  A larger jump raises the reference and asks for the split
     // to be recomputed from its first row (at most once: the second pass
     // starts from the largest max of the first).
-    float x[4][4];
+    float x[kRB][4];
     float mx = -INFINITY;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       const uint32_t fl = rvalid[buf][4 * rb + lg];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -268,9 +299,9 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     const bool jump = m_run != -INFINITY && mx > m_run + kSlack;
     if (__builtin_amdgcn_ballot_w64(jump) != 0ull && l == 0) s_restart = 1;
     if (m_run == -INFINITY || jump) m_run = mx;  // no weight so far, or a pass to be redone
-    bf16x4_t pb[4];
+    bf16x4_t pb[kRB];
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
+    for (int rb = 0; rb < kRB; ++rb) {
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -281,7 +312,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     }
     // O^T[d x heads] += V^T[d x 32 rows] . P^T[32 rows x heads] per row pair
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
+    for (int pr = 0; pr < kRB / 2; ++pr) {
       const bf16x8_t pB = __builtin_shufflevector(pb[2 * pr], pb[2 * pr + 1], 0, 1, 2, 3, 4, 5, 6, 7);
       const char* vp = T + pr * 32 * kRowB;
 #pragma unroll
@@ -293,24 +324,31 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     // keep 7 MFMAs' worth of transpose reads in flight
     __builtin_amdgcn_sched_group_barrier(0x100, 14, 2);
 #pragma unroll
-    for (int i = 0; i < 57; ++i) {
+    for (int i = 0; i < 32 * (kRB / 2) - 7; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 7, 2);
   };
 
-  // double-buffered loop, one barrier per tile: after the barrier every
-  // wave's DMAs of tile i have landed and every wave has finished tile i-1,
-  // so tile i+1 may be fetched into that buffer while tile i is computed.
+  // ring of kRing tile slots, one barrier per tile: a wave first waits for
+  // its own DMAs of tile i (the younger tiles i+1, i+2 may stay in flight);
+  // after the barrier every wave's DMAs of tile i have landed and every wave
+  // has finished tile i-1, so tile i+kRing-1 may be fetched into that slot
+  // while tile i is computed.
+  static_assert(kRing == 4, "the waits below assume two younger tiles");
   for (;;) {
     int buf = 0;
     for (int r0 = r_begin; r0 < r_end; r0 += kTN) {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      const int younger = (r_end - r0 - 1) / kTN;  // tiles after this one
+      if (younger >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * kRowsPerWave));
+      else if (younger == 1) __builtin_amdgcn_s_waitcnt(wait_vm(kRowsPerWave));
+      else __builtin_amdgcn_s_waitcnt(wait_vm(0));
       lds_barrier();
-      if (r0 + kTN < r_end) issue_tile(r0 + kTN, buf ^ 1);
+      const int rn = r0 + (kRing - 1) * kTN;
+      if (rn < r_end) issue_tile(rn, (buf + kRing - 1) & (kRing - 1));
       compute_tile(buf);
-      buf ^= 1;
+      buf = (buf + 1) & (kRing - 1);
     }
     lds_barrier();
     const int again = s_restart;
@@ -321,7 +359,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     l_lane = 0.f;
-    issue_tile(r_begin, 0);
+    prologue();
   }
 
   // per-head sum over the four lane groups
@@ -330,36 +368,36 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   Lh += __shfl_xor(Lh, 32, 64);
   const int h = h0 + li;
 
-  // lane (head li) holds d = 16dt + 4lg + i
+  // Output rows leave through LDS so that every store instruction writes one
+  // contiguous 1 KB row: lane (head li) holds d = 16dt + 4lg + i of O^T; it
+  // writes them scaled and rounded to row li of its wavefront's [16][520]
+  // bf16 staging block (row stride 1040 B keeps the 8-byte writes of 32
+  // lanes on distinct banks), then lane l copies 16 bytes of each row.
+  float f;  // output scale for this lane's head
+  uint16_t* dst_row0;  // row of this wavefront's first head
+  const size_t ostride = kC;
   if (n_split == 1) {
     const float z2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
     const float M = fmaxf(m_run, z2);
     const float em = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
     const float den = Lh * em + (z2 == -INFINITY ? 0.f : exp2f(z2 - M));
-    const float f = em / den;
+    f = em / den;
     if (a.lse && lg == 0) a.lse[(size_t)qrow * H + h] = (M + log2f(den)) * kLn2;
-    uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * H + h) * kC + 4 * lg;
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      ushort4 v;
-      v.x = f32_to_bf16(acc[dt][0] * f);
-      v.y = f32_to_bf16(acc[dt][1] * f);
-      v.z = f32_to_bf16(acc[dt][2] * f);
-      v.w = f32_to_bf16(acc[dt][3] * f);
-      *reinterpret_cast<ushort4*>(o + 16 * dt) = v;
+    dst_row0 = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * H + h0) * kC;
+  } else {
+    // partial: (m, L) and O / L in bf16
+    float* pml = reinterpret_cast<float*>(a.ws);
+    uint16_t* po = reinterpret_cast<uint16_t*>(pml + (size_t)a.B * a.Tq * n_split * H * 2);
+    const size_t slot = ((size_t)qrow * n_split + split) * H + h;
+    if (lg == 0) {
+      pml[2 * slot] = m_run;
+      pml[2 * slot + 1] = Lh;
     }
-    return;
+    f = Lh > 0.f ? 1.f / Lh : 0.f;
+    dst_row0 = po + (((size_t)qrow * n_split + split) * H + h0) * kC;
   }
-  // partial: (m, L) and O / L in bf16
-  float* pml = reinterpret_cast<float*>(a.ws);
-  uint16_t* po = reinterpret_cast<uint16_t*>(pml + (size_t)a.B * a.Tq * n_split * H * 2);
-  const size_t slot = ((size_t)qrow * n_split + split) * H + h;
-  if (lg == 0) {
-    pml[2 * slot] = m_run;
-    pml[2 * slot + 1] = Lh;
-  }
-  const float f = Lh > 0.f ? 1.f / Lh : 0.f;
-  uint16_t* o = po + slot * kC + 4 * lg;
+  constexpr int kOutLD = kC + 8;  // staging row stride (elements)
+  uint16_t* stage = reinterpret_cast<uint16_t*>(tiles[0]) + w * 16 * kOutLD;
 #pragma unroll
   for (int dt = 0; dt < 32; ++dt) {
     ushort4 v;
@@ -367,8 +405,13 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     v.y = f32_to_bf16(acc[dt][1] * f);
     v.z = f32_to_bf16(acc[dt][2] * f);
     v.w = f32_to_bf16(acc[dt][3] * f);
-    *reinterpret_cast<ushort4*>(o + 16 * dt) = v;
+    *reinterpret_cast<ushort4*>(stage + li * kOutLD + 16 * dt + 4 * lg) = v;
   }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wavefront's LDS writes (lgkmcnt 0)
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    *reinterpret_cast<uint4*>(dst_row0 + r * ostride + 8 * l) =
+        *reinterpret_cast<const uint4*>(stage + r * kOutLD + 8 * l);
 }
 
 // grid (B*Tq, H), 256 threads: wavefront w merges splits w, w+4, ... of one
