@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
 
-SOURCES = ["api.cpp", "profile.cpp", "compress.hip", "indexer.hip", "attend.hip", "attend_mfma.hip", "indexer_mfma.hip", "topk.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "compress.hip", "indexer.hip", "attend.hip", "attend_mfma.hip", "attend_rows.hip", "indexer_mfma.hip", "topk.hip"]
 
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 
@@ -29,10 +29,12 @@ FLAGS = [
 ]
 
 
-# per-source extra flags: the indexer scan keeps its MFMA results in VGPRs
+# per-source extra flags.  The indexer scan keeps its MFMA results in VGPRs
 # (its in-lane epilogue reads every result; accumulation registers would
-# need a copy per value)
-EXTRA = {"indexer_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# need a copy per value).
+EXTRA = {"indexer_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         # LDS reads clustered ahead of the products that consume them
+         "attend_rows.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
 
 
 def hipcc():

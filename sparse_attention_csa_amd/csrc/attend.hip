@@ -158,22 +158,36 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
   }
 }
 
-bool attend_mfma_supported(const AttendArgs& a);
 bool attend_mfma_shape_ok(int H, int c);
 size_t attend_mfma_ws_bytes(int BT, int H, int rows_max);
 hipError_t launch_attend_mfma(const AttendArgs& a, int rows_max, hipStream_t s);
+bool attend_rows_shape_ok(int H, int c);
+void attend_rows_plan(int BT, int H, int rows_max, int* n_split, int* rows_per_split);
+hipError_t launch_attend_rows(const AttendArgs& a, int rows_max, hipStream_t s);
+
+// partial (max, sum) pairs and bf16 outputs of the row splits
+static size_t split_ws_bytes(int BT, int H, int c, int n_split) {
+  if (n_split <= 1) return 0;
+  return (size_t)BT * n_split * H * (2 * sizeof(float) + (size_t)c * 2);
+}
 
 size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max) {
-  size_t n = 256;
-  if (attend_mfma_shape_ok(H, c)) n += attend_mfma_ws_bytes(B * Tq, H, rows_max);
-  return n;
+  size_t n = 256, extra = 0;
+  if (attend_mfma_shape_ok(H, c)) extra = attend_mfma_ws_bytes(B * Tq, H, rows_max);
+  if (attend_rows_shape_ok(H, c)) {
+    int ns, rps;
+    attend_rows_plan(B * Tq, H, rows_max, &ns, &rps);
+    const size_t r = split_ws_bytes(B * Tq, H, c, ns);
+    if (r > extra) extra = r;
+  }
+  return n + extra;
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
-  if (attend_mfma_supported(a)) {
-    const int rows_max = (a.dense ? a.E_cap : a.k) + a.n_win;
-    return launch_attend_mfma(a, rows_max, s);
-  }
+  if (a.dtype == BF16 && a.dense && attend_mfma_shape_ok(a.H, a.c))
+    return launch_attend_mfma(a, a.E_cap + a.n_win, s);
+  if (a.dtype == BF16 && !a.dense && attend_rows_shape_ok(a.H, a.c))
+    return launch_attend_rows(a, a.k + a.n_win, s);
   dim3 grid(a.B * a.Tq, (a.H + kHG - 1) / kHG), block(256);
   const size_t sh = sizeof(float) * ((size_t)kHG * a.c + (size_t)kTile * (a.c + 1) + kHG * kTile + kHG + kTile);
   if (a.dtype == F32)

@@ -1,25 +1,20 @@
-// Shared-KV attention on MFMA (bf16, entry dim 512): rows a4 / a5 / a6.
+// Dense (HCA) shared-KV attention on MFMA (bf16, entry dim 512): rows a5 +
+// a6 of the hot path.
 //
-// What it computes is the same as the generic kernel: for a query at position
-// t and every head h, one softmax over the compressed rows (top-k set or all
-// visible entries) and the window rows, with exp(sink_h) in the denominator
-// ("DeepSeek-V4" book ch. 6 "Shared key-value MQA", ch. 7 "The sliding
-// window" and "Attention sinks"; "2026 DeepSeek-V4" note, concat(selected,
-// local_kv)).  Every row is both key and value.
+// What it computes is the generic kernel's result: for a query at position t
+// and every head h, one softmax over all visible compressed entries and the
+// window rows, with exp(sink_h) in the denominator ("DeepSeek-V4" book ch. 6
+// "Shared key-value MQA", ch. 7 "The sliding window" and "Attention sinks").
+// Every row is both key and value.
 //
 // Work split.  A workgroup (4 wavefronts, one per SIMD, the whole register
 // file) owns one query, 64 heads (16 per wavefront) and a contiguous range of
 // its rows ("split"); the splits of one query are merged by
 // attend_merge_kernel with the online-softmax rule.  Every wavefront consumes
 // every row of a tile, so a row crosses HBM / L2 into LDS once per split, not
-// once per head group.  Row tiles of 64 rows (64 KB) are fetched into LDS by
-// direct global-to-LDS DMA (one 1 KB row per wave instruction), double
-// buffered: tile i+1 is in flight while tile i is computed.
-//
-// LDS layout.  Rows are unpadded (1 KB); the 16-byte chunk g of tile row r is
-// stored at chunk position g ^ swz(r % 16).  The DMA applies the permutation
-// by choosing which global chunk each lane fetches.  swz makes both LDS read
-// patterns below free of bank conflicts (checked for 32 and 64 banks).
+// once per head group.  Row tiles of 32 rows (32 KB) are fetched into LDS by
+// direct global-to-LDS DMA (one 1 KB row per wave instruction) into a ring of
+// four slots: three tiles are in flight while one is computed.
 //
 // Tied K = V on MFMA.  The score product is computed transposed,
 //   S^T[rows x heads] = K[rows x d] . Q^T[d x heads]   (v_mfma 16x16x32 bf16),
@@ -33,74 +28,26 @@
 // transpose read (ds_read_b64_tr_b16), whose per-lane addresses implement
 // that permutation.  Softmax runs in base 2.
 
-#include "common.h"
 #include "kernels.h"
+#include "mfma_tile.h"
 
 namespace csa {
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+using namespace tile;
 
 namespace {
 
-constexpr int kC = 512;        // entry / head dim
-constexpr int kHW = 64;        // heads per workgroup (16 per wavefront)
-constexpr int kTN = 32;        // rows per LDS tile
-constexpr int kRing = 4;       // LDS tile slots: kRing - 1 tiles in flight while one is computed
-constexpr int kRowB = kC * 2;  // bytes per row
-constexpr int kMaxSparseRows = 2304;  // k + n_win <= 2048 + 256
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kSlack = 20.f;  // log2 headroom of the weights over the reference max
-
-// s_waitcnt vmcnt(N), lgkmcnt / expcnt not waited (gfx9 encoding: vmcnt in
-// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kHW = 64;                // heads per workgroup (16 per wavefront)
+constexpr int kTN = 32;                // rows per LDS tile
+constexpr int kRing = 4;               // LDS tile slots: kRing - 1 tiles in flight while one is computed
 constexpr int kRowsPerWave = kTN / 4;  // DMA instructions per wave and tile
-
-CSA_DEV f32x4_t mfma(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-CSA_DEV bf16x8_t lds8(const char* p) { return *reinterpret_cast<const bf16x8_t*>(p); }
-
-CSA_DEV i16x4_t ld_tr(const char* p) {
-  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-}
-
-CSA_DEV bf16x8_t cat8(i16x4_t a, i16x4_t b) {
-  i16x8_t v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8_t, v);
-}
-
-// chunk permutation of a tile row (r % 16): a bijection on 0..15 with
-//   bits 0..3 = r2, r0, r1, r2 ^ r3
-CSA_DEV int swz(int r) {
-  return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2) | ((((r >> 2) ^ (r >> 3)) & 1) << 3);
-}
-
-// one lane's 16 bytes of a 1 KB row: global chunk (lane ^ sw) lands at LDS
-// chunk lane of the row
-CSA_DEV void dma_row(const uint16_t* src_row, char* lds_row, int lane, int sw) {
-  __builtin_amdgcn_global_load_lds(
-      (const void __attribute__((address_space(1)))*)(src_row + 8 * (lane ^ sw)),
-      (void __attribute__((address_space(3)))*)(lds_row), 16, 0, 0);
-}
-
 
 }  // namespace
 
 // 1-D grid: block L runs on XCD L % 8; the n_hg head groups of one (query,
 // split) are blocks L, L + 8, ... so they share that XCD's L2.
-template <bool kDense>
-__global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n_split,
-                                                             int rows_per_split) {
+__global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n_split, int rows_per_split) {
   __shared__ __attribute__((aligned(1024))) char tiles[kRing][kTN * kRowB];
-  __shared__ int rsrc[kMaxSparseRows];  // sparse: cache entry per row of the split (-1: none)
   __shared__ uint32_t rvalid[kRing][kTN / 4];  // byte r % 4 of word r / 4: row r is a real row
   __shared__ int s_restart;                // a wavefront asks the split to be recomputed
 
@@ -113,13 +60,15 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   if (qrow >= a.B * a.Tq) return;
 
   const int b = qrow / a.Tq;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
+  const int tid = threadIdx.x, l = tid & 63, li = l & 15, lg = l >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H;
   const int h0 = hg * kHW + 16 * w;  // this wavefront's first head
 
-  // Everything that depends only on the block index is requested at once:
-  // the query operands (vector loads) and the position, row count and window
-  // base (scalar loads), so the start-up costs one memory round trip.
+  // Everything that depends only on the block index is requested at once
+  // and awaited together (one memory round trip): the query operands and
+  // the position, entry count and window base.  After that the row DMAs are
+  // the only memory operations in flight, so the waits below count DMAs.
   // Q^T operands for this wavefront's 16 heads: lane (head li, d group lg).
   bf16x8_t qf[16];
   {
@@ -133,22 +82,16 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   const int64_t* dummy64 = reinterpret_cast<const int64_t*>(a.kv);
   const int64_t t_ld = (a.q_pos ? a.q_pos + qrow : dummy64)[0];
   const int64_t w_ld = (a.win_pos0 ? a.win_pos0 + b : dummy64)[0];
-  const int32_t cnt = kDense ? a.n_entries[b] : a.topk_cnt[qrow];
-  // all three are needed right away; one wait covers them (the empty asm
-  // keeps the compiler from sinking a load below later arithmetic)
-  __asm__ __volatile__("" ::"s"(t_ld), "s"(w_ld), "s"(cnt));
+  const int32_t cnt = a.n_entries[b];
+  __builtin_amdgcn_s_waitcnt(0);
+  __asm__ __volatile__("" ::"s"(t_ld), "s"(w_ld), "s"(cnt), "v"(qf[0]), "v"(qf[15]));
   const int64_t t = a.q_pos ? t_ld : a.q_pos0 + qrow % a.Tq;
   const int64_t wpos0 = a.win_pos0 ? w_ld : a.win_pos0_const;
-  int64_t n_c;
-  if (kDense) {
-    const int64_t lim = vis_limit(t, a.m, a.vis);
-    const int64_t have = (int64_t)cnt + a.n_add;
-    n_c = lim < have ? lim : have;
-    if (n_c > a.E_cap) n_c = a.E_cap;
-    if (n_c < 0) n_c = 0;
-  } else {
-    n_c = cnt;
-  }
+  const int64_t lim = vis_limit(t, a.m, a.vis);
+  const int64_t have = (int64_t)cnt + a.n_add;
+  int64_t n_c = lim < have ? lim : have;
+  if (n_c > a.E_cap) n_c = a.E_cap;
+  if (n_c < 0) n_c = 0;
   const int64_t n_w = (t + 1) < a.n_win ? (t + 1) : a.n_win;
   const int64_t n_rows = n_c + n_w;
   const int r_begin = split * rows_per_split;
@@ -176,32 +119,15 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   if (own >= wcap) own -= wcap;
   const uint16_t* pad_row = win + (size_t)own * kC;
 
-  if (!kDense) {
-    const int32_t* ids = a.topk_idx + (size_t)qrow * a.k;
-    for (int j = r_begin + tid; j < r_end; j += 256) {
-      int e = -1;
-      if (j < nc32) {
-        const int32_t v = ids[j];
-        e = (v >= 0 && v < a.E_cap) ? v : -1;
-      }
-      rsrc[j - r_begin] = e;
-    }
-  }
   if (tid == 0) s_restart = 0;
-  __syncthreads();  // rsrc, s_restart ready
+  __syncthreads();  // s_restart ready
 
   auto row_src = [&](int j, bool* ok) -> const uint16_t* {
     *ok = false;
     if (j >= r_end) return pad_row;
     if (j < nc32) {
-      if (kDense) {
-        *ok = true;
-        return kv + (size_t)j * kC;
-      }
-      const int e = rsrc[j - r_begin];
-      if (e < 0) return pad_row;
       *ok = true;
-      return kv + (size_t)e * kC;
+      return kv + (size_t)j * kC;
     }
     int wr = wbase + (j - nc32);
     if (wr >= wcap) wr -= wcap;
@@ -216,7 +142,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
       const int r = kRowsPerWave * w + i;
       bool ok;
       const uint16_t* src = row_src(r0 + r, &ok);
-      dma_row(src, tiles[buf] + r * kRowB, l, swz(r & 15));
+      dma_row_m0(src, lds_addr(tiles[buf] + r * kRowB), l, swz(r & 15));
       vw |= (uint32_t)ok << (8 * (i & 3));
       if ((i & 3) == 3) {
         if (l == 0) rvalid[buf][r >> 2] = vw;
@@ -225,8 +151,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     }
   };
 
-  // the first kRing - 1 tiles (the query operands, loaded earlier, are
-  // older, so waiting for a tile also covers them)
+  // the first kRing - 1 tiles
   auto prologue = [&]() {
 #pragma unroll
     for (int j = 0; j < kRing - 1; ++j)
@@ -241,19 +166,10 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_lane = 0.f;
 
-  // per-lane LDS byte offsets.  Score reads: row li of a 16-row block,
-  // chunk 4ks + lg, i.e. byte (64 ks) ^ s_x with s_x < 256, which is
-  // 256 (ks / 4) + ((64 (ks % 4)) ^ s_x): four per-lane bases, the rest is an
-  // immediate offset.  Transpose reads: row 4lg + li/4, d 16dt + 4(li%4),
-  // byte (32 dt) ^ t_x = 256 (dt / 8) + ((32 (dt % 8)) ^ t_x): eight bases.
-  const int s_x = 16 * (lg ^ swz(li));
-  const int tr_row = 4 * lg + (li >> 2);
-  const int t_x = 16 * (((li >> 1) & 1) ^ swz(tr_row));
-  int s_base[4], t_base[8];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) s_base[u] = li * kRowB + ((64 * u) ^ s_x);
-#pragma unroll
-  for (int u = 0; u < 8; ++u) t_base[u] = tr_row * kRowB + 8 * (li & 1) + ((32 * u) ^ t_x);
+  // per-lane LDS byte offsets of the score and value reads
+  const Bases bs = lane_bases(li, lg);
+  const int* s_base = bs.s;
+  const int* t_base = bs.t;
 
   auto compute_tile = [&](int buf) {
     const char* T = tiles[buf];
@@ -267,7 +183,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     for (int ks = 0; ks < 16; ++ks)
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb)
-        s[rb] = mfma(lds8(T + s_base[ks & 3] + rb * 16 * kRowB + 256 * (ks >> 2)), qf[ks], s[rb]);
+        s[rb] = mfma32(lds8(T + s_base[ks & 3] + rb * 16 * kRowB + 256 * (ks >> 2)), qf[ks], s[rb]);
     // keep 12 fragment reads in flight ahead of the MFMAs (lgkmcnt counts 15)
     __builtin_amdgcn_sched_group_barrier(0x100, 12, 1);
 #pragma unroll
@@ -318,7 +234,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
 #pragma unroll
       for (int dt = 0; dt < 32; ++dt) {
         const char* v0 = vp + t_base[dt & 7] + 256 * (dt >> 3);
-        acc[dt] = mfma(cat8(ld_tr(v0), ld_tr(v0 + 16 * kRowB)), pB, acc[dt]);
+        acc[dt] = mfma32(cat8(ld_tr(v0), ld_tr(v0 + 16 * kRowB)), pB, acc[dt]);
       }
     }
     // keep 7 MFMAs' worth of transpose reads in flight
@@ -486,8 +402,6 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
 
 bool attend_mfma_shape_ok(int H, int c) { return c == kC && H % kHW == 0; }
 
-bool attend_mfma_supported(const AttendArgs& a) { return a.dtype == BF16 && attend_mfma_shape_ok(a.H, a.c); }
-
 // Row splits per (query, head group): about one workgroup per CU (256), each
 // split a multiple of 16 rows, at most kMaxSplit splits.
 void attend_mfma_plan(int BT, int H, int rows_max, int* n_split, int* rows_per_split) {
@@ -508,22 +422,26 @@ size_t attend_mfma_ws_bytes(int BT, int H, int rows_max) {
   return (size_t)BT * ns * H * (2 * sizeof(float) + kC * sizeof(uint16_t));
 }
 
+hipError_t launch_attend_merge(const AttendArgs& a, int n_split, hipStream_t s);
+
 hipError_t launch_attend_mfma(const AttendArgs& a, int rows_max, hipStream_t s) {
   int ns, rps;
   attend_mfma_plan(a.B * a.Tq, a.H, rows_max, &ns, &rps);
-  if (!a.dense && rps > kMaxSparseRows) return hipErrorInvalidValue;
   const int n_hg = a.H / kHW;
   const long long units = (long long)ns * a.B * a.Tq;       // (query, split) pairs
   const long long blocks = (units + 7) / 8 * 8 * n_hg;      // padded to whole XCD rounds
-  if (a.dense)
-    CSA_LAUNCH("attend_dense_mfma", attend_mfma_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
-  else
-    CSA_LAUNCH("attend_sparse_mfma", attend_mfma_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+  CSA_LAUNCH("attend_dense_mfma", attend_mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
   if (ns > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    CSA_LAUNCH("attend_merge", attend_merge_kernel, dim3(a.B * a.Tq, a.H), dim3(256), 0, s, a, ns);
+    return launch_attend_merge(a, ns, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attend_merge(const AttendArgs& a, int n_split, hipStream_t s) {
+  if (n_split > kMaxSplit) return hipErrorInvalidValue;
+  CSA_LAUNCH("attend_merge", attend_merge_kernel, dim3(a.B * a.Tq, a.H), dim3(256), 0, s, a, n_split);
   return hipGetLastError();
 }
 
