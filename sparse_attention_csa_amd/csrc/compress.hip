@@ -199,6 +199,9 @@ CSA_DEV void unpack16(const uint4 u, const float*, float* o) {
 // the value of coordinate r0 + tid for tid < W.  Sources: branch a is tokens
 // e*m .. e*m+m-1 (streams 0, 1), branch b (use_b) tokens (e-1)*m .. e*m-1
 // (streams 2, 3); token p is ring slot p % R, the new token t comes from io.
+// Each thread folds its U sources per coordinate with one rescale; the G
+// partial states of a coordinate then merge across lanes (xor shuffles
+// within a wavefront) and across the four wavefronts (LDS).
 template <typename T>
 CSA_DEV float fold_job(const T* tail, const T* io, int d, int r0, int W, int m, int R, int64_t t,
                        int64_t e, bool use_b, const float* ba, const float* bb, Soft* s_part) {
@@ -251,25 +254,53 @@ CSA_DEV float fold_job(const T* tail, const T* io, int d, int r0, int W, int m, 
         }
       }
     }
+    float z[U][V], x[U][V];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      if (j0 + u * G < nsrc) {
-        float z[V], x[V];
-        unpack16(zr[u], (const T*)nullptr, z);
-        unpack16(xr[u], (const T*)nullptr, x);
+      const bool ok = j0 + u * G < nsrc;
+      unpack16(zr[u], (const T*)nullptr, z[u]);
+      unpack16(xr[u], (const T*)nullptr, x[u]);
 #pragma unroll
-        for (int v = 0; v < V; ++v) soft_push(st[v], z[v] + bz[u][v], x[v]);
+      for (int v = 0; v < V; ++v) z[u][v] = ok ? z[u][v] + bz[u][v] : -INFINITY;
+    }
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float mx = st[v].mx;
+#pragma unroll
+      for (int u = 0; u < U; ++u) mx = fmaxf(mx, z[u][v]);
+      if (mx == -INFINITY) continue;  // no source here yet
+      const float r = __expf(st[v].mx - mx);  // 0 while the state is empty
+      float l = st[v].l * r, acc = st[v].acc * r;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float e = __expf(z[u][v] - mx);  // 0 for absent sources
+        l += e;
+        acc += e * x[u][v];
       }
+      st[v] = Soft{mx, l, acc};
     }
   }
-  // merge the G groups of every coordinate: s_part[g][w]
+  // merge the G groups of every coordinate: the groups of a wavefront are
+  // lanes o, o + TR, ...; then the four wavefronts through s_part[w][W]
 #pragma unroll
-  for (int v = 0; v < V; ++v) s_part[grp * W + o * V + v] = st[v];
+  for (int msk = TR; msk < 64; msk <<= 1) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const Soft other{__shfl_xor(st[v].mx, msk, 64), __shfl_xor(st[v].l, msk, 64), __shfl_xor(st[v].acc, msk, 64)};
+      st[v] = soft_merge(st[v], other);
+    }
+  }
+  const int wv = tid >> 6;
+  if ((tid & 63) < TR) {
+#pragma unroll
+    for (int v = 0; v < V; ++v) s_part[wv * W + o * V + v] = st[v];
+  }
   __syncthreads();
   float val = 0.f;
   if (tid < W) {
     Soft acc = s_part[tid];
-    for (int g = 1; g < G; ++g) acc = soft_merge(acc, s_part[g * W + tid]);
+#pragma unroll
+    for (int g = 1; g < kFoldT / 64; ++g) acc = soft_merge(acc, s_part[g * W + tid]);
     val = acc.acc / acc.l;
   }
   __syncthreads();
@@ -284,6 +315,7 @@ __global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
   const int m = a.m, R = a.R, c = a.c;
   const int64_t t = a.pos[b];
   const int n_have = a.n_entries[b];
+  __asm__ __volatile__("" ::"s"(t), "s"(n_have));  // both loads in one round trip
   const int64_t lim = vis_limit(t, m, a.vis);
   const bool fold = (lim == (int64_t)n_have + 1) && n_have < a.E_cap;
   const int64_t e = n_have;
