@@ -133,4 +133,5 @@ CSA_DEV void lds_add_noret(int* p, int v) {
 // visible-entry limit for a query at position t
 CSA_DEV int64_t vis_limit(int64_t t, int m, int vis) { return vis == 0 ? t / m : (t + 1) / m; }
 
+
 }  // namespace csa

@@ -110,8 +110,9 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t s) {
   TopkWs tw = topk_ws_carve(ws + sc_bytes, rows, a.E_cap, split);
   const bool mfma = index_mfma_supported(a) && split;
   hipError_t e;
+  int n_wg_fused = 0;
   if (mfma) {
-    e = launch_index_score_mfma(a, tw, 1, s);
+    e = launch_index_score_mfma(a, tw, 1, 1, &n_wg_fused, s);
   } else {
     dim3 g1((a.E_cap + 255) / 256, rows), blk(256);
     if (a.idx_dtype == F32)
@@ -124,6 +125,7 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t s) {
   }
   if (e != hipSuccess) return e;
   if (mfma) {
+    if (n_wg_fused > 0) return launch_topk_fused_resolve(a, tw, n_wg_fused, s);
     const int slice_len = kTopkCollectSlice;
     const int slices = (a.E_cap + slice_len - 1) / slice_len;
     return launch_topk_collect(a, tw, slices, slice_len, s);

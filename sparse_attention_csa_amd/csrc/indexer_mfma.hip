@@ -26,6 +26,18 @@
 // they commute with ReLU).  With use_hist the wave also counts the top 11
 // bits of each score's order-preserving key into an LDS histogram that is
 // added to the row's global histogram at the end (stage 1 of the top-k).
+//
+// Fused top-k collection (fuse, decode): every workgroup also keeps its
+// scores in LDS.  When its histogram is added, it arrives on its row's
+// counter; the last workgroup of the row reads the complete histogram,
+// finds the threshold bin and publishes it; the others wait for that (the
+// grid is one round of resident workgroups, so all of them are running; the
+// wait is bounded and a row that times out falls back to a scan of its
+// scores).  Each workgroup then writes its certain winners and threshold-bin
+// candidates, in entry order, to its own region of the row's lists, with the
+// counts in wg_info, and one workgroup per row merges the lists
+// (topk_fused_resolve_kernel).  The scores are not read back from memory and
+// no list reservation contends on a counter.
 
 #include <type_traits>
 
@@ -46,6 +58,7 @@ CSA_DEV float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); 
 namespace {
 
 constexpr int kD = 128;
+constexpr int kFuseWaitTries = 40000;  // polls of the published threshold bin (about 10 ms)
 
 // Tile geometry.  e4m3: 16 keys x 128 B = 2 KB, read as two 1 KB pieces of
 // 8 keys; bf16: 16 keys x 256 B = 4 KB, four pieces of 4 keys.  In LDS, chunk
@@ -71,11 +84,13 @@ struct Geo {
 
 // grid (n_wg, rows), 256 threads
 template <int FP8, int HT>
-__global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, TopkWs ws, int use_hist) {
+__global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, TopkWs ws, int use_hist, int fuse) {
   typedef Geo<FP8> G;
   constexpr int kU = G::kU;
   __shared__ __attribute__((aligned(1024))) char s_tr[4][kU * G::kTileB];  // per-wave transpose buffer
   __shared__ int s_hist[kTopkBins];
+  __shared__ float s_sc[kTopkFuseCap];  // fused: this workgroup's scores, by entry - first entry
+  __shared__ int s_misc[16];
   const int row = blockIdx.y, b = row / a.Tq, tq = row % a.Tq;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int H = a.H_I;
@@ -252,6 +267,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
       if (e < nv && i < n && lg == 0) {
         out[e] = part[g];
         if (use_hist) atomicAdd(&s_hist[f32_key(part[g]) >> kTopkShift], 1);
+        if (fuse) s_sc[(w * per + i) * 16 + li] = part[g];
       }
     }
   };
@@ -291,6 +307,67 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
       if (v) atomicAdd(&gh[i], v);
     }
   }
+  if (!fuse || nv <= a.k) return;  // nv <= k: every visible entry is selected
+
+  // ---- fused collection.  Arrive on the row counter once this workgroup's
+  // histogram atomics have completed (device scope).
+  int* slot = ws.ctr + (size_t)row * 4;  // [2] failure flag, [3] published threshold bin
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) s_misc[15] = atomicAdd(&ws.sync[row], 1u) == gridDim.x - 1;
+  __syncthreads();
+  int b1, above;
+  if (s_misc[15]) {
+    // last of the row: the histogram is complete; read it device-coherently
+    int* gh = ws.hist + (size_t)row * kTopkBins;
+    for (int i = tid; i < kTopkBins; i += 256)
+      s_hist[i] = __hip_atomic_load(gh + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    find_bin<256>(s_hist, a.k, s_misc, s_misc + 8, &b1, &above);
+    if (tid == 0)
+      __hip_atomic_store(slot + 3, (1 << 30) | (above << 11) | b1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    if (tid == 0) {
+      int v = 0;
+      for (int it = 0; it < kFuseWaitTries && v == 0; ++it) {
+        v = __hip_atomic_load(slot + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (v == 0) __builtin_amdgcn_s_sleep(8);
+      }
+      s_misc[14] = v;
+    }
+    __syncthreads();
+    const int v = s_misc[14];
+    if (v == 0) {  // not published in time: the row falls back to a scan of its scores
+      if (tid == 0) atomicOr(slot + 2, 1);
+      return;
+    }
+    b1 = v & 2047;
+    above = (v >> 11) & 4095;
+  }
+  const int64_t e_first = (int64_t)blockIdx.x * 4 * per * 16;
+  int n_ent = (int)(nv - e_first < 0 ? 0 : nv - e_first);
+  if (n_ent > 4 * per * 16) n_ent = 4 * (int)per * 16;
+  int4* info = ws.wg_info + (size_t)row * kTopkMaxWgRow + blockIdx.x;
+  // contiguous runs per thread keep the lists in entry order
+  const int cpt = (n_ent + 255) / 256;
+  const int i0 = min(tid * cpt, n_ent), i1 = min(i0 + cpt, n_ent);
+  int cnt = 0;  // certain winners in the low half, candidates in the high half
+  for (int i = i0; i < i1; ++i) {
+    const int bin = (int)(f32_key(s_sc[i]) >> kTopkShift);
+    cnt += (bin > b1 ? 1 : 0) + (bin == b1 ? 1 << 16 : 0);
+  }
+  int total;
+  const int off = block_excl_scan<256>(cnt, s_misc, &total);
+  int os = off & 0xffff, oc = off >> 16;
+  int* lsure = ws.lsure + (size_t)row * a.E_cap + e_first;
+  uint2* lcand = ws.lcand + (size_t)row * a.E_cap + e_first;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = f32_key(s_sc[i]);
+    const int bin = (int)(key >> kTopkShift);
+    if (bin > b1) lsure[os++] = (int)e_first + i;
+    if (bin == b1) lcand[oc++] = make_uint2(key, (uint32_t)(e_first + i));
+  }
+  if (tid == 0) *info = make_int4(total & 0xffff, (unsigned)total >> 16, (int)e_first, 0);
 }
 
 bool index_mfma_supported(const IndexArgs& a) {
@@ -309,33 +386,42 @@ static int resident_wgs(K kernel) {
 }
 
 template <int FP8, int HT>
-static hipError_t launch_scorer(const IndexArgs& a, const TopkWs& ws, int use_hist, hipStream_t s) {
+static hipError_t launch_scorer(const IndexArgs& a, const TopkWs& ws, int use_hist, int allow_fuse,
+                                int* n_wg_fused, hipStream_t s) {
   // one round of resident workgroups (the scan is a single pass over the
   // keys), at most one workgroup per 16 tiles of a row
   static int resident = 0;
   if (!resident) resident = resident_wgs(index_score_mfma_kernel<FP8, HT>);
   const int rows = a.B * a.Tq;
-  int per_row = (resident + rows - 1) / rows;
+  int per_row = resident / rows;
   const int max_wg = (int)((((int64_t)a.E_cap + 15) / 16 + 15) / 16);
   if (per_row > max_wg) per_row = max_wg;
   if (per_row < 1) per_row = 1;
+  // fused collection: the grid fits on the device at once (one round of
+  // resident workgroups) and a workgroup's scores (4 waves x per tiles, for
+  // the largest visible count E_cap) fit in its LDS
+  const int64_t per = ((int64_t)a.E_cap + 15) / 16 / ((int64_t)per_row * 4) + 1;
+  const int fuse = allow_fuse && use_hist && per_row * rows <= resident && per_row <= kTopkMaxWgRow &&
+                   4 * per * 16 <= kTopkFuseCap && ws.sync != nullptr;
+  *n_wg_fused = fuse ? per_row : 0;
   dim3 grid(per_row, rows), block(256);
-  CSA_LAUNCH("index_score_mfma", (index_score_mfma_kernel<FP8, HT>), grid, block, 0, s, a, ws, use_hist);
+  CSA_LAUNCH("index_score_mfma", (index_score_mfma_kernel<FP8, HT>), grid, block, 0, s, a, ws, use_hist, fuse);
   return hipGetLastError();
 }
 
-hipError_t launch_index_score_mfma(const IndexArgs& a, const TopkWs& ws, int use_hist, hipStream_t s) {
+hipError_t launch_index_score_mfma(const IndexArgs& a, const TopkWs& ws, int use_hist, int allow_fuse,
+                                   int* n_wg_fused, hipStream_t s) {
   const int HT = a.H_I / 16;
   if (a.idx_dtype == E4M3) {
-    if (HT == 4) return launch_scorer<1, 4>(a, ws, use_hist, s);
-    if (HT == 3) return launch_scorer<1, 3>(a, ws, use_hist, s);
-    if (HT == 2) return launch_scorer<1, 2>(a, ws, use_hist, s);
-    return launch_scorer<1, 1>(a, ws, use_hist, s);
+    if (HT == 4) return launch_scorer<1, 4>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
+    if (HT == 3) return launch_scorer<1, 3>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
+    if (HT == 2) return launch_scorer<1, 2>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
+    return launch_scorer<1, 1>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
   }
-  if (HT == 4) return launch_scorer<0, 4>(a, ws, use_hist, s);
-  if (HT == 3) return launch_scorer<0, 3>(a, ws, use_hist, s);
-  if (HT == 2) return launch_scorer<0, 2>(a, ws, use_hist, s);
-  return launch_scorer<0, 1>(a, ws, use_hist, s);
+  if (HT == 4) return launch_scorer<0, 4>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
+  if (HT == 3) return launch_scorer<0, 3>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
+  if (HT == 2) return launch_scorer<0, 2>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
+  return launch_scorer<0, 1>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
 }
 
 }  // namespace csa

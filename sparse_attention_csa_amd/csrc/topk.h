@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
 #include "kernels.h"
 
 namespace csa {
@@ -13,24 +14,103 @@ constexpr int kTopkShift = 21;       // key >> 21 = bin
 constexpr int kTopkCandCap = 8192;   // threshold-bin candidates resolved in LDS
 constexpr int kTopkMaxK = 2048;      // largest k
 constexpr int kTopkCollectSlice = 4096;  // entries per collect workgroup
+constexpr int kTopkFuseCap = 4096;       // scores a fused scoring workgroup keeps in LDS
+constexpr int kTopkMaxWgRow = 1024;      // scoring workgroups per row (fused mode)
 
-// per-row scratch; hist and ctr are zero between calls (the resolving
-// workgroup returns them to zero)
+// per-row scratch; hist, ctr and sync are zero between calls (the resolving
+// workgroups return them to zero)
 struct TopkWs {
   int* hist;   // [rows][kTopkBins]
-  int* ctr;    // [rows][4]: candidates, certain winners
+  int* ctr;    // [rows][4]: candidates, certain winners; fused mode: [2] failure flag, [3] threshold bin
   uint2* cand; // [rows][kTopkCandCap] (key, id) of threshold-bin entries (split mode)
   int* sure;   // [rows][kTopkMaxK] ids above the threshold bin (split mode)
+  // fused mode (split mode, scores kept by the scoring workgroups)
+  unsigned* sync;  // [rows] arrivals of the scoring workgroups (rows <= 64)
+  int4* wg_info;   // [rows][kTopkMaxWgRow] per scoring workgroup: certain, candidates, first entry
+  int* lsure;      // [rows][E_cap] certain winners, each workgroup's at its first entry
+  uint2* lcand;    // [rows][E_cap] candidates (key, id), likewise
 };
+
+// ---- device helpers shared by the scoring and selection kernels
+
+CSA_DEV int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_up(v, o, 64);
+    if (lane >= o) v += x;
+  }
+  return v;
+}
+
+// exclusive prefix of v over the NT threads in thread order; *total = sum.
+// s_w: NT/64 ints of scratch.  Contains two barriers.
+template <int NT>
+CSA_DEV int block_excl_scan(int v, int* s_w, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int inc = wave_incl_scan(v);
+  if (lane == 63) s_w[wave] = inc;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int c = s_w[w];
+    if (w < wave) off += c;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return off + inc - v;
+}
+
+// b1 (bin of the k-th largest key) and the count above it from a kTopkBins
+// histogram (global or LDS); every thread gets both.  s_w: NT/64 ints,
+// s_out: 2 ints.
+template <int NT>
+CSA_DEV void find_bin(const int* hist, int k, int* s_w, int* s_out, int* b1, int* above) {
+  const int tid = threadIdx.x;
+  constexpr int PER = kTopkBins / NT;
+  int c[PER], tot = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    c[i] = hist[kTopkBins - 1 - (PER * tid + i)];
+    tot += c[i];
+  }
+  int all;
+  const int before = block_excl_scan<NT>(tot, s_w, &all);
+  if (before < k && before + tot >= k) {
+    int acc = before;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (acc + c[i] >= k) {
+        s_out[0] = kTopkBins - 1 - (PER * tid + i);
+        s_out[1] = acc;
+        break;
+      }
+      acc += c[i];
+    }
+  }
+  __syncthreads();
+  *b1 = s_out[0];
+  *above = s_out[1];
+  __syncthreads();
+}
 
 size_t topk_ws_bytes(int rows, int E_cap, bool split);
 TopkWs topk_ws_carve(void* base, int rows, int E_cap, bool split);
 hipError_t launch_topk_collect(const IndexArgs& a, const TopkWs& ws, int slices, int slice_len,
                                hipStream_t s);
+// fused mode: the scoring kernel classified the scores; one workgroup per row
+// merges the per-workgroup lists (n_wg scoring workgroups per row)
+hipError_t launch_topk_fused_resolve(const IndexArgs& a, const TopkWs& ws, int n_wg, hipStream_t s);
 hipError_t launch_topk_rows(const IndexArgs& a, const TopkWs& ws, hipStream_t s);
 
-// MFMA scorer (indexer_mfma.hip); with use_hist it also fills ws.hist
+// MFMA scorer (indexer_mfma.hip); with use_hist it also fills ws.hist.  With
+// allow_fuse (split mode) it may also classify the scores against the
+// threshold bin after a grid-wide barrier; *n_wg_fused is then the number of
+// scoring workgroups per row, else 0.
 bool index_mfma_supported(const IndexArgs& a);
-hipError_t launch_index_score_mfma(const IndexArgs& a, const TopkWs& ws, int use_hist, hipStream_t s);
+hipError_t launch_index_score_mfma(const IndexArgs& a, const TopkWs& ws, int use_hist, int allow_fuse,
+                                   int* n_wg_fused, hipStream_t s);
 
 }  // namespace csa

@@ -38,36 +38,6 @@ constexpr int kCollectPer = kTopkCollectSlice / kCT;  // 16 keys per thread
 
 CSA_DEV uint32_t bin_of(uint32_t key) { return key >> kTopkShift; }
 
-CSA_DEV int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int x = __shfl_up(v, o, 64);
-    if (lane >= o) v += x;
-  }
-  return v;
-}
-
-// exclusive prefix of v over the NT threads in thread order; *total = sum.
-// s_w: NT/64 ints of scratch.  Contains two barriers.
-template <int NT>
-CSA_DEV int block_excl_scan(int v, int* s_w, int* total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int inc = wave_incl_scan(v);
-  if (lane == 63) s_w[wave] = inc;
-  __syncthreads();
-  int off = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) {
-    const int c = s_w[w];
-    if (w < wave) off += c;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return off + inc - v;
-}
-
 // In a histogram of 64 * PER bins, the bin where the count accumulated from
 // the top (DESC) or the bottom first reaches `want`.  Executed by one
 // wavefront; writes (bin, count before it) to s_out[0..1].
@@ -95,39 +65,6 @@ CSA_DEV void wave_find(const int* hist, int want, int* s_out) {
       acc += c[i];
     }
   }
-}
-
-// b1 (bin of the k-th largest key) and the count above it from a kTopkBins
-// histogram (global or LDS); every thread gets both.  s_w: NT/64 ints,
-// s_out: 2 ints.
-template <int NT>
-CSA_DEV void find_bin(const int* hist, int k, int* s_w, int* s_out, int* b1, int* above) {
-  const int tid = threadIdx.x;
-  constexpr int PER = kTopkBins / NT;
-  int c[PER], tot = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    c[i] = hist[kTopkBins - 1 - (PER * tid + i)];
-    tot += c[i];
-  }
-  int all;
-  const int before = block_excl_scan<NT>(tot, s_w, &all);
-  if (before < k && before + tot >= k) {
-    int acc = before;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (acc + c[i] >= k) {
-        s_out[0] = kTopkBins - 1 - (PER * tid + i);
-        s_out[1] = acc;
-        break;
-      }
-      acc += c[i];
-    }
-  }
-  __syncthreads();
-  *b1 = s_out[0];
-  *above = s_out[1];
-  __syncthreads();
 }
 
 CSA_DEV int64_t visible(const IndexArgs& a, int b, int64_t t) {
@@ -209,6 +146,77 @@ CSA_DEV void select_candidates(Lds& L, int n, uint32_t b1, int want, int* n_win)
   __syncthreads();
   *n_win = min(L.misc[48], kTopkMaxK);
   __syncthreads();
+}
+
+// The same selection for candidates stored in ascending id order, keeping
+// that order: the selected ids go to sel[0 ..) (capacity kTopkBins, sel may
+// be L.hist: it is written after the last radix pass).  Returns their count.
+CSA_DEV int select_ordered(Lds& L, int n, uint32_t b1, int want, int* sel) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = b1;
+  int rem = want;
+  int shift = kTopkShift;
+  for (int pass = 0; pass < 3; ++pass) {  // bits 20..14, 13..7, 6..0
+    shift -= 7;
+    if (tid < 128) L.hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += kRT) {
+      const uint32_t key = L.ckey[i];
+      if ((key >> (shift + 7)) == prefix) atomicAdd(&L.hist[(key >> shift) & 127], 1);
+    }
+    __syncthreads();
+    if (tid < 64) wave_find<2, true>(L.hist, rem, L.misc);
+    __syncthreads();
+    prefix = (prefix << 7) | (uint32_t)L.misc[0];
+    rem -= L.misc[1];
+    __syncthreads();
+  }
+  const uint32_t tau = prefix;
+  // the ties with key tau are in id order: the first rem of them win
+  const int cpt = (n + kRT - 1) / kRT;
+  const int i0 = min(tid * cpt, n), i1 = min(i0 + cpt, n);
+  int nt = 0;
+  for (int i = i0; i < i1; ++i) nt += L.ckey[i] == tau;
+  int n_tie;
+  int tie_rank = block_excl_scan<kRT>(nt, L.misc + 8, &n_tie);
+  int c = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = L.ckey[i];
+    if (key > tau) ++c;
+    else if (key == tau) c += tie_rank++ < rem;
+  }
+  int tot;
+  int o = block_excl_scan<kRT>(c, L.misc + 24, &tot);
+  tie_rank -= nt;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = L.ckey[i];
+    bool take = key > tau;
+    if (key == tau) take = tie_rank++ < rem;
+    if (take && o < kTopkBins) sel[o++] = L.cid[i];
+  }
+  __syncthreads();
+  return tot;
+}
+
+CSA_DEV int lower_bound_i(const int* v, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (v[mid] < x) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// last j in [0, n) with off[j] <= g (off ascending, off[n] = total > g)
+CSA_DEV int owner_of(const int* off, int n, int g) {
+  int lo = 0, hi = n;  // off[lo] <= g < off[hi]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= g) lo = mid;
+    else hi = mid;
+  }
+  return lo;
 }
 
 // Ascending sort of the n (<= kTopkMaxK) distinct ids in win[], by buckets
@@ -433,6 +441,90 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(IndexArgs a, TopkWs w
 }
 
 // ---------------------------------------------------------------------------
+// fused mode, stage 2: grid (rows), kRT threads.  The n_wg scoring
+// workgroups of a row left their certain winners and candidates in entry
+// order, each in its own region; concatenated in workgroup order both lists
+// are sorted by id.  Radix select among the candidates (order kept), then
+// each id's output position is its rank in its own list plus its rank in
+// the other (a merge of two sorted lists).  A row whose scoring workgroups
+// did not all pass the grid barrier is resolved from its scores instead.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kRT) void topk_fused_resolve_kernel(IndexArgs a, TopkWs ws, int n_wg) {
+  extern __shared__ unsigned char dyn[];
+  Lds& L = *reinterpret_cast<Lds*>(dyn);
+  __shared__ int s_os[kTopkMaxWgRow + 1], s_oc[kTopkMaxWgRow + 1], s_e0[kTopkMaxWgRow];
+  const int row = blockIdx.x, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x;
+  int* hist = ws.hist + (size_t)row * kTopkBins;
+  int* ctr = ws.ctr + (size_t)row * 4;
+  int32_t* out = a.topk_idx + (size_t)row * a.k;
+  const int4 info = tid < n_wg ? ws.wg_info[(size_t)row * kTopkMaxWgRow + tid] : make_int4(0, 0, 0, 0);
+  const int failed = ctr[2];
+  const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
+  const int nv = (int)visible(a, b, t);
+  const int k = a.k;
+  if (nv <= k) {
+    for (int i = tid; i < k; i += kRT) out[i] = i < nv ? i : -1;
+    if (tid == 0) a.topk_cnt[row] = nv;
+  } else {
+    int b1, above;
+    find_bin<kRT>(hist, k, L.misc + 8, L.misc + 40, &b1, &above);
+    int tot_s, tot_c;
+    const int os = block_excl_scan<kRT>(info.x, L.misc + 8, &tot_s);
+    const int oc = block_excl_scan<kRT>(info.y, L.misc + 24, &tot_c);
+    if (failed || tot_s != above || tot_c > kTopkCandCap) {
+      const int n = resolve_from_row(L, a.scores + (size_t)row * a.E_cap, nv, b1, k - above, out);
+      if (tid == 0) a.topk_cnt[row] = n;
+    } else {
+      if (tid < n_wg) {
+        s_os[tid] = os;
+        s_oc[tid] = oc;
+        s_e0[tid] = info.z;
+      }
+      if (tid == 0) {
+        s_os[n_wg] = tot_s;
+        s_oc[n_wg] = tot_c;
+      }
+      __syncthreads();
+      const int* lsure = ws.lsure + (size_t)row * a.E_cap;
+      const uint2* lcand = ws.lcand + (size_t)row * a.E_cap;
+      for (int g = tid; g < tot_s; g += kRT) {
+        const int j = owner_of(s_os, n_wg, g);
+        L.win[g] = lsure[s_e0[j] + g - s_os[j]];
+      }
+      for (int g = tid; g < tot_c; g += kRT) {
+        const int j = owner_of(s_oc, n_wg, g);
+        const uint2 v = lcand[s_e0[j] + g - s_oc[j]];
+        L.ckey[g] = v.x;
+        L.cid[g] = (int)v.y;
+      }
+      __syncthreads();
+      const int want = k - above;
+      int* sel = L.hist;
+      const int n_sel = min(select_ordered(L, tot_c, (uint32_t)b1, want, sel), want);
+      for (int i = tid; i < tot_s; i += kRT) {
+        const int id = L.win[i];
+        out[i + lower_bound_i(sel, n_sel, id)] = id;
+      }
+      for (int j = tid; j < n_sel; j += kRT) {
+        const int id = sel[j];
+        out[j + lower_bound_i(L.win, tot_s, id)] = id;
+      }
+      for (int i = tot_s + n_sel + tid; i < k; i += kRT) out[i] = -1;
+      if (tid == 0) a.topk_cnt[row] = tot_s + n_sel;
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kTopkBins; i += kRT) hist[i] = 0;
+  if (tid == 0) {
+    ctr[0] = 0;
+    ctr[1] = 0;
+    ctr[2] = 0;
+    ctr[3] = 0;
+    ws.sync[row] = 0;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // row mode: grid (rows), kRT threads, one workgroup per row, scores already
 // written.
 // ---------------------------------------------------------------------------
@@ -492,24 +584,35 @@ __global__ __launch_bounds__(kRT) void topk_rowsel_kernel(IndexArgs a, TopkWs ws
 }
 
 size_t topk_ws_bytes(int rows, int E_cap, bool split) {
-  (void)E_cap;
   size_t per = kTopkBins * 4 + 16;
-  if (split) per += (size_t)kTopkCandCap * 8 + (size_t)kTopkMaxK * 4;
-  return (size_t)rows * per + 1024;
+  if (split)
+    per += (size_t)kTopkCandCap * 8 + (size_t)kTopkMaxK * 4 + (size_t)kTopkMaxWgRow * 16 +
+           (size_t)E_cap * (4 + 8);
+  return (size_t)rows * per + 2048;
 }
 
 TopkWs topk_ws_carve(void* base, int rows, int E_cap, bool split) {
-  (void)E_cap;
-  TopkWs w;
+  TopkWs w{};
+  auto align16 = [](char* q) { return reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(q) + 15) & ~uintptr_t(15)); };
   char* p = reinterpret_cast<char*>(base);
   w.hist = reinterpret_cast<int*>(p);
   p += (size_t)rows * kTopkBins * 4;
   w.ctr = reinterpret_cast<int*>(p);
   p += (size_t)rows * 16;
-  p = reinterpret_cast<char*>((reinterpret_cast<uintptr_t>(p) + 15) & ~uintptr_t(15));
-  w.cand = split ? reinterpret_cast<uint2*>(p) : nullptr;
-  if (split) p += (size_t)rows * kTopkCandCap * 8;
-  w.sure = split ? reinterpret_cast<int*>(p) : nullptr;
+  p = align16(p);
+  if (!split) return w;
+  w.cand = reinterpret_cast<uint2*>(p);
+  p += (size_t)rows * kTopkCandCap * 8;
+  w.sure = reinterpret_cast<int*>(p);
+  p += (size_t)rows * kTopkMaxK * 4;
+  p = align16(p);
+  w.sync = reinterpret_cast<unsigned*>(p);
+  p += 256;
+  w.wg_info = reinterpret_cast<int4*>(p);
+  p += (size_t)rows * kTopkMaxWgRow * 16;
+  w.lcand = reinterpret_cast<uint2*>(p);
+  p += (size_t)rows * E_cap * 8;
+  w.lsure = reinterpret_cast<int*>(p);
   return w;
 }
 
@@ -532,6 +635,14 @@ hipError_t launch_topk_collect(const IndexArgs& a, const TopkWs& ws, int slices,
   e = allow_lds(topk_resolve_kernel, sizeof(Lds), &lds_set);
   if (e != hipSuccess) return e;
   CSA_LAUNCH("topk_resolve", topk_resolve_kernel, dim3(a.B * a.Tq), dim3(kRT), sizeof(Lds), s, a, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_fused_resolve(const IndexArgs& a, const TopkWs& ws, int n_wg, hipStream_t s) {
+  static size_t lds_set = 0;
+  hipError_t e = allow_lds(topk_fused_resolve_kernel, sizeof(Lds), &lds_set);
+  if (e != hipSuccess) return e;
+  CSA_LAUNCH("topk_resolve", topk_fused_resolve_kernel, dim3(a.B * a.Tq), dim3(kRT), sizeof(Lds), s, a, ws, n_wg);
   return hipGetLastError();
 }
 
