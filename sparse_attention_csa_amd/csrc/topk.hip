@@ -82,6 +82,7 @@ struct Lds {
   int cid[kTopkCandCap];
   int win[kTopkMaxK];   // winner ids (sorted in place)
   int hist[kTopkBins];  // radix histograms / the row histogram
+  int sel[kTopkMaxK];   // selected candidates (ordered selection)
   int misc[64];
 };
 
@@ -149,53 +150,53 @@ CSA_DEV void select_candidates(Lds& L, int n, uint32_t b1, int want, int* n_win)
 }
 
 // The same selection for candidates stored in ascending id order, keeping
-// that order: the selected ids go to sel[0 ..) (capacity kTopkBins, sel may
-// be L.hist: it is written after the last radix pass).  Returns their count.
+// that order: the selected ids go to sel[0 ..) (capacity kTopkMaxK).  The
+// three radix passes count into their own
+// 128-bin histograms (cleared together up front), so a pass costs two
+// barriers; the final filter needs one scan: a thread's winners go after
+// the winners above tau of the threads before it and the first rem ties.
+// Returns the count selected.
 CSA_DEV int select_ordered(Lds& L, int n, uint32_t b1, int want, int* sel) {
   const int tid = threadIdx.x;
+  if (tid < 384) L.hist[tid] = 0;
+  __syncthreads();
   uint32_t prefix = b1;
   int rem = want;
   int shift = kTopkShift;
   for (int pass = 0; pass < 3; ++pass) {  // bits 20..14, 13..7, 6..0
     shift -= 7;
-    if (tid < 128) L.hist[tid] = 0;
-    __syncthreads();
+    int* h = L.hist + 128 * pass;
     for (int i = tid; i < n; i += kRT) {
       const uint32_t key = L.ckey[i];
-      if ((key >> (shift + 7)) == prefix) atomicAdd(&L.hist[(key >> shift) & 127], 1);
+      if ((key >> (shift + 7)) == prefix) atomicAdd(&h[(key >> shift) & 127], 1);
     }
     __syncthreads();
-    if (tid < 64) wave_find<2, true>(L.hist, rem, L.misc);
+    if (tid < 64) wave_find<2, true>(h, rem, L.misc + 2 * pass);
     __syncthreads();
-    prefix = (prefix << 7) | (uint32_t)L.misc[0];
-    rem -= L.misc[1];
-    __syncthreads();
+    prefix = (prefix << 7) | (uint32_t)L.misc[2 * pass];
+    rem -= L.misc[2 * pass + 1];
   }
   const uint32_t tau = prefix;
-  // the ties with key tau are in id order: the first rem of them win
   const int cpt = (n + kRT - 1) / kRT;
   const int i0 = min(tid * cpt, n), i1 = min(i0 + cpt, n);
-  int nt = 0;
-  for (int i = i0; i < i1; ++i) nt += L.ckey[i] == tau;
-  int n_tie;
-  int tie_rank = block_excl_scan<kRT>(nt, L.misc + 8, &n_tie);
-  int c = 0;
+  int ng = 0, nt = 0;  // keys above tau, ties
   for (int i = i0; i < i1; ++i) {
     const uint32_t key = L.ckey[i];
-    if (key > tau) ++c;
-    else if (key == tau) c += tie_rank++ < rem;
+    ng += key > tau;
+    nt += key == tau;
   }
   int tot;
-  int o = block_excl_scan<kRT>(c, L.misc + 24, &tot);
-  tie_rank -= nt;
+  const int pre = block_excl_scan<kRT>(ng | (nt << 16), L.misc + 8, &tot);
+  int tie_rank = pre >> 16;
+  int o = (pre & 0xffff) + min(tie_rank, rem);
   for (int i = i0; i < i1; ++i) {
     const uint32_t key = L.ckey[i];
     bool take = key > tau;
     if (key == tau) take = tie_rank++ < rem;
-    if (take && o < kTopkBins) sel[o++] = L.cid[i];
+    if (take && o < kTopkMaxK) sel[o++] = L.cid[i];
   }
   __syncthreads();
-  return tot;
+  return (tot & 0xffff) + min(tot >> 16, rem);
 }
 
 CSA_DEV int lower_bound_i(const int* v, int n, int x) {
@@ -453,38 +454,58 @@ __global__ __launch_bounds__(kRT) void topk_fused_resolve_kernel(IndexArgs a, To
   extern __shared__ unsigned char dyn[];
   Lds& L = *reinterpret_cast<Lds*>(dyn);
   __shared__ int s_os[kTopkMaxWgRow + 1], s_oc[kTopkMaxWgRow + 1], s_e0[kTopkMaxWgRow];
-  const int row = blockIdx.x, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x;
+  const int row = blockIdx.x, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x, lane = tid & 63;
   int* hist = ws.hist + (size_t)row * kTopkBins;
   int* ctr = ws.ctr + (size_t)row * 4;
   int32_t* out = a.topk_idx + (size_t)row * a.k;
+  // all requested at once: the workgroups' counts, the failure flag and the
+  // threshold bin the scoring kernel published, the position
   const int4 info = tid < n_wg ? ws.wg_info[(size_t)row * kTopkMaxWgRow + tid] : make_int4(0, 0, 0, 0);
-  const int failed = ctr[2];
+  const int failed = ctr[2], pub = ctr[3];
   const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
   const int nv = (int)visible(a, b, t);
   const int k = a.k;
+  bool from_row = false;
   if (nv <= k) {
     for (int i = tid; i < k; i += kRT) out[i] = i < nv ? i : -1;
     if (tid == 0) a.topk_cnt[row] = nv;
+  } else if (failed || pub == 0) {
+    from_row = true;
   } else {
-    int b1, above;
-    find_bin<kRT>(hist, k, L.misc + 8, L.misc + 40, &b1, &above);
-    int tot_s, tot_c;
-    const int os = block_excl_scan<kRT>(info.x, L.misc + 8, &tot_s);
-    const int oc = block_excl_scan<kRT>(info.y, L.misc + 24, &tot_c);
-    if (failed || tot_s != above || tot_c > kTopkCandCap) {
-      const int n = resolve_from_row(L, a.scores + (size_t)row * a.E_cap, nv, b1, k - above, out);
-      if (tid == 0) a.topk_cnt[row] = n;
+    const int b1 = pub & 2047, above = (pub >> 11) & 4095;
+    // list offsets: wave 0 scans the workgroups' counts
+    if (tid < n_wg) {
+      s_os[tid] = info.x;
+      s_oc[tid] = info.y;
+      s_e0[tid] = info.z;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const int cpw = (n_wg + 63) / 64, j0 = min(lane * cpw, n_wg), j1 = min(j0 + cpw, n_wg);
+      int cs = 0, cc = 0;
+      for (int j = j0; j < j1; ++j) {
+        cs += s_os[j];
+        cc += s_oc[j];
+      }
+      const int is = wave_incl_scan(cs), ic = wave_incl_scan(cc);
+      int os = is - cs, oc = ic - cc;
+      for (int j = j0; j < j1; ++j) {
+        const int ns = s_os[j], nc = s_oc[j];
+        s_os[j] = os;
+        s_oc[j] = oc;
+        os += ns;
+        oc += nc;
+      }
+      if (lane == 63) {
+        s_os[n_wg] = is;
+        s_oc[n_wg] = ic;
+      }
+    }
+    __syncthreads();
+    const int tot_s = s_os[n_wg], tot_c = s_oc[n_wg];
+    if (tot_s != above || tot_c > kTopkCandCap) {
+      from_row = true;
     } else {
-      if (tid < n_wg) {
-        s_os[tid] = os;
-        s_oc[tid] = oc;
-        s_e0[tid] = info.z;
-      }
-      if (tid == 0) {
-        s_os[n_wg] = tot_s;
-        s_oc[n_wg] = tot_c;
-      }
-      __syncthreads();
       const int* lsure = ws.lsure + (size_t)row * a.E_cap;
       const uint2* lcand = ws.lcand + (size_t)row * a.E_cap;
       for (int g = tid; g < tot_s; g += kRT) {
@@ -499,8 +520,13 @@ __global__ __launch_bounds__(kRT) void topk_fused_resolve_kernel(IndexArgs a, To
       }
       __syncthreads();
       const int want = k - above;
-      int* sel = L.hist;
-      const int n_sel = min(select_ordered(L, tot_c, (uint32_t)b1, want, sel), want);
+      int* sel = L.sel;
+      {
+        const int n = select_ordered(L, tot_c, (uint32_t)b1, want, sel);
+        if (tid == 0) L.misc[50] = n;
+        __syncthreads();
+      }
+      const int n_sel = min(L.misc[50], want);
       for (int i = tid; i < tot_s; i += kRT) {
         const int id = L.win[i];
         out[i + lower_bound_i(sel, n_sel, id)] = id;
@@ -512,6 +538,12 @@ __global__ __launch_bounds__(kRT) void topk_fused_resolve_kernel(IndexArgs a, To
       for (int i = tot_s + n_sel + tid; i < k; i += kRT) out[i] = -1;
       if (tid == 0) a.topk_cnt[row] = tot_s + n_sel;
     }
+  }
+  if (from_row) {  // resolve from the row's scores
+    int b1, above;
+    find_bin<kRT>(hist, k, L.misc + 8, L.misc + 40, &b1, &above);
+    const int n = resolve_from_row(L, a.scores + (size_t)row * a.E_cap, nv, b1, k - above, out);
+    if (tid == 0) a.topk_cnt[row] = n;
   }
   __syncthreads();
   for (int i = tid; i < kTopkBins; i += kRT) hist[i] = 0;
