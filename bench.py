@@ -51,19 +51,23 @@ def build_cases(name):
     raise SystemExit(f"unknown workload {name}")
 
 
-def attend_splits(BT, H, rows_max):
-    """Row splits the MFMA attention uses (mirrors attend_mfma_plan)."""
-    cols = BT * max(1, H // 64)
+def attend_splits(BT, H, rows_max, heads_per_wg=64):
+    """Row splits the MFMA attention uses (mirrors attend_mfma_plan, 64 heads
+    per workgroup, and attend_rows_plan, 16)."""
+    cols = BT * max(1, H // heads_per_wg)
     want = max(1, min(64, 256 // cols))
     rps = -(-rows_max // want)
     rps = -(-rps // 16) * 16
+    if heads_per_wg == 16:
+        rps = min(rps, 2304)
     return -(-rows_max // rps)
 
 
 # benchmark timing-hook names -> the kernel symbols rocprofv3 reports
 ROCPROF_NAMES = {
-    "attend_dense_mfma": "attend_mfma_kernel<true>",
-    "attend_sparse_mfma": "attend_mfma_kernel<false>",
+    "attend_dense_mfma": "attend_mfma_kernel",
+    "attend_sparse_rows": "attend_rows_kernel",
+    "topk_resolve": "topk_fused_resolve_kernel",
 }
 
 
@@ -111,7 +115,7 @@ def kernel_work(kname, g):
         # combination of the row splits: partials in, output out (implementation
         # traffic; the algorithmic bytes are counted in the attention kernel)
         rows = (g["k"] if g["kind"] == "csa" else g["E_cap"]) + g["n_win"]
-        ns = attend_splits(B * Tq, g["H"], rows)
+        ns = attend_splits(B * Tq, g["H"], rows, heads_per_wg=16 if g["kind"] == "csa" else 64)
         byt = B * Tq * g["H"] * (ns * (g["c"] * 2 + 8) + g["c"] * 2 + 4)
         return byt, 0.0, "hbm", A.PEAK_HBM_GBS, "GB/s"
     if kname.startswith("attend"):

@@ -35,8 +35,9 @@ KERNEL_SOURCES = {
     "index_score_mfma": ["indexer_mfma.hip", "common.h", "topk.h", "kernels.h"],
     "index_score": ["indexer.hip", "common.h", "kernels.h"],
     "topk_": ["topk.hip", "common.h", "topk.h", "kernels.h"],
-    "attend_mfma": ["attend_mfma.hip", "common.h", "kernels.h"],
-    "attend_merge": ["attend_mfma.hip", "common.h", "kernels.h"],
+    "attend_mfma": ["attend_mfma.hip", "mfma_tile.h", "common.h", "kernels.h"],
+    "attend_rows": ["attend_rows.hip", "mfma_tile.h", "common.h", "kernels.h"],
+    "attend_merge": ["attend_mfma.hip", "mfma_tile.h", "common.h", "kernels.h"],
     "attend_generic": ["attend.hip", "common.h", "kernels.h"],
     "fold_append": ["compress.hip", "common.h", "kernels.h"],
     "compress_chunk": ["compress.hip", "common.h", "kernels.h"],
