@@ -311,18 +311,25 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
   f.x_new = io->x_new; f.tail = s->tail; f.idx_tail = s->idx_tail; f.win_ring = s->win_ring;
   f.kv_cache = s->kv_cache; f.idx_cache = s->idx_cache; f.idx_scale = s->idx_scale; f.E_cap = s->E_cap;
   f.bias_a = s->bias_a; f.bias_b = s->bias_b; f.ibias_a = s->ibias_a; f.ibias_b = s->ibias_b;
-  hipError_t e = csa::launch_fold_append(f, hs);
-  if (e != hipSuccess) return from_hip(e, "hybrid_layer_decode/fold");
-
-  csa::AttendArgs a{};
+  csa::IndexArgs x{};
   if (is_csa) {
-    csa::IndexArgs x{};
     x.idx_dtype = d->idx_dtype; x.q = io->q_idx; x.q_scale = d->idx_dtype == CSA_E4M3 ? io->q_scale : nullptr;
     x.w = io->w_idx; x.keys = s->idx_cache; x.k_scale = d->idx_dtype == CSA_E4M3 ? s->idx_scale : nullptr;
     x.q_pos = io->pos; x.n_entries = s->n_entries; x.n_add = 0;
     x.B = B; x.Tq = 1; x.H_I = d->H_I; x.d_I = d->d_I; x.E_cap = s->E_cap; x.m = d->m; x.k = d->k;
     x.vis = d->vis; x.scores = nullptr; x.topk_idx = io->topk_idx; x.topk_cnt = io->topk_cnt; x.ws = w;
-    e = csa::launch_index_topk(x, hs);
+  }
+  // the fold runs first, unless the scoring kernel does it (fold workgroups)
+  const bool fold_in_scan = is_csa && csa::index_topk_fuses_fold(x, f);
+  hipError_t e = hipSuccess;
+  if (!fold_in_scan) {
+    e = csa::launch_fold_append(f, hs);
+    if (e != hipSuccess) return from_hip(e, "hybrid_layer_decode/fold");
+  }
+
+  csa::AttendArgs a{};
+  if (is_csa) {
+    e = csa::launch_index_topk(x, hs, fold_in_scan ? &f : nullptr);
     if (e != hipSuccess) return from_hip(e, "hybrid_layer_decode/index");
     w += align_up(csa::index_topk_ws_bytes(B, 1, s->E_cap, d->k));
     a.topk_idx = io->topk_idx; a.topk_cnt = io->topk_cnt; a.k = d->k; a.dense = 0;

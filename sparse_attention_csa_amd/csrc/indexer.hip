@@ -100,7 +100,11 @@ size_t index_topk_ws_bytes(int B, int Tq, int E_cap, int k) {
   return sc + topk_ws_bytes(rows, E_cap, rows <= kSplitRows);
 }
 
-hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t s) {
+bool index_topk_fuses_fold(const IndexArgs& a, const FoldArgs& f) {
+  return index_fold_fusable(a, f, a.B * a.Tq <= kSplitRows);
+}
+
+hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t s, const FoldArgs* fold) {
   IndexArgs a = a0;
   const int rows = a.B * a.Tq;
   char* ws = reinterpret_cast<char*>(a.ws);
@@ -112,7 +116,7 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t s) {
   hipError_t e;
   int n_wg_fused = 0;
   if (mfma) {
-    e = launch_index_score_mfma(a, tw, 1, 1, &n_wg_fused, s);
+    e = launch_index_score_mfma(a, tw, 1, 1, &n_wg_fused, fold, s);
   } else {
     dim3 g1((a.E_cap + 255) / 256, rows), blk(256);
     if (a.idx_dtype == F32)

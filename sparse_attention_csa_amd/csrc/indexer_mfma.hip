@@ -38,10 +38,23 @@
 // counts in wg_info, and one workgroup per row merges the lists
 // (topk_fused_resolve_kernel).  The scores are not read back from memory and
 // no list reservation contends on a counter.
+//
+// Fold workgroup (fold_mode, decode with the fused collection): the last
+// workgroup of each row scans nothing; it performs the step's compressor
+// work for its sequence instead of a separate kernel: when the block ending
+// at the query position completes, it folds the new indexer key (and
+// stores it, e4m3-quantized or bf16), scores it against the query exactly
+// as the scan would, and takes part in the histogram and the lists with that
+// one entry (the highest id, so its list comes last); it folds the new main
+// entry, appends the token to the tail rings and the window ring, and the
+// last workgroup of the row to arrive publishes the new entry count (every
+// workgroup of the row has read the old count by then).  The scan
+// workgroups cover the entries before the new one.
 
 #include <type_traits>
 
 #include "common.h"
+#include "fold.h"
 #include "topk.h"
 
 namespace csa {
@@ -84,7 +97,8 @@ struct Geo {
 
 // grid (n_wg, rows), 256 threads
 template <int FP8, int HT>
-__global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, TopkWs ws, int use_hist, int fuse) {
+__global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, TopkWs ws, int use_hist, int fuse,
+                                                                FoldArgs f, int fold_mode) {
   typedef Geo<FP8> G;
   constexpr int kU = G::kU;
   __shared__ __attribute__((aligned(1024))) char s_tr[4][kU * G::kTileB];  // per-wave transpose buffer
@@ -128,24 +142,29 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   // the visible-entry count (scalar loads), then the first two key batches
   const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
   const int32_t n_have = a.n_entries[b];
-  int64_t nv = vis_limit(t, a.m, a.vis);
+  const int64_t lim = vis_limit(t, a.m, a.vis);
+  // fold_mode: the block ending at t completes entry n_have in this step
+  const bool fold_now = fold_mode && lim == (int64_t)n_have + 1 && n_have < a.E_cap;
+  const bool fold_wg = fold_mode && blockIdx.x == gridDim.x - 1;
+  int64_t nv = lim;  // visible entries, including a new one
   {
-    const int64_t have = (int64_t)n_have + a.n_add;
+    const int64_t have = (int64_t)n_have + a.n_add + (fold_now ? 1 : 0);
     if (have < nv) nv = have;
     if (nv > a.E_cap) nv = a.E_cap;
     if (nv < 0) nv = 0;
   }
+  const int64_t nv_scan = fold_now ? nv - 1 : nv;  // the scan workgroups' entries
   const char* keys = reinterpret_cast<const char*>(a.keys) + (size_t)b * a.E_cap * G::kKeyB;
   const float* ksc = a.k_scale ? a.k_scale + (size_t)b * a.E_cap : nullptr;
   float* out = a.scores + (size_t)row * a.E_cap;
 
   // this wave's tiles [t0, t1), in batches of kU
-  const int64_t ntile = (nv + 15) / 16;
-  const int64_t nwaves = (int64_t)gridDim.x * 4;
+  const int64_t ntile = (nv_scan + 15) / 16;
+  const int64_t nwaves = (int64_t)(gridDim.x - fold_mode) * 4;
   const int64_t per = (ntile + nwaves - 1) / nwaves;
   const int64_t t0 = ((int64_t)blockIdx.x * 4 + w) * per;
   const int64_t t1 = t0 + per < ntile ? t0 + per : ntile;
-  const int n = t1 > t0 ? (int)(t1 - t0) : 0;
+  const int n = (t1 > t0 && !fold_wg) ? (int)(t1 - t0) : 0;
   const int nbatch = (n + kU - 1) / kU;
 
   // piece j of a tile: lane l reads bytes [16 l, 16 l + 16) of the piece,
@@ -155,7 +174,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   const int ld_key = l / G::kCpk, ld_chunk = l % G::kCpk;
   // the last row of this wave's run: loads past it (the tail of the run and
   // the batches after it) all re-read that row, which stays in cache
-  const int64_t e_last = (t1 * 16 < nv ? t1 * 16 : nv) - 1;
+  const int64_t e_last = (t1 * 16 < nv_scan ? t1 * 16 : nv_scan) - 1;
   auto load_batch = [&](KBatch& kreg, SBatch& sreg, int bi) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -264,7 +283,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
       if (FP8) part[g] *= sreg[u + g];
       const int i = bi * kU + u + g;
       const int64_t e = (t0 + i) * 16 + li;
-      if (e < nv && i < n && lg == 0) {
+      if (e < nv_scan && i < n && lg == 0) {
         out[e] = part[g];
         if (use_hist) atomicAdd(&s_hist[f32_key(part[g]) >> kTopkShift], 1);
         if (fuse) s_sc[(w * per + i) * 16 + li] = part[g];
@@ -299,6 +318,113 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
       }
     }
   }
+  if (fold_wg) {
+    // the step's compressor work for this sequence (the scan above was empty)
+    Soft* s_part = reinterpret_cast<Soft*>(&s_tr[0][0]);
+    float* s_red = reinterpret_cast<float*>(s_part + 4 * 256);
+    uint32_t* s_key = reinterpret_cast<uint32_t*>(s_red + 8);  // the stored new key (<= 256 B)
+    const int64_t e = n_have;
+    if (fold_now) {
+      // indexer key: fold, quantize, store
+      const bf16* itail = reinterpret_cast<const bf16*>(f.idx_tail) + (size_t)b * 4 * f.R * kD;
+      const bf16* iio = reinterpret_cast<const bf16*>(f.idx_streams) + (size_t)b * 4 * kD;
+      const float iv = fold_job<bf16>(itail, iio, kD, 0, kD, f.m, f.R, t, e, e > 0, f.ibias_a, f.ibias_b, s_part);
+      const size_t krow = (size_t)b * a.E_cap + e;
+      float ks = 1.f;
+      if constexpr (FP8) {
+        float am = wave_max(tid < kD ? fabsf(iv) : 0.f);
+        if (l == 0) s_red[w] = am;
+        __syncthreads();
+        am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+        ks = am / 448.0f;
+        if (!(ks > 0.f)) ks = 1.f;
+        if (tid < kD) {
+          const uint8_t code = f32_to_e4m3(iv / ks);
+          reinterpret_cast<uint8_t*>(f.idx_cache)[krow * kD + tid] = code;
+          reinterpret_cast<uint8_t*>(s_key)[tid] = code;
+        }
+        if (tid == 0) f.idx_scale[krow] = ks;
+      } else {
+        if (tid < kD) {
+          const uint16_t v = f32_to_bf16(iv);
+          reinterpret_cast<uint16_t*>(f.idx_cache)[krow * kD + tid] = v;
+          reinterpret_cast<uint16_t*>(s_key)[tid] = v;
+        }
+      }
+      __syncthreads();
+      // its score, as the scan computes it: sum_h w_h q_scale_h ReLU(q_h . k), times the key scale
+      if (w == 0) {
+        float part = 0.f;
+        if (l < H) {
+          // lane = head: its query row and the key as 16-byte vectors
+          constexpr int kV = kD * (FP8 ? 1 : 2) / 16;
+          const uint4* qv = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) +
+                                                           ((size_t)row * H + l) * kD * (FP8 ? 1 : 2));
+          const uint4* kv4 = reinterpret_cast<const uint4*>(s_key);
+          uint4 qr[kV];
+#pragma unroll
+          for (int j = 0; j < kV; ++j) qr[j] = qv[j];
+          float c = 0.f;
+#pragma unroll
+          for (int j = 0; j < kV; ++j) {
+            const uint4 kj = kv4[j];
+            const uint32_t qw[4] = {qr[j].x, qr[j].y, qr[j].z, qr[j].w};
+            const uint32_t kw[4] = {kj.x, kj.y, kj.z, kj.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if constexpr (FP8) {
+                c += __builtin_amdgcn_cvt_f32_fp8((int)qw[i], 0) * __builtin_amdgcn_cvt_f32_fp8((int)kw[i], 0);
+                c += __builtin_amdgcn_cvt_f32_fp8((int)qw[i], 1) * __builtin_amdgcn_cvt_f32_fp8((int)kw[i], 1);
+                c += __builtin_amdgcn_cvt_f32_fp8((int)qw[i], 2) * __builtin_amdgcn_cvt_f32_fp8((int)kw[i], 2);
+                c += __builtin_amdgcn_cvt_f32_fp8((int)qw[i], 3) * __builtin_amdgcn_cvt_f32_fp8((int)kw[i], 3);
+              } else {
+                c += __uint_as_float(qw[i] << 16) * __uint_as_float(kw[i] << 16);
+                c += __uint_as_float(qw[i] & 0xffff0000u) * __uint_as_float(kw[i] & 0xffff0000u);
+              }
+            }
+          }
+          part = FP8 ? a.w[(size_t)row * H + l] * a.q_scale[(size_t)row * H + l] * relu(c)
+                     : a.w[(size_t)row * H + l] * relu(c);
+        }
+        part = wave_sum(part);
+        if (FP8) part *= ks;
+        if (l == 0) {
+          out[e] = part;
+          s_sc[0] = part;
+          if (use_hist) s_hist[f32_key(part) >> kTopkShift] += 1;
+        }
+      }
+      // main entry: two halves of the coordinates
+      const bf16* mtail = reinterpret_cast<const bf16*>(f.tail) + (size_t)b * (f.overlap ? 4 : 2) * f.R * f.c;
+      const bf16* mio = reinterpret_cast<const bf16*>(f.streams) + (size_t)b * (f.overlap ? 4 : 2) * f.c;
+      for (int r0 = 0; r0 < f.c; r0 += 256) {
+        const int W = f.c - r0 < 256 ? f.c - r0 : 256;
+        const float v = fold_job<bf16>(mtail, mio, f.c, r0, W, f.m, f.R, t, e, f.overlap && e > 0, f.bias_a,
+                                       f.bias_b, s_part);
+        if (tid < W) reinterpret_cast<uint16_t*>(f.kv_cache)[((size_t)b * a.E_cap + e) * f.c + r0 + tid] = f32_to_bf16(v);
+      }
+    }
+    // append the new token: tail rings and window ring
+    {
+      const int nstr = f.overlap ? 4 : 2;
+      const int slot_t = (int)(t % f.R);
+      const uint16_t* mio = reinterpret_cast<const uint16_t*>(f.streams) + (size_t)b * nstr * f.c;
+      uint16_t* mtl = reinterpret_cast<uint16_t*>(f.tail) + (size_t)b * nstr * f.R * f.c;
+      for (int i = tid; i < nstr * f.c; i += 256) {
+        const int sc = i / f.c, r = i % f.c;
+        mtl[((size_t)sc * f.R + slot_t) * f.c + r] = mio[(size_t)sc * f.c + r];
+      }
+      const uint16_t* iio = reinterpret_cast<const uint16_t*>(f.idx_streams) + (size_t)b * 4 * kD;
+      uint16_t* itl = reinterpret_cast<uint16_t*>(f.idx_tail) + (size_t)b * 4 * f.R * kD;
+      for (int i = tid; i < 4 * kD; i += 256) {
+        const int sc = i / kD, r = i % kD;
+        itl[((size_t)sc * f.R + slot_t) * kD + r] = iio[(size_t)sc * kD + r];
+      }
+      uint16_t* ring = reinterpret_cast<uint16_t*>(f.win_ring) + ((size_t)b * f.n_win + t % f.n_win) * f.c;
+      const uint16_t* xn = reinterpret_cast<const uint16_t*>(f.x_new) + (size_t)b * f.c;
+      for (int i = tid; i < f.c; i += 256) ring[i] = xn[i];
+    }
+  }
   if (use_hist) {
     __syncthreads();
     int* gh = ws.hist + (size_t)row * kTopkBins;
@@ -307,15 +433,20 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
       if (v) atomicAdd(&gh[i], v);
     }
   }
-  if (!fuse || nv <= a.k) return;  // nv <= k: every visible entry is selected
+  const bool select = fuse && nv > a.k;  // nv <= k: every visible entry is selected
+  if (!select && !fold_now) return;
 
   // ---- fused collection.  Arrive on the row counter once this workgroup's
-  // histogram atomics have completed (device scope).
+  // histogram atomics (and fold stores) have completed (device scope).
   int* slot = ws.ctr + (size_t)row * 4;  // [2] failure flag, [3] published threshold bin
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) s_misc[15] = atomicAdd(&ws.sync[row], 1u) == gridDim.x - 1;
   __syncthreads();
+  // the last to arrive: every workgroup of the row has read the old count
+  if (s_misc[15] && fold_now && tid == 0)
+    __hip_atomic_store(f.n_entries + b, n_have + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!select) return;
   int b1, above;
   if (s_misc[15]) {
     // last of the row: the histogram is complete; read it device-coherently
@@ -344,9 +475,13 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
     b1 = v & 2047;
     above = (v >> 11) & 4095;
   }
-  const int64_t e_first = (int64_t)blockIdx.x * 4 * per * 16;
-  int n_ent = (int)(nv - e_first < 0 ? 0 : nv - e_first);
+  int64_t e_first = (int64_t)blockIdx.x * 4 * per * 16;
+  int n_ent = (int)(nv_scan - e_first < 0 ? 0 : nv_scan - e_first);
   if (n_ent > 4 * per * 16) n_ent = 4 * (int)per * 16;
+  if (fold_wg) {  // its one entry, the new one
+    e_first = n_have;
+    n_ent = fold_now ? 1 : 0;
+  }
   int4* info = ws.wg_info + (size_t)row * kTopkMaxWgRow + blockIdx.x;
   // contiguous runs per thread keep the lists in entry order
   const int cpt = (n_ent + 255) / 256;
@@ -385,43 +520,79 @@ static int resident_wgs(K kernel) {
   return n_cu * per_cu;
 }
 
-template <int FP8, int HT>
-static hipError_t launch_scorer(const IndexArgs& a, const TopkWs& ws, int use_hist, int allow_fuse,
-                                int* n_wg_fused, hipStream_t s) {
-  // one round of resident workgroups (the scan is a single pass over the
-  // keys), at most one workgroup per 16 tiles of a row
-  static int resident = 0;
-  if (!resident) resident = resident_wgs(index_score_mfma_kernel<FP8, HT>);
+// Grid of the scan: one round of resident workgroups (the scan is a single
+// pass over the keys), at most one workgroup per 16 tiles of a row.  Fused
+// collection when the grid fits on the device at once and a workgroup's
+// scores (4 waves x per tiles, for the largest visible count E_cap) fit in
+// its LDS; with a fold, the last workgroup of each row is the fold
+// workgroup.
+struct ScorerPlan {
+  int per_row, fuse;
+};
+static ScorerPlan scorer_plan(const IndexArgs& a, int resident, int use_hist, int allow_fuse, int with_fold) {
   const int rows = a.B * a.Tq;
   int per_row = resident / rows;
-  const int max_wg = (int)((((int64_t)a.E_cap + 15) / 16 + 15) / 16);
+  const int max_wg = (int)((((int64_t)a.E_cap + 15) / 16 + 15) / 16) + with_fold;
   if (per_row > max_wg) per_row = max_wg;
-  if (per_row < 1) per_row = 1;
-  // fused collection: the grid fits on the device at once (one round of
-  // resident workgroups) and a workgroup's scores (4 waves x per tiles, for
-  // the largest visible count E_cap) fit in its LDS
-  const int64_t per = ((int64_t)a.E_cap + 15) / 16 / ((int64_t)per_row * 4) + 1;
+  if (per_row < 1 + with_fold) per_row = 1 + with_fold;
+  const int scan_wg = per_row - with_fold;
+  const int64_t per = ((int64_t)a.E_cap + 15) / 16 / ((int64_t)scan_wg * 4) + 1;
   const int fuse = allow_fuse && use_hist && per_row * rows <= resident && per_row <= kTopkMaxWgRow &&
-                   4 * per * 16 <= kTopkFuseCap && ws.sync != nullptr;
-  *n_wg_fused = fuse ? per_row : 0;
-  dim3 grid(per_row, rows), block(256);
-  CSA_LAUNCH("index_score_mfma", (index_score_mfma_kernel<FP8, HT>), grid, block, 0, s, a, ws, use_hist, fuse);
+                   4 * per * 16 <= kTopkFuseCap;
+  return ScorerPlan{per_row, fuse};
+}
+
+template <int FP8, int HT>
+static int scorer_resident() {
+  static int resident = 0;
+  if (!resident) resident = resident_wgs(index_score_mfma_kernel<FP8, HT>);
+  return resident;
+}
+
+template <int FP8, int HT>
+static hipError_t launch_scorer(const IndexArgs& a, const TopkWs& ws, int use_hist, int allow_fuse,
+                                int* n_wg_fused, const FoldArgs* fold, hipStream_t s) {
+  const int with_fold = fold ? 1 : 0;
+  const ScorerPlan p = scorer_plan(a, scorer_resident<FP8, HT>(), use_hist, allow_fuse && ws.sync != nullptr,
+                                   with_fold);
+  if (with_fold && !p.fuse) return hipErrorInvalidValue;  // the caller checks index_fold_fusable first
+  *n_wg_fused = p.fuse ? p.per_row : 0;
+  FoldArgs f = fold ? *fold : FoldArgs{};
+  dim3 grid(p.per_row, a.B * a.Tq), block(256);
+  CSA_LAUNCH("index_score_mfma", (index_score_mfma_kernel<FP8, HT>), grid, block, 0, s, a, ws, use_hist, p.fuse,
+             f, with_fold);
   return hipGetLastError();
 }
 
+template <int FP8>
+static int resident_for(int HT) {
+  if (HT == 4) return scorer_resident<FP8, 4>();
+  if (HT == 3) return scorer_resident<FP8, 3>();
+  if (HT == 2) return scorer_resident<FP8, 2>();
+  return scorer_resident<FP8, 1>();
+}
+
+bool index_fold_fusable(const IndexArgs& a, const FoldArgs& f, bool split) {
+  if (!split || !index_mfma_supported(a) || a.Tq != 1 || f.B != a.B || f.dtype != BF16 || f.idx_dtype != a.idx_dtype ||
+      f.d_I != kD || a.n_add != 0)
+    return false;
+  const int resident = a.idx_dtype == E4M3 ? resident_for<1>(a.H_I / 16) : resident_for<0>(a.H_I / 16);
+  return scorer_plan(a, resident, 1, 1, 1).fuse != 0;
+}
+
 hipError_t launch_index_score_mfma(const IndexArgs& a, const TopkWs& ws, int use_hist, int allow_fuse,
-                                   int* n_wg_fused, hipStream_t s) {
+                                   int* n_wg_fused, const FoldArgs* fold, hipStream_t s) {
   const int HT = a.H_I / 16;
   if (a.idx_dtype == E4M3) {
-    if (HT == 4) return launch_scorer<1, 4>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
-    if (HT == 3) return launch_scorer<1, 3>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
-    if (HT == 2) return launch_scorer<1, 2>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
-    return launch_scorer<1, 1>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
+    if (HT == 4) return launch_scorer<1, 4>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+    if (HT == 3) return launch_scorer<1, 3>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+    if (HT == 2) return launch_scorer<1, 2>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+    return launch_scorer<1, 1>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
   }
-  if (HT == 4) return launch_scorer<0, 4>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
-  if (HT == 3) return launch_scorer<0, 3>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
-  if (HT == 2) return launch_scorer<0, 2>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
-  return launch_scorer<0, 1>(a, ws, use_hist, allow_fuse, n_wg_fused, s);
+  if (HT == 4) return launch_scorer<0, 4>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  if (HT == 3) return launch_scorer<0, 3>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  if (HT == 2) return launch_scorer<0, 2>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  return launch_scorer<0, 1>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
 }
 
 }  // namespace csa

@@ -100,7 +100,10 @@ struct IndexArgs {
   void* ws;             // topk scratch
 };
 size_t index_topk_ws_bytes(int B, int Tq, int E_cap, int k);
-hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s);
+// fold: the decode step's fold to run inside the scoring kernel, or null
+// (then the caller has already run it); see index_topk_fuses_fold
+hipError_t launch_index_topk(const IndexArgs& a, hipStream_t s, const FoldArgs* fold = nullptr);
+bool index_topk_fuses_fold(const IndexArgs& a, const FoldArgs& f);
 
 // ------------------------------------------------------------ attention
 struct AttendArgs {

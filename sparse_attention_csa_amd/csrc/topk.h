@@ -107,10 +107,14 @@ hipError_t launch_topk_rows(const IndexArgs& a, const TopkWs& ws, hipStream_t s)
 
 // MFMA scorer (indexer_mfma.hip); with use_hist it also fills ws.hist.  With
 // allow_fuse (split mode) it may also classify the scores against the
-// threshold bin after a grid-wide barrier; *n_wg_fused is then the number of
-// scoring workgroups per row, else 0.
+// threshold bin (per-row publication); *n_wg_fused is then the number of
+// scoring workgroups per row, else 0.  With fold (only when
+// index_fold_fusable) it also performs the decode step's fold.
 bool index_mfma_supported(const IndexArgs& a);
 hipError_t launch_index_score_mfma(const IndexArgs& a, const TopkWs& ws, int use_hist, int allow_fuse,
-                                   int* n_wg_fused, hipStream_t s);
+                                   int* n_wg_fused, const FoldArgs* fold, hipStream_t s);
+// whether the decode step's fold can run inside the scoring kernel (fold
+// workgroups); split: split-mode selection (few rows)
+bool index_fold_fusable(const IndexArgs& a, const FoldArgs& f, bool split);
 
 }  // namespace csa
