@@ -319,28 +319,32 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
     x.B = B; x.Tq = 1; x.H_I = d->H_I; x.d_I = d->d_I; x.E_cap = s->E_cap; x.m = d->m; x.k = d->k;
     x.vis = d->vis; x.scores = nullptr; x.topk_idx = io->topk_idx; x.topk_cnt = io->topk_cnt; x.ws = w;
   }
-  // the fold runs first, unless the scoring kernel does it (fold workgroups)
+  csa::AttendArgs a{};
+  a.dtype = d->kv_dtype; a.q = io->q; a.kv = s->kv_cache; a.E_cap = s->E_cap;
+  a.win = s->win_ring; a.W_cap = d->n_win; a.win_pos0 = nullptr; a.win_pos0_const = 0; a.n_win = d->n_win;
+  a.sink = s->sink; a.q_pos = io->pos; a.scale = d->scale;
+  a.B = B; a.Tq = 1; a.H = d->H; a.c = d->c; a.out = io->out; a.lse = io->lse;
+  if (!is_csa) {
+    a.n_entries = s->n_entries; a.n_add = 0; a.m = d->m; a.vis = d->vis; a.dense = 1;
+    a.ws = w; a.ws_bytes = ws_bytes - (size_t)(w - (char*)ws);
+  }
+  // the fold runs first, unless the scoring kernel (CSA) or the attention
+  // (HCA) does it
   const bool fold_in_scan = is_csa && csa::index_topk_fuses_fold(x, f);
+  const bool fold_in_attend = !is_csa && csa::attend_fuses_fold(a, f);
   hipError_t e = hipSuccess;
-  if (!fold_in_scan) {
+  if (!fold_in_scan && !fold_in_attend) {
     e = csa::launch_fold_append(f, hs);
     if (e != hipSuccess) return from_hip(e, "hybrid_layer_decode/fold");
   }
 
-  csa::AttendArgs a{};
   if (is_csa) {
     e = csa::launch_index_topk(x, hs, fold_in_scan ? &f : nullptr);
     if (e != hipSuccess) return from_hip(e, "hybrid_layer_decode/index");
     w += align_up(csa::index_topk_ws_bytes(B, 1, s->E_cap, d->k));
     a.topk_idx = io->topk_idx; a.topk_cnt = io->topk_cnt; a.k = d->k; a.dense = 0;
-  } else {
-    a.n_entries = s->n_entries; a.n_add = 0; a.m = d->m; a.vis = d->vis; a.dense = 1;
+    a.ws = w; a.ws_bytes = ws_bytes - (size_t)(w - (char*)ws);
   }
-  a.dtype = d->kv_dtype; a.q = io->q; a.kv = s->kv_cache; a.E_cap = s->E_cap;
-  a.win = s->win_ring; a.W_cap = d->n_win; a.win_pos0 = nullptr; a.win_pos0_const = 0; a.n_win = d->n_win;
-  a.sink = s->sink; a.q_pos = io->pos; a.scale = d->scale;
-  a.B = B; a.Tq = 1; a.H = d->H; a.c = d->c; a.out = io->out; a.lse = io->lse;
-  a.ws = w; a.ws_bytes = ws_bytes - (size_t)(w - (char*)ws);
   return from_hip(csa::launch_attend(a, hs), "hybrid_layer_decode/attend");
 }
 

@@ -171,7 +171,9 @@ static size_t split_ws_bytes(int BT, int H, int c, int n_split) {
   return (size_t)BT * n_split * H * (2 * sizeof(float) + (size_t)c * 2);
 }
 
-size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max) {
+// split partials, then (dense shapes) the decode fold's q . entry sums and
+// entry indices at attend_fold_ws_offset
+size_t attend_fold_ws_offset(int B, int Tq, int H, int c, int rows_max) {
   size_t n = 256, extra = 0;
   if (attend_mfma_shape_ok(H, c)) extra = attend_mfma_ws_bytes(B * Tq, H, rows_max);
   if (attend_rows_shape_ok(H, c)) {
@@ -180,7 +182,14 @@ size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max) {
     const size_t r = split_ws_bytes(B * Tq, H, c, ns);
     if (r > extra) extra = r;
   }
-  return n + extra;
+  return (n + extra + 255) / 256 * 256;
+}
+
+size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max) {
+  size_t n = attend_fold_ws_offset(B, Tq, H, c, rows_max);
+  if (attend_mfma_shape_ok(H, c))
+    n += ((size_t)B * H * 8 + 255) / 256 * 256 + ((size_t)B * 4 + 255) / 256 * 256 + ((size_t)B * c * 2 + 255) / 256 * 256;
+  return n;
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {

@@ -27,7 +27,19 @@
 // the second for i >= 4.  V^T comes from the same LDS tile through the gfx950
 // transpose read (ds_read_b64_tr_b16), whose per-lane addresses implement
 // that permutation.  Softmax runs in base 2.
+//
+// Decode with the step's fold inside (fold_mode): the splits cover the
+// entries that existed before the step; split s of head group 0 also folds
+// coordinates [s cs, s cs + cs) of the entry the block ending at the query
+// position completes (its sources are loaded after the row loop and arrive
+// while the output is written; nothing of the fold stays live across the
+// loop), stores them, adds its share of q_h . entry for every head
+// to fold_s (device-scope atomics) and appends its share of the token to the
+// tail and window rings.  The merge kernel then adds the new entry as one
+// more row, weight exp2(scale q . entry - M), and publishes the entry count.
+// The query's own window row is read from the step input x_new.
 
+#include "fold.h"
 #include "kernels.h"
 #include "mfma_tile.h"
 
@@ -41,6 +53,7 @@ constexpr int kHW = 64;                // heads per workgroup (16 per wavefront)
 constexpr int kTN = 32;                // rows per LDS tile
 constexpr int kRing = 4;               // LDS tile slots: kRing - 1 tiles in flight while one is computed
 constexpr int kRowsPerWave = kTN / 4;  // DMA instructions per wave and tile
+constexpr int kFoldU = 4;              // fold slice: sources per thread (at most)
 
 }  // namespace
 
@@ -50,6 +63,10 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   __shared__ __attribute__((aligned(1024))) char tiles[kRing][kTN * kRowB];
   __shared__ uint32_t rvalid[kRing][kTN / 4];  // byte r % 4 of word r / 4: row r is a real row
   __shared__ int s_restart;                // a wavefront asks the split to be recomputed
+  __shared__ Soft s_fpart[4][64];          // fold: per-wavefront partial states of <= 64 coordinates
+  __shared__ float s_fnew[64];             // fold: the new entry's coordinates (bf16-rounded)
+  __shared__ float s_fx[64];               // fold: the token's coordinates
+  __shared__ int s_fctx[8];                // fold: slice context kept over the row loop
 
   const int n_hg = a.H / kHW;
   const int L = blockIdx.x;
@@ -93,7 +110,9 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   if (n_c > a.E_cap) n_c = a.E_cap;
   if (n_c < 0) n_c = 0;
   const int64_t n_w = (t + 1) < a.n_win ? (t + 1) : a.n_win;
-  const int64_t n_rows = n_c + n_w;
+  // fold_mode: the query's own token is not in the window ring yet; the
+  // merge adds it as a row of its own
+  const int64_t n_rows = n_c + n_w - (a.fold_mode ? 1 : 0);
   const int r_begin = split * rows_per_split;
   const int r_end = (int)((int64_t)r_begin + rows_per_split < n_rows ? r_begin + rows_per_split : n_rows);
   const int nc32 = (int)n_c;
@@ -118,6 +137,21 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   int own = wbase + (int)n_w - 1;
   if (own >= wcap) own -= wcap;
   const uint16_t* pad_row = win + (size_t)own * kC;
+
+  // fold slice (fold_mode, head group 0): coordinates [fr0, fr0 + fW) of
+  // the entry completed by the block ending at t (entry lim - 1, stored
+  // only if it is the next one: fold_now).  Its context waits in LDS and
+  // its loads are issued after the row loop, so that none of it occupies
+  // registers during the loop.
+  if (a.fold_mode && tid == 0) {
+    const int fcs = a.fold_cs, fr0 = split * fcs;
+    s_fctx[0] = hg == 0 ? (a.c - fr0 < 0 ? 0 : (a.c - fr0 < fcs ? a.c - fr0 : fcs)) : 0;
+    s_fctx[1] = fr0;
+    s_fctx[2] = lim == (int64_t)cnt + 1 && cnt < a.E_cap;
+    s_fctx[3] = cnt;
+    s_fctx[4] = (int)(uint32_t)t;
+    s_fctx[5] = (int)(t >> 32);
+  }
 
   if (tid == 0) s_restart = 0;
   __syncthreads();  // s_restart ready
@@ -278,6 +312,80 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     prologue();
   }
 
+  // fold slice loads, in flight while the output is written.  The fold's
+  // arguments are read through the kernel-argument segment behind a
+  // compiler barrier, so they are not held in registers over the loop.
+  typedef const __attribute__((address_space(4))) AttendArgs KArgs;
+  KArgs* ka = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  __asm__ __volatile__("" : "+s"(ka));
+  KArgs& A = *ka;
+  const __attribute__((address_space(4))) FoldArgs& F = A.fold;
+  const int fW = A.fold_mode ? __builtin_amdgcn_readfirstlane(s_fctx[0]) : 0;
+  const int fr0 = __builtin_amdgcn_readfirstlane(s_fctx[1]);
+  const bool fold_now = fW > 0 && __builtin_amdgcn_readfirstlane(s_fctx[2]) != 0;
+  const int32_t fcnt = __builtin_amdgcn_readfirstlane(s_fctx[3]);
+  const int64_t ft = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(s_fctx[5]) << 32) |
+                               (uint32_t)__builtin_amdgcn_readfirstlane(s_fctx[4]));
+  // Thread (source group fj, coordinates fr0 + 8 fo ..) takes sources
+  // fj + fG u; fq: q_h over 4 coordinates for group g = tid + 256 u (head,
+  // 4 coordinates).
+  const int fTR = fW > 0 ? A.fold_cs / 8 : 1, fG = 256 / fTR;
+  const int fj = tid / fTR, fo = tid % fTR;
+  uint4 fz[kFoldU], fx[kFoldU];
+  float4 fb[kFoldU][2];
+  uint2 fq[4];
+  uint4 fapp = uint4{0, 0, 0, 0};
+#pragma unroll
+  for (int u = 0; u < kFoldU; ++u) {
+    fz[u] = fx[u] = uint4{0, 0, 0, 0};
+    fb[u][0] = fb[u][1] = float4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) fq[u] = uint2{0, 0};
+  const uint16_t* io = reinterpret_cast<const uint16_t*>(F.streams) + (size_t)b * 2 * A.c;
+  if (fW > 0) {
+    if (fold_now && fo * 8 < fW) {
+      const int64_t p0 = (int64_t)fcnt * F.m;  // first source token (entry fcnt)
+      const int slot0 = (int)(p0 % F.R);
+      const uint16_t* tl = reinterpret_cast<const uint16_t*>(F.tail) + (size_t)b * 2 * F.R * A.c;
+      const int cc = fr0 + fo * 8;
+#pragma unroll
+      for (int u = 0; u < kFoldU; ++u) {
+        const int j = fj + fG * u;
+        if (j < F.m) {
+          int slot = slot0 + j;
+          if (slot >= F.R) slot -= F.R;
+          const bool cur = p0 + j == ft;  // the current token is not in the tail yet
+          fz[u] = *reinterpret_cast<const uint4*>(cur ? io + A.c + cc : tl + ((size_t)F.R + slot) * A.c + cc);
+          fx[u] = *reinterpret_cast<const uint4*>(cur ? io + cc : tl + (size_t)slot * A.c + cc);
+          if (F.bias_a) {
+            fb[u][0] = *reinterpret_cast<const float4*>(F.bias_a + (size_t)j * A.c + cc);
+            fb[u][1] = *reinterpret_cast<const float4*>(F.bias_a + (size_t)j * A.c + cc + 4);
+          }
+        }
+      }
+    }
+    {
+      const int ng = H * fW / 4;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int g = tid + 256 * u;
+        if (g < ng) {
+          const int hh = g / (fW / 4), c4 = g % (fW / 4);
+          fq[u] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(A.q) +
+                                                  ((size_t)qrow * H + hh) * kC + fr0 + 4 * c4);
+        }
+      }
+    }
+    // the token's share for the rings: x_new, then streams 0 and 1 (8 coordinates each)
+    if (tid < 3 * fW / 8) {
+      const int which = tid / (fW / 8), cc = fr0 + 8 * (tid % (fW / 8));
+      const uint16_t* src = which == 0 ? reinterpret_cast<const uint16_t*>(F.x_new) + (size_t)b * A.c + cc
+                                       : io + (size_t)(which - 1) * A.c + cc;
+      fapp = *reinterpret_cast<const uint4*>(src);
+    }
+  }
+
   // per-head sum over the four lane groups
   float Lh = l_lane;
   Lh += __shfl_xor(Lh, 16, 64);
@@ -328,6 +436,113 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   for (int r = 0; r < 16; ++r)
     *reinterpret_cast<uint4*>(dst_row0 + r * ostride + 8 * l) =
         *reinterpret_cast<const uint4*>(stage + r * kOutLD + 8 * l);
+
+  if (fW > 0) {
+    if (fold_now) {
+      // merge the G = 256 / fTR source groups of each coordinate: in-thread
+      // over its sources, lanes fo, fo + fTR, ... of a wavefront, then the
+      // four wavefronts through LDS
+      Soft st[8];
+      {
+        float lg_[kFoldU][8], xv[kFoldU][8];
+        float mx[8];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) mx[v] = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < kFoldU; ++u) {
+          const bool ok = fo * 8 < fW && fj + fG * u < F.m;
+          float zz[8];
+          unpack16(fz[u], (const bf16*)nullptr, zz);
+          unpack16(fx[u], (const bf16*)nullptr, xv[u]);
+          const float zb[8] = {fb[u][0].x, fb[u][0].y, fb[u][0].z, fb[u][0].w,
+                               fb[u][1].x, fb[u][1].y, fb[u][1].z, fb[u][1].w};
+#pragma unroll
+          for (int v = 0; v < 8; ++v) {
+            lg_[u][v] = ok ? zz[v] + zb[v] : -INFINITY;
+            mx[v] = fmaxf(mx[v], lg_[u][v]);
+          }
+        }
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          float l_ = 0.f, acc_ = 0.f;
+#pragma unroll
+          for (int u = 0; u < kFoldU; ++u) {
+            const float e_ = lg_[u][v] == -INFINITY ? 0.f : __expf(lg_[u][v] - mx[v]);
+            l_ += e_;
+            acc_ += e_ * xv[u][v];
+          }
+          st[v] = Soft{mx[v], l_, acc_};
+        }
+      }
+      for (int msk = fTR; msk < 64; msk <<= 1) {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const Soft o{__shfl_xor(st[v].mx, msk, 64), __shfl_xor(st[v].l, msk, 64), __shfl_xor(st[v].acc, msk, 64)};
+          st[v] = soft_merge(st[v], o);
+        }
+      }
+      if (l < fTR) {
+#pragma unroll
+        for (int v = 0; v < 8; ++v)
+          if (fo * 8 + v < 64) s_fpart[w][fo * 8 + v] = st[v];
+      }
+      lds_barrier();
+      if (tid < fW) {
+        Soft acc0 = s_fpart[0][tid];
+#pragma unroll
+        for (int g = 1; g < 4; ++g) acc0 = soft_merge(acc0, s_fpart[g][tid]);
+        const uint16_t vb = f32_to_bf16(acc0.acc / acc0.l);
+        s_fnew[tid] = bf16_to_f32(vb);
+        reinterpret_cast<uint16_t*>(F.kv_cache)[((size_t)b * A.E_cap + fcnt) * kC + fr0 + tid] = vb;
+        A.fold_new[(size_t)b * kC + fr0 + tid] = vb;
+      }
+    }
+    // the token's coordinates (threads 0 .. fW / 8 - 1 hold x_new)
+    if (tid < fW / 8) {
+      float xv[8];
+      unpack16(fapp, (const bf16*)nullptr, xv);
+#pragma unroll
+      for (int v = 0; v < 8; ++v) s_fx[8 * tid + v] = xv[v];
+    }
+    lds_barrier();
+    // this slice's share of q_h . entry and q_h . token, summed over the
+    // fW / 4 groups of a head
+    const int gph = fW / 4, ng = H * gph;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int g = tid + 256 * u;
+      if (256 * u < ng) {
+        float pn = 0.f, po = 0.f;
+        if (g < ng) {
+          const int c4 = g % gph;
+          const uint2 qv = fq[u];
+          const float q0 = __uint_as_float(qv.x << 16), q1 = __uint_as_float(qv.x & 0xffff0000u);
+          const float q2 = __uint_as_float(qv.y << 16), q3 = __uint_as_float(qv.y & 0xffff0000u);
+          po = q0 * s_fx[4 * c4] + q1 * s_fx[4 * c4 + 1] + q2 * s_fx[4 * c4 + 2] + q3 * s_fx[4 * c4 + 3];
+          if (fold_now)
+            pn = q0 * s_fnew[4 * c4] + q1 * s_fnew[4 * c4 + 1] + q2 * s_fnew[4 * c4 + 2] + q3 * s_fnew[4 * c4 + 3];
+        }
+        for (int o = 1; o < gph; o <<= 1) {
+          po += __shfl_xor(po, o, 64);
+          pn += __shfl_xor(pn, o, 64);
+        }
+        if (g < ng && g % gph == 0) {
+          float* fs = A.fold_s + 2 * ((size_t)b * H + g / gph);
+          atomicAdd(fs + 1, po);
+          if (fold_now) atomicAdd(fs, pn);
+        }
+      }
+    }
+    // the token's share of the rings (every step)
+    if (tid < 3 * fW / 8) {
+      const int which = tid / (fW / 8), cc = fr0 + 8 * (tid % (fW / 8));
+      uint16_t* dst = which == 0
+                          ? reinterpret_cast<uint16_t*>(F.win_ring) + ((size_t)b * F.n_win + ft % F.n_win) * A.c + cc
+                          : reinterpret_cast<uint16_t*>(F.tail) + (((size_t)b * 2 + (which - 1)) * F.R + ft % F.R) * A.c + cc;
+      *reinterpret_cast<uint4*>(dst) = fapp;
+    }
+    if (split == 0 && tid == 0) A.fold_row[b] = fold_now ? fcnt + 1 : 0;
+  }
 }
 
 // grid (B*Tq, H), 256 threads: wavefront w merges splits w, w+4, ... of one
@@ -343,6 +558,20 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
   const float* pml = reinterpret_cast<const float*>(a.ws);
   const uint16_t* po = reinterpret_cast<const uint16_t*>(pml + (size_t)a.B * a.Tq * n_split * H * 2);
   const float z2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+  // fold_mode: the query's own token and the step's new entry (if any) as
+  // two more rows, weights exp2(s_own - M) and exp2(s_new - M)
+  const int b = qrow / a.Tq;
+  const int frow = a.fold_mode ? a.fold_row[b] : 0;
+  float2 fsv = float2{0.f, 0.f};
+  if (a.fold_mode) fsv = *reinterpret_cast<const float2*>(a.fold_s + 2 * ((size_t)b * H + h));
+  const float s_new = frow > 0 ? fsv.x * (a.scale * kLog2e) : -INFINITY;
+  const float s_own = a.fold_mode ? fsv.y * (a.scale * kLog2e) : -INFINITY;
+  // (fixed addresses: every load is issued at once)
+  uint4 nrow = uint4{0, 0, 0, 0}, xrow = nrow;
+  if (a.fold_mode) {
+    nrow = *reinterpret_cast<const uint4*>(a.fold_new + (size_t)b * kC + 8 * l);
+    xrow = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.fold.x_new) + (size_t)b * kC + 8 * l);
+  }
   // lane s holds split s's statistics
   float ms = -INFINITY, Ls = 0.f;
   if (l < n_split) {
@@ -350,7 +579,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
     ms = v.x;
     Ls = v.y;
   }
-  const float M = fmaxf(wave_max(ms), z2);
+  const float M = fmaxf(fmaxf(fmaxf(wave_max(ms), z2), s_new), s_own);
   const float wgt = (ms == -INFINITY || Ls == 0.f) ? 0.f : exp2f(ms - M) * Ls;
   // this wavefront's splits: all loads first
   uint4 raw[kMergeU];
@@ -379,17 +608,30 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) s_o[w][8 * l + i] = o[i];
+  const float w_new = frow > 0 ? exp2f(s_new - M) : 0.f;
+  const float w_own = a.fold_mode ? exp2f(s_own - M) : 0.f;
   if (w == 0) {
-    const float den = wave_sum(wgt) + (z2 == -INFINITY ? 0.f : exp2f(z2 - M));
+    const float den = wave_sum(wgt) + (z2 == -INFINITY ? 0.f : exp2f(z2 - M)) + w_new + w_own;
     if (l == 0) s_den = den;
   }
   __syncthreads();
   if (w != 0) return;
+  if (a.fold_mode && l == 0) {
+    *reinterpret_cast<float2*>(a.fold_s + 2 * ((size_t)b * H + h)) = float2{0.f, 0.f};  // zero for the next call
+    if (h == 0 && frow > 0) a.fold.n_entries[b] = frow;  // publish the new entry count
+  }
   const float den = s_den;
   const float inv = 1.f / den;
+  const uint32_t nw[4] = {nrow.x, nrow.y, nrow.z, nrow.w}, xw[4] = {xrow.x, xrow.y, xrow.z, xrow.w};
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    o[i] = (s_o[0][8 * l + i] + s_o[1][8 * l + i] + s_o[2][8 * l + i] + s_o[3][8 * l + i]) * inv;
+  for (int i = 0; i < 8; ++i) {
+    const float nv = bf16_to_f32((uint16_t)((nw[i >> 1] >> (16 * (i & 1))) & 0xffff));
+    const float xv = bf16_to_f32((uint16_t)((xw[i >> 1] >> (16 * (i & 1))) & 0xffff));
+    // (the new entry's row holds old data when no entry was completed)
+    o[i] = (s_o[0][8 * l + i] + s_o[1][8 * l + i] + s_o[2][8 * l + i] + s_o[3][8 * l + i] +
+            (frow > 0 ? w_new * nv : 0.f) + w_own * xv) *
+           inv;
+  }
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * H + h) * kC + 8 * l;
   uint4 r;
   r.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
@@ -401,6 +643,37 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
 }
 
 bool attend_mfma_shape_ok(int H, int c) { return c == kC && H % kHW == 0; }
+
+size_t attend_fold_ws_offset(int B, int Tq, int H, int c, int rows_max);
+void attend_mfma_plan(int BT, int H, int rows_max, int* n_split, int* rows_per_split);
+
+// HCA decode (one query per sequence, no overlap, bf16) with at least two
+// row splits (the merge adds the new entry): the coordinates split into
+// power-of-two slices of 8..64, one per split, every source token of a
+// block handled by one thread of its slice.
+bool attend_fuses_fold(AttendArgs& a, const FoldArgs& f) {
+  a.fold_mode = 0;
+  if (!a.dense || a.dtype != BF16 || f.dtype != BF16 || !attend_mfma_shape_ok(a.H, a.c) || a.Tq != 1 ||
+      a.n_add != 0 || a.win_pos0 != nullptr || a.win_pos0_const != 0 || f.overlap || f.idx_dtype >= 0 ||
+      f.B != a.B || f.c != a.c || f.n_win != a.W_cap || f.R < 2 * f.m)
+    return false;
+  int ns, rps;
+  attend_mfma_plan(a.B * a.Tq, a.H, a.E_cap + a.n_win, &ns, &rps);
+  if (ns < 2) return false;
+  int cs = 8;
+  while (cs * ns < a.c) cs *= 2;
+  if (cs > 64 || f.m > kFoldU * (256 / (cs / 8)) || a.H * cs > 4096) return false;
+  const size_t off = attend_fold_ws_offset(a.B, a.Tq, a.H, a.c, a.E_cap + a.n_win);
+  char* base = reinterpret_cast<char*>(a.ws);
+  a.fold_s = reinterpret_cast<float*>(base + off);
+  const size_t off_row = off + ((size_t)a.B * a.H * 8 + 255) / 256 * 256;
+  a.fold_row = reinterpret_cast<int32_t*>(base + off_row);
+  a.fold_new = reinterpret_cast<uint16_t*>(base + off_row + ((size_t)a.B * 4 + 255) / 256 * 256);
+  a.fold = f;
+  a.fold_cs = cs;
+  a.fold_mode = 1;
+  return true;
+}
 
 // Row splits per (query, head group): about one workgroup per CU (256), each
 // split a multiple of 16 rows, at most kMaxSplit splits.

@@ -135,8 +135,20 @@ struct AttendArgs {
   float* lse;
   void* ws;
   size_t ws_bytes;
+  // dense decode with the step's fold inside (see attend_fuses_fold): each
+  // split folds fold_cs coordinates of the new entry and adds its share of
+  // q . entry and q . token to fold_s; the merge adds the new entry and the
+  // query's own token as two more rows
+  int fold_mode;
+  int fold_cs;
+  FoldArgs fold;
+  float* fold_s;       // [B][H][2]: q . new entry, q . own token; zero between calls
+  int32_t* fold_row;   // [B]: new entry index + 1, or 0
+  uint16_t* fold_new;  // [B][c]: the new entry (bf16), read by the merge
 };
 size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max);
+// whether hca decode can fold inside the attention; sets a.fold_mode / fold_cs
+bool attend_fuses_fold(AttendArgs& a, const FoldArgs& f);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 
 }  // namespace csa
