@@ -53,7 +53,7 @@ constexpr int kHW = 64;                // heads per workgroup (16 per wavefront)
 constexpr int kTN = 32;                // rows per LDS tile
 constexpr int kRing = 4;               // LDS tile slots: kRing - 1 tiles in flight while one is computed
 constexpr int kRowsPerWave = kTN / 4;  // DMA instructions per wave and tile
-constexpr int kFoldU = 4;              // fold slice: sources per thread (at most)
+constexpr int kFoldS = 16;             // fold slice: sources per thread (at most)
 
 }  // namespace
 
@@ -63,10 +63,11 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   __shared__ __attribute__((aligned(1024))) char tiles[kRing][kTN * kRowB];
   __shared__ uint32_t rvalid[kRing][kTN / 4];  // byte r % 4 of word r / 4: row r is a real row
   __shared__ int s_restart;                // a wavefront asks the split to be recomputed
+  __shared__ bf16x8_t s_p[4][64];          // P^T operands of the tile, one block of 16 heads per wavefront
+  __shared__ float s_scale[kHW];           // output scale per head
   __shared__ Soft s_fpart[4][64];          // fold: per-wavefront partial states of <= 64 coordinates
   __shared__ float s_fnew[64];             // fold: the new entry's coordinates (bf16-rounded)
-  __shared__ float s_fx[64];               // fold: the token's coordinates
-  __shared__ int s_fctx[8];                // fold: slice context kept over the row loop
+  __shared__ uint4 s_fapp[24];             // fold: x_new, stream 0, stream 1 slices (<= 64 coordinates each)
 
   const int n_hg = a.H / kHW;
   const int L = blockIdx.x;
@@ -138,19 +139,60 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   if (own >= wcap) own -= wcap;
   const uint16_t* pad_row = win + (size_t)own * kC;
 
-  // fold slice (fold_mode, head group 0): coordinates [fr0, fr0 + fW) of
-  // the entry completed by the block ending at t (entry lim - 1, stored
-  // only if it is the next one: fold_now).  Its context waits in LDS and
-  // its loads are issued after the row loop, so that none of it occupies
-  // registers during the loop.
-  if (a.fold_mode && tid == 0) {
-    const int fcs = a.fold_cs, fr0 = split * fcs;
-    s_fctx[0] = hg == 0 ? (a.c - fr0 < 0 ? 0 : (a.c - fr0 < fcs ? a.c - fr0 : fcs)) : 0;
-    s_fctx[1] = fr0;
-    s_fctx[2] = lim == (int64_t)cnt + 1 && cnt < a.E_cap;
-    s_fctx[3] = cnt;
-    s_fctx[4] = (int)(uint32_t)t;
-    s_fctx[5] = (int)(t >> 32);
+  // ---- fold slice (fold_mode, head group 0): coordinates [fr0, fr0 + fW)
+  // of entry cnt, completed by the block ending at t (stored only if it is
+  // the next entry: fold_now), this slice's share of q_h . entry and
+  // q_h . token, and the token's share of the rings.  Its inputs come by DMA
+  // into LDS ahead of the first tiles (ring slot kRing - 1 and the P^T
+  // buffer are unused until the row loop starts), so the fold runs while
+  // those tiles are in flight and nothing of it is live during the loop.
+  const int fcs = a.fold_cs, fr0 = split * fcs;
+  const int fW = (a.fold_mode && hg == 0) ? (a.c - fr0 < 0 ? 0 : (a.c - fr0 < fcs ? a.c - fr0 : fcs)) : 0;
+  const bool fold_now = fW > 0 && lim == (int64_t)cnt + 1 && cnt < a.E_cap;
+  const FoldArgs& F = a.fold;
+  const int fch = fW / 8;                                  // 16-byte chunks per slice row (bf16)
+  char* const fz_l = tiles[kRing - 1];                     // [m][fW] bf16: stream 1 (logits)
+  char* const fx_l = fz_l + (size_t)F.m * fW * 2;          // [m][fW] bf16: stream 0 (values)
+  char* const fb_l = fx_l + (size_t)F.m * fW * 2;          // [m][fW] f32: positional bias
+  char* const fq_l = reinterpret_cast<char*>(&s_p[0][0]);  // [H][fW] bf16: query slice
+  char* const fa_l = reinterpret_cast<char*>(s_fapp);      // [3][fW] bf16: x_new, streams 0, 1
+  const uint16_t* const fio = reinterpret_cast<const uint16_t*>(F.streams) + (size_t)b * 2 * a.c;
+  if (fW > 0) {
+    // instruction k of a region moves its 16-byte chunks 64k .. 64k + 63,
+    // one per lane, to LDS bytes 1024k ..; wavefront k % 4 issues it
+    auto region = [&](int nq, char* dst, auto addr) {
+      const int nk = (nq + 63) / 64;
+      for (int k = w; k < nk; k += 4) {
+        const int qq = 64 * k + l;
+        if (qq < nq) dma16_m0(addr(qq), lds_addr(dst + 1024 * k));
+      }
+    };
+    if (fold_now) {
+      const int64_t p0 = (int64_t)cnt * F.m;  // first source token
+      const int slot0 = p0 < 0x7fffffff ? (int)((uint32_t)p0 % (uint32_t)F.R) : (int)(p0 % F.R);
+      const uint16_t* tl = reinterpret_cast<const uint16_t*>(F.tail) + (size_t)b * 2 * F.R * a.c;
+      auto src = [&](int qq, int stream) -> const void* {
+        const int j = qq / fch, cc = fr0 + 8 * (qq % fch);
+        int slot = slot0 + j;
+        if (slot >= F.R) slot -= F.R;
+        if (p0 + j == t) return fio + (size_t)stream * a.c + cc;  // the current token is not in the tail yet
+        return tl + ((size_t)stream * F.R + slot) * a.c + cc;
+      };
+      region(F.m * fch, fz_l, [&](int qq) { return src(qq, 1); });
+      region(F.m * fch, fx_l, [&](int qq) { return src(qq, 0); });
+      if (F.bias_a)
+        region(F.m * fW / 4, fb_l, [&](int qq) -> const void* {
+          return F.bias_a + (size_t)(qq / (fW / 4)) * a.c + fr0 + 4 * (qq % (fW / 4));
+        });
+    }
+    region(H * fch, fq_l, [&](int qq) -> const void* {
+      return reinterpret_cast<const uint16_t*>(a.q) + ((size_t)qrow * H + qq / fch) * kC + fr0 + 8 * (qq % fch);
+    });
+    region(3 * fch, fa_l, [&](int qq) -> const void* {
+      const int which = qq / fch, cc = fr0 + 8 * (qq % fch);
+      return which == 0 ? reinterpret_cast<const uint16_t*>(F.x_new) + (size_t)b * a.c + cc
+                        : fio + (size_t)(which - 1) * a.c + cc;
+    });
   }
 
   if (tid == 0) s_restart = 0;
@@ -193,8 +235,122 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   };
   prologue();
 
-  // running softmax state: the reference max per head (identical in the 4
-  // lane groups), the sum per lane over its own rows, O^T[512 d x 16 heads]
+  if (fW > 0) {
+    // this wavefront's fold DMAs are older than its tile DMAs
+    const int n_pro = r_end > r_begin ? kRowsPerWave * min(kRing - 1, (r_end - r_begin + kTN - 1) / kTN) : 0;
+    static_assert(kRing - 1 == 3, "tile DMA counts below");
+    if (n_pro >= 3 * kRowsPerWave) __builtin_amdgcn_s_waitcnt(wait_vm(3 * kRowsPerWave));
+    else if (n_pro == 2 * kRowsPerWave) __builtin_amdgcn_s_waitcnt(wait_vm(2 * kRowsPerWave));
+    else if (n_pro == kRowsPerWave) __builtin_amdgcn_s_waitcnt(wait_vm(kRowsPerWave));
+    else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    lds_barrier();
+    if (fold_now) {
+      // thread (coordinate fc, source group fg of G = 256 / fW) folds
+      // sources fg, fg + G, ... of its coordinate; the G partial states of
+      // a coordinate merge across lanes (xor fW .. 32) and then across the
+      // wavefronts.  (Reads: the lanes of one source row are consecutive
+      // coordinates, adjacent groups adjacent rows.)
+      const int fc = tid % fW, fg = tid / fW, G = 256 / fW;
+      const uint16_t* zr = reinterpret_cast<const uint16_t*>(fz_l) + fc;
+      const uint16_t* xr = reinterpret_cast<const uint16_t*>(fx_l) + fc;
+      const float* br = reinterpret_cast<const float*>(fb_l) + fc;
+      // all kFoldS sources' reads in flight together, branch-free
+      const bool has_bias = F.bias_a != nullptr;  // (else the bias region is not loaded)
+      float lgv[kFoldS], xvv[kFoldS];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kFoldS; ++u) {
+        const int j = fg + G * u;
+        const bool ok = j < F.m;
+        const int e = (ok ? j : 0) * fW;
+        const float zb = br[e];
+        // (every read is made; an absent source adds -inf, which keeps the
+        // reads out of conditional blocks)
+        lgv[u] = (bf16_to_f32(zr[e]) + (has_bias ? zb : 0.f)) + (ok ? 0.f : -INFINITY);
+        xvv[u] = bf16_to_f32(xr[e]);
+        mx = fmaxf(mx, lgv[u]);
+      }
+      float l_ = 0.f, a_ = 0.f;
+#pragma unroll
+      for (int u = 0; u < kFoldS; ++u) {
+        const float e_ = lgv[u] == -INFINITY ? 0.f : __expf(lgv[u] - mx);
+        l_ += e_;
+        a_ += e_ * xvv[u];
+      }
+      Soft st{mx, l_, a_};
+#pragma unroll
+      for (int k = 3; k < 6; ++k) {  // xor fW .. 32 (fW >= 8)
+        const int msk = 1 << k;
+        if (msk < fW) continue;
+        const Soft o{__shfl_xor(st.mx, msk, 64), __shfl_xor(st.l, msk, 64), __shfl_xor(st.acc, msk, 64)};
+        st = soft_merge_sel(st, o);
+      }
+      if (l < fW) s_fpart[w][fc] = st;
+      lds_barrier();
+      if (tid < fW) {
+        Soft acc0 = s_fpart[0][tid];
+#pragma unroll
+        for (int g = 1; g < 4; ++g) acc0 = soft_merge_sel(acc0, s_fpart[g][tid]);
+        const uint16_t vb = f32_to_bf16(acc0.acc / acc0.l);
+        s_fnew[tid] = bf16_to_f32(vb);
+        reinterpret_cast<uint16_t*>(F.kv_cache)[((size_t)b * a.E_cap + cnt) * kC + fr0 + tid] = vb;
+        a.fold_new[(size_t)b * kC + fr0 + tid] = vb;
+      }
+      lds_barrier();
+    }
+    // this slice's share of q_h . entry and q_h . token: thread (head,
+    // 8 coordinates), summed over the fch lanes of a head
+    {
+      const uint16_t* xq = reinterpret_cast<const uint16_t*>(fa_l);  // x_new slice
+      const int ng = H * fch;
+      for (int g0 = 0; g0 < ng; g0 += 256) {
+        const int g = g0 + tid;
+        float pn = 0.f, po = 0.f;
+        if (g < ng) {
+          const int hh = g / fch, c8 = 8 * (g % fch);
+          float qv[8], xv[8];
+          unpack16(*reinterpret_cast<const uint4*>(fq_l + 2 * (hh * fW + c8)), (const bf16*)nullptr, qv);
+          unpack16(*reinterpret_cast<const uint4*>(xq + c8), (const bf16*)nullptr, xv);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) po += qv[i] * xv[i];
+          if (fold_now) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) pn += qv[i] * s_fnew[c8 + i];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {  // fch <= 8
+          const int o = 1 << k;
+          if (o >= fch) break;
+          po += __shfl_xor(po, o, 64);
+          pn += __shfl_xor(pn, o, 64);
+        }
+        if (g < ng && g % fch == 0) {
+          float* fs = a.fold_s + 2 * ((size_t)b * H + g / fch);
+          atomicAdd(fs + 1, po);
+          if (fold_now) atomicAdd(fs, pn);
+        }
+      }
+    }
+    // the token's share of the rings (every step)
+    if (tid < 3 * fch) {
+      const int which = tid / fch, cc = fr0 + 8 * (tid % fch);
+      const bool small = t < 0x7fffffff;  // 32-bit remainders
+      const int ws = small ? (int)((uint32_t)t % (uint32_t)F.n_win) : (int)(t % F.n_win);
+      const int ts = small ? (int)((uint32_t)t % (uint32_t)F.R) : (int)(t % F.R);
+      uint16_t* dst = which == 0 ? reinterpret_cast<uint16_t*>(F.win_ring) + ((size_t)b * F.n_win + ws) * a.c + cc
+                                 : reinterpret_cast<uint16_t*>(F.tail) + (((size_t)b * 2 + (which - 1)) * F.R + ts) * a.c + cc;
+      *reinterpret_cast<uint4*>(dst) = s_fapp[tid];
+    }
+    if (split == 0 && tid == 0) a.fold_row[b] = fold_now ? cnt + 1 : 0;
+    // the tile waits below count DMAs only
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  }
+
+  // running softmax state of this wavefront's 16 heads: the reference max
+  // per head (identical in the 4 lane groups), the sum per lane over its own
+  // rows; accumulator: O^T[128 d x 64 heads] for the wavefront's quarter of
+  // the coordinates (acc[4 dtl + hb]: d 128 w + 16 dtl .., heads 16 hb ..)
   f32x4_t acc[32];
 #pragma unroll
   for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -207,17 +363,17 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
 
   auto compute_tile = [&](int buf) {
     const char* T = tiles[buf];
-    // S^T[32 rows x 16 heads] = K . Q^T as two 16-row blocks
-    // (the block chains interleave, so consecutive MFMAs are independent)
+    // S^T[32 rows x 16 heads] = K . Q^T as two 16-row blocks, each summed
+    // in two halves (even / odd k steps): four independent MFMA chains
     constexpr int kRB = kTN / 16;
-    f32x4_t s[kRB];
+    f32x4_t s2[kRB][2];
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) s[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int rb = 0; rb < kRB; ++rb) s2[rb][0] = s2[rb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks)
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb)
-        s[rb] = mfma32(lds8(T + s_base[ks & 3] + rb * 16 * kRowB + 256 * (ks >> 2)), qf[ks], s[rb]);
+        s2[rb][ks & 1] = mfma32(lds8(T + s_base[ks & 3] + rb * 16 * kRowB + 256 * (ks >> 2)), qf[ks], s2[rb][ks & 1]);
     // keep 12 fragment reads in flight ahead of the MFMAs (lgkmcnt counts 15)
     __builtin_amdgcn_sched_group_barrier(0x100, 12, 1);
 #pragma unroll
@@ -226,6 +382,9 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 12, 1);
+    f32x4_t s[kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) s[rb] = s2[rb][0] + s2[rb][1];
     // softmax weights against a fixed reference max per head; lane holds
     // rows 16rb + 4lg + i of head li.  The reference is the first tile's max
     // and stays put while tile maxima exceed it by at most kSlack (log2
@@ -260,32 +419,40 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
       }
       pb[rb] = bf16x4_t{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
     }
-    // O^T[d x heads] += V^T[d x 32 rows] . P^T[32 rows x heads] per row pair
+    // P^T of all four head blocks through LDS; then
+    // O^T[d x 64 heads] += V^T[d x 32 rows] . P^T[32 rows x 64 heads] for
+    // this wavefront's 128 coordinates: each V^T block (two transposed
+    // reads) serves four MFMAs, so a tile is transpose-read once per
+    // workgroup instead of once per wavefront
+    static_assert(kRB == 2, "one row pair per tile");
+    s_p[w][l] = __builtin_shufflevector(pb[0], pb[1], 0, 1, 2, 3, 4, 5, 6, 7);
+    lds_barrier();
+    bf16x8_t pa[4];
 #pragma unroll
-    for (int pr = 0; pr < kRB / 2; ++pr) {
-      const bf16x8_t pB = __builtin_shufflevector(pb[2 * pr], pb[2 * pr + 1], 0, 1, 2, 3, 4, 5, 6, 7);
-      const char* vp = T + pr * 32 * kRowB;
+    for (int hb = 0; hb < 4; ++hb) pa[hb] = s_p[hb][l];
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
-        const char* v0 = vp + t_base[dt & 7] + 256 * (dt >> 3);
-        acc[dt] = mfma32(cat8(ld_tr(v0), ld_tr(v0 + 16 * kRowB)), pB, acc[dt]);
-      }
+    for (int dtl = 0; dtl < 8; ++dtl) {
+      const char* v0 = T + t_base[dtl] + 256 * w;
+      const bf16x8_t va = cat8(ld_tr(v0), ld_tr(v0 + 16 * kRowB));
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) acc[4 * dtl + hb] = mfma32(va, pa[hb], acc[4 * dtl + hb]);
     }
-    // keep 7 MFMAs' worth of transpose reads in flight
-    __builtin_amdgcn_sched_group_barrier(0x100, 14, 2);
+    // the P^T reads and two V^T blocks ahead, then one V^T block per four MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 2);
 #pragma unroll
-    for (int i = 0; i < 32 * (kRB / 2) - 7; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 7, 2);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 2);
   };
 
-  // ring of kRing tile slots, one barrier per tile: a wave first waits for
-  // its own DMAs of tile i (the younger tiles i+1, i+2 may stay in flight);
-  // after the barrier every wave's DMAs of tile i have landed and every wave
-  // has finished tile i-1, so tile i+kRing-1 may be fetched into that slot
-  // while tile i is computed.
+  // ring of kRing tile slots: a wave first waits for its own DMAs of tile i
+  // (the younger tiles i+1, i+2 may stay in flight); after the barrier every
+  // wave's DMAs of tile i have landed and every wave has finished tile i-1
+  // (and read its P^T blocks), so tile i+kRing-1 may be fetched into that
+  // slot while tile i is computed.  A second barrier inside the tile
+  // publishes the P^T blocks.
   static_assert(kRing == 4, "the waits below assume two younger tiles");
   for (;;) {
     int buf = 0;
@@ -312,237 +479,66 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     prologue();
   }
 
-  // fold slice loads, in flight while the output is written.  The fold's
-  // arguments are read through the kernel-argument segment behind a
-  // compiler barrier, so they are not held in registers over the loop.
-  typedef const __attribute__((address_space(4))) AttendArgs KArgs;
-  KArgs* ka = (KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  __asm__ __volatile__("" : "+s"(ka));
-  KArgs& A = *ka;
-  const __attribute__((address_space(4))) FoldArgs& F = A.fold;
-  const int fW = A.fold_mode ? __builtin_amdgcn_readfirstlane(s_fctx[0]) : 0;
-  const int fr0 = __builtin_amdgcn_readfirstlane(s_fctx[1]);
-  const bool fold_now = fW > 0 && __builtin_amdgcn_readfirstlane(s_fctx[2]) != 0;
-  const int32_t fcnt = __builtin_amdgcn_readfirstlane(s_fctx[3]);
-  const int64_t ft = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane(s_fctx[5]) << 32) |
-                               (uint32_t)__builtin_amdgcn_readfirstlane(s_fctx[4]));
-  // Thread (source group fj, coordinates fr0 + 8 fo ..) takes sources
-  // fj + fG u; fq: q_h over 4 coordinates for group g = tid + 256 u (head,
-  // 4 coordinates).
-  const int fTR = fW > 0 ? A.fold_cs / 8 : 1, fG = 256 / fTR;
-  const int fj = tid / fTR, fo = tid % fTR;
-  uint4 fz[kFoldU], fx[kFoldU];
-  float4 fb[kFoldU][2];
-  uint2 fq[4];
-  uint4 fapp = uint4{0, 0, 0, 0};
-#pragma unroll
-  for (int u = 0; u < kFoldU; ++u) {
-    fz[u] = fx[u] = uint4{0, 0, 0, 0};
-    fb[u][0] = fb[u][1] = float4{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) fq[u] = uint2{0, 0};
-  const uint16_t* io = reinterpret_cast<const uint16_t*>(F.streams) + (size_t)b * 2 * A.c;
-  if (fW > 0) {
-    if (fold_now && fo * 8 < fW) {
-      const int64_t p0 = (int64_t)fcnt * F.m;  // first source token (entry fcnt)
-      const int slot0 = (int)(p0 % F.R);
-      const uint16_t* tl = reinterpret_cast<const uint16_t*>(F.tail) + (size_t)b * 2 * F.R * A.c;
-      const int cc = fr0 + fo * 8;
-#pragma unroll
-      for (int u = 0; u < kFoldU; ++u) {
-        const int j = fj + fG * u;
-        if (j < F.m) {
-          int slot = slot0 + j;
-          if (slot >= F.R) slot -= F.R;
-          const bool cur = p0 + j == ft;  // the current token is not in the tail yet
-          fz[u] = *reinterpret_cast<const uint4*>(cur ? io + A.c + cc : tl + ((size_t)F.R + slot) * A.c + cc);
-          fx[u] = *reinterpret_cast<const uint4*>(cur ? io + cc : tl + (size_t)slot * A.c + cc);
-          if (F.bias_a) {
-            fb[u][0] = *reinterpret_cast<const float4*>(F.bias_a + (size_t)j * A.c + cc);
-            fb[u][1] = *reinterpret_cast<const float4*>(F.bias_a + (size_t)j * A.c + cc + 4);
-          }
-        }
-      }
-    }
-    {
-      const int ng = H * fW / 4;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int g = tid + 256 * u;
-        if (g < ng) {
-          const int hh = g / (fW / 4), c4 = g % (fW / 4);
-          fq[u] = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(A.q) +
-                                                  ((size_t)qrow * H + hh) * kC + fr0 + 4 * c4);
-        }
-      }
-    }
-    // the token's share for the rings: x_new, then streams 0 and 1 (8 coordinates each)
-    if (tid < 3 * fW / 8) {
-      const int which = tid / (fW / 8), cc = fr0 + 8 * (tid % (fW / 8));
-      const uint16_t* src = which == 0 ? reinterpret_cast<const uint16_t*>(F.x_new) + (size_t)b * A.c + cc
-                                       : io + (size_t)(which - 1) * A.c + cc;
-      fapp = *reinterpret_cast<const uint4*>(src);
-    }
-  }
-
-  // per-head sum over the four lane groups
+  // per-head sum over the four lane groups (this wavefront's 16 heads)
   float Lh = l_lane;
   Lh += __shfl_xor(Lh, 16, 64);
   Lh += __shfl_xor(Lh, 32, 64);
   const int h = h0 + li;
 
   // Output rows leave through LDS so that every store instruction writes one
-  // contiguous 1 KB row: lane (head li) holds d = 16dt + 4lg + i of O^T; it
-  // writes them scaled and rounded to row li of its wavefront's [16][520]
-  // bf16 staging block (row stride 1040 B keeps the 8-byte writes of 32
-  // lanes on distinct banks), then lane l copies 16 bytes of each row.
-  float f;  // output scale for this lane's head
+  // contiguous 1 KB row.  The head owners publish their scales; lane (head
+  // li of block hb) holds d = 128 w + 16 dtl + 4 lg + i of O^T and writes
+  // them scaled and rounded to row 16 hb + li of the [64][520] bf16 staging
+  // block (row stride 1040 B spreads the 8-byte writes over the banks);
+  // then wavefront w copies the rows of its 16 heads, 16 bytes per lane.
   uint16_t* dst_row0;  // row of this wavefront's first head
   const size_t ostride = kC;
-  if (n_split == 1) {
-    const float z2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
-    const float M = fmaxf(m_run, z2);
-    const float em = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
-    const float den = Lh * em + (z2 == -INFINITY ? 0.f : exp2f(z2 - M));
-    f = em / den;
-    if (a.lse && lg == 0) a.lse[(size_t)qrow * H + h] = (M + log2f(den)) * kLn2;
-    dst_row0 = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * H + h0) * kC;
-  } else {
-    // partial: (m, L) and O / L in bf16
-    float* pml = reinterpret_cast<float*>(a.ws);
-    uint16_t* po = reinterpret_cast<uint16_t*>(pml + (size_t)a.B * a.Tq * n_split * H * 2);
-    const size_t slot = ((size_t)qrow * n_split + split) * H + h;
-    if (lg == 0) {
-      pml[2 * slot] = m_run;
-      pml[2 * slot + 1] = Lh;
+  {
+    float f;  // output scale for this lane's head
+    if (n_split == 1) {
+      const float z2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+      const float M = fmaxf(m_run, z2);
+      const float em = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
+      const float den = Lh * em + (z2 == -INFINITY ? 0.f : exp2f(z2 - M));
+      f = em / den;
+      if (a.lse && lg == 0) a.lse[(size_t)qrow * H + h] = (M + log2f(den)) * kLn2;
+      dst_row0 = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * H + h0) * kC;
+    } else {
+      // partial: (m, L) and O / L in bf16
+      float* pml = reinterpret_cast<float*>(a.ws);
+      uint16_t* po = reinterpret_cast<uint16_t*>(pml + (size_t)a.B * a.Tq * n_split * H * 2);
+      const size_t slot = ((size_t)qrow * n_split + split) * H + h;
+      if (lg == 0) {
+        pml[2 * slot] = m_run;
+        pml[2 * slot + 1] = Lh;
+      }
+      f = Lh > 0.f ? 1.f / Lh : 0.f;
+      dst_row0 = po + (((size_t)qrow * n_split + split) * H + h0) * kC;
     }
-    f = Lh > 0.f ? 1.f / Lh : 0.f;
-    dst_row0 = po + (((size_t)qrow * n_split + split) * H + h0) * kC;
+    if (lg == 0) s_scale[16 * w + li] = f;
   }
+  lds_barrier();
   constexpr int kOutLD = kC + 8;  // staging row stride (elements)
-  uint16_t* stage = reinterpret_cast<uint16_t*>(tiles[0]) + w * 16 * kOutLD;
+  uint16_t* stage = reinterpret_cast<uint16_t*>(tiles[0]);
 #pragma unroll
-  for (int dt = 0; dt < 32; ++dt) {
-    ushort4 v;
-    v.x = f32_to_bf16(acc[dt][0] * f);
-    v.y = f32_to_bf16(acc[dt][1] * f);
-    v.z = f32_to_bf16(acc[dt][2] * f);
-    v.w = f32_to_bf16(acc[dt][3] * f);
-    *reinterpret_cast<ushort4*>(stage + li * kOutLD + 16 * dt + 4 * lg) = v;
+  for (int hb = 0; hb < 4; ++hb) {
+    const float f = s_scale[16 * hb + li];
+#pragma unroll
+    for (int dtl = 0; dtl < 8; ++dtl) {
+      const f32x4_t v4 = acc[4 * dtl + hb];
+      ushort4 v;
+      v.x = f32_to_bf16(v4[0] * f);
+      v.y = f32_to_bf16(v4[1] * f);
+      v.z = f32_to_bf16(v4[2] * f);
+      v.w = f32_to_bf16(v4[3] * f);
+      *reinterpret_cast<ushort4*>(stage + (16 * hb + li) * kOutLD + 128 * w + 16 * dtl + 4 * lg) = v;
+    }
   }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wavefront's LDS writes (lgkmcnt 0)
+  lds_barrier();
 #pragma unroll
   for (int r = 0; r < 16; ++r)
     *reinterpret_cast<uint4*>(dst_row0 + r * ostride + 8 * l) =
-        *reinterpret_cast<const uint4*>(stage + r * kOutLD + 8 * l);
-
-  if (fW > 0) {
-    if (fold_now) {
-      // merge the G = 256 / fTR source groups of each coordinate: in-thread
-      // over its sources, lanes fo, fo + fTR, ... of a wavefront, then the
-      // four wavefronts through LDS
-      Soft st[8];
-      {
-        float lg_[kFoldU][8], xv[kFoldU][8];
-        float mx[8];
-#pragma unroll
-        for (int v = 0; v < 8; ++v) mx[v] = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < kFoldU; ++u) {
-          const bool ok = fo * 8 < fW && fj + fG * u < F.m;
-          float zz[8];
-          unpack16(fz[u], (const bf16*)nullptr, zz);
-          unpack16(fx[u], (const bf16*)nullptr, xv[u]);
-          const float zb[8] = {fb[u][0].x, fb[u][0].y, fb[u][0].z, fb[u][0].w,
-                               fb[u][1].x, fb[u][1].y, fb[u][1].z, fb[u][1].w};
-#pragma unroll
-          for (int v = 0; v < 8; ++v) {
-            lg_[u][v] = ok ? zz[v] + zb[v] : -INFINITY;
-            mx[v] = fmaxf(mx[v], lg_[u][v]);
-          }
-        }
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          float l_ = 0.f, acc_ = 0.f;
-#pragma unroll
-          for (int u = 0; u < kFoldU; ++u) {
-            const float e_ = lg_[u][v] == -INFINITY ? 0.f : __expf(lg_[u][v] - mx[v]);
-            l_ += e_;
-            acc_ += e_ * xv[u][v];
-          }
-          st[v] = Soft{mx[v], l_, acc_};
-        }
-      }
-      for (int msk = fTR; msk < 64; msk <<= 1) {
-#pragma unroll
-        for (int v = 0; v < 8; ++v) {
-          const Soft o{__shfl_xor(st[v].mx, msk, 64), __shfl_xor(st[v].l, msk, 64), __shfl_xor(st[v].acc, msk, 64)};
-          st[v] = soft_merge(st[v], o);
-        }
-      }
-      if (l < fTR) {
-#pragma unroll
-        for (int v = 0; v < 8; ++v)
-          if (fo * 8 + v < 64) s_fpart[w][fo * 8 + v] = st[v];
-      }
-      lds_barrier();
-      if (tid < fW) {
-        Soft acc0 = s_fpart[0][tid];
-#pragma unroll
-        for (int g = 1; g < 4; ++g) acc0 = soft_merge(acc0, s_fpart[g][tid]);
-        const uint16_t vb = f32_to_bf16(acc0.acc / acc0.l);
-        s_fnew[tid] = bf16_to_f32(vb);
-        reinterpret_cast<uint16_t*>(F.kv_cache)[((size_t)b * A.E_cap + fcnt) * kC + fr0 + tid] = vb;
-        A.fold_new[(size_t)b * kC + fr0 + tid] = vb;
-      }
-    }
-    // the token's coordinates (threads 0 .. fW / 8 - 1 hold x_new)
-    if (tid < fW / 8) {
-      float xv[8];
-      unpack16(fapp, (const bf16*)nullptr, xv);
-#pragma unroll
-      for (int v = 0; v < 8; ++v) s_fx[8 * tid + v] = xv[v];
-    }
-    lds_barrier();
-    // this slice's share of q_h . entry and q_h . token, summed over the
-    // fW / 4 groups of a head
-    const int gph = fW / 4, ng = H * gph;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int g = tid + 256 * u;
-      if (256 * u < ng) {
-        float pn = 0.f, po = 0.f;
-        if (g < ng) {
-          const int c4 = g % gph;
-          const uint2 qv = fq[u];
-          const float q0 = __uint_as_float(qv.x << 16), q1 = __uint_as_float(qv.x & 0xffff0000u);
-          const float q2 = __uint_as_float(qv.y << 16), q3 = __uint_as_float(qv.y & 0xffff0000u);
-          po = q0 * s_fx[4 * c4] + q1 * s_fx[4 * c4 + 1] + q2 * s_fx[4 * c4 + 2] + q3 * s_fx[4 * c4 + 3];
-          if (fold_now)
-            pn = q0 * s_fnew[4 * c4] + q1 * s_fnew[4 * c4 + 1] + q2 * s_fnew[4 * c4 + 2] + q3 * s_fnew[4 * c4 + 3];
-        }
-        for (int o = 1; o < gph; o <<= 1) {
-          po += __shfl_xor(po, o, 64);
-          pn += __shfl_xor(pn, o, 64);
-        }
-        if (g < ng && g % gph == 0) {
-          float* fs = A.fold_s + 2 * ((size_t)b * H + g / gph);
-          atomicAdd(fs + 1, po);
-          if (fold_now) atomicAdd(fs, pn);
-        }
-      }
-    }
-    // the token's share of the rings (every step)
-    if (tid < 3 * fW / 8) {
-      const int which = tid / (fW / 8), cc = fr0 + 8 * (tid % (fW / 8));
-      uint16_t* dst = which == 0
-                          ? reinterpret_cast<uint16_t*>(F.win_ring) + ((size_t)b * F.n_win + ft % F.n_win) * A.c + cc
-                          : reinterpret_cast<uint16_t*>(F.tail) + (((size_t)b * 2 + (which - 1)) * F.R + ft % F.R) * A.c + cc;
-      *reinterpret_cast<uint4*>(dst) = fapp;
-    }
-    if (split == 0 && tid == 0) A.fold_row[b] = fold_now ? fcnt + 1 : 0;
-  }
+        *reinterpret_cast<const uint4*>(stage + (16 * w + r) * kOutLD + 8 * l);
 }
 
 // grid (B*Tq, H), 256 threads: wavefront w merges splits w, w+4, ... of one
@@ -662,7 +658,10 @@ bool attend_fuses_fold(AttendArgs& a, const FoldArgs& f) {
   if (ns < 2) return false;
   int cs = 8;
   while (cs * ns < a.c) cs *= 2;
-  if (cs > 64 || f.m > kFoldU * (256 / (cs / 8)) || a.H * cs > 4096) return false;
+  // LDS: the slice's sources fill at most one ring slot, its query slice
+  // the P^T buffer
+  if (cs > 64 || f.m > kFoldS * (256 / cs) || f.m * cs * 8 > kTN * kRowB || a.H * cs * 2 > 4 * 64 * 16)
+    return false;
   const size_t off = attend_fold_ws_offset(a.B, a.Tq, a.H, a.c, a.E_cap + a.n_win);
   char* base = reinterpret_cast<char*>(a.ws);
   a.fold_s = reinterpret_cast<float*>(base + off);

@@ -35,6 +35,15 @@ CSA_DEV Soft soft_merge(Soft a, Soft b) {
   return Soft{mx, a.l * ra + b.l * rb, a.acc * ra + b.acc * rb};
 }
 
+// the same merge with selects instead of branches (no divergent paths in
+// the lane-exchange reductions)
+CSA_DEV Soft soft_merge_sel(Soft a, Soft b) {
+  const float mx = fmaxf(a.mx, b.mx);
+  const float ra = a.l == 0.f ? 0.f : __expf(a.mx - mx);
+  const float rb = b.l == 0.f ? 0.f : __expf(b.mx - mx);
+  return Soft{(a.l == 0.f && b.l == 0.f) ? a.mx : mx, a.l * ra + b.l * rb, a.acc * ra + b.acc * rb};
+}
+
 constexpr int kFoldT = 256;
 constexpr int kFoldCW = 64;  // main-entry coordinates per workgroup
 

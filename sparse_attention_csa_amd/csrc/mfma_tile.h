@@ -81,6 +81,13 @@ CSA_DEV void dma_row_m0(const uint16_t* src_row, uint32_t lds_row, int lane, int
                        : "memory");
 }
 
+// Any 16 bytes per lane, DMA'd to LDS bytes lds_base + 16 lane (same
+// rules as dma_row_m0; lds_base is wavefront-uniform).
+CSA_DEV void dma16_m0(const void* p, uint32_t lds_base) {
+  __asm__ __volatile__("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(lds_base)
+                       : "memory");
+}
+
 // LDS byte address of a pointer into a __shared__ object
 CSA_DEV uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
