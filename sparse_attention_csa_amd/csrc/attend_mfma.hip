@@ -498,8 +498,8 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     if (n_split == 1) {
       const float z2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
       const float M = fmaxf(m_run, z2);
-      const float em = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
-      const float den = Lh * em + (z2 == -INFINITY ? 0.f : exp2f(z2 - M));
+      const float em = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+      const float den = Lh * em + (z2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z2 - M));
       f = em / den;
       if (a.lse && lg == 0) a.lse[(size_t)qrow * H + h] = (M + log2f(den)) * kLn2;
       dst_row0 = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * H + h0) * kC;
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
         pml[2 * slot] = m_run;
         pml[2 * slot + 1] = Lh;
       }
-      f = Lh > 0.f ? 1.f / Lh : 0.f;
+      f = Lh > 0.f ? __builtin_amdgcn_rcpf(Lh) : 0.f;
       dst_row0 = po + (((size_t)qrow * n_split + split) * H + h0) * kC;
     }
     if (lg == 0) s_scale[16 * w + li] = f;
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
     Ls = v.y;
   }
   const float M = fmaxf(fmaxf(fmaxf(wave_max(ms), z2), s_new), s_own);
-  const float wgt = (ms == -INFINITY || Ls == 0.f) ? 0.f : exp2f(ms - M) * Ls;
+  const float wgt = (ms == -INFINITY || Ls == 0.f) ? 0.f : __builtin_amdgcn_exp2f(ms - M) * Ls;
   // this wavefront's splits: all loads first
   uint4 raw[kMergeU];
 #pragma unroll
@@ -604,10 +604,10 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) s_o[w][8 * l + i] = o[i];
-  const float w_new = frow > 0 ? exp2f(s_new - M) : 0.f;
-  const float w_own = a.fold_mode ? exp2f(s_own - M) : 0.f;
+  const float w_new = frow > 0 ? __builtin_amdgcn_exp2f(s_new - M) : 0.f;
+  const float w_own = a.fold_mode ? __builtin_amdgcn_exp2f(s_own - M) : 0.f;
   if (w == 0) {
-    const float den = wave_sum(wgt) + (z2 == -INFINITY ? 0.f : exp2f(z2 - M)) + w_new + w_own;
+    const float den = wave_sum(wgt) + (z2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z2 - M)) + w_new + w_own;
     if (l == 0) s_den = den;
   }
   __syncthreads();
@@ -617,7 +617,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
     if (h == 0 && frow > 0) a.fold.n_entries[b] = frow;  // publish the new entry count
   }
   const float den = s_den;
-  const float inv = 1.f / den;
+  const float inv = __builtin_amdgcn_rcpf(den);
   const uint32_t nw[4] = {nrow.x, nrow.y, nrow.z, nrow.w}, xw[4] = {xrow.x, xrow.y, xrow.z, xrow.w};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {

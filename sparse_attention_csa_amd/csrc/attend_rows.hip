@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
   float M = -INFINITY;
 #pragma unroll
   for (int v = 0; v < 4; ++v) M = fmaxf(M, s_m[v][li]);
-  const float fw = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
+  const float fw = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
   // staging: wavefront v's head row h (512 floats, 2 KB) at
   // red(v) + 2048 h, its 16-byte chunk c at position c ^ h (conflict-free
   // for both access patterns)
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
     float Lh = 0.f;
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      if (s_m[v][hh] != -INFINITY) Lh += s_l[v][hh] * exp2f(s_m[v][hh] - Mh);
+      if (s_m[v][hh] != -INFINITY) Lh += s_l[v][hh] * __builtin_amdgcn_exp2f(s_m[v][hh] - Mh);
     // lane l: d = 4l .. 4l+3 (chunk l) and 256 + 4l .. (chunk 64 + l)
     f32x4_t o0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, o1 = o0;
 #pragma unroll
@@ -316,8 +316,8 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
     if (n_split == 1) {
       const float z2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
       const float Mf = fmaxf(Mh, z2);
-      const float em = Mh == -INFINITY ? 0.f : exp2f(Mh - Mf);
-      const float den = Lh * em + (z2 == -INFINITY ? 0.f : exp2f(z2 - Mf));
+      const float em = Mh == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mh - Mf);
+      const float den = Lh * em + (z2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z2 - Mf));
       f = em / den;
       if (a.lse && l == 0) a.lse[(size_t)qrow * H + h] = (Mf + log2f(den)) * kLn2;
       dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * H + h) * kC;
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
         pml[2 * slot] = Mh;
         pml[2 * slot + 1] = Lh;
       }
-      f = Lh > 0.f ? 1.f / Lh : 0.f;
+      f = Lh > 0.f ? __builtin_amdgcn_rcpf(Lh) : 0.f;
       dst = po + slot * kC;
     }
     uint2 r0, r1;

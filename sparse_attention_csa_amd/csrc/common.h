@@ -15,13 +15,9 @@ struct bf16 {
 
 CSA_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
-// round to nearest even; NaN stays NaN
-CSA_DEV uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
+// round to nearest even; NaN stays NaN (the gfx950 conversion instruction,
+// no branches)
+CSA_DEV uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f)); }
 
 // element load / store for the two activation dtypes
 CSA_DEV float ld(const float* p, size_t i) { return p[i]; }
