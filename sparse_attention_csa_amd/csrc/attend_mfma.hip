@@ -198,32 +198,36 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   if (tid == 0) s_restart = 0;
   __syncthreads();  // s_restart ready
 
-  auto row_src = [&](int j, bool* ok) -> const uint16_t* {
-    *ok = false;
-    if (j >= r_end) return pad_row;
-    if (j < nc32) {
-      *ok = true;
-      return kv + (size_t)j * kC;
-    }
-    int wr = wbase + (j - nc32);
-    if (wr >= wcap) wr -= wcap;
-    *ok = true;
-    return win + (size_t)wr * kC;
-  };
-  // wave w fetches rows kRowsPerWave * w .. of a tile; every wave reads all rows
+  // Wave w fetches rows kRowsPerWave * w .. of a tile; every wave reads all
+  // rows.  Lane i (mod kRowsPerWave) computes the source of row
+  // kRowsPerWave * w + i without branches; each DMA then takes its row's
+  // address from that lane (two lane reads) and a per-lane chunk offset
+  // fixed for the kernel.
+  static_assert(kRowsPerWave == 8, "row validity words below");
+  int dofs[kRowsPerWave];  // element offset of this lane's 16-byte chunk, per row
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) dofs[i] = 8 * (l ^ swz((kRowsPerWave * w + i) & 15));
+  auto spread4 = [](uint32_t x) { return (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21); };
   auto issue_tile = [&](int r0, int buf) {
-    uint32_t vw = 0;
+    const int j = r0 + kRowsPerWave * w + (l & (kRowsPerWave - 1));
+    int wr = wbase + (j - nc32);
+    wr = wr >= wcap ? wr - wcap : wr;
+    const bool ok = j < r_end;
+    const uint16_t* src = ok ? (j < nc32 ? kv + (size_t)j * kC : win + (size_t)wr * kC) : pad_row;
+    const uint64_t okb = __builtin_amdgcn_ballot_w64(ok);
+    const uintptr_t sp = reinterpret_cast<uintptr_t>(src);
+    const uint32_t s_lo = (uint32_t)sp, s_hi = (uint32_t)(sp >> 32);
+    const uint32_t lds0 = lds_addr(tiles[buf]) + kRowsPerWave * w * kRowB;
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
-      const int r = kRowsPerWave * w + i;
-      bool ok;
-      const uint16_t* src = row_src(r0 + r, &ok);
-      dma_row_m0(src, lds_addr(tiles[buf] + r * kRowB), l, swz(r & 15));
-      vw |= (uint32_t)ok << (8 * (i & 3));
-      if ((i & 3) == 3) {
-        if (l == 0) rvalid[buf][r >> 2] = vw;
-        vw = 0;
-      }
+      // (readlane returns int: widen through uint32_t, no sign extension)
+      const uint64_t ri = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(s_hi, i) << 32) |
+                          (uint64_t)(uint32_t)__builtin_amdgcn_readlane(s_lo, i);
+      dma16_m0(reinterpret_cast<const uint16_t*>(ri) + dofs[i], lds0 + i * kRowB);
+    }
+    if (l == 0) {  // byte r % 4 of word r / 4: rows kRowsPerWave * w + i
+      rvalid[buf][2 * w] = spread4((uint32_t)okb & 15u);
+      rvalid[buf][2 * w + 1] = spread4((uint32_t)(okb >> 4) & 15u);
     }
   };
 
