@@ -147,26 +147,26 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
   f32x4_t acc[32];
   float m_run = -INFINITY, l_lane = 0.f;
 
-  // DMA of this wavefront's i-th tile into slot sl
-  auto issue = [&](int i, int sl) {
-    const int jr0 = (w + 4 * i) * kTR;
-    const int4* rs = reinterpret_cast<const int4*>(rsrc + jr0);
-    int e[16];
+  // DMA of this wavefront's i-th tile into slot sl.  Lane r (mod 16)
+  // computes the source of tile row r; each DMA takes its row's address from
+  // that lane (two lane reads) and a per-lane chunk offset fixed for the
+  // kernel.
+  int dofs[kTR];  // element offset of this lane's 16-byte chunk, per tile row
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int4 x = rs[u];
-      e[4 * u] = x.x;
-      e[4 * u + 1] = x.y;
-      e[4 * u + 2] = x.z;
-      e[4 * u + 3] = x.w;
-    }
+  for (int r = 0; r < kTR; ++r) dofs[r] = 8 * (l ^ swz(r));
+  auto issue = [&](int i, int sl) {
+    const int er = rsrc[(w + 4 * i) * kTR + (l & (kTR - 1))];
+    const int row = er >= 0 ? er : (er == -1 ? own : -2 - er);
+    const uint16_t* src = (er >= 0 ? kv : win) + (size_t)row * kC;
+    const uintptr_t sp = reinterpret_cast<uintptr_t>(src);
+    const uint32_t s_lo = (uint32_t)sp, s_hi = (uint32_t)(sp >> 32);
     const uint32_t dst = lds_addr(slots[w][sl]);
 #pragma unroll
     for (int r = 0; r < kTR; ++r) {
-      const int er = __builtin_amdgcn_readfirstlane(e[r]);
-      const uint16_t* base = er >= 0 ? kv : win;
-      const int row = er >= 0 ? er : (er == -1 ? own : -2 - er);
-      dma_row_m0(base + (size_t)row * kC, dst + r * kRowB, l, swz(r));
+      // (readlane returns int: widen through uint32_t, no sign extension)
+      const uint64_t ri = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(s_hi, r) << 32) |
+                          (uint64_t)(uint32_t)__builtin_amdgcn_readlane(s_lo, r);
+      dma16_m0(reinterpret_cast<const uint16_t*>(ri) + dofs[r], dst + r * kRowB);
     }
   };
 
