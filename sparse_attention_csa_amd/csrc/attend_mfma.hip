@@ -54,6 +54,7 @@ constexpr int kTN = 32;                // rows per LDS tile
 constexpr int kRing = 4;               // LDS tile slots: kRing - 1 tiles in flight while one is computed
 constexpr int kRowsPerWave = kTN / 4;  // DMA instructions per wave and tile
 constexpr int kFoldS = 16;             // fold slice: sources per thread (at most)
+constexpr int kFoldRowsLess = 64;      // rows a folding split gives up to the others
 
 }  // namespace
 
@@ -83,10 +84,12 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   const int H = a.H;
   const int h0 = hg * kHW + 16 * w;  // this wavefront's first head
 
-  // Everything that depends only on the block index is requested at once
-  // and awaited together (one memory round trip): the query operands and
-  // the position, entry count and window base.  After that the row DMAs are
-  // the only memory operations in flight, so the waits below count DMAs.
+  // The query operands (vector loads) and the position, entry count and
+  // window base (scalar loads) are requested first.  The first tiles' rows
+  // are usually cache entries whose addresses need neither, so their DMAs
+  // go out before the scalars return (checked below, reissued in the rare
+  // case); the vector loads are awaited before the row loop, so that the
+  // loop's waits count row DMAs only.
   // Q^T operands for this wavefront's 16 heads: lane (head li, d group lg).
   bf16x8_t qf[16];
   {
@@ -101,8 +104,45 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   const int64_t t_ld = (a.q_pos ? a.q_pos + qrow : dummy64)[0];
   const int64_t w_ld = (a.win_pos0 ? a.win_pos0 + b : dummy64)[0];
   const int32_t cnt = a.n_entries[b];
-  __builtin_amdgcn_s_waitcnt(0);
-  __asm__ __volatile__("" ::"s"(t_ld), "s"(w_ld), "s"(cnt), "v"(qf[0]), "v"(qf[15]));
+  // row range of the split: with the fold inside, the first fold_nsplit
+  // splits (the ones that fold) take fold_rows rows each, the rest
+  // rows_per_split, so that the fold's time is balanced by fewer rows
+  const int n_fs = a.fold_mode ? a.fold_nsplit : 0;
+  const int rows_here = split < n_fs ? a.fold_rows : rows_per_split;
+  const int r_begin = split < n_fs ? split * a.fold_rows : n_fs * a.fold_rows + (split - n_fs) * rows_per_split;
+  const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv) + (size_t)b * a.E_cap * kC;
+
+  // Wave w fetches rows kRowsPerWave * w .. of a tile; every wave reads all
+  // rows.  Lane i (mod kRowsPerWave) computes the source of row
+  // kRowsPerWave * w + i without branches; each DMA then takes its row's
+  // address from that lane (two lane reads) and a per-lane chunk offset
+  // fixed for the kernel.
+  static_assert(kRowsPerWave == 8, "row validity words below");
+  int dofs[kRowsPerWave];  // element offset of this lane's 16-byte chunk, per row
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) dofs[i] = 8 * (l ^ swz((kRowsPerWave * w + i) & 15));
+  auto dma_rows = [&](const uint16_t* src, int buf) {
+    const uintptr_t sp = reinterpret_cast<uintptr_t>(src);
+    const uint32_t s_lo = (uint32_t)sp, s_hi = (uint32_t)(sp >> 32);
+    const uint32_t lds0 = lds_addr(tiles[buf]) + kRowsPerWave * w * kRowB;
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      // (readlane returns int: widen through uint32_t, no sign extension)
+      const uint64_t ri = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(s_hi, i) << 32) |
+                          (uint64_t)(uint32_t)__builtin_amdgcn_readlane(s_lo, i);
+      dma16_m0(reinterpret_cast<const uint16_t*>(ri) + dofs[i], lds0 + i * kRowB);
+    }
+  };
+  // speculative: the first kRing - 1 tiles read as cache entries (in the
+  // cache buffer, so in bounds whatever the count turns out to be)
+  const bool spec = r_begin + (kRing - 1) * kTN <= a.E_cap;
+  if (spec) {
+#pragma unroll
+    for (int jt = 0; jt < kRing - 1; ++jt)
+      dma_rows(kv + (size_t)(r_begin + jt * kTN + kRowsPerWave * w + (l & (kRowsPerWave - 1))) * kC, jt);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the scalars
+  __asm__ __volatile__("" ::"s"(t_ld), "s"(w_ld), "s"(cnt));
   const int64_t t = a.q_pos ? t_ld : a.q_pos0 + qrow % a.Tq;
   const int64_t wpos0 = a.win_pos0 ? w_ld : a.win_pos0_const;
   const int64_t lim = vis_limit(t, a.m, a.vis);
@@ -114,10 +154,8 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   // fold_mode: the query's own token is not in the window ring yet; the
   // merge adds it as a row of its own
   const int64_t n_rows = n_c + n_w - (a.fold_mode ? 1 : 0);
-  const int r_begin = split * rows_per_split;
-  const int r_end = (int)((int64_t)r_begin + rows_per_split < n_rows ? r_begin + rows_per_split : n_rows);
+  const int r_end = (int)((int64_t)r_begin + rows_here < n_rows ? r_begin + rows_here : n_rows);
   const int nc32 = (int)n_c;
-  const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv) + (size_t)b * a.E_cap * kC;
   const uint16_t* win = reinterpret_cast<const uint16_t*>(a.win) + (size_t)b * a.W_cap * kC;
   const float sc2 = a.scale * kLog2e;
   // ring row of the first window position; later window rows follow with
@@ -143,9 +181,9 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   // of entry cnt, completed by the block ending at t (stored only if it is
   // the next entry: fold_now), this slice's share of q_h . entry and
   // q_h . token, and the token's share of the rings.  Its inputs come by DMA
-  // into LDS ahead of the first tiles (ring slot kRing - 1 and the P^T
-  // buffer are unused until the row loop starts), so the fold runs while
-  // those tiles are in flight and nothing of it is live during the loop.
+  // into LDS with the first tiles (ring slot kRing - 1 and the P^T buffer
+  // are unused until the row loop starts), so nothing of it is live during
+  // the loop.
   const int fcs = a.fold_cs, fr0 = split * fcs;
   const int fW = (a.fold_mode && hg == 0) ? (a.c - fr0 < 0 ? 0 : (a.c - fr0 < fcs ? a.c - fr0 : fcs)) : 0;
   const bool fold_now = fW > 0 && lim == (int64_t)cnt + 1 && cnt < a.E_cap;
@@ -198,37 +236,24 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   if (tid == 0) s_restart = 0;
   __syncthreads();  // s_restart ready
 
-  // Wave w fetches rows kRowsPerWave * w .. of a tile; every wave reads all
-  // rows.  Lane i (mod kRowsPerWave) computes the source of row
-  // kRowsPerWave * w + i without branches; each DMA then takes its row's
-  // address from that lane (two lane reads) and a per-lane chunk offset
-  // fixed for the kernel.
-  static_assert(kRowsPerWave == 8, "row validity words below");
-  int dofs[kRowsPerWave];  // element offset of this lane's 16-byte chunk, per row
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) dofs[i] = 8 * (l ^ swz((kRowsPerWave * w + i) & 15));
   auto spread4 = [](uint32_t x) { return (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21); };
-  auto issue_tile = [&](int r0, int buf) {
-    const int j = r0 + kRowsPerWave * w + (l & (kRowsPerWave - 1));
+  // source of the lane's row j of the split (branch-free); valid: j < r_end
+  auto row_src = [&](int j) -> const uint16_t* {
     int wr = wbase + (j - nc32);
     wr = wr >= wcap ? wr - wcap : wr;
-    const bool ok = j < r_end;
-    const uint16_t* src = ok ? (j < nc32 ? kv + (size_t)j * kC : win + (size_t)wr * kC) : pad_row;
-    const uint64_t okb = __builtin_amdgcn_ballot_w64(ok);
-    const uintptr_t sp = reinterpret_cast<uintptr_t>(src);
-    const uint32_t s_lo = (uint32_t)sp, s_hi = (uint32_t)(sp >> 32);
-    const uint32_t lds0 = lds_addr(tiles[buf]) + kRowsPerWave * w * kRowB;
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      // (readlane returns int: widen through uint32_t, no sign extension)
-      const uint64_t ri = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(s_hi, i) << 32) |
-                          (uint64_t)(uint32_t)__builtin_amdgcn_readlane(s_lo, i);
-      dma16_m0(reinterpret_cast<const uint16_t*>(ri) + dofs[i], lds0 + i * kRowB);
-    }
+    return j < r_end ? (j < nc32 ? kv + (size_t)j * kC : win + (size_t)wr * kC) : pad_row;
+  };
+  auto set_valid = [&](int r0, int buf) {
+    const int j = r0 + kRowsPerWave * w + (l & (kRowsPerWave - 1));
+    const uint64_t okb = __builtin_amdgcn_ballot_w64(j < r_end);
     if (l == 0) {  // byte r % 4 of word r / 4: rows kRowsPerWave * w + i
       rvalid[buf][2 * w] = spread4((uint32_t)okb & 15u);
       rvalid[buf][2 * w + 1] = spread4((uint32_t)(okb >> 4) & 15u);
     }
+  };
+  auto issue_tile = [&](int r0, int buf) {
+    dma_rows(row_src(r0 + kRowsPerWave * w + (l & (kRowsPerWave - 1))), buf);
+    set_valid(r0, buf);
   };
 
   // the first kRing - 1 tiles
@@ -237,17 +262,22 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     for (int j = 0; j < kRing - 1; ++j)
       if (r_begin + j * kTN < r_end) issue_tile(r_begin + j * kTN, j);
   };
-  prologue();
+  // the speculative tiles hold the right rows when every row of them that
+  // the split uses is a cache entry; else they are fetched again
+  if (spec && (r_end < r_begin + (kRing - 1) * kTN ? r_end : r_begin + (kRing - 1) * kTN) <= nc32) {
+#pragma unroll
+    for (int jt = 0; jt < kRing - 1; ++jt) set_valid(r_begin + jt * kTN, jt);
+  } else {
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));  // (the slots are written again)
+    prologue();
+  }
+  // every load and DMA so far, the query operands included, has landed
+  // before the fold and the row loop
+  __builtin_amdgcn_s_waitcnt(0);
+  __asm__ __volatile__("" ::"v"(qf[0]), "v"(qf[15]));
 
   if (fW > 0) {
-    // this wavefront's fold DMAs are older than its tile DMAs
-    const int n_pro = r_end > r_begin ? kRowsPerWave * min(kRing - 1, (r_end - r_begin + kTN - 1) / kTN) : 0;
-    static_assert(kRing - 1 == 3, "tile DMA counts below");
-    if (n_pro >= 3 * kRowsPerWave) __builtin_amdgcn_s_waitcnt(wait_vm(3 * kRowsPerWave));
-    else if (n_pro == 2 * kRowsPerWave) __builtin_amdgcn_s_waitcnt(wait_vm(2 * kRowsPerWave));
-    else if (n_pro == kRowsPerWave) __builtin_amdgcn_s_waitcnt(wait_vm(kRowsPerWave));
-    else __builtin_amdgcn_s_waitcnt(wait_vm(0));
-    lds_barrier();
+    lds_barrier();  // every wavefront's fold DMAs
     if (fold_now) {
       // thread (coordinate fc, source group fg of G = 256 / fW) folds
       // sources fg, fg + G, ... of its coordinate; the G partial states of
@@ -700,9 +730,26 @@ size_t attend_mfma_ws_bytes(int BT, int H, int rows_max) {
 
 hipError_t launch_attend_merge(const AttendArgs& a, int n_split, hipStream_t s);
 
-hipError_t launch_attend_mfma(const AttendArgs& a, int rows_max, hipStream_t s) {
+hipError_t launch_attend_mfma(const AttendArgs& a0, int rows_max, hipStream_t s) {
   int ns, rps;
-  attend_mfma_plan(a.B * a.Tq, a.H, rows_max, &ns, &rps);
+  attend_mfma_plan(a0.B * a0.Tq, a0.H, rows_max, &ns, &rps);
+  AttendArgs a = a0;
+  a.fold_nsplit = 0;
+  a.fold_rows = 0;
+  if (a.fold_mode) {
+    // the folding splits take kFoldRowsLess fewer rows (the same split count)
+    const int nf = (a.c + a.fold_cs - 1) / a.fold_cs;
+    if (nf < ns) {
+      int ro = (rows_max + nf * kFoldRowsLess + ns - 1) / ns;
+      ro = (ro + 15) / 16 * 16;
+      const int rf = ro - kFoldRowsLess;
+      if (rf >= 16 && (long long)nf * rf + (long long)(ns - nf) * ro >= rows_max) {
+        a.fold_nsplit = nf;
+        a.fold_rows = rf;
+        rps = ro;
+      }
+    }
+  }
   const int n_hg = a.H / kHW;
   const long long units = (long long)ns * a.B * a.Tq;       // (query, split) pairs
   const long long blocks = (units + 7) / 8 * 8 * n_hg;      // padded to whole XCD rounds

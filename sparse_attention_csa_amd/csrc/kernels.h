@@ -145,6 +145,8 @@ struct AttendArgs {
   float* fold_s;       // [B][H][2]: q . new entry, q . own token; zero between calls
   int32_t* fold_row;   // [B]: new entry index + 1, or 0
   uint16_t* fold_new;  // [B][c]: the new entry (bf16), read by the merge
+  int fold_nsplit;     // set by the launch: splits that fold (fewer rows each) ...
+  int fold_rows;       // ... and their row count
 };
 size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max);
 // whether hca decode can fold inside the attention; sets a.fold_mode / fold_cs
