@@ -48,7 +48,26 @@ def _check_decode(g, sess, label):
                 ref = OL.decode_step(g, b, selected=ids[:cnt])
         assert_close(out[b], ref["o"], kvk, f"{label} out b={b}")
         assert np.abs(lse[b] - ref["lse"]).max() < 1e-3, f"{label} lse b={b}"
+    _check_rings(g, sess, label)
     return swaps_total
+
+
+def _check_rings(g, sess, label):
+    """The step's token in the window ring and the compressor tail rings:
+    bit-equal to the step's inputs (a copy)."""
+    st = sess.state
+    torch.cuda.synchronize()
+    as_u16 = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)  # noqa
+    streams = ("ca", "za", "cb", "zb")[:st.S]
+    for b in range(g["B"]):
+        t = int(g["pos"][b])
+        assert np.array_equal(as_u16(st.win_ring[b, t % g["n_win"]]), g["x_new"][b]), f"{label} window ring b={b}"
+        for si, name in enumerate(streams):
+            assert np.array_equal(as_u16(st.tail[b, si, t % st.R]), g["new_" + name][b]), f"{label} tail {name} b={b}"
+        if g["kind"] == "csa":
+            for si, name in enumerate(("ca", "za", "cb", "zb")):
+                assert np.array_equal(as_u16(st.idx_tail[b, si, t % st.R]), g["new_i" + name][b]), \
+                    f"{label} indexer tail {name} b={b}"
 
 
 def _check_folded_key(g, sess, b, e0, ref_row, label):
@@ -125,6 +144,26 @@ def test_decode_hca_bf16_small(gpu_lib, H, c):
     sess = DecodeSession(g)
     sess.run()
     _check_decode(g, sess, f"hca-bf16-c{c}")
+
+
+@pytest.mark.parametrize("pos_off", [1, 37, 127])
+def test_decode_hca_bf16_no_fold(gpu_lib, pos_off):
+    """A step inside a block (no entry completes): the fused-fold path only
+    scores the token and appends it to the rings."""
+    from sparse_attention_csa_amd.harness import DecodeSession
+    g = workloads.flash_hca_decode(seed=35, B=3, n=128 * 200, H=64, c=512, pos_off=pos_off)
+    sess = DecodeSession(g)
+    sess.run()
+    _check_decode(g, sess, f"hca-bf16-no-fold-{pos_off}")
+
+
+@pytest.mark.parametrize("pos_off", [1, 3])
+def test_decode_csa_fp8_no_fold(gpu_lib, pos_off):
+    from sparse_attention_csa_amd.harness import DecodeSession
+    g = workloads.pro_csa_decode(seed=36, B=2, n=4 * 3000, H=128, c=512, H_I=8, d_I=64, k=128, pos_off=pos_off)
+    sess = DecodeSession(g)
+    sess.run()
+    _check_decode(g, sess, f"csa-fp8-no-fold-{pos_off}")
 
 
 @pytest.mark.parametrize("H,c", [(16, 128), (128, 512)])

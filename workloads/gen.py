@@ -108,19 +108,23 @@ def tiny_case(seed=0, n=4096, c=64, H=8, H_I=4, d_I=32, k=64, Tq=16, m=4, n_win=
 # decode workloads (one new token per sequence at t = n)
 # ---------------------------------------------------------------------------
 
-def _decode_common(rng, kind, B, n, H, c, m, n_win, overlap, kv_dtype):
+def _decode_common(rng, kind, B, n, H, c, m, n_win, overlap, kv_dtype, pos_off=0):
     """State and io shared by the CSA and HCA decode workloads.  The new token
     sits at t = n; entries 0 .. n/m-2 are in the cache and the block that
-    token n-1 completed is still in the tail, so the step folds it."""
+    token n-1 completed is still in the tail, so the step folds it.  With
+    0 < pos_off < m the new token sits at t = n + pos_off inside the next
+    block instead: all n/m entries are in the cache and the step folds
+    nothing (the common decode step)."""
     E = n // m
     tail_len = 2 * m if overlap else m
     g = dict(kind=kind, B=B, n=n, H=H, c=c, m=m, n_win=n_win, overlap=overlap,
              vis=VIS_PRIOR_BLOCKS, scale=1.0 / math.sqrt(c), kv_dtype=kv_dtype, E_cap=E)
-    g["pos"] = np.full(B, n, dtype=np.int64)
-    g["n_entries"] = np.full(B, E - 1, dtype=np.int32)
-    g["tail_pos0"] = np.full(B, n - tail_len, dtype=np.int64)
+    g["pos"] = np.full(B, n + pos_off, dtype=np.int64)
+    g["n_entries"] = np.full(B, E - 1 if pos_off == 0 else E, dtype=np.int32)
+    g["tail_pos0"] = np.full(B, n + pos_off - tail_len, dtype=np.int64)
     kv = _normal_bf16(rng, (B, E, c)) if kv_dtype == "bf16" else _normal(rng, (B, E, c))
-    kv[:, E - 1] = 0  # the pending entry is produced by the step
+    if pos_off == 0:
+        kv[:, E - 1] = 0  # the pending entry is produced by the step
     g["kv_cache"] = kv
     streams = ("ca", "za", "cb", "zb") if overlap else ("ca", "za")
     for s in streams:
@@ -185,7 +189,7 @@ def flash_csa_decode(seed=1, B=8, n=131072, H=64, c=512, H_I=64, d_I=128, k=512,
 
 
 def pro_csa_decode(seed=3, B=4, n=1 << 20, H=128, c=512, H_I=64, d_I=128, k=1024, n_win=128, m=4,
-                   nu=3.0):
+                   nu=3.0, pos_off=0):
     """Pro-shaped CSA decode: bf16 KV, fp8 e4m3 indexer queries and keys.
 
     Indexer keys K[s] = |T_s| z_s with T_s ~ Student-t(nu) and z_s ~ N(0, I),
@@ -194,7 +198,7 @@ def pro_csa_decode(seed=3, B=4, n=1 << 20, H=128, c=512, H_I=64, d_I=128, k=1024
     vector (per entry for keys, per head for queries).
     """
     rng = _rng(seed)
-    g = _decode_common(rng, "csa", B, n, H, c, m, n_win, True, "bf16")
+    g = _decode_common(rng, "csa", B, n, H, c, m, n_win, True, "bf16", pos_off)
     g["name"] = CONFIG_NAMES[4]
     _indexer_state(rng, g, H_I, d_I, k, "e4m3")
     E = g["E_cap"]
@@ -208,17 +212,18 @@ def pro_csa_decode(seed=3, B=4, n=1 << 20, H=128, c=512, H_I=64, d_I=128, k=1024
             t = np.abs(rng.standard_t(nu, size=s1 - s0)).astype(np.float32)
             z = _normal(rng, (s1 - s0, d_I))
             codes[b, s0:s1], scales[b, s0:s1] = e4m3_rows(t[:, None] * z)
-    codes[:, E - 1] = 0
-    scales[:, E - 1] = 1
+    if pos_off == 0:
+        codes[:, E - 1] = 0
+        scales[:, E - 1] = 1
     g["idx_cache"], g["idx_scale"] = codes, scales
     return g
 
 
-def flash_hca_decode(seed=2, B=8, n=1 << 20, H=64, c=512, n_win=128, m=128):
+def flash_hca_decode(seed=2, B=8, n=1 << 20, H=64, c=512, n_win=128, m=128, pos_off=0):
     """Flash-shaped HCA decode: n/m entries of dim c, dense attention over all
     of them; the step folds the m-token block that token n-1 completed."""
     rng = _rng(seed)
-    g = _decode_common(rng, "hca", B, n, H, c, m, n_win, False, "bf16")
+    g = _decode_common(rng, "hca", B, n, H, c, m, n_win, False, "bf16", pos_off)
     g["name"] = CONFIG_NAMES[3]
     g.update(idx_dtype=None, k=None)
     return g
