@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #define CSA_DEV __device__ __forceinline__
+#define CSA_HOST_DEV __host__ __device__
 
 namespace csa {
 

@@ -494,8 +494,9 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   int total;
   const int off = block_excl_scan<256>(cnt, s_misc, &total);
   int os = off & 0xffff, oc = off >> 16;
-  int* lsure = ws.lsure + (size_t)row * a.E_cap + e_first;
-  uint2* lcand = ws.lcand + (size_t)row * a.E_cap + e_first;
+  const size_t list_off = (size_t)row * ws.list_len + (size_t)blockIdx.x * ws.list_stride;
+  int* lsure = ws.lsure + list_off;
+  uint2* lcand = ws.lcand + list_off;
   for (int i = i0; i < i1; ++i) {
     const uint32_t key = f32_key(s_sc[i]);
     const int bin = (int)(key >> kTopkShift);
@@ -527,7 +528,7 @@ static int resident_wgs(K kernel) {
 // its LDS; with a fold, the last workgroup of each row is the fold
 // workgroup.
 struct ScorerPlan {
-  int per_row, fuse;
+  int per_row, fuse, list_stride;
 };
 static ScorerPlan scorer_plan(const IndexArgs& a, int resident, int use_hist, int allow_fuse, int with_fold) {
   const int rows = a.B * a.Tq;
@@ -538,8 +539,8 @@ static ScorerPlan scorer_plan(const IndexArgs& a, int resident, int use_hist, in
   const int scan_wg = per_row - with_fold;
   const int64_t per = ((int64_t)a.E_cap + 15) / 16 / ((int64_t)scan_wg * 4) + 1;
   const int fuse = allow_fuse && use_hist && per_row * rows <= resident && per_row <= kTopkMaxWgRow &&
-                   4 * per * 16 <= kTopkFuseCap;
-  return ScorerPlan{per_row, fuse};
+                   4 * per * 16 <= kTopkFuseCap && (int64_t)per_row * 4 * per * 16 <= topk_list_len(a.E_cap);
+  return ScorerPlan{per_row, fuse, (int)(4 * per * 16)};
 }
 
 template <int FP8, int HT>
@@ -550,13 +551,14 @@ static int scorer_resident() {
 }
 
 template <int FP8, int HT>
-static hipError_t launch_scorer(const IndexArgs& a, const TopkWs& ws, int use_hist, int allow_fuse,
+static hipError_t launch_scorer(const IndexArgs& a, TopkWs& ws, int use_hist, int allow_fuse,
                                 int* n_wg_fused, const FoldArgs* fold, hipStream_t s) {
   const int with_fold = fold ? 1 : 0;
   const ScorerPlan p = scorer_plan(a, scorer_resident<FP8, HT>(), use_hist, allow_fuse && ws.sync != nullptr,
                                    with_fold);
   if (with_fold && !p.fuse) return hipErrorInvalidValue;  // the caller checks index_fold_fusable first
   *n_wg_fused = p.fuse ? p.per_row : 0;
+  ws.list_stride = p.list_stride;  // (also read by the resolve kernel)
   FoldArgs f = fold ? *fold : FoldArgs{};
   dim3 grid(p.per_row, a.B * a.Tq), block(256);
   CSA_LAUNCH("index_score_mfma", (index_score_mfma_kernel<FP8, HT>), grid, block, 0, s, a, ws, use_hist, p.fuse,
@@ -580,7 +582,7 @@ bool index_fold_fusable(const IndexArgs& a, const FoldArgs& f, bool split) {
   return scorer_plan(a, resident, 1, 1, 1).fuse != 0;
 }
 
-hipError_t launch_index_score_mfma(const IndexArgs& a, const TopkWs& ws, int use_hist, int allow_fuse,
+hipError_t launch_index_score_mfma(const IndexArgs& a, TopkWs& ws, int use_hist, int allow_fuse,
                                    int* n_wg_fused, const FoldArgs* fold, hipStream_t s) {
   const int HT = a.H_I / 16;
   if (a.idx_dtype == E4M3) {

@@ -27,9 +27,15 @@ struct TopkWs {
   // fused mode (split mode, scores kept by the scoring workgroups)
   unsigned* sync;  // [rows] arrivals of the scoring workgroups (rows <= 64)
   int4* wg_info;   // [rows][kTopkMaxWgRow] per scoring workgroup: certain, candidates, first entry
-  int* lsure;      // [rows][E_cap] certain winners, each workgroup's at its first entry
-  uint2* lcand;    // [rows][E_cap] candidates (key, id), likewise
+  int* lsure;      // [rows][list_len] certain winners, workgroup j's at j * list_stride
+  uint2* lcand;    // [rows][list_len] candidates (key, id), likewise
+  int list_len;    // per row (topk_list_len)
+  int list_stride; // set by the scoring launch: the largest per-workgroup entry count
 };
+
+// per-row length of the fused lists: room for every workgroup's region of
+// list_stride entries, whatever the scan plan
+CSA_HOST_DEV inline int topk_list_len(int E_cap) { return E_cap + 64 * kTopkMaxWgRow + kTopkFuseCap; }
 
 // ---- device helpers shared by the scoring and selection kernels
 
@@ -111,7 +117,7 @@ hipError_t launch_topk_rows(const IndexArgs& a, const TopkWs& ws, hipStream_t s)
 // scoring workgroups per row, else 0.  With fold (only when
 // index_fold_fusable) it also performs the decode step's fold.
 bool index_mfma_supported(const IndexArgs& a);
-hipError_t launch_index_score_mfma(const IndexArgs& a, const TopkWs& ws, int use_hist, int allow_fuse,
+hipError_t launch_index_score_mfma(const IndexArgs& a, TopkWs& ws, int use_hist, int allow_fuse,
                                    int* n_wg_fused, const FoldArgs* fold, hipStream_t s);
 // whether the decode step's fold can run inside the scoring kernel (fold
 // workgroups); split: split-mode selection (few rows)

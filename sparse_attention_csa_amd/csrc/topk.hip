@@ -34,6 +34,8 @@ namespace {
 
 constexpr int kCT = 256;   // collect workgroup
 constexpr int kRT = 1024;  // resolve / row workgroup
+constexpr int kSpecL = 16;  // fused resolve: list entries per workgroup loaded with the counts
+constexpr int kSpecU = 4;   // ... by this many loads per thread (n_wg * kSpecL <= kSpecU * kRT)
 constexpr int kCollectPer = kTopkCollectSlice / kCT;  // 16 keys per thread
 
 CSA_DEV uint32_t bin_of(uint32_t key) { return key >> kTopkShift; }
@@ -453,16 +455,31 @@ __global__ __launch_bounds__(kRT) void topk_resolve_kernel(IndexArgs a, TopkWs w
 __global__ __launch_bounds__(kRT) void topk_fused_resolve_kernel(IndexArgs a, TopkWs ws, int n_wg) {
   extern __shared__ unsigned char dyn[];
   Lds& L = *reinterpret_cast<Lds*>(dyn);
-  __shared__ int s_os[kTopkMaxWgRow + 1], s_oc[kTopkMaxWgRow + 1], s_e0[kTopkMaxWgRow];
+  __shared__ int s_os[kTopkMaxWgRow + 1], s_oc[kTopkMaxWgRow + 1];
   const int row = blockIdx.x, b = row / a.Tq, tq = row % a.Tq, tid = threadIdx.x, lane = tid & 63;
   int* hist = ws.hist + (size_t)row * kTopkBins;
   int* ctr = ws.ctr + (size_t)row * 4;
   int32_t* out = a.topk_idx + (size_t)row * a.k;
+  const int* lsure = ws.lsure + (size_t)row * ws.list_len;
+  const uint2* lcand = ws.lcand + (size_t)row * ws.list_len;
+  const int stride = ws.list_stride;
   // all requested at once: the workgroups' counts, the failure flag and the
-  // threshold bin the scoring kernel published, the position
+  // threshold bin the scoring kernel published, the position, and the first
+  // kSpecL entries of every workgroup's two lists (at fixed places), which
+  // hold whole lists but for rare long ones
   const int4 info = tid < n_wg ? ws.wg_info[(size_t)row * kTopkMaxWgRow + tid] : make_int4(0, 0, 0, 0);
   const int failed = ctr[2], pub = ctr[3];
   const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
+  const bool spec = n_wg * kSpecL <= kSpecU * kRT;
+  int sv[kSpecU];
+  uint2 cv[kSpecU];
+#pragma unroll
+  for (int u = 0; u < kSpecU; ++u) {
+    const int f = tid + kRT * u, j = f / kSpecL, kk = f % kSpecL;
+    const size_t off = (size_t)(j < n_wg ? j : 0) * stride + kk;
+    sv[u] = spec ? lsure[off] : 0;
+    cv[u] = spec ? lcand[off] : make_uint2(0, 0);
+  }
   const int nv = (int)visible(a, b, t);
   const int k = a.k;
   bool from_row = false;
@@ -477,9 +494,9 @@ __global__ __launch_bounds__(kRT) void topk_fused_resolve_kernel(IndexArgs a, To
     if (tid < n_wg) {
       s_os[tid] = info.x;
       s_oc[tid] = info.y;
-      s_e0[tid] = info.z;
     }
-    __syncthreads();
+    // any list longer than the speculative part?
+    const int longer = __syncthreads_or(tid < n_wg && (!spec || info.x > kSpecL || info.y > kSpecL));
     if (tid < 64) {
       const int cpw = (n_wg + 63) / 64, j0 = min(lane * cpw, n_wg), j1 = min(j0 + cpw, n_wg);
       int cs = 0, cc = 0;
@@ -506,17 +523,31 @@ __global__ __launch_bounds__(kRT) void topk_fused_resolve_kernel(IndexArgs a, To
     if (tot_s != above || tot_c > kTopkCandCap) {
       from_row = true;
     } else {
-      const int* lsure = ws.lsure + (size_t)row * a.E_cap;
-      const uint2* lcand = ws.lcand + (size_t)row * a.E_cap;
-      for (int g = tid; g < tot_s; g += kRT) {
-        const int j = owner_of(s_os, n_wg, g);
-        L.win[g] = lsure[s_e0[j] + g - s_os[j]];
+      // place the speculatively loaded entries; the rest of longer lists
+      // (each workgroup's entries kSpecL ..) is fetched now, a wavefront per
+      // workgroup
+      if (spec) {
+#pragma unroll
+        for (int u = 0; u < kSpecU; ++u) {
+          const int f = tid + kRT * u, j = f / kSpecL, kk = f % kSpecL;
+          if (j < n_wg) {
+            if (kk < s_os[j + 1] - s_os[j]) L.win[s_os[j] + kk] = sv[u];
+            if (kk < s_oc[j + 1] - s_oc[j]) {
+              L.ckey[s_oc[j] + kk] = cv[u].x;
+              L.cid[s_oc[j] + kk] = (int)cv[u].y;
+            }
+          }
+        }
       }
-      for (int g = tid; g < tot_c; g += kRT) {
-        const int j = owner_of(s_oc, n_wg, g);
-        const uint2 v = lcand[s_e0[j] + g - s_oc[j]];
-        L.ckey[g] = v.x;
-        L.cid[g] = (int)v.y;
+      const int first = spec ? kSpecL : 0;
+      for (int j = tid >> 6; longer && j < n_wg; j += kRT / 64) {
+        const int ns = s_os[j + 1] - s_os[j], nc = s_oc[j + 1] - s_oc[j];
+        for (int kk = first + lane; kk < ns; kk += 64) L.win[s_os[j] + kk] = lsure[(size_t)j * stride + kk];
+        for (int kk = first + lane; kk < nc; kk += 64) {
+          const uint2 v = lcand[(size_t)j * stride + kk];
+          L.ckey[s_oc[j] + kk] = v.x;
+          L.cid[s_oc[j] + kk] = (int)v.y;
+        }
       }
       __syncthreads();
       const int want = k - above;
@@ -619,7 +650,7 @@ size_t topk_ws_bytes(int rows, int E_cap, bool split) {
   size_t per = kTopkBins * 4 + 16;
   if (split)
     per += (size_t)kTopkCandCap * 8 + (size_t)kTopkMaxK * 4 + (size_t)kTopkMaxWgRow * 16 +
-           (size_t)E_cap * (4 + 8);
+           (size_t)topk_list_len(E_cap) * (4 + 8);
   return (size_t)rows * per + 2048;
 }
 
@@ -642,8 +673,9 @@ TopkWs topk_ws_carve(void* base, int rows, int E_cap, bool split) {
   p += 256;
   w.wg_info = reinterpret_cast<int4*>(p);
   p += (size_t)rows * kTopkMaxWgRow * 16;
+  w.list_len = topk_list_len(E_cap);
   w.lcand = reinterpret_cast<uint2*>(p);
-  p += (size_t)rows * E_cap * 8;
+  p += (size_t)rows * w.list_len * 8;
   w.lsure = reinterpret_cast<int*>(p);
   return w;
 }
