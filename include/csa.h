@@ -25,7 +25,10 @@
  *   the matching *_workspace() function returns.  A workspace must be
  *   zero-filled once when first allocated; every call returns the counters it
  *   uses to zero before it completes.  Calls that share a workspace must be
- *   ordered on one stream.
+ *   ordered on one stream, and must be calls of one entry point with one
+ *   configuration (the same descriptor and sizes): other calls place other
+ *   data where its counters live, so a workspace passed to a different entry
+ *   point or configuration must be zero-filled again first.
  * - Supported shapes: c in {64, 128, 256, 512}; d_I in {32, 64, 128};
  *   H <= 128; H_I <= 64; 1 <= m <= 128; k <= 2048; n_win <= 256; at most
  *   2^19 indexer entries per sequence (a 2M-token context at m = 4).  Other
