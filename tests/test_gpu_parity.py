@@ -166,6 +166,38 @@ def test_decode_csa_fp8_no_fold(gpu_lib, pos_off):
     _check_decode(g, sess, f"csa-fp8-no-fold-{pos_off}")
 
 
+@pytest.mark.parametrize("n,pos_off", [(4 * 40, 2), (4 * 2, 0), (4 * 2, 3)])
+def test_decode_csa_short_context(gpu_lib, n, pos_off):
+    """Fewer visible entries than k (all selected) and a window that is not
+    full yet (t + 1 < n_win), down to two compressed entries."""
+    from sparse_attention_csa_amd.harness import DecodeSession
+    g = workloads.pro_csa_decode(seed=37, B=2, n=n, H=128, c=512, H_I=8, d_I=64, k=128, pos_off=pos_off)
+    sess = DecodeSession(g)
+    sess.run()
+    _check_decode(g, sess, f"csa-short-{n}-{pos_off}")
+
+
+@pytest.mark.parametrize("n,pos_off", [(128 * 1, 0), (128 * 2, 3)])
+def test_decode_hca_short_context(gpu_lib, n, pos_off):
+    """HCA decode with one or two entries (the first fold) and a window that
+    is not full yet."""
+    from sparse_attention_csa_amd.harness import DecodeSession
+    g = workloads.flash_hca_decode(seed=38, B=2, n=n, H=64, c=512, pos_off=pos_off)
+    sess = DecodeSession(g)
+    sess.run()
+    _check_decode(g, sess, f"hca-short-{n}-{pos_off}")
+
+
+def test_decode_csa_largest_k_and_window(gpu_lib):
+    """The largest supported selection and window: k = 2048, n_win = 256
+    (2304 rows per query in one split of the sparse kernel at most)."""
+    from sparse_attention_csa_amd.harness import DecodeSession
+    g = workloads.pro_csa_decode(seed=39, B=2, n=4 * 6000, H=128, c=512, H_I=16, d_I=128, k=2048, n_win=256)
+    sess = DecodeSession(g)
+    sess.run()
+    _check_decode(g, sess, "csa-k2048-win256")
+
+
 @pytest.mark.parametrize("H,c", [(16, 128), (128, 512)])
 def test_decode_csa_fp8_indexer_small(gpu_lib, H, c):
     from sparse_attention_csa_amd.harness import DecodeSession
