@@ -449,12 +449,14 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   if (!select) return;
   int b1, above;
   if (s_misc[15]) {
-    // last of the row: the histogram is complete; read it device-coherently
-    int* gh = ws.hist + (size_t)row * kTopkBins;
-    for (int i = tid; i < kTopkBins; i += 256)
-      s_hist[i] = __hip_atomic_load(gh + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    find_bin<256>(s_hist, a.k, s_misc, s_misc + 8, &b1, &above);
+    // last of the row: the histogram is complete; read it device-coherently,
+    // all eight loads of a thread in flight together (bins in descending
+    // order over the threads, as find_bin_counts takes them)
+    const int* gh = ws.hist + (size_t)row * kTopkBins + (kTopkBins - 1) - 8 * tid;
+    int c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = __hip_atomic_load(gh - i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    find_bin_counts<256>(c, a.k, s_misc, s_misc + 8, &b1, &above);
     if (tid == 0)
       __hip_atomic_store(slot + 3, (1 << 30) | (above << 11) | b1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {

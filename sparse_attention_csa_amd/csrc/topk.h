@@ -69,19 +69,17 @@ CSA_DEV int block_excl_scan(int v, int* s_w, int* total) {
   return off + inc - v;
 }
 
-// b1 (bin of the k-th largest key) and the count above it from a kTopkBins
-// histogram (global or LDS); every thread gets both.  s_w: NT/64 ints,
-// s_out: 2 ints.
+// b1 (bin of the k-th largest key) and the count above it, from each
+// thread's kTopkBins / NT bin counts c[i] = count of bin
+// kTopkBins - 1 - (PER tid + i) (bins in descending order over the threads);
+// every thread gets both.  s_w: NT/64 ints, s_out: 2 ints.
 template <int NT>
-CSA_DEV void find_bin(const int* hist, int k, int* s_w, int* s_out, int* b1, int* above) {
+CSA_DEV void find_bin_counts(const int* c, int k, int* s_w, int* s_out, int* b1, int* above) {
   const int tid = threadIdx.x;
   constexpr int PER = kTopkBins / NT;
-  int c[PER], tot = 0;
+  int tot = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    c[i] = hist[kTopkBins - 1 - (PER * tid + i)];
-    tot += c[i];
-  }
+  for (int i = 0; i < PER; ++i) tot += c[i];
   int all;
   const int before = block_excl_scan<NT>(tot, s_w, &all);
   if (before < k && before + tot >= k) {
@@ -100,6 +98,16 @@ CSA_DEV void find_bin(const int* hist, int k, int* s_w, int* s_out, int* b1, int
   *b1 = s_out[0];
   *above = s_out[1];
   __syncthreads();
+}
+
+// the same from a kTopkBins histogram (global or LDS)
+template <int NT>
+CSA_DEV void find_bin(const int* hist, int k, int* s_w, int* s_out, int* b1, int* above) {
+  constexpr int PER = kTopkBins / NT;
+  int c[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) c[i] = hist[kTopkBins - 1 - (PER * threadIdx.x + i)];
+  find_bin_counts<NT>(c, k, s_w, s_out, b1, above);
 }
 
 size_t topk_ws_bytes(int rows, int E_cap, bool split);
