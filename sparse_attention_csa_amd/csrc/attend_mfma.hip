@@ -602,16 +602,8 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
     nrow = *reinterpret_cast<const uint4*>(a.fold_new + (size_t)b * kC + 8 * l);
     xrow = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.fold.x_new) + (size_t)b * kC + 8 * l);
   }
-  // lane s holds split s's statistics
-  float ms = -INFINITY, Ls = 0.f;
-  if (l < n_split) {
-    const float2 v = *reinterpret_cast<const float2*>(pml + 2 * (((size_t)qrow * n_split + l) * H + h));
-    ms = v.x;
-    Ls = v.y;
-  }
-  const float M = fmaxf(fmaxf(fmaxf(wave_max(ms), z2), s_new), s_own);
-  const float wgt = (ms == -INFINITY || Ls == 0.f) ? 0.f : __builtin_amdgcn_exp2f(ms - M) * Ls;
-  // this wavefront's splits: all loads first
+  // this wavefront's splits' rows, then the statistics: every load is in
+  // flight before the first wait
   uint4 raw[kMergeU];
 #pragma unroll
   for (int u = 0; u < kMergeU; ++u) {
@@ -622,6 +614,15 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
       raw[u] = *reinterpret_cast<const uint4*>(po + slot * kC + 8 * l);
     }
   }
+  // lane s holds split s's statistics
+  float ms = -INFINITY, Ls = 0.f;
+  if (l < n_split) {
+    const float2 v = *reinterpret_cast<const float2*>(pml + 2 * (((size_t)qrow * n_split + l) * H + h));
+    ms = v.x;
+    Ls = v.y;
+  }
+  const float M = fmaxf(fmaxf(fmaxf(wave_max(ms), z2), s_new), s_own);
+  const float wgt = (ms == -INFINITY || Ls == 0.f) ? 0.f : __builtin_amdgcn_exp2f(ms - M) * Ls;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int u = 0; u < kMergeU; ++u) {
