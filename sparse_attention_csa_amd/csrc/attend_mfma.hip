@@ -39,6 +39,8 @@
 // more row, weight exp2(scale q . entry - M), and publishes the entry count.
 // The query's own window row is read from the step input x_new.
 
+#include <type_traits>
+
 #include "fold.h"
 #include "kernels.h"
 #include "mfma_tile.h"
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   __shared__ __attribute__((aligned(1024))) char tiles[kRing][kTN * kRowB];
   __shared__ uint32_t rvalid[kRing][kTN / 4];  // byte r % 4 of word r / 4: row r is a real row
   __shared__ int s_restart;                // a wavefront asks the split to be recomputed
-  __shared__ bf16x8_t s_p[4][64];          // P^T operands of the tile, one block of 16 heads per wavefront
+  __shared__ bf16x8_t s_p[2][4][64];       // P^T operands of a tile (two buffers), one block of 16 heads per wavefront
   __shared__ float s_scale[kHW];           // output scale per head
   __shared__ Soft s_fpart[4][64];          // fold: per-wavefront partial states of <= 64 coordinates
   __shared__ float s_fnew[64];             // fold: the new entry's coordinates (bf16-rounded)
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   char* const fz_l = tiles[kRing - 1];                     // [m][fW] bf16: stream 1 (logits)
   char* const fx_l = fz_l + (size_t)F.m * fW * 2;          // [m][fW] bf16: stream 0 (values)
   char* const fb_l = fx_l + (size_t)F.m * fW * 2;          // [m][fW] f32: positional bias
-  char* const fq_l = reinterpret_cast<char*>(&s_p[0][0]);  // [H][fW] bf16: query slice
+  char* const fq_l = reinterpret_cast<char*>(&s_p[0][0][0]);  // [H][fW] bf16: query slice
   char* const fa_l = reinterpret_cast<char*>(s_fapp);      // [3][fW] bf16: x_new, streams 0, 1
   const uint16_t* const fio = reinterpret_cast<const uint16_t*>(F.streams) + (size_t)b * 2 * a.c;
   if (fW > 0) {
@@ -395,30 +397,63 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   const int* s_base = bs.s;
   const int* t_base = bs.t;
 
-  auto compute_tile = [&](int buf) {
-    const char* T = tiles[buf];
-    // S^T[32 rows x 16 heads] = K . Q^T as two 16-row blocks, each summed
-    // in two halves (even / odd k steps): four independent MFMA chains
+  // Scores and softmax weights of the tile in slot sb: S^T[32 rows x 16
+  // heads] = K . Q^T as two 16-row blocks, each summed in two halves (even /
+  // odd k steps): four independent MFMA chains.  With WithPV, the previous
+  // tile's O^T[d x 64 heads] += V^T[d x 32 rows] . P^T[32 rows x 64 heads]
+  // (slot vb, operands pa) runs interleaved with them: two independent MFMA
+  // streams and their LDS reads keep the one wavefront per SIMD busy while
+  // either waits.  Returns this wavefront's P^T block (the rows permuted as
+  // the B operand wants).
+  auto score_tile = [&](auto with_pv, int sb, int vb, const bf16x8_t* pa) -> bf16x8_t {
+    constexpr bool kPV = decltype(with_pv)::value;
+    const char* T = tiles[sb];
+    const char* V = tiles[vb];
     constexpr int kRB = kTN / 16;
+    static_assert(kRB == 2, "one row pair per tile");
     f32x4_t s2[kRB][2];
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) s2[rb][0] = s2[rb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks)
+    for (int t = 0; t < 8; ++t) {
 #pragma unroll
-      for (int rb = 0; rb < kRB; ++rb)
-        s2[rb][ks & 1] = mfma32(lds8(T + s_base[ks & 3] + rb * 16 * kRowB + 256 * (ks >> 2)), qf[ks], s2[rb][ks & 1]);
-    // keep 12 fragment reads in flight ahead of the MFMAs (lgkmcnt counts 15)
-    __builtin_amdgcn_sched_group_barrier(0x100, 12, 1);
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int ks = 2 * t + k2;
 #pragma unroll
-    for (int i = 0; i < 16 * kRB - 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+        for (int rb = 0; rb < kRB; ++rb)
+          s2[rb][ks & 1] = mfma32(lds8(T + s_base[ks & 3] + rb * 16 * kRowB + 256 * (ks >> 2)), qf[ks], s2[rb][ks & 1]);
+      }
+      if constexpr (kPV) {
+        // each V^T block (two transposed reads) serves four MFMAs, so a
+        // tile is transpose-read once per workgroup
+        const char* v0 = V + t_base[t] + 256 * w;
+        const bf16x8_t va = cat8(ld_tr(v0), ld_tr(v0 + 16 * kRowB));
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) acc[4 * t + hb] = mfma32(va, pa[hb], acc[4 * t + hb]);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 12, 1);
-    f32x4_t s[kRB];
+    if constexpr (kPV) {
+      // eight fragment reads ahead, then one read per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 1);
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) s[rb] = s2[rb][0] + s2[rb][1];
+      for (int i = 0; i < 40; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 24, 1);
+    } else {
+      // keep 12 fragment reads in flight ahead of the MFMAs (lgkmcnt counts 15)
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 1);
+#pragma unroll
+      for (int i = 0; i < 16 * kRB - 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 12, 1);
+    }
+    f32x4_t sv[kRB];
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) sv[rb] = s2[rb][0] + s2[rb][1];
     // softmax weights against a fixed reference max per head; lane holds
     // rows 16rb + 4lg + i of head li.  The reference is the first tile's max
     // and stays put while tile maxima exceed it by at most kSlack (log2
@@ -430,10 +465,10 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     float mx = -INFINITY;
 #pragma unroll
     for (int rb = 0; rb < kRB; ++rb) {
-      const uint32_t fl = rvalid[buf][4 * rb + lg];
+      const uint32_t fl = rvalid[sb][4 * rb + lg];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[rb][i] = ((fl >> (8 * i)) & 1u) ? s[rb][i] * sc2 : -INFINITY;
+        x[rb][i] = ((fl >> (8 * i)) & 1u) ? sv[rb][i] * sc2 : -INFINITY;
         mx = fmaxf(mx, x[rb][i]);
       }
     }
@@ -453,26 +488,20 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
       }
       pb[rb] = bf16x4_t{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
     }
-    // P^T of all four head blocks through LDS; then
-    // O^T[d x 64 heads] += V^T[d x 32 rows] . P^T[32 rows x 64 heads] for
-    // this wavefront's 128 coordinates: each V^T block (two transposed
-    // reads) serves four MFMAs, so a tile is transpose-read once per
-    // workgroup instead of once per wavefront
-    static_assert(kRB == 2, "one row pair per tile");
-    s_p[w][l] = __builtin_shufflevector(pb[0], pb[1], 0, 1, 2, 3, 4, 5, 6, 7);
-    lds_barrier();
-    bf16x8_t pa[4];
-#pragma unroll
-    for (int hb = 0; hb < 4; ++hb) pa[hb] = s_p[hb][l];
+    return __builtin_shufflevector(pb[0], pb[1], 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // the last tile's O^T += V^T . P^T alone
+  auto pv_tile = [&](int vb, const bf16x8_t* pa) {
+    const char* V = tiles[vb];
 #pragma unroll
     for (int dtl = 0; dtl < 8; ++dtl) {
-      const char* v0 = T + t_base[dtl] + 256 * w;
+      const char* v0 = V + t_base[dtl] + 256 * w;
       const bf16x8_t va = cat8(ld_tr(v0), ld_tr(v0 + 16 * kRowB));
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) acc[4 * dtl + hb] = mfma32(va, pa[hb], acc[4 * dtl + hb]);
     }
-    // the P^T reads and two V^T blocks ahead, then one V^T block per four MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 2);
+    // two V^T blocks ahead, then one V^T block per four MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 2);
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 2);
@@ -480,26 +509,44 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     }
     __builtin_amdgcn_sched_group_barrier(0x008, 8, 2);
   };
+  // wait until at most `younger` of this wave's tiles issued after the one
+  // needed next are still in flight (8 DMAs per tile)
+  auto wait_tiles = [&](int younger) {
+    if (younger >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * kRowsPerWave));
+    else if (younger == 1) __builtin_amdgcn_s_waitcnt(wait_vm(kRowsPerWave));
+    else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  };
 
-  // ring of kRing tile slots: a wave first waits for its own DMAs of tile i
-  // (the younger tiles i+1, i+2 may stay in flight); after the barrier every
-  // wave's DMAs of tile i have landed and every wave has finished tile i-1
-  // (and read its P^T blocks), so tile i+kRing-1 may be fetched into that
-  // slot while tile i is computed.  A second barrier inside the tile
-  // publishes the P^T blocks.
-  static_assert(kRing == 4, "the waits below assume two younger tiles");
+  // Ring of kRing tile slots, software-pipelined by one tile: iteration j
+  // computes the scores of tile j+1 together with the P.V of tile j.  One
+  // barrier per tile: before it each wave has published tile j's P^T block
+  // and waited for its own DMAs of tile j+1; after it every wave may read
+  // all P^T blocks of tile j and tile j+1, and every wave has finished the
+  // P.V of tile j-1, whose slot then takes tile j+3 (tiles j+2, j+3 in
+  // flight while j+1 is scored).  P^T alternates between two LDS buffers.
+  static_assert(kRing == 4, "the waits below assume at most two younger tiles");
   for (;;) {
-    int buf = 0;
-    for (int r0 = r_begin; r0 < r_end; r0 += kTN) {
-      const int younger = (r_end - r0 - 1) / kTN;  // tiles after this one
-      if (younger >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * kRowsPerWave));
-      else if (younger == 1) __builtin_amdgcn_s_waitcnt(wait_vm(kRowsPerWave));
-      else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+    const int nt = r_end > r_begin ? (r_end - r_begin + kTN - 1) / kTN : 0;
+    if (nt > 0) {
+      wait_tiles(nt - 1 < 2 ? nt - 1 : 2);  // tile 0 (tiles 1, 2 may be in flight)
       lds_barrier();
-      const int rn = r0 + (kRing - 1) * kTN;
-      if (rn < r_end) issue_tile(rn, (buf + kRing - 1) & (kRing - 1));
-      compute_tile(buf);
-      buf = (buf + 1) & (kRing - 1);
+      // slot kRing - 1 is free now (the fold's staging is consumed)
+      if (nt > 3) issue_tile(r_begin + 3 * kTN, 3);
+      bf16x8_t pa[4];
+      bf16x8_t pw = score_tile(std::false_type{}, 0, 0, pa);
+      for (int j = 0;; ++j) {
+        s_p[j & 1][w][l] = pw;
+        // tiles issued so far: 0 .. min(max(j + 2, 3), nt - 1)
+        const int hi = (j + 2 > 3 ? j + 2 : 3) < nt - 1 ? (j + 2 > 3 ? j + 2 : 3) : nt - 1;
+        wait_tiles(hi - (j + 1) > 0 ? hi - (j + 1) : 0);
+        lds_barrier();
+        if (j >= 1 && j + 3 < nt) issue_tile(r_begin + (j + 3) * kTN, (j + 3) & (kRing - 1));
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) pa[hb] = s_p[j & 1][hb][l];
+        if (j + 1 == nt) break;
+        pw = score_tile(std::true_type{}, (j + 1) & (kRing - 1), j & (kRing - 1), pa);
+      }
+      pv_tile((nt - 1) & (kRing - 1), pa);
     }
     lds_barrier();
     const int again = s_restart;
