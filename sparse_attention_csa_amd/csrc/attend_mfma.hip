@@ -14,7 +14,8 @@
 // every row of a tile, so a row crosses HBM / L2 into LDS once per split, not
 // once per head group.  Row tiles of 32 rows (32 KB) are fetched into LDS by
 // direct global-to-LDS DMA (one 1 KB row per wave instruction) into a ring of
-// four slots: three tiles are in flight while one is computed.
+// four slots: while tile j+1 is scored and tile j multiplied into the output,
+// tiles j+2 and j+3 are in flight.
 //
 // Tied K = V on MFMA.  The score product is computed transposed,
 //   S^T[rows x heads] = K[rows x d] . Q^T[d x heads]   (v_mfma 16x16x32 bf16),
@@ -86,22 +87,13 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   const int H = a.H;
   const int h0 = hg * kHW + 16 * w;  // this wavefront's first head
 
-  // The query operands (vector loads) and the position, entry count and
-  // window base (scalar loads) are requested first.  The first tiles' rows
-  // are usually cache entries whose addresses need neither, so their DMAs
-  // go out before the scalars return (checked below, reissued in the rare
-  // case); the vector loads are awaited before the row loop, so that the
-  // loop's waits count row DMAs only.
-  // Q^T operands for this wavefront's 16 heads: lane (head li, d group lg).
-  bf16x8_t qf[16];
-  {
-    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)qrow * H + h0 + li) * kC + 8 * lg;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(q + 32 * ks);
-  }
-  // (unconditional loads: an absent optional array is replaced by a valid
-  // dummy address and the value discarded, so the three loads are in flight
-  // together instead of one branch and wait each)
+  // The position, entry count and window base (scalar loads) are requested
+  // first.  The first tile's rows are usually cache entries whose addresses
+  // need none of them, so its DMAs go out before they return (checked
+  // below, reissued in the rare case).  (Unconditional loads: an absent
+  // optional array is replaced by a valid dummy address and the value
+  // discarded, so the three loads are in flight together instead of one
+  // branch and wait each.)
   const int64_t* dummy64 = reinterpret_cast<const int64_t*>(a.kv);
   const int64_t t_ld = (a.q_pos ? a.q_pos + qrow : dummy64)[0];
   const int64_t w_ld = (a.win_pos0 ? a.win_pos0 + b : dummy64)[0];
@@ -135,13 +127,21 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
       dma16_m0(reinterpret_cast<const uint16_t*>(ri) + dofs[i], lds0 + i * kRowB);
     }
   };
-  // speculative: the first kRing - 1 tiles read as cache entries (in the
-  // cache buffer, so in bounds whatever the count turns out to be)
-  const bool spec = r_begin + (kRing - 1) * kTN <= a.E_cap;
-  if (spec) {
+  // speculative: the first tile read as cache entries (in the cache
+  // buffer, so in bounds whatever the count turns out to be), before
+  // anything else
+  const bool spec = r_begin + kTN <= a.E_cap;
+  if (spec) dma_rows(kv + (size_t)(r_begin + kRowsPerWave * w + (l & (kRowsPerWave - 1))) * kC, 0);
+  // Q^T operands for this wavefront's 16 heads: lane (head li, d group lg).
+  // They are requested after the first tile's DMAs and before the
+  // position, entry count and window base (scalar loads); the query loads
+  // and the first tile are awaited together before the row loop, which the
+  // later tiles' DMAs do not hold up.
+  bf16x8_t qf[16];
+  {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)qrow * H + h0 + li) * kC + 8 * lg;
 #pragma unroll
-    for (int jt = 0; jt < kRing - 1; ++jt)
-      dma_rows(kv + (size_t)(r_begin + jt * kTN + kRowsPerWave * w + (l & (kRowsPerWave - 1))) * kC, jt);
+    for (int ks = 0; ks < 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(q + 32 * ks);
   }
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the scalars
   __asm__ __volatile__("" ::"s"(t_ld), "s"(w_ld), "s"(cnt));
@@ -264,19 +264,22 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     for (int j = 0; j < kRing - 1; ++j)
       if (r_begin + j * kTN < r_end) issue_tile(r_begin + j * kTN, j);
   };
-  // the speculative tiles hold the right rows when every row of them that
-  // the split uses is a cache entry; else they are fetched again
-  if (spec && (r_end < r_begin + (kRing - 1) * kTN ? r_end : r_begin + (kRing - 1) * kTN) <= nc32) {
-#pragma unroll
-    for (int jt = 0; jt < kRing - 1; ++jt) set_valid(r_begin + jt * kTN, jt);
+  // the speculative tile holds the right rows when every row of it that
+  // the split uses is a cache entry; else it is fetched again
+  if (spec && (r_end < r_begin + kTN ? r_end : r_begin + kTN) <= nc32) {
+    set_valid(r_begin, 0);
   } else {
-    __builtin_amdgcn_s_waitcnt(wait_vm(0));  // (the slots are written again)
-    prologue();
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));  // (the slot is written again)
+    if (r_begin < r_end) issue_tile(r_begin, 0);
   }
-  // every load and DMA so far, the query operands included, has landed
-  // before the fold and the row loop
+  // every load and DMA so far (the query operands, the first tile, the
+  // fold's inputs) has landed before the fold and the row loop; then the
+  // next two tiles go out
   __builtin_amdgcn_s_waitcnt(0);
   __asm__ __volatile__("" ::"v"(qf[0]), "v"(qf[15]));
+#pragma unroll
+  for (int j = 1; j < kRing - 1; ++j)
+    if (r_begin + j * kTN < r_end) issue_tile(r_begin + j * kTN, j);
 
   if (fW > 0) {
     lds_barrier();  // every wavefront's fold DMAs
