@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   constexpr int kU = G::kU;
   __shared__ __attribute__((aligned(1024))) char s_tr[4][kU * G::kTileB];  // per-wave transpose buffer
   __shared__ int s_hist[kTopkBins];
-  __shared__ float s_sc[kTopkFuseCap];  // fused: this workgroup's scores, by entry - first entry
+  __shared__ __attribute__((aligned(16))) float s_sc[kTopkFuseCap];  // fused: this workgroup's scores, by entry - first entry
   __shared__ int s_misc[16];
   const int row = blockIdx.y, b = row / a.Tq, tq = row % a.Tq;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
@@ -485,13 +485,25 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
     n_ent = fold_now ? 1 : 0;
   }
   int4* info = ws.wg_info + (size_t)row * kTopkMaxWgRow + blockIdx.x;
-  // contiguous runs per thread keep the lists in entry order
-  const int cpt = (n_ent + 255) / 256;
-  const int i0 = min(tid * cpt, n_ent), i1 = min(i0 + cpt, n_ent);
+  // contiguous runs per thread keep the lists in entry order; a run is a
+  // multiple of 4 entries, read once as 16-byte vectors into registers
+  constexpr int kRun = kTopkFuseCap / 256;  // entries per thread, at most
+  const int cpt = ((n_ent + 255) / 256 + 3) & ~3;
+  const int i0 = tid * cpt;
+  uint32_t key[kRun];
   int cnt = 0;  // certain winners in the low half, candidates in the high half
-  for (int i = i0; i < i1; ++i) {
-    const int bin = (int)(f32_key(s_sc[i]) >> kTopkShift);
-    cnt += (bin > b1 ? 1 : 0) + (bin == b1 ? 1 << 16 : 0);
+#pragma unroll
+  for (int v = 0; v < kRun / 4; ++v) {
+    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (4 * v < cpt && i0 + 4 * v < n_ent) f = *reinterpret_cast<const float4*>(s_sc + i0 + 4 * v);
+    const float fv[4] = {f.x, f.y, f.z, f.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = 4 * v + u;
+      key[i] = f32_key(fv[u]);
+      const int bin = (int)(key[i] >> kTopkShift);
+      if (i < cpt && i0 + i < n_ent) cnt += (bin > b1 ? 1 : 0) + (bin == b1 ? 1 << 16 : 0);
+    }
   }
   int total;
   const int off = block_excl_scan<256>(cnt, s_misc, &total);
@@ -499,11 +511,12 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   const size_t list_off = (size_t)row * ws.list_len + (size_t)blockIdx.x * ws.list_stride;
   int* lsure = ws.lsure + list_off;
   uint2* lcand = ws.lcand + list_off;
-  for (int i = i0; i < i1; ++i) {
-    const uint32_t key = f32_key(s_sc[i]);
-    const int bin = (int)(key >> kTopkShift);
-    if (bin > b1) lsure[os++] = (int)e_first + i;
-    if (bin == b1) lcand[oc++] = make_uint2(key, (uint32_t)(e_first + i));
+#pragma unroll
+  for (int i = 0; i < kRun; ++i) {
+    const bool in = i < cpt && i0 + i < n_ent;
+    const int bin = (int)(key[i] >> kTopkShift);
+    if (in && bin > b1) lsure[os++] = (int)e_first + i0 + i;
+    if (in && bin == b1) lcand[oc++] = make_uint2(key[i], (uint32_t)(e_first + i0 + i));
   }
   if (tid == 0) *info = make_int4(total & 0xffff, (unsigned)total >> 16, (int)e_first, 0);
 }
