@@ -30,15 +30,16 @@
 // that permutation.  Softmax runs in base 2.
 //
 // Decode with the step's fold inside (fold_mode): the splits cover the
-// entries that existed before the step; split s of head group 0 also folds
-// coordinates [s cs, s cs + cs) of the entry the block ending at the query
-// position completes (its sources are loaded after the row loop and arrive
-// while the output is written; nothing of the fold stays live across the
-// loop), stores them, adds its share of q_h . entry for every head
-// to fold_s (device-scope atomics) and appends its share of the token to the
-// tail and window rings.  The merge kernel then adds the new entry as one
-// more row, weight exp2(scale q . entry - M), and publishes the entry count.
-// The query's own window row is read from the step input x_new.
+// entries that existed before the step and the window rows but the query's
+// own token.  Split s of head group 0 also folds coordinates
+// [s cs, s cs + cs) of the entry that the block ending at the query position
+// completes: its sources, query slice and token slice arrive by DMA in the
+// ring slot not yet in use, the fold runs before the row loop (nothing of it
+// stays live across the loop), stores its slice of the entry, adds its share
+// of q_h . entry and q_h . token for every head to fold_s (device-scope
+// atomics) and appends its share of the token to the tail and window rings.
+// The merge kernel then adds the new entry and the query's own token as two
+// more rows, weights exp2(scale q . x - M), and publishes the entry count.
 
 #include <type_traits>
 
