@@ -55,7 +55,7 @@ namespace {
 
 constexpr int kHW = 64;                // heads per workgroup (16 per wavefront)
 constexpr int kTN = 32;                // rows per LDS tile
-constexpr int kRing = 4;               // LDS tile slots: kRing - 1 tiles in flight while one is computed
+constexpr int kRing = 4;               // LDS tile slots: two tiles in use (scores, P.V), two in flight
 constexpr int kRowsPerWave = kTN / 4;  // DMA instructions per wave and tile
 constexpr int kFoldS = 16;             // fold slice: sources per thread (at most)
 constexpr int kFoldRowsLess = 64;      // rows a folding split gives up to the others
@@ -259,7 +259,8 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     set_valid(r0, buf);
   };
 
-  // the first kRing - 1 tiles
+  // the first kRing - 1 tiles (a pass recomputed after a jump of the
+  // reference max)
   auto prologue = [&]() {
 #pragma unroll
     for (int j = 0; j < kRing - 1; ++j)
