@@ -71,7 +71,7 @@ CSA_DEV float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); 
 namespace {
 
 constexpr int kD = 128;
-constexpr int kFuseWaitTries = 40000;  // polls of the published threshold bin (about 10 ms)
+constexpr int kFuseWaitTries = 40000;  // polls of the published threshold bin (a few ms)
 
 // Tile geometry.  e4m3: 16 keys x 128 B = 2 KB, read as two 1 KB pieces of
 // 8 keys; bf16: 16 keys x 256 B = 4 KB, four pieces of 4 keys.  In LDS, chunk
@@ -461,10 +461,19 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
       __hip_atomic_store(slot + 3, (1 << 30) | (above << 11) | b1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
     if (tid == 0) {
+      // four polls in flight, issued about 0.05 us apart: the publication
+      // is seen about one round trip after it lands, not one round trip
+      // plus a poll period
       int v = 0;
-      for (int it = 0; it < kFuseWaitTries && v == 0; ++it) {
-        v = __hip_atomic_load(slot + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (v == 0) __builtin_amdgcn_s_sleep(8);
+      for (int it = 0; it < kFuseWaitTries / 4 && v == 0; ++it) {
+        const int v0 = __hip_atomic_load(slot + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_sleep(2);
+        const int v1 = __hip_atomic_load(slot + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_sleep(2);
+        const int v2 = __hip_atomic_load(slot + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_sleep(2);
+        const int v3 = __hip_atomic_load(slot + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        v = v0 ? v0 : (v1 ? v1 : (v2 ? v2 : v3));
       }
       s_misc[14] = v;
     }
