@@ -153,10 +153,11 @@ CSA_DEV void select_candidates(Lds& L, int n, uint32_t b1, int want, int* n_win)
 
 // The same selection for candidates stored in ascending id order, keeping
 // that order: the selected ids go to sel[0 ..) (capacity kTopkMaxK).  The
-// three radix passes count into their own
-// 128-bin histograms (cleared together up front), so a pass costs two
-// barriers; the final filter needs one scan: a thread's winners go after
-// the winners above tau of the threads before it and the first rem ties.
+// (up to) three radix passes count into their own 128-bin histograms
+// (cleared together up front), so a pass costs two barriers; they stop once
+// the boundary bin holds exactly the keys still wanted.  The final filter
+// needs one scan: a thread's winners go after the winners above tau (on the
+// resolved top bits) of the threads before it and the first rem ties.
 // Returns the count selected.
 CSA_DEV int select_ordered(Lds& L, int n, uint32_t b1, int want, int* sel) {
   const int tid = threadIdx.x;
@@ -177,13 +178,16 @@ CSA_DEV int select_ordered(Lds& L, int n, uint32_t b1, int want, int* sel) {
     __syncthreads();
     prefix = (prefix << 7) | (uint32_t)L.misc[2 * pass];
     rem -= L.misc[2 * pass + 1];
+    // every key with this prefix is taken: the lower bits need no pass
+    if (h[L.misc[2 * pass]] == rem) break;
   }
+  // the threshold on the resolved top bits of the key (21 bits below b1's)
   const uint32_t tau = prefix;
   const int cpt = (n + kRT - 1) / kRT;
   const int i0 = min(tid * cpt, n), i1 = min(i0 + cpt, n);
   int ng = 0, nt = 0;  // keys above tau, ties
   for (int i = i0; i < i1; ++i) {
-    const uint32_t key = L.ckey[i];
+    const uint32_t key = L.ckey[i] >> shift;
     ng += key > tau;
     nt += key == tau;
   }
@@ -192,7 +196,7 @@ CSA_DEV int select_ordered(Lds& L, int n, uint32_t b1, int want, int* sel) {
   int tie_rank = pre >> 16;
   int o = (pre & 0xffff) + min(tie_rank, rem);
   for (int i = i0; i < i1; ++i) {
-    const uint32_t key = L.ckey[i];
+    const uint32_t key = L.ckey[i] >> shift;
     bool take = key > tau;
     if (key == tau) take = tie_rank++ < rem;
     if (take && o < kTopkMaxK) sel[o++] = L.cid[i];
