@@ -14,6 +14,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "mfma_tile.h"
 #include "topk.h"
 
 namespace csa {
@@ -87,6 +88,125 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
 }
 
 // --------------------------------------------------------------------------
+// scoring of many queries of one sequence (prefill) on MFMA, bf16, 64 heads
+// of dim 128: a workgroup scores four consecutive queries (one per
+// wavefront) against a chunk of kPfChunk entries.  The chunk streams through
+// LDS in 64-entry key tiles (16 KB, double-buffered, the next tile's loads in
+// flight while one is scored) shared by the four queries, so a key crosses
+// HBM / L2 once per four queries.  Per wavefront and 16-entry block:
+//   D[16 heads x 16 entries] = Q[16 heads x 128] . K^T[128 x 16 entries]
+// (v_mfma_f32_16x16x32_bf16, four head tiles, Q in registers); lane (head
+// row group g, entry i) holds heads 4g .. 4g+3 of entry i, so ReLU and the
+// head weights are in-lane and the head sum takes two lane exchanges.
+// --------------------------------------------------------------------------
+namespace {
+constexpr int kPfTile = 64;     // entries per LDS key tile
+constexpr int kPfChunk = 1024;  // entries per workgroup
+constexpr int kPfD = 128, kPfH = 64;
+}  // namespace
+
+bool index_prefill_mfma_supported(const IndexArgs& a) {
+  return a.idx_dtype == BF16 && a.H_I == kPfH && a.d_I == kPfD && a.Tq % 4 == 0;
+}
+
+__global__ __launch_bounds__(256) void index_score_prefill_kernel(IndexArgs a) {
+  using namespace tile;
+  // key tile: row = entry (256 B), its 16-byte chunk c stored at c ^ (row % 16)
+  __shared__ __attribute__((aligned(16))) uint4 s_k[2][kPfTile * 16];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
+  const int row0 = blockIdx.y * 4, row = row0 + w;  // the four rows share their sequence (Tq % 4 == 0)
+  const int b = row0 / a.Tq;
+  // visible entries of each of the four queries (every thread computes all
+  // four: the chunk is needed up to the largest)
+  int64_t nv_q = 0, nv_max = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tq = (row0 + j) % a.Tq;
+    const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
+    const int64_t nv = n_visible(a, b, t);
+    if (j == w) nv_q = nv;
+    nv_max = nv > nv_max ? nv : nv_max;
+  }
+  const int64_t e0 = (int64_t)blockIdx.x * kPfChunk;
+  if (e0 >= nv_max) return;
+  const int64_t e1 = e0 + kPfChunk < nv_max ? e0 + kPfChunk : nv_max;
+  const int ntiles = (int)((e1 - e0 + kPfTile - 1) / kPfTile);
+  const uint16_t* keys = reinterpret_cast<const uint16_t*>(a.keys) + (size_t)b * a.E_cap * kPfD;
+
+  // A operands: Q rows = heads 16 ht + li, d = 32 ks + 8 lg .. +7
+  bf16x8_t qa[4][4];
+  float wr[4][4];  // weights of heads 16 ht + 4 lg + i
+  {
+    const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + (size_t)row * kPfH * kPfD;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        qa[ht][ks] = *reinterpret_cast<const bf16x8_t*>(q + (size_t)(16 * ht + li) * kPfD + 32 * ks + 8 * lg);
+      const float4 wv = *reinterpret_cast<const float4*>(a.w + (size_t)row * kPfH + 16 * ht + 4 * lg);
+      wr[ht][0] = wv.x; wr[ht][1] = wv.y; wr[ht][2] = wv.z; wr[ht][3] = wv.w;
+    }
+  }
+  // thread's share of a tile: chunks tid + 256 u (entry c / 16, chunk c % 16);
+  // entries past the last visible one re-read it
+  struct Share {
+    uint4 v0, v1, v2, v3;
+  };
+  auto chunk_ptr = [&](int j, int u) -> const uint4* {
+    const int c = tid + 256 * u;
+    int64_t e = e0 + (int64_t)j * kPfTile + (c >> 4);
+    if (e > e1 - 1) e = e1 - 1;
+    return reinterpret_cast<const uint4*>(keys + (size_t)e * kPfD + 8 * (c & 15));
+  };
+  auto load_tile = [&](int j) -> Share {
+    return Share{*chunk_ptr(j, 0), *chunk_ptr(j, 1), *chunk_ptr(j, 2), *chunk_ptr(j, 3)};
+  };
+  auto slot = [&](int buf, int u) -> uint4* {
+    const int c = tid + 256 * u, kk = c >> 4;
+    return &s_k[buf][kk * 16 + ((c & 15) ^ (kk & 15))];
+  };
+  auto store_tile = [&](int buf, const Share& r) {
+    *slot(buf, 0) = r.v0;
+    *slot(buf, 1) = r.v1;
+    *slot(buf, 2) = r.v2;
+    *slot(buf, 3) = r.v3;
+  };
+  float* out = a.scores + (size_t)row * a.E_cap;
+  store_tile(0, load_tile(0));
+  __syncthreads();
+  for (int j = 0; j < ntiles; ++j) {
+    Share next{};
+    if (j + 1 < ntiles) next = load_tile(j + 1);  // in flight while tile j is scored
+    const uint4* T = s_k[j & 1];
+    const int64_t te = e0 + (int64_t)j * kPfTile;
+#pragma unroll
+    for (int kb = 0; kb < kPfTile / 16; ++kb) {
+      f32x4_t c[4];
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht) c[ht] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        // B operand: entry 16 kb + li, d = 32 ks + 8 lg .. +7 (chunk 4 ks + lg)
+        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, T[(16 * kb + li) * 16 + ((4 * ks + lg) ^ li)]);
+#pragma unroll
+        for (int ht = 0; ht < 4; ++ht) c[ht] = mfma32(qa[ht][ks], kf, c[ht]);
+      }
+      float part = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part += wr[ht][i] * fmaxf(c[ht][i], 0.f);
+      part += __shfl_xor(part, 16, 64);
+      part += __shfl_xor(part, 32, 64);
+      const int64_t e = te + 16 * kb + li;
+      if (lg == 0 && e < nv_q && e < e1) out[e] = part;
+    }
+    if (j + 1 < ntiles) store_tile((j + 1) & 1, next);
+    __syncthreads();
+  }
+}
+
+// --------------------------------------------------------------------------
 // scoring + selection
 // --------------------------------------------------------------------------
 namespace {
@@ -117,6 +237,10 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t s, const FoldArgs*
   int n_wg_fused = 0;
   if (mfma) {
     e = launch_index_score_mfma(a, tw, 1, 1, &n_wg_fused, fold, s);
+  } else if (index_prefill_mfma_supported(a)) {
+    dim3 g1((a.E_cap + kPfChunk - 1) / kPfChunk, rows / 4), blk(256);
+    CSA_LAUNCH("index_score", index_score_prefill_kernel, g1, blk, 0, s, a);
+    e = hipGetLastError();
   } else {
     dim3 g1((a.E_cap + 255) / 256, rows), blk(256);
     if (a.idx_dtype == F32)
