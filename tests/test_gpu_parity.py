@@ -232,6 +232,18 @@ def _check_prefill(g, sess, label, queries=None):
         assert np.abs(lse[0, i] - ref["lse"]).max() < 1e-3
 
 
+def test_prefill_csa_mfma_indexer(gpu_lib):
+    # 64 indexer heads of dim 128 (bf16), 64 queries (16 groups of four):
+    # the MFMA prefill scorer over two 1024-entry chunks, the last one a
+    # ragged tile; every query checked against the oracle
+    from sparse_attention_csa_amd.harness import PrefillSession
+    a, _ = workloads.flash_prefill(seed=35, T=64, n0=4500, H=64, c=512, H_I=64, d_I=128, k=64,
+                                   m_hca=128)
+    sess = PrefillSession(a)
+    sess.run()
+    _check_prefill(a, sess, "prefill-csa-mfma-indexer")
+
+
 @pytest.mark.parametrize("H,c", [(8, 64), (64, 512)])
 def test_prefill_csa_and_hca_small(gpu_lib, H, c):
     from sparse_attention_csa_amd.harness import PrefillSession
