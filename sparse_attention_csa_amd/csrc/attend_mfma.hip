@@ -815,8 +815,64 @@ hipError_t launch_attend_mfma(const AttendArgs& a0, int rows_max, hipStream_t s)
   return hipGetLastError();
 }
 
+// Few splits and no fold: grid (B*Tq, H/4), wavefront w merges every split
+// of head 4 y + w by itself (lane = 8 coordinates), so no workgroup
+// exchange is needed.  The same combination as attend_merge_kernel.
+constexpr int kMergeSmall = 16;
+__global__ __launch_bounds__(256) void attend_merge_small_kernel(AttendArgs a, int n_split) {
+  const int qrow = blockIdx.x, w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int h = blockIdx.y * 4 + w;
+  const int H = a.H;
+  const float* pml = reinterpret_cast<const float*>(a.ws);
+  const uint16_t* po = reinterpret_cast<const uint16_t*>(pml + (size_t)a.B * a.Tq * n_split * H * 2);
+  // every split's row, then the statistics: all loads in flight before the
+  // first wait
+  uint4 raw[kMergeSmall];
+#pragma unroll
+  for (int u = 0; u < kMergeSmall; ++u) {
+    raw[u] = uint4{0, 0, 0, 0};
+    if (u < n_split) raw[u] = *reinterpret_cast<const uint4*>(po + (((size_t)qrow * n_split + u) * H + h) * kC + 8 * l);
+  }
+  float ms = -INFINITY, Ls = 0.f;
+  if (l < n_split) {
+    const float2 v = *reinterpret_cast<const float2*>(pml + 2 * (((size_t)qrow * n_split + l) * H + h));
+    ms = v.x;
+    Ls = v.y;
+  }
+  const float z2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+  const float M = fmaxf(wave_max(ms), z2);
+  const float wgt = (ms == -INFINITY || Ls == 0.f) ? 0.f : __builtin_amdgcn_exp2f(ms - M) * Ls;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < kMergeSmall; ++u) {
+    const float ws = __shfl(wgt, u, 64);
+    if (u < n_split) {
+      const uint32_t v[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[2 * i] += ws * bf16_to_f32((uint16_t)(v[i] & 0xffff));
+        o[2 * i + 1] += ws * bf16_to_f32((uint16_t)(v[i] >> 16));
+      }
+    }
+  }
+  const float den = wave_sum(wgt) + (z2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z2 - M));
+  const float inv = __builtin_amdgcn_rcpf(den);
+  uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * H + h) * kC + 8 * l;
+  uint4 r;
+  r.x = (uint32_t)f32_to_bf16(o[0] * inv) | ((uint32_t)f32_to_bf16(o[1] * inv) << 16);
+  r.y = (uint32_t)f32_to_bf16(o[2] * inv) | ((uint32_t)f32_to_bf16(o[3] * inv) << 16);
+  r.z = (uint32_t)f32_to_bf16(o[4] * inv) | ((uint32_t)f32_to_bf16(o[5] * inv) << 16);
+  r.w = (uint32_t)f32_to_bf16(o[6] * inv) | ((uint32_t)f32_to_bf16(o[7] * inv) << 16);
+  *reinterpret_cast<uint4*>(out) = r;
+  if (a.lse && l == 0) a.lse[(size_t)qrow * H + h] = (M + log2f(den)) * kLn2;
+}
+
 hipError_t launch_attend_merge(const AttendArgs& a, int n_split, hipStream_t s) {
   if (n_split > kMaxSplit) return hipErrorInvalidValue;
+  if (!a.fold_mode && n_split <= kMergeSmall && a.H % 4 == 0) {
+    CSA_LAUNCH("attend_merge", attend_merge_small_kernel, dim3(a.B * a.Tq, a.H / 4), dim3(256), 0, s, a, n_split);
+    return hipGetLastError();
+  }
   CSA_LAUNCH("attend_merge", attend_merge_kernel, dim3(a.B * a.Tq, a.H), dim3(256), 0, s, a, n_split);
   return hipGetLastError();
 }
