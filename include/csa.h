@@ -299,6 +299,18 @@ typedef struct {
 csa_status csa_profile_enable(int on);
 int csa_profile_collect(csa_kernel_time* out, int max_entries);
 
+/* Test hook (diagnostics, not part of the method).  In a decode-shaped
+ * csa_index_topk / hybrid_layer_decode call, the scoring workgroups of a row
+ * wait (polling device memory) for the row's threshold bin, which the last of
+ * them publishes; a workgroup that does not see it within `polls` polls gives
+ * up, and the row's selection is then rebuilt from its scores by the resolve
+ * kernel (same result, slower).  Sets that budget for later calls (rounded
+ * down to a multiple of 4; a negative value restores the default of 40000,
+ * a few ms) and returns the previous one.  0 makes every waiting workgroup
+ * give up at once, so tests can check the fallback against the oracle.
+ * Process-wide; not synchronised with calls in flight on other threads. */
+int csa_test_set_fused_wait_polls(int polls);
+
 #ifdef __cplusplus
 }
 #endif

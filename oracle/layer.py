@@ -81,7 +81,7 @@ def decode_step(case, b, selected=None):
         new = _dec(g["new_" + name][b][None], d_kind)
         return np.concatenate([hist, new], axis=0)
 
-    folded_kv, folded_idx = [], []
+    folded_kv, folded_idx, folded_idx_raw = [], [], []
     if need > n_have:
         overlap = g["overlap"]
         s = {n: stream(n, kvk) for n in (("ca", "za", "cb", "zb") if overlap else ("ca", "za"))}
@@ -109,6 +109,7 @@ def decode_step(case, b, selected=None):
                 else:
                     ik = csa.compress_entry(si["ca"][a], si["za"][a], g["ibias_a"])
                 folded_idx.append(_store_key(ik, idk))
+                folded_idx_raw.append(ik)
     n_total = max(n_have, need)
     kv = CacheView(Stored(g["kv_cache"][b], kvk), n_have,
                    np.array(folded_kv) if folded_kv else None)
@@ -123,7 +124,9 @@ def decode_step(case, b, selected=None):
 
     q = _dec(g["q"][b], kvk)
     sink = None if g["sink"] is None else np.asarray(g["sink"], np.float64)
-    out = {"folded_kv": folded_kv, "folded_idx": folded_idx}
+    # (folded_idx_raw: the indexer keys before rounding to storage, for tests
+    # that must know which stored codes a rounding decision settles)
+    out = {"folded_kv": folded_kv, "folded_idx": folded_idx, "folded_idx_raw": folded_idx_raw}
     if g["kind"] == "csa":
         keys = CacheView(Stored(g["idx_cache"][b], idk,
                                 None if g["idx_scale"] is None else g["idx_scale"][b]),
@@ -145,9 +148,10 @@ def decode_step(case, b, selected=None):
 # prefill chunk
 # ---------------------------------------------------------------------------
 
-def prefill_entries(case, b):
+def prefill_entries(case, b, raw=False):
     """Compress a prefill chunk of sequence b into new cache entries (main KV
-    and, for CSA, indexer keys), rounded to their storage formats."""
+    and, for CSA, indexer keys), rounded to their storage formats.  With
+    raw=True the indexer keys before rounding are returned as a third value."""
     g = case
     m = g["m"]
     kvk, idk = g["kv_dtype"], g["idx_dtype"]
@@ -168,6 +172,8 @@ def prefill_entries(case, b):
             idx_new = csa.e4m3_quantize_rows(ik)[0]
         else:
             idx_new = csa.store_as(ik, idk)
+    if raw:
+        return kv_new, idx_new, (ik if g["kind"] == "csa" else None)
     return kv_new, idx_new
 
 

@@ -23,7 +23,7 @@ EXPORTS = [
     "csa_last_error", "csa_abi_version", "csa_compress", "csa_index_topk_workspace",
     "csa_index_topk", "csa_attend_workspace", "csa_attend", "hca_attend",
     "hybrid_layer_workspace", "hybrid_layer_decode", "hybrid_layer_prefill",
-    "csa_profile_enable", "csa_profile_collect",
+    "csa_profile_enable", "csa_profile_collect", "csa_test_set_fused_wait_polls",
 ]
 
 
@@ -92,6 +92,7 @@ def _declare(lib):
                                      C.POINTER(PrefillIO), P, SZ, P]),
         "csa_profile_enable": (I, [I]),
         "csa_profile_collect": (I, [C.POINTER(KernelTime), I]),
+        "csa_test_set_fused_wait_polls": (I, [I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -240,6 +241,12 @@ def hybrid_layer_decode(desc, state, io, ws, stream=None):
 def hybrid_layer_prefill(desc, state, io, ws, stream=None):
     check(lib().hybrid_layer_prefill(C.byref(desc), C.byref(state), C.byref(io), ptr(ws),
                                      ws.numel(), stream_handle(stream)))
+
+
+def set_fused_wait_polls(polls):
+    """Test hook: the fused top-k's poll budget (negative = default); returns
+    the previous value."""
+    return lib().csa_test_set_fused_wait_polls(int(polls))
 
 
 def profile_enable(on=True):

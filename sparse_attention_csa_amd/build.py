@@ -16,7 +16,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
 
-SOURCES = ["api.cpp", "profile.cpp", "compress.hip", "indexer.hip", "attend.hip", "attend_mfma.hip", "attend_rows.hip", "indexer_mfma.hip", "topk.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "compress.hip", "indexer.hip", "attend.hip", "attend_mfma.hip", "attend_rows.hip",
+           "indexer_mfma.hip", "topk.hip"]
 
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 

@@ -10,6 +10,7 @@
 
 #include "csa.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace {
 
@@ -72,11 +73,25 @@ csa_status check_idx_dims(int H_I, int d_I) {
 
 }  // namespace
 
+namespace csa {
+int set_error(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return status;
+}
+}  // namespace csa
+
 extern "C" {
 
 const char* csa_last_error(void) { return g_err.c_str(); }
 
 int csa_abi_version(void) { return 1; }
+
+int csa_test_set_fused_wait_polls(int polls) { return csa::set_fused_wait_polls(polls); }
 
 // ------------------------------------------------------------------ a1
 csa_status csa_compress(csa_dtype dtype, const void* content_a, const void* logits_a,
@@ -280,20 +295,33 @@ size_t hybrid_layer_workspace(const csa_layer_desc* d, int B, int T, int E_cap) 
   return bytes;
 }
 
-csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, const csa_decode_io* io,
-                               void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace csa {
+// every argument check of a decode step but the workspace's (nothing enqueued)
+csa_status decode_check(const csa_layer_desc* d, const csa_layer_state* s, const csa_decode_io* io) {
   csa_status st = check_desc(d);
   if (st != CSA_OK) return st;
   st = check_state(d, s);
   if (st != CSA_OK) return st;
   REQ_PTR(io);
   REQ_PTR(io->pos); REQ_PTR(io->q); REQ_PTR(io->x_new); REQ_PTR(io->streams); REQ_PTR(io->out);
-  const bool is_csa = d->kind == CSA_LAYER_CSA;
-  if (is_csa) {
+  if (d->kind == CSA_LAYER_CSA) {
     REQ_PTR(io->q_idx); REQ_PTR(io->w_idx); REQ_PTR(io->idx_streams);
     REQ_PTR(io->topk_idx); REQ_PTR(io->topk_cnt);
     REQUIRE(d->idx_dtype != CSA_E4M3 || io->q_scale != nullptr, CSA_ERR_ARG, "E4M3 indexer needs q_scale");
   }
+  return CSA_OK;
+}
+}  // namespace csa
+
+extern "C" {
+
+csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, const csa_decode_io* io,
+                               void* ws, size_t ws_bytes, void* stream) {
+  csa_status st = csa::decode_check(d, s, io);
+  if (st != CSA_OK) return st;
+  const bool is_csa = d->kind == CSA_LAYER_CSA;
   const int B = s->B;
   const size_t need = hybrid_layer_workspace(d, B, 1, s->E_cap);
   REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "workspace of %zu bytes required", need);

@@ -188,7 +188,7 @@ size_t attend_fold_ws_offset(int B, int Tq, int H, int c, int rows_max) {
 size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max) {
   size_t n = attend_fold_ws_offset(B, Tq, H, c, rows_max);
   if (attend_mfma_shape_ok(H, c))
-    n += ((size_t)B * H * 8 + 255) / 256 * 256 + ((size_t)B * 4 + 255) / 256 * 256 + ((size_t)B * c * 2 + 255) / 256 * 256;
+    n += ((size_t)B * H * 64 * 8 + 255) / 256 * 256 + ((size_t)B * 4 + 255) / 256 * 256 + ((size_t)B * c * 2 + 255) / 256 * 256;
   return n;
 }
 

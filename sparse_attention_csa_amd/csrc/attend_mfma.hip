@@ -35,11 +35,13 @@
 // [s cs, s cs + cs) of the entry that the block ending at the query position
 // completes: its sources, query slice and token slice arrive by DMA in the
 // ring slot not yet in use, the fold runs before the row loop (nothing of it
-// stays live across the loop), stores its slice of the entry, adds its share
-// of q_h . entry and q_h . token for every head to fold_s (device-scope
-// atomics) and appends its share of the token to the tail and window rings.
-// The merge kernel then adds the new entry and the query's own token as two
-// more rows, weights exp2(scale q . x - M), and publishes the entry count.
+// stays live across the loop), stores its slice of the entry, writes its
+// share of q_h . entry and q_h . token for every head to its own slot of
+// fold_s and appends its share of the token to the tail and window rings.
+// The merge kernel then sums the slices' shares in slice order (the same
+// order on every run: no atomics in the result path), adds the new entry and
+// the query's own token as two more rows, weights exp2(scale q . x - M), and
+// publishes the entry count.
 
 #include <type_traits>
 
@@ -59,6 +61,7 @@ constexpr int kRing = 4;               // LDS tile slots: two tiles in use (scor
 constexpr int kRowsPerWave = kTN / 4;  // DMA instructions per wave and tile
 constexpr int kFoldS = 16;             // fold slice: sources per thread (at most)
 constexpr int kFoldRowsLess = 64;      // rows a folding split gives up to the others
+constexpr int kFoldSlots = 64;         // fold slices at most (c / 8): one fold_s slot each
 
 }  // namespace
 
@@ -367,9 +370,9 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
           pn += __shfl_xor(pn, o, 64);
         }
         if (g < ng && g % fch == 0) {
-          float* fs = a.fold_s + 2 * ((size_t)b * H + g / fch);
-          atomicAdd(fs + 1, po);
-          if (fold_now) atomicAdd(fs, pn);
+          // this slice's own slot: (q . new entry, q . token) shares
+          float* fs = a.fold_s + 2 * (((size_t)b * H + g / fch) * kFoldSlots + split);
+          *reinterpret_cast<float2*>(fs) = float2{fold_now ? pn : 0.f, po};
         }
       }
     }
@@ -644,8 +647,15 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
   // two more rows, weights exp2(s_own - M) and exp2(s_new - M)
   const int b = qrow / a.Tq;
   const int frow = a.fold_mode ? a.fold_row[b] : 0;
+  // the fold slices' shares of q . new entry and q . token, lane = slice,
+  // summed in the same lane order on every run
   float2 fsv = float2{0.f, 0.f};
-  if (a.fold_mode) fsv = *reinterpret_cast<const float2*>(a.fold_s + 2 * ((size_t)b * H + h));
+  if (a.fold_mode) {
+    const int nf = (a.c + a.fold_cs - 1) / a.fold_cs;
+    if (l < nf) fsv = *reinterpret_cast<const float2*>(a.fold_s + 2 * (((size_t)b * H + h) * kFoldSlots + l));
+    fsv.x = wave_sum(fsv.x);
+    fsv.y = wave_sum(fsv.y);
+  }
   const float s_new = frow > 0 ? fsv.x * (a.scale * kLog2e) : -INFINITY;
   const float s_own = a.fold_mode ? fsv.y * (a.scale * kLog2e) : -INFINITY;
   // (fixed addresses: every load is issued at once)
@@ -699,10 +709,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
   }
   __syncthreads();
   if (w != 0) return;
-  if (a.fold_mode && l == 0) {
-    *reinterpret_cast<float2*>(a.fold_s + 2 * ((size_t)b * H + h)) = float2{0.f, 0.f};  // zero for the next call
-    if (h == 0 && frow > 0) a.fold.n_entries[b] = frow;  // publish the new entry count
-  }
+  if (a.fold_mode && l == 0 && h == 0 && frow > 0) a.fold.n_entries[b] = frow;  // publish the new entry count
   const float den = s_den;
   const float inv = __builtin_amdgcn_rcpf(den);
   const uint32_t nw[4] = {nrow.x, nrow.y, nrow.z, nrow.w}, xw[4] = {xrow.x, xrow.y, xrow.z, xrow.w};
@@ -747,12 +754,12 @@ bool attend_fuses_fold(AttendArgs& a, const FoldArgs& f) {
   while (cs * ns < a.c) cs *= 2;
   // LDS: the slice's sources fill at most one ring slot, its query slice
   // the P^T buffer
-  if (cs > 64 || f.m > kFoldS * (256 / cs) || f.m * cs * 8 > kTN * kRowB || a.H * cs * 2 > 4 * 64 * 16)
+  if (cs > 64 || a.c / cs > kFoldSlots || f.m > kFoldS * (256 / cs) || f.m * cs * 8 > kTN * kRowB || a.H * cs * 2 > 4 * 64 * 16)
     return false;
   const size_t off = attend_fold_ws_offset(a.B, a.Tq, a.H, a.c, a.E_cap + a.n_win);
   char* base = reinterpret_cast<char*>(a.ws);
   a.fold_s = reinterpret_cast<float*>(base + off);
-  const size_t off_row = off + ((size_t)a.B * a.H * 8 + 255) / 256 * 256;
+  const size_t off_row = off + ((size_t)a.B * a.H * kFoldSlots * 8 + 255) / 256 * 256;
   a.fold_row = reinterpret_cast<int32_t*>(base + off_row);
   a.fold_new = reinterpret_cast<uint16_t*>(base + off_row + ((size_t)a.B * 4 + 255) / 256 * 256);
   a.fold = f;

@@ -4,10 +4,12 @@
 // design 1" and "Key design 2" equations; "DeepSeek-V4" book ch. 5 "One weight
 // distribution per coordinate" and the start-of-sequence rule).
 //
-// Both kernels are HBM-streaming: a wavefront covers 64 consecutive
-// coordinates of one source row, so every load is a contiguous 128 B (bf16)
-// or 256 B (f32) segment; the per-coordinate softmax is an online max/sum
-// across source tokens, split over token groups and merged through LDS.
+// compress_chunk_kernel (a prefill chunk, csa_compress): one workgroup per
+// entry, a thread per coordinate walks the entry's sources with an online
+// max / sum (consecutive threads read consecutive coordinates of a source
+// row).  fold_append_kernel (a decode step): source tokens split over thread
+// groups, the groups' online states merged by lane shuffles and through LDS
+// (fold.h).
 
 #include "common.h"
 #include "fold.h"

@@ -239,7 +239,7 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t s, const FoldArgs*
     e = launch_index_score_mfma(a, tw, 1, 1, &n_wg_fused, fold, s);
   } else if (index_prefill_mfma_supported(a)) {
     dim3 g1((a.E_cap + kPfChunk - 1) / kPfChunk, rows / 4), blk(256);
-    CSA_LAUNCH("index_score", index_score_prefill_kernel, g1, blk, 0, s, a);
+    CSA_LAUNCH("index_score_prefill", index_score_prefill_kernel, g1, blk, 0, s, a);
     e = hipGetLastError();
   } else {
     dim3 g1((a.E_cap + 255) / 256, rows), blk(256);

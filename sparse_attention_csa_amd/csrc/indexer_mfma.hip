@@ -51,6 +51,7 @@
 // workgroup of the row has read the old count by then).  The scan
 // workgroups cover the entries before the new one.
 
+#include <atomic>
 #include <type_traits>
 
 #include "common.h"
@@ -71,7 +72,6 @@ CSA_DEV float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); 
 namespace {
 
 constexpr int kD = 128;
-constexpr int kFuseWaitTries = 40000;  // polls of the published threshold bin (a few ms)
 
 // Tile geometry.  e4m3: 16 keys x 128 B = 2 KB, read as two 1 KB pieces of
 // 8 keys; bf16: 16 keys x 256 B = 4 KB, four pieces of 4 keys.  In LDS, chunk
@@ -96,9 +96,11 @@ struct Geo {
 }  // namespace
 
 // grid (n_wg, rows), 256 threads
+// wait_polls: how many times a waiting workgroup polls for its row's
+// published threshold bin before it gives up (a multiple of 4)
 template <int FP8, int HT>
 __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, TopkWs ws, int use_hist, int fuse,
-                                                                FoldArgs f, int fold_mode) {
+                                                                FoldArgs f, int fold_mode, int wait_polls) {
   typedef Geo<FP8> G;
   constexpr int kU = G::kU;
   __shared__ __attribute__((aligned(1024))) char s_tr[4][kU * G::kTileB];  // per-wave transpose buffer
@@ -465,7 +467,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
       // is seen about one round trip after it lands, not one round trip
       // plus a poll period
       int v = 0;
-      for (int it = 0; it < kFuseWaitTries / 4 && v == 0; ++it) {
+      for (int it = 0; it < wait_polls / 4 && v == 0; ++it) {
         const int v0 = __hip_atomic_load(slot + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_s_sleep(2);
         const int v1 = __hip_atomic_load(slot + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -567,11 +569,18 @@ static ScorerPlan scorer_plan(const IndexArgs& a, int resident, int use_hist, in
   return ScorerPlan{per_row, fuse, (int)(4 * per * 16)};
 }
 
+// per device: the grid of the scan is sized to the device's resident count
 template <int FP8, int HT>
 static int scorer_resident() {
-  static int resident = 0;
-  if (!resident) resident = resident_wgs(index_score_mfma_kernel<FP8, HT>);
-  return resident;
+  static std::atomic<int> resident[kMaxDevices];
+  const int dev = current_device();
+  if (dev < 0) return resident_wgs(index_score_mfma_kernel<FP8, HT>);
+  int r = resident[dev].load(std::memory_order_relaxed);
+  if (!r) {
+    r = resident_wgs(index_score_mfma_kernel<FP8, HT>);
+    resident[dev].store(r, std::memory_order_relaxed);
+  }
+  return r;
 }
 
 template <int FP8, int HT>
@@ -586,7 +595,7 @@ static hipError_t launch_scorer(const IndexArgs& a, TopkWs& ws, int use_hist, in
   FoldArgs f = fold ? *fold : FoldArgs{};
   dim3 grid(p.per_row, a.B * a.Tq), block(256);
   CSA_LAUNCH("index_score_mfma", (index_score_mfma_kernel<FP8, HT>), grid, block, 0, s, a, ws, use_hist, p.fuse,
-             f, with_fold);
+             f, with_fold, fused_wait_polls());
   return hipGetLastError();
 }
 

@@ -5,7 +5,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "csa.h"
+
 namespace csa {
+
+// sets the thread-local message csa_last_error() returns (api.cpp)
+int set_error(int status, const char* fmt, ...);
+// argument checks of a decode step, all but the workspace (api.cpp)
+csa_status decode_check(const csa_layer_desc* d, const csa_layer_state* s, const csa_decode_io* io);
 
 // kernel timing hook (profile.cpp): records events around a launch when enabled
 class ProfScope {
@@ -26,6 +33,17 @@ class ProfScope {
   } while (0)
 
 enum Dt { F32 = 0, BF16 = 1, E4M3 = 2 };
+
+// Host-side values that depend on the device (occupancy, LDS attributes set
+// on a kernel) are cached per device id, below this bound.
+constexpr int kMaxDevices = 64;
+// the current device id, or -1 if it cannot be determined (out of range
+// too): callers then compute the value without caching it
+inline int current_device() {
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= kMaxDevices) return -1;
+  return d;
+}
 
 // ------------------------------------------------------------ compressor
 struct CompressArgs {
@@ -136,13 +154,14 @@ struct AttendArgs {
   void* ws;
   size_t ws_bytes;
   // dense decode with the step's fold inside (see attend_fuses_fold): each
-  // split folds fold_cs coordinates of the new entry and adds its share of
-  // q . entry and q . token to fold_s; the merge adds the new entry and the
-  // query's own token as two more rows
+  // split folds fold_cs coordinates of the new entry and writes its share of
+  // q . entry and q . token to its slot of fold_s; the merge sums the slots
+  // in slice order and adds the new entry and the query's own token as two
+  // more rows
   int fold_mode;
   int fold_cs;
   FoldArgs fold;
-  float* fold_s;       // [B][H][2]: q . new entry, q . own token; zero between calls
+  float* fold_s;       // [B][H][64 slices][2]: shares of q . new entry, q . own token
   int32_t* fold_row;   // [B]: new entry index + 1, or 0
   uint16_t* fold_new;  // [B][c]: the new entry (bf16), read by the merge
   int fold_nsplit;     // set by the launch: splits that fold (fewer rows each) ...

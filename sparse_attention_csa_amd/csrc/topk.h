@@ -110,6 +110,12 @@ CSA_DEV void find_bin(const int* hist, int k, int* s_w, int* s_out, int* b1, int
   find_bin_counts<NT>(c, k, s_w, s_out, b1, above);
 }
 
+// Polls a fused scoring workgroup makes for its row's published threshold
+// bin before it gives up and leaves the row to the resolve's fallback (a few
+// ms at the default).  Settable from the host for tests of that fallback.
+int fused_wait_polls();
+int set_fused_wait_polls(int polls);
+
 size_t topk_ws_bytes(int rows, int E_cap, bool split);
 TopkWs topk_ws_carve(void* base, int rows, int E_cap, bool split);
 hipError_t launch_topk_collect(const IndexArgs& a, const TopkWs& ws, int slices, int slice_len,

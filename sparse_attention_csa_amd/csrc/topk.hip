@@ -11,18 +11,21 @@
 //     (there are fewer than k of them); entries in bin b1 are candidates.
 //  2. exact: the (k - #certain) largest candidates are found by radix select
 //     on the remaining 21 key bits and, among equal keys, on the entry id.
-//     Certain winners and selected candidates (exactly k ids) are sorted
-//     ascending by a bitonic sort in LDS and written out.
 // If bin b1 holds more candidates than fit in LDS, the threshold is refined
 // over the whole row instead and the winners are emitted by one in-order
-// scan of the row (no sort needed).
+// scan of the row.
 //
-// Split mode (few long rows, decode): the histogram is accumulated by the
-// scoring kernel; many workgroups scan slices of a row and append certain
-// winners and candidates to two per-row lists (one atomic reservation per
-// list and workgroup); then one workgroup per row resolves.  No workgroup
-// waits on another.  Row mode (many rows, prefill): one workgroup per row
-// does everything from the row's scores.
+// Fused mode (decode, few long rows): the scoring kernel accumulates the
+// histogram, publishes b1 per row and leaves each workgroup's certain winners
+// and candidates in entry order in its own list region; one workgroup per row
+// (topk_fused_resolve_kernel) selects among the candidates keeping their
+// order and places every id at its rank in its own list plus its rank in the
+// other: a merge of two sorted lists, no sort.  Split mode (the same rows when
+// the scorer cannot fuse): collect workgroups append both lists per row, and
+// the resolve sorts the winners by id buckets.  Row mode (many rows, prefill):
+// one workgroup per row does everything from the row's scores.
+
+#include <atomic>
 
 #include "common.h"
 #include "kernels.h"
@@ -650,6 +653,18 @@ __global__ __launch_bounds__(kRT) void topk_rowsel_kernel(IndexArgs a, TopkWs ws
   }
 }
 
+namespace {
+constexpr int kDefaultWaitPolls = 40000;
+std::atomic<int> g_wait_polls{kDefaultWaitPolls};
+}  // namespace
+
+int fused_wait_polls() { return g_wait_polls.load(std::memory_order_relaxed); }
+
+int set_fused_wait_polls(int polls) {
+  if (polls < 0) polls = kDefaultWaitPolls;
+  return g_wait_polls.exchange(polls & ~3, std::memory_order_relaxed);
+}
+
 size_t topk_ws_bytes(int rows, int E_cap, bool split) {
   size_t per = kTopkBins * 4 + 16;
   if (split)
@@ -684,12 +699,14 @@ TopkWs topk_ws_carve(void* base, int rows, int E_cap, bool split) {
   return w;
 }
 
+// raises the kernel's dynamic LDS limit once per device (done[device])
 template <typename K>
-static hipError_t allow_lds(K kernel, size_t bytes, size_t* done) {
-  if (*done >= bytes) return hipSuccess;
+static hipError_t allow_lds(K kernel, size_t bytes, std::atomic<size_t>* done) {
+  const int dev = current_device();
+  if (dev >= 0 && done[dev].load(std::memory_order_relaxed) >= bytes) return hipSuccess;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e == hipSuccess) *done = bytes;
+  if (e == hipSuccess && dev >= 0) done[dev].store(bytes, std::memory_order_relaxed);
   return e;
 }
 
@@ -699,24 +716,24 @@ hipError_t launch_topk_collect(const IndexArgs& a, const TopkWs& ws, int slices,
              slice_len);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  static size_t lds_set = 0;
-  e = allow_lds(topk_resolve_kernel, sizeof(Lds), &lds_set);
+  static std::atomic<size_t> lds_set[kMaxDevices];
+  e = allow_lds(topk_resolve_kernel, sizeof(Lds), lds_set);
   if (e != hipSuccess) return e;
   CSA_LAUNCH("topk_resolve", topk_resolve_kernel, dim3(a.B * a.Tq), dim3(kRT), sizeof(Lds), s, a, ws);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_fused_resolve(const IndexArgs& a, const TopkWs& ws, int n_wg, hipStream_t s) {
-  static size_t lds_set = 0;
-  hipError_t e = allow_lds(topk_fused_resolve_kernel, sizeof(Lds), &lds_set);
+  static std::atomic<size_t> lds_set[kMaxDevices];
+  hipError_t e = allow_lds(topk_fused_resolve_kernel, sizeof(Lds), lds_set);
   if (e != hipSuccess) return e;
   CSA_LAUNCH("topk_resolve", topk_fused_resolve_kernel, dim3(a.B * a.Tq), dim3(kRT), sizeof(Lds), s, a, ws, n_wg);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_rows(const IndexArgs& a, const TopkWs& ws, hipStream_t s) {
-  static size_t lds_set = 0;
-  hipError_t e = allow_lds(topk_rowsel_kernel, sizeof(Lds), &lds_set);
+  static std::atomic<size_t> lds_set[kMaxDevices];
+  hipError_t e = allow_lds(topk_rowsel_kernel, sizeof(Lds), lds_set);
   if (e != hipSuccess) return e;
   CSA_LAUNCH("topk_rows", topk_rowsel_kernel, dim3(a.B * a.Tq), dim3(kRT), sizeof(Lds), s, a, ws);
   return hipGetLastError();

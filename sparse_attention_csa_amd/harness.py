@@ -125,14 +125,6 @@ class DecodeSession:
                 for j in range(src.shape[1]):
                     tail[b, si, int(tail0[b] + j) % st.R] = src[b, j]
         st.tail.copy_(tail)
-        io = {}
-        io["pos"] = dev(pos, "i64", device)
-        io["q"] = dev(g["q"], kvk, device)
-        io["x_new"] = dev(g["x_new"], kvk, device)
-        io["streams"] = torch.stack([dev(g["new_" + s], kvk, device) for s in streams], dim=1)
-        H = g["H"]
-        io["out"] = torch.empty((B, H, c), dtype=_KV[kvk], device=device)
-        io["lse"] = torch.empty((B, H), dtype=torch.float32, device=device)
         if g["kind"] == "csa":
             idk = g["idx_dtype"]
             st.idx_cache.copy_(dev(g["idx_cache"], idk, device))
@@ -145,28 +137,43 @@ class DecodeSession:
                     for j in range(src.shape[1]):
                         itail[b, si, int(tail0[b] + j) % st.R] = src[b, j]
             st.idx_tail.copy_(itail)
-            io["idx_streams"] = torch.stack(
-                [dev(g["new_" + s], kvk, device) for s in ("ica", "iza", "icb", "izb")], dim=1)
-            io["q_idx"] = dev(g["q_idx"], idk, device)
-            io["q_scale"] = dev(g["q_scale"], "f32", device) if idk == "e4m3" else None
-            io["w_idx"] = dev(g["w_idx"], "f32", device)
-            io["topk_idx"] = torch.empty((B, g["k"]), dtype=torch.int32, device=device)
-            io["topk_cnt"] = torch.empty((B,), dtype=torch.int32, device=device)
-        self.io = io
+        self.io, self._io_struct = decode_io(g, device)
         self.ws = torch.zeros(max(256, L.hybrid_layer_workspace(self.desc, B, 1, E_cap)),
                               dtype=torch.uint8, device=device)
-        self._io_struct = self._make_io()
         self._state_struct = st.struct()
-
-    def _make_io(self):
-        s = L.DecodeIO()
-        for name in ("pos", "q", "q_idx", "q_scale", "w_idx", "x_new", "streams", "idx_streams",
-                     "out", "lse", "topk_idx", "topk_cnt"):
-            setattr(s, name, L.ptr(self.io.get(name)))
-        return s
 
     def run(self, stream=None):
         L.hybrid_layer_decode(self.desc, self._state_struct, self._io_struct, self.ws, stream)
+
+
+def decode_io(g, device="cuda"):
+    """The per-step inputs and outputs of a decode step (one token per
+    sequence) of workload ``g``: a dict of device tensors and the DecodeIO
+    structure pointing at them."""
+    B, c, H = g["B"], g["c"], g["H"]
+    kvk = g["kv_dtype"]
+    streams = ("ca", "za", "cb", "zb") if g["overlap"] else ("ca", "za")
+    io = {}
+    io["pos"] = dev(np.asarray(g["pos"], np.int64), "i64", device)
+    io["q"] = dev(g["q"], kvk, device)
+    io["x_new"] = dev(g["x_new"], kvk, device)
+    io["streams"] = torch.stack([dev(g["new_" + s], kvk, device) for s in streams], dim=1)
+    io["out"] = torch.empty((B, H, c), dtype=_KV[kvk], device=device)
+    io["lse"] = torch.empty((B, H), dtype=torch.float32, device=device)
+    if g["kind"] == "csa":
+        idk = g["idx_dtype"]
+        io["idx_streams"] = torch.stack(
+            [dev(g["new_" + s], kvk, device) for s in ("ica", "iza", "icb", "izb")], dim=1)
+        io["q_idx"] = dev(g["q_idx"], idk, device)
+        io["q_scale"] = dev(g["q_scale"], "f32", device) if idk == "e4m3" else None
+        io["w_idx"] = dev(g["w_idx"], "f32", device)
+        io["topk_idx"] = torch.empty((B, g["k"]), dtype=torch.int32, device=device)
+        io["topk_cnt"] = torch.empty((B,), dtype=torch.int32, device=device)
+    s = L.DecodeIO()
+    for name in ("pos", "q", "q_idx", "q_scale", "w_idx", "x_new", "streams", "idx_streams",
+                 "out", "lse", "topk_idx", "topk_cnt"):
+        setattr(s, name, L.ptr(io.get(name)))
+    return io, s
 
 
 class PrefillSession:
@@ -204,7 +211,9 @@ class PrefillSession:
             io["idx_streams"] = torch.stack([dev(g[s], kvk, device) for s in ("ica", "iza", "icb", "izb")],
                                             dim=1)
             io["q_idx"] = dev(g["q_idx"], idk, device)
-            io["q_scale"] = None
+            io["q_scale"] = dev(g["q_scale"], "f32", device) if idk == "e4m3" else None
+            if idk == "e4m3":
+                st.idx_scale.copy_(dev(g["idx_scale"], "f32", device))
             io["w_idx"] = dev(g["w_idx"], "f32", device)
             io["topk_idx"] = torch.empty((B, T, g["k"]), dtype=torch.int32, device=device)
             io["topk_cnt"] = torch.empty((B, T), dtype=torch.int32, device=device)
@@ -219,6 +228,20 @@ class PrefillSession:
             setattr(s, name, L.ptr(io.get(name)))
         self._io_struct = s
         self._state_struct = st.struct()
+        self.dec_ws = None
 
     def run(self, stream=None):
         L.hybrid_layer_prefill(self.desc, self._state_struct, self._io_struct, self.ws, stream)
+
+    def decode(self, g_step, stream=None):
+        """Continue the same layer state with one decode step whose per-token
+        inputs are those of decode workload ``g_step`` (its cache and state
+        fields are not used: the state is the one this session holds).
+        Returns the step's io tensors."""
+        if self.dec_ws is None:
+            self.dec_ws = torch.zeros(
+                max(256, L.hybrid_layer_workspace(self.desc, self.g["B"], 1, self.g["E_cap"])),
+                dtype=torch.uint8, device=self.state.kv_cache.device)
+        io, s = decode_io(g_step, self.state.kv_cache.device)
+        L.hybrid_layer_decode(self.desc, self._state_struct, s, self.dec_ws, stream)
+        return io

@@ -7,6 +7,7 @@ recommends in ch. 13).
 """
 
 import numpy as np
+import torch
 
 from oracle.formats import f64_to_bf16_bits
 
@@ -17,26 +18,42 @@ def _bits(x, kind):
     return np.asarray(x, dtype=np.float32)
 
 
+def e4m3_codes_of(rows):
+    """(codes, scales) of float64 rows that are e4m3 values times one float32
+    scale per row with max |row| = 448 * scale (as the oracle's e4m3
+    quantiser leaves them); an all-zero row has scale 1.  Pure re-encoding:
+    every value divided by its scale is an e4m3 value, so torch's cast is
+    exact here."""
+    rows = np.asarray(rows, np.float64)
+    amax = np.abs(rows).max(axis=-1)
+    scale = np.where(amax > 0, amax / 448.0, 1.0).astype(np.float32)
+    y = rows / scale.astype(np.float64)[..., None]
+    codes = torch.from_numpy(y.astype(np.float32)).to(torch.float8_e4m3fn)
+    back = codes.to(torch.float32).numpy().astype(np.float64)
+    assert np.array_equal(back, y), "row is not an e4m3 row times its scale"
+    return codes.view(torch.uint8).numpy(), scale
+
+
 def prefix_case(pre, T):
     """The same prefill workload cut to its first T chunk tokens."""
     g = dict(pre)
     g["T"] = T
-    for n in ("ca", "za", "cb", "zb", "ica", "iza", "icb", "izb", "q", "q_idx", "w_idx"):
+    for n in ("ca", "za", "cb", "zb", "ica", "iza", "icb", "izb", "q", "q_idx", "w_idx", "q_scale"):
         if n in g and g[n] is not None:
             g[n] = g[n][:, :T]
     g["win"] = pre["win"][:, :pre["n_win"] - 1 + T]
     return g
 
 
-def decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv=(), extra_idx=()):
-    """Decode inputs for the token at position t, after a prefill of the first
-    T_done chunk tokens produced entries ``kv_new`` / ``idx_new`` (float64,
-    rounded to storage) and later decode steps produced ``extra_*`` entries.
-    Only batch row 0 is used."""
+def decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv=(), extra_idx=(), b=0):
+    """Decode inputs for sequence b's token at position t, after a prefill of
+    the first T_done chunk tokens produced entries ``kv_new`` / ``idx_new``
+    (float64, rounded to storage) and later decode steps produced ``extra_*``
+    entries.  The result is a one-sequence decode workload."""
     m, c, n_win = pre["m"], pre["c"], pre["n_win"]
     pos0 = int(pre["pos0"])
     kvk = pre["kv_dtype"]
-    n_old = int(pre["n_entries"][0])
+    n_old = int(pre["n_entries"][b])
     kv_rows = list(kv_new) + list(extra_kv)
     n_have = n_old + len(kv_rows)
     E_cap = max(pre["E_cap"], n_have + 1)
@@ -46,7 +63,7 @@ def decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv=(), extra_idx=
     g["pos"] = np.array([t], dtype=np.int64)
     g["n_entries"] = np.array([n_have], dtype=np.int32)
     kv = np.zeros((1, E_cap, c), dtype=pre["kv_cache"].dtype)
-    kv[0, :n_old] = pre["kv_cache"][0, :n_old]
+    kv[0, :n_old] = pre["kv_cache"][b, :n_old]
     if kv_rows:
         kv[0, n_old:n_have] = _bits(np.array(kv_rows), kvk)
     g["kv_cache"] = kv
@@ -54,28 +71,35 @@ def decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv=(), extra_idx=
     g["tail_pos0"] = np.array([t - tail_len], dtype=np.int64)
     lo, hi = t - tail_len - pos0, t - pos0
     assert lo >= 0, "tail reaches before the chunk"
+    sl = slice(b, b + 1)
     streams = ("ca", "za", "cb", "zb") if pre["overlap"] else ("ca", "za")
     for s in streams:
-        g["tail_" + s] = pre[s][:, lo:hi]
-        g["new_" + s] = pre[s][:, hi]
+        g["tail_" + s] = pre[s][sl, lo:hi]
+        g["new_" + s] = pre[s][sl, hi]
     w0 = t - (n_win - 1) - (pos0 - (n_win - 1))
-    g["win_hist"] = pre["win"][:, w0:w0 + n_win - 1]
-    g["x_new"] = pre["win"][:, w0 + n_win - 1]
-    g["q"] = pre["q"][:, hi]
+    g["win_hist"] = pre["win"][sl, w0:w0 + n_win - 1]
+    g["x_new"] = pre["win"][sl, w0 + n_win - 1]
+    g["q"] = pre["q"][sl, hi]
     if pre["kind"] == "csa":
         d_I = pre["d_I"]
         g.update(H_I=pre["H_I"], d_I=d_I, ibias_a=pre["ibias_a"], ibias_b=pre["ibias_b"])
         ik = np.zeros((1, E_cap, d_I), dtype=pre["idx_cache"].dtype)
-        ik[0, :n_old] = pre["idx_cache"][0, :n_old]
+        ik[0, :n_old] = pre["idx_cache"][b, :n_old]
         idx_rows = list(idx_new) + list(extra_idx)
-        if idx_rows:
+        g["idx_scale"] = None
+        if pre["idx_dtype"] == "e4m3":
+            sc = np.ones((1, E_cap), np.float32)
+            sc[0, :n_old] = pre["idx_scale"][b, :n_old]
+            if idx_rows:
+                ik[0, n_old:n_have], sc[0, n_old:n_have] = e4m3_codes_of(np.array(idx_rows))
+            g["idx_scale"] = sc
+        elif idx_rows:
             ik[0, n_old:n_have] = _bits(np.array(idx_rows), pre["idx_dtype"])
         g["idx_cache"] = ik
-        g["idx_scale"] = None
         for s in ("ca", "za", "cb", "zb"):
-            g["tail_i" + s] = pre["i" + s][:, lo:hi]
-            g["new_i" + s] = pre["i" + s][:, hi]
-        g["q_idx"] = pre["q_idx"][:, hi]
-        g["q_scale"] = None
-        g["w_idx"] = pre["w_idx"][:, hi]
+            g["tail_i" + s] = pre["i" + s][sl, lo:hi]
+            g["new_i" + s] = pre["i" + s][sl, hi]
+        g["q_idx"] = pre["q_idx"][sl, hi]
+        g["q_scale"] = None if pre.get("q_scale") is None else pre["q_scale"][sl, hi]
+        g["w_idx"] = pre["w_idx"][sl, hi]
     return g

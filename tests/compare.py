@@ -2,8 +2,13 @@
 
 * Top-k sets are bit-exact, except that an id in the symmetric difference is
   allowed when its oracle (float64) score lies within 1e-6 relative of the
-  oracle's k-th score tau (the float32 score-gap rule).  Such swaps are
-  counted and reported.
+  oracle's k-th score tau (the float32 score-gap rule), or within the float32
+  evaluation error bound of the two scores when that is larger (signed head
+  weights make the score a sum with cancellation: score_error_bound).  Such
+  swaps are counted and reported.
+* Layer-produced e4m3 keys: a stored code may be either neighbour when the
+  value sits within float32 accuracy of a rounding boundary; selections are
+  accepted when some such rounding makes them a top-k (topk_check_bounds).
 * Floating outputs: per row, max|gpu - ref| / max(max|ref|, 1e-3 * median
   row max) <= tol, with tol = 1e-4 for float32 paths and 2e-2 for bfloat16.
   The worst row, the global max-abs error and the lse error are reported.
@@ -14,8 +19,27 @@ import numpy as np
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 
 
-def topk_check(gpu_ids, gpu_cnt, oracle_sel, scores, k, rel_gap=1e-6):
-    """Returns (ok, n_swaps, message)."""
+def score_error_bound(q, w, K):
+    """Worst-case |float32 score - exact score| of every row of K: the score
+    is a sum over d_I exact products per head (one float32 sum each), a
+    product by the head weight (and scales), a sum over H_I heads and a
+    product by the key scale, so a float32 evaluation in any order is within
+    (d_I + H_I + 3) u M_s of the exact score (the standard bound for
+    floating-point sums), u = 2**-24, M_s the same score of |q|, |w| and |K|
+    (no cancellation)."""
+    from oracle.csa import index_scores
+    q = np.abs(np.asarray(q, np.float64))
+    H_I, d_I = q.shape
+    M = index_scores(q, np.abs(np.asarray(w, np.float64)), np.abs(np.asarray(K, np.float64)))
+    return (d_I + H_I + 3) * 2.0 ** -24 * M
+
+
+def topk_check(gpu_ids, gpu_cnt, oracle_sel, scores, k, rel_gap=1e-6, err=None):
+    """Returns (ok, n_swaps, message).  ``err`` (optional): an array of
+    per-entry float32 evaluation error bounds (score_error_bound), or a
+    function returning it, evaluated only when the sets differ; an id in
+    the symmetric difference is then also allowed when its score lies within
+    its bound plus the k-th entry's bound of tau."""
     gpu = np.asarray(gpu_ids)[:int(gpu_cnt)]
     if np.any(np.diff(gpu) <= 0):
         return False, 0, "gpu ids not strictly ascending"
@@ -26,11 +50,135 @@ def topk_check(gpu_ids, gpu_cnt, oracle_sel, scores, k, rel_gap=1e-6):
     diff = np.setxor1d(gpu, oracle_sel)
     if diff.size and (diff.min() < 0 or diff.max() >= len(scores)):
         return False, 0, "gpu id outside the visible range"
-    tau = np.sort(scores)[::-1][min(k, len(scores)) - 1]
-    bad = [int(s) for s in diff if abs(scores[s] - tau) > rel_gap * abs(tau)]
+    order = np.lexsort((np.arange(len(scores)), -np.asarray(scores)))
+    kth = order[min(k, len(scores)) - 1]
+    tau = scores[kth]
+    tol = np.full(len(diff), rel_gap * abs(tau))
+    e = None
+    if err is not None:
+        e = np.asarray(err() if callable(err) else err, np.float64)
+        tol = np.maximum(tol, e[diff] + e[kth])
+    bad = [int(s) for s, t in zip(diff, tol) if abs(scores[s] - tau) > t]
     if bad:
-        return False, len(diff), f"ids {bad[:8]} differ with score gaps beyond {rel_gap} (tau={tau})"
+        extra = "" if e is None else f", fp32 error bound at tau {e[kth]:.3g}"
+        return False, len(diff), f"ids {bad[:8]} differ with score gaps beyond {rel_gap}{extra} (tau={tau})"
     return True, len(diff) // 2, ""
+
+
+# relative accuracy of a float32 fold's value (softmax of a few logits,
+# hardware exp, accumulation, the division by the scale)
+FOLD_REL = 4e-6
+
+
+def e4m3_alternatives(raw_row, rel=FOLD_REL, max_amb=6):
+    """Every value row (codes times scale, float64) that rounding ``raw_row``
+    to e4m3 with one scale per row may give when the value is computed in
+    float32: the oracle's rounding, plus the other neighbouring code for each
+    coordinate whose value / scale lies within ``rel`` of a rounding boundary
+    (both roundings are then correct within the float32 computation).  At
+    most 2**max_amb rows."""
+    from oracle.csa import e4m3_quantize_rows
+    x = np.asarray(raw_row, np.float64)
+    base, scale = e4m3_quantize_rows(x[None])
+    base, sc = base[0], float(scale[0])
+    y = np.abs(x) / sc
+    _, e = np.frexp(np.where(y > 0, y, 1.0))
+    sp = np.ldexp(1.0, np.maximum(e - 4, -9))
+    frac = y / sp - np.floor(y / sp)
+    amb = np.where((np.abs(frac - 0.5) * sp <= rel * np.maximum(y, 1e-30)) & (y < 448.0))[0]
+    assert len(amb) <= max_amb, f"{len(amb)} ambiguous codes in one key"
+    rows = [base]
+    for i in amb:
+        lo, hi = np.floor(y[i] / sp[i]) * sp[i], np.ceil(y[i] / sp[i]) * sp[i]
+        other = hi if abs(base[i]) / sc == lo else lo
+        alt = []
+        for r in rows:
+            r2 = r.copy()
+            r2[i] = np.copysign(other * sc, x[i])
+            alt.append(r2)
+        rows += alt
+    return rows
+
+
+def ambiguous_e4m3_keys(raw_rows, ids, rel=FOLD_REL):
+    """{id: alternative value rows} for the layer-produced e4m3 keys (given
+    before rounding) whose stored codes are not settled by float32 accuracy;
+    keys with a single valid rounding are left out."""
+    out = {}
+    for s, raw in zip(ids, raw_rows):
+        alts = e4m3_alternatives(raw, rel)
+        if len(alts) > 1:
+            out[int(s)] = alts
+    return out
+
+
+def score_bounds(q, w, amb):
+    """{id: (lo, hi)} index scores of each ambiguous key's alternatives, for
+    one query (q [H_I][d_I], w [H_I], as the oracle scores them)."""
+    from oracle.csa import index_scores
+    out = {}
+    for s, alts in amb.items():
+        sc = index_scores(q, w, np.array(alts))
+        out[s] = (float(sc.min()), float(sc.max()))
+    return out
+
+
+def topk_check_bounds(gpu_ids, gpu_cnt, oracle_sel, scores, k, bounds, rel_gap=1e-6, err=None):
+    """topk_check for selections over keys some of whose scores are only
+    known within bounds ({id: (lo, hi)}, see score_bounds): the GPU set S
+    is accepted when some scores within the bounds make it a top-k, i.e.
+    min over S of the upper bounds >= max over the rest of the lower bounds,
+    up to the float32 score-gap rule.  Returns (ok, n_swaps, message)."""
+    ok, swaps, msg = topk_check(gpu_ids, gpu_cnt, oracle_sel, scores, k, rel_gap, err)
+    if ok or not bounds:
+        return ok, swaps, msg
+    gpu = np.asarray(gpu_ids)[:int(gpu_cnt)]
+    if len(gpu) != len(oracle_sel) or np.any(np.diff(gpu) <= 0) or gpu.min() < 0 or gpu.max() >= len(scores):
+        return ok, swaps, msg
+    lo = np.array(scores, np.float64)
+    hi = lo.copy()
+    for s, (a, b) in bounds.items():
+        if s < len(lo):
+            lo[s], hi[s] = a, b
+    inside = np.zeros(len(lo), bool)
+    inside[gpu] = True
+    tau = np.sort(scores)[::-1][min(k, len(scores)) - 1]
+    if inside.all() or hi[inside].min() >= lo[~inside].max() - rel_gap * abs(tau):
+        return True, len(np.setxor1d(gpu, oracle_sel)) // 2, ""
+    return False, 0, msg + " (also beyond the e4m3 rounding bounds)"
+
+
+def decode_err(g, b, ref):
+    """score_error_bound of the entries visible to sequence b of decode
+    workload g (the cache rows, then the key the step folded), as a
+    function for topk_check's lazy ``err``."""
+    def f():
+        from oracle.formats import Stored
+        from oracle.layer import CacheView
+        idk = g["idx_dtype"]
+        sc = g.get("idx_scale")
+        keys = CacheView(Stored(g["idx_cache"][b], idk, None if sc is None else sc[b]), int(g["n_entries"][b]),
+                         np.array(ref["folded_idx"]) if ref["folded_idx"] else None)
+        qs = g.get("q_scale")
+        q = Stored(g["q_idx"][b], idk, None if qs is None else qs[b]).all()
+        return score_error_bound(q, g["w_idx"][b], keys.rows(slice(0, len(ref["scores"]))))
+    return f
+
+
+def prefill_err(g, b, i, idx_new, n_vis):
+    """score_error_bound for chunk query i of sequence b of prefill workload
+    g over its n_vis visible entries (cache rows, then the chunk's keys)."""
+    def f():
+        from oracle.formats import Stored
+        from oracle.layer import CacheView
+        idk = g["idx_dtype"]
+        sc = g.get("idx_scale")
+        keys = CacheView(Stored(g["idx_cache"][b], idk, None if sc is None else sc[b]), int(g["n_entries"][b]),
+                         idx_new)
+        qs = g.get("q_scale")
+        q = Stored(g["q_idx"][b][i], idk, None if qs is None else qs[b][i]).all()
+        return score_error_bound(q, g["w_idx"][b][i], keys.rows(slice(0, n_vis)))
+    return f
 
 
 def rel_err_rows(gpu, ref):

@@ -12,7 +12,8 @@ import torch
 import workloads
 from oracle import layer as OL
 from oracle.formats import Stored
-from tests.compare import assert_close, topk_check
+from tests.compare import (ambiguous_e4m3_keys, assert_close, decode_err, prefill_err, score_bounds,
+                           score_error_bound, topk_check, topk_check_bounds)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,7 +42,14 @@ def _check_decode(g, sess, label):
                 _check_folded_key(g, sess, b, e0, ref["folded_idx"][0], label)
             ids = sess.io["topk_idx"][b].cpu().numpy()
             cnt = int(sess.io["topk_cnt"][b].item())
-            ok, swaps, msg = topk_check(ids, cnt, ref["sel"], ref["scores"], g["k"])
+            bd = {}
+            if g["idx_dtype"] == "e4m3" and ref["folded_idx_raw"]:
+                amb = ambiguous_e4m3_keys(ref["folded_idx_raw"][:1], [e0])
+                if amb:
+                    q = Stored(g["q_idx"][b], "e4m3", g["q_scale"][b]).all()
+                    bd = score_bounds(q, np.asarray(g["w_idx"][b], np.float64), amb)
+            ok, swaps, msg = topk_check_bounds(ids, cnt, ref["sel"], ref["scores"], g["k"], bd,
+                                               err=decode_err(g, b, ref))
             assert ok, f"{label} b={b}: {msg}"
             swaps_total += swaps
             if swaps:
@@ -109,7 +117,9 @@ def test_tiny_fp32_whole_context(gpu_lib):
     ids, cnt, out, lse = ids.cpu().numpy(), cnt.cpu().numpy(), f64(out), f64(lse)
     for i in range(g["Tq"]):
         o, l, sel, scores = OL.tiny_query(g, i, kv_ref, keys_ref)
-        ok, swaps, msg = topk_check(ids[0, i], cnt[0, i], sel, scores, g["k"])
+        ok, swaps, msg = topk_check(ids[0, i], cnt[0, i], sel, scores, g["k"],
+                                    err=lambda: score_error_bound(g["q_idx"][0][i], g["w_idx"][0][i],
+                                                                  keys_ref[:len(scores)]))
         assert ok, f"query {i}: {msg}"
         if swaps:
             o, l, _, _ = OL.tiny_query(g, i, kv_ref, keys_ref, selected=ids[0, i, :cnt[0, i]])
@@ -224,24 +234,13 @@ def _check_prefill(g, sess, label, queries=None):
     for i in qs:
         ref = OL.prefill_query(g, 0, i, kv_new, idx_new)
         if g["kind"] == "csa":
-            ok, swaps, msg = topk_check(ids[i], cnt[i], ref["sel"], ref["scores"], g["k"])
+            ok, swaps, msg = topk_check(ids[i], cnt[i], ref["sel"], ref["scores"], g["k"],
+                                        err=prefill_err(g, 0, i, idx_new, len(ref["scores"])))
             assert ok, f"{label} q{i}: {msg}"
             if swaps:
                 ref = OL.prefill_query(g, 0, i, kv_new, idx_new, selected=ids[i, :cnt[i]])
         assert_close(out[0, i], ref["o"], kvk, f"{label} out q{i}")
         assert np.abs(lse[0, i] - ref["lse"]).max() < 1e-3
-
-
-def test_prefill_csa_mfma_indexer(gpu_lib):
-    # 64 indexer heads of dim 128 (bf16), 64 queries (16 groups of four):
-    # the MFMA prefill scorer over two 1024-entry chunks, the last one a
-    # ragged tile; every query checked against the oracle
-    from sparse_attention_csa_amd.harness import PrefillSession
-    a, _ = workloads.flash_prefill(seed=35, T=64, n0=4500, H=64, c=512, H_I=64, d_I=128, k=64,
-                                   m_hca=128)
-    sess = PrefillSession(a)
-    sess.run()
-    _check_prefill(a, sess, "prefill-csa-mfma-indexer")
 
 
 @pytest.mark.parametrize("H,c", [(8, 64), (64, 512)])

@@ -10,7 +10,7 @@ import torch
 
 from oracle import csa as OC
 from oracle.formats import Stored
-from tests.compare import topk_check
+from tests.compare import score_error_bound, topk_check
 
 pytestmark = pytest.mark.gpu
 
@@ -43,9 +43,11 @@ def _check(kbits, qbits, w, k, n_entries, q_pos, ids, cnt, m=4):
         K = Stored(kbits[b], "bf16")
         for t in range(Tq):
             nv = OC.visible_entries(int(q_pos[b][t]), m, int(n_entries[b]))
-            s = OC.index_scores(Stored(qbits[b, t], "bf16").all(), w[b, t], K.rows(slice(0, nv)))
+            q, Kv = Stored(qbits[b, t], "bf16").all(), K.rows(slice(0, nv))
+            s = OC.index_scores(q, w[b, t], Kv)
             sel = OC.topk_select(s, k)
-            ok, swaps, msg = topk_check(ids[b, t], cnt[b, t], sel, s, k)
+            ok, swaps, msg = topk_check(ids[b, t], cnt[b, t], sel, s, k,
+                                        err=lambda: score_error_bound(q, w[b, t], Kv))
             assert ok, f"b={b} t={t}: {msg}"
 
 

@@ -10,18 +10,18 @@ from oracle import layer
 from tests.cases import decode_from_prefill, prefix_case
 
 
-def _continuation(pre, T_done, T_full):
+def _continuation(pre, T_done, T_full, b=0):
     full = prefix_case(pre, T_full)
-    kv_full, idx_full = layer.prefill_entries(full, 0)
+    kv_full, idx_full = layer.prefill_entries(full, b)
     part = prefix_case(pre, T_done)
-    kv_new, idx_new = layer.prefill_entries(part, 0)
+    kv_new, idx_new = layer.prefill_entries(part, b)
     extra_kv, extra_idx = [], []
     pos0 = int(pre["pos0"])
     for i in range(T_done, T_full):
         t = pos0 + i
-        dec = decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv, extra_idx)
+        dec = decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv, extra_idx, b=b)
         got = layer.decode_step(dec, 0)
-        want = layer.prefill_query(full, 0, i, kv_full, idx_full)
+        want = layer.prefill_query(full, b, i, kv_full, idx_full)
         assert np.allclose(got["o"], want["o"], rtol=0, atol=1e-12), (pre["kind"], i)
         assert np.allclose(got["lse"], want["lse"], rtol=0, atol=1e-12)
         if pre["kind"] == "csa":
@@ -36,6 +36,15 @@ def _continuation(pre, T_done, T_full):
 def test_continuation_csa():
     a, _ = workloads.flash_prefill(seed=21, T=40, n0=64, H=3, c=16, H_I=2, d_I=8, k=6)
     _continuation(a, 32, 40)
+
+
+def test_continuation_csa_e4m3_indexer_second_sequence():
+    """The e4m3 indexer (keys the layer produces are quantised with one scale
+    per key, then re-encoded into the decode step's cache) and a sequence
+    other than the first of the batch."""
+    a, _ = workloads.flash_prefill(seed=23, B=2, T=40, n0=64, H=3, c=16, H_I=2, d_I=8, k=6,
+                                   idx_dtype="e4m3")
+    _continuation(a, 32, 40, b=1)
 
 
 def test_continuation_hca():

@@ -233,7 +233,8 @@ def flash_hca_decode(seed=2, B=8, n=1 << 20, H=64, c=512, n_win=128, m=128, pos_
 # 5. prefill chunk: one CSA layer then one HCA layer
 # ---------------------------------------------------------------------------
 
-def _prefill_case(rng, kind, B, T, n0, H, c, m, n_win, overlap, k=None, H_I=None, d_I=None):
+def _prefill_case(rng, kind, B, T, n0, H, c, m, n_win, overlap, k=None, H_I=None, d_I=None,
+                  idx_dtype="bf16"):
     E0 = n0 // m
     E_cap = (n0 + T) // m
     g = dict(kind=kind, B=B, T=T, pos0=n0, H=H, c=c, m=m, n_win=n_win, overlap=overlap,
@@ -254,9 +255,17 @@ def _prefill_case(rng, kind, B, T, n0, H, c, m, n_win, overlap, k=None, H_I=None
     g["q"] = _normal_bf16(rng, (B, T, H, c))
     g["sink"] = _normal(rng, (H,))
     if kind == "csa":
-        g.update(H_I=H_I, d_I=d_I, idx_dtype="bf16", idx_scale=None, q_scale=None)
-        ik = np.zeros((B, E_cap, d_I), dtype=np.uint16)
-        ik[:, :E0] = _normal_bf16(rng, (B, E0, d_I))
+        g.update(H_I=H_I, d_I=d_I, idx_dtype=idx_dtype, idx_scale=None, q_scale=None)
+        if idx_dtype == "e4m3":
+            # cached keys and the chunk's indexer queries in e4m3, one scale
+            # per vector; entries from E0 on are produced by the chunk
+            ik = np.zeros((B, E_cap, d_I), dtype=np.uint8)
+            isc = np.ones((B, E_cap), dtype=np.float32)
+            ik[:, :E0], isc[:, :E0] = e4m3_rows(_normal(rng, (B, E0, d_I)))
+            g["idx_scale"] = isc
+        else:
+            ik = np.zeros((B, E_cap, d_I), dtype=np.uint16)
+            ik[:, :E0] = _normal_bf16(rng, (B, E0, d_I))
         g["idx_cache"] = ik
         for s in ("ca", "za", "cb", "zb"):
             g["i" + s] = _normal_bf16(rng, (B, T, d_I))
@@ -264,7 +273,10 @@ def _prefill_case(rng, kind, B, T, n0, H, c, m, n_win, overlap, k=None, H_I=None
         g["prev_izb"] = _normal_bf16(rng, (B, m, d_I))
         g["ibias_a"] = _normal(rng, (m, d_I))
         g["ibias_b"] = _normal(rng, (m, d_I))
-        g["q_idx"] = _normal_bf16(rng, (B, T, H_I, d_I))
+        if idx_dtype == "e4m3":
+            g["q_idx"], g["q_scale"] = e4m3_rows(_normal(rng, (B, T, H_I, d_I)))
+        else:
+            g["q_idx"] = _normal_bf16(rng, (B, T, H_I, d_I))
         g["w_idx"] = _normal(rng, (B, T, H_I))
     else:
         g["idx_dtype"] = None
@@ -272,12 +284,14 @@ def _prefill_case(rng, kind, B, T, n0, H, c, m, n_win, overlap, k=None, H_I=None
 
 
 def flash_prefill(seed=4, B=1, T=4096, n0=262144, H=64, c=512, H_I=64, d_I=128, k=512,
-                  n_win=128, m_csa=4, m_hca=128):
+                  n_win=128, m_csa=4, m_hca=128, idx_dtype="bf16"):
     """Flash-shaped hybrid prefill: a T-token chunk appended to an n0-token
     context, through one CSA layer (overlap compressor, indexer, top-k) and one
-    HCA layer (non-overlapping compressor, dense), each with its own inputs."""
+    HCA layer (non-overlapping compressor, dense), each with its own inputs.
+    ``idx_dtype="e4m3"`` stores the CSA indexer keys and queries in e4m3 with
+    one scale per vector (the Pro layout)."""
     rng = _rng(seed)
-    csa = _prefill_case(rng, "csa", B, T, n0, H, c, m_csa, n_win, True, k, H_I, d_I)
+    csa = _prefill_case(rng, "csa", B, T, n0, H, c, m_csa, n_win, True, k, H_I, d_I, idx_dtype)
     hca = _prefill_case(rng, "hca", B, T, n0, H, c, m_hca, n_win, False)
     csa["name"] = CONFIG_NAMES[5] + ":csa"
     hca["name"] = CONFIG_NAMES[5] + ":hca"
