@@ -283,6 +283,23 @@ csa_status hybrid_layer_decode(const csa_layer_desc* desc, csa_layer_state* stat
 csa_status hybrid_layer_prefill(const csa_layer_desc* desc, csa_layer_state* state,
                                 const csa_prefill_io* io, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): hybrid_layer_decode
+ * with its workspace in a device array inside the library, one per device,
+ * of hybrid_layer_noalloc_scratch_bytes() bytes (32 MiB: enough for a
+ * Pro-shaped CSA layer of 4 sequences x 262,144 entries with k = 1024, or a
+ * Flash-shaped HCA layer of 8 x 8,192 entries).  The caller still passes the
+ * state, inputs and outputs.  Same arguments, results and errors as
+ * hybrid_layer_decode, plus CSA_ERR_WORKSPACE when the call needs more than
+ * the array holds.  It allocates and frees nothing.  Calls on one device share
+ * its array and must not overlap (calls on different streams of one device, or
+ * from several threads at once, race); the array keeps the last call's
+ * contents and is cleared by the library (on the call's stream) whenever the
+ * configuration (descriptor, B, E_cap) differs from the previous call's. */
+size_t hybrid_layer_noalloc_scratch_bytes(void);
+csa_status hybrid_layer_decode_noalloc(const csa_layer_desc* desc, csa_layer_state* state,
+                                       const csa_decode_io* io, void* stream);
+
 /* ------------------------------------------------------------------------
  * Kernel timing (diagnostics, not part of the method).  While enabled, every
  * kernel the library launches is bracketed by two hipEvents recorded on its

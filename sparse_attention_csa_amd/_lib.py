@@ -24,6 +24,7 @@ EXPORTS = [
     "csa_index_topk", "csa_attend_workspace", "csa_attend", "hca_attend",
     "hybrid_layer_workspace", "hybrid_layer_decode", "hybrid_layer_prefill",
     "csa_profile_enable", "csa_profile_collect", "csa_test_set_fused_wait_polls",
+    "hybrid_layer_noalloc_scratch_bytes", "hybrid_layer_decode_noalloc",
 ]
 
 
@@ -93,6 +94,9 @@ def _declare(lib):
         "csa_profile_enable": (I, [I]),
         "csa_profile_collect": (I, [C.POINTER(KernelTime), I]),
         "csa_test_set_fused_wait_polls": (I, [I]),
+        "hybrid_layer_noalloc_scratch_bytes": (SZ, []),
+        "hybrid_layer_decode_noalloc": (I, [C.POINTER(LayerDesc), C.POINTER(LayerState),
+                                            C.POINTER(DecodeIO), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -236,6 +240,11 @@ def hybrid_layer_workspace(desc, B, T, E_cap):
 def hybrid_layer_decode(desc, state, io, ws, stream=None):
     check(lib().hybrid_layer_decode(C.byref(desc), C.byref(state), C.byref(io), ptr(ws), ws.numel(),
                                     stream_handle(stream)))
+
+
+def hybrid_layer_decode_noalloc(desc, state, io, stream=None):
+    check(lib().hybrid_layer_decode_noalloc(C.byref(desc), C.byref(state), C.byref(io),
+                                            stream_handle(stream)))
 
 
 def hybrid_layer_prefill(desc, state, io, ws, stream=None):

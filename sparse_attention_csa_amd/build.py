@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
 
 SOURCES = ["api.cpp", "profile.cpp", "compress.hip", "indexer.hip", "attend.hip", "attend_mfma.hip", "attend_rows.hip",
-           "indexer_mfma.hip", "topk.hip"]
+           "indexer_mfma.hip", "topk.hip", "noalloc.hip"]
 
 ARCH = os.environ.get("CSA_OFFLOAD_ARCH", "gfx950")
 
