@@ -146,8 +146,44 @@ def kernel_work(kname, g):
     return 0, 0.0, "hbm", A.PEAK_HBM_GBS, "GB/s"
 
 
+def layer_work(g):
+    """(algorithmic bytes, algorithmic flops) of one step of layer g."""
+    from sparse_attention_csa_amd import accounting as A
+    if "T" in g:
+        fl = A.prefill_layer_flops(g["kind"], g["T"], g["pos0"], g["m"], g["H"], g["c"], g["n_win"], g.get("k"),
+                                   g.get("H_I"), g.get("d_I")) * g["B"]
+        return 0, fl
+    E = int(g["n_entries"][0]) + 1 if int(g["pos"][0]) % g["m"] == 0 else int(g["n_entries"][0])
+    byt = A.decode_layer_bytes(g["kind"], g["B"], E, g["H"], g["c"], g["n_win"], g.get("k"), g.get("H_I"),
+                               g.get("d_I"), g.get("idx_dtype"), g["m"], g["overlap"], g["kv_dtype"])
+    return byt, 0.0
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = "unknown"
+    try:
+        from threadpoolctl import threadpool_info
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if infos:
+            blas = "{} {} ({})".format(infos[0].get("internal_api"), infos[0].get("version"),
+                                       infos[0].get("threading_layer", ""))
+    except Exception:  # noqa: BLE001
+        pass
+    return model, blas
+
+
 def cpu_baseline(cases, prefill):
-    """Time the oracle (as it stands) on a bounded sample of the same work."""
+    """Time the oracle (as it stands) on a bounded sample of the same work:
+    three timed repetitions, the median reported."""
     import numpy as np
     from oracle import layer as OL
     try:
@@ -155,41 +191,135 @@ def cpu_baseline(cases, prefill):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # noqa: BLE001
         cores = len(os.sched_getaffinity(0))
-    tokens, secs, parts = 0, 0.0, []
-    per_step_tokens, per_step_secs = 0, 0.0
-    for name, g in cases:
-        if prefill:
+    model, blas = cpu_info()
+    reps = []
+    parts = []
+    for rep in range(3):
+        tokens, secs = 0, 0.0
+        for name, g in cases:
             t0 = time.perf_counter()
-            kv_new, idx_new = OL.prefill_entries(g, 0)
-            n_q = 4
-            for i in np.linspace(0, g["T"] - 1, n_q).astype(int):
-                OL.prefill_query(g, 0, int(i), kv_new, idx_new)
-            dt = time.perf_counter() - t0
-            # the chunk's compression is shared; queries scale linearly
-            tokens += n_q
-            parts.append(f"{name}: compress chunk + {n_q} queries")
-        else:
-            # whole decode steps of every sequence, repeated until about 7 s
-            # of CPU work per layer (at most 64 passes)
-            t0 = time.perf_counter()
-            passes = 0
-            while passes < 64 and (passes == 0 or time.perf_counter() - t0 < 7.0):
+            if prefill:
+                kv_new, idx_new = OL.prefill_entries(g, 0)
+                n_q = 4
+                for i in np.linspace(0, g["T"] - 1, n_q).astype(int):
+                    OL.prefill_query(g, 0, int(i), kv_new, idx_new)
+                tokens += n_q
+                if rep == 0:
+                    parts.append(f"{name}: compress chunk + {n_q} queries")
+            else:
+                # one whole decode step of every sequence of the layer
                 for b in range(g["B"]):
                     OL.decode_step(g, b)
-                passes += 1
-            dt = time.perf_counter() - t0
-            # one step of every layer, as the timed GPU step: the time of one
-            # pass per layer, the tokens of one pass
-            per_step_secs += dt / passes
-            per_step_tokens += g["B"]
-            tokens += g["B"] * passes
-            parts.append(f"{name}: {passes} x full decode step of all {g['B']} sequences")
-        secs += dt
+                tokens += g["B"]
+                if rep == 0:
+                    parts.append(f"{name}: one decode step of all {g['B']} sequences")
+            secs += time.perf_counter() - t0
+        reps.append((secs, tokens))
+    secs = sorted(r[0] for r in reps)[1]
+    tokens = reps[0][1]
     unit = "prefill tokens/s per layer" if prefill else "decode tokens/s per layer"
-    value = tokens / secs if prefill else per_step_tokens / per_step_secs
-    return {"value": value, "unit": unit, "cores": int(cores), "kind": "oracle",
-            "sample": "; ".join(parts) + f" ({secs:.1f} s of CPU work)" +
-                      ("" if prefill else "; value = tokens of one step of each layer / time of one step of each layer")}
+    return {"value": tokens / secs, "unit": unit, "cores": int(cores), "kind": "oracle",
+            "cpu_model": model, "blas": blas, "repetitions": 3, "statistic": "median",
+            "sample": "; ".join(parts) + f" (median of 3 repetitions: {secs:.2f} s); value = tokens of one "
+                      "step of each layer / time of one step of each layer"}
+
+
+def measure(cases, steps, warmup, rotate, prefill, profile=True):
+    """Time `steps` steps (every layer of `cases` once per step) after
+    `warmup` untimed ones, cycling through `rotate` state copies; then each
+    layer alone, and each kernel through the timing hook."""
+    import torch
+    from sparse_attention_csa_amd import _lib as L
+    from sparse_attention_csa_amd.harness import DecodeSession, PrefillSession
+
+    rot = 1 if prefill else max(1, rotate)
+    t0 = time.time()
+    sessions = []
+    for name, g in cases:
+        S = PrefillSession if prefill else DecodeSession
+        sessions.append((name, g, [S(g) for _ in range(rot)]))
+    saved = [[s.state.n_entries.clone() for s in ss] for _, _, ss in sessions]
+    torch.cuda.synchronize()
+    log(f"uploaded {rot} state copies of {'+'.join(n for n, _ in cases)} in {time.time() - t0:.1f} s")
+
+    def reset(i):
+        for li, (_, _, ss) in enumerate(sessions):
+            ss[i % rot].state.n_entries.copy_(saved[li][i % rot])
+
+    def step(i):
+        for _, _, ss in sessions:
+            ss[i % rot].run()
+
+    for i in range(warmup):
+        reset(i)
+        step(i)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(steps):
+        reset(i)
+        starts[i].record()
+        step(i)
+        ends[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    ms = sum(step_ms) / len(step_ms)
+    log(f"steps: mean {ms:.4f} ms, min {min(step_ms):.4f} ms, wall/step {wall / steps * 1e3:.3f} ms")
+
+    layers = {}
+    for name, g, ss in sessions:
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+        for i in range(steps):
+            reset(i)
+            ev[2 * i].record()
+            ss[i % rot].run()
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        lm = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps
+        toks = g["B"] * (g["T"] if prefill else 1)
+        byt, fl = layer_work(g)
+        rec = {"ms": round(lm, 5), "tokens_per_s": round(toks / (lm / 1e3), 1)}
+        from sparse_attention_csa_amd import accounting as A
+        if prefill:
+            tf = fl / (lm / 1e3) / 1e12
+            rec.update(alg_tflop=round(fl / 1e12, 4), achieved_tflops=round(tf, 2), bound="mfma",
+                       peak_tflops=A.PEAK_BF16_TFLOPS, frac=round(tf / A.PEAK_BF16_TFLOPS, 4))
+        else:
+            gbs = byt / (lm / 1e3) / 1e9
+            rec.update(alg_bytes=int(byt), achieved_gbs=round(gbs, 1), bound="hbm", peak_gbs=A.PEAK_HBM_GBS,
+                       frac=round(gbs / A.PEAK_HBM_GBS, 4))
+        layers[name] = rec
+
+    kernels = {}
+    best = None
+    if profile:
+        L.profile_enable(True)
+        kern = {}
+        for name, g, ss in sessions:
+            L.profile_collect()
+            for i in range(steps):
+                reset(i)
+                ss[i % rot].run()
+            torch.cuda.synchronize()
+            for kname, (n, tot) in L.profile_collect().items():
+                kern[f"{name}:{kname}"] = (n, tot, g, kname)
+        L.profile_enable(False)
+        for key, (n, tot, g, kname) in kern.items():
+            avg = tot / n
+            byt, fl, bound, peak, unit = kernel_work(kname, g)
+            ach = (byt / (avg / 1e3) / 1e9) if unit == "GB/s" else (fl / (avg / 1e3) / 1e12)
+            kernels[key] = {"avg_ms": round(avg, 5), "launches": n,
+                            "alg_bytes": int(byt), "alg_flops": float(fl),
+                            "achieved": round(ach, 2), "unit": unit, "frac": round(ach / peak, 4)}
+            if best is None or tot > best[1]:
+                best = (key, tot, ach, peak, unit, bound, byt, fl)
+    tokens = sum(g["B"] * (g["T"] if prefill else 1) for _, g, _ in sessions)
+    out = {"ms_per_step": ms, "tokens": tokens, "layers": layers, "kernels": kernels, "best": best,
+           "sessions": sessions, "rot": rot}
+    return out
 
 
 def main():
@@ -200,6 +330,8 @@ def main():
     ap.add_argument("--workload", default="decode_1m")
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra workloads measured after the headline one")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB 10 times (counter calibration)")
     args = ap.parse_args()
@@ -222,109 +354,81 @@ def main():
         return
 
     from sparse_attention_csa_amd import _lib as L
-    from sparse_attention_csa_amd.harness import DecodeSession, PrefillSession
 
     L.lib()
     prefill = args.workload == "prefill"
     t0 = time.time()
     cases = build_cases(args.workload)
     log(f"generated inputs in {time.time() - t0:.1f} s")
-    rot = 1 if prefill else max(1, args.rotate)
-    sessions = []
-    for name, g in cases:
-        S = PrefillSession if prefill else DecodeSession
-        sessions.append((name, g, [S(g) for _ in range(rot)]))
-    saved = [[s.state.n_entries.clone() for s in ss] for _, _, ss in sessions]
-    torch.cuda.synchronize()
-    log(f"uploaded {rot} state copies in {time.time() - t0:.1f} s")
-
-    def reset(i):
-        for li, (_, _, ss) in enumerate(sessions):
-            ss[i % rot].state.n_entries.copy_(saved[li][i % rot])
-
-    def step(i):
-        for _, _, ss in sessions:
-            ss[i % rot].run()
-
-    for i in range(args.warmup):
-        reset(i)
-        step(i)
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for i in range(args.steps):
-        reset(i)
-        starts[i].record()
-        step(i)
-        ends[i].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    step_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ms = sum(step_ms) / len(step_ms)
-    tokens = sum(g["B"] * (g["T"] if prefill else 1) for _, g, _ in sessions)
+    res = measure(cases, args.steps, args.warmup, args.rotate, prefill)
+    ms, tokens, layers, kernels = res["ms_per_step"], res["tokens"], res["layers"], res["kernels"]
     value = tokens / (ms / 1e3)
-    log(f"steps: mean {ms:.4f} ms, min {min(step_ms):.4f} ms, wall/step {wall / args.steps * 1e3:.3f} ms")
-
-    # per-layer times and per-kernel durations (timing hook, a separate pass)
-    layers = {}
-    for name, g, ss in sessions:
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
-        for i in range(args.steps):
-            reset(i)
-            ev[2 * i].record()
-            ss[i % rot].run()
-            ev[2 * i + 1].record()
-        torch.cuda.synchronize()
-        lm = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)) / args.steps
-        toks = g["B"] * (g["T"] if prefill else 1)
-        layers[name] = {"ms": round(lm, 5), "tokens_per_s": round(toks / (lm / 1e3), 1)}
-    L.profile_enable(True)
-    kern = {}
-    for name, g, ss in sessions:
-        L.profile_collect()
-        for i in range(args.steps):
-            reset(i)
-            ss[i % rot].run()
-        torch.cuda.synchronize()
-        for kname, (n, tot) in L.profile_collect().items():
-            kern[f"{name}:{kname}"] = (n, tot, g, kname)
-    L.profile_enable(False)
-    kernels = {}
-    best = None
-    for key, (n, tot, g, kname) in kern.items():
-        avg = tot / n
-        byt, fl, bound, peak, unit = kernel_work(kname, g)
-        ach = (byt / (avg / 1e3) / 1e9) if unit == "GB/s" else (fl / (avg / 1e3) / 1e12)
-        kernels[key] = {"avg_ms": round(avg, 5), "launches": n,
-                        "alg_bytes": int(byt), "alg_flops": float(fl),
-                        "achieved": round(ach, 2), "unit": unit, "frac": round(ach / peak, 4)}
-        if best is None or tot > best[1]:
-            best = (key, tot, ach, peak, unit, bound, byt)
-    key, _, ach, peak, unit, bound, byt = best
+    key, _, ach, peak, unit, bound, byt, fl = res["best"]
     traffic = profiled_traffic(args.workload, key.split(":", 1)[1])
     roofline = {"bound": bound, "achieved": round(ach, 2), "peak": peak, "unit": unit,
                 "frac": round(ach / peak, 4), "traffic": traffic, "kernel": key,
-                "alg_bytes_per_launch": int(byt)}
-
-    cpu = None
-    if not args.no_cpu:
-        log("timing the oracle on a bounded sample ...")
-        cpu = cpu_baseline([(n, g) for n, g, _ in sessions], prefill)
-
+                "alg_bytes_per_launch": int(byt) if unit == "GB/s" else None,
+                "alg_flops_per_launch": float(fl) if unit != "GB/s" else None}
+    rot = res["rot"]
+    sessions = res["sessions"]
     names = "+".join(n for n, _, _ in sessions)
     cfg = {"workload": names, "layers": list(layers.keys()),
            "batch": {n: g["B"] for n, g, _ in sessions},
            "context_tokens": {n: int(g.get("n", g.get("pos0", 0))) for n, g, _ in sessions},
            "rotate_state_copies": rot}
+    # the whole step against the roofline: every layer's algorithmic bytes
+    # (flops for prefill) over the step time
+    tot_b = sum(layer_work(g)[0] for _, g, _ in sessions)
+    tot_f = sum(layer_work(g)[1] for _, g, _ in sessions)
+    from sparse_attention_csa_amd import accounting as A
+    if prefill:
+        step_roof = {"bound": "mfma", "alg_tflop": round(tot_f / 1e12, 4),
+                     "achieved_tflops": round(tot_f / (ms / 1e3) / 1e12, 2), "peak_tflops": A.PEAK_BF16_TFLOPS,
+                     "frac": round(tot_f / (ms / 1e3) / 1e12 / A.PEAK_BF16_TFLOPS, 4)}
+    else:
+        step_roof = {"bound": "hbm", "alg_bytes": int(tot_b),
+                     "achieved_gbs": round(tot_b / (ms / 1e3) / 1e9, 1), "peak_gbs": A.PEAK_HBM_GBS,
+                     "frac": round(tot_b / (ms / 1e3) / 1e9 / A.PEAK_HBM_GBS, 4)}
+    del res, sessions
+    torch.cuda.empty_cache()
+
+    # the other configurations, timed in the same run: the Flash-shaped CSA
+    # decode at 128K context and the hybrid prefill chunk
+    extra = {}
+    if args.workload == "decode_1m" and not args.no_extra:
+        for wl, steps, warm in (("flash_csa_128k", args.steps, args.warmup),
+                                ("prefill", max(3, min(args.steps, 5)), 1)):
+            t1 = time.time()
+            c2 = build_cases(wl)
+            log(f"generated {wl} inputs in {time.time() - t1:.1f} s")
+            r2 = measure(c2, steps, warm, args.rotate, wl == "prefill", profile=False)
+            ms2 = r2["ms_per_step"]
+            byt2 = sum(layer_work(g)[0] for _, g in c2)
+            fl2 = sum(layer_work(g)[1] for _, g in c2)
+            rec = {"ms_per_step": round(ms2, 5), "tokens_per_s_per_layer": round(r2["tokens"] / (ms2 / 1e3), 1),
+                   "steps": steps, "layers": r2["layers"]}
+            if wl == "prefill":
+                rec["unit"] = "prefill tokens/s per layer"
+                rec["frac_bf16_peak"] = round(fl2 / (ms2 / 1e3) / 1e12 / A.PEAK_BF16_TFLOPS, 4)
+            else:
+                rec["unit"] = "decode tokens/s per layer"
+                rec["frac_hbm"] = round(byt2 / (ms2 / 1e3) / 1e9 / A.PEAK_HBM_GBS, 4)
+            extra[wl] = rec
+            del r2, c2
+            torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the oracle on a bounded sample ...")
+        cpu = cpu_baseline(cases, prefill)
+
     out = {"metric": METRIC, "value": round(value, 2),
            "unit": "prefill tokens/s per layer" if prefill else "decode tokens/s per layer",
            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded; shapes of the pages' Flash/Pro configurations)",
-           "config": cfg, "roofline": roofline, "cpu_baseline": cpu,
-           "layer_times": layers, "kernels": kernels}
+           "config": cfg, "roofline": roofline, "step_roofline": step_roof, "cpu_baseline": cpu,
+           "layer_times": layers, "kernels": kernels, "other_workloads": extra}
     print(json.dumps(out), flush=True)
 
 

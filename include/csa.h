@@ -69,7 +69,8 @@ typedef enum {
 /* Thread-local text of the last error, or "" after a successful call. */
 const char* csa_last_error(void);
 
-/* ABI version of this header (bumped on incompatible change). */
+/* ABI version of this header (bumped on incompatible change; 2 added
+ * csa_layer_desc.split_rows). */
 int csa_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -209,6 +210,14 @@ typedef struct {
   int kv_dtype;      /* F32 or BF16: activations, caches, outputs             */
   int idx_dtype;     /* F32, BF16 or E4M3: indexer queries and keys (CSA)     */
   float scale;       /* attention logit scale (1/sqrt(c) for the pages)       */
+  int split_rows;    /* decode: 0 = the attention's row splits are sized for  */
+                     /* the batch; > 0 (a multiple of 16) = every query's     */
+                     /* rows are cut into splits of this many rows whatever   */
+                     /* the batch, so a token's output is bitwise the same    */
+                     /* wherever it sits in a batch ([book] ch. 12 "Batch      */
+                     /* invariance"); at most 64 splits per query, and at     */
+                     /* most 2304 rows per split for CSA (else               */
+                     /* CSA_ERR_UNSUPPORTED).  Prefill chunks ignore it.      */
 } csa_layer_desc;
 
 /* Number of compressor streams per token: 4 (ca, za, cb, zb) with overlap,

@@ -38,7 +38,7 @@ class LayerDesc(C.Structure):
     _fields_ = [("kind", C.c_int), ("H", C.c_int), ("c", C.c_int), ("H_I", C.c_int),
                 ("d_I", C.c_int), ("m", C.c_int), ("overlap", C.c_int), ("k", C.c_int),
                 ("n_win", C.c_int), ("vis", C.c_int), ("kv_dtype", C.c_int),
-                ("idx_dtype", C.c_int), ("scale", C.c_float)]
+                ("idx_dtype", C.c_int), ("scale", C.c_float), ("split_rows", C.c_int)]
 
 
 class LayerState(C.Structure):

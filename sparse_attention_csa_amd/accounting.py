@@ -94,3 +94,41 @@ def fold_bytes(B, m, c, streams, kv_dtype="bf16"):
     entry out, biases once."""
     kb = DTYPE_BYTES[kv_dtype]
     return B * (streams * m * c * kb + c * kb) + (streams // 2) * m * c * 4
+
+
+# ---------------------------------------------------------------------------
+# a whole layer step
+# ---------------------------------------------------------------------------
+
+def decode_layer_bytes(kind, B, E, H, c, n_win, k=None, H_I=None, d_I=None, idx_dtype=None, m=None,
+                       overlap=False, kv_dtype="bf16"):
+    """Algorithmic HBM bytes of one decode step of a layer (one token per
+    sequence, E entries visible): the fold of the completed block, the
+    indexer-key scan (CSA), the rows attended (the k selected, or all E, plus
+    the window), q in and o out."""
+    S = 4 if overlap else 2
+    byt = fold_bytes(B, m, c, S, kv_dtype)
+    if kind == "csa":
+        byt += fold_bytes(B, m, d_I, 4, kv_dtype)
+        byt += index_scan_bytes(B, 1, E, H_I, d_I, idx_dtype)
+        rows = min(k, E) + n_win
+    else:
+        rows = E + n_win
+    return byt + attend_bytes(B, 1, rows, H, c, kv_dtype)
+
+
+def prefill_layer_flops(kind, T, pos0, m, H, c, n_win, k=None, H_I=None, d_I=None):
+    """Algorithmic FLOPs of a prefill chunk of T queries at positions
+    pos0 .. pos0+T-1 (causal): the indexer over each query's visible entries
+    (CSA), attention over min(k, visible) (CSA) or all visible (HCA) entries
+    plus the window rows."""
+    fl = 0.0
+    for i in range(T):
+        vis = (pos0 + i) // m
+        w = min(n_win, pos0 + i + 1)
+        if kind == "csa":
+            fl += index_scan_flops(1, 1, vis, H_I, d_I)
+            fl += attend_flops(1, 1, min(k, vis) + w, H, c)
+        else:
+            fl += attend_flops(1, 1, vis + w, H, c)
+    return fl

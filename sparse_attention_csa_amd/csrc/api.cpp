@@ -89,7 +89,7 @@ extern "C" {
 
 const char* csa_last_error(void) { return g_err.c_str(); }
 
-int csa_abi_version(void) { return 1; }
+int csa_abi_version(void) { return 2; }
 
 int csa_test_set_fused_wait_polls(int polls) { return csa::set_fused_wait_polls(polls); }
 
@@ -257,6 +257,8 @@ static csa_status check_desc(const csa_layer_desc* d) {
   REQUIRE(d->vis == 0 || d->vis == 1, CSA_ERR_ARG, "bad visibility");
   REQUIRE(d->kv_dtype == CSA_F32 || d->kv_dtype == CSA_BF16, CSA_ERR_UNSUPPORTED, "kv_dtype must be F32 or BF16");
   REQUIRE(d->overlap == 0 || d->overlap == 1, CSA_ERR_ARG, "overlap must be 0 or 1");
+  REQUIRE(d->split_rows >= 0 && d->split_rows % 16 == 0, CSA_ERR_ARG,
+          "split_rows must be 0 or a positive multiple of 16 (got %d)", d->split_rows);
   if (d->kind == CSA_LAYER_CSA) {
     st = check_idx_dims(d->H_I, d->d_I);
     if (st != CSA_OK) return st;
@@ -264,6 +266,10 @@ static csa_status check_desc(const csa_layer_desc* d) {
     REQUIRE(d->k <= 2048, CSA_ERR_UNSUPPORTED, "k <= 2048 supported");
     REQUIRE(d->idx_dtype == CSA_F32 || d->idx_dtype == CSA_BF16 || d->idx_dtype == CSA_E4M3, CSA_ERR_ARG,
             "bad idx_dtype");
+    REQUIRE(d->split_rows == 0 || (d->split_rows <= 2304 &&
+                                   (d->k + d->n_win + d->split_rows - 1) / d->split_rows <= csa::kMaxRowSplits),
+            CSA_ERR_UNSUPPORTED, "split_rows %d: at most 2304 rows and %d splits of k + n_win rows", d->split_rows,
+            csa::kMaxRowSplits);
   }
   return CSA_OK;
 }
@@ -291,7 +297,7 @@ size_t hybrid_layer_workspace(const csa_layer_desc* d, int B, int T, int E_cap) 
     bytes += align_up(csa::index_topk_ws_bytes(B, T, E_cap, d->k));
     rows = (size_t)d->k + d->n_win;
   }
-  bytes += align_up(csa::attend_ws_bytes(B, T, d->H, d->c, (int)rows));
+  bytes += align_up(csa::attend_ws_bytes(B, T, d->H, d->c, (int)rows, T == 1 ? d->split_rows : 0));
   return bytes;
 }
 
@@ -304,6 +310,10 @@ csa_status decode_check(const csa_layer_desc* d, const csa_layer_state* s, const
   if (st != CSA_OK) return st;
   st = check_state(d, s);
   if (st != CSA_OK) return st;
+  REQUIRE(d->kind == CSA_LAYER_CSA || d->split_rows == 0 ||
+              ((int64_t)s->E_cap + d->n_win + d->split_rows - 1) / d->split_rows <= csa::kMaxRowSplits,
+          CSA_ERR_UNSUPPORTED, "split_rows %d: more than %d splits of E_cap + n_win rows", d->split_rows,
+          csa::kMaxRowSplits);
   REQ_PTR(io);
   REQ_PTR(io->pos); REQ_PTR(io->q); REQ_PTR(io->x_new); REQ_PTR(io->streams); REQ_PTR(io->out);
   if (d->kind == CSA_LAYER_CSA) {
@@ -352,6 +362,7 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
   a.win = s->win_ring; a.W_cap = d->n_win; a.win_pos0 = nullptr; a.win_pos0_const = 0; a.n_win = d->n_win;
   a.sink = s->sink; a.q_pos = io->pos; a.scale = d->scale;
   a.B = B; a.Tq = 1; a.H = d->H; a.c = d->c; a.out = io->out; a.lse = io->lse;
+  a.split_rows = d->split_rows;
   if (!is_csa) {
     a.n_entries = s->n_entries; a.n_add = 0; a.m = d->m; a.vis = d->vis; a.dense = 1;
     a.ws = w; a.ws_bytes = ws_bytes - (size_t)(w - (char*)ws);

@@ -159,10 +159,10 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
 }
 
 bool attend_mfma_shape_ok(int H, int c);
-size_t attend_mfma_ws_bytes(int BT, int H, int rows_max);
+size_t attend_mfma_ws_bytes(int BT, int H, int rows_max, int split_rows);
 hipError_t launch_attend_mfma(const AttendArgs& a, int rows_max, hipStream_t s);
 bool attend_rows_shape_ok(int H, int c);
-void attend_rows_plan(int BT, int H, int rows_max, int* n_split, int* rows_per_split);
+void attend_rows_plan(int BT, int H, int rows_max, int split_rows, int* n_split, int* rows_per_split);
 hipError_t launch_attend_rows(const AttendArgs& a, int rows_max, hipStream_t s);
 
 // partial (max, sum) pairs and bf16 outputs of the row splits
@@ -173,20 +173,20 @@ static size_t split_ws_bytes(int BT, int H, int c, int n_split) {
 
 // split partials, then (dense shapes) the decode fold's q . entry sums and
 // entry indices at attend_fold_ws_offset
-size_t attend_fold_ws_offset(int B, int Tq, int H, int c, int rows_max) {
+size_t attend_fold_ws_offset(int B, int Tq, int H, int c, int rows_max, int split_rows) {
   size_t n = 256, extra = 0;
-  if (attend_mfma_shape_ok(H, c)) extra = attend_mfma_ws_bytes(B * Tq, H, rows_max);
+  if (attend_mfma_shape_ok(H, c)) extra = attend_mfma_ws_bytes(B * Tq, H, rows_max, split_rows);
   if (attend_rows_shape_ok(H, c)) {
     int ns, rps;
-    attend_rows_plan(B * Tq, H, rows_max, &ns, &rps);
+    attend_rows_plan(B * Tq, H, rows_max, split_rows, &ns, &rps);
     const size_t r = split_ws_bytes(B * Tq, H, c, ns);
     if (r > extra) extra = r;
   }
   return (n + extra + 255) / 256 * 256;
 }
 
-size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max) {
-  size_t n = attend_fold_ws_offset(B, Tq, H, c, rows_max);
+size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max, int split_rows) {
+  size_t n = attend_fold_ws_offset(B, Tq, H, c, rows_max, split_rows);
   if (attend_mfma_shape_ok(H, c))
     n += ((size_t)B * H * 64 * 8 + 255) / 256 * 256 + ((size_t)B * 4 + 255) / 256 * 256 + ((size_t)B * c * 2 + 255) / 256 * 256;
   return n;

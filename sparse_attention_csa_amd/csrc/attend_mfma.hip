@@ -734,8 +734,8 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
 
 bool attend_mfma_shape_ok(int H, int c) { return c == kC && H % kHW == 0; }
 
-size_t attend_fold_ws_offset(int B, int Tq, int H, int c, int rows_max);
-void attend_mfma_plan(int BT, int H, int rows_max, int* n_split, int* rows_per_split);
+size_t attend_fold_ws_offset(int B, int Tq, int H, int c, int rows_max, int split_rows);
+void attend_mfma_plan(int BT, int H, int rows_max, int split_rows, int* n_split, int* rows_per_split);
 
 // HCA decode (one query per sequence, no overlap, bf16) with at least two
 // row splits (the merge adds the new entry): the coordinates split into
@@ -748,7 +748,7 @@ bool attend_fuses_fold(AttendArgs& a, const FoldArgs& f) {
       f.B != a.B || f.c != a.c || f.n_win != a.W_cap || f.R < 2 * f.m)
     return false;
   int ns, rps;
-  attend_mfma_plan(a.B * a.Tq, a.H, a.E_cap + a.n_win, &ns, &rps);
+  attend_mfma_plan(a.B * a.Tq, a.H, a.E_cap + a.n_win, a.split_rows, &ns, &rps);
   if (ns < 2) return false;
   int cs = 8;
   while (cs * ns < a.c) cs *= 2;
@@ -756,7 +756,7 @@ bool attend_fuses_fold(AttendArgs& a, const FoldArgs& f) {
   // the P^T buffer
   if (cs > 64 || a.c / cs > kFoldSlots || f.m > kFoldS * (256 / cs) || f.m * cs * 8 > kTN * kRowB || a.H * cs * 2 > 4 * 64 * 16)
     return false;
-  const size_t off = attend_fold_ws_offset(a.B, a.Tq, a.H, a.c, a.E_cap + a.n_win);
+  const size_t off = attend_fold_ws_offset(a.B, a.Tq, a.H, a.c, a.E_cap + a.n_win, a.split_rows);
   char* base = reinterpret_cast<char*>(a.ws);
   a.fold_s = reinterpret_cast<float*>(base + off);
   const size_t off_row = off + ((size_t)a.B * a.H * kFoldSlots * 8 + 255) / 256 * 256;
@@ -769,8 +769,14 @@ bool attend_fuses_fold(AttendArgs& a, const FoldArgs& f) {
 }
 
 // Row splits per (query, head group): about one workgroup per CU (256), each
-// split a multiple of 16 rows, at most kMaxSplit splits.
-void attend_mfma_plan(int BT, int H, int rows_max, int* n_split, int* rows_per_split) {
+// split a multiple of 16 rows, at most kMaxSplit splits; or split_rows rows
+// each whatever the batch.
+void attend_mfma_plan(int BT, int H, int rows_max, int split_rows, int* n_split, int* rows_per_split) {
+  if (split_rows > 0) {
+    *rows_per_split = split_rows;
+    *n_split = (rows_max + split_rows - 1) / split_rows;
+    return;
+  }
   const int cols = BT * (H / kHW);
   int want = 256 / cols;
   if (want < 1) want = 1;
@@ -781,9 +787,9 @@ void attend_mfma_plan(int BT, int H, int rows_max, int* n_split, int* rows_per_s
   *n_split = (rows_max + rps - 1) / rps;
 }
 
-size_t attend_mfma_ws_bytes(int BT, int H, int rows_max) {
+size_t attend_mfma_ws_bytes(int BT, int H, int rows_max, int split_rows) {
   int ns, rps;
-  attend_mfma_plan(BT, H, rows_max, &ns, &rps);
+  attend_mfma_plan(BT, H, rows_max, split_rows, &ns, &rps);
   if (ns <= 1) return 0;
   return (size_t)BT * ns * H * (2 * sizeof(float) + kC * sizeof(uint16_t));
 }
@@ -792,11 +798,11 @@ hipError_t launch_attend_merge(const AttendArgs& a, int n_split, hipStream_t s);
 
 hipError_t launch_attend_mfma(const AttendArgs& a0, int rows_max, hipStream_t s) {
   int ns, rps;
-  attend_mfma_plan(a0.B * a0.Tq, a0.H, rows_max, &ns, &rps);
+  attend_mfma_plan(a0.B * a0.Tq, a0.H, rows_max, a0.split_rows, &ns, &rps);
   AttendArgs a = a0;
   a.fold_nsplit = 0;
   a.fold_rows = 0;
-  if (a.fold_mode) {
+  if (a.fold_mode && a.split_rows == 0) {
     // the folding splits take kFoldRowsLess fewer rows (the same split count)
     const int nf = (a.c + a.fold_cs - 1) / a.fold_cs;
     if (nf < ns) {

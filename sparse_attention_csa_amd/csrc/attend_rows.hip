@@ -343,8 +343,14 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
 bool attend_rows_shape_ok(int H, int c) { return c == kC && H % 16 == 0; }
 
 // Splits per (query, head group): about one workgroup per CU (256), each a
-// multiple of the 16-row tile, at most kMaxRows rows and 64 splits.
-void attend_rows_plan(int BT, int H, int rows_max, int* n_split, int* rows_per_split) {
+// multiple of the 16-row tile, at most kMaxRows rows and 64 splits; or
+// split_rows rows each whatever the batch.
+void attend_rows_plan(int BT, int H, int rows_max, int split_rows, int* n_split, int* rows_per_split) {
+  if (split_rows > 0) {
+    *rows_per_split = split_rows;
+    *n_split = (rows_max + split_rows - 1) / split_rows;
+    return;
+  }
   const int cols = BT * (H / 16);
   int want = 256 / cols;
   if (want < 1) want = 1;
@@ -360,7 +366,7 @@ hipError_t launch_attend_merge(const AttendArgs& a, int n_split, hipStream_t s);
 
 hipError_t launch_attend_rows(const AttendArgs& a, int rows_max, hipStream_t s) {
   int ns, rps;
-  attend_rows_plan(a.B * a.Tq, a.H, rows_max, &ns, &rps);
+  attend_rows_plan(a.B * a.Tq, a.H, rows_max, a.split_rows, &ns, &rps);
   if (ns > 64) return hipErrorInvalidValue;
   const int n_hg = a.H / 16;
   const long long units = (long long)ns * a.B * a.Tq;   // (query, split) pairs

@@ -153,6 +153,10 @@ struct AttendArgs {
   float* lse;
   void* ws;
   size_t ws_bytes;
+  // > 0: every query's rows are cut into splits of this many rows (a multiple
+  // of 16) whatever the batch, so a query's result does not depend on the
+  // batch it is in; 0: the split size is chosen for the batch
+  int split_rows;
   // dense decode with the step's fold inside (see attend_fuses_fold): each
   // split folds fold_cs coordinates of the new entry and writes its share of
   // q . entry and q . token to its slot of fold_s; the merge sums the slots
@@ -167,7 +171,11 @@ struct AttendArgs {
   int fold_nsplit;     // set by the launch: splits that fold (fewer rows each) ...
   int fold_rows;       // ... and their row count
 };
-size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max);
+// split_rows > 0: rows per split fixed (batch-invariant launch plan), else
+// chosen for the batch
+size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max, int split_rows = 0);
+// the largest number of row splits a query's rows may be cut into
+constexpr int kMaxRowSplits = 64;
 // whether hca decode can fold inside the attention; sets a.fold_mode / fold_cs
 bool attend_fuses_fold(AttendArgs& a, const FoldArgs& f);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);

@@ -53,6 +53,7 @@ def make_desc(g):
     d.kv_dtype = DTYPE_CODE[g["kv_dtype"]]
     d.idx_dtype = DTYPE_CODE[g["idx_dtype"]] if g.get("idx_dtype") else 0
     d.scale = g["scale"]
+    d.split_rows = int(g.get("split_rows") or 0)
     return d
 
 

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = L.lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.csa_abi_version() == 1
+    assert lib.csa_abi_version() == 2
 
 
 def _status(fn, *args):
@@ -115,6 +115,16 @@ def test_layer_rejects_bad_descriptors():
     d.n_win = 1000
     st = lib.hybrid_layer_decode(C.byref(d), C.byref(s), C.byref(io), None, 0, None)
     assert st == L.CSA_ERR_UNSUPPORTED
+    d.n_win = 128
+    d.split_rows = 40  # batch-invariant split size: a multiple of 16
+    st = lib.hybrid_layer_decode(C.byref(d), C.byref(s), C.byref(io), None, 0, None)
+    assert st == L.CSA_ERR_ARG and "split_rows" in L.last_error()
+    d.split_rows = 16  # (512 + 128) / 16 = 40 splits fit; 2304 rows at most
+    assert lib.hybrid_layer_workspace(C.byref(d), 8, 1, 32768) > 0
+    d.split_rows = 2320
+    st = lib.hybrid_layer_decode(C.byref(d), C.byref(s), C.byref(io), None, 0, None)
+    assert st == L.CSA_ERR_UNSUPPORTED and "split_rows" in L.last_error()
+    d.split_rows = 0
     assert lib.hybrid_layer_workspace(C.byref(d), 8, 1, 32768) > 0
 
 
