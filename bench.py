@@ -224,10 +224,13 @@ def cpu_baseline(cases, prefill):
                       "step of each layer / time of one step of each layer"}
 
 
-def measure(cases, steps, warmup, rotate, prefill, profile=True):
+def measure(cases, steps, warmup, rotate, prefill, profile=True, use_graph=False):
     """Time `steps` steps (every layer of `cases` once per step) after
     `warmup` untimed ones, cycling through `rotate` state copies; then each
-    layer alone, and each kernel through the timing hook."""
+    layer alone, and each kernel through the timing hook.  With use_graph each
+    (layer, state copy) step is captured once into a HIP graph and the timed
+    steps replay the graphs (the launch path of a serving loop); the kernel
+    timing hook always runs eagerly."""
     import torch
     from sparse_attention_csa_amd import _lib as L
     from sparse_attention_csa_amd.harness import DecodeSession, PrefillSession
@@ -250,6 +253,34 @@ def measure(cases, steps, warmup, rotate, prefill, profile=True):
         for _, _, ss in sessions:
             ss[i % rot].run()
 
+    for i in range(max(warmup, rot)):
+        reset(i)
+        step(i)
+    torch.cuda.synchronize()
+    if use_graph:
+        graphs = []
+        for li, (_, _, ss) in enumerate(sessions):
+            gl = []
+            for r, sess in enumerate(ss):
+                ss[r].state.n_entries.copy_(saved[li][r])
+                torch.cuda.synchronize()
+                gr = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gr):
+                    sess.run()
+                gl.append(gr)
+            graphs.append(gl)
+        torch.cuda.synchronize()
+
+        def run_layer(li, i):
+            graphs[li][i % rot].replay()
+    else:
+        def run_layer(li, i):
+            sessions[li][2][i % rot].run()
+
+    def step(i):  # noqa: F811
+        for li in range(len(sessions)):
+            run_layer(li, i)
+
     for i in range(warmup):
         reset(i)
         step(i)
@@ -270,12 +301,12 @@ def measure(cases, steps, warmup, rotate, prefill, profile=True):
     log(f"steps: mean {ms:.4f} ms, min {min(step_ms):.4f} ms, wall/step {wall / steps * 1e3:.3f} ms")
 
     layers = {}
-    for name, g, ss in sessions:
+    for li, (name, g, ss) in enumerate(sessions):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
         for i in range(steps):
             reset(i)
             ev[2 * i].record()
-            ss[i % rot].run()
+            run_layer(li, i)
             ev[2 * i + 1].record()
         torch.cuda.synchronize()
         lm = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps
@@ -318,7 +349,9 @@ def measure(cases, steps, warmup, rotate, prefill, profile=True):
                 best = (key, tot, ach, peak, unit, bound, byt, fl)
     tokens = sum(g["B"] * (g["T"] if prefill else 1) for _, g, _ in sessions)
     out = {"ms_per_step": ms, "tokens": tokens, "layers": layers, "kernels": kernels, "best": best,
-           "sessions": sessions, "rot": rot}
+           "sessions": sessions, "rot": rot, "graph": bool(use_graph)}
+    if use_graph:
+        del graphs
     return out
 
 
@@ -330,6 +363,8 @@ def main():
     ap.add_argument("--workload", default="decode_1m")
     ap.add_argument("--rotate", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each layer step from a captured HIP graph instead of launching eagerly")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra workloads measured after the headline one")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -360,7 +395,7 @@ def main():
     t0 = time.time()
     cases = build_cases(args.workload)
     log(f"generated inputs in {time.time() - t0:.1f} s")
-    res = measure(cases, args.steps, args.warmup, args.rotate, prefill)
+    res = measure(cases, args.steps, args.warmup, args.rotate, prefill, use_graph=args.graph)
     ms, tokens, layers, kernels = res["ms_per_step"], res["tokens"], res["layers"], res["kernels"]
     value = tokens / (ms / 1e3)
     key, _, ach, peak, unit, bound, byt, fl = res["best"]
@@ -375,7 +410,7 @@ def main():
     cfg = {"workload": names, "layers": list(layers.keys()),
            "batch": {n: g["B"] for n, g, _ in sessions},
            "context_tokens": {n: int(g.get("n", g.get("pos0", 0))) for n, g, _ in sessions},
-           "rotate_state_copies": rot}
+           "rotate_state_copies": rot, "launch": "hip graph replay" if res["graph"] else "eager"}
     # the whole step against the roofline: every layer's algorithmic bytes
     # (flops for prefill) over the step time
     tot_b = sum(layer_work(g)[0] for _, g, _ in sessions)
@@ -401,7 +436,7 @@ def main():
             t1 = time.time()
             c2 = build_cases(wl)
             log(f"generated {wl} inputs in {time.time() - t1:.1f} s")
-            r2 = measure(c2, steps, warm, args.rotate, wl == "prefill", profile=False)
+            r2 = measure(c2, steps, warm, args.rotate, wl == "prefill", profile=False, use_graph=args.graph)
             ms2 = r2["ms_per_step"]
             byt2 = sum(layer_work(g)[0] for _, g in c2)
             fl2 = sum(layer_work(g)[1] for _, g in c2)

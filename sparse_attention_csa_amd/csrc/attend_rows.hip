@@ -14,7 +14,11 @@
 // belongs to wavefront j % 4: each wavefront runs its own pipeline (two LDS
 // slots, direct global-to-LDS DMA of the gathered rows, no workgroup
 // barrier) and the four partial softmax states are combined through LDS at
-// the end.  With only 16 heads per workgroup a split's partial output is
+// the end.  When a split has at most kBufs tiles (144 rows: the Pro-shaped
+// decode's splits) every tile has its own LDS buffer and a wavefront issues
+// the DMAs of all its tiles at once, so the split waits for one gather round
+// trip instead of one per tile; longer splits run a two-slot ring per
+// wavefront.  With only 16 heads per workgroup a split's partial output is
 // 16 KB, which keeps the merge traffic small next to the gathered rows; the
 // head groups of one (query, split) run on the same XCD and share its L2.
 //
@@ -37,7 +41,8 @@ namespace {
 
 constexpr int kTR = 16;                      // rows per tile
 constexpr int kTileB = kTR * kRowB;          // 16 KB
-constexpr int kSlots = 2;                    // LDS slots per wavefront
+constexpr int kSlots = 2;                    // LDS slots per wavefront (ring mode)
+constexpr int kBufs = 9;                     // tile buffers in LDS (144 KB)
 constexpr int kMaxRows = 2304;               // rows per split (k + n_win <= 2048 + 256)
 constexpr int kFill = kMaxRows / 256;        // row-source loads per thread
 
@@ -46,8 +51,10 @@ constexpr int kFill = kMaxRows / 256;        // row-source loads per thread
 // 1-D grid: block L runs on XCD L % 8; the n_hg head groups of one (query,
 // split) are blocks L, L + 8, ... so they gather the same rows through one L2.
 __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n_split, int rows_per_split) {
-  // two tile slots per wavefront; reused as the epilogue's staging area
-  __shared__ __attribute__((aligned(1024))) char slots[4][kSlots][kTileB];
+  // tile buffers: tile j of the split in buffer j when the split has at
+  // most kBufs tiles, else buffers 2w, 2w+1 are wavefront w's ring; reused as
+  // the epilogue's staging area
+  __shared__ __attribute__((aligned(1024))) char bufs[kBufs][kTileB];
   // source of each row of the split: >= 0 cache entry, -1 none (masked),
   // <= -2 window ring row (-2 - ring row)
   __shared__ __attribute__((aligned(16))) int rsrc[kMaxRows];
@@ -142,6 +149,9 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
   lds_barrier();  // rsrc ready
 
   const int n_mine = n_tiles > w ? (n_tiles - w + 3) / 4 : 0;  // tiles j = w + 4i
+  const bool all_in = n_tiles <= kBufs;  // every tile in its own buffer
+  // buffer of this wavefront's i-th tile
+  auto buf_of = [&](int i) -> char* { return all_in ? bufs[w + 4 * i] : bufs[kSlots * w + (i & 1)]; };
 
   const Bases bs = lane_bases(li, lg);
   f32x4_t acc[32];
@@ -154,13 +164,13 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
   int dofs[kTR];  // element offset of this lane's 16-byte chunk, per tile row
 #pragma unroll
   for (int r = 0; r < kTR; ++r) dofs[r] = 8 * (l ^ swz(r));
-  auto issue = [&](int i, int sl) {
+  auto issue = [&](int i) {
     const int er = rsrc[(w + 4 * i) * kTR + (l & (kTR - 1))];
     const int row = er >= 0 ? er : (er == -1 ? own : -2 - er);
     const uint16_t* src = (er >= 0 ? kv : win) + (size_t)row * kC;
     const uintptr_t sp = reinterpret_cast<uintptr_t>(src);
     const uint32_t s_lo = (uint32_t)sp, s_hi = (uint32_t)(sp >> 32);
-    const uint32_t dst = lds_addr(slots[w][sl]);
+    const uint32_t dst = lds_addr(buf_of(i));
 #pragma unroll
     for (int r = 0; r < kTR; ++r) {
       // (readlane returns int: widen through uint32_t, no sign extension)
@@ -170,8 +180,8 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
     }
   };
 
-  auto compute = [&](int i, int sl) {
-    const char* T = slots[w][sl];
+  auto compute = [&](int i) {
+    const char* T = buf_of(i);
     // S^T as two interleaved chains (even / odd k steps); fragment reads
     // run one group of four k steps ahead of the products
     f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
@@ -238,30 +248,47 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
     return redo;
   };
 
-  // this wavefront's pipeline: tile i computed while tile i+1 is in flight.
-  // The waits are explicit (the DMAs are the only memory operations in
-  // flight here; the empty asm statements keep LDS reads behind them).
-  // tile i computed while tile i+1 is in flight (explicit waits: the DMAs
-  // are the only memory operations in flight in the loop)
+  // this wavefront's tiles.  All in: every DMA issued up front, tile i
+  // computed once its own DMAs (and the older ones) have landed.  Ring: tile
+  // i computed while tile i+1 is in flight.  The waits are explicit (the
+  // DMAs are the only memory operations in flight here; the empty asm
+  // statements keep LDS reads behind them).
+  static_assert(kBufs / 4 * kTR <= 63 - kTR, "DMAs in flight must fit the vmcnt counter");
   for (;;) {
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     l_lane = 0.f;
-    if (n_mine > 0) issue(0, 0);
-    if (n_mine > 1) issue(1, 1);
     bool redo = false;
-    for (int i = 0; i < n_mine; ++i) {
-      if (i + 1 < n_mine) __builtin_amdgcn_s_waitcnt(wait_vm(kTR));
-      else __builtin_amdgcn_s_waitcnt(wait_vm(0));
-      __asm__ __volatile__("" ::: "memory");
-      redo |= compute(i, i & 1);
-      if (i + 2 < n_mine) {
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this slot's reads are done
+    if (all_in) {
+      for (int i = 0; i < n_mine; ++i) issue(i);
+      for (int i = 0; i < n_mine; ++i) {
+        const int younger = n_mine - 1 - i;  // tiles issued after tile i (at most 2)
+        if (younger >= 2) __builtin_amdgcn_s_waitcnt(wait_vm(2 * kTR));
+        else if (younger == 1) __builtin_amdgcn_s_waitcnt(wait_vm(kTR));
+        else __builtin_amdgcn_s_waitcnt(wait_vm(0));
         __asm__ __volatile__("" ::: "memory");
-        issue(i + 2, i & 1);
+        redo |= compute(i);
+      }
+    } else {
+      if (n_mine > 0) issue(0);
+      if (n_mine > 1) issue(1);
+      for (int i = 0; i < n_mine; ++i) {
+        if (i + 1 < n_mine) __builtin_amdgcn_s_waitcnt(wait_vm(kTR));
+        else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+        __asm__ __volatile__("" ::: "memory");
+        redo |= compute(i);
+        if (i + 2 < n_mine) {
+          __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // this slot's reads are done
+          __asm__ __volatile__("" ::: "memory");
+          issue(i + 2);
+        }
       }
     }
     if (!redo) break;
+    // a redo re-fetches this wavefront's tiles into the same buffers: its own
+    // reads of them are done (LDS operations complete in order)
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __asm__ __volatile__("" ::: "memory");
   }
 
   // combine the four wavefronts' states: per head the max of the reference
@@ -281,7 +308,7 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
   // staging: wavefront v's head row h (512 floats, 2 KB) at
   // red(v) + 2048 h, its 16-byte chunk c at position c ^ h (conflict-free
   // for both access patterns)
-  auto red = [&](int v) -> char* { return &slots[v][0][0]; };
+  auto red = [&](int v) -> char* { return bufs[2 * v]; };  // 32 KB per wavefront
   {
     char* rw = red(w) + li * 2048;
 #pragma unroll

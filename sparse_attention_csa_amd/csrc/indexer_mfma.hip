@@ -72,6 +72,10 @@ CSA_DEV float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); 
 namespace {
 
 constexpr int kD = 128;
+// the fold workgroup stages every source of a block at once when the block
+// has at most kFastFoldM tokens per branch and kFastFoldC coordinates
+constexpr int kFastFoldM = 4;
+constexpr int kFastFoldC = 512;
 
 // Tile geometry.  e4m3: 16 keys x 128 B = 2 KB, read as two 1 KB pieces of
 // 8 keys; bf16: 16 keys x 256 B = 4 KB, four pieces of 4 keys.  In LDS, chunk
@@ -112,12 +116,21 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   const int H = a.H_I;
 
   // query operands and head weights first: small, their loads go out
-  // before the key stream so they do not queue behind it
+  // before the key stream so they do not queue behind it (the fold
+  // workgroup does not scan and skips them)
+  const bool is_fold_wg = fold_mode && blockIdx.x == gridDim.x - 1;
   bf16x8_t qb[HT][4];
   i32x8_t q8[HT];
   float wr[HT][4];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
+    if (is_fold_wg) {
+      q8[ht] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qb[ht][ks] = bf16x8_t{};
+      wr[ht][0] = wr[ht][1] = wr[ht][2] = wr[ht][3] = 0.f;
+      continue;
+    }
     const int h = 16 * ht + li;
     if constexpr (FP8) {
       const uint8_t* q = reinterpret_cast<const uint8_t*>(a.q) + ((size_t)row * H + h) * kD + 16 * lg;
@@ -137,7 +150,8 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   if constexpr (FP8) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
-      qs[ht] = *reinterpret_cast<const float4*>(a.q_scale + (size_t)row * H + 16 * ht + 4 * lg);
+      qs[ht] = is_fold_wg ? make_float4(0.f, 0.f, 0.f, 0.f)
+                          : *reinterpret_cast<const float4*>(a.q_scale + (size_t)row * H + 16 * ht + 4 * lg);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -147,7 +161,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   const int64_t lim = vis_limit(t, a.m, a.vis);
   // fold_mode: the block ending at t completes entry n_have in this step
   const bool fold_now = fold_mode && lim == (int64_t)n_have + 1 && n_have < a.E_cap;
-  const bool fold_wg = fold_mode && blockIdx.x == gridDim.x - 1;
+  const bool fold_wg = is_fold_wg;
   int64_t nv = lim;  // visible entries, including a new one
   {
     const int64_t have = (int64_t)n_have + a.n_add + (fold_now ? 1 : 0);
@@ -321,16 +335,81 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
     }
   }
   if (fold_wg) {
-    // the step's compressor work for this sequence (the scan above was empty)
+    // the step's compressor work for this sequence (the scan above was empty).
+    // First the new token's appends to the tail rings and the window ring:
+    // they need only the step's inputs, and the tail slot they write
+    // (t mod R, with R > 2m) is never a source of the fold.
+    {
+      const int nstr = f.overlap ? 4 : 2;
+      const int slot_t = (int)(t % f.R);
+      const uint16_t* mio = reinterpret_cast<const uint16_t*>(f.streams) + (size_t)b * nstr * f.c;
+      uint16_t* mtl = reinterpret_cast<uint16_t*>(f.tail) + (size_t)b * nstr * f.R * f.c;
+      for (int i = tid; i < nstr * f.c; i += 256) {
+        const int sc = i / f.c, r = i % f.c;
+        mtl[((size_t)sc * f.R + slot_t) * f.c + r] = mio[(size_t)sc * f.c + r];
+      }
+      const uint16_t* iio = reinterpret_cast<const uint16_t*>(f.idx_streams) + (size_t)b * 4 * kD;
+      uint16_t* itl = reinterpret_cast<uint16_t*>(f.idx_tail) + (size_t)b * 4 * f.R * kD;
+      for (int i = tid; i < 4 * kD; i += 256) {
+        const int sc = i / kD, r = i % kD;
+        itl[((size_t)sc * f.R + slot_t) * kD + r] = iio[(size_t)sc * kD + r];
+      }
+      uint16_t* ring = reinterpret_cast<uint16_t*>(f.win_ring) + ((size_t)b * f.n_win + t % f.n_win) * f.c;
+      const uint16_t* xn = reinterpret_cast<const uint16_t*>(f.x_new) + (size_t)b * f.c;
+      for (int i = tid; i < f.c; i += 256) ring[i] = xn[i];
+    }
+  
     Soft* s_part = reinterpret_cast<Soft*>(&s_tr[0][0]);
     float* s_red = reinterpret_cast<float*>(s_part + 4 * 256);
     uint32_t* s_key = reinterpret_cast<uint32_t*>(s_red + 8);  // the stored new key (<= 256 B)
     const int64_t e = n_have;
-    if (fold_now) {
-      // indexer key: fold, quantize, store
-      const bf16* itail = reinterpret_cast<const bf16*>(f.idx_tail) + (size_t)b * 4 * f.R * kD;
-      const bf16* iio = reinterpret_cast<const bf16*>(f.idx_streams) + (size_t)b * 4 * kD;
-      const float iv = fold_job<bf16>(itail, iio, kD, 0, kD, f.m, f.R, t, e, e > 0, f.ibias_a, f.ibias_b, s_part);
+    // the new key's score, as the scan computes it: sum_h w_h q_scale_h
+    // ReLU(q_h . k), times the key scale (wave 0, lane = head; qv_reg holds
+    // the lane's query row when pre, else it is loaded here)
+    auto score_new_key = [&](float ks, const uint4* qv_reg, bool pre) {
+      if (w != 0) return;
+      constexpr int kV = kD * (FP8 ? 1 : 2) / 16;
+      float part = 0.f;
+      if (l < H) {
+        const uint4* qv = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) +
+                                                         ((size_t)row * H + l) * kD * (FP8 ? 1 : 2));
+        const uint4* kv4 = reinterpret_cast<const uint4*>(s_key);
+        uint4 qr[kV];
+#pragma unroll
+        for (int j = 0; j < kV; ++j) qr[j] = pre ? qv_reg[j] : qv[j];
+        float c = 0.f;
+#pragma unroll
+        for (int j = 0; j < kV; ++j) {
+          const uint4 kj = kv4[j];
+          const uint32_t qw[4] = {qr[j].x, qr[j].y, qr[j].z, qr[j].w};
+          const uint32_t kw[4] = {kj.x, kj.y, kj.z, kj.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (FP8) {
+              c += __builtin_amdgcn_cvt_f32_fp8((int)qw[i], 0) * __builtin_amdgcn_cvt_f32_fp8((int)kw[i], 0);
+              c += __builtin_amdgcn_cvt_f32_fp8((int)qw[i], 1) * __builtin_amdgcn_cvt_f32_fp8((int)kw[i], 1);
+              c += __builtin_amdgcn_cvt_f32_fp8((int)qw[i], 2) * __builtin_amdgcn_cvt_f32_fp8((int)kw[i], 2);
+              c += __builtin_amdgcn_cvt_f32_fp8((int)qw[i], 3) * __builtin_amdgcn_cvt_f32_fp8((int)kw[i], 3);
+            } else {
+              c += __uint_as_float(qw[i] << 16) * __uint_as_float(kw[i] << 16);
+              c += __uint_as_float(qw[i] & 0xffff0000u) * __uint_as_float(kw[i] & 0xffff0000u);
+            }
+          }
+        }
+        part = FP8 ? a.w[(size_t)row * H + l] * a.q_scale[(size_t)row * H + l] * relu(c)
+                   : a.w[(size_t)row * H + l] * relu(c);
+      }
+      part = wave_sum(part);
+      if (FP8) part *= ks;
+      if (l == 0) {
+        out[e] = part;
+        s_sc[0] = part;
+        if (use_hist) s_hist[f32_key(part) >> kTopkShift] += 1;
+      }
+    };
+    // the new indexer key (value iv of coordinate tid < kD) to its storage
+    // format, into the cache and s_key; returns its scale (1 for bf16)
+    auto store_key = [&](float iv) -> float {
       const size_t krow = (size_t)b * a.E_cap + e;
       float ks = 1.f;
       if constexpr (FP8) {
@@ -354,48 +433,143 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
         }
       }
       __syncthreads();
-      // its score, as the scan computes it: sum_h w_h q_scale_h ReLU(q_h . k), times the key scale
-      if (w == 0) {
-        float part = 0.f;
-        if (l < H) {
-          // lane = head: its query row and the key as 16-byte vectors
-          constexpr int kV = kD * (FP8 ? 1 : 2) / 16;
-          const uint4* qv = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) +
-                                                           ((size_t)row * H + l) * kD * (FP8 ? 1 : 2));
-          const uint4* kv4 = reinterpret_cast<const uint4*>(s_key);
-          uint4 qr[kV];
+      return ks;
+    };
+    if (fold_now && f.m <= kFastFoldM && f.c <= kFastFoldC) {
+      // Every source of the block, for the main entry and the indexer key,
+      // with its positional bias, staged in LDS by one round of loads
+      // (kFastFoldM sources per branch, kFastFoldC coordinates at most: 24
+      // KB in the transpose buffer, the main entry's biases (16 KB) in the
+      // score buffer, of which this workgroup needs only its first slot, and
+      // only after the fold), and the query rows the new key's score needs
+      // loaded with them; then each thread folds whole coordinates.
+      const int m = f.m, c = f.c, R = f.R;
+      const bool use_bm = f.overlap && e > 0;  // the main entry's branch b (the previous block)
+      const bool use_bi = e > 0;               // the indexer key always overlaps
+      const int Sm = use_bm ? 2 * m : m, Si = use_bi ? 2 * m : m;
+      constexpr int kS = 2 * kFastFoldM;
+      static_assert(kS * kFastFoldC * 2 * 2 + kS * kD * 8 + 288 <= 4 * kU * G::kTileB, "fold staging fits");
+      static_assert(kS * kFastFoldC <= kTopkFuseCap, "main biases fit the score buffer");
+      uint16_t* mz = reinterpret_cast<uint16_t*>(&s_tr[0][0]);  // [kS][kFastFoldC] logits
+      uint16_t* mx = mz + kS * kFastFoldC;                      // [kS][kFastFoldC] contents
+      float* mb = s_sc;                                         // [kS][kFastFoldC] biases
+      uint16_t* iz = mx + kS * kFastFoldC;                      // [kS][kD]
+      uint16_t* ix = iz + kS * kD;
+      float* ib = reinterpret_cast<float*>(ix + kS * kD);
+      s_red = ib + kS * kD;
+      s_key = reinterpret_cast<uint32_t*>(s_red + 8);
+      const int mstr = f.overlap ? 4 : 2;
+      const uint16_t* mtail = reinterpret_cast<const uint16_t*>(f.tail) + (size_t)b * mstr * R * c;
+      const uint16_t* mio = reinterpret_cast<const uint16_t*>(f.streams) + (size_t)b * mstr * c;
+      const uint16_t* itail = reinterpret_cast<const uint16_t*>(f.idx_tail) + (size_t)b * 4 * R * kD;
+      const uint16_t* iio = reinterpret_cast<const uint16_t*>(f.idx_streams) + (size_t)b * 4 * kD;
+      // row of source j of a block's fold in stream (0: content, 1: logit):
+      // j < m is token e m + j of branch a, else token (e-1) m + j - m of
+      // branch b; the new token t comes from the step's inputs
+      auto src = [&](const uint16_t* tail, const uint16_t* io, int width, int j, int logit) -> const uint16_t* {
+        const int stream = (j < m ? 0 : 2) + logit;
+        const int64_t tok = j < m ? e * m + j : (e - 1) * m + (j - m);
+        if (tok == t) return io + (size_t)stream * width;
+        return tail + ((size_t)stream * R + (size_t)(tok % R)) * width;
+      };
+      auto bias = [&](const float* ba, const float* bb, int width, int j) -> const float* {
+        const float* p = j < m ? ba : bb;
+        return p ? p + (size_t)(j < m ? j : j - m) * width : nullptr;
+      };
+      constexpr int kMC = kS * kFastFoldC / 8 / 256;  // 16-byte chunks per thread (logits, contents)
+      constexpr int kMB = kS * kFastFoldC / 4 / 256;  // (biases)
+      uint4 rz[kMC], rx[kMC], rb[kMB], riz, rix, rib;
+      const int cpr = c / 8, bpr = c / 4;  // 16-byte chunks per main row (bf16, f32)
 #pragma unroll
-          for (int j = 0; j < kV; ++j) qr[j] = qv[j];
-          float c = 0.f;
-#pragma unroll
-          for (int j = 0; j < kV; ++j) {
-            const uint4 kj = kv4[j];
-            const uint32_t qw[4] = {qr[j].x, qr[j].y, qr[j].z, qr[j].w};
-            const uint32_t kw[4] = {kj.x, kj.y, kj.z, kj.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if constexpr (FP8) {
-                c += __builtin_amdgcn_cvt_f32_fp8((int)qw[i], 0) * __builtin_amdgcn_cvt_f32_fp8((int)kw[i], 0);
-                c += __builtin_amdgcn_cvt_f32_fp8((int)qw[i], 1) * __builtin_amdgcn_cvt_f32_fp8((int)kw[i], 1);
-                c += __builtin_amdgcn_cvt_f32_fp8((int)qw[i], 2) * __builtin_amdgcn_cvt_f32_fp8((int)kw[i], 2);
-                c += __builtin_amdgcn_cvt_f32_fp8((int)qw[i], 3) * __builtin_amdgcn_cvt_f32_fp8((int)kw[i], 3);
-              } else {
-                c += __uint_as_float(qw[i] << 16) * __uint_as_float(kw[i] << 16);
-                c += __uint_as_float(qw[i] & 0xffff0000u) * __uint_as_float(kw[i] & 0xffff0000u);
-              }
-            }
-          }
-          part = FP8 ? a.w[(size_t)row * H + l] * a.q_scale[(size_t)row * H + l] * relu(c)
-                     : a.w[(size_t)row * H + l] * relu(c);
-        }
-        part = wave_sum(part);
-        if (FP8) part *= ks;
-        if (l == 0) {
-          out[e] = part;
-          s_sc[0] = part;
-          if (use_hist) s_hist[f32_key(part) >> kTopkShift] += 1;
+      for (int u = 0; u < kMC; ++u) {
+        const int i = tid + 256 * u, j = i / cpr, cc = i % cpr;
+        rz[u] = rx[u] = uint4{0, 0, 0, 0};
+        if (j < Sm) {
+          rz[u] = *reinterpret_cast<const uint4*>(src(mtail, mio, c, j, 1) + 8 * cc);
+          rx[u] = *reinterpret_cast<const uint4*>(src(mtail, mio, c, j, 0) + 8 * cc);
         }
       }
+#pragma unroll
+      for (int u = 0; u < kMB; ++u) {
+        const int i = tid + 256 * u, j = i / bpr, cc = i % bpr;
+        const float* bp = j < Sm ? bias(f.bias_a, f.bias_b, c, j) : nullptr;
+        rb[u] = bp ? *reinterpret_cast<const uint4*>(bp + 4 * cc) : uint4{0, 0, 0, 0};
+      }
+      {
+        const int j = tid / (kD / 8), cc = tid % (kD / 8);
+        riz = rix = uint4{0, 0, 0, 0};
+        if (j < Si) {
+          riz = *reinterpret_cast<const uint4*>(src(itail, iio, kD, j, 1) + 8 * cc);
+          rix = *reinterpret_cast<const uint4*>(src(itail, iio, kD, j, 0) + 8 * cc);
+        }
+        const int jb = tid / (kD / 4), cb = tid % (kD / 4);
+        const float* bp = jb < Si ? bias(f.ibias_a, f.ibias_b, kD, jb) : nullptr;
+        rib = bp ? *reinterpret_cast<const uint4*>(bp + 4 * cb) : uint4{0, 0, 0, 0};
+      }
+      constexpr int kV = kD * (FP8 ? 1 : 2) / 16;
+      uint4 qreg[kV];
+      if (w == 0 && l < H) {
+        const uint4* qv = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) +
+                                                         ((size_t)row * H + l) * kD * (FP8 ? 1 : 2));
+#pragma unroll
+        for (int j = 0; j < kV; ++j) qreg[j] = qv[j];
+      }
+      // to LDS (row j at j * width)
+#pragma unroll
+      for (int u = 0; u < kMC; ++u) {
+        const int i = tid + 256 * u, j = i / cpr, cc = i % cpr;
+        if (j < Sm) {
+          *reinterpret_cast<uint4*>(mz + j * kFastFoldC + 8 * cc) = rz[u];
+          *reinterpret_cast<uint4*>(mx + j * kFastFoldC + 8 * cc) = rx[u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kMB; ++u) {
+        const int i = tid + 256 * u, j = i / bpr, cc = i % bpr;
+        if (j < Sm) *reinterpret_cast<uint4*>(mb + j * kFastFoldC + 4 * cc) = rb[u];
+      }
+      {
+        const int j = tid / (kD / 8), cc = tid % (kD / 8);
+        if (j < Si) {
+          *reinterpret_cast<uint4*>(iz + j * kD + 8 * cc) = riz;
+          *reinterpret_cast<uint4*>(ix + j * kD + 8 * cc) = rix;
+        }
+        const int jb = tid / (kD / 4), cb = tid % (kD / 4);
+        if (jb < Si) *reinterpret_cast<uint4*>(ib + jb * kD + 4 * cb) = rib;
+      }
+      __syncthreads();
+      // one coordinate per thread: a softmax over the sources' logits
+      // (+ biases) weights their contents
+      auto fold_coord = [&](const uint16_t* zr, const uint16_t* xr, const float* br, int width, int S, int r) {
+        float mxv = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kS; ++j)
+          if (j < S) mxv = fmaxf(mxv, bf16_to_f32(zr[j * width + r]) + br[j * width + r]);
+        float lsum = 0.f, acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < kS; ++j) {
+          if (j < S) {
+            const float ex = __expf(bf16_to_f32(zr[j * width + r]) + br[j * width + r] - mxv);
+            lsum += ex;
+            acc += ex * bf16_to_f32(xr[j * width + r]);
+          }
+        }
+        return acc / lsum;
+      };
+      const float iv = tid < kD ? fold_coord(iz, ix, ib, kD, Si, tid) : 0.f;
+      const float ks = store_key(iv);
+      for (int r = tid; r < c; r += 256)
+        reinterpret_cast<uint16_t*>(f.kv_cache)[((size_t)b * a.E_cap + e) * c + r] =
+            f32_to_bf16(fold_coord(mz, mx, mb, kFastFoldC, Sm, r));
+      __syncthreads();  // every read of the biases in s_sc is done
+      score_new_key(ks, qreg, true);
+    } else if (fold_now) {
+      // indexer key: fold, quantize, store
+      const bf16* itail = reinterpret_cast<const bf16*>(f.idx_tail) + (size_t)b * 4 * f.R * kD;
+      const bf16* iio = reinterpret_cast<const bf16*>(f.idx_streams) + (size_t)b * 4 * kD;
+      const float iv = fold_job<bf16>(itail, iio, kD, 0, kD, f.m, f.R, t, e, e > 0, f.ibias_a, f.ibias_b, s_part);
+      const float ks = store_key(iv);
+      score_new_key(ks, nullptr, false);
       // main entry: two halves of the coordinates
       const bf16* mtail = reinterpret_cast<const bf16*>(f.tail) + (size_t)b * (f.overlap ? 4 : 2) * f.R * f.c;
       const bf16* mio = reinterpret_cast<const bf16*>(f.streams) + (size_t)b * (f.overlap ? 4 : 2) * f.c;
@@ -405,26 +579,6 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
                                        f.bias_b, s_part);
         if (tid < W) reinterpret_cast<uint16_t*>(f.kv_cache)[((size_t)b * a.E_cap + e) * f.c + r0 + tid] = f32_to_bf16(v);
       }
-    }
-    // append the new token: tail rings and window ring
-    {
-      const int nstr = f.overlap ? 4 : 2;
-      const int slot_t = (int)(t % f.R);
-      const uint16_t* mio = reinterpret_cast<const uint16_t*>(f.streams) + (size_t)b * nstr * f.c;
-      uint16_t* mtl = reinterpret_cast<uint16_t*>(f.tail) + (size_t)b * nstr * f.R * f.c;
-      for (int i = tid; i < nstr * f.c; i += 256) {
-        const int sc = i / f.c, r = i % f.c;
-        mtl[((size_t)sc * f.R + slot_t) * f.c + r] = mio[(size_t)sc * f.c + r];
-      }
-      const uint16_t* iio = reinterpret_cast<const uint16_t*>(f.idx_streams) + (size_t)b * 4 * kD;
-      uint16_t* itl = reinterpret_cast<uint16_t*>(f.idx_tail) + (size_t)b * 4 * f.R * kD;
-      for (int i = tid; i < 4 * kD; i += 256) {
-        const int sc = i / kD, r = i % kD;
-        itl[((size_t)sc * f.R + slot_t) * kD + r] = iio[(size_t)sc * kD + r];
-      }
-      uint16_t* ring = reinterpret_cast<uint16_t*>(f.win_ring) + ((size_t)b * f.n_win + t % f.n_win) * f.c;
-      const uint16_t* xn = reinterpret_cast<const uint16_t*>(f.x_new) + (size_t)b * f.c;
-      for (int i = tid; i < f.c; i += 256) ring[i] = xn[i];
     }
   }
   if (use_hist) {
