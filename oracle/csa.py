@@ -25,7 +25,7 @@ import math
 
 import numpy as np
 
-from .formats import Stored, round_to_bf16
+from .formats import FP8_DIMS, Stored, mxfp4_quantize, round_to_bf16
 
 VIS_PRIOR_BLOCKS = 0  # entry s visible to a query at t iff s < floor(t / m)
 VIS_COMPLETED = 1  # entry s visible iff s < floor((t + 1) / m)
@@ -263,7 +263,7 @@ def attend_partial(q, rows, scale):
 # ---------------------------------------------------------------------------
 
 def csa_query(q, q_idx, w_idx, t, kv: Stored, keys: Stored, n_entries, win_rows,
-              sink, m, k, n_win, scale, vis=VIS_PRIOR_BLOCKS, selected=None):
+              sink, m, k, n_win, scale, vis=VIS_PRIOR_BLOCKS, selected=None, score_dtype="f32"):
     """CSA for one query at position t.
 
     Score the visible compressed entries with the indexer, keep the top-k,
@@ -271,12 +271,17 @@ def csa_query(q, q_idx, w_idx, t, kv: Stored, keys: Stored, n_entries, win_rows,
     ("2026 DeepSeek-V4" note, "Key design 1"; "DeepSeek-V4" book ch. 6).
     ``win_rows(positions)`` returns the raw window rows.  ``selected`` may
     override the top-k set (used to evaluate attention on an equally valid
-    set when two scores tie within rounding).
+    set when two scores tie within rounding).  ``score_dtype="bf16"`` rounds
+    the index scores to bfloat16 before the selection ("DeepSeek-V4" book
+    ch. 16 "BF16 index scores"); ties, now frequent, still go to the lower
+    entry id, and the rounded scores are returned.
 
     Returns (o [H][c], lse [H], selected ids, scores of the visible entries).
     """
     n_vis = visible_entries(t, m, n_entries, vis)
     scores = index_scores_stored(q_idx, w_idx, keys, n_vis)
+    if score_dtype == "bf16":
+        scores = round_to_bf16(scores)
     sel = topk_select(scores, k) if selected is None else np.asarray(selected)
     rows = np.concatenate([kv.rows(sel), win_rows(window_positions(t, n_win))], axis=0)
     o, lse = attend(q, rows, sink, scale)
@@ -300,13 +305,20 @@ def hca_query(q, t, kv: Stored, n_entries, win_rows, sink, m, n_win, scale,
 # ---------------------------------------------------------------------------
 
 def store_as(x, kind):
-    """Value of x after storage in ``kind`` ("f32" or "bf16"), rounded to
-    nearest-even once."""
+    """Value of x after storage in ``kind``: "f32" or "bf16" (rounded to
+    nearest-even once), "mxfp4" (OCP MX FP4, blocks of 32 along the last
+    axis) or "fp8bf16" (the 576-byte entry: the first 448 coordinates e4m3
+    with one scale per vector, the last 64 bf16)."""
     x = np.asarray(x, dtype=np.float64)
     if kind == "bf16":
         return round_to_bf16(x)
     if kind == "f32":
         return x.astype(np.float32).astype(np.float64)
+    if kind == "mxfp4":
+        return mxfp4_quantize(x)[2]
+    if kind == "fp8bf16":
+        head = e4m3_quantize_rows(x[..., :FP8_DIMS])[0]
+        return np.concatenate([head, round_to_bf16(x[..., FP8_DIMS:])], axis=-1)
     raise ValueError(kind)
 
 

@@ -27,7 +27,7 @@ class CacheView:
     def __init__(self, base: Stored, n_base, extra=None):
         self.base = base
         self.n_base = int(n_base)
-        self.extra = np.zeros((0, base.shape[-1])) if extra is None else np.asarray(extra)
+        self.extra = np.zeros((0, base.width)) if extra is None else np.asarray(extra)
 
     def __len__(self):
         return self.n_base + len(self.extra)
@@ -36,7 +36,7 @@ class CacheView:
         if isinstance(idx, slice):
             idx = np.arange(*idx.indices(len(self)))
         idx = np.asarray(idx, dtype=np.int64)
-        out = np.empty((idx.shape[0], self.base.shape[-1]))
+        out = np.empty((idx.shape[0], self.base.width))
         lo = idx < self.n_base
         if lo.any():
             out[lo] = self.base.rows(idx[lo])
@@ -49,6 +49,14 @@ def _store_key(x, kind):
     if kind == "e4m3":
         return csa.e4m3_quantize_rows(x[None, :])[0][0]
     return csa.store_as(x, kind)
+
+
+def _act(g):
+    """Storage kind of the activations (token streams, window rows,
+    queries): that of the cache, except under the mixed FP8 + BF16 cache,
+    whose activations stay bf16."""
+    k = g["kv_dtype"]
+    return "bf16" if k == "fp8bf16" else k
 
 
 def _dec(x, kind, scale=None):
@@ -71,6 +79,7 @@ def decode_step(case, b, selected=None):
     t = int(g["pos"][b])
     m, c = g["m"], g["c"]
     kvk, idk = g["kv_dtype"], g["idx_dtype"]
+    act = _act(g)
     n_have = int(g["n_entries"][b])
     need = t // m if g["vis"] == csa.VIS_PRIOR_BLOCKS else (t + 1) // m
     p0 = int(g["tail_pos0"][b])
@@ -84,10 +93,10 @@ def decode_step(case, b, selected=None):
     folded_kv, folded_idx, folded_idx_raw = [], [], []
     if need > n_have:
         overlap = g["overlap"]
-        s = {n: stream(n, kvk) for n in (("ca", "za", "cb", "zb") if overlap else ("ca", "za"))}
+        s = {n: stream(n, act) for n in (("ca", "za", "cb", "zb") if overlap else ("ca", "za"))}
         si = {}
         if g["kind"] == "csa":
-            si = {n: stream("i" + n, kvk) for n in ("ca", "za", "cb", "zb")}
+            si = {n: stream("i" + n, act) for n in ("ca", "za", "cb", "zb")}
         for e in range(n_have, need):
             a = slice(m * e - p0, m * e + m - p0)
             if a.start < 0 or a.stop > t - p0 + 1:
@@ -111,18 +120,18 @@ def decode_step(case, b, selected=None):
                 folded_idx.append(_store_key(ik, idk))
                 folded_idx_raw.append(ik)
     n_total = max(n_have, need)
-    kv = CacheView(Stored(g["kv_cache"][b], kvk), n_have,
-                   np.array(folded_kv) if folded_kv else None)
+    kv = CacheView(Stored(g["kv_cache"][b], kvk, None if g.get("kv_scale") is None else g["kv_scale"][b]),
+                   n_have, np.array(folded_kv) if folded_kv else None)
 
-    win_hist = _dec(g["win_hist"][b], kvk)  # positions t-(n_win-1) .. t-1
-    x_new = _dec(g["x_new"][b][None], kvk)
+    win_hist = _dec(g["win_hist"][b], act)  # positions t-(n_win-1) .. t-1
+    x_new = _dec(g["x_new"][b][None], act)
     win_all = np.concatenate([win_hist, x_new], axis=0)
     wp0 = t - win_hist.shape[0]
 
     def win_rows(pos):
         return win_all[np.asarray(pos) - wp0]
 
-    q = _dec(g["q"][b], kvk)
+    q = _dec(g["q"][b], act)
     sink = None if g["sink"] is None else np.asarray(g["sink"], np.float64)
     # (folded_idx_raw: the indexer keys before rounding to storage, for tests
     # that must know which stored codes a rounding decision settles)
@@ -135,7 +144,7 @@ def decode_step(case, b, selected=None):
         w = np.asarray(g["w_idx"][b], np.float64)
         o, lse, sel, scores = csa.csa_query(q, qi, w, t, kv, keys, n_total, win_rows, sink,
                                             m, g["k"], g["n_win"], g["scale"], g["vis"],
-                                            selected=selected)
+                                            selected=selected, score_dtype=g.get("score_dtype", "f32"))
         out.update(o=o, lse=lse, sel=sel, scores=scores)
     else:
         o, lse = csa.hca_query(q, t, kv, n_total, win_rows, sink, m, g["n_win"], g["scale"],
@@ -155,7 +164,8 @@ def prefill_entries(case, b, raw=False):
     g = case
     m = g["m"]
     kvk, idk = g["kv_dtype"], g["idx_dtype"]
-    d = lambda n: _dec(g[n][b], kvk)  # noqa: E731
+    act = _act(g)
+    d = lambda n: _dec(g[n][b], act)  # noqa: E731
     if g["overlap"]:
         first = int(g["pos0"]) == 0
         ent = csa.compress(d("ca"), d("za"), m, g["bias_a"], d("cb"), d("zb"), g["bias_b"],
@@ -185,15 +195,17 @@ def prefill_query(case, b, i, kv_new, idx_new, selected=None):
     kvk, idk = g["kv_dtype"], g["idx_dtype"]
     t = int(g["pos0"]) + i
     n_have = int(g["n_entries"][b])
-    kv = CacheView(Stored(g["kv_cache"][b], kvk), n_have, kv_new)
+    kv = CacheView(Stored(g["kv_cache"][b], kvk, None if g.get("kv_scale") is None else g["kv_scale"][b]),
+                   n_have, kv_new)
     n_total = n_have + len(kv_new)
     wp0 = int(g["pos0"]) - (g["n_win"] - 1)
-    wstore = Stored(g["win"][b], kvk)
+    act = _act(g)
+    wstore = Stored(g["win"][b], act)
 
     def win_rows(pos):
         return wstore.rows(np.asarray(pos) - wp0)
 
-    q = _dec(g["q"][b][i], kvk)
+    q = _dec(g["q"][b][i], act)
     sink = None if g["sink"] is None else np.asarray(g["sink"], np.float64)
     if g["kind"] == "csa":
         keys = CacheView(Stored(g["idx_cache"][b], idk,
@@ -204,7 +216,7 @@ def prefill_query(case, b, i, kv_new, idx_new, selected=None):
         w = np.asarray(g["w_idx"][b][i], np.float64)
         o, lse, sel, scores = csa.csa_query(q, qi, w, t, kv, keys, n_total, win_rows, sink,
                                             m, g["k"], g["n_win"], g["scale"], g["vis"],
-                                            selected=selected)
+                                            selected=selected, score_dtype=g.get("score_dtype", "f32"))
         return {"o": o, "lse": lse, "sel": sel, "scores": scores}
     o, lse = csa.hca_query(q, t, kv, n_total, win_rows, sink, m, g["n_win"], g["scale"],
                            g["vis"])

@@ -34,6 +34,18 @@ def e4m3_codes_of(rows):
     return codes.view(torch.uint8).numpy(), scale
 
 
+def mxfp4_codes_of(rows):
+    """(packed codes, E8M0 scales) of float64 rows that already are MXFP4
+    values (E2M1 values times a power-of-two scale per block of 32, as the
+    oracle's quantiser leaves them): re-encoding them is exact."""
+    import workloads
+    rows = np.asarray(rows, np.float64)
+    packed, scales = workloads.gen.mxfp4_rows(rows.astype(np.float32))
+    from oracle.formats import mxfp4_decode
+    assert np.array_equal(mxfp4_decode(packed, scales), rows), "row is not an MXFP4 row"
+    return packed, scales
+
+
 def prefix_case(pre, T):
     """The same prefill workload cut to its first T chunk tokens."""
     g = dict(pre)
@@ -59,6 +71,7 @@ def decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv=(), extra_idx=
     E_cap = max(pre["E_cap"], n_have + 1)
     g = {k: pre[k] for k in ("kind", "H", "c", "m", "n_win", "overlap", "vis", "scale",
                              "kv_dtype", "k", "idx_dtype", "sink", "bias_a", "bias_b")}
+    g["score_dtype"] = pre.get("score_dtype", "f32")
     g.update(B=1, E_cap=E_cap)
     g["pos"] = np.array([t], dtype=np.int64)
     g["n_entries"] = np.array([n_have], dtype=np.int32)
@@ -83,7 +96,7 @@ def decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv=(), extra_idx=
     if pre["kind"] == "csa":
         d_I = pre["d_I"]
         g.update(H_I=pre["H_I"], d_I=d_I, ibias_a=pre["ibias_a"], ibias_b=pre["ibias_b"])
-        ik = np.zeros((1, E_cap, d_I), dtype=pre["idx_cache"].dtype)
+        ik = np.zeros((1, E_cap, pre["idx_cache"].shape[-1]), dtype=pre["idx_cache"].dtype)
         ik[0, :n_old] = pre["idx_cache"][b, :n_old]
         idx_rows = list(idx_new) + list(extra_idx)
         g["idx_scale"] = None
@@ -92,6 +105,12 @@ def decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv=(), extra_idx=
             sc[0, :n_old] = pre["idx_scale"][b, :n_old]
             if idx_rows:
                 ik[0, n_old:n_have], sc[0, n_old:n_have] = e4m3_codes_of(np.array(idx_rows))
+            g["idx_scale"] = sc
+        elif pre["idx_dtype"] == "mxfp4":
+            sc = np.zeros((1, E_cap, d_I // 32), np.uint8)
+            sc[0, :n_old] = pre["idx_scale"][b, :n_old]
+            if idx_rows:
+                ik[0, n_old:n_have], sc[0, n_old:n_have] = mxfp4_codes_of(np.array(idx_rows))
             g["idx_scale"] = sc
         elif idx_rows:
             ik[0, n_old:n_have] = _bits(np.array(idx_rows), pre["idx_dtype"])

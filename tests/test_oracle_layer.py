@@ -47,6 +47,16 @@ def test_continuation_csa_e4m3_indexer_second_sequence():
     _continuation(a, 32, 40, b=1)
 
 
+def test_continuation_csa_mxfp4_indexer_bf16_scores():
+    """The pages' FP4 indexer: keys the layer produces are quantised to
+    MXFP4 and re-encoded into the decode step's cache; selection on bf16
+    index scores."""
+    a, _ = workloads.flash_prefill(seed=24, B=1, T=40, n0=64, H=3, c=16, H_I=2, d_I=64, k=6,
+                                   idx_dtype="mxfp4")
+    a["score_dtype"] = "bf16"
+    _continuation(a, 32, 40)
+
+
 def test_continuation_hca():
     _, h = workloads.flash_prefill(seed=22, T=512, n0=256, H=2, c=8, m_hca=128, k=4, H_I=2,
                                    d_I=8)

@@ -56,6 +56,42 @@ def e4m3_rows(x):
     return codes, scale
 
 
+def mxfp4_rows(x):
+    """float32 [..., d] (d a multiple of 32) -> (packed E2M1 codes [..., d/2]
+    uint8, E8M0 block scales [..., d/32] uint8), OCP MX rules: per block of
+    32 the scale is 2**(floor(log2 max|v|) - 2), elements v / scale rounded
+    to the nearest E2M1 value (ties to the even code), saturating at 6;
+    element 2j in the low nibble of byte j."""
+    x = np.asarray(x, dtype=np.float64)
+    blk = x.reshape(x.shape[:-1] + (-1, 32))
+    amax = np.abs(blk).max(axis=-1)
+    e = np.floor(np.log2(np.where(amax > 0, amax, 1.0))).astype(np.int64)
+    code = np.where(amax > 0, np.clip(e - 2 + 127, 0, 254), 0).astype(np.uint8)
+    y = blk / np.ldexp(1.0, code.astype(np.int64) - 127)[..., None]
+    grid = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    a = np.minimum(np.abs(y), 6.0)
+    # nearest grid value; at a midpoint the even code
+    idx = np.clip(np.searchsorted(grid, a), 1, 7)
+    lo, hi = grid[idx - 1], grid[idx]
+    up = (a - lo > hi - a) | ((a - lo == hi - a) & ((idx % 2) == 0))
+    mag = np.where(up, idx, idx - 1).astype(np.uint8)
+    codes = np.where(np.signbit(y) & (mag > 0), mag | 8, mag).astype(np.uint8).reshape(x.shape)
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8), code
+
+
+def fp8bf16_rows(x):
+    """float32 [..., 512] -> (576-byte rows: the first 448 values as e4m3fn
+    codes, the last 64 as little-endian bf16; float32 scale per row for the
+    e4m3 part, max|v| / 448)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    codes, scale = e4m3_rows(x[..., :448])
+    bits = bf16_bits(x[..., 448:])
+    out = np.empty(x.shape[:-1] + (576,), np.uint8)
+    out[..., :448] = codes
+    out[..., 448:] = bits.view(np.uint8).reshape(x.shape[:-1] + (128,))
+    return out, scale
+
+
 def _normal(rng, shape, std=1.0):
     return (rng.standard_normal(shape, dtype=np.float32) * np.float32(std)).astype(np.float32)
 
@@ -189,32 +225,41 @@ def flash_csa_decode(seed=1, B=8, n=131072, H=64, c=512, H_I=64, d_I=128, k=512,
 
 
 def pro_csa_decode(seed=3, B=4, n=1 << 20, H=128, c=512, H_I=64, d_I=128, k=1024, n_win=128, m=4,
-                   nu=3.0, pos_off=0):
+                   nu=3.0, pos_off=0, idx_dtype="e4m3", score_dtype="f32"):
     """Pro-shaped CSA decode: bf16 KV, fp8 e4m3 indexer queries and keys.
 
     Indexer keys K[s] = |T_s| z_s with T_s ~ Student-t(nu) and z_s ~ N(0, I),
     which makes the index scores heavy-tailed (the score is positively
     homogeneous in K); keys and queries are stored as e4m3 with one scale per
-    vector (per entry for keys, per head for queries).
+    vector (per entry for keys, per head for queries).  idx_dtype="mxfp4"
+    stores them as OCP MXFP4 instead (E2M1 with one E8M0 scale per block of
+    32: the pages' FP4 indexer path), drawn from the same values;
+    score_dtype="bf16" selects on bf16-rounded index scores.
     """
     rng = _rng(seed)
     g = _decode_common(rng, "csa", B, n, H, c, m, n_win, True, "bf16", pos_off)
     g["name"] = CONFIG_NAMES[4]
-    _indexer_state(rng, g, H_I, d_I, k, "e4m3")
+    _indexer_state(rng, g, H_I, d_I, k, idx_dtype)
+    g["score_dtype"] = score_dtype
     E = g["E_cap"]
+    enc = e4m3_rows if idx_dtype == "e4m3" else mxfp4_rows
     qi = _normal(rng, (B, H_I, d_I))
-    g["q_idx"], g["q_scale"] = e4m3_rows(qi)
-    codes = np.empty((B, E, d_I), dtype=np.uint8)
-    scales = np.empty((B, E), dtype=np.float32)
+    g["q_idx"], g["q_scale"] = enc(qi)
+    if idx_dtype == "e4m3":
+        codes = np.empty((B, E, d_I), dtype=np.uint8)
+        scales = np.empty((B, E), dtype=np.float32)
+    else:
+        codes = np.empty((B, E, d_I // 2), dtype=np.uint8)
+        scales = np.empty((B, E, d_I // 32), dtype=np.uint8)
     for b in range(B):
         for s0 in range(0, E, 65536):
             s1 = min(E, s0 + 65536)
             t = np.abs(rng.standard_t(nu, size=s1 - s0)).astype(np.float32)
             z = _normal(rng, (s1 - s0, d_I))
-            codes[b, s0:s1], scales[b, s0:s1] = e4m3_rows(t[:, None] * z)
+            codes[b, s0:s1], scales[b, s0:s1] = enc(t[:, None] * z)
     if pos_off == 0:
         codes[:, E - 1] = 0
-        scales[:, E - 1] = 1
+        scales[:, E - 1] = 1 if idx_dtype == "e4m3" else 0
     g["idx_cache"], g["idx_scale"] = codes, scales
     return g
 
@@ -263,6 +308,11 @@ def _prefill_case(rng, kind, B, T, n0, H, c, m, n_win, overlap, k=None, H_I=None
             isc = np.ones((B, E_cap), dtype=np.float32)
             ik[:, :E0], isc[:, :E0] = e4m3_rows(_normal(rng, (B, E0, d_I)))
             g["idx_scale"] = isc
+        elif idx_dtype == "mxfp4":
+            ik = np.zeros((B, E_cap, d_I // 2), dtype=np.uint8)
+            isc = np.zeros((B, E_cap, d_I // 32), dtype=np.uint8)
+            ik[:, :E0], isc[:, :E0] = mxfp4_rows(_normal(rng, (B, E0, d_I)))
+            g["idx_scale"] = isc
         else:
             ik = np.zeros((B, E_cap, d_I), dtype=np.uint16)
             ik[:, :E0] = _normal_bf16(rng, (B, E0, d_I))
@@ -275,6 +325,8 @@ def _prefill_case(rng, kind, B, T, n0, H, c, m, n_win, overlap, k=None, H_I=None
         g["ibias_b"] = _normal(rng, (m, d_I))
         if idx_dtype == "e4m3":
             g["q_idx"], g["q_scale"] = e4m3_rows(_normal(rng, (B, T, H_I, d_I)))
+        elif idx_dtype == "mxfp4":
+            g["q_idx"], g["q_scale"] = mxfp4_rows(_normal(rng, (B, T, H_I, d_I)))
         else:
             g["q_idx"] = _normal_bf16(rng, (B, T, H_I, d_I))
         g["w_idx"] = _normal(rng, (B, T, H_I))
