@@ -15,7 +15,7 @@ steps, outside the timed events) and cycles through --rotate independent copies
 of the state so that the working set exceeds the 256 MiB MALL.
 
 Prints one JSON line.  Other workloads: --workload flash_csa_128k |
-flash_hca_1m | pro_csa_1m | prefill.
+flash_hca_1m | pro_csa_1m | pro_csa_1m_mxfp4 | prefill.
 """
 
 import argparse
@@ -45,6 +45,9 @@ def build_cases(name):
         return [("flash_hca_1m", workloads.flash_hca_decode())]
     if name == "pro_csa_1m":
         return [("pro_csa_1m", workloads.pro_csa_decode())]
+    if name == "pro_csa_1m_mxfp4":
+        # the pages' FP4 indexer path: MXFP4 queries and keys, bf16 scores
+        return [("pro_csa_1m_mxfp4", workloads.pro_csa_decode(idx_dtype="mxfp4", score_dtype="bf16"))]
     if name == "prefill":
         a, h = workloads.flash_prefill()
         return [("prefill_csa", a), ("prefill_hca", h)]
@@ -428,10 +431,12 @@ def main():
     torch.cuda.empty_cache()
 
     # the other configurations, timed in the same run: the Flash-shaped CSA
-    # decode at 128K context and the hybrid prefill chunk
+    # decode at 128K context, the Pro CSA layer with the FP4 indexer and
+    # bf16 scores, and the hybrid prefill chunk
     extra = {}
     if args.workload == "decode_1m" and not args.no_extra:
         for wl, steps, warm in (("flash_csa_128k", args.steps, args.warmup),
+                                ("pro_csa_1m_mxfp4", args.steps, args.warmup),
                                 ("prefill", max(3, min(args.steps, 5)), 1)):
             t1 = time.time()
             c2 = build_cases(wl)

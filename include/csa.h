@@ -55,7 +55,12 @@ typedef enum {
 typedef enum {
   CSA_F32 = 0,  /* IEEE binary32                                            */
   CSA_BF16 = 1, /* bfloat16                                                 */
-  CSA_E4M3 = 2  /* OCP FP8 E4M3FN, one float32 scale per vector (v = q * s) */
+  CSA_E4M3 = 2, /* OCP FP8 E4M3FN, one float32 scale per vector (v = q * s) */
+  CSA_MXFP4 = 3 /* OCP MX FP4: E2M1 values, two per byte (element 2j in the
+                   low nibble of byte j), one E8M0 scale byte per block of 32
+                   consecutive values (v = e2m1 * 2^(code - 127)); [book]
+                   ch. 16 "Why use fine-grained scales?", ch. 8: a 128-dim
+                   indexer key is 64 bytes plus four scale bytes            */
 } csa_dtype;
 
 /* Which compressed entries a query at position t may read ([book] ch. 5 "When
@@ -70,7 +75,8 @@ typedef enum {
 const char* csa_last_error(void);
 
 /* ABI version of this header (bumped on incompatible change; 2 added
- * csa_layer_desc.split_rows). */
+ * csa_layer_desc.split_rows; 3 added CSA_MXFP4 with untyped scale pointers,
+ * csa_layer_desc.score_bf16 and the score_bf16 argument of csa_index_topk). */
 int csa_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -104,15 +110,20 @@ int csa_abi_version(void);
  *   B, T, c, m     T % m == 0.
  *   out            [B][E_cap][c] in out_dtype; entry i of sequence b goes to
  *                  row out_first_entry + i.  out_first_entry + T/m <= E_cap.
- *   out_dtype      F32, BF16, or E4M3 (then out_scale [B][E_cap] receives
- *                  scale = max|entry| / 448 and the codes round to nearest
- *                  even; an all-zero entry gets scale 1).
+ *   out_dtype      F32, BF16, E4M3 (then out_scale, float32 [B][E_cap],
+ *                  receives scale = max|entry| / 448 and the codes round to
+ *                  nearest even; an all-zero entry gets scale 1) or MXFP4
+ *                  (out is [B][E_cap][c/2] bytes and out_scale, uint8
+ *                  [B][E_cap][c/32], receives each block's E8M0 code
+ *                  floor(log2 max|block|) - 2 + 127, the smallest code for
+ *                  an all-zero block; values round to the nearest E2M1
+ *                  value, ties to the even code, saturating at 6).
  * ------------------------------------------------------------------------ */
 csa_status csa_compress(csa_dtype dtype, const void* content_a, const void* logits_a,
                         int logit_width, const float* score_w, const float* bias_a,
                         const void* content_b, const void* logits_b, const float* bias_b,
                         const void* prev_content_b, const void* prev_logits_b, int B, int T,
-                        int c, int m, void* out, csa_dtype out_dtype, float* out_scale,
+                        int c, int m, void* out, csa_dtype out_dtype, void* out_scale,
                         int E_cap, int64_t out_first_entry, void* stream);
 
 /* ------------------------------------------------------------------------
@@ -126,9 +137,16 @@ csa_status csa_compress(csa_dtype dtype, const void* content_a, const void* logi
  * Ties between equal float32 scores go to the lower entry id.
  *
  *   idx_dtype  F32, BF16 or E4M3 for q_idx and k_idx.
- *   q_idx      [B][Tq][H_I][d_I];  q_scale [B][Tq][H_I] float32 iff E4M3.
+ *   q_idx      [B][Tq][H_I][d_I];  q_scale [B][Tq][H_I] float32 iff E4M3,
+ *              [B][Tq][H_I][d_I/32] uint8 E8M0 codes iff MXFP4 (an MXFP4
+ *              vector is d_I/2 bytes).
  *   w_idx      [B][Tq][H_I] float32 head weights.
- *   k_idx      [B][E_cap][d_I];    k_scale [B][E_cap] float32 iff E4M3.
+ *   k_idx      [B][E_cap][d_I];    k_scale [B][E_cap] float32 iff E4M3,
+ *              [B][E_cap][d_I/32] uint8 iff MXFP4; NULL otherwise.
+ *   score_bf16 1: every score is rounded to bfloat16 (nearest even) before
+ *              the selection ([book] ch. 16 "BF16 index scores"), and the
+ *              rounded scores are written; ties, then frequent, still go to
+ *              the lower id.  0: float32 scores.
  *   q_pos      [B][Tq] int64 query positions.
  *   n_entries  [B] int32 entries present in the cache.
  *   topk_idx   [B][Tq][k] int32 out: selected ids ascending, -1 padded.
@@ -138,10 +156,11 @@ csa_status csa_compress(csa_dtype dtype, const void* content_a, const void* logi
  *   ws         workspace of csa_index_topk_workspace(B, Tq, E_cap, k) bytes.
  * ------------------------------------------------------------------------ */
 size_t csa_index_topk_workspace(int B, int Tq, int E_cap, int k);
-csa_status csa_index_topk(csa_dtype idx_dtype, const void* q_idx, const float* q_scale,
-                          const float* w_idx, const void* k_idx, const float* k_scale,
+csa_status csa_index_topk(csa_dtype idx_dtype, const void* q_idx, const void* q_scale,
+                          const float* w_idx, const void* k_idx, const void* k_scale,
                           const int64_t* q_pos, const int32_t* n_entries, int B, int Tq, int H_I,
-                          int d_I, int E_cap, int m, int k, csa_visibility vis, int32_t* topk_idx,
+                          int d_I, int E_cap, int m, int k, csa_visibility vis, int score_bf16,
+                          int32_t* topk_idx,
                           int32_t* topk_cnt, float* scores, void* ws, size_t ws_bytes,
                           void* stream);
 
@@ -208,7 +227,7 @@ typedef struct {
   int n_win;         /* sliding-window width                                  */
   int vis;           /* csa_visibility                                        */
   int kv_dtype;      /* F32 or BF16: activations, caches, outputs             */
-  int idx_dtype;     /* F32, BF16 or E4M3: indexer queries and keys (CSA)     */
+  int idx_dtype;     /* F32, BF16, E4M3 or MXFP4: indexer queries and keys    */
   float scale;       /* attention logit scale (1/sqrt(c) for the pages)       */
   int split_rows;    /* decode: 0 = the attention's row splits are sized for  */
                      /* the batch; > 0 (a multiple of 16) = every query's     */
@@ -218,6 +237,8 @@ typedef struct {
                      /* invariance"); at most 64 splits per query, and at     */
                      /* most 2304 rows per split for CSA (else               */
                      /* CSA_ERR_UNSUPPORTED).  Prefill chunks ignore it.      */
+  int score_bf16;    /* CSA: 1 = index scores rounded to bfloat16 before the  */
+                     /* top-k (see csa_index_topk); 0 = float32 scores        */
 } csa_layer_desc;
 
 /* Number of compressor streams per token: 4 (ca, za, cb, zb) with overlap,
@@ -225,8 +246,9 @@ typedef struct {
 typedef struct {
   int B, E_cap;
   void* kv_cache;        /* [B][E_cap][c] kv_dtype                             */
-  void* idx_cache;       /* [B][E_cap][d_I] idx_dtype (CSA)                    */
-  float* idx_scale;      /* [B][E_cap] (E4M3 only)                             */
+  void* idx_cache;       /* [B][E_cap][d_I] idx_dtype (CSA; MXFP4: d_I/2 bytes) */
+  void* idx_scale;       /* E4M3: float32 [B][E_cap]; MXFP4: uint8             */
+                         /* [B][E_cap][d_I/32]; NULL otherwise                 */
   int32_t* n_entries;    /* [B] completed entries in the cache                 */
   void* win_ring;        /* [B][n_win][c]: position p lives in slot p % n_win  */
   void* tail;            /* [B][streams][R][c]: position p in slot p % R       */
@@ -243,7 +265,8 @@ typedef struct {
   const int64_t* pos;       /* [B]                                             */
   const void* q;            /* [B][H][c]                                       */
   const void* q_idx;        /* [B][H_I][d_I] (CSA)                             */
-  const float* q_scale;     /* [B][H_I] (E4M3)                                 */
+  const void* q_scale;      /* E4M3: float32 [B][H_I]; MXFP4: uint8            */
+                            /* [B][H_I][d_I/32]                                */
   const float* w_idx;       /* [B][H_I] (CSA)                                  */
   const void* x_new;        /* [B][c] the new token's window row               */
   const void* streams;      /* [B][streams][c] the new token's compressor rows */
@@ -261,7 +284,8 @@ typedef struct {
   int T;
   const void* q;            /* [B][T][H][c]                                    */
   const void* q_idx;        /* [B][T][H_I][d_I] (CSA)                          */
-  const float* q_scale;     /* [B][T][H_I] (E4M3)                              */
+  const void* q_scale;      /* E4M3: float32 [B][T][H_I]; MXFP4: uint8         */
+                            /* [B][T][H_I][d_I/32]                             */
   const float* w_idx;       /* [B][T][H_I] (CSA)                               */
   const void* win;          /* [B][n_win-1+T][c]: rows of positions
                                pos0-n_win+1 .. pos0+T-1                        */

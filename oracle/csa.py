@@ -263,7 +263,8 @@ def attend_partial(q, rows, scale):
 # ---------------------------------------------------------------------------
 
 def csa_query(q, q_idx, w_idx, t, kv: Stored, keys: Stored, n_entries, win_rows,
-              sink, m, k, n_win, scale, vis=VIS_PRIOR_BLOCKS, selected=None, score_dtype="f32"):
+              sink, m, k, n_win, scale, vis=VIS_PRIOR_BLOCKS, selected=None, score_dtype="f32",
+              return_raw=False):
     """CSA for one query at position t.
 
     Score the visible compressed entries with the indexer, keep the top-k,
@@ -276,15 +277,17 @@ def csa_query(q, q_idx, w_idx, t, kv: Stored, keys: Stored, n_entries, win_rows,
     ch. 16 "BF16 index scores"); ties, now frequent, still go to the lower
     entry id, and the rounded scores are returned.
 
-    Returns (o [H][c], lse [H], selected ids, scores of the visible entries).
+    Returns (o [H][c], lse [H], selected ids, scores of the visible entries),
+    and with return_raw the scores before any rounding as a fifth value.
     """
     n_vis = visible_entries(t, m, n_entries, vis)
-    scores = index_scores_stored(q_idx, w_idx, keys, n_vis)
-    if score_dtype == "bf16":
-        scores = round_to_bf16(scores)
+    raw = index_scores_stored(q_idx, w_idx, keys, n_vis)
+    scores = round_to_bf16(raw) if score_dtype == "bf16" else raw
     sel = topk_select(scores, k) if selected is None else np.asarray(selected)
     rows = np.concatenate([kv.rows(sel), win_rows(window_positions(t, n_win))], axis=0)
     o, lse = attend(q, rows, sink, scale)
+    if return_raw:
+        return o, lse, sel, scores, raw
     return o, lse, sel, scores
 
 

@@ -73,7 +73,8 @@ def decode_step(case, b, selected=None):
     The new token at t = pos[b] is appended to the state, every block that a
     query at t may read but that is not yet in the cache is folded, and the
     query is answered.  Returns a dict with o [H][c], lse [H], and for CSA the
-    selected ids and the visible scores, plus the folded entries.
+    selected ids and the visible scores (as selected on, and before any
+    rounding: scores_raw), plus the folded entries.
     """
     g = case
     t = int(g["pos"][b])
@@ -142,10 +143,11 @@ def decode_step(case, b, selected=None):
                          n_have, np.array(folded_idx) if folded_idx else None)
         qi = _dec(g["q_idx"][b], idk, None if g["q_scale"] is None else g["q_scale"][b])
         w = np.asarray(g["w_idx"][b], np.float64)
-        o, lse, sel, scores = csa.csa_query(q, qi, w, t, kv, keys, n_total, win_rows, sink,
-                                            m, g["k"], g["n_win"], g["scale"], g["vis"],
-                                            selected=selected, score_dtype=g.get("score_dtype", "f32"))
-        out.update(o=o, lse=lse, sel=sel, scores=scores)
+        o, lse, sel, scores, raw = csa.csa_query(q, qi, w, t, kv, keys, n_total, win_rows, sink,
+                                                 m, g["k"], g["n_win"], g["scale"], g["vis"],
+                                                 selected=selected, score_dtype=g.get("score_dtype", "f32"),
+                                                 return_raw=True)
+        out.update(o=o, lse=lse, sel=sel, scores=scores, scores_raw=raw)
     else:
         o, lse = csa.hca_query(q, t, kv, n_total, win_rows, sink, m, g["n_win"], g["scale"],
                                g["vis"])
@@ -214,10 +216,11 @@ def prefill_query(case, b, i, kv_new, idx_new, selected=None):
         qi = _dec(g["q_idx"][b][i], idk,
                   None if g.get("q_scale") is None else g["q_scale"][b][i])
         w = np.asarray(g["w_idx"][b][i], np.float64)
-        o, lse, sel, scores = csa.csa_query(q, qi, w, t, kv, keys, n_total, win_rows, sink,
-                                            m, g["k"], g["n_win"], g["scale"], g["vis"],
-                                            selected=selected, score_dtype=g.get("score_dtype", "f32"))
-        return {"o": o, "lse": lse, "sel": sel, "scores": scores}
+        o, lse, sel, scores, raw = csa.csa_query(q, qi, w, t, kv, keys, n_total, win_rows, sink,
+                                                 m, g["k"], g["n_win"], g["scale"], g["vis"],
+                                                 selected=selected, score_dtype=g.get("score_dtype", "f32"),
+                                                 return_raw=True)
+        return {"o": o, "lse": lse, "sel": sel, "scores": scores, "scores_raw": raw}
     o, lse = csa.hca_query(q, t, kv, n_total, win_rows, sink, m, g["n_win"], g["scale"],
                            g["vis"])
     return {"o": o, "lse": lse}

@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libcsa.so")
 
 CSA_OK, CSA_ERR_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_DEVICE = range(5)
-CSA_F32, CSA_BF16, CSA_E4M3 = 0, 1, 2
+CSA_F32, CSA_BF16, CSA_E4M3, CSA_MXFP4 = 0, 1, 2, 3
 CSA_VIS_PRIOR_BLOCKS, CSA_VIS_COMPLETED = 0, 1
 CSA_LAYER_CSA, CSA_LAYER_HCA = 1, 2
 
@@ -38,7 +38,8 @@ class LayerDesc(C.Structure):
     _fields_ = [("kind", C.c_int), ("H", C.c_int), ("c", C.c_int), ("H_I", C.c_int),
                 ("d_I", C.c_int), ("m", C.c_int), ("overlap", C.c_int), ("k", C.c_int),
                 ("n_win", C.c_int), ("vis", C.c_int), ("kv_dtype", C.c_int),
-                ("idx_dtype", C.c_int), ("scale", C.c_float), ("split_rows", C.c_int)]
+                ("idx_dtype", C.c_int), ("scale", C.c_float), ("split_rows", C.c_int),
+                ("score_bf16", C.c_int)]
 
 
 class LayerState(C.Structure):
@@ -82,7 +83,7 @@ def _declare(lib):
         "csa_abi_version": (I, []),
         "csa_compress": (I, [I, P, P, I, P, P, P, P, P, P, P, I, I, I, I, P, I, P, I, I64, P]),
         "csa_index_topk_workspace": (SZ, [I, I, I, I]),
-        "csa_index_topk": (I, [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, SZ, P]),
+        "csa_index_topk": (I, [I, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, P, P, P, P, SZ, P]),
         "csa_attend_workspace": (SZ, [I, I, I, I, I]),
         "csa_attend": (I, [I, P, P, I, P, P, I, P, I, P, I, P, P, F, I, I, I, I, P, P, P, SZ, P]),
         "hca_attend": (I, [I, P, P, I, P, I, I, P, I, P, I, P, P, F, I, I, I, I, P, P, P, SZ, P]),
@@ -161,9 +162,11 @@ def _ws(nbytes, device):
 # ---------------------------------------------------------------- entry points
 def csa_compress(content_a, logits_a, m, bias_a=None, content_b=None, logits_b=None, bias_b=None,
                  prev_content_b=None, prev_logits_b=None, score_w=None, out=None, out_scale=None,
-                 out_dtype=None, out_first_entry=0, stream=None):
+                 out_dtype=None, out_first_entry=0, out_code=None, stream=None):
     """Compress a block-aligned chunk.  content_a [B][T][c]; logits [B][T][c|1]
-    (or score_w [c]); out [B][E_cap][c] (allocated [B][T/m][c] when None)."""
+    (or score_w [c]); out [B][E_cap][c] (allocated [B][T/m][c] when None).
+    out_code overrides the storage format taken from out's dtype (CSA_MXFP4:
+    out is uint8 [B][E_cap][c/2], out_scale uint8 [B][E_cap][c/32])."""
     import torch
     B, T, c = content_a.shape
     lw = logits_a.shape[-1] if logits_a is not None else 1
@@ -171,7 +174,7 @@ def csa_compress(content_a, logits_a, m, bias_a=None, content_b=None, logits_b=N
         od = out_dtype if out_dtype is not None else content_a.dtype
         out = torch.empty((B, T // m, c), dtype=od, device=content_a.device)
     E_cap = out.shape[1]
-    code = dtype_code(out)
+    code = dtype_code(out) if out_code is None else out_code
     check(lib().csa_compress(dtype_code(content_a), ptr(content_a), ptr(logits_a), lw, ptr(score_w),
                              ptr(bias_a), ptr(content_b), ptr(logits_b), ptr(bias_b),
                              ptr(prev_content_b), ptr(prev_logits_b), B, T, c, m, ptr(out), code,
@@ -180,10 +183,16 @@ def csa_compress(content_a, logits_a, m, bias_a=None, content_b=None, logits_b=N
 
 
 def csa_index_topk(q_idx, w_idx, k_idx, q_pos, n_entries, m, k, vis=CSA_VIS_PRIOR_BLOCKS,
-                   q_scale=None, k_scale=None, scores=None, ws=None, stream=None):
-    """Indexer scores + top-k.  Returns (topk_idx [B][Tq][k], topk_cnt [B][Tq])."""
+                   q_scale=None, k_scale=None, scores=None, ws=None, idx_dtype=None, score_bf16=False,
+                   stream=None):
+    """Indexer scores + top-k.  Returns (topk_idx [B][Tq][k], topk_cnt [B][Tq]).
+    idx_dtype (a CSA_* code) overrides the format taken from q_idx's dtype;
+    CSA_MXFP4 vectors are uint8 [..][d_I/2] with uint8 scales [..][d_I/32]."""
     import torch
+    code = dtype_code(q_idx) if idx_dtype is None else idx_dtype
     B, Tq, H_I, d_I = q_idx.shape
+    if code == CSA_MXFP4:
+        d_I *= 2
     E_cap = k_idx.shape[1]
     dev = q_idx.device
     topk_idx = torch.empty((B, Tq, k), dtype=torch.int32, device=dev)
@@ -191,9 +200,9 @@ def csa_index_topk(q_idx, w_idx, k_idx, q_pos, n_entries, m, k, vis=CSA_VIS_PRIO
     need = lib().csa_index_topk_workspace(B, Tq, E_cap, k)
     if ws is None:
         ws = _ws(need, dev)
-    check(lib().csa_index_topk(dtype_code(q_idx), ptr(q_idx), ptr(q_scale), ptr(w_idx), ptr(k_idx),
+    check(lib().csa_index_topk(code, ptr(q_idx), ptr(q_scale), ptr(w_idx), ptr(k_idx),
                                ptr(k_scale), ptr(q_pos), ptr(n_entries), B, Tq, H_I, d_I, E_cap, m,
-                               k, vis, ptr(topk_idx), ptr(topk_cnt), ptr(scores), ptr(ws),
+                               k, vis, int(bool(score_bf16)), ptr(topk_idx), ptr(topk_cnt), ptr(scores), ptr(ws),
                                ws.numel(), stream_handle(stream)))
     return topk_idx, topk_cnt
 

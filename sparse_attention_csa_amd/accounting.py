@@ -65,12 +65,19 @@ def indexer_flops_per_query(H_I, d_I, n_tokens, m=4):
 # algorithmic bytes / flops of the kernels, per launch
 # ---------------------------------------------------------------------------
 
+def vector_bytes(d, dtype):
+    """Bytes of one stored vector of d values with its scales: float32 per
+    vector for e4m3, one E8M0 byte per 32 values for MXFP4 (d/2 code bytes)."""
+    if dtype == "mxfp4":
+        return d // 2 + d // 32
+    return d * DTYPE_BYTES[dtype] + (4 if dtype == "e4m3" else 0)
+
+
 def index_scan_bytes(B, Tq, E_vis, H_I, d_I, idx_dtype):
-    """Indexer scan: every visible key once (+ its fp32 scale for e4m3), the
-    queries and head weights once."""
-    kb = DTYPE_BYTES[idx_dtype]
-    keys = B * E_vis * d_I * kb + (B * E_vis * 4 if idx_dtype == "e4m3" else 0)
-    q = B * Tq * H_I * (d_I * kb + 4 + (4 if idx_dtype == "e4m3" else 0))
+    """Indexer scan: every visible key once (with its scales), the queries
+    and head weights once (a fused selection need not write the scores)."""
+    keys = B * E_vis * vector_bytes(d_I, idx_dtype)
+    q = B * Tq * H_I * (vector_bytes(d_I, idx_dtype) + 4)
     return keys + q
 
 

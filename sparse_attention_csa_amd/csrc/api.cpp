@@ -89,7 +89,7 @@ extern "C" {
 
 const char* csa_last_error(void) { return g_err.c_str(); }
 
-int csa_abi_version(void) { return 2; }
+int csa_abi_version(void) { return 3; }
 
 int csa_test_set_fused_wait_polls(int polls) { return csa::set_fused_wait_polls(polls); }
 
@@ -98,10 +98,11 @@ csa_status csa_compress(csa_dtype dtype, const void* content_a, const void* logi
                         int logit_width, const float* score_w, const float* bias_a,
                         const void* content_b, const void* logits_b, const float* bias_b,
                         const void* prev_content_b, const void* prev_logits_b, int B, int T,
-                        int c, int m, void* out, csa_dtype out_dtype, float* out_scale,
+                        int c, int m, void* out, csa_dtype out_dtype, void* out_scale,
                         int E_cap, int64_t out_first_entry, void* stream) {
   REQUIRE(dtype == CSA_F32 || dtype == CSA_BF16, CSA_ERR_UNSUPPORTED, "compressor input dtype must be F32 or BF16");
-  REQUIRE(out_dtype == CSA_F32 || out_dtype == CSA_BF16 || out_dtype == CSA_E4M3, CSA_ERR_ARG, "bad out_dtype");
+  REQUIRE(out_dtype == CSA_F32 || out_dtype == CSA_BF16 || out_dtype == CSA_E4M3 || out_dtype == CSA_MXFP4,
+          CSA_ERR_ARG, "bad out_dtype");
   REQ_PTR(content_a);
   REQ_PTR(out);
   REQUIRE(logits_a != nullptr || score_w != nullptr, CSA_ERR_ARG, "need logits_a or score_w");
@@ -116,7 +117,8 @@ csa_status csa_compress(csa_dtype dtype, const void* content_a, const void* logi
   REQUIRE(T % m == 0, CSA_ERR_ARG, "T (%d) must be a multiple of m (%d)", T, m);
   REQUIRE(is_pow2_in(c, 32, 512), CSA_ERR_UNSUPPORTED, "c in {32..512}, power of two (got %d)", c);
   REQUIRE(logit_width == 1 || logit_width == c, CSA_ERR_ARG, "logit_width must be 1 or c");
-  REQUIRE(out_dtype != CSA_E4M3 || out_scale != nullptr, CSA_ERR_ARG, "E4M3 output needs out_scale");
+  REQUIRE((out_dtype != CSA_E4M3 && out_dtype != CSA_MXFP4) || out_scale != nullptr, CSA_ERR_ARG,
+          "E4M3 and MXFP4 output need out_scale");
   REQUIRE(out_first_entry >= 0 && out_first_entry + T / m <= (int64_t)E_cap, CSA_ERR_ARG,
           "entries [%lld, %lld) do not fit E_cap %d", (long long)out_first_entry,
           (long long)(out_first_entry + T / m), E_cap);
@@ -136,15 +138,18 @@ size_t csa_index_topk_workspace(int B, int Tq, int E_cap, int k) {
   return align_up(csa::index_topk_ws_bytes(B, Tq, E_cap, k));
 }
 
-static csa_status check_index(csa_dtype idx_dtype, const void* q_idx, const float* q_scale,
-                              const float* w_idx, const void* k_idx, const float* k_scale,
+static bool scaled(int dt) { return dt == CSA_E4M3 || dt == CSA_MXFP4; }
+
+static csa_status check_index(csa_dtype idx_dtype, const void* q_idx, const void* q_scale,
+                              const float* w_idx, const void* k_idx, const void* k_scale,
                               const int64_t* q_pos, const int32_t* n_entries, int B, int Tq,
                               int H_I, int d_I, int E_cap, int m, int k, int vis,
                               int32_t* topk_idx, int32_t* topk_cnt) {
-  REQUIRE(idx_dtype == CSA_F32 || idx_dtype == CSA_BF16 || idx_dtype == CSA_E4M3, CSA_ERR_ARG, "bad idx_dtype");
+  REQUIRE(idx_dtype == CSA_F32 || idx_dtype == CSA_BF16 || idx_dtype == CSA_E4M3 || idx_dtype == CSA_MXFP4,
+          CSA_ERR_ARG, "bad idx_dtype");
   REQ_PTR(q_idx); REQ_PTR(w_idx); REQ_PTR(k_idx); REQ_PTR(q_pos); REQ_PTR(n_entries);
   REQ_PTR(topk_idx); REQ_PTR(topk_cnt);
-  REQUIRE(idx_dtype != CSA_E4M3 || (q_scale && k_scale), CSA_ERR_ARG, "E4M3 needs q_scale and k_scale");
+  REQUIRE(!scaled(idx_dtype) || (q_scale && k_scale), CSA_ERR_ARG, "E4M3 and MXFP4 need q_scale and k_scale");
   REQUIRE(B >= 1 && Tq >= 1 && E_cap >= 1 && m >= 1, CSA_ERR_ARG, "B, Tq, E_cap, m must be >= 1");
   csa_status st = check_idx_dims(H_I, d_I);
   if (st != CSA_OK) return st;
@@ -157,21 +162,24 @@ static csa_status check_index(csa_dtype idx_dtype, const void* q_idx, const floa
   return CSA_OK;
 }
 
-csa_status csa_index_topk(csa_dtype idx_dtype, const void* q_idx, const float* q_scale,
-                          const float* w_idx, const void* k_idx, const float* k_scale,
+csa_status csa_index_topk(csa_dtype idx_dtype, const void* q_idx, const void* q_scale,
+                          const float* w_idx, const void* k_idx, const void* k_scale,
                           const int64_t* q_pos, const int32_t* n_entries, int B, int Tq, int H_I,
-                          int d_I, int E_cap, int m, int k, csa_visibility vis, int32_t* topk_idx,
+                          int d_I, int E_cap, int m, int k, csa_visibility vis, int score_bf16,
+                          int32_t* topk_idx,
                           int32_t* topk_cnt, float* scores, void* ws, size_t ws_bytes,
                           void* stream) {
   csa_status st = check_index(idx_dtype, q_idx, q_scale, w_idx, k_idx, k_scale, q_pos, n_entries,
                               B, Tq, H_I, d_I, E_cap, m, k, vis, topk_idx, topk_cnt);
   if (st != CSA_OK) return st;
+  REQUIRE(score_bf16 == 0 || score_bf16 == 1, CSA_ERR_ARG, "score_bf16 must be 0 or 1");
   const size_t need = csa_index_topk_workspace(B, Tq, E_cap, k);
   REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "workspace of %zu bytes required (got %zu)",
           need, ws ? ws_bytes : (size_t)0);
   csa::IndexArgs a{};
-  a.idx_dtype = idx_dtype; a.q = q_idx; a.q_scale = idx_dtype == CSA_E4M3 ? q_scale : nullptr;
-  a.w = w_idx; a.keys = k_idx; a.k_scale = idx_dtype == CSA_E4M3 ? k_scale : nullptr;
+  a.idx_dtype = idx_dtype; a.q = q_idx; a.q_scale = scaled(idx_dtype) ? q_scale : nullptr;
+  a.w = w_idx; a.keys = k_idx; a.k_scale = scaled(idx_dtype) ? k_scale : nullptr;
+  a.score_bf16 = score_bf16;
   a.q_pos = q_pos; a.n_entries = n_entries; a.n_add = 0;
   a.B = B; a.Tq = Tq; a.H_I = H_I; a.d_I = d_I; a.E_cap = E_cap; a.m = m; a.k = k; a.vis = vis;
   a.scores = scores; a.topk_idx = topk_idx; a.topk_cnt = topk_cnt; a.ws = ws;
@@ -264,8 +272,10 @@ static csa_status check_desc(const csa_layer_desc* d) {
     if (st != CSA_OK) return st;
     REQUIRE(d->k >= 1, CSA_ERR_ARG, "k must be >= 1");
     REQUIRE(d->k <= 2048, CSA_ERR_UNSUPPORTED, "k <= 2048 supported");
-    REQUIRE(d->idx_dtype == CSA_F32 || d->idx_dtype == CSA_BF16 || d->idx_dtype == CSA_E4M3, CSA_ERR_ARG,
-            "bad idx_dtype");
+    REQUIRE(d->idx_dtype == CSA_F32 || d->idx_dtype == CSA_BF16 || d->idx_dtype == CSA_E4M3 ||
+                d->idx_dtype == CSA_MXFP4,
+            CSA_ERR_ARG, "bad idx_dtype");
+    REQUIRE(d->score_bf16 == 0 || d->score_bf16 == 1, CSA_ERR_ARG, "score_bf16 must be 0 or 1");
     REQUIRE(d->split_rows == 0 || (d->split_rows <= 2304 &&
                                    (d->k + d->n_win + d->split_rows - 1) / d->split_rows <= csa::kMaxRowSplits),
             CSA_ERR_UNSUPPORTED, "split_rows %d: at most 2304 rows and %d splits of k + n_win rows", d->split_rows,
@@ -284,7 +294,8 @@ static csa_status check_state(const csa_layer_desc* d, const csa_layer_state* s)
     REQ_PTR(s->idx_cache); REQ_PTR(s->idx_tail);
     REQUIRE(s->E_cap <= kMaxIndexEntries, CSA_ERR_UNSUPPORTED, "E_cap <= %d supported for CSA layers",
             kMaxIndexEntries);
-    REQUIRE(d->idx_dtype != CSA_E4M3 || s->idx_scale != nullptr, CSA_ERR_ARG, "E4M3 indexer cache needs idx_scale");
+    REQUIRE(!scaled(d->idx_dtype) || s->idx_scale != nullptr, CSA_ERR_ARG,
+            "E4M3 and MXFP4 indexer caches need idx_scale");
   }
   return CSA_OK;
 }
@@ -319,7 +330,7 @@ csa_status decode_check(const csa_layer_desc* d, const csa_layer_state* s, const
   if (d->kind == CSA_LAYER_CSA) {
     REQ_PTR(io->q_idx); REQ_PTR(io->w_idx); REQ_PTR(io->idx_streams);
     REQ_PTR(io->topk_idx); REQ_PTR(io->topk_cnt);
-    REQUIRE(d->idx_dtype != CSA_E4M3 || io->q_scale != nullptr, CSA_ERR_ARG, "E4M3 indexer needs q_scale");
+    REQUIRE(!scaled(d->idx_dtype) || io->q_scale != nullptr, CSA_ERR_ARG, "E4M3 and MXFP4 indexers need q_scale");
   }
   return CSA_OK;
 }
@@ -351,8 +362,9 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
   f.bias_a = s->bias_a; f.bias_b = s->bias_b; f.ibias_a = s->ibias_a; f.ibias_b = s->ibias_b;
   csa::IndexArgs x{};
   if (is_csa) {
-    x.idx_dtype = d->idx_dtype; x.q = io->q_idx; x.q_scale = d->idx_dtype == CSA_E4M3 ? io->q_scale : nullptr;
-    x.w = io->w_idx; x.keys = s->idx_cache; x.k_scale = d->idx_dtype == CSA_E4M3 ? s->idx_scale : nullptr;
+    x.idx_dtype = d->idx_dtype; x.q = io->q_idx; x.q_scale = scaled(d->idx_dtype) ? io->q_scale : nullptr;
+    x.w = io->w_idx; x.keys = s->idx_cache; x.k_scale = scaled(d->idx_dtype) ? s->idx_scale : nullptr;
+    x.score_bf16 = d->score_bf16;
     x.q_pos = io->pos; x.n_entries = s->n_entries; x.n_add = 0;
     x.B = B; x.Tq = 1; x.H_I = d->H_I; x.d_I = d->d_I; x.E_cap = s->E_cap; x.m = d->m; x.k = d->k;
     x.vis = d->vis; x.scores = nullptr; x.topk_idx = io->topk_idx; x.topk_cnt = io->topk_cnt; x.ws = w;
@@ -399,7 +411,7 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
   if (is_csa) {
     REQ_PTR(io->q_idx); REQ_PTR(io->w_idx); REQ_PTR(io->idx_streams);
     REQ_PTR(io->topk_idx); REQ_PTR(io->topk_cnt);
-    REQUIRE(d->idx_dtype != CSA_E4M3 || io->q_scale != nullptr, CSA_ERR_ARG, "E4M3 indexer needs q_scale");
+    REQUIRE(!scaled(d->idx_dtype) || io->q_scale != nullptr, CSA_ERR_ARG, "E4M3 and MXFP4 indexers need q_scale");
   }
   const int B = s->B, T = io->T, m = d->m;
   REQUIRE(T >= 1 && io->pos0 >= 0, CSA_ERR_ARG, "T must be >= 1 and pos0 >= 0");
@@ -417,7 +429,7 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
 
   // compress the chunk's blocks: main entries, then (CSA) indexer keys
   auto compress = [&](const void* streams, int width, const void* tail, void* out, int out_dtype,
-                      float* out_scale, const float* ba, const float* bb, bool overlap) -> hipError_t {
+                      void* out_scale, const float* ba, const float* bb, bool overlap) -> hipError_t {
     csa::CompressArgs c{};
     const int ns = overlap ? 4 : 2;
     const char* base = (const char*)streams;
@@ -450,8 +462,9 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
   }
   if (is_csa) {
     csa::IndexArgs x{};
-    x.idx_dtype = d->idx_dtype; x.q = io->q_idx; x.q_scale = d->idx_dtype == CSA_E4M3 ? io->q_scale : nullptr;
-    x.w = io->w_idx; x.keys = s->idx_cache; x.k_scale = d->idx_dtype == CSA_E4M3 ? s->idx_scale : nullptr;
+    x.idx_dtype = d->idx_dtype; x.q = io->q_idx; x.q_scale = scaled(d->idx_dtype) ? io->q_scale : nullptr;
+    x.w = io->w_idx; x.keys = s->idx_cache; x.k_scale = scaled(d->idx_dtype) ? s->idx_scale : nullptr;
+    x.score_bf16 = d->score_bf16;
     x.q_pos = nullptr; x.q_pos0 = io->pos0; x.n_entries = s->n_entries; x.n_add = n_new;
     x.B = B; x.Tq = T; x.H_I = d->H_I; x.d_I = d->d_I; x.E_cap = s->E_cap; x.m = m; x.k = d->k;
     x.vis = d->vis; x.scores = nullptr; x.topk_idx = io->topk_idx; x.topk_cnt = io->topk_cnt; x.ws = w;

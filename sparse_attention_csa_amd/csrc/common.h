@@ -62,7 +62,57 @@ CSA_DEV uint8_t f32_to_e4m3(float y) {
   return sign | (uint8_t)(((E + 7) << 3) | f);
 }
 
+// ---------------------------------------------------------------- OCP MX FP4
+// E2M1 elements (1 sign, 2 exponent bits with bias 1, 1 fraction bit;
+// magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) in blocks of 32 sharing one E8M0
+// scale 2^(code - 127).  Two elements per byte, element 2j in the low
+// nibble of byte j.
+struct mx4 {};  // tag type: MXFP4 storage (a kernel template argument)
+
+CSA_DEV float e2m1_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, f = c & 1u;
+  const float mag = e == 0 ? 0.5f * (float)f : ldexpf(1.0f + 0.5f * (float)f, (int)e - 1);
+  return (c & 8u) ? -mag : mag;
+}
+
+CSA_DEV float e8m0_to_f32(uint32_t code) { return ldexpf(1.0f, (int)code - 127); }
+
+// E2M1 code of y (already divided by its block scale): the nearest value,
+// ties to the even code, saturating at 6
+CSA_DEV uint32_t f32_to_e2m1(float y) {
+  const float a = fabsf(y);
+  const float sp = a < 2.f ? 0.5f : (a < 4.f ? 1.f : 2.f);
+  const float r = fminf(rintf(a / sp) * sp, 6.f);  // rintf: half to even on the multiple
+  const uint32_t mag = r < 2.f ? (uint32_t)(2.f * r) : (r < 4.f ? 2u + (uint32_t)r : (r == 4.f ? 6u : 7u));
+  return (y < 0.f && mag) ? (mag | 8u) : mag;
+}
+
+// E8M0 code of a block whose largest magnitude is amax:
+// 2^(floor(log2 amax) - 2), the smallest scale for an all-zero block
+CSA_DEV uint32_t mx_scale_code(float amax) {
+  if (!(amax > 0.f)) return 0u;
+  int e;
+  frexpf(amax, &e);  // amax = f 2^e, f in [0.5, 1): floor(log2 amax) = e - 1
+  const int c = e - 1 - 2 + 127;
+  return (uint32_t)(c < 0 ? 0 : (c > 254 ? 254 : c));
+}
+
+// The lanes of aligned groups of 32 hold one block's elements (lane
+// i of the group: element i).  Returns this lane's E2M1 code; *scale gets
+// the block's E8M0 code.
+CSA_DEV uint32_t mx_quantize_lane(float v, uint32_t* scale) {
+  float am = fabsf(v);
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+  const uint32_t sc = mx_scale_code(am);
+  *scale = sc;
+  return f32_to_e2m1(ldexpf(v, 127 - (int)sc));
+}
+
 // ---------------------------------------------------------------- top-k keys
+// nearest-even bf16 value of f, as a float (bf16 index scores)
+CSA_DEV float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
 // order-preserving map float -> uint32 (larger float -> larger key)
 CSA_DEV uint32_t f32_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -10,6 +10,13 @@
 // row).  fold_append_kernel (a decode step): source tokens split over thread
 // groups, the groups' online states merged by lane shuffles and through LDS
 // (fold.h).
+//
+// Produced indexer keys are stored in the cache's format: bf16 / f32, e4m3
+// with one float32 scale per key (max |v| / 448), or OCP MXFP4 (E2M1 pairs,
+// one E8M0 scale 2^(floor(log2 max |v|) - 2) per block of 32; "DeepSeek-V4"
+// book ch. 16 "Why use fine-grained scales?").
+
+#include <type_traits>
 
 #include "common.h"
 #include "fold.h"
@@ -90,7 +97,20 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
   }
 
   const size_t orow = ((size_t)b * a.E_cap + (size_t)(a.first + i)) * c;
-  if constexpr (sizeof(TO) == 1) {
+  if constexpr (std::is_same<TO, mx4>::value) {
+    // MXFP4 output (c a multiple of 32): the 32 lanes of an aligned lane
+    // group hold one block; a pair of neighbouring lanes forms one byte
+    uint8_t* o = reinterpret_cast<uint8_t*>(a.out) + orow / 2;
+    uint8_t* so = reinterpret_cast<uint8_t*>(a.out_scale) + orow / 32;
+    for (int u = 0; u < (c + 255) / 256; ++u) {  // the same trip count in every lane
+      const int r = tid + 256 * u;
+      uint32_t sc;
+      const uint32_t code = mx_quantize_lane(r < c ? vals[u] : 0.f, &sc);
+      const uint32_t odd = __shfl_xor(code, 1, 64);
+      if (r < c && (r & 1) == 0) o[r / 2] = (uint8_t)(code | (odd << 4));
+      if (r < c && (r & 31) == 0) so[r / 32] = (uint8_t)sc;
+    }
+  } else if constexpr (sizeof(TO) == 1) {
     // e4m3 output: one scale per entry = max|v| / 448
     float amax = 0.f;
     for (int u = 0; u < nv; ++u) amax = fmaxf(amax, fabsf(vals[u]));
@@ -103,7 +123,7 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
     uint8_t* o = reinterpret_cast<uint8_t*>(a.out) + orow;
     int u = 0;
     for (int r = tid; r < c; r += 256, ++u) o[r] = f32_to_e4m3(vals[u] / scale);
-    if (tid == 0) a.out_scale[(size_t)b * a.E_cap + a.first + i] = scale;
+    if (tid == 0) reinterpret_cast<float*>(a.out_scale)[(size_t)b * a.E_cap + a.first + i] = scale;
   } else {
     TO* o = reinterpret_cast<TO*>(a.out) + orow;
     int u = 0;
@@ -111,23 +131,24 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
   }
 }
 
+template <typename T>
+static void launch_compress_to(const CompressArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.out_dtype == F32)
+    CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<T, float>), grid, block, 0, s, a);
+  else if (a.out_dtype == BF16)
+    CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<T, bf16>), grid, block, 0, s, a);
+  else if (a.out_dtype == E4M3)
+    CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<T, uint8_t>), grid, block, 0, s, a);
+  else
+    CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<T, mx4>), grid, block, 0, s, a);
+}
+
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   dim3 grid(a.T / a.m, a.B), block(256);
-  if (a.dtype == F32) {
-    if (a.out_dtype == F32)
-      CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<float, float>), grid, block, 0, s, a);
-    else if (a.out_dtype == BF16)
-      CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<float, bf16>), grid, block, 0, s, a);
-    else
-      CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<float, uint8_t>), grid, block, 0, s, a);
-  } else {
-    if (a.out_dtype == F32)
-      CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<bf16, float>), grid, block, 0, s, a);
-    else if (a.out_dtype == BF16)
-      CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<bf16, bf16>), grid, block, 0, s, a);
-    else
-      CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<bf16, uint8_t>), grid, block, 0, s, a);
-  }
+  if (a.dtype == F32)
+    launch_compress_to<float>(a, grid, block, s);
+  else
+    launch_compress_to<bf16>(a, grid, block, s);
   return hipGetLastError();
 }
 
@@ -189,7 +210,15 @@ __global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
     if (fold) {
       const float iv = fold_job<T>(itail, iio, d, 0, d, m, R, t, e, e > 0, a.ibias_a, a.ibias_b, s_part);
       const size_t row = (size_t)b * a.E_cap + e;
-      if constexpr (sizeof(TI) == 1) {
+      if constexpr (std::is_same<TI, mx4>::value) {
+        // MXFP4 (d a multiple of 32, every lane takes part in the block maxima)
+        uint32_t sc;
+        const uint32_t code = mx_quantize_lane(tid < d ? iv : 0.f, &sc);
+        const uint32_t odd = __shfl_xor(code, 1, 64);
+        if (tid < d && (tid & 1) == 0)
+          reinterpret_cast<uint8_t*>(a.idx_cache)[row * (d / 2) + tid / 2] = (uint8_t)(code | (odd << 4));
+        if (tid < d && (tid & 31) == 0) reinterpret_cast<uint8_t*>(a.idx_scale)[row * (d / 32) + tid / 32] = (uint8_t)sc;
+      } else if constexpr (sizeof(TI) == 1) {
         float am = wave_max(tid < d ? fabsf(iv) : 0.f);
         if ((tid & 63) == 0) s_red[tid >> 6] = am;
         __syncthreads();
@@ -197,7 +226,7 @@ __global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
         float scale = am / 448.0f;
         if (!(scale > 0.f)) scale = 1.f;
         if (tid < d) reinterpret_cast<uint8_t*>(a.idx_cache)[row * d + tid] = f32_to_e4m3(iv / scale);
-        if (tid == 0) a.idx_scale[row] = scale;
+        if (tid == 0) reinterpret_cast<float*>(a.idx_scale)[row] = scale;
       } else {
         if (tid < d) st(reinterpret_cast<TI*>(a.idx_cache), row * d + tid, iv);
       }
@@ -219,23 +248,24 @@ __global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
   }
 }
 
+template <typename T>
+static void launch_fold_to(const FoldArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  if (a.idx_dtype == E4M3)
+    CSA_LAUNCH("fold_append", (fold_append_kernel<T, uint8_t>), grid, block, 0, s, a);
+  else if (a.idx_dtype == MXFP4)
+    CSA_LAUNCH("fold_append", (fold_append_kernel<T, mx4>), grid, block, 0, s, a);
+  else if (a.idx_dtype == F32)
+    CSA_LAUNCH("fold_append", (fold_append_kernel<T, float>), grid, block, 0, s, a);
+  else  // BF16, or no indexer
+    CSA_LAUNCH("fold_append", (fold_append_kernel<T, bf16>), grid, block, 0, s, a);
+}
+
 hipError_t launch_fold_append(const FoldArgs& a, hipStream_t s) {
   dim3 grid(a.c / kFoldCW + (a.idx_dtype >= 0 ? 1 : 0), a.B), block(kFoldT);
-  if (a.dtype == F32) {
-    if (a.idx_dtype == E4M3)
-      CSA_LAUNCH("fold_append", (fold_append_kernel<float, uint8_t>), grid, block, 0, s, a);
-    else if (a.idx_dtype == BF16)
-      CSA_LAUNCH("fold_append", (fold_append_kernel<float, bf16>), grid, block, 0, s, a);
-    else
-      CSA_LAUNCH("fold_append", (fold_append_kernel<float, float>), grid, block, 0, s, a);
-  } else {
-    if (a.idx_dtype == E4M3)
-      CSA_LAUNCH("fold_append", (fold_append_kernel<bf16, uint8_t>), grid, block, 0, s, a);
-    else if (a.idx_dtype == F32)
-      CSA_LAUNCH("fold_append", (fold_append_kernel<bf16, float>), grid, block, 0, s, a);
-    else
-      CSA_LAUNCH("fold_append", (fold_append_kernel<bf16, bf16>), grid, block, 0, s, a);
-  }
+  if (a.dtype == F32)
+    launch_fold_to<float>(a, grid, block, s);
+  else
+    launch_fold_to<bf16>(a, grid, block, s);
   return hipGetLastError();
 }
 

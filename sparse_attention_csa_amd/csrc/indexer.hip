@@ -4,13 +4,19 @@
 // ("2026 DeepSeek-V4" note, "Key design 1" indexer equation; "DeepSeek-V4"
 // book ch. 6 "The index score").  For e4m3 the per-vector scales are positive,
 // so ReLU(sq*sk*x) = sq*sk*ReLU(x): the query scale folds into w and the key
-// scale multiplies the head sum once.
+// scale multiplies the head sum once.  MXFP4 vectors (E2M1 pairs with one
+// E8M0 scale per 32 values; "DeepSeek-V4" book ch. 16 "The two main FP4
+// targets") are decoded element by element in the VALU form.  With
+// score_bf16 the scores are rounded to bfloat16 before the selection (book
+// ch. 16 "BF16 index scores"; ties, then frequent, still go to the lower id).
 //
 // Top-k: C_t = TopK_k(I[t, :]) (same equation; book ch. 6 "Top-k is a budget
 // over compressed entries"), ties to the lower entry id, ids ascending.  The
 // k-th largest score is found exactly by a radix select on order-preserving
 // 32-bit keys (8 bits per pass over the row, LDS histograms), then one
 // in-order pass emits every id above the threshold plus the lowest-id ties.
+
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -26,6 +32,11 @@ CSA_DEV float ld_key(const T* p, size_t i) {
   return ld(p, i);
 }
 CSA_DEV float ld_key(const uint8_t* p, size_t i) { return e4m3_to_f32(p[i]); }
+// element i of an MXFP4 vector (packed codes p, E8M0 block scales sc)
+CSA_DEV float ld_mx4(const uint8_t* p, const uint8_t* sc, int i) {
+  const uint32_t byte = p[i >> 1];
+  return e2m1_to_f32((i & 1) ? byte >> 4 : byte & 15u) * e8m0_to_f32(sc[i >> 5]);
+}
 
 CSA_DEV int64_t n_visible(const IndexArgs& a, int b, int64_t t) {
   const int64_t lim = vis_limit(t, a.m, a.vis);
@@ -40,6 +51,7 @@ CSA_DEV int64_t n_visible(const IndexArgs& a, int b, int64_t t) {
 // --------------------------------------------------------------------------
 template <typename TK>
 __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
+  constexpr bool MX = std::is_same<TK, mx4>::value;
   const int row = blockIdx.y, b = row / a.Tq, tq = row % a.Tq;
   const int tid = threadIdx.x;
   const int H = a.H_I, D = a.d_I;
@@ -50,25 +62,41 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
 
   __shared__ float q_s[kHMax * 128];
   __shared__ float w_s[kHMax];
-  const TK* q = reinterpret_cast<const TK*>(a.q) + (size_t)row * H * D;
-  for (int i = tid; i < H * D; i += 256) q_s[i] = ld_key(q, i);
+  if constexpr (MX) {
+    // the row's H vectors are contiguous: element i of the row at byte i/2,
+    // its block scale at i/32 (D is a multiple of 32)
+    const uint8_t* q = reinterpret_cast<const uint8_t*>(a.q) + (size_t)row * H * D / 2;
+    const uint8_t* qs = reinterpret_cast<const uint8_t*>(a.q_scale) + (size_t)row * H * D / 32;
+    for (int i = tid; i < H * D; i += 256) q_s[i] = ld_mx4(q, qs, i);
+  } else {
+    const TK* q = reinterpret_cast<const TK*>(a.q) + (size_t)row * H * D;
+    for (int i = tid; i < H * D; i += 256) q_s[i] = ld_key(q, i);
+  }
   if (tid < H) {
     float w = a.w[(size_t)row * H + tid];
-    if (a.q_scale) w *= a.q_scale[(size_t)row * H + tid];
+    if (!MX && a.q_scale) w *= reinterpret_cast<const float*>(a.q_scale)[(size_t)row * H + tid];
     w_s[tid] = w;
   }
   __syncthreads();
 
   const int64_t s = s0 + tid;
   if (s >= nv) return;
-  const TK* key = reinterpret_cast<const TK*>(a.keys) + ((size_t)b * a.E_cap + s) * D;
+  const size_t krow = (size_t)b * a.E_cap + s;
   float acc[kHMax];
 #pragma unroll
   for (int h = 0; h < kHMax; ++h) acc[h] = 0.f;
   for (int d0 = 0; d0 < D; d0 += 8) {
     float kv[8];
+    if constexpr (MX) {
+      const uint8_t* key = reinterpret_cast<const uint8_t*>(a.keys) + krow * D / 2;
+      const uint8_t* ks = reinterpret_cast<const uint8_t*>(a.k_scale) + krow * D / 32;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kv[j] = ld_key(key, d0 + j);
+      for (int j = 0; j < 8; ++j) kv[j] = ld_mx4(key, ks, d0 + j);
+    } else {
+      const TK* key = reinterpret_cast<const TK*>(a.keys) + krow * D;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kv[j] = ld_key(key, d0 + j);
+    }
 #pragma unroll
     for (int h = 0; h < kHMax; ++h) {
       if (h < H) {
@@ -83,7 +111,8 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
 #pragma unroll
   for (int h = 0; h < kHMax; ++h)
     if (h < H) score += w_s[h] * fmaxf(acc[h], 0.f);
-  if (a.k_scale) score *= a.k_scale[(size_t)b * a.E_cap + s];
+  if (!MX && a.k_scale) score *= reinterpret_cast<const float*>(a.k_scale)[krow];
+  if (a.score_bf16) score = round_bf16(score);
   a.scores[(size_t)row * a.E_cap + s] = score;
 }
 
@@ -199,7 +228,7 @@ __global__ __launch_bounds__(256) void index_score_prefill_kernel(IndexArgs a) {
       part += __shfl_xor(part, 16, 64);
       part += __shfl_xor(part, 32, 64);
       const int64_t e = te + 16 * kb + li;
-      if (lg == 0 && e < nv_q && e < e1) out[e] = part;
+      if (lg == 0 && e < nv_q && e < e1) out[e] = a.score_bf16 ? round_bf16(part) : part;
     }
     if (j + 1 < ntiles) store_tile((j + 1) & 1, next);
     __syncthreads();
@@ -247,8 +276,10 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t s, const FoldArgs*
       CSA_LAUNCH("index_score", index_score_kernel<float>, g1, blk, 0, s, a);
     else if (a.idx_dtype == BF16)
       CSA_LAUNCH("index_score", index_score_kernel<bf16>, g1, blk, 0, s, a);
-    else
+    else if (a.idx_dtype == E4M3)
       CSA_LAUNCH("index_score", index_score_kernel<uint8_t>, g1, blk, 0, s, a);
+    else
+      CSA_LAUNCH("index_score", index_score_kernel<mx4>, g1, blk, 0, s, a);
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;

@@ -77,19 +77,23 @@ constexpr int kD = 128;
 constexpr int kFastFoldM = 4;
 constexpr int kFastFoldC = 512;
 
+// Key formats of the scan (FMT): 0 bf16, 1 e4m3 with a float32 scale per
+// key, 2 MXFP4 (E2M1 pairs, one E8M0 scale per 32 values).
+//
 // Tile geometry.  e4m3: 16 keys x 128 B = 2 KB, read as two 1 KB pieces of
 // 8 keys; bf16: 16 keys x 256 B = 4 KB, four pieces of 4 keys.  In LDS, chunk
 // q of key (piece j, key-in-piece k) sits at chunk position kCpk*k + (q ^ s)
-// of piece j, s = k ^ j (e4m3) or k + 4j (bf16).
-template <int FP8>
+// of piece j, s = k ^ j (e4m3) or k + 4j (bf16).  MXFP4: 16 keys x 64 B =
+// 1 KB, loaded straight into the MFMA operand layout (no LDS).
+template <int FMT>
 struct Geo {
-  static constexpr int kKeyB = FP8 ? 128 : 256;
+  static constexpr int kKeyB = FMT == 2 ? 64 : (FMT == 1 ? 128 : 256);
   static constexpr int kTileB = 16 * kKeyB;
   static constexpr int kPieces = kTileB / 1024;
   static constexpr int kKpp = 16 / kPieces;  // keys per piece
   static constexpr int kCpk = kKeyB / 16;    // 16-byte chunks per key
-  static constexpr int kU = FP8 ? 6 : 4;     // tiles per batch (even)
-  CSA_DEV static int sw(int k, int j) { return FP8 ? (k ^ j) : (k + 4 * j); }
+  static constexpr int kU = FMT == 2 ? 8 : (FMT == 1 ? 6 : 4);  // tiles per batch (even)
+  CSA_DEV static int sw(int k, int j) { return FMT == 1 ? (k ^ j) : (k + 4 * j); }
   // LDS byte offset of chunk q of key c within a tile
   CSA_DEV static int lds_off(int c, int q) {
     const int j = c / kKpp, k = c % kKpp;
@@ -102,10 +106,11 @@ struct Geo {
 // grid (n_wg, rows), 256 threads
 // wait_polls: how many times a waiting workgroup polls for its row's
 // published threshold bin before it gives up (a multiple of 4)
-template <int FP8, int HT>
+template <int FMT, int HT>
 __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, TopkWs ws, int use_hist, int fuse,
                                                                 FoldArgs f, int fold_mode, int wait_polls) {
-  typedef Geo<FP8> G;
+  constexpr bool FP8 = FMT == 1, FP4 = FMT == 2;
+  typedef Geo<FMT> G;
   constexpr int kU = G::kU;
   __shared__ __attribute__((aligned(1024))) char s_tr[4][kU * G::kTileB];  // per-wave transpose buffer
   __shared__ int s_hist[kTopkBins];
@@ -121,18 +126,27 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   const bool is_fold_wg = fold_mode && blockIdx.x == gridDim.x - 1;
   bf16x8_t qb[HT][4];
   i32x8_t q8[HT];
+  int qsc[HT];  // MXFP4: the E8M0 scale of the lane's query block
   float wr[HT][4];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     if (is_fold_wg) {
       q8[ht] = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
+      qsc[ht] = 127;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) qb[ht][ks] = bf16x8_t{};
       wr[ht][0] = wr[ht][1] = wr[ht][2] = wr[ht][3] = 0.f;
       continue;
     }
     const int h = 16 * ht + li;
-    if constexpr (FP8) {
+    if constexpr (FP4) {
+      // the lane's operand: block lg (32 values, 16 bytes) of head h, with
+      // the block's scale
+      const uint8_t* q = reinterpret_cast<const uint8_t*>(a.q) + ((size_t)row * H + h) * (kD / 2) + 16 * lg;
+      const uint4 v = *reinterpret_cast<const uint4*>(q);
+      q8[ht] = i32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      qsc[ht] = reinterpret_cast<const uint8_t*>(a.q_scale)[((size_t)row * H + h) * (kD / 32) + lg];
+    } else if constexpr (FP8) {
       const uint8_t* q = reinterpret_cast<const uint8_t*>(a.q) + ((size_t)row * H + h) * kD + 16 * lg;
       const uint4 v0 = *reinterpret_cast<const uint4*>(q), v1 = *reinterpret_cast<const uint4*>(q + 64);
       q8[ht] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
@@ -151,7 +165,8 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
       qs[ht] = is_fold_wg ? make_float4(0.f, 0.f, 0.f, 0.f)
-                          : *reinterpret_cast<const float4*>(a.q_scale + (size_t)row * H + 16 * ht + 4 * lg);
+                          : *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(a.q_scale) +
+                                                             (size_t)row * H + 16 * ht + 4 * lg);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -171,7 +186,8 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   }
   const int64_t nv_scan = fold_now ? nv - 1 : nv;  // the scan workgroups' entries
   const char* keys = reinterpret_cast<const char*>(a.keys) + (size_t)b * a.E_cap * G::kKeyB;
-  const float* ksc = a.k_scale ? a.k_scale + (size_t)b * a.E_cap : nullptr;
+  const float* ksc = FP8 ? reinterpret_cast<const float*>(a.k_scale) + (size_t)b * a.E_cap : nullptr;
+  const uint8_t* ksc4 = FP4 ? reinterpret_cast<const uint8_t*>(a.k_scale) + (size_t)b * a.E_cap * (kD / 32) : nullptr;
   float* out = a.scores + (size_t)row * a.E_cap;
 
   // this wave's tiles [t0, t1), in batches of kU
@@ -184,10 +200,11 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   const int nbatch = (n + kU - 1) / kU;
 
   // piece j of a tile: lane l reads bytes [16 l, 16 l + 16) of the piece,
-  // i.e. chunk (l % kCpk) of key kKpp*j + l / kCpk
+  // i.e. chunk (l % kCpk) of key kKpp*j + l / kCpk; MXFP4: lane (li, lg)
+  // reads block lg of key li, its MFMA operand (and that block's scale)
   typedef u32x4_t KBatch[kU][G::kPieces];
-  typedef float SBatch[kU];
-  const int ld_key = l / G::kCpk, ld_chunk = l % G::kCpk;
+  typedef typename std::conditional<FP4, uint32_t, float>::type SBatch[kU];
+  const int ld_key = FP4 ? li : l / G::kCpk, ld_chunk = FP4 ? lg : l % G::kCpk;
   // the last row of this wave's run: loads past it (the tail of the run and
   // the batches after it) all re-read that row, which stays in cache
   const int64_t e_last = (t1 * 16 < nv_scan ? t1 * 16 : nv_scan) - 1;
@@ -205,6 +222,11 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
         int64_t e = e0 + li;
         if (e > e_last) e = e_last;
         sreg[u] = ksc[e];
+      }
+      if constexpr (FP4) {
+        int64_t e = e0 + li;
+        if (e > e_last) e = e_last;
+        sreg[u] = ksc4[(size_t)e * (kD / 32) + lg];
       }
     }
   };
@@ -240,11 +262,30 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   // score tiles u, u+1 of the batch in the transpose buffer (interleaved so
   // the two latency chains overlap)
   constexpr int kG = 2;
-  auto score = [&](const SBatch& sreg, int bi, int u) __attribute__((always_inline)) {
+  auto score = [&](const KBatch& kcur, const SBatch& sreg, int bi, int u) __attribute__((always_inline)) {
     float part[kG];
 #pragma unroll
     for (int g = 0; g < kG; ++g) part[g] = 0.f;
-    if constexpr (FP8) {
+    if constexpr (FP4) {
+      // the block scales of both operands enter the MFMA (per lane: the
+      // query block's and the key block's E8M0 codes)
+      f32x4_t c[HT][kG];
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int g = 0; g < kG; ++g) {
+          const u32x4_t k4 = kcur[u + g][0];
+          const i32x8_t kb = i32x8_t{(int)k4.x, (int)k4.y, (int)k4.z, (int)k4.w, 0, 0, 0, 0};
+          c[ht][g] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(q8[ht], kb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 4, 4,
+                                                                      0, qsc[ht], 0, (int)sreg[u + g]);
+        }
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int g = 0; g < kG; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) part[g] += wr[ht][r] * relu(c[ht][g][r]);
+    } else if constexpr (FP8) {
       i32x8_t kb[kG];
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
@@ -297,6 +338,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
       // head sum over the four lane groups: lanes l, l^16, l^32, l^48
       part[g] = lane_sum_xor16_32(part[g]);
       if (FP8) part[g] *= sreg[u + g];
+      if (a.score_bf16) part[g] = round_bf16(part[g]);
       const int i = bi * kU + u + g;
       const int64_t e = (t0 + i) * 16 + li;
       if (e < nv_scan && i < n && lg == 0) {
@@ -308,15 +350,18 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   };
 
   // transpose a batch through this wavefront's LDS buffer and score it; the
-  // writes land before the reads (the wavefront's own LDS operations, in order)
+  // writes land before the reads (the wavefront's own LDS operations, in
+  // order).  MXFP4 batches are already in operand layout.
   auto run_batch = [&](KBatch& kcur, SBatch& scur, int bi) __attribute__((always_inline)) {
+    if constexpr (!FP4) {
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
+      for (int u = 0; u < kU; ++u)
 #pragma unroll
-      for (int j = 0; j < G::kPieces; ++j)
-        *reinterpret_cast<u32x4_t*>(tr + u * G::kTileB + wr_off[j]) = kcur[u][j];
+        for (int j = 0; j < G::kPieces; ++j)
+          *reinterpret_cast<u32x4_t*>(tr + u * G::kTileB + wr_off[j]) = kcur[u][j];
+    }
 #pragma unroll
-    for (int u = 0; u < kU; u += kG) score(scur, bi, u);
+    for (int u = 0; u < kU; u += kG) score(kcur, scur, bi, u);
   };
   // two register batches alternate; loads are unconditional (past the run
   // they hit one cached row), so the compiler's wait bookkeeping sees the
@@ -359,6 +404,9 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
       for (int i = tid; i < f.c; i += 256) ring[i] = xn[i];
     }
   
+    // bytes of one query vector, in 16-byte loads
+    constexpr int kQB = FP4 ? kD / 2 : (FP8 ? kD : 2 * kD);
+    constexpr int kV = kQB / 16;
     Soft* s_part = reinterpret_cast<Soft*>(&s_tr[0][0]);
     float* s_red = reinterpret_cast<float*>(s_part + 4 * 256);
     uint32_t* s_key = reinterpret_cast<uint32_t*>(s_red + 8);  // the stored new key (<= 256 B)
@@ -368,16 +416,35 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
     // the lane's query row when pre, else it is loaded here)
     auto score_new_key = [&](float ks, const uint4* qv_reg, bool pre) {
       if (w != 0) return;
-      constexpr int kV = kD * (FP8 ? 1 : 2) / 16;
       float part = 0.f;
       if (l < H) {
         const uint4* qv = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) +
-                                                         ((size_t)row * H + l) * kD * (FP8 ? 1 : 2));
+                                                         ((size_t)row * H + l) * kQB);
         const uint4* kv4 = reinterpret_cast<const uint4*>(s_key);
         uint4 qr[kV];
 #pragma unroll
         for (int j = 0; j < kV; ++j) qr[j] = pre ? qv_reg[j] : qv[j];
         float c = 0.f;
+        if constexpr (FP4) {
+          // per block of 32: the E2M1 products summed exactly, then both
+          // block scales (as the scaled MFMA applies them)
+          const uint32_t qs4 = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(a.q_scale) +
+                                                                  ((size_t)row * H + l) * (kD / 32));
+          const uint32_t ks4 = s_key[kD / 8];  // the four key scales after the 64 code bytes
+#pragma unroll
+          for (int j = 0; j < kV; ++j) {
+            const uint4 kj = kv4[j];
+            const uint32_t qw[4] = {qr[j].x, qr[j].y, qr[j].z, qr[j].w};
+            const uint32_t kw[4] = {kj.x, kj.y, kj.z, kj.w};
+            float blk = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int n = 0; n < 8; ++n)
+                blk += e2m1_to_f32((qw[i] >> (4 * n)) & 15u) * e2m1_to_f32((kw[i] >> (4 * n)) & 15u);
+            c += blk * e8m0_to_f32((qs4 >> (8 * j)) & 255u) * e8m0_to_f32((ks4 >> (8 * j)) & 255u);
+          }
+        } else {
 #pragma unroll
         for (int j = 0; j < kV; ++j) {
           const uint4 kj = kv4[j];
@@ -396,11 +463,14 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
             }
           }
         }
-        part = FP8 ? a.w[(size_t)row * H + l] * a.q_scale[(size_t)row * H + l] * relu(c)
+        }
+        part = FP8 ? a.w[(size_t)row * H + l] * reinterpret_cast<const float*>(a.q_scale)[(size_t)row * H + l] *
+                         relu(c)
                    : a.w[(size_t)row * H + l] * relu(c);
       }
       part = wave_sum(part);
       if (FP8) part *= ks;
+      if (a.score_bf16) part = round_bf16(part);
       if (l == 0) {
         out[e] = part;
         s_sc[0] = part;
@@ -412,7 +482,22 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
     auto store_key = [&](float iv) -> float {
       const size_t krow = (size_t)b * a.E_cap + e;
       float ks = 1.f;
-      if constexpr (FP8) {
+      if constexpr (FP4) {
+        // blocks of 32 coordinates = lane groups of 32 of waves 0 and 1;
+        // codes to the cache and to s_key (64 bytes), then the 4 scales
+        uint32_t sc;
+        const uint32_t code = mx_quantize_lane(tid < kD ? iv : 0.f, &sc);
+        const uint32_t odd = __shfl_xor(code, 1, 64);
+        if (tid < kD && (tid & 1) == 0) {
+          const uint8_t byte = (uint8_t)(code | (odd << 4));
+          reinterpret_cast<uint8_t*>(f.idx_cache)[krow * (kD / 2) + tid / 2] = byte;
+          reinterpret_cast<uint8_t*>(s_key)[tid / 2] = byte;
+        }
+        if (tid < kD && (tid & 31) == 0) {
+          reinterpret_cast<uint8_t*>(f.idx_scale)[krow * (kD / 32) + tid / 32] = (uint8_t)sc;
+          reinterpret_cast<uint8_t*>(s_key)[kD / 2 + tid / 32] = (uint8_t)sc;
+        }
+      } else if constexpr (FP8) {
         float am = wave_max(tid < kD ? fabsf(iv) : 0.f);
         if (l == 0) s_red[w] = am;
         __syncthreads();
@@ -424,7 +509,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
           reinterpret_cast<uint8_t*>(f.idx_cache)[krow * kD + tid] = code;
           reinterpret_cast<uint8_t*>(s_key)[tid] = code;
         }
-        if (tid == 0) f.idx_scale[krow] = ks;
+        if (tid == 0) reinterpret_cast<float*>(f.idx_scale)[krow] = ks;
       } else {
         if (tid < kD) {
           const uint16_t v = f32_to_bf16(iv);
@@ -506,11 +591,10 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
         const float* bp = jb < Si ? bias(f.ibias_a, f.ibias_b, kD, jb) : nullptr;
         rib = bp ? *reinterpret_cast<const uint4*>(bp + 4 * cb) : uint4{0, 0, 0, 0};
       }
-      constexpr int kV = kD * (FP8 ? 1 : 2) / 16;
       uint4 qreg[kV];
       if (w == 0 && l < H) {
         const uint4* qv = reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(a.q) +
-                                                         ((size_t)row * H + l) * kD * (FP8 ? 1 : 2));
+                                                         ((size_t)row * H + l) * kQB);
 #pragma unroll
         for (int j = 0; j < kV; ++j) qreg[j] = qv[j];
       }
@@ -687,7 +771,8 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
 }
 
 bool index_mfma_supported(const IndexArgs& a) {
-  return (a.idx_dtype == BF16 || a.idx_dtype == E4M3) && a.d_I == kD && a.H_I % 16 == 0 && a.H_I <= 64;
+  return (a.idx_dtype == BF16 || a.idx_dtype == E4M3 || a.idx_dtype == MXFP4) && a.d_I == kD && a.H_I % 16 == 0 &&
+         a.H_I <= 64;
 }
 
 // workgroups that fit on the device at once for a kernel of 256 threads
@@ -724,64 +809,71 @@ static ScorerPlan scorer_plan(const IndexArgs& a, int resident, int use_hist, in
 }
 
 // per device: the grid of the scan is sized to the device's resident count
-template <int FP8, int HT>
+template <int FMT, int HT>
 static int scorer_resident() {
   static std::atomic<int> resident[kMaxDevices];
   const int dev = current_device();
-  if (dev < 0) return resident_wgs(index_score_mfma_kernel<FP8, HT>);
+  if (dev < 0) return resident_wgs(index_score_mfma_kernel<FMT, HT>);
   int r = resident[dev].load(std::memory_order_relaxed);
   if (!r) {
-    r = resident_wgs(index_score_mfma_kernel<FP8, HT>);
+    r = resident_wgs(index_score_mfma_kernel<FMT, HT>);
     resident[dev].store(r, std::memory_order_relaxed);
   }
   return r;
 }
 
-template <int FP8, int HT>
+template <int FMT, int HT>
 static hipError_t launch_scorer(const IndexArgs& a, TopkWs& ws, int use_hist, int allow_fuse,
                                 int* n_wg_fused, const FoldArgs* fold, hipStream_t s) {
   const int with_fold = fold ? 1 : 0;
-  const ScorerPlan p = scorer_plan(a, scorer_resident<FP8, HT>(), use_hist, allow_fuse && ws.sync != nullptr,
+  const ScorerPlan p = scorer_plan(a, scorer_resident<FMT, HT>(), use_hist, allow_fuse && ws.sync != nullptr,
                                    with_fold);
   if (with_fold && !p.fuse) return hipErrorInvalidValue;  // the caller checks index_fold_fusable first
   *n_wg_fused = p.fuse ? p.per_row : 0;
   ws.list_stride = p.list_stride;  // (also read by the resolve kernel)
   FoldArgs f = fold ? *fold : FoldArgs{};
   dim3 grid(p.per_row, a.B * a.Tq), block(256);
-  CSA_LAUNCH("index_score_mfma", (index_score_mfma_kernel<FP8, HT>), grid, block, 0, s, a, ws, use_hist, p.fuse,
+  CSA_LAUNCH("index_score_mfma", (index_score_mfma_kernel<FMT, HT>), grid, block, 0, s, a, ws, use_hist, p.fuse,
              f, with_fold, fused_wait_polls());
   return hipGetLastError();
 }
 
-template <int FP8>
+template <int FMT>
 static int resident_for(int HT) {
-  if (HT == 4) return scorer_resident<FP8, 4>();
-  if (HT == 3) return scorer_resident<FP8, 3>();
-  if (HT == 2) return scorer_resident<FP8, 2>();
-  return scorer_resident<FP8, 1>();
+  if (HT == 4) return scorer_resident<FMT, 4>();
+  if (HT == 3) return scorer_resident<FMT, 3>();
+  if (HT == 2) return scorer_resident<FMT, 2>();
+  return scorer_resident<FMT, 1>();
 }
+
+static int scan_format(int idx_dtype) { return idx_dtype == MXFP4 ? 2 : (idx_dtype == E4M3 ? 1 : 0); }
 
 bool index_fold_fusable(const IndexArgs& a, const FoldArgs& f, bool split) {
   if (!split || !index_mfma_supported(a) || a.Tq != 1 || f.B != a.B || f.dtype != BF16 || f.idx_dtype != a.idx_dtype ||
       f.d_I != kD || a.n_add != 0)
     return false;
-  const int resident = a.idx_dtype == E4M3 ? resident_for<1>(a.H_I / 16) : resident_for<0>(a.H_I / 16);
+  const int fmt = scan_format(a.idx_dtype);
+  const int resident = fmt == 2 ? resident_for<2>(a.H_I / 16)
+                                : (fmt == 1 ? resident_for<1>(a.H_I / 16) : resident_for<0>(a.H_I / 16));
   return scorer_plan(a, resident, 1, 1, 1).fuse != 0;
+}
+
+template <int FMT>
+static hipError_t launch_scorer_fmt(const IndexArgs& a, TopkWs& ws, int use_hist, int allow_fuse,
+                                    int* n_wg_fused, const FoldArgs* fold, hipStream_t s) {
+  const int HT = a.H_I / 16;
+  if (HT == 4) return launch_scorer<FMT, 4>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  if (HT == 3) return launch_scorer<FMT, 3>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  if (HT == 2) return launch_scorer<FMT, 2>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  return launch_scorer<FMT, 1>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
 }
 
 hipError_t launch_index_score_mfma(const IndexArgs& a, TopkWs& ws, int use_hist, int allow_fuse,
                                    int* n_wg_fused, const FoldArgs* fold, hipStream_t s) {
-  const int HT = a.H_I / 16;
-  if (a.idx_dtype == E4M3) {
-    if (HT == 4) return launch_scorer<1, 4>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
-    if (HT == 3) return launch_scorer<1, 3>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
-    if (HT == 2) return launch_scorer<1, 2>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
-    return launch_scorer<1, 1>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
-  }
-  if (HT == 4) return launch_scorer<0, 4>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
-  if (HT == 3) return launch_scorer<0, 3>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
-  if (HT == 2) return launch_scorer<0, 2>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
-  return launch_scorer<0, 1>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  const int fmt = scan_format(a.idx_dtype);
+  if (fmt == 2) return launch_scorer_fmt<2>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  if (fmt == 1) return launch_scorer_fmt<1>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  return launch_scorer_fmt<0>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
 }
 
 }  // namespace csa

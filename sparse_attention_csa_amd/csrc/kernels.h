@@ -32,7 +32,9 @@ class ProfScope {
     hipLaunchKernelGGL(kern, grid, block, shm, stream, __VA_ARGS__);    \
   } while (0)
 
-enum Dt { F32 = 0, BF16 = 1, E4M3 = 2 };
+// storage formats (the csa_dtype codes); MXFP4 vectors are packed E2M1
+// pairs with one E8M0 scale byte per 32 values
+enum Dt { F32 = 0, BF16 = 1, E4M3 = 2, MXFP4 = 3 };
 
 // Host-side values that depend on the device (occupancy, LDS attributes set
 // on a kernel) are cached per device id, below this bound.
@@ -54,7 +56,7 @@ struct CompressArgs {
   int B, T, c, m;
   void* out;
   int out_dtype;
-  float* out_scale;
+  void* out_scale;  // E4M3: float [B][E_cap]; MXFP4: uint8 [B][E_cap][c/32]
   int E_cap;
   int64_t first;
   size_t seq_stride;       // elements between sequences of ca/za/cb/zb (0: T*c or T*lw)
@@ -65,7 +67,7 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 // decode-step fold of the pending block + append of the new token
 struct FoldArgs {
   int dtype;      // kv dtype (F32 / BF16) of streams, tails, caches
-  int idx_dtype;  // indexer-cache dtype (F32 / BF16 / E4M3) or -1 (no indexer)
+  int idx_dtype;  // indexer-cache dtype (F32 / BF16 / E4M3 / MXFP4) or -1 (no indexer)
   int B, c, d_I, m, R, n_win, vis, overlap;
   const int64_t* pos;
   int32_t* n_entries;
@@ -77,8 +79,8 @@ struct FoldArgs {
   void* idx_tail;           // [B][4][R][d_I]
   void* win_ring;           // [B][n_win][c]
   void* kv_cache;           // [B][E_cap][c]
-  void* idx_cache;          // [B][E_cap][d_I]
-  float* idx_scale;         // [B][E_cap]
+  void* idx_cache;          // [B][E_cap][d_I] (MXFP4: [B][E_cap][d_I/2] bytes)
+  void* idx_scale;          // E4M3: float [B][E_cap]; MXFP4: uint8 [B][E_cap][d_I/32]
   int E_cap;
   const float *bias_a, *bias_b, *ibias_a, *ibias_b;
 };
@@ -102,11 +104,12 @@ hipError_t launch_prefill_state(const PrefillStateArgs& a, hipStream_t s);
 // ------------------------------------------------------------ indexer + top-k
 struct IndexArgs {
   int idx_dtype;
-  const void* q;        // [B][Tq][H_I][d_I]
-  const float* q_scale; // [B][Tq][H_I]
+  const void* q;        // [B][Tq][H_I][d_I] (MXFP4: d_I/2 bytes per vector)
+  const void* q_scale;  // E4M3: float [B][Tq][H_I]; MXFP4: uint8 [B][Tq][H_I][d_I/32]
   const float* w;       // [B][Tq][H_I]
   const void* keys;     // [B][E_cap][d_I]
-  const float* k_scale; // [B][E_cap]
+  const void* k_scale;  // E4M3: float [B][E_cap]; MXFP4: uint8 [B][E_cap][d_I/32]
+  int score_bf16;       // 1: scores are rounded to bfloat16 (nearest-even) before the selection
   const int64_t* q_pos; // [B][Tq], or null: query tq is at q_pos0 + tq
   int64_t q_pos0;
   const int32_t* n_entries;

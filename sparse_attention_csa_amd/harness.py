@@ -1,7 +1,8 @@
 """Device-side sessions for a decode step or a prefill chunk of one layer.
 
 A session takes inputs given *by position* (a dict of NumPy arrays: bf16 as
-uint16 bit patterns, e4m3 as uint8 codes with float32 scales, float32 as is)
+uint16 bit patterns, e4m3 as uint8 codes with float32 scales, mxfp4 as packed
+uint8 codes with uint8 E8M0 block scales, float32 as is)
 and lays them into the library's state layout: the window ring (position p in
 slot p % n_win), the compression tail ring (slot p % R, R = 3m with overlap
 and 2m without), the compressed caches and their entry counts.  It then calls
@@ -21,7 +22,7 @@ def dev(arr, kind, device="cuda"):
     a = np.ascontiguousarray(arr)
     if kind == "bf16":
         return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
-    if kind == "e4m3":
+    if kind in ("e4m3", "mxfp4", "u8"):
         return torch.from_numpy(a.view(np.uint8)).to(device)
     if kind == "f32":
         return torch.from_numpy(a.astype(np.float32)).to(device)
@@ -37,7 +38,13 @@ def to_host_bits(t):
     return t.cpu().numpy()
 
 
-DTYPE_CODE = {"f32": L.CSA_F32, "bf16": L.CSA_BF16, "e4m3": L.CSA_E4M3}
+DTYPE_CODE = {"f32": L.CSA_F32, "bf16": L.CSA_BF16, "e4m3": L.CSA_E4M3, "mxfp4": L.CSA_MXFP4}
+SCALE_KIND = {"e4m3": "f32", "mxfp4": "u8"}  # storage of the scales of a scaled format
+
+
+def scales_dev(arr, idk, device):
+    """Upload the scales of a scaled indexer format (None otherwise)."""
+    return dev(arr, SCALE_KIND[idk], device) if idk in SCALE_KIND else None
 
 
 def make_desc(g):
@@ -54,6 +61,7 @@ def make_desc(g):
     d.idx_dtype = DTYPE_CODE[g["idx_dtype"]] if g.get("idx_dtype") else 0
     d.scale = g["scale"]
     d.split_rows = int(g.get("split_rows") or 0)
+    d.score_bf16 = 1 if g.get("score_dtype") == "bf16" else 0
     return d
 
 
@@ -76,9 +84,14 @@ class _State:
         self.idx_cache = self.idx_scale = self.idx_tail = self.ibias_a = self.ibias_b = None
         if g["kind"] == "csa":
             d_I = g["d_I"]
-            idt = torch.uint8 if g["idx_dtype"] == "e4m3" else _KV[g["idx_dtype"]]
-            self.idx_cache = torch.zeros((B, E_cap, d_I), dtype=idt, device=device)
-            if g["idx_dtype"] == "e4m3":
+            idk = g["idx_dtype"]
+            if idk == "mxfp4":
+                self.idx_cache = torch.zeros((B, E_cap, d_I // 2), dtype=torch.uint8, device=device)
+                self.idx_scale = torch.zeros((B, E_cap, d_I // 32), dtype=torch.uint8, device=device)
+            else:
+                idt = torch.uint8 if idk == "e4m3" else _KV[idk]
+                self.idx_cache = torch.zeros((B, E_cap, d_I), dtype=idt, device=device)
+            if idk == "e4m3":
                 self.idx_scale = torch.ones((B, E_cap), dtype=torch.float32, device=device)
             self.idx_tail = torch.zeros((B, 4, self.R, d_I), dtype=tdt, device=device)
             self.ibias_a = dev(g["ibias_a"], "f32", device)
@@ -129,8 +142,8 @@ class DecodeSession:
         if g["kind"] == "csa":
             idk = g["idx_dtype"]
             st.idx_cache.copy_(dev(g["idx_cache"], idk, device))
-            if idk == "e4m3":
-                st.idx_scale.copy_(dev(g["idx_scale"], "f32", device))
+            if idk in SCALE_KIND:
+                st.idx_scale.copy_(scales_dev(g["idx_scale"], idk, device))
             itail = torch.zeros_like(st.idx_tail)
             for si, sname in enumerate(("ica", "iza", "icb", "izb")):
                 src = dev(g["tail_" + sname], kvk, device)
@@ -166,7 +179,7 @@ def decode_io(g, device="cuda"):
         io["idx_streams"] = torch.stack(
             [dev(g["new_" + s], kvk, device) for s in ("ica", "iza", "icb", "izb")], dim=1)
         io["q_idx"] = dev(g["q_idx"], idk, device)
-        io["q_scale"] = dev(g["q_scale"], "f32", device) if idk == "e4m3" else None
+        io["q_scale"] = scales_dev(g["q_scale"], idk, device)
         io["w_idx"] = dev(g["w_idx"], "f32", device)
         io["topk_idx"] = torch.empty((B, g["k"]), dtype=torch.int32, device=device)
         io["topk_cnt"] = torch.empty((B,), dtype=torch.int32, device=device)
@@ -212,9 +225,9 @@ class PrefillSession:
             io["idx_streams"] = torch.stack([dev(g[s], kvk, device) for s in ("ica", "iza", "icb", "izb")],
                                             dim=1)
             io["q_idx"] = dev(g["q_idx"], idk, device)
-            io["q_scale"] = dev(g["q_scale"], "f32", device) if idk == "e4m3" else None
-            if idk == "e4m3":
-                st.idx_scale.copy_(dev(g["idx_scale"], "f32", device))
+            io["q_scale"] = scales_dev(g["q_scale"], idk, device)
+            if idk in SCALE_KIND:
+                st.idx_scale.copy_(scales_dev(g["idx_scale"], idk, device))
             io["w_idx"] = dev(g["w_idx"], "f32", device)
             io["topk_idx"] = torch.empty((B, T, g["k"]), dtype=torch.int32, device=device)
             io["topk_cnt"] = torch.empty((B, T), dtype=torch.int32, device=device)

@@ -9,6 +9,13 @@
 * Layer-produced e4m3 keys: a stored code may be either neighbour when the
   value sits within float32 accuracy of a rounding boundary; selections are
   accepted when some such rounding makes them a top-k (topk_check_bounds).
+* MXFP4 keys the layer produces: a block's scale or an element's code may
+  take either rounding when the value sits within float32 accuracy of a
+  boundary (mxfp4_alternatives).
+* bf16 index scores: each entry's score is known within the bf16 roundings
+  of its float32 error interval; the selection must be the exact top-k,
+  ties to the lower id, of some scores within those intervals
+  (topk_check_intervals).
 * Floating outputs: per row, max|gpu - ref| / max(max|ref|, 1e-3 * median
   row max) <= tol, with tol = 1e-4 for float32 paths and 2e-2 for bfloat16.
   The worst row, the global max-abs error and the lse error are reported.
@@ -179,6 +186,133 @@ def prefill_err(g, b, i, idx_new, n_vis):
         q = Stored(g["q_idx"][b][i], idk, None if qs is None else qs[b][i]).all()
         return score_error_bound(q, g["w_idx"][b][i], keys.rows(slice(0, n_vis)))
     return f
+
+
+def mxfp4_alternatives(raw_row, rel=FOLD_REL, max_amb=6):
+    """Every value row that quantising ``raw_row`` to MXFP4 may give when
+    the value is computed in float32 (relative accuracy ``rel``): per block
+    of 32, each E8M0 scale that a block maximum within rel of the exact one
+    selects, and under each scale, both E2M1 neighbours of every element
+    within rel of a rounding boundary.  Rounding is monotone, so the
+    candidates are the roundings of the value moved by -rel and +rel.  At
+    most 2**max_amb rows."""
+    from oracle.formats import MX_BLOCK, _round_e2m1, e2m1_to_f64, mxfp4_quantize
+    x = np.asarray(raw_row, np.float64)
+    rows = [mxfp4_quantize(x)[2]]
+
+    def code_of(amax):
+        if amax <= 0:
+            return 0
+        _, e = np.frexp(amax)
+        return int(np.clip(e - 1 - 2 + 127, 0, 254))
+
+    for blk in range(x.size // MX_BLOCK):
+        sl = slice(blk * MX_BLOCK, (blk + 1) * MX_BLOCK)
+        xb = x[sl]
+        amax = float(np.abs(xb).max())
+        variants = []
+        for code in sorted({code_of(amax * (1 - rel)), code_of(amax), code_of(amax * (1 + rel))}):
+            scale = np.ldexp(1.0, code - 127)
+            y = xb / scale
+            lo = e2m1_to_f64(_round_e2m1(np.abs(y) * (1 - rel)))
+            hi = e2m1_to_f64(_round_e2m1(np.abs(y) * (1 + rel)))
+            vs = [lo.copy()]
+            for i in np.where(lo != hi)[0]:
+                vs += [v.copy() for v in vs]
+                for v in vs[len(vs) // 2:]:
+                    v[i] = hi[i]
+            variants += [np.sign(y) * v * scale for v in vs]
+        uniq = []
+        for v in variants:
+            if not any(np.array_equal(v, u) for u in uniq):
+                uniq.append(v)
+        if len(uniq) > 1:
+            assert len(rows) * len(uniq) <= 2 ** max_amb, "too many ambiguous roundings in one key"
+            new = []
+            for r in rows:
+                for v in uniq:
+                    r2 = r.copy()
+                    r2[sl] = v
+                    new.append(r2)
+            rows = new
+    return rows
+
+
+def ambiguous_mxfp4_keys(raw_rows, ids, rel=FOLD_REL):
+    """{id: alternative value rows} for layer-produced MXFP4 keys whose
+    stored codes or scales are not settled by float32 accuracy."""
+    out = {}
+    for s, raw in zip(ids, raw_rows):
+        alts = mxfp4_alternatives(raw, rel)
+        if len(alts) > 1:
+            out[int(s)] = alts
+    return out
+
+
+def bf16_score_intervals(scores, err, bounds=None):
+    """(lo, hi): the bfloat16 scores a float32 evaluation may round to, per
+    entry.  ``scores`` are the exact (float64, unrounded) scores, ``err``
+    their float32 evaluation error bounds, ``bounds`` ({id: (lo, hi)})
+    widens entries whose key is only known within its rounding
+    alternatives.  Rounding to bf16 is monotone, so the evaluated score
+    within [s - e, s + e] rounds into [bf16(s - e), bf16(s + e)]."""
+    from oracle.formats import round_to_bf16
+    s = np.asarray(scores, np.float64)
+    e = np.asarray(err, np.float64)
+    lo, hi = s - e, s + e
+    for i, (a, b) in (bounds or {}).items():
+        if i < len(s):
+            lo[i], hi[i] = a - e[i], b + e[i]
+    return round_to_bf16(lo), round_to_bf16(hi)
+
+
+def topk_check_intervals(gpu_ids, gpu_cnt, k, lo, hi):
+    """Exact top-k check over scores known within intervals [lo, hi] (the
+    bf16 scores): the GPU set S must be the top-k, ties to the lower id, of
+    some scores within the intervals.  The most favourable choice is hi on S
+    and lo elsewhere, so S is valid iff every pair i in S, j outside has
+    hi_i > lo_j, or hi_i == lo_j and i < j.  Returns (ok, n_uncertain,
+    message), n_uncertain counting the members of S whose interval is not a
+    single value."""
+    lo, hi = np.asarray(lo, np.float64), np.asarray(hi, np.float64)
+    n = len(lo)
+    gpu = np.asarray(gpu_ids)[:int(gpu_cnt)]
+    if len(gpu) != min(k, n):
+        return False, 0, f"count {len(gpu)} != {min(k, n)}"
+    if len(gpu) and (np.any(np.diff(gpu) <= 0) or gpu.min() < 0 or gpu.max() >= n):
+        return False, 0, "gpu ids not strictly ascending within the visible range"
+    inside = np.zeros(n, bool)
+    inside[gpu] = True
+    if inside.all() or not inside.any():
+        return True, 0, ""
+    m = hi[inside].min()
+    out_lo = lo[~inside]
+    if out_lo.max() > m:
+        j = int(np.where(~inside)[0][np.argmax(out_lo)])
+        return False, 0, f"entry {j} (score >= {lo[j]}) outranks a selected entry (score <= {m})"
+    at_m_in = np.where(inside & (hi == m))[0]
+    at_m_out = np.where(~inside & (lo == m))[0]
+    if at_m_out.size and at_m_in.max() > at_m_out.min():
+        return False, 0, f"tie at {m}: selected id {at_m_in.max()} above unselected id {at_m_out.min()}"
+    return True, int(np.count_nonzero(lo[inside] != hi[inside])), ""
+
+
+def check_selection(ids, cnt, k, ref, err, bounds=None, score_dtype="f32"):
+    """The selection rule for one query.  ``ref`` is the oracle's answer
+    (sel, scores, scores_raw), ``err`` its score_error_bound (array or lazy
+    function), ``bounds`` the score bounds of keys with several valid
+    roundings.  float32 scores: topk_check_bounds; bf16 scores:
+    topk_check_intervals over the bf16 roundings of the float32 error
+    intervals.  Returns (ok, swapped, message), swapped true when the GPU
+    set differs from the oracle's (its attention must then be compared
+    with the oracle's on the GPU set)."""
+    if score_dtype != "bf16":
+        return topk_check_bounds(ids, cnt, ref["sel"], ref["scores"], k, bounds or {}, err=err)
+    e = err() if callable(err) else err
+    lo, hi = bf16_score_intervals(ref["scores_raw"], e, bounds)
+    ok, _, msg = topk_check_intervals(ids, cnt, k, lo, hi)
+    gpu = np.asarray(ids)[:int(cnt)]
+    return ok, int(not np.array_equal(gpu, ref["sel"])), msg
 
 
 def rel_err_rows(gpu, ref):

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = L.lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.csa_abi_version() == 2
+    assert lib.csa_abi_version() == 3
 
 
 def _status(fn, *args):
@@ -53,10 +53,11 @@ def test_compress_rejects_bad_arguments():
     s = lib.csa_compress(1, P, P, 512, None, None, None, None, None, None, None,
                          1, 8, 512, 4, P, 1, None, 2, 1, None)
     assert s == L.CSA_ERR_ARG and "E_cap" in L.last_error()
-    # E4M3 output without scales
-    s = lib.csa_compress(1, P, P, 512, None, None, None, None, None, None, None,
-                         1, 8, 512, 4, P, 2, None, 2, 0, None)
-    assert s == L.CSA_ERR_ARG
+    # E4M3 / MXFP4 output without scales
+    for out_dt in (2, 3):
+        s = lib.csa_compress(1, P, P, 512, None, None, None, None, None, None, None,
+                             1, 8, 512, 4, P, out_dt, None, 2, 0, None)
+        assert s == L.CSA_ERR_ARG
 
 
 def test_index_topk_rejects_bad_arguments():
@@ -65,7 +66,7 @@ def test_index_topk_rejects_bad_arguments():
     ws_need = lib.csa_index_topk_workspace(2, 1, 1024, 64)
     assert ws_need >= 2 * 1024 * 4
     args = dict(dt=1, q=P, qs=None, w=P, k_=P, ks=None, pos=P, ne=P, B=2, Tq=1, H_I=64, d_I=128,
-                E=1024, m=4, k=64, vis=0, ti=P, tc=P, sc=None, ws=P, wsb=ws_need, st=None)
+                E=1024, m=4, k=64, vis=0, sb=0, ti=P, tc=P, sc=None, ws=P, wsb=ws_need, st=None)
 
     def call(**kw):
         a = dict(args, **kw)
@@ -76,6 +77,10 @@ def test_index_topk_rejects_bad_arguments():
     assert call(k=4096) == L.CSA_ERR_UNSUPPORTED
     assert call(k=0) == L.CSA_ERR_ARG
     assert call(dt=2) == L.CSA_ERR_ARG  # E4M3 without scales
+    assert call(dt=3) == L.CSA_ERR_ARG  # MXFP4 without scales
+    assert call(dt=3, qs=None, ks=P) == L.CSA_ERR_ARG
+    assert call(dt=4) == L.CSA_ERR_ARG  # no such format
+    assert call(sb=2) == L.CSA_ERR_ARG  # score_bf16 is 0 or 1
     assert call(wsb=ws_need - 1) == L.CSA_ERR_WORKSPACE
     assert call(ws=None) == L.CSA_ERR_WORKSPACE
     assert call(pos=None) == L.CSA_ERR_ARG
@@ -126,6 +131,13 @@ def test_layer_rejects_bad_descriptors():
     assert st == L.CSA_ERR_UNSUPPORTED and "split_rows" in L.last_error()
     d.split_rows = 0
     assert lib.hybrid_layer_workspace(C.byref(d), 8, 1, 32768) > 0
+    d.score_bf16 = 2
+    st = lib.hybrid_layer_decode(C.byref(d), C.byref(s), C.byref(io), None, 0, None)
+    assert st == L.CSA_ERR_ARG and "score_bf16" in L.last_error()
+    d.score_bf16 = 0
+    d.idx_dtype = 5
+    st = lib.hybrid_layer_decode(C.byref(d), C.byref(s), C.byref(io), None, 0, None)
+    assert st == L.CSA_ERR_ARG and "idx_dtype" in L.last_error()
 
 
 def test_product_path_does_not_import_the_oracle():

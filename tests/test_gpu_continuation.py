@@ -19,7 +19,8 @@ import workloads
 from oracle import layer as OL
 from oracle.formats import Stored
 from tests.cases import decode_from_prefill, prefix_case
-from tests.compare import ambiguous_e4m3_keys, assert_close, decode_err, prefill_err, score_bounds, topk_check_bounds
+from tests.compare import (ambiguous_e4m3_keys, ambiguous_mxfp4_keys, assert_close, check_selection, decode_err,
+                           mxfp4_alternatives, prefill_err, score_bounds)
 
 pytestmark = pytest.mark.gpu
 
@@ -76,15 +77,26 @@ def _check_e4m3_key(codes, scale, ref_row, label):
     assert flips.mean() <= 0.02, f"{label}: {flips.mean():.3f} codes differ"
 
 
-@pytest.mark.parametrize("kind,idx", [("csa", "bf16"), ("csa", "e4m3"), ("hca", None)])
+def _ambiguous(idx, raw_rows, ids):
+    if idx == "e4m3":
+        return ambiguous_e4m3_keys(raw_rows, ids)
+    if idx == "mxfp4":
+        return ambiguous_mxfp4_keys(raw_rows, ids)
+    return {}
+
+
+# (the MXFP4 case also rounds its index scores to bf16)
+@pytest.mark.parametrize("kind,idx", [("csa", "bf16"), ("csa", "e4m3"), ("csa", "mxfp4"), ("hca", None)])
 def test_prefill_then_260_decode_steps(gpu_lib, kind, idx):
     from sparse_attention_csa_amd.harness import PrefillSession
     label = f"cont-{kind}-{idx}"
     B, n0 = 2, 4096
-    H = 128 if idx == "e4m3" else 64
+    H = 128 if idx in ("e4m3", "mxfp4") else 64
     a, h = workloads.flash_prefill(seed=41, B=B, T=T0 + STEPS, n0=n0, H=H, c=512, H_I=64, d_I=128,
                                    k=128, idx_dtype=idx or "bf16")
     full = a if kind == "csa" else h
+    sdt = "bf16" if idx == "mxfp4" else "f32"
+    full["score_dtype"] = sdt
     pre = prefix_case(full, T0)
     print(f"[{label}] prefill {T0} tokens at {n0}", flush=True)
     sess = PrefillSession(pre)
@@ -92,8 +104,8 @@ def test_prefill_then_260_decode_steps(gpu_lib, kind, idx):
     torch.cuda.synchronize()
     _check_state_after_prefill(pre, sess, label)
     kv_new, idx_new, extra_kv, extra_idx = [], [], [], []
-    # e4m3 keys the layer produced whose codes float32 accuracy does not
-    # settle: their scores are checked within the bounds of both roundings
+    # e4m3 / MXFP4 keys the layer produced whose codes float32 accuracy does
+    # not settle: their scores are checked within the bounds of every rounding
     amb = [{} for _ in range(B)]
     E0 = int(pre["n_entries"][0])
     for b in range(B):
@@ -102,13 +114,19 @@ def test_prefill_then_260_decode_steps(gpu_lib, kind, idx):
         idx_new.append(ixn if ixn is not None else [])
         extra_kv.append([])
         extra_idx.append([])
-        if idx == "e4m3":
-            amb[b].update(ambiguous_e4m3_keys(raw, range(E0, E0 + len(raw))))
+        if kind == "csa":
+            amb[b].update(_ambiguous(idx, raw, range(E0, E0 + len(raw))))
+            if idx == "mxfp4":
+                got = Stored(sess.state.idx_cache[b, E0:E0 + len(raw)].cpu().numpy(), "mxfp4",
+                             sess.state.idx_scale[b, E0:E0 + len(raw)].cpu().numpy()).all()
+                for i in range(len(raw)):
+                    assert any(np.array_equal(got[i], x) for x in mxfp4_alternatives(raw[i])), \
+                        f"{label} prefill key {E0 + i} b={b}"
 
     def bounds(g1, b):
         if not amb[b]:
             return {}
-        q = Stored(g1["q_idx"][0], "e4m3", g1["q_scale"][0]).all()
+        q = Stored(g1["q_idx"][0], idx, g1["q_scale"][0]).all()
         return score_bounds(q, np.asarray(g1["w_idx"][0], np.float64), amb[b])
     # the chunk's outputs on a sample of its queries (every query is checked
     # by the prefill parity tests)
@@ -121,10 +139,10 @@ def test_prefill_then_260_decode_steps(gpu_lib, kind, idx):
                 cnt = int(sess.io["topk_cnt"][b, i])
                 bd = {}
                 if amb[b]:
-                    q = Stored(pre["q_idx"][b, i], "e4m3", pre["q_scale"][b, i]).all()
+                    q = Stored(pre["q_idx"][b, i], idx, pre["q_scale"][b, i]).all()
                     bd = score_bounds(q, np.asarray(pre["w_idx"][b, i], np.float64), amb[b])
-                ok, swaps, msg = topk_check_bounds(ids, cnt, ref["sel"], ref["scores"], pre["k"], bd,
-                                                   err=prefill_err(pre, b, i, idx_new[b], len(ref["scores"])))
+                ok, swaps, msg = check_selection(ids, cnt, pre["k"], ref,
+                                                 prefill_err(pre, b, i, idx_new[b], len(ref["scores"])), bd, sdt)
                 assert ok, f"{label} prefill q{i} b={b}: {msg}"
                 if swaps:
                     ref = OL.prefill_query(pre, b, i, kv_new[b], idx_new[b], selected=ids[:cnt])
@@ -152,19 +170,24 @@ def test_prefill_then_260_decode_steps(gpu_lib, kind, idx):
                         _check_e4m3_key(sess.state.idx_cache[b, e_before].cpu().numpy(),
                                         float(sess.state.idx_scale[b, e_before]), ref["folded_idx"][0],
                                         f"{label} t={t} folded key b={b}")
+                    elif idx == "mxfp4":
+                        got = Stored(sess.state.idx_cache[b, e_before].cpu().numpy()[None], "mxfp4",
+                                     sess.state.idx_scale[b, e_before].cpu().numpy()[None]).all()[0]
+                        assert any(np.array_equal(got, x) for x in mxfp4_alternatives(ref["folded_idx_raw"][0])), \
+                            f"{label} t={t} folded key b={b}"
                     else:
                         assert_close(f64(sess.state.idx_cache[b, e_before])[None], ref["folded_idx"][0][None],
                                      "bf16", f"{label} t={t} folded key b={b}")
-                if idx == "e4m3":
-                    amb[b].update(ambiguous_e4m3_keys(ref["folded_idx_raw"], [e_before]))
+                if kind == "csa":
+                    amb[b].update(_ambiguous(idx, ref["folded_idx_raw"], [e_before]))
                 extra_kv[b] += ref["folded_kv"]
                 extra_idx[b] += ref["folded_idx"]
             assert n_ent[b] == E_pre + len(extra_kv[b]), f"{label} t={t} n_entries b={b}"
             if kind == "csa":
                 ids = io["topk_idx"][b].cpu().numpy()
                 cnt = int(io["topk_cnt"][b])
-                ok, swaps, msg = topk_check_bounds(ids, cnt, ref["sel"], ref["scores"], full["k"], bounds(gs[b], b),
-                                                   err=decode_err(gs[b], 0, ref))
+                ok, swaps, msg = check_selection(ids, cnt, full["k"], ref, decode_err(gs[b], 0, ref),
+                                                 bounds(gs[b], b), sdt)
                 assert ok, f"{label} t={t} b={b}: {msg}"
                 swaps_total += swaps
                 if swaps:

@@ -12,8 +12,9 @@ import torch
 import workloads
 from oracle import layer as OL
 from oracle.formats import Stored
-from tests.compare import (ambiguous_e4m3_keys, assert_close, decode_err, prefill_err, score_bounds,
-                           score_error_bound, topk_check, topk_check_bounds)
+from tests.compare import (ambiguous_e4m3_keys, ambiguous_mxfp4_keys, assert_close, check_selection, decode_err,
+                           mxfp4_alternatives, prefill_err, score_bounds, score_error_bound, topk_check,
+                           topk_check_bounds)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,18 +39,21 @@ def _check_decode(g, sess, label):
             gk = f64(sess.state.kv_cache[b, e0])
             assert_close(gk[None], np.array(ref["folded_kv"][:1]), kvk, f"{label} folded kv b={b}")
         if g["kind"] == "csa":
+            idk = g["idx_dtype"]
             if ref["folded_idx"]:
-                _check_folded_key(g, sess, b, e0, ref["folded_idx"][0], label)
+                _check_folded_key(g, sess, b, e0, ref["folded_idx"][0], label, ref["folded_idx_raw"][0])
             ids = sess.io["topk_idx"][b].cpu().numpy()
             cnt = int(sess.io["topk_cnt"][b].item())
-            bd = {}
-            if g["idx_dtype"] == "e4m3" and ref["folded_idx_raw"]:
+            bd, amb = {}, {}
+            if idk == "e4m3" and ref["folded_idx_raw"]:
                 amb = ambiguous_e4m3_keys(ref["folded_idx_raw"][:1], [e0])
-                if amb:
-                    q = Stored(g["q_idx"][b], "e4m3", g["q_scale"][b]).all()
-                    bd = score_bounds(q, np.asarray(g["w_idx"][b], np.float64), amb)
-            ok, swaps, msg = topk_check_bounds(ids, cnt, ref["sel"], ref["scores"], g["k"], bd,
-                                               err=decode_err(g, b, ref))
+            elif idk == "mxfp4" and ref["folded_idx_raw"]:
+                amb = ambiguous_mxfp4_keys(ref["folded_idx_raw"][:1], [e0])
+            if amb:
+                q = Stored(g["q_idx"][b], idk, g["q_scale"][b]).all()
+                bd = score_bounds(q, np.asarray(g["w_idx"][b], np.float64), amb)
+            ok, swaps, msg = check_selection(ids, cnt, g["k"], ref, decode_err(g, b, ref), bd,
+                                             g.get("score_dtype", "f32"))
             assert ok, f"{label} b={b}: {msg}"
             swaps_total += swaps
             if swaps:
@@ -78,8 +82,16 @@ def _check_rings(g, sess, label):
                     f"{label} indexer tail {name} b={b}"
 
 
-def _check_folded_key(g, sess, b, e0, ref_row, label):
-    if g["idx_dtype"] == "e4m3":
+def _check_folded_key(g, sess, b, e0, ref_row, label, raw_row=None):
+    if g["idx_dtype"] == "mxfp4":
+        # the stored codes and scales must be one of the roundings float32
+        # accuracy allows (the oracle's own rounding in all but rare cases)
+        codes = sess.state.idx_cache[b, e0].cpu().numpy()
+        scales = sess.state.idx_scale[b, e0].cpu().numpy()
+        got = Stored(codes[None], "mxfp4", scales[None]).all()[0]
+        alts = mxfp4_alternatives(raw_row) if raw_row is not None else [ref_row]
+        assert any(np.array_equal(got, a) for a in alts), f"{label} mxfp4 key b={b}"
+    elif g["idx_dtype"] == "e4m3":
         codes = sess.state.idx_cache[b, e0].cpu().numpy()
         scale = sess.state.idx_scale[b, e0].cpu().numpy()
         got = Stored(codes[None], "e4m3", np.array([scale])).all()[0]
