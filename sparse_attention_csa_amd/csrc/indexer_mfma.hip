@@ -93,6 +93,9 @@ struct Geo {
   static constexpr int kKpp = 16 / kPieces;  // keys per piece
   static constexpr int kCpk = kKeyB / 16;    // 16-byte chunks per key
   static constexpr int kU = FMT == 2 ? 8 : (FMT == 1 ? 6 : 4);  // tiles per batch (even)
+  // per-wavefront LDS: a batch's transpose buffer; MXFP4 needs none, only
+  // room for the fold workgroup's staging (a quarter each)
+  static constexpr int kTrB = FMT == 2 ? 8192 : kU * kTileB;
   CSA_DEV static int sw(int k, int j) { return FMT == 1 ? (k ^ j) : (k + 4 * j); }
   // LDS byte offset of chunk q of key c within a tile
   CSA_DEV static int lds_off(int c, int q) {
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   constexpr bool FP8 = FMT == 1, FP4 = FMT == 2;
   typedef Geo<FMT> G;
   constexpr int kU = G::kU;
-  __shared__ __attribute__((aligned(1024))) char s_tr[4][kU * G::kTileB];  // per-wave transpose buffer
+  __shared__ __attribute__((aligned(1024))) char s_tr[4][G::kTrB];  // per-wave transpose buffer
   __shared__ int s_hist[kTopkBins];
   __shared__ __attribute__((aligned(16))) float s_sc[kTopkFuseCap];  // fused: this workgroup's scores, by entry - first entry
   __shared__ int s_misc[16];
@@ -381,29 +384,47 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   }
   if (fold_wg) {
     // the step's compressor work for this sequence (the scan above was empty).
-    // First the new token's appends to the tail rings and the window ring:
-    // they need only the step's inputs, and the tail slot they write
-    // (t mod R, with R > 2m) is never a source of the fold.
-    {
-      const int nstr = f.overlap ? 4 : 2;
-      const int slot_t = (int)(t % f.R);
-      const uint16_t* mio = reinterpret_cast<const uint16_t*>(f.streams) + (size_t)b * nstr * f.c;
-      uint16_t* mtl = reinterpret_cast<uint16_t*>(f.tail) + (size_t)b * nstr * f.R * f.c;
-      for (int i = tid; i < nstr * f.c; i += 256) {
-        const int sc = i / f.c, r = i % f.c;
-        mtl[((size_t)sc * f.R + slot_t) * f.c + r] = mio[(size_t)sc * f.c + r];
-      }
-      const uint16_t* iio = reinterpret_cast<const uint16_t*>(f.idx_streams) + (size_t)b * 4 * kD;
-      uint16_t* itl = reinterpret_cast<uint16_t*>(f.idx_tail) + (size_t)b * 4 * f.R * kD;
-      for (int i = tid; i < 4 * kD; i += 256) {
-        const int sc = i / kD, r = i % kD;
-        itl[((size_t)sc * f.R + slot_t) * kD + r] = iio[(size_t)sc * kD + r];
-      }
-      uint16_t* ring = reinterpret_cast<uint16_t*>(f.win_ring) + ((size_t)b * f.n_win + t % f.n_win) * f.c;
-      const uint16_t* xn = reinterpret_cast<const uint16_t*>(f.x_new) + (size_t)b * f.c;
-      for (int i = tid; i < f.c; i += 256) ring[i] = xn[i];
+    // The new token's appends to the tail rings and the window ring need only
+    // the step's inputs, and the tail slot they write (t mod R, with R > 2m)
+    // is never a source of the fold: their loads go out first, together with
+    // the fold's (one round trip for both), and their stores come last.  In
+    // 16-byte chunks: the main streams, the indexer streams, the window row.
+    const int nstr = f.overlap ? 4 : 2;
+    const int slot_t = (int)(t % f.R);
+    const int n_mc = nstr * f.c / 8, n_ic = 4 * kD / 8, n_ap = n_mc + n_ic + f.c / 8;
+    constexpr int kAp = 2;  // chunks per thread: n_ap <= 4 * 512 / 8 + 64 + 64 = 384
+    uint4 ap[kAp];
+#pragma unroll
+    for (int u = 0; u < kAp; ++u) {
+      const int i = tid + 256 * u;
+      const uint16_t* src = nullptr;
+      if (i < n_mc)
+        src = reinterpret_cast<const uint16_t*>(f.streams) + (size_t)b * nstr * f.c + 8 * i;
+      else if (i < n_mc + n_ic)
+        src = reinterpret_cast<const uint16_t*>(f.idx_streams) + (size_t)b * 4 * kD + 8 * (i - n_mc);
+      else if (i < n_ap)
+        src = reinterpret_cast<const uint16_t*>(f.x_new) + (size_t)b * f.c + 8 * (i - n_mc - n_ic);
+      ap[u] = src ? *reinterpret_cast<const uint4*>(src) : uint4{0, 0, 0, 0};
     }
-  
+    auto store_appends = [&]() {
+#pragma unroll
+      for (int u = 0; u < kAp; ++u) {
+        const int i = tid + 256 * u;
+        uint16_t* dst = nullptr;
+        if (i < n_mc) {
+          const int sc = 8 * i / f.c, r = 8 * i % f.c;
+          dst = reinterpret_cast<uint16_t*>(f.tail) + (((size_t)b * nstr + sc) * f.R + slot_t) * f.c + r;
+        } else if (i < n_mc + n_ic) {
+          const int j = 8 * (i - n_mc), sc = j / kD, r = j % kD;
+          dst = reinterpret_cast<uint16_t*>(f.idx_tail) + (((size_t)b * 4 + sc) * f.R + slot_t) * kD + r;
+        } else if (i < n_ap) {
+          dst = reinterpret_cast<uint16_t*>(f.win_ring) + ((size_t)b * f.n_win + t % f.n_win) * f.c +
+                8 * (i - n_mc - n_ic);
+        }
+        if (dst) *reinterpret_cast<uint4*>(dst) = ap[u];
+      }
+    };
+
     // bytes of one query vector, in 16-byte loads
     constexpr int kQB = FP4 ? kD / 2 : (FP8 ? kD : 2 * kD);
     constexpr int kV = kQB / 16;
@@ -533,7 +554,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
       const bool use_bi = e > 0;               // the indexer key always overlaps
       const int Sm = use_bm ? 2 * m : m, Si = use_bi ? 2 * m : m;
       constexpr int kS = 2 * kFastFoldM;
-      static_assert(kS * kFastFoldC * 2 * 2 + kS * kD * 8 + 288 <= 4 * kU * G::kTileB, "fold staging fits");
+      static_assert(kS * kFastFoldC * 2 * 2 + kS * kD * 8 + 288 <= sizeof(s_tr), "fold staging fits");
       static_assert(kS * kFastFoldC <= kTopkFuseCap, "main biases fit the score buffer");
       uint16_t* mz = reinterpret_cast<uint16_t*>(&s_tr[0][0]);  // [kS][kFastFoldC] logits
       uint16_t* mx = mz + kS * kFastFoldC;                      // [kS][kFastFoldC] contents
@@ -664,6 +685,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
         if (tid < W) reinterpret_cast<uint16_t*>(f.kv_cache)[((size_t)b * a.E_cap + e) * f.c + r0 + tid] = f32_to_bf16(v);
       }
     }
+    store_appends();
   }
   if (use_hist) {
     __syncthreads();
