@@ -76,7 +76,8 @@ const char* csa_last_error(void);
 
 /* ABI version of this header (bumped on incompatible change; 2 added
  * csa_layer_desc.split_rows; 3 added CSA_MXFP4 with untyped scale pointers,
- * csa_layer_desc.score_bf16 and the score_bf16 argument of csa_index_topk). */
+ * csa_layer_desc.score_bf16, the score_bf16 argument of csa_index_topk, and
+ * the normalisation / rotary fields of csa_layer_desc and csa_layer_state). */
 int csa_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -239,6 +240,19 @@ typedef struct {
                      /* CSA_ERR_UNSUPPORTED).  Prefill chunks ignore it.      */
   int score_bf16;    /* CSA: 1 = index scores rounded to bfloat16 before the  */
                      /* top-k (see csa_index_topk); 0 = float32 scores        */
+  int norm_rope;     /* 1: the steps on either side of the core attention     */
+                     /* ([book] ch. 7 "Query and KV normalization", "Partial  */
+                     /* rotary position embeddings", "Why the output is      */
+                     /* de-rotated"): every query head and every produced KV  */
+                     /* vector (compressed entry, window row) is RMSNorm-ed,  */
+                     /* v * g / sqrt(mean(v^2) + norm_eps), then its last     */
+                     /* rope_dims coordinates are rotated in pairs (2i, 2i+1) */
+                     /* by pos * inv_freq[i]; the output's last rope_dims     */
+                     /* coordinates are rotated back by the query position.   */
+                     /* Positions: a query or window row its token's, entry e */
+                     /* m * e (its block's first token).  0: off.             */
+  int rope_dims;     /* rotated coordinates (even, 2..c) when norm_rope       */
+  float norm_eps;    /* RMSNorm epsilon when norm_rope                        */
 } csa_layer_desc;
 
 /* Number of compressor streams per token: 4 (ca, za, cb, zb) with overlap,
@@ -258,6 +272,11 @@ typedef struct {
   const float* ibias_a;  /* [m][d_I] indexer-key biases (CSA, or NULL)         */
   const float* ibias_b;
   const float* sink;     /* [H] sink logits or NULL                            */
+  const float* q_norm_w;       /* [c] RMSNorm scale of the query heads         */
+  const float* kv_norm_w;      /* [c] RMSNorm scale of the KV head             */
+  const double* rope_inv_freq; /* [rope_dims/2] inverse frequencies (the      */
+                               /* caller's scaling, e.g. base^(-2i/rope_dims)) */
+                               /* (the three only read when norm_rope)         */
 } csa_layer_state;
 
 /* One decode step: one new token per sequence at position pos[b]. */
@@ -305,14 +324,18 @@ size_t hybrid_layer_workspace(const csa_layer_desc* desc, int B, int T, int E_ca
  * entry becomes visible at this position (at most one per step; the caller
  * steps every position); CSA: score the visible entries, keep the top-k and
  * attend over them + window + sink; HCA: attend over all visible entries +
- * window + sink.  n_entries is updated on the device. */
+ * window + sink.  n_entries is updated on the device.  With norm_rope the
+ * new token's window row enters the ring prepared (normalised and rotated),
+ * as does the folded entry; the ring and the cache hold prepared vectors. */
 csa_status hybrid_layer_decode(const csa_layer_desc* desc, csa_layer_state* state,
                                const csa_decode_io* io, void* ws, size_t ws_bytes, void* stream);
 
 /* Prefill chunk: compress the chunk's blocks into the cache (the first uses
  * the previous block's branch b from the tail unless pos0 == 0), answer all T
  * queries causally, then leave the window ring and the tail holding the
- * chunk's last tokens so that decode can continue at pos0 + T. */
+ * chunk's last tokens so that decode can continue at pos0 + T.  With
+ * norm_rope the chunk's window rows (io->win, raw) and queries are prepared
+ * in the workspace, and the ring receives prepared rows. */
 csa_status hybrid_layer_prefill(const csa_layer_desc* desc, csa_layer_state* state,
                                 const csa_prefill_io* io, void* ws, size_t ws_bytes, void* stream);
 

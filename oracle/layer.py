@@ -12,11 +12,19 @@ is retained during decode"): a classical cache of completed entries plus
 bounded state (window rows and the compression tail).  Here the state is
 given by position (``tail_*`` arrays hold tokens ``tail_pos0 ..``); how the
 HIP path lays it out in memory is its own business.
+
+With ``norm_rope`` set in a case, the steps on either side of the core
+attention are included ("DeepSeek-V4" book ch. 7 "Query and KV
+normalization", "Partial rotary position embeddings", "Why the output is
+de-rotated"; see position.py): produced entries and window rows are
+normalised and rotated at their positions before storage, the query at its
+position, and the output is rotated back by the query's rotation.
 """
 
 import numpy as np
 
 from . import csa
+from . import position as P
 from .formats import Stored
 
 
@@ -63,6 +71,29 @@ def _dec(x, kind, scale=None):
     return Stored(x, kind, scale).all()
 
 
+def _nr(g):
+    """(q scale, KV scale, eps, inverse frequencies) when the layer
+    normalises and rotates its queries and KV vectors, else None."""
+    if not g.get("norm_rope"):
+        return None
+    return (g["q_norm_w"], g["kv_norm_w"], float(g["norm_eps"]), g["rope_inv_freq"])
+
+
+def _prep_kv(nr, x, pos):
+    """A produced KV vector (entry or window row) as stored for attention."""
+    return x if nr is None else P.prepare(x, nr[1], nr[2], pos, nr[3])
+
+
+def _prep_q(nr, q, t, act):
+    """The query the core attention reads: prepared, then held in the
+    activation format like every input of the core attention."""
+    return q if nr is None else csa.store_as(P.prepare(q, nr[0], nr[2], t, nr[3]), act)
+
+
+def _post(nr, o, t):
+    return o if nr is None else P.derotate(o, t, nr[3])
+
+
 # ---------------------------------------------------------------------------
 # decode step: one new token per sequence
 # ---------------------------------------------------------------------------
@@ -81,6 +112,7 @@ def decode_step(case, b, selected=None):
     m, c = g["m"], g["c"]
     kvk, idk = g["kv_dtype"], g["idx_dtype"]
     act = _act(g)
+    nr = _nr(g)
     n_have = int(g["n_entries"][b])
     need = t // m if g["vis"] == csa.VIS_PRIOR_BLOCKS else (t + 1) // m
     p0 = int(g["tail_pos0"][b])
@@ -111,7 +143,7 @@ def decode_step(case, b, selected=None):
                                          s["cb"][pb], s["zb"][pb], g["bias_b"])
             else:
                 ent = csa.compress_entry(s["ca"][a], s["za"][a], g["bias_a"])
-            folded_kv.append(csa.store_as(ent, kvk))
+            folded_kv.append(csa.store_as(_prep_kv(nr, ent, P.entry_position(e, m)), kvk))
             if g["kind"] == "csa":
                 if use_prev:
                     ik = csa.compress_entry(si["ca"][a], si["za"][a], g["ibias_a"],
@@ -124,15 +156,20 @@ def decode_step(case, b, selected=None):
     kv = CacheView(Stored(g["kv_cache"][b], kvk, None if g.get("kv_scale") is None else g["kv_scale"][b]),
                    n_have, np.array(folded_kv) if folded_kv else None)
 
+    # the window ring holds rows as stored: with normalisation and rotary
+    # positions on, the history rows are already prepared and the new
+    # token's row is prepared (and rounded to storage) by the step
     win_hist = _dec(g["win_hist"][b], act)  # positions t-(n_win-1) .. t-1
     x_new = _dec(g["x_new"][b][None], act)
+    if nr is not None:
+        x_new = csa.store_as(_prep_kv(nr, x_new, t), act)
     win_all = np.concatenate([win_hist, x_new], axis=0)
     wp0 = t - win_hist.shape[0]
 
     def win_rows(pos):
         return win_all[np.asarray(pos) - wp0]
 
-    q = _dec(g["q"][b], act)
+    q = _prep_q(nr, _dec(g["q"][b], act), t, act)
     sink = None if g["sink"] is None else np.asarray(g["sink"], np.float64)
     # (folded_idx_raw: the indexer keys before rounding to storage, for tests
     # that must know which stored codes a rounding decision settles)
@@ -147,11 +184,11 @@ def decode_step(case, b, selected=None):
                                                  m, g["k"], g["n_win"], g["scale"], g["vis"],
                                                  selected=selected, score_dtype=g.get("score_dtype", "f32"),
                                                  return_raw=True)
-        out.update(o=o, lse=lse, sel=sel, scores=scores, scores_raw=raw)
+        out.update(o=_post(nr, o, t), lse=lse, sel=sel, scores=scores, scores_raw=raw)
     else:
         o, lse = csa.hca_query(q, t, kv, n_total, win_rows, sink, m, g["n_win"], g["scale"],
                                g["vis"])
-        out.update(o=o, lse=lse)
+        out.update(o=_post(nr, o, t), lse=lse)
     return out
 
 
@@ -167,6 +204,7 @@ def prefill_entries(case, b, raw=False):
     m = g["m"]
     kvk, idk = g["kv_dtype"], g["idx_dtype"]
     act = _act(g)
+    nr = _nr(g)
     d = lambda n: _dec(g[n][b], act)  # noqa: E731
     if g["overlap"]:
         first = int(g["pos0"]) == 0
@@ -174,6 +212,9 @@ def prefill_entries(case, b, raw=False):
                            None if first else d("prev_cb"), None if first else d("prev_zb"))
     else:
         ent = csa.compress(d("ca"), d("za"), m, g["bias_a"])
+    first = int(g["pos0"]) // m  # the chunk's first entry
+    if nr is not None:
+        ent = _prep_kv(nr, ent, P.entry_position(first + np.arange(len(ent)), m))
     kv_new = csa.store_as(ent, kvk)
     idx_new = None
     if g["kind"] == "csa":
@@ -202,12 +243,17 @@ def prefill_query(case, b, i, kv_new, idx_new, selected=None):
     n_total = n_have + len(kv_new)
     wp0 = int(g["pos0"]) - (g["n_win"] - 1)
     act = _act(g)
+    nr = _nr(g)
     wstore = Stored(g["win"][b], act)
 
     def win_rows(pos):
-        return wstore.rows(np.asarray(pos) - wp0)
+        pos = np.asarray(pos)
+        rows = wstore.rows(pos - wp0)
+        # with normalisation and rotary positions on, the chunk's window rows
+        # are prepared at their positions and stored for the attention
+        return rows if nr is None else csa.store_as(_prep_kv(nr, rows, pos), act)
 
-    q = _dec(g["q"][b][i], act)
+    q = _prep_q(nr, _dec(g["q"][b][i], act), t, act)
     sink = None if g["sink"] is None else np.asarray(g["sink"], np.float64)
     if g["kind"] == "csa":
         keys = CacheView(Stored(g["idx_cache"][b], idk,
@@ -220,10 +266,10 @@ def prefill_query(case, b, i, kv_new, idx_new, selected=None):
                                                  m, g["k"], g["n_win"], g["scale"], g["vis"],
                                                  selected=selected, score_dtype=g.get("score_dtype", "f32"),
                                                  return_raw=True)
-        return {"o": o, "lse": lse, "sel": sel, "scores": scores, "scores_raw": raw}
+        return {"o": _post(nr, o, t), "lse": lse, "sel": sel, "scores": scores, "scores_raw": raw}
     o, lse = csa.hca_query(q, t, kv, n_total, win_rows, sink, m, g["n_win"], g["scale"],
                            g["vis"])
-    return {"o": o, "lse": lse}
+    return {"o": _post(nr, o, t), "lse": lse}
 
 
 # ---------------------------------------------------------------------------

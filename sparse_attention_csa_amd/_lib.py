@@ -39,7 +39,8 @@ class LayerDesc(C.Structure):
                 ("d_I", C.c_int), ("m", C.c_int), ("overlap", C.c_int), ("k", C.c_int),
                 ("n_win", C.c_int), ("vis", C.c_int), ("kv_dtype", C.c_int),
                 ("idx_dtype", C.c_int), ("scale", C.c_float), ("split_rows", C.c_int),
-                ("score_bf16", C.c_int)]
+                ("score_bf16", C.c_int), ("norm_rope", C.c_int), ("rope_dims", C.c_int),
+                ("norm_eps", C.c_float)]
 
 
 class LayerState(C.Structure):
@@ -47,7 +48,8 @@ class LayerState(C.Structure):
                 ("idx_cache", C.c_void_p), ("idx_scale", C.c_void_p), ("n_entries", C.c_void_p),
                 ("win_ring", C.c_void_p), ("tail", C.c_void_p), ("idx_tail", C.c_void_p),
                 ("bias_a", C.c_void_p), ("bias_b", C.c_void_p), ("ibias_a", C.c_void_p),
-                ("ibias_b", C.c_void_p), ("sink", C.c_void_p)]
+                ("ibias_b", C.c_void_p), ("sink", C.c_void_p), ("q_norm_w", C.c_void_p),
+                ("kv_norm_w", C.c_void_p), ("rope_inv_freq", C.c_void_p)]
 
 
 class DecodeIO(C.Structure):

@@ -267,6 +267,12 @@ static csa_status check_desc(const csa_layer_desc* d) {
   REQUIRE(d->overlap == 0 || d->overlap == 1, CSA_ERR_ARG, "overlap must be 0 or 1");
   REQUIRE(d->split_rows >= 0 && d->split_rows % 16 == 0, CSA_ERR_ARG,
           "split_rows must be 0 or a positive multiple of 16 (got %d)", d->split_rows);
+  REQUIRE(d->norm_rope == 0 || d->norm_rope == 1, CSA_ERR_ARG, "norm_rope must be 0 or 1");
+  if (d->norm_rope) {
+    REQUIRE(d->rope_dims >= 2 && d->rope_dims % 2 == 0 && d->rope_dims <= d->c, CSA_ERR_ARG,
+            "rope_dims must be even, 2..c (got %d)", d->rope_dims);
+    REQUIRE(d->norm_eps >= 0.f && d->norm_eps < 1e30f, CSA_ERR_ARG, "norm_eps must be finite and >= 0");
+  }
   if (d->kind == CSA_LAYER_CSA) {
     st = check_idx_dims(d->H_I, d->d_I);
     if (st != CSA_OK) return st;
@@ -297,12 +303,34 @@ static csa_status check_state(const csa_layer_desc* d, const csa_layer_state* s)
     REQUIRE(!scaled(d->idx_dtype) || s->idx_scale != nullptr, CSA_ERR_ARG,
             "E4M3 and MXFP4 indexer caches need idx_scale");
   }
+  if (d->norm_rope) {
+    REQ_PTR(s->q_norm_w); REQ_PTR(s->kv_norm_w); REQ_PTR(s->rope_inv_freq);
+  }
   return CSA_OK;
+}
+
+// norm_rope: the prepared queries [B][T][H][c] and (prefill) window rows
+// [B][n_win-1+T][c], at the start of the workspace after the fold counters
+static size_t prep_q_bytes(const csa_layer_desc* d, int B, int T) {
+  return d->norm_rope ? align_up((size_t)B * T * d->H * d->c * (d->kv_dtype == CSA_F32 ? 4 : 2)) : 0;
+}
+static size_t prep_win_bytes(const csa_layer_desc* d, int B, int T) {
+  return d->norm_rope ? align_up((size_t)B * (d->n_win - 1 + T) * d->c * (d->kv_dtype == CSA_F32 ? 4 : 2)) : 0;
+}
+static csa::NormRope norm_rope_of(const csa_layer_desc* d, const csa_layer_state* s) {
+  csa::NormRope nr{};
+  nr.on = d->norm_rope;
+  nr.rope_dims = d->rope_dims;
+  nr.eps = d->norm_eps;
+  nr.g_q = s->q_norm_w;
+  nr.g_kv = s->kv_norm_w;
+  nr.inv_freq = s->rope_inv_freq;
+  return nr;
 }
 
 size_t hybrid_layer_workspace(const csa_layer_desc* d, int B, int T, int E_cap) {
   if (!d || B < 1 || T < 1 || E_cap < 1) return 0;
-  size_t bytes = align_up((size_t)B * sizeof(int32_t));
+  size_t bytes = align_up((size_t)B * sizeof(int32_t)) + prep_q_bytes(d, B, T) + prep_win_bytes(d, B, T);
   size_t rows = (size_t)E_cap + d->n_win;
   if (d->kind == CSA_LAYER_CSA) {
     bytes += align_up(csa::index_topk_ws_bytes(B, T, E_cap, d->k));
@@ -350,6 +378,8 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
   char* w = (char*)ws;
   int32_t* fold_counters = (int32_t*)w;
   w += align_up((size_t)B * sizeof(int32_t));
+  void* q_prep = w;  // norm_rope
+  w += prep_q_bytes(d, B, 1) + prep_win_bytes(d, B, 1);
 
   csa::FoldArgs f{};
   f.counters = fold_counters;
@@ -360,6 +390,8 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
   f.x_new = io->x_new; f.tail = s->tail; f.idx_tail = s->idx_tail; f.win_ring = s->win_ring;
   f.kv_cache = s->kv_cache; f.idx_cache = s->idx_cache; f.idx_scale = s->idx_scale; f.E_cap = s->E_cap;
   f.bias_a = s->bias_a; f.bias_b = s->bias_b; f.ibias_a = s->ibias_a; f.ibias_b = s->ibias_b;
+  f.nr = norm_rope_of(d, s);
+  f.H = d->H; f.q = io->q; f.q_prep = q_prep;
   csa::IndexArgs x{};
   if (is_csa) {
     x.idx_dtype = d->idx_dtype; x.q = io->q_idx; x.q_scale = scaled(d->idx_dtype) ? io->q_scale : nullptr;
@@ -375,14 +407,20 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
   a.sink = s->sink; a.q_pos = io->pos; a.scale = d->scale;
   a.B = B; a.Tq = 1; a.H = d->H; a.c = d->c; a.out = io->out; a.lse = io->lse;
   a.split_rows = d->split_rows;
+  if (d->norm_rope) {  // the fold kernel prepares the queries; the output is rotated back
+    a.q = q_prep;
+    a.derot_freq = s->rope_inv_freq;
+    a.rope_dims = d->rope_dims;
+  }
   if (!is_csa) {
     a.n_entries = s->n_entries; a.n_add = 0; a.m = d->m; a.vis = d->vis; a.dense = 1;
     a.ws = w; a.ws_bytes = ws_bytes - (size_t)(w - (char*)ws);
   }
   // the fold runs first, unless the scoring kernel (CSA) or the attention
-  // (HCA) does it
-  const bool fold_in_scan = is_csa && csa::index_topk_fuses_fold(x, f);
-  const bool fold_in_attend = !is_csa && csa::attend_fuses_fold(a, f);
+  // (HCA) does it (not with norm_rope: the fold kernel also prepares the
+  // queries and normalises whole entries)
+  const bool fold_in_scan = is_csa && !d->norm_rope && csa::index_topk_fuses_fold(x, f);
+  const bool fold_in_attend = !is_csa && !d->norm_rope && csa::attend_fuses_fold(a, f);
   hipError_t e = hipSuccess;
   if (!fold_in_scan && !fold_in_attend) {
     e = csa::launch_fold_append(f, hs);
@@ -422,6 +460,10 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
   REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
   hipStream_t hs = (hipStream_t)stream;
   char* w = (char*)ws + align_up((size_t)B * sizeof(int32_t));
+  void* q_prep = w;  // norm_rope: prepared queries, then window rows
+  void* win_prep = w + prep_q_bytes(d, B, T);
+  w += prep_q_bytes(d, B, T) + prep_win_bytes(d, B, T);
+  const csa::NormRope nr = norm_rope_of(d, s);
   const int S = n_streams(d), R = tail_depth(d);
   const int64_t first = io->pos0 / m;
   const int n_new = T / m;
@@ -429,8 +471,9 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
 
   // compress the chunk's blocks: main entries, then (CSA) indexer keys
   auto compress = [&](const void* streams, int width, const void* tail, void* out, int out_dtype,
-                      void* out_scale, const float* ba, const float* bb, bool overlap) -> hipError_t {
+                      void* out_scale, const float* ba, const float* bb, bool overlap, bool prep) -> hipError_t {
     csa::CompressArgs c{};
+    if (prep) c.nr = nr;
     const int ns = overlap ? 4 : 2;
     const char* base = (const char*)streams;
     const size_t plane = (size_t)T * width * esz;
@@ -452,12 +495,12 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
     return csa::launch_compress(c, hs);
   };
   hipError_t e = compress(io->streams, d->c, s->tail, s->kv_cache, d->kv_dtype, nullptr, s->bias_a,
-                          s->bias_b, d->overlap != 0);
+                          s->bias_b, d->overlap != 0, d->norm_rope != 0);
   if (e != hipSuccess) return from_hip(e, "hybrid_layer_prefill/compress");
   csa::AttendArgs a{};
   if (is_csa) {
     e = compress(io->idx_streams, d->d_I, s->idx_tail, s->idx_cache, d->idx_dtype, s->idx_scale,
-                 s->ibias_a, s->ibias_b, true);
+                 s->ibias_a, s->ibias_b, true, false);
     if (e != hipSuccess) return from_hip(e, "hybrid_layer_prefill/compress_idx");
   }
   if (is_csa) {
@@ -481,12 +524,25 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
   a.sink = s->sink; a.q_pos = nullptr; a.q_pos0 = io->pos0; a.scale = d->scale;
   a.B = B; a.Tq = T; a.H = d->H; a.c = d->c; a.out = io->out; a.lse = io->lse;
   a.ws = w; a.ws_bytes = ws_bytes - (size_t)(w - (char*)ws);
+  if (d->norm_rope) {
+    // the chunk's queries and window rows prepared for the attention
+    csa::PrepArgs pa{};
+    pa.dtype = d->kv_dtype; pa.B = B; pa.T = T; pa.H = d->H; pa.c = d->c; pa.n_win = d->n_win;
+    pa.pos0 = io->pos0; pa.nr = nr; pa.q = io->q; pa.win = io->win; pa.q_prep = q_prep; pa.win_prep = win_prep;
+    e = csa::launch_prep_rows(pa, hs);
+    if (e != hipSuccess) return from_hip(e, "hybrid_layer_prefill/prep");
+    a.q = q_prep;
+    a.win = win_prep;
+    a.derot_freq = s->rope_inv_freq;
+    a.rope_dims = d->rope_dims;
+  }
   e = csa::launch_attend(a, hs);
   if (e != hipSuccess) return from_hip(e, "hybrid_layer_prefill/attend");
 
   csa::PrefillStateArgs p{};
   p.dtype = d->kv_dtype; p.B = B; p.T = T; p.c = d->c; p.d_I = d->d_I; p.R = R; p.n_win = d->n_win; p.S = S;
-  p.pos0 = io->pos0; p.win = io->win; p.streams = io->streams; p.idx_streams = is_csa ? io->idx_streams : nullptr;
+  p.pos0 = io->pos0; p.win = d->norm_rope ? win_prep : io->win;  // the ring holds prepared rows
+  p.streams = io->streams; p.idx_streams = is_csa ? io->idx_streams : nullptr;
   p.win_ring = s->win_ring; p.tail = s->tail; p.idx_tail = s->idx_tail; p.n_entries = s->n_entries;
   p.new_entries = n_new;
   return from_hip(csa::launch_prefill_state(p, hs), "hybrid_layer_prefill/state");

@@ -149,12 +149,25 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
     if (a.lse && h < H) a.lse[(size_t)row * H + h] = M + __logf(den);
   }
   __syncthreads();
-  if (h0 + ph < H) {
+  {
     const float f = p_s[ph];
     T* o = reinterpret_cast<T*>(a.out) + ((size_t)row * H + h0 + ph) * c;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j < nd) st(o, pd + 32 * j, acc[j] * f);
+    for (int j = 0; j < 16; ++j) {
+      if (j < nd) {
+        float v = acc[j] * f;
+        // norm_rope: rotary coordinates rotated back by the query position;
+        // the pair partner of coordinate d is d ^ 1, held by lane tid ^ 1
+        const float other = __shfl_xor(v, 1, 64);
+        const int d = pd + 32 * j, R = a.rope_dims;
+        if (a.derot_freq && d >= c - R) {
+          float cs, sn;
+          rope_cs(-t, a.derot_freq[(d - (c - R)) >> 1], &cs, &sn);
+          v = (d & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
+        }
+        if (h0 + ph < H) st(o, d, v);
+      }
+    }
   }
 }
 

@@ -615,11 +615,15 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
 #pragma unroll
     for (int dtl = 0; dtl < 8; ++dtl) {
       const f32x4_t v4 = acc[4 * dtl + hb];
+      float x[4] = {v4[0] * f, v4[1] * f, v4[2] * f, v4[3] * f};
+      // norm_rope: the rotary coordinates rotated back by the query position
+      // (linear, so partials may be rotated before the merge)
+      if (a.derot_freq) rope_pairs<4>(x, 4, 128 * w + 16 * dtl + 4 * lg, kC, a.rope_dims, a.derot_freq, -t);
       ushort4 v;
-      v.x = f32_to_bf16(v4[0] * f);
-      v.y = f32_to_bf16(v4[1] * f);
-      v.z = f32_to_bf16(v4[2] * f);
-      v.w = f32_to_bf16(v4[3] * f);
+      v.x = f32_to_bf16(x[0]);
+      v.y = f32_to_bf16(x[1]);
+      v.z = f32_to_bf16(x[2]);
+      v.w = f32_to_bf16(x[3]);
       *reinterpret_cast<ushort4*>(stage + (16 * hb + li) * kOutLD + 128 * w + 16 * dtl + 4 * lg) = v;
     }
   }

@@ -357,11 +357,17 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
       f = Lh > 0.f ? __builtin_amdgcn_rcpf(Lh) : 0.f;
       dst = po + slot * kC;
     }
+    float x0[4] = {o0[0] * f, o0[1] * f, o0[2] * f, o0[3] * f};
+    float x1[4] = {o1[0] * f, o1[1] * f, o1[2] * f, o1[3] * f};
+    if (a.derot_freq) {  // norm_rope: rotary coordinates rotated back by the query position
+      rope_pairs<4>(x0, 4, 4 * l, kC, a.rope_dims, a.derot_freq, -t);
+      rope_pairs<4>(x1, 4, 256 + 4 * l, kC, a.rope_dims, a.derot_freq, -t);
+    }
     uint2 r0, r1;
-    r0.x = (uint32_t)f32_to_bf16(o0[0] * f) | ((uint32_t)f32_to_bf16(o0[1] * f) << 16);
-    r0.y = (uint32_t)f32_to_bf16(o0[2] * f) | ((uint32_t)f32_to_bf16(o0[3] * f) << 16);
-    r1.x = (uint32_t)f32_to_bf16(o1[0] * f) | ((uint32_t)f32_to_bf16(o1[1] * f) << 16);
-    r1.y = (uint32_t)f32_to_bf16(o1[2] * f) | ((uint32_t)f32_to_bf16(o1[3] * f) << 16);
+    r0.x = (uint32_t)f32_to_bf16(x0[0]) | ((uint32_t)f32_to_bf16(x0[1]) << 16);
+    r0.y = (uint32_t)f32_to_bf16(x0[2]) | ((uint32_t)f32_to_bf16(x0[3]) << 16);
+    r1.x = (uint32_t)f32_to_bf16(x1[0]) | ((uint32_t)f32_to_bf16(x1[1]) << 16);
+    r1.y = (uint32_t)f32_to_bf16(x1[2]) | ((uint32_t)f32_to_bf16(x1[3]) << 16);
     *reinterpret_cast<uint2*>(dst + 4 * l) = r0;
     *reinterpret_cast<uint2*>(dst + 256 + 4 * l) = r1;
   }

@@ -131,6 +131,35 @@ CSA_DEV float wave_max(float v) {
   return v;
 }
 
+// ---------------------------------------------------------------- rotary positions
+// cos and sin of the angle pos * f: the product and its reduction to
+// [-pi, pi] in double (a float angle at position 10^6 would be off by a
+// large fraction of a radian), the functions in float
+CSA_DEV void rope_cs(int64_t pos, double f, float* cs, float* sn) {
+  const double ang = (double)pos * f;
+  const double r = ang - 6.283185307179586 * rint(ang * 0.15915494309189535);
+  sincosf((float)r, sn, cs);
+}
+
+// Rotate the pairs (v[j], v[j+1]), j even and j < n <= N, holding
+// coordinates d0 + j of a vector of length c whose last R coordinates are
+// rotary (d0 and c - R even), by the angles pos * inv_freq[i] (pair
+// i = (d - (c - R)) / 2); the other coordinates stay.
+template <int N>
+CSA_DEV void rope_pairs(float* v, int n, int d0, int c, int R, const double* inv_freq, int64_t pos) {
+#pragma unroll
+  for (int j = 0; j < N; j += 2) {
+    const int d = d0 + j;
+    if (j < n && d >= c - R) {
+      float cs, sn;
+      rope_cs(pos, inv_freq[(d - (c - R)) >> 1], &cs, &sn);
+      const float x = v[j], y = v[j + 1];
+      v[j] = x * cs - y * sn;
+      v[j + 1] = x * sn + y * cs;
+    }
+  }
+}
+
 // v + the values of lanes l^16, l^32 and l^48 (the four 16-lane rows), with
 // the gfx950 lane-swap instructions instead of LDS permutes
 CSA_DEV float lane_sum_xor16_32(float v) {

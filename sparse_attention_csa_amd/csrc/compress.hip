@@ -124,6 +124,33 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
     int u = 0;
     for (int r = tid; r < c; r += 256, ++u) o[r] = f32_to_e4m3(vals[u] / scale);
     if (tid == 0) reinterpret_cast<float*>(a.out_scale)[(size_t)b * a.E_cap + a.first + i] = scale;
+  } else if (a.nr.on) {
+    // the entry prepared for the core attention: RMSNorm over its c
+    // coordinates, then the rotary pairs (neighbouring lanes) at its position,
+    // the first token of its block
+    TO* o = reinterpret_cast<TO*>(a.out) + orow;
+    const int nu = (c + 255) / 256;  // the same trip count in every lane
+    float ss = 0.f;
+    for (int u = 0; u < nu; ++u)
+      if (tid + 256 * u < c) ss += vals[u] * vals[u];
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) s_red[tid >> 6] = ss;
+    __syncthreads();
+    ss = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+    const float inv = 1.0f / sqrtf(ss / (float)c + a.nr.eps);
+    const int64_t pos = (int64_t)m * (a.first + i);
+    const int R = a.nr.rope_dims;
+    for (int u = 0; u < nu; ++u) {
+      const int r = tid + 256 * u;
+      float v = r < c ? vals[u] * inv * a.nr.g_kv[r] : 0.f;
+      const float other = __shfl_xor(v, 1, 64);
+      if (r < c && r >= c - R) {
+        float cs, sn;
+        rope_cs(pos, a.nr.inv_freq[(r - (c - R)) >> 1], &cs, &sn);
+        v = (r & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
+      }
+      if (r < c) st(o, r, v);
+    }
   } else {
     TO* o = reinterpret_cast<TO*>(a.out) + orow;
     int u = 0;
@@ -185,8 +212,58 @@ __global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
   const int64_t e = n_have;
   const int nstr = a.overlap ? 4 : 2;
   const int slot = (int)(t % R);
+  const bool has_idx = a.idx_dtype >= 0;
+  const int main_jobs = a.nr.on ? 1 : c / kFoldCW;
 
-  if (job < c / kFoldCW) {
+  if (a.nr.on && job == 0) {
+    // the whole main entry, prepared (RMSNorm, then rotary pairs at its
+    // position m e), the main streams' appends and the new window row,
+    // prepared at t
+    T* tail = reinterpret_cast<T*>(a.tail) + (size_t)b * nstr * R * c;
+    const T* io = reinterpret_cast<const T*>(a.streams) + (size_t)b * nstr * c;
+    if (fold) {
+      const int nu = (c + 255) / 256;
+      float val[2] = {0.f, 0.f};
+      for (int u = 0; u < nu; ++u) {
+        const int r0 = 256 * u, W = c - r0 < 256 ? c - r0 : 256;
+        val[u] = fold_job<T>(tail, io, c, r0, W, m, R, t, e, a.overlap && e > 0, a.bias_a, a.bias_b, s_part);
+      }
+      float ss = 0.f;
+      for (int u = 0; u < nu; ++u)
+        if (256 * u + tid < c) ss += val[u] * val[u];
+      ss = wave_sum(ss);
+      if ((tid & 63) == 0) s_red[tid >> 6] = ss;
+      __syncthreads();
+      ss = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+      const float inv = 1.0f / sqrtf(ss / (float)c + a.nr.eps);
+      const int Rd = a.nr.rope_dims;
+      for (int u = 0; u < nu; ++u) {
+        const int r = 256 * u + tid;
+        float v = r < c ? val[u] * inv * a.nr.g_kv[r] : 0.f;
+        const float other = __shfl_xor(v, 1, 64);
+        if (r < c && r >= c - Rd) {
+          float cs, sn;
+          rope_cs((int64_t)m * e, a.nr.inv_freq[(r - (c - Rd)) >> 1], &cs, &sn);
+          v = (r & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
+        }
+        if (r < c) st(reinterpret_cast<T*>(a.kv_cache), ((size_t)b * a.E_cap + e) * c + r, v);
+      }
+    }
+    for (int i = tid; i < nstr * c; i += kFoldT) {
+      const int sc = i / c, r = i % c;
+      tail[((size_t)sc * R + slot) * c + r] = io[(size_t)sc * c + r];
+    }
+    if (tid < 64)
+      prep_row_wave(reinterpret_cast<const T*>(a.x_new) + (size_t)b * c,
+                    reinterpret_cast<T*>(a.win_ring) + ((size_t)b * a.n_win + (size_t)(t % a.n_win)) * c, c, a.nr,
+                    a.nr.g_kv, t);
+  } else if (job >= main_jobs + (has_idx ? 1 : 0)) {
+    // the step's queries, prepared at t: one head per wavefront
+    const int h = 4 * (job - main_jobs - (has_idx ? 1 : 0)) + (tid >> 6);
+    if (h < a.H)
+      prep_row_wave(reinterpret_cast<const T*>(a.q) + ((size_t)b * a.H + h) * c,
+                    reinterpret_cast<T*>(a.q_prep) + ((size_t)b * a.H + h) * c, c, a.nr, a.nr.g_q, t);
+  } else if (job < main_jobs) {
     const int r0 = job * kFoldCW;
     T* tail = reinterpret_cast<T*>(a.tail) + (size_t)b * nstr * R * c;
     const T* io = reinterpret_cast<const T*>(a.streams) + (size_t)b * nstr * c;
@@ -261,11 +338,48 @@ static void launch_fold_to(const FoldArgs& a, dim3 grid, dim3 block, hipStream_t
 }
 
 hipError_t launch_fold_append(const FoldArgs& a, hipStream_t s) {
-  dim3 grid(a.c / kFoldCW + (a.idx_dtype >= 0 ? 1 : 0), a.B), block(kFoldT);
+  // main-entry jobs (one with norm_rope: the entry's norm needs all of it),
+  // the indexer-key job, the query jobs (norm_rope, four heads each)
+  const int jobs = (a.nr.on ? 1 : a.c / kFoldCW) + (a.idx_dtype >= 0 ? 1 : 0) + (a.nr.on ? (a.H + 3) / 4 : 0);
+  dim3 grid(jobs, a.B), block(kFoldT);
   if (a.dtype == F32)
     launch_fold_to<float>(a, grid, block, s);
   else
     launch_fold_to<bf16>(a, grid, block, s);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
+// norm_rope prefill: the chunk's queries and window rows prepared for the
+// core attention (RMSNorm, then the rotary pairs at their positions), one
+// wavefront per row.  grid (rows / 4), 256 threads.
+// --------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void prep_rows_kernel(PrepArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t nq = (int64_t)a.B * a.T * a.H;
+  const int W = a.n_win - 1 + a.T;
+  const int64_t nw = (int64_t)a.B * W;
+  const int c = a.c;
+  if (row < nq) {
+    const int tq = (int)((row / a.H) % a.T);
+    prep_row_wave(cptr<T>(a.q) + row * c, reinterpret_cast<T*>(a.q_prep) + row * c, c, a.nr, a.nr.g_q,
+                  a.pos0 + tq);
+  } else if (row < nq + nw) {
+    const int64_t r = row - nq;
+    const int j = (int)(r % W);
+    prep_row_wave(cptr<T>(a.win) + r * c, reinterpret_cast<T*>(a.win_prep) + r * c, c, a.nr, a.nr.g_kv,
+                  a.pos0 - (a.n_win - 1) + j);
+  }
+}
+
+hipError_t launch_prep_rows(const PrepArgs& a, hipStream_t s) {
+  const int64_t rows = (int64_t)a.B * a.T * a.H + (int64_t)a.B * (a.n_win - 1 + a.T);
+  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (a.dtype == F32)
+    CSA_LAUNCH("prep_rows", prep_rows_kernel<float>, grid, block, 0, s, a);
+  else
+    CSA_LAUNCH("prep_rows", prep_rows_kernel<bf16>, grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -6,6 +6,7 @@
 #pragma once
 
 #include "common.h"
+#include "kernels.h"
 
 namespace csa {
 
@@ -176,6 +177,41 @@ CSA_DEV float fold_job(const T* tail, const T* io, int d, int r0, int W, int m, 
   }
   __syncthreads();
   return val;
+}
+
+// One wavefront prepares one vector of length c (64..512, a multiple of 64)
+// for the core attention: RMSNorm with scale g, v * g / sqrt(mean(v^2) +
+// eps), then the rotary pairs of its last rope_dims coordinates at position
+// pos.  Lane l holds coordinates E l .. E l + E - 1, E = c / 64; with E = 1 a
+// pair spans lanes l, l ^ 1.  Called by whole wavefronts.
+template <typename T>
+CSA_DEV void prep_row_wave(const T* src, T* dst, int c, const NormRope& nr, const float* g, int64_t pos) {
+  const int l = threadIdx.x & 63, E = c / 64, R = nr.rope_dims;
+  float v[8];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    v[j] = j < E ? ld(src, (size_t)l * E + j) : 0.f;
+    ss += v[j] * v[j];
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)c + nr.eps);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < E) v[j] *= inv * g[l * E + j];
+  if (E >= 2) {
+    rope_pairs<8>(v, E, l * E, c, R, nr.inv_freq, pos);
+  } else {
+    const float o = __shfl_xor(v[0], 1, 64);
+    if (l >= c - R) {
+      float cs, sn;
+      rope_cs(pos, nr.inv_freq[(l - (c - R)) >> 1], &cs, &sn);
+      v[0] = (l & 1) ? (o * sn + v[0] * cs) : (v[0] * cs - o * sn);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < E) st(dst, (size_t)l * E + j, v[j]);
 }
 
 }  // namespace csa

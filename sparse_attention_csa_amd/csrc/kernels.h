@@ -47,6 +47,18 @@ inline int current_device() {
   return d;
 }
 
+// RMSNorm and partial RoPE of produced KV vectors and queries (norm_rope):
+// v * g / sqrt(mean(v^2) + eps), then pairs (2i, 2i+1) of the last
+// rope_dims coordinates rotated by pos * inv_freq[i]
+struct NormRope {
+  int on;
+  int rope_dims;
+  float eps;
+  const float* g_q;         // [c] query heads
+  const float* g_kv;        // [c] KV head
+  const double* inv_freq;   // [rope_dims / 2]
+};
+
 // ------------------------------------------------------------ compressor
 struct CompressArgs {
   int dtype;  // input dtype (F32 / BF16)
@@ -61,6 +73,7 @@ struct CompressArgs {
   int64_t first;
   size_t seq_stride;       // elements between sequences of ca/za/cb/zb (0: T*c or T*lw)
   size_t prev_seq_stride;  // elements between sequences of prev_cb/prev_zb (0: m*c or m*lw)
+  NormRope nr;             // on: entry first + i is prepared at position m * (first + i)
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 
@@ -83,8 +96,28 @@ struct FoldArgs {
   void* idx_scale;          // E4M3: float [B][E_cap]; MXFP4: uint8 [B][E_cap][d_I/32]
   int E_cap;
   const float *bias_a, *bias_b, *ibias_a, *ibias_b;
+  // norm_rope: the folded entry and the new window row are prepared, and
+  // the step's queries q [B][H][c] are prepared into q_prep
+  NormRope nr;
+  int H;
+  const void* q;
+  void* q_prep;
 };
 hipError_t launch_fold_append(const FoldArgs& a, hipStream_t s);
+
+// norm_rope prefill: queries [B][T][H][c] at positions pos0 + t and window
+// rows [B][n_win-1+T][c] at pos0 - (n_win-1) + j, prepared into q_prep and
+// win_prep (same layouts)
+struct PrepArgs {
+  int dtype, B, T, H, c, n_win;
+  int64_t pos0;
+  NormRope nr;
+  const void* q;
+  const void* win;
+  void* q_prep;
+  void* win_prep;
+};
+hipError_t launch_prep_rows(const PrepArgs& a, hipStream_t s);
 
 // prefill epilogue: copy the chunk's last tokens into the window ring / tail
 struct PrefillStateArgs {
@@ -173,6 +206,10 @@ struct AttendArgs {
   uint16_t* fold_new;  // [B][c]: the new entry (bf16), read by the merge
   int fold_nsplit;     // set by the launch: splits that fold (fewer rows each) ...
   int fold_rows;       // ... and their row count
+  // norm_rope: the output's last rope_dims coordinates are rotated back by
+  // the query position (pairs (2i, 2i+1), angle -t * derot_freq[i]); null: off
+  const double* derot_freq;
+  int rope_dims;
 };
 // split_rows > 0: rows per split fixed (batch-invariant launch plan), else
 // chosen for the batch

@@ -26,6 +26,8 @@ def dev(arr, kind, device="cuda"):
         return torch.from_numpy(a.view(np.uint8)).to(device)
     if kind == "f32":
         return torch.from_numpy(a.astype(np.float32)).to(device)
+    if kind == "f64":
+        return torch.from_numpy(a.astype(np.float64)).to(device)
     if kind in ("i32", "i64"):
         return torch.from_numpy(a.astype(np.int32 if kind == "i32" else np.int64)).to(device)
     raise ValueError(kind)
@@ -62,6 +64,10 @@ def make_desc(g):
     d.scale = g["scale"]
     d.split_rows = int(g.get("split_rows") or 0)
     d.score_bf16 = 1 if g.get("score_dtype") == "bf16" else 0
+    if g.get("norm_rope"):
+        d.norm_rope = 1
+        d.rope_dims = int(g["rope_dims"])
+        d.norm_eps = float(g["norm_eps"])
     return d
 
 
@@ -81,6 +87,11 @@ class _State:
         self.bias_a = dev(g["bias_a"], "f32", device) if g.get("bias_a") is not None else None
         self.bias_b = dev(g["bias_b"], "f32", device) if g.get("bias_b") is not None else None
         self.sink = dev(g["sink"], "f32", device) if g.get("sink") is not None else None
+        self.q_norm_w = self.kv_norm_w = self.rope_inv_freq = None
+        if g.get("norm_rope"):
+            self.q_norm_w = dev(g["q_norm_w"], "f32", device)
+            self.kv_norm_w = dev(g["kv_norm_w"], "f32", device)
+            self.rope_inv_freq = dev(g["rope_inv_freq"], "f64", device)
         self.idx_cache = self.idx_scale = self.idx_tail = self.ibias_a = self.ibias_b = None
         if g["kind"] == "csa":
             d_I = g["d_I"]
@@ -102,7 +113,8 @@ class _State:
         s = L.LayerState()
         s.B, s.E_cap = self.B, self.E_cap
         for name in ("kv_cache", "idx_cache", "idx_scale", "n_entries", "win_ring", "tail",
-                     "idx_tail", "bias_a", "bias_b", "ibias_a", "ibias_b", "sink"):
+                     "idx_tail", "bias_a", "bias_b", "ibias_a", "ibias_b", "sink", "q_norm_w",
+                     "kv_norm_w", "rope_inv_freq"):
             setattr(s, name, L.ptr(getattr(self, name)))
         return s
 

@@ -1,4 +1,6 @@
-"""Test-side helpers that re-slice generated inputs (no method arithmetic).
+"""Test-side helpers that re-slice generated inputs (no method arithmetic of
+their own: where a layer stores prepared window rows, they are prepared by
+the oracle).
 
 ``decode_from_prefill`` turns a prefill workload into the decode-step inputs
 of one later token, so that prefill(n) + decode steps can be checked against
@@ -72,6 +74,9 @@ def decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv=(), extra_idx=
     g = {k: pre[k] for k in ("kind", "H", "c", "m", "n_win", "overlap", "vis", "scale",
                              "kv_dtype", "k", "idx_dtype", "sink", "bias_a", "bias_b")}
     g["score_dtype"] = pre.get("score_dtype", "f32")
+    for k_ in ("norm_rope", "q_norm_w", "kv_norm_w", "rope_inv_freq", "rope_dims", "norm_eps"):
+        if k_ in pre:
+            g[k_] = pre[k_]
     g.update(B=1, E_cap=E_cap)
     g["pos"] = np.array([t], dtype=np.int64)
     g["n_entries"] = np.array([n_have], dtype=np.int32)
@@ -91,6 +96,15 @@ def decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv=(), extra_idx=
         g["new_" + s] = pre[s][sl, hi]
     w0 = t - (n_win - 1) - (pos0 - (n_win - 1))
     g["win_hist"] = pre["win"][sl, w0:w0 + n_win - 1]
+    if pre.get("norm_rope"):
+        # the ring holds the history rows prepared at their positions, as stored
+        from oracle import position as P
+        from oracle.csa import store_as
+        from oracle.formats import Stored
+        raw = Stored(g["win_hist"][0], kvk).all()
+        hp = np.arange(t - (n_win - 1), t)
+        prep = store_as(P.prepare(raw, pre["kv_norm_w"], pre["norm_eps"], hp, pre["rope_inv_freq"]), kvk)
+        g["win_hist"] = _bits(prep, kvk)[None]
     g["x_new"] = pre["win"][sl, w0 + n_win - 1]
     g["q"] = pre["q"][sl, hi]
     if pre["kind"] == "csa":

@@ -73,7 +73,16 @@ def _check_rings(g, sess, label):
     streams = ("ca", "za", "cb", "zb")[:st.S]
     for b in range(g["B"]):
         t = int(g["pos"][b])
-        assert np.array_equal(as_u16(st.win_ring[b, t % g["n_win"]]), g["x_new"][b]), f"{label} window ring b={b}"
+        if g.get("norm_rope"):
+            # the ring receives the row prepared at t (normalised, rotated)
+            from oracle import position as P
+            from oracle.csa import store_as
+            raw = Stored(g["x_new"][b][None], g["kv_dtype"]).all()[0]
+            want = store_as(P.prepare(raw, g["kv_norm_w"], g["norm_eps"], t, g["rope_inv_freq"]), g["kv_dtype"])
+            assert_close(f64(st.win_ring[b, t % g["n_win"]])[None], want[None], g["kv_dtype"],
+                         f"{label} prepared window row b={b}")
+        else:
+            assert np.array_equal(as_u16(st.win_ring[b, t % g["n_win"]]), g["x_new"][b]), f"{label} window ring b={b}"
         for si, name in enumerate(streams):
             assert np.array_equal(as_u16(st.tail[b, si, t % st.R]), g["new_" + name][b]), f"{label} tail {name} b={b}"
         if g["kind"] == "csa":

@@ -12,5 +12,6 @@ from .gen import (  # noqa: F401
     flash_hca_decode,
     pro_csa_decode,
     flash_prefill,
+    with_norm_rope,
     CONFIG_NAMES,
 )

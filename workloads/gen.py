@@ -348,3 +348,26 @@ def flash_prefill(seed=4, B=1, T=4096, n0=262144, H=64, c=512, H_I=64, d_I=128, 
     csa["name"] = CONFIG_NAMES[5] + ":csa"
     hca["name"] = CONFIG_NAMES[5] + ":hca"
     return csa, hca
+
+
+# ---------------------------------------------------------------------------
+# 6. query / KV normalisation and partial rotary positions (any layer case)
+# ---------------------------------------------------------------------------
+
+def with_norm_rope(g, seed=7, rope_dims=64, base=10000.0, eps=1e-6):
+    """A copy of layer case g with query / KV RMSNorm and partial RoPE on:
+    learned scales 1 + 0.1 N(0, 1) (one vector for the query heads, one for
+    the KV head), inverse frequencies base^(-2i / rope_dims) as float64,
+    epsilon ``eps``.  Drawn from their own generator, so g's other inputs
+    are unchanged; g's cached entries and window history stand for vectors
+    already prepared."""
+    rng = _rng(seed)
+    c = g["c"]
+    out = dict(g)
+    out["norm_rope"] = True
+    out["q_norm_w"] = (1.0 + 0.1 * rng.standard_normal(c)).astype(np.float32)
+    out["kv_norm_w"] = (1.0 + 0.1 * rng.standard_normal(c)).astype(np.float32)
+    out["rope_inv_freq"] = base ** (-np.arange(rope_dims // 2, dtype=np.float64) * 2.0 / rope_dims)
+    out["rope_dims"] = rope_dims
+    out["norm_eps"] = eps
+    return out
