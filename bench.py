@@ -68,8 +68,8 @@ def attend_splits(BT, H, rows_max, heads_per_wg=64):
 
 # benchmark timing-hook names -> the kernel symbols rocprofv3 reports
 ROCPROF_NAMES = {
-    "attend_dense_mfma": "attend_mfma_kernel",
-    "attend_sparse_rows": "attend_rows_kernel",
+    "attend_dense_mfma": "attend_mfma_kernel<0>",
+    "attend_sparse_rows": "attend_rows_kernel<0>",
     "topk_resolve": "topk_fused_resolve_kernel",
 }
 

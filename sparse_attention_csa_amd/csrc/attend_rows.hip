@@ -50,6 +50,9 @@ constexpr int kFill = kMaxRows / 256;        // row-source loads per thread
 
 // 1-D grid: block L runs on XCD L % 8; the n_hg head groups of one (query,
 // split) are blocks L, L + 8, ... so they gather the same rows through one L2.
+// DEROT: the output's rotary coordinates are rotated back by the query
+// position (norm_rope); a separate instantiation leaves the default one as it was
+template <int DEROT>
 __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n_split, int rows_per_split) {
   // tile buffers: tile j of the split in buffer j when the split has at
   // most kBufs tiles, else buffers 2w, 2w+1 are wavefront w's ring; reused as
@@ -359,7 +362,7 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
     }
     float x0[4] = {o0[0] * f, o0[1] * f, o0[2] * f, o0[3] * f};
     float x1[4] = {o1[0] * f, o1[1] * f, o1[2] * f, o1[3] * f};
-    if (a.derot_freq) {  // norm_rope: rotary coordinates rotated back by the query position
+    if (DEROT) {  // norm_rope: rotary coordinates rotated back by the query position
       rope_pairs<4>(x0, 4, 4 * l, kC, a.rope_dims, a.derot_freq, -t);
       rope_pairs<4>(x1, 4, 256 + 4 * l, kC, a.rope_dims, a.derot_freq, -t);
     }
@@ -404,7 +407,10 @@ hipError_t launch_attend_rows(const AttendArgs& a, int rows_max, hipStream_t s) 
   const int n_hg = a.H / 16;
   const long long units = (long long)ns * a.B * a.Tq;   // (query, split) pairs
   const long long blocks = (units + 7) / 8 * 8 * n_hg;  // padded to whole XCD rounds
-  CSA_LAUNCH("attend_sparse_rows", attend_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+  if (a.derot_freq)
+    CSA_LAUNCH("attend_sparse_rows", attend_rows_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+  else
+    CSA_LAUNCH("attend_sparse_rows", attend_rows_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
   if (ns > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

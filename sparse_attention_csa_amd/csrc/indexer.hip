@@ -118,11 +118,11 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
 
 // --------------------------------------------------------------------------
 // scoring of many queries of one sequence (prefill) on MFMA, bf16, 64 heads
-// of dim 128: a workgroup scores four consecutive queries (one per
+// of dim 128: a workgroup scores QPW consecutive queries (one per
 // wavefront) against a chunk of kPfChunk entries.  The chunk streams through
 // LDS in 64-entry key tiles (16 KB, double-buffered, the next tile's loads in
-// flight while one is scored) shared by the four queries, so a key crosses
-// HBM / L2 once per four queries.  Per wavefront and 16-entry block:
+// flight while one is scored) shared by the QPW queries, so a key crosses
+// HBM / L2 once per QPW queries.  Per wavefront and 16-entry block:
 //   D[16 heads x 16 entries] = Q[16 heads x 128] . K^T[128 x 16 entries]
 // (v_mfma_f32_16x16x32_bf16, four head tiles, Q in registers); lane (head
 // row group g, entry i) holds heads 4g .. 4g+3 of entry i, so ReLU and the
@@ -132,24 +132,31 @@ namespace {
 constexpr int kPfTile = 64;     // entries per LDS key tile
 constexpr int kPfChunk = 1024;  // entries per workgroup
 constexpr int kPfD = 128, kPfH = 64;
+// queries per workgroup (Tq % kPfQpw == 0).  Measured on the 4096-query
+// chunk: 8 gave the same time as 4 (the kernel is not bound by the key
+// traffic), 16 spilled registers and was slower.
+constexpr int kPfQpw = 4;
 }  // namespace
 
 bool index_prefill_mfma_supported(const IndexArgs& a) {
-  return a.idx_dtype == BF16 && a.H_I == kPfH && a.d_I == kPfD && a.Tq % 4 == 0;
+  return a.idx_dtype == BF16 && a.H_I == kPfH && a.d_I == kPfD && a.Tq % kPfQpw == 0;
 }
 
-__global__ __launch_bounds__(256) void index_score_prefill_kernel(IndexArgs a) {
+template <int QPW>
+__global__ __launch_bounds__(64 * QPW) void index_score_prefill_kernel(IndexArgs a) {
   using namespace tile;
+  constexpr int kT = 64 * QPW;               // threads
+  constexpr int kCpt = kPfTile * 16 / kT;    // 16-byte chunks of a key tile per thread
   // key tile: row = entry (256 B), its 16-byte chunk c stored at c ^ (row % 16)
   __shared__ __attribute__((aligned(16))) uint4 s_k[2][kPfTile * 16];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
-  const int row0 = blockIdx.y * 4, row = row0 + w;  // the four rows share their sequence (Tq % 4 == 0)
+  const int row0 = blockIdx.y * QPW, row = row0 + w;  // the rows share their sequence (Tq % QPW == 0)
   const int b = row0 / a.Tq;
   // visible entries of each of the four queries (every thread computes all
   // four: the chunk is needed up to the largest)
   int64_t nv_q = 0, nv_max = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < QPW; ++j) {
     const int tq = (row0 + j) % a.Tq;
     const int64_t t = a.q_pos ? a.q_pos[(size_t)b * a.Tq + tq] : a.q_pos0 + tq;
     const int64_t nv = n_visible(a, b, t);
@@ -176,29 +183,30 @@ __global__ __launch_bounds__(256) void index_score_prefill_kernel(IndexArgs a) {
       wr[ht][0] = wv.x; wr[ht][1] = wv.y; wr[ht][2] = wv.z; wr[ht][3] = wv.w;
     }
   }
-  // thread's share of a tile: chunks tid + 256 u (entry c / 16, chunk c % 16);
+  // thread's share of a tile: chunks tid + kT u (entry c / 16, chunk c % 16);
   // entries past the last visible one re-read it
   struct Share {
-    uint4 v0, v1, v2, v3;
+    uint4 v[kCpt];
   };
   auto chunk_ptr = [&](int j, int u) -> const uint4* {
-    const int c = tid + 256 * u;
+    const int c = tid + kT * u;
     int64_t e = e0 + (int64_t)j * kPfTile + (c >> 4);
     if (e > e1 - 1) e = e1 - 1;
     return reinterpret_cast<const uint4*>(keys + (size_t)e * kPfD + 8 * (c & 15));
   };
   auto load_tile = [&](int j) -> Share {
-    return Share{*chunk_ptr(j, 0), *chunk_ptr(j, 1), *chunk_ptr(j, 2), *chunk_ptr(j, 3)};
+    Share r;
+#pragma unroll
+    for (int u = 0; u < kCpt; ++u) r.v[u] = *chunk_ptr(j, u);
+    return r;
   };
   auto slot = [&](int buf, int u) -> uint4* {
-    const int c = tid + 256 * u, kk = c >> 4;
+    const int c = tid + kT * u, kk = c >> 4;
     return &s_k[buf][kk * 16 + ((c & 15) ^ (kk & 15))];
   };
   auto store_tile = [&](int buf, const Share& r) {
-    *slot(buf, 0) = r.v0;
-    *slot(buf, 1) = r.v1;
-    *slot(buf, 2) = r.v2;
-    *slot(buf, 3) = r.v3;
+#pragma unroll
+    for (int u = 0; u < kCpt; ++u) *slot(buf, u) = r.v[u];
   };
   float* out = a.scores + (size_t)row * a.E_cap;
   store_tile(0, load_tile(0));
@@ -267,8 +275,9 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t s, const FoldArgs*
   if (mfma) {
     e = launch_index_score_mfma(a, tw, 1, 1, &n_wg_fused, fold, s);
   } else if (index_prefill_mfma_supported(a)) {
-    dim3 g1((a.E_cap + kPfChunk - 1) / kPfChunk, rows / 4), blk(256);
-    CSA_LAUNCH("index_score_prefill", index_score_prefill_kernel, g1, blk, 0, s, a);
+    const unsigned gx = (a.E_cap + kPfChunk - 1) / kPfChunk;
+    CSA_LAUNCH("index_score_prefill", index_score_prefill_kernel<kPfQpw>, dim3(gx, rows / kPfQpw),
+               dim3(64 * kPfQpw), 0, s, a);
     e = hipGetLastError();
   } else {
     dim3 g1((a.E_cap + 255) / 256, rows), blk(256);

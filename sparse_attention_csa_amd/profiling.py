@@ -32,16 +32,17 @@ CSRC = os.path.join(PKG, "csrc")
 
 # kernel name prefix -> the sources that define it (hashed together)
 KERNEL_SOURCES = {
-    "index_score_mfma": ["indexer_mfma.hip", "common.h", "topk.h", "kernels.h"],
+    "index_score_mfma": ["indexer_mfma.hip", "common.h", "topk.h", "kernels.h", "fold.h"],
     "index_score": ["indexer.hip", "common.h", "kernels.h"],
     "topk_": ["topk.hip", "common.h", "topk.h", "kernels.h"],
     "attend_mfma": ["attend_mfma.hip", "mfma_tile.h", "common.h", "kernels.h"],
     "attend_rows": ["attend_rows.hip", "mfma_tile.h", "common.h", "kernels.h"],
     "attend_merge": ["attend_mfma.hip", "mfma_tile.h", "common.h", "kernels.h"],
     "attend_generic": ["attend.hip", "common.h", "kernels.h"],
-    "fold_append": ["compress.hip", "common.h", "kernels.h"],
-    "compress_chunk": ["compress.hip", "common.h", "kernels.h"],
-    "prefill_state": ["compress.hip", "common.h", "kernels.h"],
+    "fold_append": ["compress.hip", "common.h", "kernels.h", "fold.h"],
+    "compress_chunk": ["compress.hip", "common.h", "kernels.h", "fold.h"],
+    "prefill_state": ["compress.hip", "common.h", "kernels.h", "fold.h"],
+    "prep_rows": ["compress.hip", "common.h", "kernels.h", "fold.h"],
 }
 
 
