@@ -17,6 +17,10 @@ reports the traffic only while the kernel is unchanged.
     python -m sparse_attention_csa_amd.profiling --workload decode_1m \\
         --trace DIR --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \\
         --copy-mib 512 --command "..." --out OUTDIR
+
+``--mfma-util DIR --mops DIR`` (a ``MfmaUtil`` pass and a pass of the
+``SQ_INSTS_VALU_MFMA_MOPS_*`` counters) writes the MFMA utilisation summary
+instead.
 """
 
 import argparse
@@ -154,19 +158,58 @@ def summarize(args):
     print(f"wrote {txt} and {js}")
 
 
+MOPS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_INSTS_VALU_MFMA_MOPS_F6F4")
+
+
+def summarize_mfma(args):
+    """MFMA utilisation per kernel: the derived MfmaUtil (percent of the
+    time the matrix cores are busy, summed over the SIMDs over GPU-active
+    cycles times the SIMD count) and the MFMA operation counts (512 FLOP
+    per counted op, as the derived MfmaFlops* counters define them), with
+    the trace's average duration for the achieved rate."""
+    stats = kernel_stats(args.trace)
+    util = counter_means(args.mfma_util, "MfmaUtil")
+    mops = {c: counter_means(args.mops, c) for c in MOPS}
+    lines = [f"# rocprofv3 MFMA summary: workload {args.workload}", "",
+             "commands:", f"  {args.command_pmc}", "",
+             "MfmaUtil = sum over SIMDs of SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE max * SIMDs) * 100;",
+             "flop = 512 * SQ_INSTS_VALU_MFMA_MOPS_<type> per dispatch; rate over the trace's average duration", "",
+             f"{'kernel':40s} {'avg_us':>9s} {'MfmaUtil%':>10s} {'bf16_GF':>9s} {'f8_GF':>9s} {'f6f4_GF':>9s} "
+             f"{'TFLOP/s':>9s}"]
+    for k in sorted(util, key=lambda k: -util[k]):
+        if "at::" in k or "rocclr" in k or k not in stats:
+            continue
+        avg = stats[k][1]
+        gf = [mops[c].get(k, 0.0) * 512 / 1e9 for c in MOPS]
+        rate = sum(gf) / 1e3 / (avg / 1e6) if avg > 0 else 0.0
+        lines.append(f"{k[:40]:40s} {avg:9.2f} {util[k]:10.2f} {gf[0]:9.2f} {gf[1]:9.2f} {gf[2]:9.2f} {rate:9.1f}")
+    os.makedirs(args.out, exist_ok=True)
+    path = os.path.join(args.out, f"{args.workload}_mfma.txt")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    print("wrote", path)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
     ap.add_argument("--trace", required=True)
-    ap.add_argument("--fetch", required=True)
-    ap.add_argument("--write", required=True)
-    ap.add_argument("--copy-fetch", required=True)
-    ap.add_argument("--copy-write", required=True)
-    ap.add_argument("--copy-mib", type=int, required=True)
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
+    ap.add_argument("--copy-mib", type=int)
+    ap.add_argument("--mfma-util", help="MfmaUtil counter run (MFMA summary instead of traffic)")
+    ap.add_argument("--mops", help="SQ_INSTS_VALU_MFMA_MOPS_* counter run")
     ap.add_argument("--command-trace", default="")
     ap.add_argument("--command-pmc", default="")
     ap.add_argument("--out", required=True)
-    summarize(ap.parse_args())
+    args = ap.parse_args()
+    if args.mfma_util:
+        summarize_mfma(args)
+    else:
+        summarize(args)
 
 
 if __name__ == "__main__":
