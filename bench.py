@@ -67,9 +67,10 @@ def attend_splits(BT, H, rows_max, heads_per_wg=64):
 
 
 # benchmark timing-hook names -> the kernel symbols rocprofv3 reports
+# (prefixes: a workload's profile holds one instantiation of each)
 ROCPROF_NAMES = {
-    "attend_dense_mfma": "attend_mfma_kernel<0>",
-    "attend_sparse_rows": "attend_rows_kernel<0>",
+    "attend_dense_mfma": "attend_mfma_kernel<",
+    "attend_sparse_rows": "attend_rows_kernel<",
     "topk_resolve": "topk_fused_resolve_kernel",
 }
 
@@ -84,7 +85,7 @@ def profiled_traffic(workload, hook_name):
     with open(path) as fh:
         rec = json.load(fh)
     want = ROCPROF_NAMES.get(hook_name)
-    names = [k for k in rec["kernels"] if (k == want if want else k.startswith(hook_name + "_kernel"))]
+    names = [k for k in rec["kernels"] if k.startswith(want if want else hook_name + "_kernel")]
     if len(names) != 1:
         return None
     k = names[0]

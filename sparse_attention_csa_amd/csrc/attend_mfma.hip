@@ -34,12 +34,10 @@
 // own token.  Split s of head group 0 also folds coordinates
 // [s cs, s cs + cs) of the entry that the block ending at the query position
 // completes: its sources, query slice and token slice arrive by DMA in the
-// ring slot not yet in use, the fold runs before the row loop (its results
-// wait in small LDS arrays: no registers stay live across the loop) and,
-// after the loop (so that the loop's waits count tile DMAs only), stores its
-// slice of the entry, writes its share of q_h . entry and q_h . token for
-// every head to its own slot of fold_s and appends its share of the token to
-// the tail and window rings.
+// ring slot not yet in use, the fold runs before the row loop (nothing of it
+// stays live across the loop), stores its slice of the entry, writes its
+// share of q_h . entry and q_h . token for every head to its own slot of
+// fold_s and appends its share of the token to the tail and window rings.
 // The merge kernel then sums the slices' shares in slice order (the same
 // order on every run: no atomics in the result path), adds the new entry and
 // the query's own token as two more rows, weights exp2(scale q . x - M), and
@@ -70,8 +68,10 @@ constexpr int kFoldSlots = 64;         // fold slices at most (c / 8): one fold_
 // 1-D grid: block L runs on XCD L % 8; the n_hg head groups of one (query,
 // split) are blocks L, L + 8, ... so they share that XCD's L2.
 // DEROT: the output's rotary coordinates are rotated back by the query
-// position (norm_rope); a separate instantiation leaves the default one as it was
-template <int DEROT>
+// position (norm_rope); FOLD: the decode fold runs inside (fold_mode).
+// Separate instantiations keep the code of one out of the others' register
+// allocation (the row loop's schedule depends on it).
+template <int DEROT, int FOLD>
 __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n_split, int rows_per_split) {
   __shared__ __attribute__((aligned(1024))) char tiles[kRing][kTN * kRowB];
   __shared__ uint32_t rvalid[kRing][kTN / 4];  // byte r % 4 of word r / 4: row r is a real row
@@ -81,7 +81,6 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   __shared__ Soft s_fpart[4][64];          // fold: per-wavefront partial states of <= 64 coordinates
   __shared__ float s_fnew[64];             // fold: the new entry's coordinates (bf16-rounded)
   __shared__ uint4 s_fapp[24];             // fold: x_new, stream 0, stream 1 slices (<= 64 coordinates each)
-  __shared__ float2 s_fshare[128];         // fold: this slice's (q . new entry, q . token) share per head
 
   const int n_hg = a.H / kHW;
   const int L = blockIdx.x;
@@ -194,10 +193,10 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   // the next entry: fold_now), this slice's share of q_h . entry and
   // q_h . token, and the token's share of the rings.  Its inputs come by DMA
   // into LDS with the first tiles (ring slot kRing - 1 and the P^T buffer
-  // are unused until the row loop starts); its results wait in small LDS
-  // arrays of their own, stored after the loop.
+  // are unused until the row loop starts), so nothing of it is live during
+  // the loop.
   const int fcs = a.fold_cs, fr0 = split * fcs;
-  const int fW = (a.fold_mode && hg == 0) ? (a.c - fr0 < 0 ? 0 : (a.c - fr0 < fcs ? a.c - fr0 : fcs)) : 0;
+  const int fW = (FOLD && a.fold_mode && hg == 0) ? (a.c - fr0 < 0 ? 0 : (a.c - fr0 < fcs ? a.c - fr0 : fcs)) : 0;
   const bool fold_now = fW > 0 && lim == (int64_t)cnt + 1 && cnt < a.E_cap;
   const FoldArgs& F = a.fold;
   const int fch = fW / 8;                                  // 16-byte chunks per slice row (bf16)
@@ -341,7 +340,10 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
         Soft acc0 = s_fpart[0][tid];
 #pragma unroll
         for (int g = 1; g < 4; ++g) acc0 = soft_merge_sel(acc0, s_fpart[g][tid]);
-        s_fnew[tid] = bf16_to_f32(f32_to_bf16(acc0.acc / acc0.l));  // (stored after the row loop)
+        const uint16_t vb = f32_to_bf16(acc0.acc / acc0.l);
+        s_fnew[tid] = bf16_to_f32(vb);
+        reinterpret_cast<uint16_t*>(F.kv_cache)[((size_t)b * a.E_cap + cnt) * kC + fr0 + tid] = vb;
+        a.fold_new[(size_t)b * kC + fr0 + tid] = vb;
       }
       lds_barrier();
     }
@@ -372,12 +374,26 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
           po += __shfl_xor(po, o, 64);
           pn += __shfl_xor(pn, o, 64);
         }
-        if (g < ng && g % fch == 0) s_fshare[g / fch] = float2{fold_now ? pn : 0.f, po};
+        if (g < ng && g % fch == 0) {
+          // this slice's own slot: (q . new entry, q . token) shares
+          float* fs = a.fold_s + 2 * (((size_t)b * H + g / fch) * kFoldSlots + split);
+          *reinterpret_cast<float2*>(fs) = float2{fold_now ? pn : 0.f, po};
+        }
       }
     }
-    // (the fold's global stores wait until after the row loop: the loop's
-    // waits then count tile DMAs only, with no wait for the tiles in flight
-    // before it starts)
+    // the token's share of the rings (every step)
+    if (tid < 3 * fch) {
+      const int which = tid / fch, cc = fr0 + 8 * (tid % fch);
+      const bool small = t < 0x7fffffff;  // 32-bit remainders
+      const int ws = small ? (int)((uint32_t)t % (uint32_t)F.n_win) : (int)(t % F.n_win);
+      const int ts = small ? (int)((uint32_t)t % (uint32_t)F.R) : (int)(t % F.R);
+      uint16_t* dst = which == 0 ? reinterpret_cast<uint16_t*>(F.win_ring) + ((size_t)b * F.n_win + ws) * a.c + cc
+                                 : reinterpret_cast<uint16_t*>(F.tail) + (((size_t)b * 2 + (which - 1)) * F.R + ts) * a.c + cc;
+      *reinterpret_cast<uint4*>(dst) = s_fapp[tid];
+    }
+    if (split == 0 && tid == 0) a.fold_row[b] = fold_now ? cnt + 1 : 0;
+    // the tile waits below count DMAs only
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
   }
 
   // running softmax state of this wavefront's 16 heads: the reference max
@@ -555,29 +571,6 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     for (int dt = 0; dt < 32; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     l_lane = 0.f;
     prologue();
-  }
-
-  if (fW > 0) {
-    // the fold's stores: the new entry's slice (cache and the merge's copy),
-    // this slice's (q . entry, q . token) share of every head in its own
-    // slot, and the token's share of the rings (every step)
-    if (fold_now && tid < fW) {
-      const uint16_t vb = f32_to_bf16(s_fnew[tid]);
-      reinterpret_cast<uint16_t*>(F.kv_cache)[((size_t)b * a.E_cap + cnt) * kC + fr0 + tid] = vb;
-      a.fold_new[(size_t)b * kC + fr0 + tid] = vb;
-    }
-    for (int hh = tid; hh < H; hh += 256)
-      *reinterpret_cast<float2*>(a.fold_s + 2 * (((size_t)b * H + hh) * kFoldSlots + split)) = s_fshare[hh];
-    if (tid < 3 * fch) {
-      const int which = tid / fch, cc = fr0 + 8 * (tid % fch);
-      const bool small = t < 0x7fffffff;  // 32-bit remainders
-      const int ws = small ? (int)((uint32_t)t % (uint32_t)F.n_win) : (int)(t % F.n_win);
-      const int ts = small ? (int)((uint32_t)t % (uint32_t)F.R) : (int)(t % F.R);
-      uint16_t* dst = which == 0 ? reinterpret_cast<uint16_t*>(F.win_ring) + ((size_t)b * F.n_win + ws) * a.c + cc
-                                 : reinterpret_cast<uint16_t*>(F.tail) + (((size_t)b * 2 + (which - 1)) * F.R + ts) * a.c + cc;
-      *reinterpret_cast<uint4*>(dst) = s_fapp[tid];
-    }
-    if (split == 0 && tid == 0) a.fold_row[b] = fold_now ? cnt + 1 : 0;
   }
 
   // per-head sum over the four lane groups (this wavefront's 16 heads)
@@ -836,9 +829,11 @@ hipError_t launch_attend_mfma(const AttendArgs& a0, int rows_max, hipStream_t s)
   const long long units = (long long)ns * a.B * a.Tq;       // (query, split) pairs
   const long long blocks = (units + 7) / 8 * 8 * n_hg;      // padded to whole XCD rounds
   if (a.derot_freq)
-    CSA_LAUNCH("attend_dense_mfma", attend_mfma_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<1, 0>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+  else if (a.fold_mode)
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
   else
-    CSA_LAUNCH("attend_dense_mfma", attend_mfma_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 0>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
   if (ns > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

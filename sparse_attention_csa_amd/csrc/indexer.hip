@@ -136,13 +136,17 @@ constexpr int kPfD = 128, kPfH = 64;
 // chunk: 8 gave the same time as 4 (the kernel is not bound by the key
 // traffic), 16 spilled registers and was slower.
 constexpr int kPfQpw = 4;
+// MFMA shape of the scorer: 16 (16x16x32) or 32 (32x32x16).  Measured on
+// the 4096-query chunk: 4.94 ms with 16, 5.23 ms with 32 (180 VGPRs: two
+// wavefronts per SIMD instead of three), 5.12 ms with 32 and 8 queries.
+constexpr int kPfMfma = 16;
 }  // namespace
 
 bool index_prefill_mfma_supported(const IndexArgs& a) {
   return a.idx_dtype == BF16 && a.H_I == kPfH && a.d_I == kPfD && a.Tq % kPfQpw == 0;
 }
 
-template <int QPW>
+template <int QPW, int MF>
 __global__ __launch_bounds__(64 * QPW) void index_score_prefill_kernel(IndexArgs a) {
   using namespace tile;
   constexpr int kT = 64 * QPW;               // threads
@@ -169,18 +173,35 @@ __global__ __launch_bounds__(64 * QPW) void index_score_prefill_kernel(IndexArgs
   const int ntiles = (int)((e1 - e0 + kPfTile - 1) / kPfTile);
   const uint16_t* keys = reinterpret_cast<const uint16_t*>(a.keys) + (size_t)b * a.E_cap * kPfD;
 
-  // A operands: Q rows = heads 16 ht + li, d = 32 ks + 8 lg .. +7
-  bf16x8_t qa[4][4];
-  float wr[4][4];  // weights of heads 16 ht + 4 lg + i
+  // A operands.  16x16x32: Q rows = heads 16 ht + li, d = 32 ks + 8 lg ..
+  // +7, weights of heads 16 ht + 4 lg + i.  32x32x16: Q rows = heads
+  // 32 ht + (l % 32), d = 16 ks + 8 (l / 32) .. +7, weights of heads
+  // 32 ht + 8 j + 4 (l / 32) + r (the rows of the lane's accumulator).
+  constexpr int kHT = MF == 32 ? 2 : 4, kKS = MF == 32 ? 8 : 4, kNW = MF == 32 ? 16 : 4;
+  bf16x8_t qa[kHT][kKS];
+  float wr[kHT][kNW];
   {
     const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + (size_t)row * kPfH * kPfD;
+    const float* wrow = a.w + (size_t)row * kPfH;
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) {
+    for (int ht = 0; ht < kHT; ++ht) {
+      if constexpr (MF == 32) {
+        const int hi = l & 31, half = l >> 5;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        qa[ht][ks] = *reinterpret_cast<const bf16x8_t*>(q + (size_t)(16 * ht + li) * kPfD + 32 * ks + 8 * lg);
-      const float4 wv = *reinterpret_cast<const float4*>(a.w + (size_t)row * kPfH + 16 * ht + 4 * lg);
-      wr[ht][0] = wv.x; wr[ht][1] = wv.y; wr[ht][2] = wv.z; wr[ht][3] = wv.w;
+        for (int ks = 0; ks < kKS; ++ks)
+          qa[ht][ks] = *reinterpret_cast<const bf16x8_t*>(q + (size_t)(32 * ht + hi) * kPfD + 16 * ks + 8 * half);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 wv = *reinterpret_cast<const float4*>(wrow + 32 * ht + 8 * j + 4 * half);
+          wr[ht][4 * j] = wv.x; wr[ht][4 * j + 1] = wv.y; wr[ht][4 * j + 2] = wv.z; wr[ht][4 * j + 3] = wv.w;
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks)
+          qa[ht][ks] = *reinterpret_cast<const bf16x8_t*>(q + (size_t)(16 * ht + li) * kPfD + 32 * ks + 8 * lg);
+        const float4 wv = *reinterpret_cast<const float4*>(wrow + 16 * ht + 4 * lg);
+        wr[ht][0] = wv.x; wr[ht][1] = wv.y; wr[ht][2] = wv.z; wr[ht][3] = wv.w;
+      }
     }
   }
   // thread's share of a tile: chunks tid + kT u (entry c / 16, chunk c % 16);
@@ -216,6 +237,33 @@ __global__ __launch_bounds__(64 * QPW) void index_score_prefill_kernel(IndexArgs
     if (j + 1 < ntiles) next = load_tile(j + 1);  // in flight while tile j is scored
     const uint4* T = s_k[j & 1];
     const int64_t te = e0 + (int64_t)j * kPfTile;
+    if constexpr (MF == 32) {
+      // 32-entry blocks: D[32 heads x 32 entries] per head tile on
+      // v_mfma_f32_32x32x16_bf16; lane (entry l % 32) holds 16 heads of each
+      // tile, so the head sum is in-lane plus one exchange (l ^ 32)
+#pragma unroll
+      for (int kb = 0; kb < kPfTile / 32; ++kb) {
+        const int ek = 32 * kb + (l & 31);
+        f32x16_t c[kHT];
+#pragma unroll
+        for (int ht = 0; ht < kHT; ++ht) c[ht] = f32x16_t{};
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks) {
+          // B operand: entry ek, d = 16 ks + 8 (l / 32) .. +7 (chunk 2 ks + l / 32)
+          const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, T[ek * 16 + ((2 * ks + (l >> 5)) ^ (ek & 15))]);
+#pragma unroll
+          for (int ht = 0; ht < kHT; ++ht) c[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][ks], kf, c[ht], 0, 0, 0);
+        }
+        float part = 0.f;
+#pragma unroll
+        for (int ht = 0; ht < kHT; ++ht)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) part += wr[ht][i] * fmaxf(c[ht][i], 0.f);
+        part += __shfl_xor(part, 32, 64);
+        const int64_t e = te + ek;
+        if (l < 32 && e < nv_q && e < e1) out[e] = a.score_bf16 ? round_bf16(part) : part;
+      }
+    } else
 #pragma unroll
     for (int kb = 0; kb < kPfTile / 16; ++kb) {
       f32x4_t c[4];
@@ -276,7 +324,7 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t s, const FoldArgs*
     e = launch_index_score_mfma(a, tw, 1, 1, &n_wg_fused, fold, s);
   } else if (index_prefill_mfma_supported(a)) {
     const unsigned gx = (a.E_cap + kPfChunk - 1) / kPfChunk;
-    CSA_LAUNCH("index_score_prefill", index_score_prefill_kernel<kPfQpw>, dim3(gx, rows / kPfQpw),
+    CSA_LAUNCH("index_score_prefill", (index_score_prefill_kernel<kPfQpw, kPfMfma>), dim3(gx, rows / kPfQpw),
                dim3(64 * kPfQpw), 0, s, a);
     e = hipGetLastError();
   } else {
