@@ -56,11 +56,17 @@ typedef enum {
   CSA_F32 = 0,  /* IEEE binary32                                            */
   CSA_BF16 = 1, /* bfloat16                                                 */
   CSA_E4M3 = 2, /* OCP FP8 E4M3FN, one float32 scale per vector (v = q * s) */
-  CSA_MXFP4 = 3 /* OCP MX FP4: E2M1 values, two per byte (element 2j in the
+  CSA_MXFP4 = 3, /* OCP MX FP4: E2M1 values, two per byte (element 2j in the
                    low nibble of byte j), one E8M0 scale byte per block of 32
                    consecutive values (v = e2m1 * 2^(code - 127)); [book]
                    ch. 16 "Why use fine-grained scales?", ch. 8: a 128-dim
                    indexer key is 64 bytes plus four scale bytes            */
+  CSA_FP8BF16 = 4 /* the main compressed entry of [book] ch. 8 "The main
+                   compressed-entry payload" (c = 512): 448 E4M3FN codes
+                   with one float32 scale per entry (max |v[0:448]| / 448)
+                   then the 64 rotary coordinates as bf16, 576 bytes; as a
+                   layer's kv_dtype the activations (queries, window rows,
+                   token streams, outputs) are bf16                          */
 } csa_dtype;
 
 /* Which compressed entries a query at position t may read ([book] ch. 5 "When
@@ -76,8 +82,9 @@ const char* csa_last_error(void);
 
 /* ABI version of this header (bumped on incompatible change; 2 added
  * csa_layer_desc.split_rows; 3 added CSA_MXFP4 with untyped scale pointers,
- * csa_layer_desc.score_bf16, the score_bf16 argument of csa_index_topk, and
- * the normalisation / rotary fields of csa_layer_desc and csa_layer_state). */
+ * csa_layer_desc.score_bf16, the score_bf16 argument of csa_index_topk, the
+ * normalisation / rotary fields of csa_layer_desc and csa_layer_state, and
+ * the FP8BF16 main entry with csa_layer_state.kv_scale). */
 int csa_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -227,7 +234,8 @@ typedef struct {
   int k;             /* top-k budget (CSA)                                    */
   int n_win;         /* sliding-window width                                  */
   int vis;           /* csa_visibility                                        */
-  int kv_dtype;      /* F32 or BF16: activations, caches, outputs             */
+  int kv_dtype;      /* F32 or BF16: activations, caches, outputs; FP8BF16:  */
+                     /* 576-byte cache entries, bf16 activations (c = 512)   */
   int idx_dtype;     /* F32, BF16, E4M3 or MXFP4: indexer queries and keys    */
   float scale;       /* attention logit scale (1/sqrt(c) for the pages)       */
   int split_rows;    /* decode: 0 = the attention's row splits are sized for  */
@@ -277,6 +285,7 @@ typedef struct {
   const double* rope_inv_freq; /* [rope_dims/2] inverse frequencies (the      */
                                /* caller's scaling, e.g. base^(-2i/rope_dims)) */
                                /* (the three only read when norm_rope)         */
+  float* kv_scale;             /* [B][E_cap] per-entry scales (FP8BF16)        */
 } csa_layer_state;
 
 /* One decode step: one new token per sequence at position pos[b]. */

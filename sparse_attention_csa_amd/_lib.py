@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libcsa.so")
 
 CSA_OK, CSA_ERR_ARG, CSA_ERR_UNSUPPORTED, CSA_ERR_WORKSPACE, CSA_ERR_DEVICE = range(5)
-CSA_F32, CSA_BF16, CSA_E4M3, CSA_MXFP4 = 0, 1, 2, 3
+CSA_F32, CSA_BF16, CSA_E4M3, CSA_MXFP4, CSA_FP8BF16 = 0, 1, 2, 3, 4
 CSA_VIS_PRIOR_BLOCKS, CSA_VIS_COMPLETED = 0, 1
 CSA_LAYER_CSA, CSA_LAYER_HCA = 1, 2
 
@@ -49,7 +49,7 @@ class LayerState(C.Structure):
                 ("win_ring", C.c_void_p), ("tail", C.c_void_p), ("idx_tail", C.c_void_p),
                 ("bias_a", C.c_void_p), ("bias_b", C.c_void_p), ("ibias_a", C.c_void_p),
                 ("ibias_b", C.c_void_p), ("sink", C.c_void_p), ("q_norm_w", C.c_void_p),
-                ("kv_norm_w", C.c_void_p), ("rope_inv_freq", C.c_void_p)]
+                ("kv_norm_w", C.c_void_p), ("rope_inv_freq", C.c_void_p), ("kv_scale", C.c_void_p)]
 
 
 class DecodeIO(C.Structure):

@@ -263,7 +263,10 @@ static csa_status check_desc(const csa_layer_desc* d) {
   REQUIRE(d->n_win >= 1, CSA_ERR_ARG, "n_win must be >= 1");
   REQUIRE(d->n_win <= 256, CSA_ERR_UNSUPPORTED, "n_win <= 256 supported");
   REQUIRE(d->vis == 0 || d->vis == 1, CSA_ERR_ARG, "bad visibility");
-  REQUIRE(d->kv_dtype == CSA_F32 || d->kv_dtype == CSA_BF16, CSA_ERR_UNSUPPORTED, "kv_dtype must be F32 or BF16");
+  REQUIRE(d->kv_dtype == CSA_F32 || d->kv_dtype == CSA_BF16 || d->kv_dtype == CSA_FP8BF16, CSA_ERR_UNSUPPORTED,
+          "kv_dtype must be F32, BF16 or FP8BF16");
+  REQUIRE(d->kv_dtype != CSA_FP8BF16 || d->c == csa::kF8Dims + 64, CSA_ERR_UNSUPPORTED,
+          "FP8BF16 entries are 448 + 64 coordinates (c = 512, got %d)", d->c);
   REQUIRE(d->overlap == 0 || d->overlap == 1, CSA_ERR_ARG, "overlap must be 0 or 1");
   REQUIRE(d->split_rows >= 0 && d->split_rows % 16 == 0, CSA_ERR_ARG,
           "split_rows must be 0 or a positive multiple of 16 (got %d)", d->split_rows);
@@ -306,8 +309,13 @@ static csa_status check_state(const csa_layer_desc* d, const csa_layer_state* s)
   if (d->norm_rope) {
     REQ_PTR(s->q_norm_w); REQ_PTR(s->kv_norm_w); REQ_PTR(s->rope_inv_freq);
   }
+  REQUIRE(d->kv_dtype != CSA_FP8BF16 || s->kv_scale != nullptr, CSA_ERR_ARG, "FP8BF16 entries need kv_scale");
   return CSA_OK;
 }
+
+// the activations' dtype (queries, window rows, streams, outputs): bf16
+// under the FP8 + BF16 cache entry
+static int act_dtype(const csa_layer_desc* d) { return d->kv_dtype == CSA_FP8BF16 ? CSA_BF16 : d->kv_dtype; }
 
 // norm_rope: the prepared queries [B][T][H][c] and (prefill) window rows
 // [B][n_win-1+T][c], at the start of the workspace after the fold counters
@@ -383,7 +391,8 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
 
   csa::FoldArgs f{};
   f.counters = fold_counters;
-  f.dtype = d->kv_dtype; f.idx_dtype = is_csa ? d->idx_dtype : -1;
+  f.dtype = act_dtype(d); f.idx_dtype = is_csa ? d->idx_dtype : -1;
+  f.kv_fmt = d->kv_dtype == CSA_FP8BF16; f.kv_scale = s->kv_scale;
   f.B = B; f.c = d->c; f.d_I = d->d_I; f.m = d->m; f.R = tail_depth(d); f.n_win = d->n_win;
   f.vis = d->vis; f.overlap = d->overlap;
   f.pos = io->pos; f.n_entries = s->n_entries; f.streams = io->streams; f.idx_streams = io->idx_streams;
@@ -402,7 +411,8 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
     x.vis = d->vis; x.scores = nullptr; x.topk_idx = io->topk_idx; x.topk_cnt = io->topk_cnt; x.ws = w;
   }
   csa::AttendArgs a{};
-  a.dtype = d->kv_dtype; a.q = io->q; a.kv = s->kv_cache; a.E_cap = s->E_cap;
+  a.dtype = act_dtype(d); a.q = io->q; a.kv = s->kv_cache; a.E_cap = s->E_cap;
+  a.kv_fmt = d->kv_dtype == CSA_FP8BF16; a.kv_scale = s->kv_scale;
   a.win = s->win_ring; a.W_cap = d->n_win; a.win_pos0 = nullptr; a.win_pos0_const = 0; a.n_win = d->n_win;
   a.sink = s->sink; a.q_pos = io->pos; a.scale = d->scale;
   a.B = B; a.Tq = 1; a.H = d->H; a.c = d->c; a.out = io->out; a.lse = io->lse;
@@ -467,7 +477,7 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
   const int S = n_streams(d), R = tail_depth(d);
   const int64_t first = io->pos0 / m;
   const int n_new = T / m;
-  const size_t esz = d->kv_dtype == CSA_F32 ? 4 : 2;
+  const size_t esz = act_dtype(d) == CSA_F32 ? 4 : 2;
 
   // compress the chunk's blocks: main entries, then (CSA) indexer keys
   auto compress = [&](const void* streams, int width, const void* tail, void* out, int out_dtype,
@@ -477,7 +487,7 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
     const int ns = overlap ? 4 : 2;
     const char* base = (const char*)streams;
     const size_t plane = (size_t)T * width * esz;
-    c.dtype = d->kv_dtype;
+    c.dtype = act_dtype(d);
     c.ca = base; c.za = base + plane;
     c.cb = overlap ? base + 2 * plane : nullptr;
     c.zb = overlap ? base + 3 * plane : nullptr;
@@ -494,7 +504,7 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
     c.out = out; c.out_dtype = out_dtype; c.out_scale = out_scale; c.E_cap = s->E_cap; c.first = first;
     return csa::launch_compress(c, hs);
   };
-  hipError_t e = compress(io->streams, d->c, s->tail, s->kv_cache, d->kv_dtype, nullptr, s->bias_a,
+  hipError_t e = compress(io->streams, d->c, s->tail, s->kv_cache, d->kv_dtype, s->kv_scale, s->bias_a,
                           s->bias_b, d->overlap != 0, d->norm_rope != 0);
   if (e != hipSuccess) return from_hip(e, "hybrid_layer_prefill/compress");
   csa::AttendArgs a{};
@@ -518,7 +528,8 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
   } else {
     a.n_entries = s->n_entries; a.n_add = n_new; a.m = m; a.vis = d->vis; a.dense = 1;
   }
-  a.dtype = d->kv_dtype; a.q = io->q; a.kv = s->kv_cache; a.E_cap = s->E_cap;
+  a.dtype = act_dtype(d); a.q = io->q; a.kv = s->kv_cache; a.E_cap = s->E_cap;
+  a.kv_fmt = d->kv_dtype == CSA_FP8BF16; a.kv_scale = s->kv_scale;
   a.win = io->win; a.W_cap = d->n_win - 1 + T; a.win_pos0 = nullptr;
   a.win_pos0_const = io->pos0 - (d->n_win - 1); a.n_win = d->n_win;
   a.sink = s->sink; a.q_pos = nullptr; a.q_pos0 = io->pos0; a.scale = d->scale;
@@ -527,7 +538,7 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
   if (d->norm_rope) {
     // the chunk's queries and window rows prepared for the attention
     csa::PrepArgs pa{};
-    pa.dtype = d->kv_dtype; pa.B = B; pa.T = T; pa.H = d->H; pa.c = d->c; pa.n_win = d->n_win;
+    pa.dtype = act_dtype(d); pa.B = B; pa.T = T; pa.H = d->H; pa.c = d->c; pa.n_win = d->n_win;
     pa.pos0 = io->pos0; pa.nr = nr; pa.q = io->q; pa.win = io->win; pa.q_prep = q_prep; pa.win_prep = win_prep;
     e = csa::launch_prep_rows(pa, hs);
     if (e != hipSuccess) return from_hip(e, "hybrid_layer_prefill/prep");
@@ -540,7 +551,7 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
   if (e != hipSuccess) return from_hip(e, "hybrid_layer_prefill/attend");
 
   csa::PrefillStateArgs p{};
-  p.dtype = d->kv_dtype; p.B = B; p.T = T; p.c = d->c; p.d_I = d->d_I; p.R = R; p.n_win = d->n_win; p.S = S;
+  p.dtype = act_dtype(d); p.B = B; p.T = T; p.c = d->c; p.d_I = d->d_I; p.R = R; p.n_win = d->n_win; p.S = S;
   p.pos0 = io->pos0; p.win = d->norm_rope ? win_prep : io->win;  // the ring holds prepared rows
   p.streams = io->streams; p.idx_streams = is_csa ? io->idx_streams : nullptr;
   p.win_ring = s->win_ring; p.tail = s->tail; p.idx_tail = s->idx_tail; p.n_entries = s->n_entries;

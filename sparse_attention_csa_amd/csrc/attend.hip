@@ -8,7 +8,9 @@
 // Generic VALU kernel: one WG per (query, group of 8 heads); row tiles are
 // gathered into LDS (rows padded by one float against bank conflicts), the
 // online softmax runs per head, and each thread accumulates 1/32 of a head's
-// output row.
+// output row.  It also reads the 576-byte FP8 + BF16 entries ([book] ch. 8
+// "The main compressed-entry payload"), decoding each coordinate as it
+// gathers the row.
 
 #include "common.h"
 #include "kernels.h"
@@ -52,6 +54,8 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
     q_s[i] = (h0 + h < H) ? ld(q, i) * a.scale : 0.f;
   }
   const T* kv = reinterpret_cast<const T*>(a.kv) + (size_t)b * a.E_cap * c;
+  const uint8_t* kv8 = reinterpret_cast<const uint8_t*>(a.kv) + (size_t)b * a.E_cap * kF8RowB;  // (kv_fmt)
+  const float* ksc = a.kv_scale ? a.kv_scale + (size_t)b * a.E_cap : nullptr;
   const T* win = reinterpret_cast<const T*>(a.win) + (size_t)b * a.W_cap * c;
   const int32_t* ids = a.dense ? nullptr : a.topk_idx + (size_t)row * a.k;
 
@@ -83,7 +87,13 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
       if (valid_s[r]) {
         if (j < n_c) {
           const int64_t e = a.dense ? j : ids[j];
-          v = ld(kv, (size_t)e * c + d);
+          if (a.kv_fmt) {  // the 576-byte entry: scaled e4m3 codes, then bf16
+            const uint8_t* er = kv8 + (size_t)e * kF8RowB;
+            v = d < kF8Dims ? e4m3_to_f32(er[d]) * ksc[e]
+                            : bf16_to_f32(*reinterpret_cast<const uint16_t*>(er + kF8Dims + 2 * (d - kF8Dims)));
+          } else {
+            v = ld(kv, (size_t)e * c + d);
+          }
         } else {
           const int64_t p = t - n_w + 1 + (j - n_c);
           int64_t wr = (p - wpos0) % a.W_cap;
@@ -206,9 +216,10 @@ size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max, int split_rows
 }
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
-  if (a.dtype == BF16 && a.dense && attend_mfma_shape_ok(a.H, a.c))
+  // (576-byte entries: the generic kernel decodes them row by row)
+  if (a.dtype == BF16 && !a.kv_fmt && a.dense && attend_mfma_shape_ok(a.H, a.c))
     return launch_attend_mfma(a, a.E_cap + a.n_win, s);
-  if (a.dtype == BF16 && !a.dense && attend_rows_shape_ok(a.H, a.c))
+  if (a.dtype == BF16 && !a.kv_fmt && !a.dense && attend_rows_shape_ok(a.H, a.c))
     return launch_attend_rows(a, a.k + a.n_win, s);
   dim3 grid(a.B * a.Tq, (a.H + kHG - 1) / kHG), block(256);
   const size_t sh = sizeof(float) * ((size_t)kHG * a.c + (size_t)kTile * (a.c + 1) + kHG * kTile + kHG + kTile);

@@ -752,7 +752,8 @@ void attend_mfma_plan(int BT, int H, int rows_max, int split_rows, int* n_split,
 // block handled by one thread of its slice.
 bool attend_fuses_fold(AttendArgs& a, const FoldArgs& f) {
   a.fold_mode = 0;
-  if (!a.dense || a.dtype != BF16 || f.dtype != BF16 || !attend_mfma_shape_ok(a.H, a.c) || a.Tq != 1 ||
+  if (!a.dense || a.dtype != BF16 || f.dtype != BF16 || a.kv_fmt || f.kv_fmt || !attend_mfma_shape_ok(a.H, a.c) ||
+      a.Tq != 1 ||
       a.n_add != 0 || a.win_pos0 != nullptr || a.win_pos0_const != 0 || f.overlap || f.idx_dtype >= 0 ||
       f.B != a.B || f.c != a.c || f.n_win != a.W_cap || f.R < 2 * f.m)
     return false;

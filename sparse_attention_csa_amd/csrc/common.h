@@ -67,7 +67,8 @@ CSA_DEV uint8_t f32_to_e4m3(float y) {
 // magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) in blocks of 32 sharing one E8M0
 // scale 2^(code - 127).  Two elements per byte, element 2j in the low
 // nibble of byte j.
-struct mx4 {};  // tag type: MXFP4 storage (a kernel template argument)
+struct mx4 {};   // tag type: MXFP4 storage (a kernel template argument)
+struct f8b16 {};  // tag type: the 576-byte FP8 + BF16 main entry
 
 CSA_DEV float e2m1_to_f32(uint32_t c) {
   const uint32_t e = (c >> 1) & 3u, f = c & 1u;

@@ -29,6 +29,19 @@ CSA_DEV const T* cptr(const void* p) {
   return reinterpret_cast<const T*>(p);
 }
 
+// the element type a compressor output is stored as when it is not the
+// 576-byte entry (the FP8 + BF16 tag maps to bf16, never used for it)
+template <typename TO>
+struct TIOf {
+  typedef TO type;
+};
+template <>
+struct TIOf<f8b16> {
+  typedef bf16 type;
+};
+template <typename TO>
+using TI_of = typename TIOf<TO>::type;
+
 // --------------------------------------------------------------------------
 // csa_compress: entries of a chunk.  grid (T/m, B), 256 threads.  Each thread
 // owns up to 2 coordinates (c <= 512) and walks all sources of its entry.
@@ -110,7 +123,7 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
       if (r < c && (r & 1) == 0) o[r / 2] = (uint8_t)(code | (odd << 4));
       if (r < c && (r & 31) == 0) so[r / 32] = (uint8_t)sc;
     }
-  } else if constexpr (sizeof(TO) == 1) {
+  } else if constexpr (std::is_same<TO, uint8_t>::value) {
     // e4m3 output: one scale per entry = max|v| / 448
     float amax = 0.f;
     for (int u = 0; u < nv; ++u) amax = fmaxf(amax, fabsf(vals[u]));
@@ -124,12 +137,16 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
     int u = 0;
     for (int r = tid; r < c; r += 256, ++u) o[r] = f32_to_e4m3(vals[u] / scale);
     if (tid == 0) reinterpret_cast<float*>(a.out_scale)[(size_t)b * a.E_cap + a.first + i] = scale;
-  } else if (a.nr.on) {
-    // the entry prepared for the core attention: RMSNorm over its c
+  } else if (a.nr.on || std::is_same<TO, f8b16>::value) {
+    // the entry prepared for the core attention (nr.on): RMSNorm over its c
     // coordinates, then the rotary pairs (neighbouring lanes) at its position,
-    // the first token of its block
-    TO* o = reinterpret_cast<TO*>(a.out) + orow;
+    // the first token of its block; stored as T or as the 576-byte entry
     const int nu = (c + 255) / 256;  // the same trip count in every lane
+    if (!a.nr.on) {
+      store_entry<TI_of<TO>>(vals, nu, c, std::is_same<TO, f8b16>::value, a.out,
+                             reinterpret_cast<float*>(a.out_scale), (size_t)b * a.E_cap + a.first + i, s_red);
+      return;
+    }
     float ss = 0.f;
     for (int u = 0; u < nu; ++u)
       if (tid + 256 * u < c) ss += vals[u] * vals[u];
@@ -149,9 +166,11 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
         rope_cs(pos, a.nr.inv_freq[(r - (c - R)) >> 1], &cs, &sn);
         v = (r & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
       }
-      if (r < c) st(o, r, v);
+      vals[u] = v;
     }
-  } else {
+    store_entry<TI_of<TO>>(vals, nu, c, std::is_same<TO, f8b16>::value, a.out, reinterpret_cast<float*>(a.out_scale),
+                           (size_t)b * a.E_cap + a.first + i, s_red);
+  } else if constexpr (!std::is_same<TO, f8b16>::value) {
     TO* o = reinterpret_cast<TO*>(a.out) + orow;
     int u = 0;
     for (int r = tid; r < c; r += 256, ++u) st(o, r, vals[u]);
@@ -166,6 +185,8 @@ static void launch_compress_to(const CompressArgs& a, dim3 grid, dim3 block, hip
     CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<T, bf16>), grid, block, 0, s, a);
   else if (a.out_dtype == E4M3)
     CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<T, uint8_t>), grid, block, 0, s, a);
+  else if (a.out_dtype == FP8BF16)
+    CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<T, f8b16>), grid, block, 0, s, a);
   else
     CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<T, mx4>), grid, block, 0, s, a);
 }
@@ -213,12 +234,13 @@ __global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
   const int nstr = a.overlap ? 4 : 2;
   const int slot = (int)(t % R);
   const bool has_idx = a.idx_dtype >= 0;
-  const int main_jobs = a.nr.on ? 1 : c / kFoldCW;
+  const bool whole = a.nr.on || a.kv_fmt;  // one workgroup folds the whole entry
+  const int main_jobs = whole ? 1 : c / kFoldCW;
 
-  if (a.nr.on && job == 0) {
-    // the whole main entry, prepared (RMSNorm, then rotary pairs at its
-    // position m e), the main streams' appends and the new window row,
-    // prepared at t
+  if (whole && job == 0) {
+    // the whole main entry (norm_rope: prepared, RMSNorm then rotary pairs
+    // at its position m e; stored as T or as the 576-byte entry), the main
+    // streams' appends and the new window row (prepared at t with norm_rope)
     T* tail = reinterpret_cast<T*>(a.tail) + (size_t)b * nstr * R * c;
     const T* io = reinterpret_cast<const T*>(a.streams) + (size_t)b * nstr * c;
     if (fold) {
@@ -228,35 +250,41 @@ __global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
         const int r0 = 256 * u, W = c - r0 < 256 ? c - r0 : 256;
         val[u] = fold_job<T>(tail, io, c, r0, W, m, R, t, e, a.overlap && e > 0, a.bias_a, a.bias_b, s_part);
       }
-      float ss = 0.f;
-      for (int u = 0; u < nu; ++u)
-        if (256 * u + tid < c) ss += val[u] * val[u];
-      ss = wave_sum(ss);
-      if ((tid & 63) == 0) s_red[tid >> 6] = ss;
-      __syncthreads();
-      ss = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-      const float inv = 1.0f / sqrtf(ss / (float)c + a.nr.eps);
-      const int Rd = a.nr.rope_dims;
-      for (int u = 0; u < nu; ++u) {
-        const int r = 256 * u + tid;
-        float v = r < c ? val[u] * inv * a.nr.g_kv[r] : 0.f;
-        const float other = __shfl_xor(v, 1, 64);
-        if (r < c && r >= c - Rd) {
-          float cs, sn;
-          rope_cs((int64_t)m * e, a.nr.inv_freq[(r - (c - Rd)) >> 1], &cs, &sn);
-          v = (r & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
+      if (a.nr.on) {
+        float ss = 0.f;
+        for (int u = 0; u < nu; ++u)
+          if (256 * u + tid < c) ss += val[u] * val[u];
+        ss = wave_sum(ss);
+        if ((tid & 63) == 0) s_red[tid >> 6] = ss;
+        __syncthreads();
+        ss = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+        const float inv = 1.0f / sqrtf(ss / (float)c + a.nr.eps);
+        const int Rd = a.nr.rope_dims;
+        for (int u = 0; u < nu; ++u) {
+          const int r = 256 * u + tid;
+          float v = r < c ? val[u] * inv * a.nr.g_kv[r] : 0.f;
+          const float other = __shfl_xor(v, 1, 64);
+          if (r < c && r >= c - Rd) {
+            float cs, sn;
+            rope_cs((int64_t)m * e, a.nr.inv_freq[(r - (c - Rd)) >> 1], &cs, &sn);
+            v = (r & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
+          }
+          val[u] = v;
         }
-        if (r < c) st(reinterpret_cast<T*>(a.kv_cache), ((size_t)b * a.E_cap + e) * c + r, v);
       }
+      store_entry<T>(val, nu, c, a.kv_fmt, a.kv_cache, a.kv_scale, (size_t)b * a.E_cap + e, s_red);
     }
     for (int i = tid; i < nstr * c; i += kFoldT) {
       const int sc = i / c, r = i % c;
       tail[((size_t)sc * R + slot) * c + r] = io[(size_t)sc * c + r];
     }
-    if (tid < 64)
-      prep_row_wave(reinterpret_cast<const T*>(a.x_new) + (size_t)b * c,
-                    reinterpret_cast<T*>(a.win_ring) + ((size_t)b * a.n_win + (size_t)(t % a.n_win)) * c, c, a.nr,
-                    a.nr.g_kv, t);
+    T* ring = reinterpret_cast<T*>(a.win_ring) + ((size_t)b * a.n_win + (size_t)(t % a.n_win)) * c;
+    const T* xn = reinterpret_cast<const T*>(a.x_new) + (size_t)b * c;
+    if (a.nr.on) {
+      if (tid < 64) prep_row_wave(xn, ring, c, a.nr, a.nr.g_kv, t);
+    } else {
+      for (int r = tid; r < c; r += kFoldT) ring[r] = xn[r];
+    }
   } else if (job >= main_jobs + (has_idx ? 1 : 0)) {
     // the step's queries, prepared at t: one head per wavefront
     const int h = 4 * (job - main_jobs - (has_idx ? 1 : 0)) + (tid >> 6);
@@ -340,7 +368,7 @@ static void launch_fold_to(const FoldArgs& a, dim3 grid, dim3 block, hipStream_t
 hipError_t launch_fold_append(const FoldArgs& a, hipStream_t s) {
   // main-entry jobs (one with norm_rope: the entry's norm needs all of it),
   // the indexer-key job, the query jobs (norm_rope, four heads each)
-  const int jobs = (a.nr.on ? 1 : a.c / kFoldCW) + (a.idx_dtype >= 0 ? 1 : 0) + (a.nr.on ? (a.H + 3) / 4 : 0);
+  const int jobs = ((a.nr.on || a.kv_fmt) ? 1 : a.c / kFoldCW) + (a.idx_dtype >= 0 ? 1 : 0) + (a.nr.on ? (a.H + 3) / 4 : 0);
   dim3 grid(jobs, a.B), block(kFoldT);
   if (a.dtype == F32)
     launch_fold_to<float>(a, grid, block, s);

@@ -179,6 +179,44 @@ CSA_DEV float fold_job(const T* tail, const T* io, int d, int r0, int W, int m, 
   return val;
 }
 
+// Stores coordinates 256 u + tid (u < nu) of an entry that a workgroup of
+// 256 threads holds (vals[u]) to row `row` of the cache: as T (fmt 0), or as
+// the 576-byte FP8 + BF16 entry (fmt 1, c = 512): scale = max |v[0:448]| /
+// 448 formed in float32 (1 for an all-zero part), codes e4m3(v / scale),
+// then the last 64 coordinates as bf16.  Called by every thread; s_red holds
+// four floats.
+template <typename T>
+CSA_DEV void store_entry(const float* vals, int nu, int c, int fmt, void* cache, float* scales, size_t row,
+                         float* s_red) {
+  const int tid = threadIdx.x;
+  if (!fmt) {
+    for (int u = 0; u < nu; ++u) {
+      const int r = 256 * u + tid;
+      if (r < c) st(reinterpret_cast<T*>(cache), row * c + r, vals[u]);
+    }
+    return;
+  }
+  float am = 0.f;
+  for (int u = 0; u < nu; ++u)
+    if (256 * u + tid < kF8Dims) am = fmaxf(am, fabsf(vals[u]));
+  am = wave_max(am);
+  __syncthreads();  // s_red is free (earlier reductions' readers are done)
+  if ((tid & 63) == 0) s_red[tid >> 6] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  float scale = am / 448.0f;
+  if (!(scale > 0.f)) scale = 1.f;
+  uint8_t* o = reinterpret_cast<uint8_t*>(cache) + row * kF8RowB;
+  for (int u = 0; u < nu; ++u) {
+    const int r = 256 * u + tid;
+    if (r < kF8Dims)
+      o[r] = f32_to_e4m3(vals[u] / scale);
+    else if (r < c)
+      *reinterpret_cast<uint16_t*>(o + kF8Dims + 2 * (r - kF8Dims)) = f32_to_bf16(vals[u]);
+  }
+  if (tid == 0) scales[row] = scale;
+}
+
 // One wavefront prepares one vector of length c (64..512, a multiple of 64)
 // for the core attention: RMSNorm with scale g, v * g / sqrt(mean(v^2) +
 // eps), then the rotary pairs of its last rope_dims coordinates at position

@@ -871,7 +871,8 @@ static int resident_for(int HT) {
 static int scan_format(int idx_dtype) { return idx_dtype == MXFP4 ? 2 : (idx_dtype == E4M3 ? 1 : 0); }
 
 bool index_fold_fusable(const IndexArgs& a, const FoldArgs& f, bool split) {
-  if (!split || !index_mfma_supported(a) || a.Tq != 1 || f.B != a.B || f.dtype != BF16 || f.idx_dtype != a.idx_dtype ||
+  if (!split || !index_mfma_supported(a) || a.Tq != 1 || f.B != a.B || f.dtype != BF16 || f.kv_fmt ||
+      f.idx_dtype != a.idx_dtype ||
       f.d_I != kD || a.n_add != 0)
     return false;
   const int fmt = scan_format(a.idx_dtype);

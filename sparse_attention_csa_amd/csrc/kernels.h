@@ -34,7 +34,10 @@ class ProfScope {
 
 // storage formats (the csa_dtype codes); MXFP4 vectors are packed E2M1
 // pairs with one E8M0 scale byte per 32 values
-enum Dt { F32 = 0, BF16 = 1, E4M3 = 2, MXFP4 = 3 };
+enum Dt { F32 = 0, BF16 = 1, E4M3 = 2, MXFP4 = 3, FP8BF16 = 4 };
+// the 576-byte main entry: 448 e4m3 codes (one float32 scale per entry),
+// then 64 bf16
+constexpr int kF8Dims = 448, kF8RowB = 576;
 
 // Host-side values that depend on the device (occupancy, LDS attributes set
 // on a kernel) are cached per device id, below this bound.
@@ -102,6 +105,9 @@ struct FoldArgs {
   int H;
   const void* q;
   void* q_prep;
+  // main entries stored as FP8BF16 (576 bytes + a float32 scale in kv_scale)
+  int kv_fmt;
+  float* kv_scale;
 };
 hipError_t launch_fold_append(const FoldArgs& a, hipStream_t s);
 
@@ -210,6 +216,10 @@ struct AttendArgs {
   // the query position (pairs (2i, 2i+1), angle -t * derot_freq[i]); null: off
   const double* derot_freq;
   int rope_dims;
+  // compressed rows stored as FP8BF16 (576 bytes, scale in kv_scale); the
+  // window rows and q stay in dtype
+  int kv_fmt;
+  const float* kv_scale;
 };
 // split_rows > 0: rows per split fixed (batch-invariant launch plan), else
 // chosen for the batch

@@ -17,12 +17,18 @@ from . import _lib as L
 _KV = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
+def act_kind(kvk):
+    """Storage of the activations (queries, window rows, token streams,
+    outputs): bf16 under the 576-byte FP8 + BF16 cache entry."""
+    return "bf16" if kvk == "fp8bf16" else kvk
+
+
 def dev(arr, kind, device="cuda"):
     """Upload a host array in its storage format."""
     a = np.ascontiguousarray(arr)
     if kind == "bf16":
         return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
-    if kind in ("e4m3", "mxfp4", "u8"):
+    if kind in ("e4m3", "mxfp4", "u8", "fp8bf16"):
         return torch.from_numpy(a.view(np.uint8)).to(device)
     if kind == "f32":
         return torch.from_numpy(a.astype(np.float32)).to(device)
@@ -40,7 +46,8 @@ def to_host_bits(t):
     return t.cpu().numpy()
 
 
-DTYPE_CODE = {"f32": L.CSA_F32, "bf16": L.CSA_BF16, "e4m3": L.CSA_E4M3, "mxfp4": L.CSA_MXFP4}
+DTYPE_CODE = {"f32": L.CSA_F32, "bf16": L.CSA_BF16, "e4m3": L.CSA_E4M3, "mxfp4": L.CSA_MXFP4,
+              "fp8bf16": L.CSA_FP8BF16}
 SCALE_KIND = {"e4m3": "f32", "mxfp4": "u8"}  # storage of the scales of a scaled format
 
 
@@ -79,8 +86,13 @@ class _State:
         c, m = g["c"], g["m"]
         self.R = 3 * m if g["overlap"] else 2 * m
         self.S = 4 if g["overlap"] else 2
-        tdt = _KV[kvk]
-        self.kv_cache = torch.zeros((B, E_cap, c), dtype=tdt, device=device)
+        tdt = _KV[act_kind(kvk)]
+        self.kv_scale = None
+        if kvk == "fp8bf16":  # 576-byte entries and their scales
+            self.kv_cache = torch.zeros((B, E_cap, 576), dtype=torch.uint8, device=device)
+            self.kv_scale = torch.ones((B, E_cap), dtype=torch.float32, device=device)
+        else:
+            self.kv_cache = torch.zeros((B, E_cap, c), dtype=tdt, device=device)
         self.n_entries = torch.zeros(B, dtype=torch.int32, device=device)
         self.win_ring = torch.zeros((B, g["n_win"], c), dtype=tdt, device=device)
         self.tail = torch.zeros((B, self.S, self.R, c), dtype=tdt, device=device)
@@ -114,7 +126,7 @@ class _State:
         s.B, s.E_cap = self.B, self.E_cap
         for name in ("kv_cache", "idx_cache", "idx_scale", "n_entries", "win_ring", "tail",
                      "idx_tail", "bias_a", "bias_b", "ibias_a", "ibias_b", "sink", "q_norm_w",
-                     "kv_norm_w", "rope_inv_freq"):
+                     "kv_norm_w", "rope_inv_freq", "kv_scale"):
             setattr(s, name, L.ptr(getattr(self, name)))
         return s
 
@@ -130,6 +142,9 @@ class DecodeSession:
         st = _State(g, B, E_cap, device)
         self.state = st
         st.kv_cache.copy_(dev(g["kv_cache"], kvk, device))
+        if st.kv_scale is not None:
+            st.kv_scale.copy_(dev(g["kv_scale"], "f32", device))
+        kvk = act_kind(kvk)  # the state's rows below are activations
         st.n_entries.copy_(dev(g["n_entries"], "i32", device))
         pos = np.asarray(g["pos"], np.int64)
         # window ring: positions t-(n_win-1) .. t-1
@@ -177,7 +192,7 @@ def decode_io(g, device="cuda"):
     sequence) of workload ``g``: a dict of device tensors and the DecodeIO
     structure pointing at them."""
     B, c, H = g["B"], g["c"], g["H"]
-    kvk = g["kv_dtype"]
+    kvk = act_kind(g["kv_dtype"])
     streams = ("ca", "za", "cb", "zb") if g["overlap"] else ("ca", "za")
     io = {}
     io["pos"] = dev(np.asarray(g["pos"], np.int64), "i64", device)
@@ -213,6 +228,9 @@ class PrefillSession:
         st = _State(g, B, E_cap, device)
         self.state = st
         st.kv_cache.copy_(dev(g["kv_cache"], kvk, device))
+        if st.kv_scale is not None:
+            st.kv_scale.copy_(dev(g["kv_scale"], "f32", device))
+        kvk = act_kind(kvk)
         st.n_entries.copy_(dev(g["n_entries"], "i32", device))
         pos0 = int(g["pos0"])
         if g["overlap"] and pos0 > 0:

@@ -36,6 +36,20 @@ def e4m3_codes_of(rows):
     return codes.view(torch.uint8).numpy(), scale
 
 
+def fp8bf16_codes_of(rows):
+    """(576-byte rows, float32 scales) of float64 rows that already are
+    FP8 + BF16 entries (the first 448 values e4m3 times one scale, the last
+    64 bf16 values): a pure re-encoding."""
+    from oracle.formats import FP8_DIMS
+    rows = np.asarray(rows, np.float64)
+    codes, scale = e4m3_codes_of(rows[..., :FP8_DIMS])
+    tail = f64_to_bf16_bits(rows[..., FP8_DIMS:]).astype(np.uint16)
+    out = np.empty(rows.shape[:-1] + (576,), np.uint8)
+    out[..., :FP8_DIMS] = codes
+    out[..., FP8_DIMS:] = tail.view(np.uint8).reshape(rows.shape[:-1] + (128,))
+    return out, scale
+
+
 def mxfp4_codes_of(rows):
     """(packed codes, E8M0 scales) of float64 rows that already are MXFP4
     values (E2M1 values times a power-of-two scale per block of 32, as the
@@ -73,6 +87,7 @@ def decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv=(), extra_idx=
     E_cap = max(pre["E_cap"], n_have + 1)
     g = {k: pre[k] for k in ("kind", "H", "c", "m", "n_win", "overlap", "vis", "scale",
                              "kv_dtype", "k", "idx_dtype", "sink", "bias_a", "bias_b")}
+    act = "bf16" if kvk == "fp8bf16" else kvk  # activations' storage
     g["score_dtype"] = pre.get("score_dtype", "f32")
     for k_ in ("norm_rope", "q_norm_w", "kv_norm_w", "rope_inv_freq", "rope_dims", "norm_eps"):
         if k_ in pre:
@@ -80,9 +95,15 @@ def decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv=(), extra_idx=
     g.update(B=1, E_cap=E_cap)
     g["pos"] = np.array([t], dtype=np.int64)
     g["n_entries"] = np.array([n_have], dtype=np.int32)
-    kv = np.zeros((1, E_cap, c), dtype=pre["kv_cache"].dtype)
+    kv = np.zeros((1, E_cap, pre["kv_cache"].shape[-1]), dtype=pre["kv_cache"].dtype)
     kv[0, :n_old] = pre["kv_cache"][b, :n_old]
-    if kv_rows:
+    if kvk == "fp8bf16":
+        ks = np.ones((1, E_cap), np.float32)
+        ks[0, :n_old] = pre["kv_scale"][b, :n_old]
+        if kv_rows:
+            kv[0, n_old:n_have], ks[0, n_old:n_have] = fp8bf16_codes_of(np.array(kv_rows))
+        g["kv_scale"] = ks
+    elif kv_rows:
         kv[0, n_old:n_have] = _bits(np.array(kv_rows), kvk)
     g["kv_cache"] = kv
     tail_len = 2 * m if pre["overlap"] else m
@@ -101,10 +122,10 @@ def decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv=(), extra_idx=
         from oracle import position as P
         from oracle.csa import store_as
         from oracle.formats import Stored
-        raw = Stored(g["win_hist"][0], kvk).all()
+        raw = Stored(g["win_hist"][0], act).all()
         hp = np.arange(t - (n_win - 1), t)
-        prep = store_as(P.prepare(raw, pre["kv_norm_w"], pre["norm_eps"], hp, pre["rope_inv_freq"]), kvk)
-        g["win_hist"] = _bits(prep, kvk)[None]
+        prep = store_as(P.prepare(raw, pre["kv_norm_w"], pre["norm_eps"], hp, pre["rope_inv_freq"]), act)
+        g["win_hist"] = _bits(prep, act)[None]
     g["x_new"] = pre["win"][sl, w0 + n_win - 1]
     g["q"] = pre["q"][sl, hi]
     if pre["kind"] == "csa":

@@ -315,6 +315,38 @@ def check_selection(ids, cnt, k, ref, err, bounds=None, score_dtype="f32"):
     return ok, int(not np.array_equal(gpu, ref["sel"])), msg
 
 
+def gpu_entries(state, b, sl, kvk):
+    """Main-cache rows sl of sequence b of a device state, as float64 (the
+    576-byte FP8 + BF16 rows decoded with their scales)."""
+    from oracle.formats import Stored
+    import torch
+    if kvk == "fp8bf16":
+        codes = state.kv_cache[b, sl].cpu().numpy()
+        sc = state.kv_scale[b, sl].cpu().numpy()
+        return Stored(codes, "fp8bf16", sc).all()
+    return state.kv_cache[b, sl].detach().to(torch.float64).cpu().numpy()
+
+
+def assert_entry_close(got, ref, kvk, what):
+    """Produced main entries: with the FP8 + BF16 entry, the e4m3 part
+    within one quantum of the oracle's value everywhere (the float32 value
+    may sit on a rounding tie, and the scale may differ by float32 rounding)
+    with at most 2 % of the codes flipped, and the bf16 part within the bf16
+    tolerance; other formats: assert_close."""
+    got = np.atleast_2d(np.asarray(got, np.float64))
+    ref = np.atleast_2d(np.asarray(ref, np.float64))
+    if kvk != "fp8bf16":
+        return assert_close(got, ref, kvk, what)
+    from oracle.formats import FP8_DIMS
+    g8, r8 = got[:, :FP8_DIMS], ref[:, :FP8_DIMS]
+    scale = np.abs(r8).max(axis=1, keepdims=True) / 448.0
+    step = np.abs(r8) / 8 + scale * 2.0 ** -9
+    assert np.all(np.abs(g8 - r8) <= step * 1.0001 + 1e-30), f"{what}: e4m3 part beyond one quantum"
+    flips = np.abs(g8 - r8) > 1e-5 * np.maximum(np.abs(r8).max(axis=1, keepdims=True), 1e-30)
+    assert flips.mean() <= 0.02, f"{what}: {flips.mean():.3f} e4m3 codes differ"
+    return assert_close(got[:, FP8_DIMS:], ref[:, FP8_DIMS:], "bf16", what + " (bf16 part)")
+
+
 def rel_err_rows(gpu, ref):
     """Per-row relative errors (rows = last axis vectors)."""
     g = np.asarray(gpu, np.float64).reshape(-1, np.shape(gpu)[-1])

@@ -12,9 +12,9 @@ import torch
 import workloads
 from oracle import layer as OL
 from oracle.formats import Stored
-from tests.compare import (ambiguous_e4m3_keys, ambiguous_mxfp4_keys, assert_close, check_selection, decode_err,
-                           mxfp4_alternatives, prefill_err, score_bounds, score_error_bound, topk_check,
-                           topk_check_bounds)
+from tests.compare import (ambiguous_e4m3_keys, ambiguous_mxfp4_keys, assert_close, assert_entry_close,
+                           check_selection, decode_err, gpu_entries, mxfp4_alternatives, prefill_err, score_bounds,
+                           score_error_bound, topk_check, topk_check_bounds)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +29,7 @@ def _check_decode(g, sess, label):
     out, lse = f64(sess.io["out"]), f64(sess.io["lse"])
     n_ent = sess.state.n_entries.cpu().numpy()
     kvk = g["kv_dtype"]
+    act = "bf16" if kvk == "fp8bf16" else kvk  # outputs are activations
     swaps_total = 0
     for b in range(g["B"]):
         print(f"[{label}] seq {b}", flush=True)
@@ -36,8 +37,8 @@ def _check_decode(g, sess, label):
         e0 = int(g["n_entries"][b])
         assert n_ent[b] == e0 + len(ref["folded_kv"]), "n_entries not advanced by the fold"
         if ref["folded_kv"]:
-            gk = f64(sess.state.kv_cache[b, e0])
-            assert_close(gk[None], np.array(ref["folded_kv"][:1]), kvk, f"{label} folded kv b={b}")
+            gk = gpu_entries(sess.state, b, slice(e0, e0 + 1), kvk)
+            assert_entry_close(gk, np.array(ref["folded_kv"][:1]), kvk, f"{label} folded kv b={b}")
         if g["kind"] == "csa":
             idk = g["idx_dtype"]
             if ref["folded_idx"]:
@@ -58,7 +59,7 @@ def _check_decode(g, sess, label):
             swaps_total += swaps
             if swaps:
                 ref = OL.decode_step(g, b, selected=ids[:cnt])
-        assert_close(out[b], ref["o"], kvk, f"{label} out b={b}")
+        assert_close(out[b], ref["o"], act, f"{label} out b={b}")
         assert np.abs(lse[b] - ref["lse"]).max() < 1e-3, f"{label} lse b={b}"
     _check_rings(g, sess, label)
     return swaps_total
@@ -77,9 +78,10 @@ def _check_rings(g, sess, label):
             # the ring receives the row prepared at t (normalised, rotated)
             from oracle import position as P
             from oracle.csa import store_as
-            raw = Stored(g["x_new"][b][None], g["kv_dtype"]).all()[0]
-            want = store_as(P.prepare(raw, g["kv_norm_w"], g["norm_eps"], t, g["rope_inv_freq"]), g["kv_dtype"])
-            assert_close(f64(st.win_ring[b, t % g["n_win"]])[None], want[None], g["kv_dtype"],
+            act = "bf16" if g["kv_dtype"] == "fp8bf16" else g["kv_dtype"]
+            raw = Stored(g["x_new"][b][None], act).all()[0]
+            want = store_as(P.prepare(raw, g["kv_norm_w"], g["norm_eps"], t, g["rope_inv_freq"]), act)
+            assert_close(f64(st.win_ring[b, t % g["n_win"]])[None], want[None], act,
                          f"{label} prepared window row b={b}")
         else:
             assert np.array_equal(as_u16(st.win_ring[b, t % g["n_win"]]), g["x_new"][b]), f"{label} window ring b={b}"
@@ -242,10 +244,11 @@ def _check_prefill(g, sess, label, queries=None):
     torch.cuda.synchronize()
     out, lse = f64(sess.io["out"]), f64(sess.io["lse"])
     kvk = g["kv_dtype"]
+    act = "bf16" if kvk == "fp8bf16" else kvk
     kv_new, idx_new = OL.prefill_entries(g, 0)
     E0, n_new = int(g["n_entries"][0]), len(kv_new)
     assert int(sess.state.n_entries[0].item()) == E0 + n_new
-    assert_close(f64(sess.state.kv_cache[0, E0:E0 + n_new]), kv_new, kvk, f"{label} entries")
+    assert_entry_close(gpu_entries(sess.state, 0, slice(E0, E0 + n_new), kvk), kv_new, kvk, f"{label} entries")
     if g["kind"] == "csa":
         assert_close(f64(sess.state.idx_cache[0, E0:E0 + n_new]), idx_new, g["idx_dtype"],
                      f"{label} keys")
@@ -260,7 +263,7 @@ def _check_prefill(g, sess, label, queries=None):
             assert ok, f"{label} q{i}: {msg}"
             if swaps:
                 ref = OL.prefill_query(g, 0, i, kv_new, idx_new, selected=ids[i, :cnt[i]])
-        assert_close(out[0, i], ref["o"], kvk, f"{label} out q{i}")
+        assert_close(out[0, i], ref["o"], act, f"{label} out q{i}")
         assert np.abs(lse[0, i] - ref["lse"]).max() < 1e-3
 
 

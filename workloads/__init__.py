@@ -13,5 +13,6 @@ from .gen import (  # noqa: F401
     pro_csa_decode,
     flash_prefill,
     with_norm_rope,
+    with_fp8bf16_cache,
     CONFIG_NAMES,
 )

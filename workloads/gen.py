@@ -371,3 +371,16 @@ def with_norm_rope(g, seed=7, rope_dims=64, base=10000.0, eps=1e-6):
     out["rope_dims"] = rope_dims
     out["norm_eps"] = eps
     return out
+
+
+def with_fp8bf16_cache(g):
+    """A copy of layer case g whose main compressed cache is stored as the
+    576-byte FP8 + BF16 entry (the first 448 coordinates e4m3 with one
+    float32 scale per entry, the last 64 bf16), re-encoding g's bf16 entries;
+    activations stay bf16."""
+    out = dict(g)
+    kv = np.asarray(g["kv_cache"])
+    vals = (kv.astype(np.uint32) << 16).view(np.float32)
+    out["kv_cache"], out["kv_scale"] = fp8bf16_rows(vals)
+    out["kv_dtype"] = "fp8bf16"
+    return out
