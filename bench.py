@@ -15,7 +15,7 @@ steps, outside the timed events) and cycles through --rotate independent copies
 of the state so that the working set exceeds the 256 MiB MALL.
 
 Prints one JSON line.  Other workloads: --workload flash_csa_128k |
-flash_hca_1m | pro_csa_1m | pro_csa_1m_mxfp4 | prefill.
+flash_hca_1m | pro_csa_1m | pro_csa_1m_mxfp4 | decode_1m_paged | prefill.
 """
 
 import argparse
@@ -48,6 +48,11 @@ def build_cases(name):
     if name == "pro_csa_1m_mxfp4":
         # the pages' FP4 indexer path: MXFP4 queries and keys, bf16 scores
         return [("pro_csa_1m_mxfp4", workloads.pro_csa_decode(idx_dtype="mxfp4", score_dtype="bf16"))]
+    if name == "decode_1m_paged":
+        # the default step with the compressed caches in 128-token pages
+        # (32 CSA entries, one HCA entry per page), pages in random order
+        return [("pro_csa_1m_paged", workloads.with_pages(workloads.pro_csa_decode(), 32, seed=31)),
+                ("flash_hca_1m_paged", workloads.with_pages(workloads.flash_hca_decode(), 1, seed=32))]
     if name == "prefill":
         a, h = workloads.flash_prefill()
         return [("prefill_csa", a), ("prefill_hca", h)]
@@ -245,6 +250,9 @@ def measure(cases, steps, warmup, rotate, prefill, profile=True, use_graph=False
     for name, g in cases:
         S = PrefillSession if prefill else DecodeSession
         sessions.append((name, g, [S(g) for _ in range(rot)]))
+    for _, _, ss in sessions:
+        for sess in ss:
+            sess.state.auto_gather = False  # (paged caches: no host-side views needed)
     saved = [[s.state.n_entries.clone() for s in ss] for _, _, ss in sessions]
     torch.cuda.synchronize()
     log(f"uploaded {rot} state copies of {'+'.join(n for n, _ in cases)} in {time.time() - t0:.1f} s")
@@ -438,6 +446,7 @@ def main():
     if args.workload == "decode_1m" and not args.no_extra:
         for wl, steps, warm in (("flash_csa_128k", args.steps, args.warmup),
                                 ("pro_csa_1m_mxfp4", args.steps, args.warmup),
+                                ("decode_1m_paged", args.steps, args.warmup),
                                 ("prefill", max(3, min(args.steps, 5)), 1)):
             t1 = time.time()
             c2 = build_cases(wl)

@@ -84,7 +84,8 @@ const char* csa_last_error(void);
  * csa_layer_desc.split_rows; 3 added CSA_MXFP4 with untyped scale pointers,
  * csa_layer_desc.score_bf16, the score_bf16 argument of csa_index_topk, the
  * normalisation / rotary fields of csa_layer_desc and csa_layer_state, and
- * the FP8BF16 main entry with csa_layer_state.kv_scale). */
+ * the FP8BF16 main entry with csa_layer_state.kv_scale; 4 added the paged
+ * cache, csa_layer_state.block_table and page_entries). */
 int csa_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -286,6 +287,23 @@ typedef struct {
                                /* caller's scaling, e.g. base^(-2i/rope_dims)) */
                                /* (the three only read when norm_rope)         */
   float* kv_scale;             /* [B][E_cap] per-entry scales (FP8BF16)        */
+  /* Paged compressed cache ([book] ch. 13 "Aligning original-token blocks":
+   * an allocation unit of original tokens shared by the layers, e.g. 128
+   * tokens = 32 CSA entries (m = 4) = 1 HCA entry (m = 128), so one block
+   * table serves a CSA and an HCA layer).  NULL: the per-sequence layout
+   * above.  Else kv_cache, kv_scale, idx_cache and idx_scale are pools of
+   * pages of page_entries rows each (the row layouts above), shared by the
+   * sequences, and entry e of sequence b lives in row
+   * block_table[b][e / page_entries] * page_entries + e % page_entries.
+   * block_table is int32 [B][E_cap / page_entries] on the device; the pages
+   * a sequence's entries reach (the visible ones, and those a call
+   * appends) must hold ids of pages inside the pools, each page owned by
+   * one sequence (the library does not read the pools' sizes).  Entries
+   * of a page are appended in order, so a page is allocated before the
+   * step or chunk that writes its first entry.  Window ring and tails
+   * stay per sequence (the bounded state cache). */
+  const int32_t* block_table;
+  int page_entries;            /* power of two, divides E_cap (block_table)   */
 } csa_layer_state;
 
 /* One decode step: one new token per sequence at position pos[b]. */
@@ -392,6 +410,16 @@ int csa_profile_collect(csa_kernel_time* out, int max_entries);
  * give up at once, so tests can check the fallback against the oracle.
  * Process-wide; not synchronised with calls in flight on other threads. */
 int csa_test_set_fused_wait_polls(int polls);
+
+/* Test hook (diagnostics, not part of the method).  Whether a decode step
+ * may fold its pending block inside the scoring kernel (CSA) or the dense
+ * attention (HCA) rather than in the separate fold kernel (1, the default)
+ * or never (0).  The two paths add the new entry's terms in different
+ * orders, so they agree within float32 rounding, not bit for bit; a test
+ * that compares two cache layouts of one step bit for bit turns fusion off
+ * (a paged cache never fuses).  Returns the previous setting.
+ * Process-wide; not synchronised with calls in flight on other threads. */
+int csa_test_set_fold_fusion(int on);
 
 #ifdef __cplusplus
 }

@@ -24,6 +24,7 @@ EXPORTS = [
     "csa_index_topk", "csa_attend_workspace", "csa_attend", "hca_attend",
     "hybrid_layer_workspace", "hybrid_layer_decode", "hybrid_layer_prefill",
     "csa_profile_enable", "csa_profile_collect", "csa_test_set_fused_wait_polls",
+    "csa_test_set_fold_fusion",
     "hybrid_layer_noalloc_scratch_bytes", "hybrid_layer_decode_noalloc",
 ]
 
@@ -49,7 +50,8 @@ class LayerState(C.Structure):
                 ("win_ring", C.c_void_p), ("tail", C.c_void_p), ("idx_tail", C.c_void_p),
                 ("bias_a", C.c_void_p), ("bias_b", C.c_void_p), ("ibias_a", C.c_void_p),
                 ("ibias_b", C.c_void_p), ("sink", C.c_void_p), ("q_norm_w", C.c_void_p),
-                ("kv_norm_w", C.c_void_p), ("rope_inv_freq", C.c_void_p), ("kv_scale", C.c_void_p)]
+                ("kv_norm_w", C.c_void_p), ("rope_inv_freq", C.c_void_p), ("kv_scale", C.c_void_p),
+                ("block_table", C.c_void_p), ("page_entries", C.c_int)]
 
 
 class DecodeIO(C.Structure):
@@ -97,6 +99,7 @@ def _declare(lib):
         "csa_profile_enable": (I, [I]),
         "csa_profile_collect": (I, [C.POINTER(KernelTime), I]),
         "csa_test_set_fused_wait_polls": (I, [I]),
+        "csa_test_set_fold_fusion": (I, [I]),
         "hybrid_layer_noalloc_scratch_bytes": (SZ, []),
         "hybrid_layer_decode_noalloc": (I, [C.POINTER(LayerDesc), C.POINTER(LayerState),
                                             C.POINTER(DecodeIO), P]),
@@ -267,6 +270,12 @@ def set_fused_wait_polls(polls):
     """Test hook: the fused top-k's poll budget (negative = default); returns
     the previous value."""
     return lib().csa_test_set_fused_wait_polls(int(polls))
+
+
+def set_fold_fusion(on):
+    """Test hook: whether decode steps may fold inside the scoring kernel or
+    the dense attention; returns the previous setting."""
+    return lib().csa_test_set_fold_fusion(1 if on else 0)
 
 
 def profile_enable(on=True):

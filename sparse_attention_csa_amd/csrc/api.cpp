@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -89,9 +90,12 @@ extern "C" {
 
 const char* csa_last_error(void) { return g_err.c_str(); }
 
-int csa_abi_version(void) { return 3; }
+int csa_abi_version(void) { return 4; }
 
 int csa_test_set_fused_wait_polls(int polls) { return csa::set_fused_wait_polls(polls); }
+
+static std::atomic<int> g_fold_fusion{1};
+int csa_test_set_fold_fusion(int on) { return g_fold_fusion.exchange(on ? 1 : 0, std::memory_order_relaxed); }
 
 // ------------------------------------------------------------------ a1
 csa_status csa_compress(csa_dtype dtype, const void* content_a, const void* logits_a,
@@ -310,7 +314,24 @@ static csa_status check_state(const csa_layer_desc* d, const csa_layer_state* s)
     REQ_PTR(s->q_norm_w); REQ_PTR(s->kv_norm_w); REQ_PTR(s->rope_inv_freq);
   }
   REQUIRE(d->kv_dtype != CSA_FP8BF16 || s->kv_scale != nullptr, CSA_ERR_ARG, "FP8BF16 entries need kv_scale");
+  if (s->block_table) {
+    REQ_ALIGNED(s->block_table);
+    REQUIRE(is_pow2_in(s->page_entries, 1, 1 << 20), CSA_ERR_ARG,
+            "page_entries must be a power of two (got %d)", s->page_entries);
+    REQUIRE(s->E_cap % s->page_entries == 0, CSA_ERR_ARG, "page_entries (%d) must divide E_cap (%d)",
+            s->page_entries, s->E_cap);
+  }
   return CSA_OK;
+}
+
+// the rows of the compressed caches: paged (block_table) or per sequence
+static csa::PageMap page_map_of(const csa_layer_state* s) {
+  csa::PageMap p{};
+  p.table = s->block_table;
+  p.shift = 0;
+  if (s->block_table)
+    while ((1 << p.shift) < s->page_entries) ++p.shift;
+  return p;
 }
 
 // the activations' dtype (queries, window rows, streams, outputs): bf16
@@ -398,6 +419,7 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
   f.pos = io->pos; f.n_entries = s->n_entries; f.streams = io->streams; f.idx_streams = io->idx_streams;
   f.x_new = io->x_new; f.tail = s->tail; f.idx_tail = s->idx_tail; f.win_ring = s->win_ring;
   f.kv_cache = s->kv_cache; f.idx_cache = s->idx_cache; f.idx_scale = s->idx_scale; f.E_cap = s->E_cap;
+  f.pg = page_map_of(s);
   f.bias_a = s->bias_a; f.bias_b = s->bias_b; f.ibias_a = s->ibias_a; f.ibias_b = s->ibias_b;
   f.nr = norm_rope_of(d, s);
   f.H = d->H; f.q = io->q; f.q_prep = q_prep;
@@ -409,9 +431,11 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
     x.q_pos = io->pos; x.n_entries = s->n_entries; x.n_add = 0;
     x.B = B; x.Tq = 1; x.H_I = d->H_I; x.d_I = d->d_I; x.E_cap = s->E_cap; x.m = d->m; x.k = d->k;
     x.vis = d->vis; x.scores = nullptr; x.topk_idx = io->topk_idx; x.topk_cnt = io->topk_cnt; x.ws = w;
+    x.pg = page_map_of(s);
   }
   csa::AttendArgs a{};
   a.dtype = act_dtype(d); a.q = io->q; a.kv = s->kv_cache; a.E_cap = s->E_cap;
+  a.pg = page_map_of(s);
   a.kv_fmt = d->kv_dtype == CSA_FP8BF16; a.kv_scale = s->kv_scale;
   a.win = s->win_ring; a.W_cap = d->n_win; a.win_pos0 = nullptr; a.win_pos0_const = 0; a.n_win = d->n_win;
   a.sink = s->sink; a.q_pos = io->pos; a.scale = d->scale;
@@ -429,8 +453,9 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
   // the fold runs first, unless the scoring kernel (CSA) or the attention
   // (HCA) does it (not with norm_rope: the fold kernel also prepares the
   // queries and normalises whole entries)
-  const bool fold_in_scan = is_csa && !d->norm_rope && csa::index_topk_fuses_fold(x, f);
-  const bool fold_in_attend = !is_csa && !d->norm_rope && csa::attend_fuses_fold(a, f);
+  const bool fuse = g_fold_fusion.load(std::memory_order_relaxed) != 0;
+  const bool fold_in_scan = fuse && is_csa && !d->norm_rope && csa::index_topk_fuses_fold(x, f);
+  const bool fold_in_attend = fuse && !is_csa && !d->norm_rope && csa::attend_fuses_fold(a, f);
   hipError_t e = hipSuccess;
   if (!fold_in_scan && !fold_in_attend) {
     e = csa::launch_fold_append(f, hs);
@@ -502,6 +527,7 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
     c.logit_width = width; c.score_w = nullptr; c.bias_a = ba; c.bias_b = overlap ? bb : nullptr;
     c.B = B; c.T = T; c.c = width; c.m = m;
     c.out = out; c.out_dtype = out_dtype; c.out_scale = out_scale; c.E_cap = s->E_cap; c.first = first;
+    c.pg = page_map_of(s);
     return csa::launch_compress(c, hs);
   };
   hipError_t e = compress(io->streams, d->c, s->tail, s->kv_cache, d->kv_dtype, s->kv_scale, s->bias_a,
@@ -521,6 +547,7 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
     x.q_pos = nullptr; x.q_pos0 = io->pos0; x.n_entries = s->n_entries; x.n_add = n_new;
     x.B = B; x.Tq = T; x.H_I = d->H_I; x.d_I = d->d_I; x.E_cap = s->E_cap; x.m = m; x.k = d->k;
     x.vis = d->vis; x.scores = nullptr; x.topk_idx = io->topk_idx; x.topk_cnt = io->topk_cnt; x.ws = w;
+    x.pg = page_map_of(s);
     e = csa::launch_index_topk(x, hs);
     if (e != hipSuccess) return from_hip(e, "hybrid_layer_prefill/index");
     w += align_up(csa::index_topk_ws_bytes(B, T, s->E_cap, d->k));
@@ -530,6 +557,7 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
   }
   a.dtype = act_dtype(d); a.q = io->q; a.kv = s->kv_cache; a.E_cap = s->E_cap;
   a.kv_fmt = d->kv_dtype == CSA_FP8BF16; a.kv_scale = s->kv_scale;
+  a.pg = page_map_of(s);
   a.win = io->win; a.W_cap = d->n_win - 1 + T; a.win_pos0 = nullptr;
   a.win_pos0_const = io->pos0 - (d->n_win - 1); a.n_win = d->n_win;
   a.sink = s->sink; a.q_pos = nullptr; a.q_pos0 = io->pos0; a.scale = d->scale;

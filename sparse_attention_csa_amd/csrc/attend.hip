@@ -53,9 +53,11 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
     const int h = i / c;
     q_s[i] = (h0 + h < H) ? ld(q, i) * a.scale : 0.f;
   }
-  const T* kv = reinterpret_cast<const T*>(a.kv) + (size_t)b * a.E_cap * c;
-  const uint8_t* kv8 = reinterpret_cast<const uint8_t*>(a.kv) + (size_t)b * a.E_cap * kF8RowB;  // (kv_fmt)
-  const float* ksc = a.kv_scale ? a.kv_scale + (size_t)b * a.E_cap : nullptr;
+  // compressed rows by their cache row (page_row: paged or per sequence)
+  __shared__ size_t s_crow[kTile];
+  const T* kv = reinterpret_cast<const T*>(a.kv);
+  const uint8_t* kv8 = reinterpret_cast<const uint8_t*>(a.kv);  // (kv_fmt)
+  const float* ksc = a.kv_scale;
   const T* win = reinterpret_cast<const T*>(a.win) + (size_t)b * a.W_cap * c;
   const int32_t* ids = a.dense ? nullptr : a.topk_idx + (size_t)row * a.k;
 
@@ -73,9 +75,10 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
     if (tid < kTile) {
       const int64_t j = r0 + tid;
       int okr = j < n_rows;
-      if (okr && j < n_c && !a.dense) {
-        const int64_t e = ids[j];
+      if (okr && j < n_c) {
+        const int64_t e = a.dense ? j : ids[j];
         okr = e >= 0 && e < a.E_cap;
+        if (okr) s_crow[tid] = page_row(a.pg, b, e, a.E_cap);
       }
       valid_s[tid] = okr;
     }
@@ -86,7 +89,7 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
       float v = 0.f;
       if (valid_s[r]) {
         if (j < n_c) {
-          const int64_t e = a.dense ? j : ids[j];
+          const size_t e = s_crow[r];
           if (a.kv_fmt) {  // the 576-byte entry: scaled e4m3 codes, then bf16
             const uint8_t* er = kv8 + (size_t)e * kF8RowB;
             v = d < kF8Dims ? e4m3_to_f32(er[d]) * ksc[e]
@@ -184,6 +187,7 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
 bool attend_mfma_shape_ok(int H, int c);
 size_t attend_mfma_ws_bytes(int BT, int H, int rows_max, int split_rows);
 hipError_t launch_attend_mfma(const AttendArgs& a, int rows_max, hipStream_t s);
+bool attend_mfma_pages_fit(const AttendArgs& a, int rows_max);
 bool attend_rows_shape_ok(int H, int c);
 void attend_rows_plan(int BT, int H, int rows_max, int split_rows, int* n_split, int* rows_per_split);
 hipError_t launch_attend_rows(const AttendArgs& a, int rows_max, hipStream_t s);
@@ -217,7 +221,10 @@ size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max, int split_rows
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   // (576-byte entries: the generic kernel decodes them row by row)
-  if (a.dtype == BF16 && !a.kv_fmt && a.dense && attend_mfma_shape_ok(a.H, a.c))
+  // (a paged cache whose split spans more pages than the dense kernel's
+  // table holds: the generic kernel)
+  if (a.dtype == BF16 && !a.kv_fmt && a.dense && attend_mfma_shape_ok(a.H, a.c) &&
+      attend_mfma_pages_fit(a, a.E_cap + a.n_win))
     return launch_attend_mfma(a, a.E_cap + a.n_win, s);
   if (a.dtype == BF16 && !a.kv_fmt && !a.dense && attend_rows_shape_ok(a.H, a.c))
     return launch_attend_rows(a, a.k + a.n_win, s);

@@ -62,18 +62,21 @@ constexpr int kRowsPerWave = kTN / 4;  // DMA instructions per wave and tile
 constexpr int kFoldS = 16;             // fold slice: sources per thread (at most)
 constexpr int kFoldRowsLess = 64;      // rows a folding split gives up to the others
 constexpr int kFoldSlots = 64;         // fold slices at most (c / 8): one fold_s slot each
+constexpr int kPgSplit = 2048;         // paged cache: page ids of one split's rows in LDS (at most)
 
 }  // namespace
 
 // 1-D grid: block L runs on XCD L % 8; the n_hg head groups of one (query,
 // split) are blocks L, L + 8, ... so they share that XCD's L2.
 // DEROT: the output's rotary coordinates are rotated back by the query
-// position (norm_rope); FOLD: the decode fold runs inside (fold_mode).
+// position (norm_rope); FOLD: the decode fold runs inside (fold_mode); PG:
+// the cache is paged (the split's page ids are read into LDS first).
 // Separate instantiations keep the code of one out of the others' register
 // allocation (the row loop's schedule depends on it).
-template <int DEROT, int FOLD>
+template <int DEROT, int FOLD, int PG>
 __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n_split, int rows_per_split) {
   __shared__ __attribute__((aligned(1024))) char tiles[kRing][kTN * kRowB];
+  __shared__ int32_t s_pg[PG ? kPgSplit : 1];  // PG: page ids of the split's cache rows
   __shared__ uint32_t rvalid[kRing][kTN / 4];  // byte r % 4 of word r / 4: row r is a real row
   __shared__ int s_restart;                // a wavefront asks the split to be recomputed
   __shared__ bf16x8_t s_p[2][4][64];       // P^T operands of a tile (two buffers), one block of 16 heads per wavefront
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   const int n_fs = a.fold_mode ? a.fold_nsplit : 0;
   const int rows_here = split < n_fs ? a.fold_rows : rows_per_split;
   const int r_begin = split < n_fs ? split * a.fold_rows : n_fs * a.fold_rows + (split - n_fs) * rows_per_split;
-  const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv) + (size_t)b * a.E_cap * kC;
+  const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv) + (PG ? 0 : (size_t)b * a.E_cap * kC);
 
   // Wave w fetches rows kRowsPerWave * w .. of a tile; every wave reads all
   // rows.  Lane i (mod kRowsPerWave) computes the source of row
@@ -127,7 +130,10 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   auto dma_rows = [&](const uint16_t* src, int buf) {
     const uintptr_t sp = reinterpret_cast<uintptr_t>(src);
     const uint32_t s_lo = (uint32_t)sp, s_hi = (uint32_t)(sp >> 32);
-    const uint32_t lds0 = lds_addr(tiles[buf]) + kRowsPerWave * w * kRowB;
+    uint32_t lds0 = lds_addr(tiles[buf]) + kRowsPerWave * w * kRowB;
+    // (PG: the page-id reads before it leave the compiler unsure that the
+    // slot address is uniform; it is)
+    if constexpr (PG) lds0 = __builtin_amdgcn_readfirstlane(lds0);
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       // (readlane returns int: widen through uint32_t, no sign extension)
@@ -139,7 +145,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   // speculative: the first tile read as cache entries (in the cache
   // buffer, so in bounds whatever the count turns out to be), before
   // anything else
-  const bool spec = r_begin + kTN <= a.E_cap;
+  const bool spec = !PG && r_begin + kTN <= a.E_cap;
   if (spec) dma_rows(kv + (size_t)(r_begin + kRowsPerWave * w + (l & (kRowsPerWave - 1))) * kC, 0);
   // Q^T operands for this wavefront's 16 heads: lane (head li, d group lg).
   // They are requested after the first tile's DMAs and before the
@@ -245,14 +251,31 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   }
 
   if (tid == 0) s_restart = 0;
-  __syncthreads();  // s_restart ready
+  // PG: page ids of the split's cache rows [r_begin, min(r_end, n_c))
+  const int sh = a.pg.shift, p_first = r_begin >> sh;
+  if constexpr (PG) {
+    const int ce = r_end < nc32 ? r_end : nc32;
+    if (r_begin < ce) {
+      const int np = ((ce - 1) >> sh) - p_first + 1;  // <= kPgSplit (checked at launch)
+      const int32_t* tb = a.pg.table + (size_t)b * (a.E_cap >> sh) + p_first;
+      for (int i0 = 0; i0 < np; i0 += 256)  // (a uniform loop)
+        if (i0 + tid < np) s_pg[i0 + tid] = tb[i0 + tid];
+    }
+  }
+  __syncthreads();  // s_restart (and s_pg) ready
 
   auto spread4 = [](uint32_t x) { return (x & 1u) | ((x & 2u) << 7) | ((x & 4u) << 14) | ((x & 8u) << 21); };
   // source of the lane's row j of the split (branch-free); valid: j < r_end
   auto row_src = [&](int j) -> const uint16_t* {
     int wr = wbase + (j - nc32);
     wr = wr >= wcap ? wr - wcap : wr;
-    return j < r_end ? (j < nc32 ? kv + (size_t)j * kC : win + (size_t)wr * kC) : pad_row;
+    size_t cr = (size_t)j;  // the cache row of entry j
+    if constexpr (PG) {
+      int pi = (j >> sh) - p_first;
+      pi = pi < 0 ? 0 : (pi >= kPgSplit ? kPgSplit - 1 : pi);  // (rows that are not entries)
+      cr = ((size_t)(uint32_t)s_pg[pi] << sh) + (size_t)(j & ((1 << sh) - 1));
+    }
+    return j < r_end ? (j < nc32 ? kv + cr * kC : win + (size_t)wr * kC) : pad_row;
   };
   auto set_valid = [&](int r0, int buf) {
     const int j = r0 + kRowsPerWave * w + (l & (kRowsPerWave - 1));
@@ -752,7 +775,8 @@ void attend_mfma_plan(int BT, int H, int rows_max, int split_rows, int* n_split,
 // block handled by one thread of its slice.
 bool attend_fuses_fold(AttendArgs& a, const FoldArgs& f) {
   a.fold_mode = 0;
-  if (!a.dense || a.dtype != BF16 || f.dtype != BF16 || a.kv_fmt || f.kv_fmt || !attend_mfma_shape_ok(a.H, a.c) ||
+  if (!a.dense || a.dtype != BF16 || f.dtype != BF16 || a.kv_fmt || f.kv_fmt || a.pg.table ||
+      !attend_mfma_shape_ok(a.H, a.c) ||
       a.Tq != 1 ||
       a.n_add != 0 || a.win_pos0 != nullptr || a.win_pos0_const != 0 || f.overlap || f.idx_dtype >= 0 ||
       f.B != a.B || f.c != a.c || f.n_win != a.W_cap || f.R < 2 * f.m)
@@ -806,6 +830,14 @@ size_t attend_mfma_ws_bytes(int BT, int H, int rows_max, int split_rows) {
 
 hipError_t launch_attend_merge(const AttendArgs& a, int n_split, hipStream_t s);
 
+// paged cache: a split's page ids fit the kernel's LDS table
+bool attend_mfma_pages_fit(const AttendArgs& a, int rows_max) {
+  if (!a.pg.table) return true;
+  int ns, rps;
+  attend_mfma_plan(a.B * a.Tq, a.H, rows_max, a.split_rows, &ns, &rps);
+  return ((rps - 1) >> a.pg.shift) + 2 <= kPgSplit;
+}
+
 hipError_t launch_attend_mfma(const AttendArgs& a0, int rows_max, hipStream_t s) {
   int ns, rps;
   attend_mfma_plan(a0.B * a0.Tq, a0.H, rows_max, a0.split_rows, &ns, &rps);
@@ -829,12 +861,16 @@ hipError_t launch_attend_mfma(const AttendArgs& a0, int rows_max, hipStream_t s)
   const int n_hg = a.H / kHW;
   const long long units = (long long)ns * a.B * a.Tq;       // (query, split) pairs
   const long long blocks = (units + 7) / 8 * 8 * n_hg;      // padded to whole XCD rounds
-  if (a.derot_freq)
-    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<1, 0>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+  if (a.pg.table && a.derot_freq)
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<1, 0, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+  else if (a.pg.table)
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 0, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+  else if (a.derot_freq)
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<1, 0, 0>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
   else if (a.fold_mode)
-    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 1, 0>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
   else
-    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 0>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 0, 0>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
   if (ns > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -51,8 +51,10 @@ constexpr int kFill = kMaxRows / 256;        // row-source loads per thread
 // 1-D grid: block L runs on XCD L % 8; the n_hg head groups of one (query,
 // split) are blocks L, L + 8, ... so they gather the same rows through one L2.
 // DEROT: the output's rotary coordinates are rotated back by the query
-// position (norm_rope); a separate instantiation leaves the default one as it was
-template <int DEROT>
+// position (norm_rope); PG: the cache is paged (the selected entries' cache
+// rows are read from the block table before the row DMAs start).  Separate
+// instantiations leave the default one as it was.
+template <int DEROT, int PG>
 __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n_split, int rows_per_split) {
   // tile buffers: tile j of the split in buffer j when the split has at
   // most kBufs tiles, else buffers 2w, 2w+1 are wavefront w's ring; reused as
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
   const int n_rows = n_c + (int)n_w;
   const int r_end = r_begin + rows_per_split < n_rows ? r_begin + rows_per_split : n_rows;
   const int n_tiles = r_end > r_begin ? (r_end - r_begin + kTR - 1) / kTR : 0;
-  const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv) + (size_t)b * a.E_cap * kC;
+  const uint16_t* kv = reinterpret_cast<const uint16_t*>(a.kv) + (PG ? 0 : (size_t)b * a.E_cap * kC);
   const uint16_t* win = reinterpret_cast<const uint16_t*>(a.win) + (size_t)b * a.W_cap * kC;
   const float sc2 = a.scale * kLog2e;
   // ring row of the first window position (32-bit remainder when it fits)
@@ -129,6 +131,19 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
   int own = wbase + (int)n_w - 1;
   if (own >= wcap) own -= wcap;
 
+  if constexpr (PG) {
+    // the selected entries' cache rows (pool rows < 2^31), one round of
+    // block-table loads for all of them (an id outside [0, E_cap) reads the
+    // sequence's first page id and becomes -1)
+    const int sh = a.pg.shift;
+    const int32_t* tb = a.pg.table + (size_t)b * (a.E_cap >> sh);
+    int32_t pid[kFill];
+#pragma unroll
+    for (int u = 0; u < kFill; ++u) pid[u] = tb[(v[u] >= 0 && v[u] < a.E_cap) ? (v[u] >> sh) : 0];
+#pragma unroll
+    for (int u = 0; u < kFill; ++u)
+      v[u] = (v[u] >= 0 && v[u] < a.E_cap) ? (int)(((uint32_t)pid[u] << sh) + (uint32_t)(v[u] & ((1 << sh) - 1))) : -1;
+  }
   // row sources of the split
   {
 #pragma unroll
@@ -138,7 +153,10 @@ __global__ __launch_bounds__(256, 1) void attend_rows_kernel(AttendArgs a, int n
         const int j = r_begin + jr;
         int e = -1;
         if (j < n_c) {
-          e = (v[u] >= 0 && v[u] < a.E_cap) ? v[u] : -1;
+          if constexpr (PG)
+            e = v[u];  // already the cache row, or -1
+          else
+            e = (v[u] >= 0 && v[u] < a.E_cap) ? v[u] : -1;
         } else if (j < r_end) {
           int wr = wbase + (j - n_c);
           if (wr >= wcap) wr -= wcap;
@@ -407,10 +425,14 @@ hipError_t launch_attend_rows(const AttendArgs& a, int rows_max, hipStream_t s) 
   const int n_hg = a.H / 16;
   const long long units = (long long)ns * a.B * a.Tq;   // (query, split) pairs
   const long long blocks = (units + 7) / 8 * 8 * n_hg;  // padded to whole XCD rounds
-  if (a.derot_freq)
-    CSA_LAUNCH("attend_sparse_rows", attend_rows_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+  if (a.pg.table && a.derot_freq)
+    CSA_LAUNCH("attend_sparse_rows", (attend_rows_kernel<1, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+  else if (a.pg.table)
+    CSA_LAUNCH("attend_sparse_rows", (attend_rows_kernel<0, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+  else if (a.derot_freq)
+    CSA_LAUNCH("attend_sparse_rows", (attend_rows_kernel<1, 0>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
   else
-    CSA_LAUNCH("attend_sparse_rows", attend_rows_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+    CSA_LAUNCH("attend_sparse_rows", (attend_rows_kernel<0, 0>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
   if (ns > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

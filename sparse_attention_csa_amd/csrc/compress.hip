@@ -109,7 +109,8 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
     vals[nv] = s.acc / s.l;
   }
 
-  const size_t orow = ((size_t)b * a.E_cap + (size_t)(a.first + i)) * c;
+  const size_t erow = page_row(a.pg, b, a.first + i, a.E_cap);  // the entry's cache row
+  const size_t orow = erow * c;
   if constexpr (std::is_same<TO, mx4>::value) {
     // MXFP4 output (c a multiple of 32): the 32 lanes of an aligned lane
     // group hold one block; a pair of neighbouring lanes forms one byte
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
     uint8_t* o = reinterpret_cast<uint8_t*>(a.out) + orow;
     int u = 0;
     for (int r = tid; r < c; r += 256, ++u) o[r] = f32_to_e4m3(vals[u] / scale);
-    if (tid == 0) reinterpret_cast<float*>(a.out_scale)[(size_t)b * a.E_cap + a.first + i] = scale;
+    if (tid == 0) reinterpret_cast<float*>(a.out_scale)[erow] = scale;
   } else if (a.nr.on || std::is_same<TO, f8b16>::value) {
     // the entry prepared for the core attention (nr.on): RMSNorm over its c
     // coordinates, then the rotary pairs (neighbouring lanes) at its position,
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
     const int nu = (c + 255) / 256;  // the same trip count in every lane
     if (!a.nr.on) {
       store_entry<TI_of<TO>>(vals, nu, c, std::is_same<TO, f8b16>::value, a.out,
-                             reinterpret_cast<float*>(a.out_scale), (size_t)b * a.E_cap + a.first + i, s_red);
+                             reinterpret_cast<float*>(a.out_scale), erow, s_red);
       return;
     }
     float ss = 0.f;
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
       vals[u] = v;
     }
     store_entry<TI_of<TO>>(vals, nu, c, std::is_same<TO, f8b16>::value, a.out, reinterpret_cast<float*>(a.out_scale),
-                           (size_t)b * a.E_cap + a.first + i, s_red);
+                           erow, s_red);
   } else if constexpr (!std::is_same<TO, f8b16>::value) {
     TO* o = reinterpret_cast<TO*>(a.out) + orow;
     int u = 0;
@@ -231,6 +232,7 @@ __global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
   const int64_t lim = vis_limit(t, m, a.vis);
   const bool fold = (lim == (int64_t)n_have + 1) && n_have < a.E_cap;
   const int64_t e = n_have;
+  const size_t erow = fold ? page_row(a.pg, b, e, a.E_cap) : 0;  // the new entry's cache row
   const int nstr = a.overlap ? 4 : 2;
   const int slot = (int)(t % R);
   const bool has_idx = a.idx_dtype >= 0;
@@ -272,7 +274,7 @@ __global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
           val[u] = v;
         }
       }
-      store_entry<T>(val, nu, c, a.kv_fmt, a.kv_cache, a.kv_scale, (size_t)b * a.E_cap + e, s_red);
+      store_entry<T>(val, nu, c, a.kv_fmt, a.kv_cache, a.kv_scale, erow, s_red);
     }
     for (int i = tid; i < nstr * c; i += kFoldT) {
       const int sc = i / c, r = i % c;
@@ -298,7 +300,7 @@ __global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
     if (fold) {
       const float val = fold_job<T>(tail, io, c, r0, kFoldCW, m, R, t, e, a.overlap && e > 0, a.bias_a,
                                     a.bias_b, s_part);
-      if (tid < kFoldCW) st(reinterpret_cast<T*>(a.kv_cache), ((size_t)b * a.E_cap + e) * c + r0 + tid, val);
+      if (tid < kFoldCW) st(reinterpret_cast<T*>(a.kv_cache), erow * c + r0 + tid, val);
     }
     for (int i = tid; i < nstr * kFoldCW; i += kFoldT) {
       const int sc = i / kFoldCW, r = r0 + i % kFoldCW;
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
     const T* iio = reinterpret_cast<const T*>(a.idx_streams) + (size_t)b * 4 * d;
     if (fold) {
       const float iv = fold_job<T>(itail, iio, d, 0, d, m, R, t, e, e > 0, a.ibias_a, a.ibias_b, s_part);
-      const size_t row = (size_t)b * a.E_cap + e;
+      const size_t row = erow;
       if constexpr (std::is_same<TI, mx4>::value) {
         // MXFP4 (d a multiple of 32, every lane takes part in the block maxima)
         uint32_t sc;

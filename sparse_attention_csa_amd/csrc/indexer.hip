@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
 
   const int64_t s = s0 + tid;
   if (s >= nv) return;
-  const size_t krow = (size_t)b * a.E_cap + s;
+  const size_t krow = page_row(a.pg, b, s, a.E_cap);  // the key's cache row
   float acc[kHMax];
 #pragma unroll
   for (int h = 0; h < kHMax; ++h) acc[h] = 0.f;
@@ -146,13 +146,15 @@ bool index_prefill_mfma_supported(const IndexArgs& a) {
   return a.idx_dtype == BF16 && a.H_I == kPfH && a.d_I == kPfD && a.Tq % kPfQpw == 0;
 }
 
-template <int QPW, int MF>
+template <int QPW, int MF, int PG>
 __global__ __launch_bounds__(64 * QPW) void index_score_prefill_kernel(IndexArgs a) {
   using namespace tile;
   constexpr int kT = 64 * QPW;               // threads
   constexpr int kCpt = kPfTile * 16 / kT;    // 16-byte chunks of a key tile per thread
   // key tile: row = entry (256 B), its 16-byte chunk c stored at c ^ (row % 16)
   __shared__ __attribute__((aligned(16))) uint4 s_k[2][kPfTile * 16];
+  // PG: page ids of the chunk's entries (paged key cache)
+  __shared__ int32_t s_pg[PG ? kPfChunk + 1 : 1];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, li = l & 15, lg = l >> 4;
   const int row0 = blockIdx.y * QPW, row = row0 + w;  // the rows share their sequence (Tq % QPW == 0)
   const int b = row0 / a.Tq;
@@ -171,7 +173,15 @@ __global__ __launch_bounds__(64 * QPW) void index_score_prefill_kernel(IndexArgs
   if (e0 >= nv_max) return;
   const int64_t e1 = e0 + kPfChunk < nv_max ? e0 + kPfChunk : nv_max;
   const int ntiles = (int)((e1 - e0 + kPfTile - 1) / kPfTile);
-  const uint16_t* keys = reinterpret_cast<const uint16_t*>(a.keys) + (size_t)b * a.E_cap * kPfD;
+  const uint16_t* keys = reinterpret_cast<const uint16_t*>(a.keys) + (PG ? 0 : (size_t)b * a.E_cap * kPfD);
+  const int sh = a.pg.shift;
+  const int p_first = (int)(e0 >> sh);
+  if constexpr (PG) {
+    const int np = (int)((e1 - 1) >> sh) - p_first + 1;  // <= kPfChunk + 1
+    const int32_t* tb = a.pg.table + (size_t)b * (a.E_cap >> sh) + p_first;
+    for (int i = tid; i < np; i += kT) s_pg[i] = tb[i];
+    __syncthreads();
+  }
 
   // A operands.  16x16x32: Q rows = heads 16 ht + li, d = 32 ks + 8 lg ..
   // +7, weights of heads 16 ht + 4 lg + i.  32x32x16: Q rows = heads
@@ -213,7 +223,9 @@ __global__ __launch_bounds__(64 * QPW) void index_score_prefill_kernel(IndexArgs
     const int c = tid + kT * u;
     int64_t e = e0 + (int64_t)j * kPfTile + (c >> 4);
     if (e > e1 - 1) e = e1 - 1;
-    return reinterpret_cast<const uint4*>(keys + (size_t)e * kPfD + 8 * (c & 15));
+    size_t r = (size_t)e;
+    if constexpr (PG) r = ((size_t)(uint32_t)s_pg[(int)(e >> sh) - p_first] << sh) + (size_t)(e & ((1 << sh) - 1));
+    return reinterpret_cast<const uint4*>(keys + r * kPfD + 8 * (c & 15));
   };
   auto load_tile = [&](int j) -> Share {
     Share r;
@@ -317,15 +329,19 @@ hipError_t launch_index_topk(const IndexArgs& a0, hipStream_t s, const FoldArgs*
   if (!a.scores) a.scores = reinterpret_cast<float*>(ws);
   const bool split = rows <= kSplitRows;
   TopkWs tw = topk_ws_carve(ws + sc_bytes, rows, a.E_cap, split);
-  const bool mfma = index_mfma_supported(a) && split;
+  const bool mfma = index_mfma_supported(a) && split && index_mfma_pages_fit(a);
   hipError_t e;
   int n_wg_fused = 0;
   if (mfma) {
     e = launch_index_score_mfma(a, tw, 1, 1, &n_wg_fused, fold, s);
   } else if (index_prefill_mfma_supported(a)) {
     const unsigned gx = (a.E_cap + kPfChunk - 1) / kPfChunk;
-    CSA_LAUNCH("index_score_prefill", (index_score_prefill_kernel<kPfQpw, kPfMfma>), dim3(gx, rows / kPfQpw),
-               dim3(64 * kPfQpw), 0, s, a);
+    if (a.pg.table)
+      CSA_LAUNCH("index_score_prefill", (index_score_prefill_kernel<kPfQpw, kPfMfma, 1>), dim3(gx, rows / kPfQpw),
+                 dim3(64 * kPfQpw), 0, s, a);
+    else
+      CSA_LAUNCH("index_score_prefill", (index_score_prefill_kernel<kPfQpw, kPfMfma, 0>), dim3(gx, rows / kPfQpw),
+                 dim3(64 * kPfQpw), 0, s, a);
     e = hipGetLastError();
   } else {
     dim3 g1((a.E_cap + 255) / 256, rows), blk(256);

@@ -109,7 +109,7 @@ struct Geo {
 // grid (n_wg, rows), 256 threads
 // wait_polls: how many times a waiting workgroup polls for its row's
 // published threshold bin before it gives up (a multiple of 4)
-template <int FMT, int HT>
+template <int FMT, int HT, int PG>
 __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, TopkWs ws, int use_hist, int fuse,
                                                                 FoldArgs f, int fold_mode, int wait_polls) {
   constexpr bool FP8 = FMT == 1, FP4 = FMT == 2;
@@ -188,9 +188,11 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
     if (nv < 0) nv = 0;
   }
   const int64_t nv_scan = fold_now ? nv - 1 : nv;  // the scan workgroups' entries
-  const char* keys = reinterpret_cast<const char*>(a.keys) + (size_t)b * a.E_cap * G::kKeyB;
-  const float* ksc = FP8 ? reinterpret_cast<const float*>(a.k_scale) + (size_t)b * a.E_cap : nullptr;
-  const uint8_t* ksc4 = FP4 ? reinterpret_cast<const uint8_t*>(a.k_scale) + (size_t)b * a.E_cap * (kD / 32) : nullptr;
+  // PG (paged key cache): the pool's base; rows below come from the pages
+  const size_t seq0 = PG ? 0 : (size_t)b * a.E_cap;
+  const char* keys = reinterpret_cast<const char*>(a.keys) + seq0 * G::kKeyB;
+  const float* ksc = FP8 ? reinterpret_cast<const float*>(a.k_scale) + seq0 : nullptr;
+  const uint8_t* ksc4 = FP4 ? reinterpret_cast<const uint8_t*>(a.k_scale) + seq0 * (kD / 32) : nullptr;
   float* out = a.scores + (size_t)row * a.E_cap;
 
   // this wave's tiles [t0, t1), in batches of kU
@@ -211,25 +213,45 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
   // the last row of this wave's run: loads past it (the tail of the run and
   // the batches after it) all re-read that row, which stays in cache
   const int64_t e_last = (t1 * 16 < nv_scan ? t1 * 16 : nv_scan) - 1;
+  // PG: lane i holds the page id of the run's page p_first + i (a run
+  // spans at most 64 pages of >= 16 entries, which the launch checks); a
+  // tile's 16 entries (and the clamped re-reads) share one page, whose id
+  // a lane read takes from that register
+  const int sh = a.pg.shift;
+  const int64_t p_first = (t0 * 16) >> sh;
+  int lane_pg = 0;
+  if constexpr (PG) {
+    if (n > 0) {
+      const int64_t np_row = (int64_t)(a.E_cap >> sh);
+      const int64_t p = p_first + l < np_row ? p_first + l : np_row - 1;
+      lane_pg = a.pg.table[(size_t)b * np_row + p];
+    }
+  }
   auto load_batch = [&](KBatch& kreg, SBatch& sreg, int bi) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int64_t e0 = (t0 + (int64_t)bi * kU + u) * 16;
+      int64_t delta = 0;  // cache row - entry index for the tile's page
+      if constexpr (PG) {
+        const int64_t ee = e0 < e_last ? e0 : e_last;
+        const int pid = __builtin_amdgcn_readlane(lane_pg, (int)((ee >> sh) - p_first));
+        delta = ((int64_t)(uint32_t)pid - (ee >> sh)) << sh;
+      }
 #pragma unroll
       for (int j = 0; j < G::kPieces; ++j) {
         int64_t e = e0 + G::kKpp * j + ld_key;
         if (e > e_last) e = e_last;
-        kreg[u][j] = *reinterpret_cast<const u32x4_t*>(keys + (size_t)e * G::kKeyB + 16 * ld_chunk);
+        kreg[u][j] = *reinterpret_cast<const u32x4_t*>(keys + (size_t)(e + delta) * G::kKeyB + 16 * ld_chunk);
       }
       if constexpr (FP8) {
         int64_t e = e0 + li;
         if (e > e_last) e = e_last;
-        sreg[u] = ksc[e];
+        sreg[u] = ksc[e + delta];
       }
       if constexpr (FP4) {
         int64_t e = e0 + li;
         if (e > e_last) e = e_last;
-        sreg[u] = ksc4[(size_t)e * (kD / 32) + lg];
+        sreg[u] = ksc4[(size_t)(e + delta) * (kD / 32) + lg];
       }
     }
   };
@@ -831,72 +853,94 @@ static ScorerPlan scorer_plan(const IndexArgs& a, int resident, int use_hist, in
 }
 
 // per device: the grid of the scan is sized to the device's resident count
-template <int FMT, int HT>
+// (of the instantiation that runs: contiguous or paged keys)
+template <int FMT, int HT, int PG>
 static int scorer_resident() {
   static std::atomic<int> resident[kMaxDevices];
   const int dev = current_device();
-  if (dev < 0) return resident_wgs(index_score_mfma_kernel<FMT, HT>);
+  if (dev < 0) return resident_wgs(index_score_mfma_kernel<FMT, HT, PG>);
   int r = resident[dev].load(std::memory_order_relaxed);
   if (!r) {
-    r = resident_wgs(index_score_mfma_kernel<FMT, HT>);
+    r = resident_wgs(index_score_mfma_kernel<FMT, HT, PG>);
     resident[dev].store(r, std::memory_order_relaxed);
   }
   return r;
 }
 
-template <int FMT, int HT>
+template <int FMT, int HT, int PG>
 static hipError_t launch_scorer(const IndexArgs& a, TopkWs& ws, int use_hist, int allow_fuse,
                                 int* n_wg_fused, const FoldArgs* fold, hipStream_t s) {
   const int with_fold = fold ? 1 : 0;
-  const ScorerPlan p = scorer_plan(a, scorer_resident<FMT, HT>(), use_hist, allow_fuse && ws.sync != nullptr,
+  const ScorerPlan p = scorer_plan(a, scorer_resident<FMT, HT, PG>(), use_hist, allow_fuse && ws.sync != nullptr,
                                    with_fold);
   if (with_fold && !p.fuse) return hipErrorInvalidValue;  // the caller checks index_fold_fusable first
   *n_wg_fused = p.fuse ? p.per_row : 0;
   ws.list_stride = p.list_stride;  // (also read by the resolve kernel)
   FoldArgs f = fold ? *fold : FoldArgs{};
   dim3 grid(p.per_row, a.B * a.Tq), block(256);
-  CSA_LAUNCH("index_score_mfma", (index_score_mfma_kernel<FMT, HT>), grid, block, 0, s, a, ws, use_hist, p.fuse,
+  CSA_LAUNCH("index_score_mfma", (index_score_mfma_kernel<FMT, HT, PG>), grid, block, 0, s, a, ws, use_hist, p.fuse,
              f, with_fold, fused_wait_polls());
   return hipGetLastError();
 }
 
-template <int FMT>
+template <int FMT, int PG>
 static int resident_for(int HT) {
-  if (HT == 4) return scorer_resident<FMT, 4>();
-  if (HT == 3) return scorer_resident<FMT, 3>();
-  if (HT == 2) return scorer_resident<FMT, 2>();
-  return scorer_resident<FMT, 1>();
+  if (HT == 4) return scorer_resident<FMT, 4, PG>();
+  if (HT == 3) return scorer_resident<FMT, 3, PG>();
+  if (HT == 2) return scorer_resident<FMT, 2, PG>();
+  return scorer_resident<FMT, 1, PG>();
 }
 
 static int scan_format(int idx_dtype) { return idx_dtype == MXFP4 ? 2 : (idx_dtype == E4M3 ? 1 : 0); }
 
+// paged keys: a 16-entry tile within one page (>= 16 entries per page) and
+// a wave's run within 64 pages (the run of the scan's grid for E_cap)
+bool index_mfma_pages_fit(const IndexArgs& a) {
+  if (!a.pg.table) return true;
+  if (a.pg.shift < 4) return false;
+  const int fmt = scan_format(a.idx_dtype);
+  const int resident = fmt == 2 ? resident_for<2, 1>(a.H_I / 16)
+                                : (fmt == 1 ? resident_for<1, 1>(a.H_I / 16) : resident_for<0, 1>(a.H_I / 16));
+  const ScorerPlan p = scorer_plan(a, resident, 1, 1, 0);
+  const int64_t ntile = ((int64_t)a.E_cap + 15) / 16, nwaves = (int64_t)p.per_row * 4;
+  const int64_t per = (ntile + nwaves - 1) / nwaves;
+  return ((per * 16) >> a.pg.shift) + 2 <= 64;
+}
+
 bool index_fold_fusable(const IndexArgs& a, const FoldArgs& f, bool split) {
-  if (!split || !index_mfma_supported(a) || a.Tq != 1 || f.B != a.B || f.dtype != BF16 || f.kv_fmt ||
+  if (!split || !index_mfma_supported(a) || a.Tq != 1 || f.B != a.B || f.dtype != BF16 || f.kv_fmt || a.pg.table ||
       f.idx_dtype != a.idx_dtype ||
       f.d_I != kD || a.n_add != 0)
     return false;
   const int fmt = scan_format(a.idx_dtype);
-  const int resident = fmt == 2 ? resident_for<2>(a.H_I / 16)
-                                : (fmt == 1 ? resident_for<1>(a.H_I / 16) : resident_for<0>(a.H_I / 16));
+  const int resident = fmt == 2 ? resident_for<2, 0>(a.H_I / 16)
+                                : (fmt == 1 ? resident_for<1, 0>(a.H_I / 16) : resident_for<0, 0>(a.H_I / 16));
   return scorer_plan(a, resident, 1, 1, 1).fuse != 0;
 }
 
-template <int FMT>
+template <int FMT, int PG>
 static hipError_t launch_scorer_fmt(const IndexArgs& a, TopkWs& ws, int use_hist, int allow_fuse,
                                     int* n_wg_fused, const FoldArgs* fold, hipStream_t s) {
   const int HT = a.H_I / 16;
-  if (HT == 4) return launch_scorer<FMT, 4>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
-  if (HT == 3) return launch_scorer<FMT, 3>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
-  if (HT == 2) return launch_scorer<FMT, 2>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
-  return launch_scorer<FMT, 1>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  if (HT == 4) return launch_scorer<FMT, 4, PG>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  if (HT == 3) return launch_scorer<FMT, 3, PG>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  if (HT == 2) return launch_scorer<FMT, 2, PG>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  return launch_scorer<FMT, 1, PG>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+}
+
+template <int PG>
+static hipError_t launch_scorer_pg(const IndexArgs& a, TopkWs& ws, int use_hist, int allow_fuse,
+                                   int* n_wg_fused, const FoldArgs* fold, hipStream_t s) {
+  const int fmt = scan_format(a.idx_dtype);
+  if (fmt == 2) return launch_scorer_fmt<2, PG>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  if (fmt == 1) return launch_scorer_fmt<1, PG>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  return launch_scorer_fmt<0, PG>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
 }
 
 hipError_t launch_index_score_mfma(const IndexArgs& a, TopkWs& ws, int use_hist, int allow_fuse,
                                    int* n_wg_fused, const FoldArgs* fold, hipStream_t s) {
-  const int fmt = scan_format(a.idx_dtype);
-  if (fmt == 2) return launch_scorer_fmt<2>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
-  if (fmt == 1) return launch_scorer_fmt<1>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
-  return launch_scorer_fmt<0>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  if (a.pg.table) return launch_scorer_pg<1>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
+  return launch_scorer_pg<0>(a, ws, use_hist, allow_fuse, n_wg_fused, fold, s);
 }
 
 }  // namespace csa

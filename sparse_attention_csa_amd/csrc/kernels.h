@@ -62,6 +62,22 @@ struct NormRope {
   const double* inv_freq;   // [rope_dims / 2]
 };
 
+// Paged compressed caches ([book] ch. 13 "Aligning original-token blocks"):
+// with a block table, entry e of sequence b lives in row
+// table[b][e >> shift] * 2^shift + (e & (2^shift - 1)) of a pool of pages
+// shared by all sequences (the main cache, the indexer keys and their
+// scales, the entry scales: one row each per entry); without one, in row
+// b * E_cap + e.
+struct PageMap {
+  const int32_t* table;  // [B][E_cap >> shift] page ids, or null
+  int shift;             // log2 of the entries per page
+};
+__host__ __device__ inline size_t page_row(const PageMap& p, int b, int64_t e, int E_cap) {
+  if (!p.table) return (size_t)b * E_cap + (size_t)e;
+  const int32_t pg = p.table[(size_t)b * (size_t)(E_cap >> p.shift) + (size_t)(e >> p.shift)];
+  return ((size_t)(uint32_t)pg << p.shift) + (size_t)(e & ((1 << p.shift) - 1));
+}
+
 // ------------------------------------------------------------ compressor
 struct CompressArgs {
   int dtype;  // input dtype (F32 / BF16)
@@ -77,6 +93,7 @@ struct CompressArgs {
   size_t seq_stride;       // elements between sequences of ca/za/cb/zb (0: T*c or T*lw)
   size_t prev_seq_stride;  // elements between sequences of prev_cb/prev_zb (0: m*c or m*lw)
   NormRope nr;             // on: entry first + i is prepared at position m * (first + i)
+  PageMap pg;              // rows of out / out_scale
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 
@@ -108,6 +125,7 @@ struct FoldArgs {
   // main entries stored as FP8BF16 (576 bytes + a float32 scale in kv_scale)
   int kv_fmt;
   float* kv_scale;
+  PageMap pg;  // rows of kv_cache, kv_scale, idx_cache, idx_scale
 };
 hipError_t launch_fold_append(const FoldArgs& a, hipStream_t s);
 
@@ -158,6 +176,7 @@ struct IndexArgs {
   int32_t* topk_idx;    // [B][Tq][k]
   int32_t* topk_cnt;    // [B][Tq]
   void* ws;             // topk scratch
+  PageMap pg;           // rows of keys / k_scale
 };
 size_t index_topk_ws_bytes(int B, int Tq, int E_cap, int k);
 // fold: the decode step's fold to run inside the scoring kernel, or null
@@ -220,6 +239,7 @@ struct AttendArgs {
   // window rows and q stay in dtype
   int kv_fmt;
   const float* kv_scale;
+  PageMap pg;  // rows of kv / kv_scale
 };
 // split_rows > 0: rows per split fixed (batch-invariant launch plan), else
 // chosen for the batch

@@ -35,6 +35,7 @@ static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 struct Config {
   csa_layer_desc d;
   int B, E_cap;
+  int paged;  // a paged cache runs other kernels (the fold apart from the scan)
   bool operator==(const Config& o) const { return std::memcmp(this, &o, sizeof(Config)) == 0; }
 };
 
@@ -87,6 +88,7 @@ csa_status hybrid_layer_decode_noalloc(const csa_layer_desc* desc, csa_layer_sta
   cfg.d = *desc;
   cfg.B = state->B;
   cfg.E_cap = state->E_cap;
+  cfg.paged = state->block_table != nullptr;
   if (!ds.have_cfg || !(ds.cfg == cfg)) {
     // another configuration places other data where this one's counters
     // live: clear what this call uses (stream-ordered before it)

@@ -131,6 +131,8 @@ hipError_t launch_topk_rows(const IndexArgs& a, const TopkWs& ws, hipStream_t s)
 // scoring workgroups per row, else 0.  With fold (only when
 // index_fold_fusable) it also performs the decode step's fold.
 bool index_mfma_supported(const IndexArgs& a);
+// paged keys (a.pg.table): whether the scan's paged form takes them
+bool index_mfma_pages_fit(const IndexArgs& a);
 hipError_t launch_index_score_mfma(const IndexArgs& a, TopkWs& ws, int use_hist, int allow_fuse,
                                    int* n_wg_fused, const FoldArgs* fold, hipStream_t s);
 // whether the decode step's fold can run inside the scoring kernel (fold

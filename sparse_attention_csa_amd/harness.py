@@ -120,6 +120,42 @@ class _State:
             self.ibias_a = dev(g["ibias_a"], "f32", device)
             self.ibias_b = dev(g["ibias_b"], "f32", device)
         self.B, self.E_cap = B, E_cap
+        self.pools = {}  # paged: the pools behind the per-sequence caches
+        self.table = None
+        self.page_entries = 0
+        self.auto_gather = True  # paged: refresh the per-sequence views after each call
+
+    _PAGED = ("kv_cache", "kv_scale", "idx_cache", "idx_scale")
+
+    def page_in(self, g):
+        """Paged cache (g["block_table"], g["page_entries"], g["n_pages"]):
+        move the per-sequence caches into pools of pages (rows no sequence
+        owns hold all-ones bytes, NaN in every float format), which the
+        library then reads and writes; the per-sequence tensors become views
+        refreshed by gather()."""
+        P = int(g["page_entries"])
+        table = np.asarray(g["block_table"], np.int32)
+        B, E = self.B, self.E_cap
+        assert table.shape == (B, E // P) and E % P == 0
+        e = np.arange(E)
+        rows = table[:, e // P].astype(np.int64) * P + e % P
+        device = self.kv_cache.device
+        self.rows = torch.from_numpy(rows).to(device)
+        self.table = dev(table, "i32", device)
+        self.page_entries = P
+        for name in self._PAGED:
+            x = getattr(self, name)
+            if x is None:
+                continue
+            pool = torch.empty((int(g["n_pages"]) * P,) + tuple(x.shape[2:]), dtype=x.dtype, device=device)
+            pool.view(torch.uint8).fill_(0xFF)
+            pool[self.rows.reshape(-1)] = x.reshape((-1,) + tuple(x.shape[2:]))
+            self.pools[name] = pool
+
+    def gather(self):
+        """Paged: refresh the per-sequence caches from the pools (stream-ordered)."""
+        for name, pool in self.pools.items():
+            getattr(self, name).copy_(pool[self.rows])
 
     def struct(self):
         s = L.LayerState()
@@ -127,7 +163,9 @@ class _State:
         for name in ("kv_cache", "idx_cache", "idx_scale", "n_entries", "win_ring", "tail",
                      "idx_tail", "bias_a", "bias_b", "ibias_a", "ibias_b", "sink", "q_norm_w",
                      "kv_norm_w", "rope_inv_freq", "kv_scale"):
-            setattr(s, name, L.ptr(getattr(self, name)))
+            setattr(s, name, L.ptr(self.pools.get(name, getattr(self, name))))
+        s.block_table = L.ptr(self.table)
+        s.page_entries = self.page_entries
         return s
 
 
@@ -181,10 +219,13 @@ class DecodeSession:
         self.io, self._io_struct = decode_io(g, device)
         self.ws = torch.zeros(max(256, L.hybrid_layer_workspace(self.desc, B, 1, E_cap)),
                               dtype=torch.uint8, device=device)
+        if g.get("block_table") is not None:
+            st.page_in(g)
         self._state_struct = st.struct()
 
     def run(self, stream=None):
         L.hybrid_layer_decode(self.desc, self._state_struct, self._io_struct, self.ws, stream)
+        _after(self.state, stream)
 
 
 def decode_io(g, device="cuda"):
@@ -271,11 +312,14 @@ class PrefillSession:
                      "topk_idx", "topk_cnt"):
             setattr(s, name, L.ptr(io.get(name)))
         self._io_struct = s
+        if g.get("block_table") is not None:
+            st.page_in(g)
         self._state_struct = st.struct()
         self.dec_ws = None
 
     def run(self, stream=None):
         L.hybrid_layer_prefill(self.desc, self._state_struct, self._io_struct, self.ws, stream)
+        _after(self.state, stream)
 
     def decode(self, g_step, stream=None):
         """Continue the same layer state with one decode step whose per-token
@@ -288,4 +332,16 @@ class PrefillSession:
                 dtype=torch.uint8, device=self.state.kv_cache.device)
         io, s = decode_io(g_step, self.state.kv_cache.device)
         L.hybrid_layer_decode(self.desc, self._state_struct, s, self.dec_ws, stream)
+        _after(self.state, stream)
         return io
+
+
+def _after(st, stream):
+    """Paged state: the per-sequence views follow the pools after a call."""
+    if not st.pools or not st.auto_gather:
+        return
+    if stream is None:
+        st.gather()
+    else:
+        with torch.cuda.stream(stream):
+            st.gather()

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     lib = L.lib()
     for name in header_functions():
         assert hasattr(lib, name), name
-    assert lib.csa_abi_version() == 3
+    assert lib.csa_abi_version() == 4
 
 
 def _status(fn, *args):
@@ -154,3 +154,30 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "libcsa.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         L.lib()
+
+
+def test_layer_rejects_bad_pages():
+    """The paged cache's arguments are checked before anything is enqueued
+    (the state's pointers here are never dereferenced)."""
+    lib = L.lib()
+    d = L.LayerDesc(kind=L.CSA_LAYER_CSA, H=64, c=512, H_I=64, d_I=128, m=4, overlap=1, k=512, n_win=128,
+                    vis=0, kv_dtype=1, idx_dtype=1, scale=0.044)
+    s = L.LayerState(B=2, E_cap=4096)
+    fake = 1 << 20
+    for n in ("kv_cache", "n_entries", "win_ring", "tail", "idx_cache", "idx_tail"):
+        setattr(s, n, fake)
+    io = L.DecodeIO()
+    s.block_table = fake
+    for P in (24, 0, -32, 8192):  # not a power of two; 8192 does not divide E_cap
+        s.page_entries = P
+        st = lib.hybrid_layer_decode(C.byref(d), C.byref(s), C.byref(io), None, 0, None)
+        assert st == L.CSA_ERR_ARG and "page_entries" in L.last_error(), (P, L.last_error())
+    s.page_entries = 32
+    s.block_table = fake + 4
+    st = lib.hybrid_layer_decode(C.byref(d), C.byref(s), C.byref(io), None, 0, None)
+    assert st == L.CSA_ERR_ARG and "block_table" in L.last_error()
+    s.block_table = fake  # a valid paged state: the next check is the io's
+    st = lib.hybrid_layer_decode(C.byref(d), C.byref(s), C.byref(io), None, 0, None)
+    assert st == L.CSA_ERR_ARG and "pos" in L.last_error()
+    st = lib.hybrid_layer_prefill(C.byref(d), C.byref(s), C.byref(L.PrefillIO()), None, 0, None)
+    assert st == L.CSA_ERR_ARG and "page_entries" not in L.last_error()

@@ -14,5 +14,7 @@ from .gen import (  # noqa: F401
     flash_prefill,
     with_norm_rope,
     with_fp8bf16_cache,
+    with_pages,
+    block_table,
     CONFIG_NAMES,
 )

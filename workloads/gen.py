@@ -384,3 +384,41 @@ def with_fp8bf16_cache(g):
     out["kv_cache"], out["kv_scale"] = fp8bf16_rows(vals)
     out["kv_dtype"] = "fp8bf16"
     return out
+
+
+def block_table(B, n_blocks, seed=11, spare=3):
+    """A seeded random block table [B][n_blocks] over a pool of
+    B * n_blocks + spare pages (each page owned by one sequence), and the
+    pool's page count."""
+    rng = _rng(seed)
+    n_pages = B * n_blocks + spare
+    perm = rng.permutation(n_pages)[:B * n_blocks].astype(np.int32)
+    return perm.reshape(B, n_blocks), n_pages
+
+
+def with_pages(g, page_entries, table=None, n_pages=None, seed=11):
+    """A copy of layer case g whose compressed caches live in pages of
+    page_entries entries ("DeepSeek-V4" book ch. 13 "Aligning
+    original-token blocks": with one 128-token unit per table slot, a CSA
+    layer's page holds 32 entries and an HCA layer's one, so one table
+    serves both).  The per-sequence caches are padded with empty rows to
+    n_blocks * page_entries entries (the capacity the table maps); the
+    device state scatters them into a pool of n_pages pages.  Without a
+    table, a seeded random one with just enough blocks."""
+    out = dict(g)
+    B, E = g["B"], g["E_cap"]
+    if table is None:
+        table, n_pages = block_table(B, -(-E // page_entries), seed)
+    table = np.asarray(table, np.int32)
+    assert table.shape[0] == B and n_pages is not None
+    E_new = table.shape[1] * page_entries
+    assert E_new >= E, "the table maps fewer entries than the case holds"
+    for name in ("kv_cache", "kv_scale", "idx_cache", "idx_scale"):
+        x = g.get(name)
+        if x is None:
+            continue
+        x = np.asarray(x)
+        pad = np.zeros((B, E_new - E) + x.shape[2:], x.dtype)
+        out[name] = np.concatenate([x, pad], axis=1)
+    out.update(E_cap=E_new, page_entries=page_entries, block_table=table, n_pages=n_pages)
+    return out
