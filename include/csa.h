@@ -85,7 +85,8 @@ const char* csa_last_error(void);
  * csa_layer_desc.score_bf16, the score_bf16 argument of csa_index_topk, the
  * normalisation / rotary fields of csa_layer_desc and csa_layer_state, and
  * the FP8BF16 main entry with csa_layer_state.kv_scale; 4 added the paged
- * cache, csa_layer_state.block_table and page_entries). */
+ * cache, csa_layer_state.block_table and page_entries, and variable-length
+ * prefill chunks, csa_prefill_io.seq_pos0 and seq_len). */
 int csa_abi_version(void);
 
 /* ------------------------------------------------------------------------
@@ -324,7 +325,23 @@ typedef struct {
 } csa_decode_io;
 
 /* A prefill chunk of T tokens per sequence starting at position pos0 (all
- * sequences aligned); pos0 % m == 0 and T % m == 0. */
+ * sequences aligned); pos0 % m == 0 and T % m == 0.  Or, with seq_pos0 and
+ * seq_len, a variable-length batch ([book] ch. 11 "Packing and attention
+ * boundaries"): sequence b's chunk holds positions seq_pos0[b] ..
+ * seq_pos0[b] + seq_len[b] - 1 (0 <= seq_len[b] <= T, seq_pos0[b] >= 0;
+ * neither needs to be a multiple of m) in rows 0 .. seq_len[b] - 1 of the
+ * [B][T] inputs, and pos0 is not used.  A block becomes an entry when its
+ * last token is in the chunk; the block's earlier tokens (and, with
+ * overlap, the previous block's) come from the state's tail, as the
+ * decode fold takes them, so a trailing fragment shorter than m produces no
+ * entry and stays in the tail for the next chunk or decode step, and no
+ * block mixes two sequences.  The state must be the one the sequence's
+ * earlier calls left: n_entries[b] = floor(seq_pos0[b] / m) completed
+ * entries and the tails holding the positions before seq_pos0[b].  Rows
+ * >= seq_len[b] are padding: they are read (as queries of the sequence's
+ * last position) and their outputs and top-k rows are unspecified; the
+ * window rows win[b] are those of positions seq_pos0[b] - (n_win - 1) ..
+ * Entries past E_cap are not produced (a chunk must not need them). */
 typedef struct {
   int64_t pos0;
   int T;
@@ -341,6 +358,8 @@ typedef struct {
   float* lse;               /* [B][T][H] or NULL                               */
   int32_t* topk_idx;        /* [B][T][k] out (CSA)                             */
   int32_t* topk_cnt;        /* [B][T] out (CSA)                                */
+  const int64_t* seq_pos0;  /* [B] device, or NULL (all chunks start at pos0) */
+  const int32_t* seq_len;   /* [B] device (with seq_pos0)                      */
 } csa_prefill_io;
 
 /* Workspace for hybrid_layer_decode / hybrid_layer_prefill (T = 1 for decode). */

@@ -65,7 +65,8 @@ class PrefillIO(C.Structure):
     _fields_ = [("pos0", C.c_int64), ("T", C.c_int), ("q", C.c_void_p), ("q_idx", C.c_void_p),
                 ("q_scale", C.c_void_p), ("w_idx", C.c_void_p), ("win", C.c_void_p),
                 ("streams", C.c_void_p), ("idx_streams", C.c_void_p), ("out", C.c_void_p),
-                ("lse", C.c_void_p), ("topk_idx", C.c_void_p), ("topk_cnt", C.c_void_p)]
+                ("lse", C.c_void_p), ("topk_idx", C.c_void_p), ("topk_cnt", C.c_void_p),
+                ("seq_pos0", C.c_void_p), ("seq_len", C.c_void_p)]
 
 
 class KernelTime(C.Structure):

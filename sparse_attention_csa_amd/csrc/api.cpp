@@ -357,9 +357,16 @@ static csa::NormRope norm_rope_of(const csa_layer_desc* d, const csa_layer_state
   return nr;
 }
 
+// variable-length prefill: each query row's position [B][T] and each
+// sequence's first window position [B] (int64), after the prepared rows
+static size_t varlen_bytes(int B, int T) {
+  return align_up((size_t)B * T * sizeof(int64_t)) + align_up((size_t)B * sizeof(int64_t));
+}
+
 size_t hybrid_layer_workspace(const csa_layer_desc* d, int B, int T, int E_cap) {
   if (!d || B < 1 || T < 1 || E_cap < 1) return 0;
-  size_t bytes = align_up((size_t)B * sizeof(int32_t)) + prep_q_bytes(d, B, T) + prep_win_bytes(d, B, T);
+  size_t bytes = align_up((size_t)B * sizeof(int32_t)) + prep_q_bytes(d, B, T) + prep_win_bytes(d, B, T) +
+                 varlen_bytes(B, T);
   size_t rows = (size_t)E_cap + d->n_win;
   if (d->kind == CSA_LAYER_CSA) {
     bytes += align_up(csa::index_topk_ws_bytes(B, T, E_cap, d->k));
@@ -487,10 +494,19 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
     REQUIRE(!scaled(d->idx_dtype) || io->q_scale != nullptr, CSA_ERR_ARG, "E4M3 and MXFP4 indexers need q_scale");
   }
   const int B = s->B, T = io->T, m = d->m;
-  REQUIRE(T >= 1 && io->pos0 >= 0, CSA_ERR_ARG, "T must be >= 1 and pos0 >= 0");
-  REQUIRE(io->pos0 % m == 0 && T % m == 0, CSA_ERR_UNSUPPORTED,
-          "prefill chunks must start and end on block boundaries (pos0 %% m == 0, T %% m == 0)");
-  REQUIRE((io->pos0 + T) / m <= (int64_t)s->E_cap, CSA_ERR_ARG, "E_cap too small for the chunk's entries");
+  // variable-length chunks: per-sequence starts and lengths on the device
+  const bool varlen = io->seq_pos0 != nullptr;
+  REQUIRE((io->seq_pos0 == nullptr) == (io->seq_len == nullptr), CSA_ERR_ARG, "seq_pos0 and seq_len go together");
+  if (varlen) {
+    REQ_PTR(io->seq_pos0); REQ_PTR(io->seq_len);
+    REQUIRE(T >= 1, CSA_ERR_ARG, "T must be >= 1");
+  } else {
+    REQUIRE(T >= 1 && io->pos0 >= 0, CSA_ERR_ARG, "T must be >= 1 and pos0 >= 0");
+    REQUIRE(io->pos0 % m == 0 && T % m == 0, CSA_ERR_UNSUPPORTED,
+            "prefill chunks must start and end on block boundaries (pos0 %% m == 0, T %% m == 0) "
+            "unless given per sequence (seq_pos0, seq_len)");
+    REQUIRE((io->pos0 + T) / m <= (int64_t)s->E_cap, CSA_ERR_ARG, "E_cap too small for the chunk's entries");
+  }
   const size_t need = hybrid_layer_workspace(d, B, T, s->E_cap);
   REQUIRE(ws != nullptr && ws_bytes >= need, CSA_ERR_WORKSPACE, "workspace of %zu bytes required", need);
   hipStream_t hs = (hipStream_t)stream;
@@ -498,11 +514,23 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
   void* q_prep = w;  // norm_rope: prepared queries, then window rows
   void* win_prep = w + prep_q_bytes(d, B, T);
   w += prep_q_bytes(d, B, T) + prep_win_bytes(d, B, T);
+  int64_t* vl_qpos = (int64_t*)w;  // variable-length chunks: query positions, window starts
+  int64_t* vl_win0 = (int64_t*)(w + align_up((size_t)B * T * sizeof(int64_t)));
+  w += varlen_bytes(B, T);
   const csa::NormRope nr = norm_rope_of(d, s);
   const int S = n_streams(d), R = tail_depth(d);
-  const int64_t first = io->pos0 / m;
-  const int n_new = T / m;
+  const int64_t first = varlen ? 0 : io->pos0 / m;
+  const int n_new = varlen ? 0 : T / m;  // (variable-length: the counts are set first)
   const size_t esz = act_dtype(d) == CSA_F32 ? 4 : 2;
+  hipError_t e = hipSuccess;
+  if (varlen) {
+    csa::VarlenArgs v{};
+    v.B = B; v.T = T; v.m = m; v.n_win = d->n_win; v.E_cap = s->E_cap;
+    v.seq_pos0 = io->seq_pos0; v.seq_len = io->seq_len;
+    v.q_pos = vl_qpos; v.win_pos0 = vl_win0; v.n_entries = s->n_entries;
+    e = csa::launch_varlen_setup(v, hs);
+    if (e != hipSuccess) return from_hip(e, "hybrid_layer_prefill/varlen");
+  }
 
   // compress the chunk's blocks: main entries, then (CSA) indexer keys
   auto compress = [&](const void* streams, int width, const void* tail, void* out, int out_dtype,
@@ -517,7 +545,9 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
     c.cb = overlap ? base + 2 * plane : nullptr;
     c.zb = overlap ? base + 3 * plane : nullptr;
     c.seq_stride = (size_t)ns * T * width;
-    if (overlap && io->pos0 > 0) {
+    if (varlen) {
+      c.seq_pos0 = io->seq_pos0; c.seq_len = io->seq_len; c.tail = tail; c.R = R;
+    } else if (overlap && io->pos0 > 0) {
       const char* tb = (const char*)tail;
       const size_t slot = (size_t)((io->pos0 - m) % R);
       c.prev_cb = tb + ((size_t)2 * R + slot) * width * esz;
@@ -530,7 +560,7 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
     c.pg = page_map_of(s);
     return csa::launch_compress(c, hs);
   };
-  hipError_t e = compress(io->streams, d->c, s->tail, s->kv_cache, d->kv_dtype, s->kv_scale, s->bias_a,
+  e = compress(io->streams, d->c, s->tail, s->kv_cache, d->kv_dtype, s->kv_scale, s->bias_a,
                           s->bias_b, d->overlap != 0, d->norm_rope != 0);
   if (e != hipSuccess) return from_hip(e, "hybrid_layer_prefill/compress");
   csa::AttendArgs a{};
@@ -544,7 +574,7 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
     x.idx_dtype = d->idx_dtype; x.q = io->q_idx; x.q_scale = scaled(d->idx_dtype) ? io->q_scale : nullptr;
     x.w = io->w_idx; x.keys = s->idx_cache; x.k_scale = scaled(d->idx_dtype) ? s->idx_scale : nullptr;
     x.score_bf16 = d->score_bf16;
-    x.q_pos = nullptr; x.q_pos0 = io->pos0; x.n_entries = s->n_entries; x.n_add = n_new;
+    x.q_pos = varlen ? vl_qpos : nullptr; x.q_pos0 = io->pos0; x.n_entries = s->n_entries; x.n_add = n_new;
     x.B = B; x.Tq = T; x.H_I = d->H_I; x.d_I = d->d_I; x.E_cap = s->E_cap; x.m = m; x.k = d->k;
     x.vis = d->vis; x.scores = nullptr; x.topk_idx = io->topk_idx; x.topk_cnt = io->topk_cnt; x.ws = w;
     x.pg = page_map_of(s);
@@ -558,16 +588,17 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
   a.dtype = act_dtype(d); a.q = io->q; a.kv = s->kv_cache; a.E_cap = s->E_cap;
   a.kv_fmt = d->kv_dtype == CSA_FP8BF16; a.kv_scale = s->kv_scale;
   a.pg = page_map_of(s);
-  a.win = io->win; a.W_cap = d->n_win - 1 + T; a.win_pos0 = nullptr;
+  a.win = io->win; a.W_cap = d->n_win - 1 + T; a.win_pos0 = varlen ? vl_win0 : nullptr;
   a.win_pos0_const = io->pos0 - (d->n_win - 1); a.n_win = d->n_win;
-  a.sink = s->sink; a.q_pos = nullptr; a.q_pos0 = io->pos0; a.scale = d->scale;
+  a.sink = s->sink; a.q_pos = varlen ? vl_qpos : nullptr; a.q_pos0 = io->pos0; a.scale = d->scale;
   a.B = B; a.Tq = T; a.H = d->H; a.c = d->c; a.out = io->out; a.lse = io->lse;
   a.ws = w; a.ws_bytes = ws_bytes - (size_t)(w - (char*)ws);
   if (d->norm_rope) {
     // the chunk's queries and window rows prepared for the attention
     csa::PrepArgs pa{};
     pa.dtype = act_dtype(d); pa.B = B; pa.T = T; pa.H = d->H; pa.c = d->c; pa.n_win = d->n_win;
-    pa.pos0 = io->pos0; pa.nr = nr; pa.q = io->q; pa.win = io->win; pa.q_prep = q_prep; pa.win_prep = win_prep;
+    pa.pos0 = io->pos0; pa.seq_pos0 = io->seq_pos0;
+    pa.nr = nr; pa.q = io->q; pa.win = io->win; pa.q_prep = q_prep; pa.win_prep = win_prep;
     e = csa::launch_prep_rows(pa, hs);
     if (e != hipSuccess) return from_hip(e, "hybrid_layer_prefill/prep");
     a.q = q_prep;
@@ -584,6 +615,7 @@ csa_status hybrid_layer_prefill(const csa_layer_desc* d, csa_layer_state* s, con
   p.streams = io->streams; p.idx_streams = is_csa ? io->idx_streams : nullptr;
   p.win_ring = s->win_ring; p.tail = s->tail; p.idx_tail = s->idx_tail; p.n_entries = s->n_entries;
   p.new_entries = n_new;
+  p.seq_pos0 = io->seq_pos0; p.seq_len = io->seq_len;
   return from_hip(csa::launch_prefill_state(p, hs), "hybrid_layer_prefill/state");
 }
 

@@ -58,7 +58,22 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
   const T* cb = a.cb ? cptr<T>(a.cb) + (size_t)b * sc : nullptr;
   const T* za = a.za ? cptr<T>(a.za) + (size_t)b * sz : nullptr;
   const T* zb = a.zb ? cptr<T>(a.zb) + (size_t)b * sz : nullptr;
-  const bool has_b = (cb != nullptr) && (i > 0 || a.prev_cb != nullptr);
+  // the entry; variable-length chunks: the sequence's chunk starts at vp0,
+  // its entries run from floor(vp0 / m) to the last block that ends in it,
+  // and sources before vp0 come from the tail ring (blocks never cross
+  // sequences: a trailing fragment stays in the tail)
+  int64_t e = a.first + i, vp0 = 0;
+  const T* vtail = nullptr;
+  if (a.seq_pos0) {
+    vp0 = a.seq_pos0[b];
+    vp0 = vp0 < 0 ? 0 : vp0;
+    int64_t len = a.seq_len[b];
+    len = len < 0 ? 0 : (len > Tn ? Tn : len);
+    e = vp0 / m + i;
+    if (e >= (vp0 + len) / m || e >= a.E_cap) return;  // (uniform in the workgroup)
+    vtail = cptr<T>(a.tail) + (size_t)b * (a.cb ? 4 : 2) * a.R * c;
+  }
+  const bool has_b = a.seq_pos0 ? (cb != nullptr && e > 0) : ((cb != nullptr) && (i > 0 || a.prev_cb != nullptr));
   const T* pcb = a.prev_cb ? cptr<T>(a.prev_cb) + (size_t)b * pc : nullptr;
   const T* pzb = a.prev_zb ? cptr<T>(a.prev_zb) + (size_t)b * pz : nullptr;
 
@@ -81,6 +96,30 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
   int nv = 0;
   for (int r = tid; r < c; r += 256, ++nv) {
     Soft s{-INFINITY, 0.f, 0.f};
+    if (a.seq_pos0) {
+      // stream st (0 content a, 1 logits a, 2 content b, 3 logits b) at
+      // position p (logit width c)
+      auto row = [&](int st, int64_t p) -> const T* {
+        const T* ch = st == 0 ? ca : (st == 1 ? za : (st == 2 ? cb : zb));
+        return p >= vp0 ? ch + (size_t)(p - vp0) * c : vtail + ((size_t)st * a.R + (size_t)(p % a.R)) * c;
+      };
+      for (int j = 0; j < m; ++j) {
+        const int64_t p = (int64_t)m * e + j;
+        float lg = ld(row(1, p), r);
+        if (a.bias_a) lg += a.bias_a[j * c + r];
+        soft_push(s, lg, ld(row(0, p), r));
+      }
+      if (has_b) {
+        for (int j = 0; j < m; ++j) {
+          const int64_t p = (int64_t)m * (e - 1) + j;
+          float lg = ld(row(3, p), r);
+          if (a.bias_b) lg += a.bias_b[j * c + r];
+          soft_push(s, lg, ld(row(2, p), r));
+        }
+      }
+      vals[nv] = s.acc / s.l;
+      continue;
+    }
     for (int j = 0; j < m; ++j) {
       const int tok = m * i + j;
       float lg;
@@ -109,7 +148,7 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
     vals[nv] = s.acc / s.l;
   }
 
-  const size_t erow = page_row(a.pg, b, a.first + i, a.E_cap);  // the entry's cache row
+  const size_t erow = page_row(a.pg, b, e, a.E_cap);  // the entry's cache row
   const size_t orow = erow * c;
   if constexpr (std::is_same<TO, mx4>::value) {
     // MXFP4 output (c a multiple of 32): the 32 lanes of an aligned lane
@@ -156,7 +195,7 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
     __syncthreads();
     ss = s_red[0] + s_red[1] + s_red[2] + s_red[3];
     const float inv = 1.0f / sqrtf(ss / (float)c + a.nr.eps);
-    const int64_t pos = (int64_t)m * (a.first + i);
+    const int64_t pos = (int64_t)m * e;
     const int R = a.nr.rope_dims;
     for (int u = 0; u < nu; ++u) {
       const int r = tid + 256 * u;
@@ -193,7 +232,8 @@ static void launch_compress_to(const CompressArgs& a, dim3 grid, dim3 block, hip
 }
 
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
-  dim3 grid(a.T / a.m, a.B), block(256);
+  // (variable-length chunks: a chunk of T tokens ends at most ceil(T/m) blocks)
+  dim3 grid(a.seq_pos0 ? (a.T + a.m - 1) / a.m : a.T / a.m, a.B), block(256);
   if (a.dtype == F32)
     launch_compress_to<float>(a, grid, block, s);
   else
@@ -393,13 +433,14 @@ __global__ __launch_bounds__(256) void prep_rows_kernel(PrepArgs a) {
   const int c = a.c;
   if (row < nq) {
     const int tq = (int)((row / a.H) % a.T);
-    prep_row_wave(cptr<T>(a.q) + row * c, reinterpret_cast<T*>(a.q_prep) + row * c, c, a.nr, a.nr.g_q,
-                  a.pos0 + tq);
+    const int64_t p0 = a.seq_pos0 ? a.seq_pos0[row / ((int64_t)a.H * a.T)] : a.pos0;
+    prep_row_wave(cptr<T>(a.q) + row * c, reinterpret_cast<T*>(a.q_prep) + row * c, c, a.nr, a.nr.g_q, p0 + tq);
   } else if (row < nq + nw) {
     const int64_t r = row - nq;
     const int j = (int)(r % W);
+    const int64_t p0 = a.seq_pos0 ? a.seq_pos0[r / W] : a.pos0;
     prep_row_wave(cptr<T>(a.win) + r * c, reinterpret_cast<T*>(a.win_prep) + r * c, c, a.nr, a.nr.g_kv,
-                  a.pos0 - (a.n_win - 1) + j);
+                  p0 - (a.n_win - 1) + j);
   }
 }
 
@@ -421,19 +462,33 @@ hipError_t launch_prep_rows(const PrepArgs& a, hipStream_t s) {
 template <typename T>
 __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillStateArgs a) {
   const int b = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
-  const int n_w = a.n_win < (a.n_win - 1 + a.T) ? a.n_win : (a.n_win - 1 + a.T);
-  const int n_t = a.R < a.T ? a.R : a.T;
-  if (row < n_w) {
-    // window row of position p = pos0 + T - n_w + row
-    const int64_t p = a.pos0 + a.T - n_w + row;
-    const int64_t src_row = p - (a.pos0 - (a.n_win - 1));
+  // the sequence's chunk: positions pos0 .. pos0 + len - 1 (variable-length
+  // chunks: its own start and length; rows of the grid past its count exit)
+  int64_t pos0 = a.pos0;
+  int len = a.T;
+  if (a.seq_pos0) {
+    pos0 = a.seq_pos0[b] < 0 ? 0 : a.seq_pos0[b];
+    len = a.seq_len[b] < 0 ? 0 : (a.seq_len[b] > a.T ? a.T : a.seq_len[b]);
+  }
+  const int gw = a.n_win < (a.n_win - 1 + a.T) ? a.n_win : (a.n_win - 1 + a.T);  // grid rows of each part
+  const int gt = a.R < a.T ? a.R : a.T;
+  const int n_w = len == 0 ? 0 : (a.n_win < (a.n_win - 1 + len) ? a.n_win : (a.n_win - 1 + len));
+  const int n_t = a.R < len ? a.R : len;
+  if (row < gw) {
+    if (row >= n_w) return;
+    // window row of position p = pos0 + len - n_w + row (none before the
+    // sequence's start)
+    const int64_t p = pos0 + len - n_w + row;
+    if (p < 0) return;
+    const int64_t src_row = p - (pos0 - (a.n_win - 1));
     const T* src = cptr<T>(a.win) + ((size_t)b * (a.n_win - 1 + a.T) + src_row) * a.c;
     T* dst = reinterpret_cast<T*>(a.win_ring) + ((size_t)b * a.n_win + (size_t)(p % a.n_win)) * a.c;
     for (int r = tid; r < a.c; r += 256) dst[r] = src[r];
-  } else if (row < n_w + n_t) {
-    const int j = row - n_w;
-    const int64_t p = a.pos0 + a.T - n_t + j;
-    const int64_t tok = p - a.pos0;
+  } else if (row < gw + gt) {
+    const int j = row - gw;
+    if (j >= n_t) return;
+    const int64_t p = pos0 + len - n_t + j;
+    const int64_t tok = p - pos0;
     for (int sc = 0; sc < a.S; ++sc) {
       const T* src = cptr<T>(a.streams) + (((size_t)b * a.S + sc) * a.T + tok) * a.c;
       T* dst = reinterpret_cast<T*>(a.tail) + (((size_t)b * a.S + sc) * a.R + (size_t)(p % a.R)) * a.c;
@@ -446,9 +501,33 @@ __global__ __launch_bounds__(256) void prefill_state_kernel(PrefillStateArgs a) 
         for (int r = tid; r < a.d_I; r += 256) dst[r] = src[r];
       }
     }
-  } else if (row == n_w + n_t && tid == 0) {
+  } else if (row == gw + gt && tid == 0 && a.new_entries) {
     a.n_entries[b] += a.new_entries;
   }
+}
+
+// variable-length prefill set-up: one thread per (sequence, row)
+__global__ __launch_bounds__(256) void varlen_setup_kernel(VarlenArgs a) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)a.B * a.T) return;
+  const int b = (int)(i / a.T), tq = (int)(i % a.T);
+  int64_t p0 = a.seq_pos0[b];
+  p0 = p0 < 0 ? 0 : p0;
+  int len = a.seq_len[b];
+  len = len < 0 ? 0 : (len > a.T ? a.T : len);
+  // padding rows ask as the last token (or the chunk's start when empty)
+  a.q_pos[i] = p0 + (tq < len ? tq : (len > 0 ? len - 1 : 0));
+  if (tq == 0) {
+    a.win_pos0[b] = p0 - (a.n_win - 1);
+    int64_t n = (p0 + len) / a.m;
+    a.n_entries[b] = (int32_t)(n < a.E_cap ? n : a.E_cap);
+  }
+}
+
+hipError_t launch_varlen_setup(const VarlenArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.B * a.T;
+  CSA_LAUNCH("varlen_setup", varlen_setup_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill_state(const PrefillStateArgs& a, hipStream_t s) {

@@ -94,6 +94,15 @@ struct CompressArgs {
   size_t prev_seq_stride;  // elements between sequences of prev_cb/prev_zb (0: m*c or m*lw)
   NormRope nr;             // on: entry first + i is prepared at position m * (first + i)
   PageMap pg;              // rows of out / out_scale
+  // variable-length chunks (seq_pos0 non-null; first and prev_* unused):
+  // sequence b's chunk holds positions seq_pos0[b] .. + seq_len[b] - 1 in
+  // rows 0 ..; its entries floor(seq_pos0[b] / m) + blockIdx.x below
+  // floor((seq_pos0[b] + seq_len[b]) / m) (and E_cap) are produced, a source
+  // token p before the chunk read from slot p % R of its stream in tail
+  const int64_t* seq_pos0;
+  const int32_t* seq_len;
+  const void* tail;  // [B][ns][R][c]: ns = 4 (ca, za, cb, zb) with overlap, else 2
+  int R;
 };
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 
@@ -135,6 +144,7 @@ hipError_t launch_fold_append(const FoldArgs& a, hipStream_t s);
 struct PrepArgs {
   int dtype, B, T, H, c, n_win;
   int64_t pos0;
+  const int64_t* seq_pos0;  // [B] or null: per-sequence chunk starts (replace pos0)
   NormRope nr;
   const void* q;
   const void* win;
@@ -155,8 +165,27 @@ struct PrefillStateArgs {
   void* idx_tail;
   int32_t* n_entries;
   int new_entries;
+  // variable-length chunks (replace pos0 and T per sequence; new_entries 0:
+  // the counts were set by launch_varlen_setup)
+  const int64_t* seq_pos0;
+  const int32_t* seq_len;
 };
 hipError_t launch_prefill_state(const PrefillStateArgs& a, hipStream_t s);
+
+// variable-length prefill: each query row's position (row tq of sequence b
+// at seq_pos0[b] + tq, padding rows at the sequence's last position) into
+// q_pos [B][T], the window input's first position into win_pos0 [B], and the
+// entry counts after the chunk, floor((seq_pos0[b] + seq_len[b]) / m) (at
+// most E_cap), into n_entries
+struct VarlenArgs {
+  int B, T, m, n_win, E_cap;
+  const int64_t* seq_pos0;
+  const int32_t* seq_len;
+  int64_t* q_pos;
+  int64_t* win_pos0;
+  int32_t* n_entries;
+};
+hipError_t launch_varlen_setup(const VarlenArgs& a, hipStream_t s);
 
 // ------------------------------------------------------------ indexer + top-k
 struct IndexArgs {

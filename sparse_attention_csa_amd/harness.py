@@ -259,7 +259,11 @@ def decode_io(g, device="cuda"):
 
 
 class PrefillSession:
-    """One prefill chunk of a CSA or HCA layer (all sequences aligned)."""
+    """Prefill chunks of a CSA or HCA layer: the state built from workload g
+    (its cache, entry counts and, with overlap, the previous block's branch-b
+    streams), the first chunk from g's inputs; later chunks (``prefill``) and
+    decode steps (``decode``) continue on the library's own state.  A chunk
+    with ``seq_pos0`` / ``seq_len`` is a variable-length batch."""
 
     def __init__(self, g, device="cuda"):
         self.g = g
@@ -279,12 +283,6 @@ class PrefillSession:
                 src = dev(g[sname], kvk, device)
                 for j in range(m):
                     st.tail[:, si, (pos0 - m + j) % st.R] = src[:, j]
-        streams = ("ca", "za", "cb", "zb")[:st.S]
-        io = {"q": dev(g["q"], kvk, device), "win": dev(g["win"], kvk, device)}
-        io["streams"] = torch.stack([dev(g[s], kvk, device) for s in streams], dim=1)
-        H = g["H"]
-        io["out"] = torch.empty((B, T, H, c), dtype=_KV[kvk], device=device)
-        io["lse"] = torch.empty((B, T, H), dtype=torch.float32, device=device)
         if g["kind"] == "csa":
             idk = g["idx_dtype"]
             st.idx_cache.copy_(dev(g["idx_cache"], idk, device))
@@ -293,25 +291,12 @@ class PrefillSession:
                     src = dev(g[sname], kvk, device)
                     for j in range(m):
                         st.idx_tail[:, si, (pos0 - m + j) % st.R] = src[:, j]
-            io["idx_streams"] = torch.stack([dev(g[s], kvk, device) for s in ("ica", "iza", "icb", "izb")],
-                                            dim=1)
-            io["q_idx"] = dev(g["q_idx"], idk, device)
-            io["q_scale"] = scales_dev(g["q_scale"], idk, device)
             if idk in SCALE_KIND:
                 st.idx_scale.copy_(scales_dev(g["idx_scale"], idk, device))
-            io["w_idx"] = dev(g["w_idx"], "f32", device)
-            io["topk_idx"] = torch.empty((B, T, g["k"]), dtype=torch.int32, device=device)
-            io["topk_cnt"] = torch.empty((B, T), dtype=torch.int32, device=device)
-        self.io = io
+        self.io, self._io_struct = prefill_io(g, device)
         self.pos0, self.T = pos0, T
         self.ws = torch.zeros(max(256, L.hybrid_layer_workspace(self.desc, B, T, E_cap)),
                               dtype=torch.uint8, device=device)
-        s = L.PrefillIO()
-        s.pos0, s.T = pos0, T
-        for name in ("q", "q_idx", "q_scale", "w_idx", "win", "streams", "idx_streams", "out", "lse",
-                     "topk_idx", "topk_cnt"):
-            setattr(s, name, L.ptr(io.get(name)))
-        self._io_struct = s
         if g.get("block_table") is not None:
             st.page_in(g)
         self._state_struct = st.struct()
@@ -320,6 +305,19 @@ class PrefillSession:
     def run(self, stream=None):
         L.hybrid_layer_prefill(self.desc, self._state_struct, self._io_struct, self.ws, stream)
         _after(self.state, stream)
+
+    def prefill(self, g_chunk, stream=None):
+        """Another chunk on the same state, with the per-token inputs of
+        workload ``g_chunk`` (its cache and state fields are not used).
+        Returns the chunk's io tensors."""
+        device = self.state.kv_cache.device
+        io, s = prefill_io(g_chunk, device)
+        ws = torch.zeros(max(256, L.hybrid_layer_workspace(self.desc, self.g["B"], int(g_chunk["T"]),
+                                                             self.g["E_cap"])), dtype=torch.uint8, device=device)
+        L.hybrid_layer_prefill(self.desc, self._state_struct, s, ws, stream)
+        _after(self.state, stream)
+        io["_ws"] = ws
+        return io
 
     def decode(self, g_step, stream=None):
         """Continue the same layer state with one decode step whose per-token
@@ -334,6 +332,36 @@ class PrefillSession:
         L.hybrid_layer_decode(self.desc, self._state_struct, s, self.dec_ws, stream)
         _after(self.state, stream)
         return io
+
+
+def prefill_io(g, device="cuda"):
+    """The inputs and outputs of a prefill chunk of workload ``g`` ([B][T]
+    rows; with ``seq_pos0`` / ``seq_len`` a variable-length batch): a dict of
+    device tensors and the PrefillIO structure pointing at them."""
+    B, c, H, T = g["B"], g["c"], g["H"], int(g["T"])
+    kvk = act_kind(g["kv_dtype"])
+    streams = ("ca", "za", "cb", "zb") if g["overlap"] else ("ca", "za")
+    io = {"q": dev(g["q"], kvk, device), "win": dev(g["win"], kvk, device)}
+    io["streams"] = torch.stack([dev(g[s], kvk, device) for s in streams], dim=1)
+    io["out"] = torch.empty((B, T, H, c), dtype=_KV[kvk], device=device)
+    io["lse"] = torch.empty((B, T, H), dtype=torch.float32, device=device)
+    if g["kind"] == "csa":
+        idk = g["idx_dtype"]
+        io["idx_streams"] = torch.stack([dev(g[s], kvk, device) for s in ("ica", "iza", "icb", "izb")], dim=1)
+        io["q_idx"] = dev(g["q_idx"], idk, device)
+        io["q_scale"] = scales_dev(g["q_scale"], idk, device)
+        io["w_idx"] = dev(g["w_idx"], "f32", device)
+        io["topk_idx"] = torch.empty((B, T, g["k"]), dtype=torch.int32, device=device)
+        io["topk_cnt"] = torch.empty((B, T), dtype=torch.int32, device=device)
+    if g.get("seq_pos0") is not None:
+        io["seq_pos0"] = dev(np.asarray(g["seq_pos0"], np.int64), "i64", device)
+        io["seq_len"] = dev(np.asarray(g["seq_len"], np.int32), "i32", device)
+    s = L.PrefillIO()
+    s.pos0, s.T = int(g["pos0"]), T
+    for name in ("q", "q_idx", "q_scale", "w_idx", "win", "streams", "idx_streams", "out", "lse",
+                 "topk_idx", "topk_cnt", "seq_pos0", "seq_len"):
+        setattr(s, name, L.ptr(io.get(name)))
+    return io, s
 
 
 def _after(st, stream):

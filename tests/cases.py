@@ -157,3 +157,34 @@ def decode_from_prefill(pre, T_done, kv_new, idx_new, t, extra_kv=(), extra_idx=
         g["q_scale"] = None if pre.get("q_scale") is None else pre["q_scale"][sl, hi]
         g["w_idx"] = pre["w_idx"][sl, hi]
     return g
+
+
+def varlen_chunk(full, offs, lens, T):
+    """A variable-length chunk cut from the aligned prefill workload ``full``
+    (whose chunk starts at position full["pos0"]): sequence b's chunk holds
+    full's chunk tokens offs[b] .. offs[b] + lens[b] - 1 (seq_pos0 =
+    pos0 + offs[b], seq_len = lens[b]) in rows 0 .. lens[b] - 1 of [B][T]
+    arrays, the other rows zero; its window rows start n_win - 1 positions
+    before the sequence's chunk."""
+    g = dict(full)
+    B, pos0, n_win = full["B"], int(full["pos0"]), full["n_win"]
+    offs = np.asarray(offs, np.int64)
+    lens = np.asarray(lens, np.int32)
+    g["T"] = T
+    g["seq_pos0"] = pos0 + offs
+    g["seq_len"] = lens
+    for n in ("ca", "za", "cb", "zb", "ica", "iza", "icb", "izb", "q", "q_idx", "w_idx", "q_scale"):
+        x = full.get(n)
+        if x is None:
+            continue
+        out = np.zeros((B, T) + x.shape[2:], x.dtype)
+        for b in range(B):
+            out[b, :lens[b]] = x[b, offs[b]:offs[b] + lens[b]]
+        g[n] = out
+    W = n_win - 1 + T
+    win = np.zeros((B, W) + full["win"].shape[2:], full["win"].dtype)
+    for b in range(B):
+        n = min(W, full["win"].shape[1] - int(offs[b]))
+        win[b, :n] = full["win"][b, offs[b]:offs[b] + n]
+    g["win"] = win
+    return g

@@ -181,3 +181,27 @@ def test_layer_rejects_bad_pages():
     assert st == L.CSA_ERR_ARG and "pos" in L.last_error()
     st = lib.hybrid_layer_prefill(C.byref(d), C.byref(s), C.byref(L.PrefillIO()), None, 0, None)
     assert st == L.CSA_ERR_ARG and "page_entries" not in L.last_error()
+
+
+def test_prefill_chunk_arguments():
+    """Aligned chunks must start and end on block boundaries; per-sequence
+    chunks (seq_pos0 with seq_len) need both arrays.  The checks fail before
+    anything is enqueued (the pointers are never dereferenced)."""
+    lib = L.lib()
+    d = L.LayerDesc(kind=L.CSA_LAYER_HCA, H=64, c=512, m=128, overlap=0, n_win=128, vis=0, kv_dtype=1,
+                    scale=0.044)
+    s = L.LayerState(B=2, E_cap=64)
+    fake = 1 << 20
+    for n in ("kv_cache", "n_entries", "win_ring", "tail"):
+        setattr(s, n, fake)
+    io = L.PrefillIO(pos0=128, T=100)
+    for n in ("q", "win", "streams", "out"):
+        setattr(io, n, fake)
+    st = lib.hybrid_layer_prefill(C.byref(d), C.byref(s), C.byref(io), None, 0, None)
+    assert st == L.CSA_ERR_UNSUPPORTED and "block boundaries" in L.last_error()
+    io.seq_pos0 = fake
+    st = lib.hybrid_layer_prefill(C.byref(d), C.byref(s), C.byref(io), None, 0, None)
+    assert st == L.CSA_ERR_ARG and "seq_len" in L.last_error()
+    io.seq_len = fake
+    st = lib.hybrid_layer_prefill(C.byref(d), C.byref(s), C.byref(io), None, 0, None)
+    assert st == L.CSA_ERR_WORKSPACE  # the chunk itself is accepted
