@@ -435,8 +435,8 @@ int csa_test_set_fused_wait_polls(int polls);
  * attention (HCA) rather than in the separate fold kernel (1, the default)
  * or never (0).  The two paths add the new entry's terms in different
  * orders, so they agree within float32 rounding, not bit for bit; a test
- * that compares two cache layouts of one step bit for bit turns fusion off
- * (a paged cache never fuses).  Returns the previous setting.
+ * that compares the two paths' results bit for bit turns fusion off.
+ * Returns the previous setting.
  * Process-wide; not synchronised with calls in flight on other threads. */
 int csa_test_set_fold_fusion(int on);
 

@@ -204,6 +204,9 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   const int fcs = a.fold_cs, fr0 = split * fcs;
   const int fW = (FOLD && a.fold_mode && hg == 0) ? (a.c - fr0 < 0 ? 0 : (a.c - fr0 < fcs ? a.c - fr0 : fcs)) : 0;
   const bool fold_now = fW > 0 && lim == (int64_t)cnt + 1 && cnt < a.E_cap;
+  // the new entry's cache row (PG: through the block table)
+  size_t frow = (size_t)b * a.E_cap + cnt;
+  if constexpr (PG && FOLD) frow = fold_now ? page_row(a.pg, b, cnt, a.E_cap) : 0;
   const FoldArgs& F = a.fold;
   const int fch = fW / 8;                                  // 16-byte chunks per slice row (bf16)
   char* const fz_l = tiles[kRing - 1];                     // [m][fW] bf16: stream 1 (logits)
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
         for (int g = 1; g < 4; ++g) acc0 = soft_merge_sel(acc0, s_fpart[g][tid]);
         const uint16_t vb = f32_to_bf16(acc0.acc / acc0.l);
         s_fnew[tid] = bf16_to_f32(vb);
-        reinterpret_cast<uint16_t*>(F.kv_cache)[((size_t)b * a.E_cap + cnt) * kC + fr0 + tid] = vb;
+        reinterpret_cast<uint16_t*>(F.kv_cache)[frow * kC + fr0 + tid] = vb;
         a.fold_new[(size_t)b * kC + fr0 + tid] = vb;
       }
       lds_barrier();
@@ -773,10 +776,12 @@ void attend_mfma_plan(int BT, int H, int rows_max, int split_rows, int* n_split,
 // row splits (the merge adds the new entry): the coordinates split into
 // power-of-two slices of 8..64, one per split, every source token of a
 // block handled by one thread of its slice.
+bool attend_mfma_pages_fit(const AttendArgs& a, int rows_max);
+
 bool attend_fuses_fold(AttendArgs& a, const FoldArgs& f) {
   a.fold_mode = 0;
-  if (!a.dense || a.dtype != BF16 || f.dtype != BF16 || a.kv_fmt || f.kv_fmt || a.pg.table ||
-      !attend_mfma_shape_ok(a.H, a.c) ||
+  if (!a.dense || a.dtype != BF16 || f.dtype != BF16 || a.kv_fmt || f.kv_fmt ||
+      !attend_mfma_shape_ok(a.H, a.c) || !attend_mfma_pages_fit(a, a.E_cap + a.n_win) ||
       a.Tq != 1 ||
       a.n_add != 0 || a.win_pos0 != nullptr || a.win_pos0_const != 0 || f.overlap || f.idx_dtype >= 0 ||
       f.B != a.B || f.c != a.c || f.n_win != a.W_cap || f.R < 2 * f.m)
@@ -863,6 +868,8 @@ hipError_t launch_attend_mfma(const AttendArgs& a0, int rows_max, hipStream_t s)
   const long long blocks = (units + 7) / 8 * 8 * n_hg;      // padded to whole XCD rounds
   if (a.pg.table && a.derot_freq)
     CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<1, 0, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+  else if (a.pg.table && a.fold_mode)
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 1, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
   else if (a.pg.table)
     CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 0, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
   else if (a.derot_freq)

@@ -454,6 +454,10 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
     float* s_red = reinterpret_cast<float*>(s_part + 4 * 256);
     uint32_t* s_key = reinterpret_cast<uint32_t*>(s_red + 8);  // the stored new key (<= 256 B)
     const int64_t e = n_have;
+    // the new entry's cache row (PG: through the block table; its load goes
+    // out with the fold's sources)
+    size_t frow = (size_t)b * a.E_cap + e;
+    if constexpr (PG) frow = fold_now ? page_row(a.pg, b, e, a.E_cap) : 0;
     // the new key's score, as the scan computes it: sum_h w_h q_scale_h
     // ReLU(q_h . k), times the key scale (wave 0, lane = head; qv_reg holds
     // the lane's query row when pre, else it is loaded here)
@@ -523,7 +527,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
     // the new indexer key (value iv of coordinate tid < kD) to its storage
     // format, into the cache and s_key; returns its scale (1 for bf16)
     auto store_key = [&](float iv) -> float {
-      const size_t krow = (size_t)b * a.E_cap + e;
+      const size_t krow = frow;
       float ks = 1.f;
       if constexpr (FP4) {
         // blocks of 32 coordinates = lane groups of 32 of waves 0 and 1;
@@ -686,7 +690,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
       const float iv = tid < kD ? fold_coord(iz, ix, ib, kD, Si, tid) : 0.f;
       const float ks = store_key(iv);
       for (int r = tid; r < c; r += 256)
-        reinterpret_cast<uint16_t*>(f.kv_cache)[((size_t)b * a.E_cap + e) * c + r] =
+        reinterpret_cast<uint16_t*>(f.kv_cache)[frow * c + r] =
             f32_to_bf16(fold_coord(mz, mx, mb, kFastFoldC, Sm, r));
       __syncthreads();  // every read of the biases in s_sc is done
       score_new_key(ks, qreg, true);
@@ -704,7 +708,7 @@ __global__ __launch_bounds__(256) void index_score_mfma_kernel(IndexArgs a, Topk
         const int W = f.c - r0 < 256 ? f.c - r0 : 256;
         const float v = fold_job<bf16>(mtail, mio, f.c, r0, W, f.m, f.R, t, e, f.overlap && e > 0, f.bias_a,
                                        f.bias_b, s_part);
-        if (tid < W) reinterpret_cast<uint16_t*>(f.kv_cache)[((size_t)b * a.E_cap + e) * f.c + r0 + tid] = f32_to_bf16(v);
+        if (tid < W) reinterpret_cast<uint16_t*>(f.kv_cache)[frow * f.c + r0 + tid] = f32_to_bf16(v);
       }
     }
     store_appends();
@@ -895,27 +899,33 @@ static int scan_format(int idx_dtype) { return idx_dtype == MXFP4 ? 2 : (idx_dty
 
 // paged keys: a 16-entry tile within one page (>= 16 entries per page) and
 // a wave's run within 64 pages (the run of the scan's grid for E_cap)
-bool index_mfma_pages_fit(const IndexArgs& a) {
+static int resident_of(const IndexArgs& a) {
+  const int fmt = scan_format(a.idx_dtype), HT = a.H_I / 16;
+  if (a.pg.table)
+    return fmt == 2 ? resident_for<2, 1>(HT) : (fmt == 1 ? resident_for<1, 1>(HT) : resident_for<0, 1>(HT));
+  return fmt == 2 ? resident_for<2, 0>(HT) : (fmt == 1 ? resident_for<1, 0>(HT) : resident_for<0, 0>(HT));
+}
+
+// paged keys: a 16-entry tile within one page (>= 16 entries per page) and
+// a wave's run within 64 pages (the run of the scan's grid for E_cap, with
+// or without the fold workgroup)
+static bool pages_fit(const IndexArgs& a, int with_fold) {
   if (!a.pg.table) return true;
   if (a.pg.shift < 4) return false;
-  const int fmt = scan_format(a.idx_dtype);
-  const int resident = fmt == 2 ? resident_for<2, 1>(a.H_I / 16)
-                                : (fmt == 1 ? resident_for<1, 1>(a.H_I / 16) : resident_for<0, 1>(a.H_I / 16));
-  const ScorerPlan p = scorer_plan(a, resident, 1, 1, 0);
-  const int64_t ntile = ((int64_t)a.E_cap + 15) / 16, nwaves = (int64_t)p.per_row * 4;
+  const ScorerPlan p = scorer_plan(a, resident_of(a), 1, 1, with_fold);
+  const int64_t ntile = ((int64_t)a.E_cap + 15) / 16, nwaves = (int64_t)(p.per_row - with_fold) * 4;
   const int64_t per = (ntile + nwaves - 1) / nwaves;
   return ((per * 16) >> a.pg.shift) + 2 <= 64;
 }
 
+bool index_mfma_pages_fit(const IndexArgs& a) { return pages_fit(a, 0); }
+
 bool index_fold_fusable(const IndexArgs& a, const FoldArgs& f, bool split) {
-  if (!split || !index_mfma_supported(a) || a.Tq != 1 || f.B != a.B || f.dtype != BF16 || f.kv_fmt || a.pg.table ||
+  if (!split || !index_mfma_supported(a) || a.Tq != 1 || f.B != a.B || f.dtype != BF16 || f.kv_fmt ||
       f.idx_dtype != a.idx_dtype ||
-      f.d_I != kD || a.n_add != 0)
+      f.d_I != kD || a.n_add != 0 || !pages_fit(a, 1))
     return false;
-  const int fmt = scan_format(a.idx_dtype);
-  const int resident = fmt == 2 ? resident_for<2, 0>(a.H_I / 16)
-                                : (fmt == 1 ? resident_for<1, 0>(a.H_I / 16) : resident_for<0, 0>(a.H_I / 16));
-  return scorer_plan(a, resident, 1, 1, 1).fuse != 0;
+  return scorer_plan(a, resident_of(a), 1, 1, 1).fuse != 0;
 }
 
 template <int FMT, int PG>
