@@ -188,6 +188,7 @@ bool attend_mfma_shape_ok(int H, int c);
 size_t attend_mfma_ws_bytes(int BT, int H, int rows_max, int split_rows);
 hipError_t launch_attend_mfma(const AttendArgs& a, int rows_max, hipStream_t s);
 bool attend_mfma_pages_fit(const AttendArgs& a, int rows_max);
+bool attend_mfma_sparse_fits(const AttendArgs& a, int rows_max);
 bool attend_rows_shape_ok(int H, int c);
 void attend_rows_plan(int BT, int H, int rows_max, int split_rows, int* n_split, int* rows_per_split);
 hipError_t launch_attend_rows(const AttendArgs& a, int rows_max, hipStream_t s);
@@ -226,6 +227,9 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.dtype == BF16 && !a.kv_fmt && a.dense && attend_mfma_shape_ok(a.H, a.c) &&
       attend_mfma_pages_fit(a, a.E_cap + a.n_win))
     return launch_attend_mfma(a, a.E_cap + a.n_win, s);
+  if (a.dtype == BF16 && !a.kv_fmt && !a.dense && attend_mfma_shape_ok(a.H, a.c) &&
+      attend_mfma_sparse_fits(a, a.k + a.n_win))
+    return launch_attend_mfma(a, a.k + a.n_win, s);
   if (a.dtype == BF16 && !a.kv_fmt && !a.dense && attend_rows_shape_ok(a.H, a.c))
     return launch_attend_rows(a, a.k + a.n_win, s);
   dim3 grid(a.B * a.Tq, (a.H + kHG - 1) / kHG), block(256);

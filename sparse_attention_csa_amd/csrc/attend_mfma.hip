@@ -70,13 +70,18 @@ constexpr int kPgSplit = 2048;         // paged cache: page ids of one split's r
 // split) are blocks L, L + 8, ... so they share that XCD's L2.
 // DEROT: the output's rotary coordinates are rotated back by the query
 // position (norm_rope); FOLD: the decode fold runs inside (fold_mode); PG:
-// the cache is paged (the split's page ids are read into LDS first).
-// Separate instantiations keep the code of one out of the others' register
+// the cache is paged (the split's page ids are read into LDS first); SP:
+// the compressed rows are a query's selected entries (sparse attention over
+// a top-k list: the split's cache rows are read into LDS first, so the 64
+// heads of a workgroup share one gather of each row).  Separate
+// instantiations keep the code of one out of the others' register
 // allocation (the row loop's schedule depends on it).
-template <int DEROT, int FOLD, int PG>
+template <int DEROT, int FOLD, int PG, int SP>
 __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n_split, int rows_per_split) {
   __shared__ __attribute__((aligned(1024))) char tiles[kRing][kTN * kRowB];
-  __shared__ int32_t s_pg[PG ? kPgSplit : 1];  // PG: page ids of the split's cache rows
+  // PG: page ids of the split's cache rows; SP: the split's selected
+  // entries' cache rows (-1: an id outside the cache, masked)
+  __shared__ int32_t s_pg[(PG || SP) ? kPgSplit : 1];
   __shared__ uint32_t rvalid[kRing][kTN / 4];  // byte r % 4 of word r / 4: row r is a real row
   __shared__ int s_restart;                // a wavefront asks the split to be recomputed
   __shared__ bf16x8_t s_p[2][4][64];       // P^T operands of a tile (two buffers), one block of 16 heads per wavefront
@@ -109,7 +114,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   const int64_t* dummy64 = reinterpret_cast<const int64_t*>(a.kv);
   const int64_t t_ld = (a.q_pos ? a.q_pos + qrow : dummy64)[0];
   const int64_t w_ld = (a.win_pos0 ? a.win_pos0 + b : dummy64)[0];
-  const int32_t cnt = a.n_entries[b];
+  const int32_t cnt = SP ? a.topk_cnt[qrow] : a.n_entries[b];
   // row range of the split: with the fold inside, the first fold_nsplit
   // splits (the ones that fold) take fold_rows rows each, the rest
   // rows_per_split, so that the fold's time is balanced by fewer rows
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     uint32_t lds0 = lds_addr(tiles[buf]) + kRowsPerWave * w * kRowB;
     // (PG: the page-id reads before it leave the compiler unsure that the
     // slot address is uniform; it is)
-    if constexpr (PG) lds0 = __builtin_amdgcn_readfirstlane(lds0);
+    if constexpr (PG || SP) lds0 = __builtin_amdgcn_readfirstlane(lds0);
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       // (readlane returns int: widen through uint32_t, no sign extension)
@@ -145,7 +150,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   // speculative: the first tile read as cache entries (in the cache
   // buffer, so in bounds whatever the count turns out to be), before
   // anything else
-  const bool spec = !PG && r_begin + kTN <= a.E_cap;
+  const bool spec = !PG && !SP && r_begin + kTN <= a.E_cap;
   if (spec) dma_rows(kv + (size_t)(r_begin + kRowsPerWave * w + (l & (kRowsPerWave - 1))) * kC, 0);
   // Q^T operands for this wavefront's 16 heads: lane (head li, d group lg).
   // They are requested after the first tile's DMAs and before the
@@ -167,6 +172,7 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   int64_t n_c = lim < have ? lim : have;
   if (n_c > a.E_cap) n_c = a.E_cap;
   if (n_c < 0) n_c = 0;
+  if constexpr (SP) n_c = cnt < 0 ? 0 : (cnt > a.k ? a.k : cnt);  // the selection (visible entries only)
   const int64_t n_w = (t + 1) < a.n_win ? (t + 1) : a.n_win;
   // fold_mode: the query's own token is not in the window ring yet; the
   // merge adds it as a row of its own
@@ -255,8 +261,22 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
 
   if (tid == 0) s_restart = 0;
   // PG: page ids of the split's cache rows [r_begin, min(r_end, n_c))
-  const int sh = a.pg.shift, p_first = r_begin >> sh;
-  if constexpr (PG) {
+  const int sh = a.pg.shift, p_first = SP ? 0 : r_begin >> sh;
+  if constexpr (SP) {
+    // the selected entries of rows [r_begin, min(r_end, n_c)): their cache
+    // rows (paged: through the block table, a second round of loads)
+    const int ce = r_end < nc32 ? r_end : nc32;
+    const int32_t* ids = a.topk_idx + (size_t)qrow * a.k;
+    for (int i0 = r_begin; i0 < ce; i0 += 256) {  // (a uniform loop)
+      const int j = i0 + tid;
+      if (j < ce) {
+        const int32_t id = ids[j];
+        int32_t row = -1;
+        if (id >= 0 && id < a.E_cap) row = PG ? (int32_t)page_row(a.pg, b, id, a.E_cap) : id;
+        s_pg[j - r_begin] = row;
+      }
+    }
+  } else if constexpr (PG) {
     const int ce = r_end < nc32 ? r_end : nc32;
     if (r_begin < ce) {
       const int np = ((ce - 1) >> sh) - p_first + 1;  // <= kPgSplit (checked at launch)
@@ -273,16 +293,27 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
     int wr = wbase + (j - nc32);
     wr = wr >= wcap ? wr - wcap : wr;
     size_t cr = (size_t)j;  // the cache row of entry j
-    if constexpr (PG) {
+    bool ok = true;         // SP: a selected id inside the cache
+    if constexpr (SP) {
+      int pi = j - r_begin;
+      pi = pi < 0 ? 0 : (pi >= kPgSplit ? kPgSplit - 1 : pi);  // (rows that are not entries)
+      const int32_t r = s_pg[pi];
+      ok = r >= 0;
+      cr = (size_t)(uint32_t)(ok ? r : 0);
+    } else if constexpr (PG) {
       int pi = (j >> sh) - p_first;
       pi = pi < 0 ? 0 : (pi >= kPgSplit ? kPgSplit - 1 : pi);  // (rows that are not entries)
       cr = ((size_t)(uint32_t)s_pg[pi] << sh) + (size_t)(j & ((1 << sh) - 1));
     }
-    return j < r_end ? (j < nc32 ? kv + cr * kC : win + (size_t)wr * kC) : pad_row;
+    return j < r_end ? (j < nc32 ? (ok ? kv + cr * kC : pad_row) : win + (size_t)wr * kC) : pad_row;
   };
   auto set_valid = [&](int r0, int buf) {
     const int j = r0 + kRowsPerWave * w + (l & (kRowsPerWave - 1));
-    const uint64_t okb = __builtin_amdgcn_ballot_w64(j < r_end);
+    bool okr = j < r_end;
+    if constexpr (SP) {  // (an id outside the cache: a masked row)
+      if (okr && j < nc32) okr = s_pg[j - r_begin] >= 0;
+    }
+    const uint64_t okb = __builtin_amdgcn_ballot_w64(okr);
     if (l == 0) {  // byte r % 4 of word r / 4: rows kRowsPerWave * w + i
       rvalid[buf][2 * w] = spread4((uint32_t)okb & 15u);
       rvalid[buf][2 * w + 1] = spread4((uint32_t)(okb >> 4) & 15u);
@@ -843,6 +874,17 @@ bool attend_mfma_pages_fit(const AttendArgs& a, int rows_max) {
   return ((rps - 1) >> a.pg.shift) + 2 <= kPgSplit;
 }
 
+// sparse rows on the 64-head kernel: for batches of many queries (the plan
+// cuts no query's rows, so each selected row is gathered once per query and
+// 64 heads), when a split's rows fit the LDS table.  Fewer queries (decode)
+// go to the 16-head gather kernel, whose row splits fill the device.
+bool attend_mfma_sparse_fits(const AttendArgs& a, int rows_max) {
+  if (a.B * a.Tq * (a.H / kHW) < 256) return false;
+  int ns, rps;
+  attend_mfma_plan(a.B * a.Tq, a.H, rows_max, a.split_rows, &ns, &rps);
+  return rps <= kPgSplit;
+}
+
 hipError_t launch_attend_mfma(const AttendArgs& a0, int rows_max, hipStream_t s) {
   int ns, rps;
   attend_mfma_plan(a0.B * a0.Tq, a0.H, rows_max, a0.split_rows, &ns, &rps);
@@ -866,18 +908,28 @@ hipError_t launch_attend_mfma(const AttendArgs& a0, int rows_max, hipStream_t s)
   const int n_hg = a.H / kHW;
   const long long units = (long long)ns * a.B * a.Tq;       // (query, split) pairs
   const long long blocks = (units + 7) / 8 * 8 * n_hg;      // padded to whole XCD rounds
-  if (a.pg.table && a.derot_freq)
-    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<1, 0, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+  const dim3 grid((unsigned)blocks), blk(256);
+  if (!a.dense) {  // the sparse rows of a selection (prefill-shaped batches)
+    if (a.pg.table && a.derot_freq)
+      CSA_LAUNCH("attend_sparse_mfma", (attend_mfma_kernel<1, 0, 1, 1>), grid, blk, 0, s, a, ns, rps);
+    else if (a.pg.table)
+      CSA_LAUNCH("attend_sparse_mfma", (attend_mfma_kernel<0, 0, 1, 1>), grid, blk, 0, s, a, ns, rps);
+    else if (a.derot_freq)
+      CSA_LAUNCH("attend_sparse_mfma", (attend_mfma_kernel<1, 0, 0, 1>), grid, blk, 0, s, a, ns, rps);
+    else
+      CSA_LAUNCH("attend_sparse_mfma", (attend_mfma_kernel<0, 0, 0, 1>), grid, blk, 0, s, a, ns, rps);
+  } else if (a.pg.table && a.derot_freq)
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<1, 0, 1, 0>), grid, blk, 0, s, a, ns, rps);
   else if (a.pg.table && a.fold_mode)
-    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 1, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 1, 1, 0>), grid, blk, 0, s, a, ns, rps);
   else if (a.pg.table)
-    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 0, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 0, 1, 0>), grid, blk, 0, s, a, ns, rps);
   else if (a.derot_freq)
-    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<1, 0, 0>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<1, 0, 0, 0>), grid, blk, 0, s, a, ns, rps);
   else if (a.fold_mode)
-    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 1, 0>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 1, 0, 0>), grid, blk, 0, s, a, ns, rps);
   else
-    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 0, 0>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
+    CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 0, 0, 0>), grid, blk, 0, s, a, ns, rps);
   if (ns > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -96,6 +96,24 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
   int nv = 0;
   for (int r = tid; r < c; r += 256, ++nv) {
     Soft s{-INFINITY, 0.f, 0.f};
+    // the m sources of a branch in batches whose loads are in flight
+    // together (the online softmax takes them in source order; loads past
+    // the last source re-read it and are dropped)
+    constexpr int kSrcB = 8;
+    auto push_branch = [&](auto logit_of, auto value_of) {
+      for (int j0 = 0; j0 < m; j0 += kSrcB) {
+        float lgs[kSrcB], vs[kSrcB];
+#pragma unroll
+        for (int u = 0; u < kSrcB; ++u) {
+          const int j = j0 + u < m ? j0 + u : m - 1;
+          lgs[u] = logit_of(j);
+          vs[u] = value_of(j);
+        }
+#pragma unroll
+        for (int u = 0; u < kSrcB; ++u)
+          if (j0 + u < m) soft_push(s, lgs[u], vs[u]);
+      }
+    };
     if (a.seq_pos0) {
       // stream st (0 content a, 1 logits a, 2 content b, 3 logits b) at
       // position p (logit width c)
@@ -103,47 +121,31 @@ __global__ __launch_bounds__(256) void compress_chunk_kernel(CompressArgs a) {
         const T* ch = st == 0 ? ca : (st == 1 ? za : (st == 2 ? cb : zb));
         return p >= vp0 ? ch + (size_t)(p - vp0) * c : vtail + ((size_t)st * a.R + (size_t)(p % a.R)) * c;
       };
-      for (int j = 0; j < m; ++j) {
-        const int64_t p = (int64_t)m * e + j;
-        float lg = ld(row(1, p), r);
-        if (a.bias_a) lg += a.bias_a[j * c + r];
-        soft_push(s, lg, ld(row(0, p), r));
-      }
-      if (has_b) {
-        for (int j = 0; j < m; ++j) {
-          const int64_t p = (int64_t)m * (e - 1) + j;
-          float lg = ld(row(3, p), r);
-          if (a.bias_b) lg += a.bias_b[j * c + r];
-          soft_push(s, lg, ld(row(2, p), r));
-        }
-      }
+      const int64_t pa = (int64_t)m * e, pb = (int64_t)m * (e - 1);
+      push_branch([&](int j) { return ld(row(1, pa + j), r) + (a.bias_a ? a.bias_a[j * c + r] : 0.f); },
+                  [&](int j) { return ld(row(0, pa + j), r); });
+      if (has_b)
+        push_branch([&](int j) { return ld(row(3, pb + j), r) + (a.bias_b ? a.bias_b[j * c + r] : 0.f); },
+                    [&](int j) { return ld(row(2, pb + j), r); });
       vals[nv] = s.acc / s.l;
       continue;
     }
-    for (int j = 0; j < m; ++j) {
-      const int tok = m * i + j;
-      float lg;
-      if (a.score_w)
-        lg = s_logit[j];
-      else
-        lg = ld(za, (size_t)tok * lw + (lw == 1 ? 0 : r));
-      if (a.bias_a) lg += a.bias_a[j * c + r];
-      soft_push(s, lg, ld(ca, (size_t)tok * c + r));
-    }
+    push_branch(
+        [&](int j) {
+          const int tok = m * i + j;
+          const float lg = a.score_w ? s_logit[j] : ld(za, (size_t)tok * lw + (lw == 1 ? 0 : r));
+          return lg + (a.bias_a ? a.bias_a[j * c + r] : 0.f);
+        },
+        [&](int j) { return ld(ca, (size_t)(m * i + j) * c + r); });
     if (has_b) {
-      for (int j = 0; j < m; ++j) {
-        float lg, v;
-        if (i > 0) {
-          const int tok = m * (i - 1) + j;
-          lg = ld(zb, (size_t)tok * lw + (lw == 1 ? 0 : r));
-          v = ld(cb, (size_t)tok * c + r);
-        } else {
-          lg = ld(pzb, (size_t)j * lw + (lw == 1 ? 0 : r));
-          v = ld(pcb, (size_t)j * c + r);
-        }
-        if (a.bias_b) lg += a.bias_b[j * c + r];
-        soft_push(s, lg, v);
-      }
+      // the previous block: in the chunk, or (first entry) in prev_*
+      const T* zsrc = i > 0 ? zb + (size_t)m * (i - 1) * lw : pzb;
+      const T* csrc = i > 0 ? cb + (size_t)m * (i - 1) * c : pcb;
+      push_branch(
+          [&](int j) {
+            return ld(zsrc, (size_t)j * lw + (lw == 1 ? 0 : r)) + (a.bias_b ? a.bias_b[j * c + r] : 0.f);
+          },
+          [&](int j) { return ld(csrc, (size_t)j * c + r); });
     }
     vals[nv] = s.acc / s.l;
   }
