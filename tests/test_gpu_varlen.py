@@ -30,8 +30,12 @@ def _pad4(n):
     return max(4, -(-int(n) // 4) * 4)
 
 
-@pytest.mark.parametrize("kind", ["csa", "hca"])
-def test_two_varlen_chunks_then_decode(gpu_lib, kind):
+@pytest.mark.parametrize("kind,variant", [("csa", None), ("hca", None), ("csa", "norm_rope"), ("hca", "norm_rope"),
+                                          ("csa", "paged"), ("hca", "paged")])
+def test_two_varlen_chunks_then_decode(gpu_lib, kind, variant):
+    """variant: norm_rope (queries, window rows and entries prepared at
+    each sequence's own positions) or paged (the state's caches in pages of
+    one 128-token unit)."""
     from sparse_attention_csa_amd.harness import PrefillSession
     from tests.test_gpu_continuation import _stack_steps
     B, n0, steps = 3, 1024, 12
@@ -42,12 +46,16 @@ def test_two_varlen_chunks_then_decode(gpu_lib, kind):
     Ttot = -(-(max(a + b for a, b in zip(L1, L2)) + steps) // 128) * 128  # (the aligned chunk: whole blocks)
     a, h = workloads.flash_prefill(seed=171, B=B, T=Ttot, n0=n0, H=64, c=512, H_I=64, d_I=128, k=128)
     full = a if kind == "csa" else h
+    if variant == "norm_rope":
+        full = workloads.with_norm_rope(full, seed=172)
     m = full["m"]
-    label = f"varlen-{kind}"
+    label = f"varlen-{kind}-{variant}"
     kv_full, idx_full = zip(*[OL.prefill_entries(full, b) for b in range(B)])
     E0 = int(full["n_entries"][0])
 
     c1 = varlen_chunk(full, [0] * B, L1, _pad4(max(L1)))
+    if variant == "paged":
+        c1 = workloads.with_pages(c1, 32 if kind == "csa" else 1, seed=173)
     sess = PrefillSession(c1)
     sess.run()
     io1 = sess.io
