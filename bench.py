@@ -15,7 +15,7 @@ steps, outside the timed events) and cycles through --rotate independent copies
 of the state so that the working set exceeds the 256 MiB MALL.
 
 Prints one JSON line.  Other workloads: --workload flash_csa_128k |
-flash_hca_1m | pro_csa_1m | pro_csa_1m_mxfp4 | decode_1m_paged | prefill.
+flash_hca_1m | pro_csa_1m | pro_csa_1m_mxfp4 | decode_1m_norm_rope | decode_1m_paged | prefill.
 """
 
 import argparse
@@ -48,6 +48,12 @@ def build_cases(name):
     if name == "pro_csa_1m_mxfp4":
         # the pages' FP4 indexer path: MXFP4 queries and keys, bf16 scores
         return [("pro_csa_1m_mxfp4", workloads.pro_csa_decode(idx_dtype="mxfp4", score_dtype="bf16"))]
+    if name == "decode_1m_norm_rope":
+        # the default step with the steps on either side of the core
+        # attention: RMSNorm and rotary positions of queries and produced KV,
+        # the output rotated back
+        return [("pro_csa_1m_norm_rope", workloads.with_norm_rope(workloads.pro_csa_decode())),
+                ("flash_hca_1m_norm_rope", workloads.with_norm_rope(workloads.flash_hca_decode()))]
     if name == "decode_1m_paged":
         # the default step with the compressed caches in 128-token pages
         # (32 CSA entries, one HCA entry per page), pages in random order

@@ -363,10 +363,15 @@ static size_t varlen_bytes(int B, int T) {
   return align_up((size_t)B * T * sizeof(int64_t)) + align_up((size_t)B * sizeof(int64_t));
 }
 
+// the decode fold's whole-entry staging (norm_rope / FP8BF16): [B][c] fp32
+static size_t fold_buf_bytes(const csa_layer_desc* d, int B) {
+  return (d->norm_rope || d->kv_dtype == CSA_FP8BF16) ? align_up((size_t)B * d->c * sizeof(float)) : 0;
+}
+
 size_t hybrid_layer_workspace(const csa_layer_desc* d, int B, int T, int E_cap) {
   if (!d || B < 1 || T < 1 || E_cap < 1) return 0;
   size_t bytes = align_up((size_t)B * sizeof(int32_t)) + prep_q_bytes(d, B, T) + prep_win_bytes(d, B, T) +
-                 varlen_bytes(B, T);
+                 varlen_bytes(B, T) + fold_buf_bytes(d, B);
   size_t rows = (size_t)E_cap + d->n_win;
   if (d->kind == CSA_LAYER_CSA) {
     bytes += align_up(csa::index_topk_ws_bytes(B, T, E_cap, d->k));
@@ -416,9 +421,12 @@ csa_status hybrid_layer_decode(const csa_layer_desc* d, csa_layer_state* s, cons
   w += align_up((size_t)B * sizeof(int32_t));
   void* q_prep = w;  // norm_rope
   w += prep_q_bytes(d, B, 1) + prep_win_bytes(d, B, 1);
+  float* fold_buf = (float*)w;  // norm_rope / FP8BF16: the fold's whole-entry staging
+  w += fold_buf_bytes(d, B);
 
   csa::FoldArgs f{};
   f.counters = fold_counters;
+  f.fold_buf = fold_buf;
   f.dtype = act_dtype(d); f.idx_dtype = is_csa ? d->idx_dtype : -1;
   f.kv_fmt = d->kv_dtype == CSA_FP8BF16; f.kv_scale = s->kv_scale;
   f.B = B; f.c = d->c; f.d_I = d->d_I; f.m = d->m; f.R = tail_depth(d); f.n_win = d->n_win;

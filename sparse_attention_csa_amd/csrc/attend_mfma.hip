@@ -788,6 +788,10 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
             (frow > 0 ? w_new * nv : 0.f) + w_own * xv) *
            inv;
   }
+  if (a.derot_freq) {  // norm_rope: the rotary pairs of the lane's 8 coordinates rotated back by t
+    const int64_t t = a.q_pos ? a.q_pos[qrow] : a.q_pos0 + qrow % a.Tq;
+    rope_pairs<8>(o, 8, 8 * l, kC, a.rope_dims, a.derot_freq, -t);
+  }
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * H + h) * kC + 8 * l;
   uint4 r;
   r.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
@@ -909,22 +913,25 @@ hipError_t launch_attend_mfma(const AttendArgs& a0, int rows_max, hipStream_t s)
   const long long units = (long long)ns * a.B * a.Tq;       // (query, split) pairs
   const long long blocks = (units + 7) / 8 * 8 * n_hg;      // padded to whole XCD rounds
   const dim3 grid((unsigned)blocks), blk(256);
+  // norm_rope: with row splits the merge rotates the output back (the
+  // kernel's de-rotating form has a slower register allocation)
+  const bool derot = a.derot_freq && ns == 1;
   if (!a.dense) {  // the sparse rows of a selection (prefill-shaped batches)
-    if (a.pg.table && a.derot_freq)
+    if (a.pg.table && derot)
       CSA_LAUNCH("attend_sparse_mfma", (attend_mfma_kernel<1, 0, 1, 1>), grid, blk, 0, s, a, ns, rps);
     else if (a.pg.table)
       CSA_LAUNCH("attend_sparse_mfma", (attend_mfma_kernel<0, 0, 1, 1>), grid, blk, 0, s, a, ns, rps);
-    else if (a.derot_freq)
+    else if (derot)
       CSA_LAUNCH("attend_sparse_mfma", (attend_mfma_kernel<1, 0, 0, 1>), grid, blk, 0, s, a, ns, rps);
     else
       CSA_LAUNCH("attend_sparse_mfma", (attend_mfma_kernel<0, 0, 0, 1>), grid, blk, 0, s, a, ns, rps);
-  } else if (a.pg.table && a.derot_freq)
+  } else if (a.pg.table && derot)
     CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<1, 0, 1, 0>), grid, blk, 0, s, a, ns, rps);
   else if (a.pg.table && a.fold_mode)
     CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 1, 1, 0>), grid, blk, 0, s, a, ns, rps);
   else if (a.pg.table)
     CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 0, 1, 0>), grid, blk, 0, s, a, ns, rps);
-  else if (a.derot_freq)
+  else if (derot)
     CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<1, 0, 0, 0>), grid, blk, 0, s, a, ns, rps);
   else if (a.fold_mode)
     CSA_LAUNCH("attend_dense_mfma", (attend_mfma_kernel<0, 1, 0, 0>), grid, blk, 0, s, a, ns, rps);
@@ -980,12 +987,18 @@ __global__ __launch_bounds__(256) void attend_merge_small_kernel(AttendArgs a, i
   }
   const float den = wave_sum(wgt) + (z2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(z2 - M));
   const float inv = __builtin_amdgcn_rcpf(den);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] *= inv;
+  if (a.derot_freq) {  // norm_rope: the rotary pairs of the lane's 8 coordinates rotated back by t
+    const int64_t t = a.q_pos ? a.q_pos[qrow] : a.q_pos0 + qrow % a.Tq;
+    rope_pairs<8>(o, 8, 8 * l, kC, a.rope_dims, a.derot_freq, -t);
+  }
   uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + ((size_t)qrow * H + h) * kC + 8 * l;
   uint4 r;
-  r.x = (uint32_t)f32_to_bf16(o[0] * inv) | ((uint32_t)f32_to_bf16(o[1] * inv) << 16);
-  r.y = (uint32_t)f32_to_bf16(o[2] * inv) | ((uint32_t)f32_to_bf16(o[3] * inv) << 16);
-  r.z = (uint32_t)f32_to_bf16(o[4] * inv) | ((uint32_t)f32_to_bf16(o[5] * inv) << 16);
-  r.w = (uint32_t)f32_to_bf16(o[6] * inv) | ((uint32_t)f32_to_bf16(o[7] * inv) << 16);
+  r.x = (uint32_t)f32_to_bf16(o[0]) | ((uint32_t)f32_to_bf16(o[1]) << 16);
+  r.y = (uint32_t)f32_to_bf16(o[2]) | ((uint32_t)f32_to_bf16(o[3]) << 16);
+  r.z = (uint32_t)f32_to_bf16(o[4]) | ((uint32_t)f32_to_bf16(o[5]) << 16);
+  r.w = (uint32_t)f32_to_bf16(o[6]) | ((uint32_t)f32_to_bf16(o[7]) << 16);
   *reinterpret_cast<uint4*>(out) = r;
   if (a.lse && l == 0) a.lse[(size_t)qrow * H + h] = (M + log2f(den)) * kLn2;
 }

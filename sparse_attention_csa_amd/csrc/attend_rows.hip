@@ -425,11 +425,13 @@ hipError_t launch_attend_rows(const AttendArgs& a, int rows_max, hipStream_t s) 
   const int n_hg = a.H / 16;
   const long long units = (long long)ns * a.B * a.Tq;   // (query, split) pairs
   const long long blocks = (units + 7) / 8 * 8 * n_hg;  // padded to whole XCD rounds
-  if (a.pg.table && a.derot_freq)
+  // norm_rope: with row splits the merge rotates the output back
+  const bool derot = a.derot_freq && ns == 1;
+  if (a.pg.table && derot)
     CSA_LAUNCH("attend_sparse_rows", (attend_rows_kernel<1, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
   else if (a.pg.table)
     CSA_LAUNCH("attend_sparse_rows", (attend_rows_kernel<0, 1>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
-  else if (a.derot_freq)
+  else if (derot)
     CSA_LAUNCH("attend_sparse_rows", (attend_rows_kernel<1, 0>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);
   else
     CSA_LAUNCH("attend_sparse_rows", (attend_rows_kernel<0, 0>), dim3((unsigned)blocks), dim3(256), 0, s, a, ns, rps);

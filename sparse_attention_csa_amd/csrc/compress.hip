@@ -278,56 +278,40 @@ __global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
   const int nstr = a.overlap ? 4 : 2;
   const int slot = (int)(t % R);
   const bool has_idx = a.idx_dtype >= 0;
-  const bool whole = a.nr.on || a.kv_fmt;  // one workgroup folds the whole entry
-  const int main_jobs = whole ? 1 : c / kFoldCW;
+  // whole: the entry's epilogue needs all of it (norm_rope: RMSNorm and the
+  // rotary pairs; the 576-byte entry: the scale of its e4m3 part).  The
+  // coordinate slices are folded in parallel as always and parked in
+  // fold_buf; the last workgroup of the sequence finishes and stores the
+  // entry.
+  const bool whole = a.nr.on || a.kv_fmt;
+  const int main_jobs = c / kFoldCW;
+  __shared__ int s_last;
 
-  if (whole && job == 0) {
-    // the whole main entry (norm_rope: prepared, RMSNorm then rotary pairs
-    // at its position m e; stored as T or as the 576-byte entry), the main
-    // streams' appends and the new window row (prepared at t with norm_rope)
+  if (whole && job < main_jobs) {
+    const int r0 = job * kFoldCW;
     T* tail = reinterpret_cast<T*>(a.tail) + (size_t)b * nstr * R * c;
     const T* io = reinterpret_cast<const T*>(a.streams) + (size_t)b * nstr * c;
-    if (fold) {
-      const int nu = (c + 255) / 256;
-      float val[2] = {0.f, 0.f};
-      for (int u = 0; u < nu; ++u) {
-        const int r0 = 256 * u, W = c - r0 < 256 ? c - r0 : 256;
-        val[u] = fold_job<T>(tail, io, c, r0, W, m, R, t, e, a.overlap && e > 0, a.bias_a, a.bias_b, s_part);
-      }
-      if (a.nr.on) {
-        float ss = 0.f;
-        for (int u = 0; u < nu; ++u)
-          if (256 * u + tid < c) ss += val[u] * val[u];
-        ss = wave_sum(ss);
-        if ((tid & 63) == 0) s_red[tid >> 6] = ss;
-        __syncthreads();
-        ss = s_red[0] + s_red[1] + s_red[2] + s_red[3];
-        const float inv = 1.0f / sqrtf(ss / (float)c + a.nr.eps);
-        const int Rd = a.nr.rope_dims;
-        for (int u = 0; u < nu; ++u) {
-          const int r = 256 * u + tid;
-          float v = r < c ? val[u] * inv * a.nr.g_kv[r] : 0.f;
-          const float other = __shfl_xor(v, 1, 64);
-          if (r < c && r >= c - Rd) {
-            float cs, sn;
-            rope_cs((int64_t)m * e, a.nr.inv_freq[(r - (c - Rd)) >> 1], &cs, &sn);
-            v = (r & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
-          }
-          val[u] = v;
-        }
-      }
-      store_entry<T>(val, nu, c, a.kv_fmt, a.kv_cache, a.kv_scale, erow, s_red);
-    }
-    for (int i = tid; i < nstr * c; i += kFoldT) {
-      const int sc = i / c, r = i % c;
+    // the new token's appends first (the fold never reads its slot), so
+    // their loads overlap the fold's
+    for (int i = tid; i < nstr * kFoldCW; i += kFoldT) {
+      const int sc = i / kFoldCW, r = r0 + i % kFoldCW;
       tail[((size_t)sc * R + slot) * c + r] = io[(size_t)sc * c + r];
     }
+    if (fold) {
+      const float val = fold_job<T>(tail, io, c, r0, kFoldCW, m, R, t, e, a.overlap && e > 0, a.bias_a,
+                                    a.bias_b, s_part);
+      // (device-coherent stores: the last workgroup reads them)
+      if (tid < kFoldCW)
+        __hip_atomic_store(a.fold_buf + (size_t)b * c + r0 + tid, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // the new window row (prepared at t with norm_rope: one wavefront, the
+    // whole row)
     T* ring = reinterpret_cast<T*>(a.win_ring) + ((size_t)b * a.n_win + (size_t)(t % a.n_win)) * c;
     const T* xn = reinterpret_cast<const T*>(a.x_new) + (size_t)b * c;
     if (a.nr.on) {
-      if (tid < 64) prep_row_wave(xn, ring, c, a.nr, a.nr.g_kv, t);
-    } else {
-      for (int r = tid; r < c; r += kFoldT) ring[r] = xn[r];
+      if (job == 0 && tid < 64) prep_row_wave(xn, ring, c, a.nr, a.nr.g_kv, t);
+    } else if (tid < kFoldCW) {
+      ring[r0 + tid] = xn[r0 + tid];
     }
   } else if (job >= main_jobs + (has_idx ? 1 : 0)) {
     // the step's queries, prepared at t: one head per wavefront
@@ -385,15 +369,50 @@ __global__ __launch_bounds__(kFoldT) void fold_append_kernel(FoldArgs a) {
       itail[((size_t)sc * R + slot) * d + r] = iio[(size_t)sc * d + r];
     }
   }
-  // the last workgroup of the sequence publishes the count; every
-  // workgroup's read of n_entries[b] completed before its increment
+  // the last workgroup of the sequence finishes a whole entry and publishes
+  // the count; every workgroup's read of n_entries[b], and its fold_buf
+  // stores, completed before its increment
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (tid == 0) {
-    const int done = atomicAdd(&a.counters[b], 1);
-    if (done == (int)gridDim.x - 1) {
-      a.counters[b] = 0;
-      if (fold) a.n_entries[b] = n_have + 1;
+  if (tid == 0) s_last = atomicAdd(&a.counters[b], 1) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  if (whole && fold) {
+    const int nu = (c + 255) / 256;  // the same trip count in every lane
+    float val[2] = {0.f, 0.f};
+    for (int u = 0; u < nu; ++u)
+      if (256 * u + tid < c)
+        val[u] = __hip_atomic_load(a.fold_buf + (size_t)b * c + 256 * u + tid, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+    if (a.nr.on) {
+      // RMSNorm over the c coordinates, then the rotary pairs (neighbouring
+      // lanes) at the entry's position m e
+      float ss = 0.f;
+      for (int u = 0; u < nu; ++u)
+        if (256 * u + tid < c) ss += val[u] * val[u];
+      ss = wave_sum(ss);
+      if ((tid & 63) == 0) s_red[tid >> 6] = ss;
+      __syncthreads();
+      ss = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+      const float inv = 1.0f / sqrtf(ss / (float)c + a.nr.eps);
+      const int Rd = a.nr.rope_dims;
+      for (int u = 0; u < nu; ++u) {
+        const int r = 256 * u + tid;
+        float v = r < c ? val[u] * inv * a.nr.g_kv[r] : 0.f;
+        const float other = __shfl_xor(v, 1, 64);
+        if (r < c && r >= c - Rd) {
+          float cs, sn;
+          rope_cs((int64_t)m * e, a.nr.inv_freq[(r - (c - Rd)) >> 1], &cs, &sn);
+          v = (r & 1) ? (other * sn + v * cs) : (v * cs - other * sn);
+        }
+        val[u] = v;
+      }
     }
+    store_entry<T>(val, nu, c, a.kv_fmt, a.kv_cache, a.kv_scale, erow, s_red);
+  }
+  if (tid == 0) {
+    a.counters[b] = 0;
+    if (fold) a.n_entries[b] = n_have + 1;
   }
 }
 
@@ -410,9 +429,9 @@ static void launch_fold_to(const FoldArgs& a, dim3 grid, dim3 block, hipStream_t
 }
 
 hipError_t launch_fold_append(const FoldArgs& a, hipStream_t s) {
-  // main-entry jobs (one with norm_rope: the entry's norm needs all of it),
-  // the indexer-key job, the query jobs (norm_rope, four heads each)
-  const int jobs = ((a.nr.on || a.kv_fmt) ? 1 : a.c / kFoldCW) + (a.idx_dtype >= 0 ? 1 : 0) + (a.nr.on ? (a.H + 3) / 4 : 0);
+  // main-entry jobs (64 coordinates each), the indexer-key job, the query
+  // jobs (norm_rope, four heads each)
+  const int jobs = a.c / kFoldCW + (a.idx_dtype >= 0 ? 1 : 0) + (a.nr.on ? (a.H + 3) / 4 : 0);
   dim3 grid(jobs, a.B), block(kFoldT);
   if (a.dtype == F32)
     launch_fold_to<float>(a, grid, block, s);

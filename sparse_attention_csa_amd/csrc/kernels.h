@@ -114,6 +114,7 @@ struct FoldArgs {
   const int64_t* pos;
   int32_t* n_entries;
   int32_t* counters;        // [B] workspace, zero between calls
+  float* fold_buf;          // [B][c] workspace: a whole entry's folded values (norm_rope / FP8BF16)
   const void* streams;      // [B][S][c]
   const void* idx_streams;  // [B][4][d_I]
   const void* x_new;        // [B][c]
