@@ -453,6 +453,7 @@ def main():
         for wl, steps, warm in (("flash_csa_128k", args.steps, args.warmup),
                                 ("pro_csa_1m_mxfp4", args.steps, args.warmup),
                                 ("decode_1m_paged", args.steps, args.warmup),
+                                ("decode_1m_norm_rope", args.steps, args.warmup),
                                 ("prefill", max(3, min(args.steps, 5)), 1)):
             t1 = time.time()
             c2 = build_cases(wl)
