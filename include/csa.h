@@ -10,7 +10,10 @@
  * ---------------------------------------
  * - All tensor pointers are DEVICE pointers, row-major and contiguous, with
  *   the shapes given per argument, and 16-byte aligned (kernels load rows in
- *   16-byte pieces); a misaligned pointer is CSA_ERR_ARG.  The caller owns every buffer (inputs,
+ *   16-byte pieces); a misaligned pointer is CSA_ERR_ARG.  (There are no
+ *   strided views: a layer whose compressed caches live in a larger shared
+ *   allocation passes it as a paged pool with a block table, see
+ *   csa_layer_state.)  The caller owns every buffer (inputs,
  *   outputs, caches, state, workspace); the library never allocates, frees or
  *   keeps a pointer after the call returns.
  * - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
