@@ -130,7 +130,11 @@ __global__ __launch_bounds__(256) void index_score_kernel(IndexArgs a) {
 // --------------------------------------------------------------------------
 namespace {
 constexpr int kPfTile = 64;     // entries per LDS key tile
-constexpr int kPfChunk = 1024;  // entries per workgroup
+// entries per workgroup (the queries' operands are loaded once per chunk):
+// measured on the 4096-query chunk 4.91 ms with 1024, 4.78 with 2048, 4.70-4.74
+// with 4096 or 8192, 4.75 with 16384; 128-entry key tiles instead of 64 took
+// 11.3 ms (twice the LDS per workgroup)
+constexpr int kPfChunk = 4096;
 constexpr int kPfD = 128, kPfH = 64;
 // queries per workgroup (Tq % kPfQpw == 0).  Measured on the 4096-query
 // chunk: 8 gave the same time as 4 (the kernel is not bound by the key
