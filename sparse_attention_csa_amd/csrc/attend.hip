@@ -187,7 +187,6 @@ __global__ __launch_bounds__(256) void attend_generic_kernel(AttendArgs a) {
 bool attend_mfma_shape_ok(int H, int c);
 size_t attend_mfma_ws_bytes(int BT, int H, int rows_max, int split_rows);
 hipError_t launch_attend_mfma(const AttendArgs& a, int rows_max, hipStream_t s);
-bool attend_mfma_pages_fit(const AttendArgs& a, int rows_max);
 bool attend_mfma_sparse_fits(const AttendArgs& a, int rows_max);
 bool attend_rows_shape_ok(int H, int c);
 void attend_rows_plan(int BT, int H, int rows_max, int split_rows, int* n_split, int* rows_per_split);
@@ -222,10 +221,7 @@ size_t attend_ws_bytes(int B, int Tq, int H, int c, int rows_max, int split_rows
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   // (576-byte entries: the generic kernel decodes them row by row)
-  // (a paged cache whose split spans more pages than the dense kernel's
-  // table holds: the generic kernel)
-  if (a.dtype == BF16 && !a.kv_fmt && a.dense && attend_mfma_shape_ok(a.H, a.c) &&
-      attend_mfma_pages_fit(a, a.E_cap + a.n_win))
+  if (a.dtype == BF16 && !a.kv_fmt && a.dense && attend_mfma_shape_ok(a.H, a.c))
     return launch_attend_mfma(a, a.E_cap + a.n_win, s);
   if (a.dtype == BF16 && !a.kv_fmt && !a.dense && attend_mfma_shape_ok(a.H, a.c) &&
       attend_mfma_sparse_fits(a, a.k + a.n_win))

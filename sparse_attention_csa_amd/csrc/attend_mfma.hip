@@ -62,7 +62,8 @@ constexpr int kRowsPerWave = kTN / 4;  // DMA instructions per wave and tile
 constexpr int kFoldS = 16;             // fold slice: sources per thread (at most)
 constexpr int kFoldRowsLess = 64;      // rows a folding split gives up to the others
 constexpr int kFoldSlots = 64;         // fold slices at most (c / 8): one fold_s slot each
-constexpr int kPgSplit = 2048;         // paged cache: page ids of one split's rows in LDS (at most)
+constexpr int kPgSplit = 4096;         // paged cache: page ids of one split's rows in LDS (at most;
+                                       // pages past them are read from the table)
 
 }  // namespace
 
@@ -279,7 +280,8 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   } else if constexpr (PG) {
     const int ce = r_end < nc32 ? r_end : nc32;
     if (r_begin < ce) {
-      const int np = ((ce - 1) >> sh) - p_first + 1;  // <= kPgSplit (checked at launch)
+      int np = ((ce - 1) >> sh) - p_first + 1;
+      np = np < kPgSplit ? np : kPgSplit;  // (the rest: row_src reads the table)
       const int32_t* tb = a.pg.table + (size_t)b * (a.E_cap >> sh) + p_first;
       for (int i0 = 0; i0 < np; i0 += 256)  // (a uniform loop)
         if (i0 + tid < np) s_pg[i0 + tid] = tb[i0 + tid];
@@ -302,8 +304,17 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
       cr = (size_t)(uint32_t)(ok ? r : 0);
     } else if constexpr (PG) {
       int pi = (j >> sh) - p_first;
-      pi = pi < 0 ? 0 : (pi >= kPgSplit ? kPgSplit - 1 : pi);  // (rows that are not entries)
-      cr = ((size_t)(uint32_t)s_pg[pi] << sh) + (size_t)(j & ((1 << sh) - 1));
+      int32_t pg;
+      if (pi >= kPgSplit && j < nc32) {
+        // a page past the LDS table (splits of more than kPgSplit pages): its
+        // id from the block table (the wait for it also waits for the DMAs
+        // in flight)
+        pg = a.pg.table[(size_t)b * (a.E_cap >> sh) + (j >> sh)];
+      } else {
+        pi = pi < 0 ? 0 : (pi >= kPgSplit ? kPgSplit - 1 : pi);  // (rows that are not entries)
+        pg = s_pg[pi];
+      }
+      cr = ((size_t)(uint32_t)pg << sh) + (size_t)(j & ((1 << sh) - 1));
     }
     return j < r_end ? (j < nc32 ? (ok ? kv + cr * kC : pad_row) : win + (size_t)wr * kC) : pad_row;
   };
@@ -811,12 +822,10 @@ void attend_mfma_plan(int BT, int H, int rows_max, int split_rows, int* n_split,
 // row splits (the merge adds the new entry): the coordinates split into
 // power-of-two slices of 8..64, one per split, every source token of a
 // block handled by one thread of its slice.
-bool attend_mfma_pages_fit(const AttendArgs& a, int rows_max);
-
 bool attend_fuses_fold(AttendArgs& a, const FoldArgs& f) {
   a.fold_mode = 0;
   if (!a.dense || a.dtype != BF16 || f.dtype != BF16 || a.kv_fmt || f.kv_fmt ||
-      !attend_mfma_shape_ok(a.H, a.c) || !attend_mfma_pages_fit(a, a.E_cap + a.n_win) ||
+      !attend_mfma_shape_ok(a.H, a.c) ||
       a.Tq != 1 ||
       a.n_add != 0 || a.win_pos0 != nullptr || a.win_pos0_const != 0 || f.overlap || f.idx_dtype >= 0 ||
       f.B != a.B || f.c != a.c || f.n_win != a.W_cap || f.R < 2 * f.m)
@@ -869,14 +878,6 @@ size_t attend_mfma_ws_bytes(int BT, int H, int rows_max, int split_rows) {
 }
 
 hipError_t launch_attend_merge(const AttendArgs& a, int n_split, hipStream_t s);
-
-// paged cache: a split's page ids fit the kernel's LDS table
-bool attend_mfma_pages_fit(const AttendArgs& a, int rows_max) {
-  if (!a.pg.table) return true;
-  int ns, rps;
-  attend_mfma_plan(a.B * a.Tq, a.H, rows_max, a.split_rows, &ns, &rps);
-  return ((rps - 1) >> a.pg.shift) + 2 <= kPgSplit;
-}
 
 // sparse rows on the 64-head kernel: for batches of many queries (the plan
 // cuts no query's rows, so each selected row is gathered once per query and

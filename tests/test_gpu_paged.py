@@ -200,3 +200,30 @@ def test_full_size_decode_paged_matches_per_sequence_layout(gpu_lib):
         print(f"[{label}] paged = per-sequence layout", flush=True)
         del paged, flat
         torch.cuda.empty_cache()
+
+
+def test_full_size_prefill_paged_matches_per_sequence_layout(gpu_lib):
+    """The 4096-token prefill chunk over a 262,144-token context (both
+    layers) with its caches in 128-token pages: bit for bit the per-sequence
+    layout's outputs, selections and produced entries; and a second run of
+    the paged chunk on a fresh state gives the same bits (run-to-run
+    determinism of the paged forms)."""
+    from sparse_attention_csa_amd.harness import PrefillSession
+    a, h = workloads.flash_prefill()
+    for g, P, label in ((a, 32, "full-prefill-csa"), (h, 1, "full-prefill-hca")):
+        print(f"[{label}] build", flush=True)
+        gp = workloads.with_pages(g, P, seed=174)
+        paged, flat = PrefillSession(gp), PrefillSession(g)
+        paged.run()
+        flat.run()
+        torch.cuda.synchronize()
+        _same_io(paged.io, flat.io, label)
+        _same_entries(paged.state, flat.state, flat.state.n_entries.cpu().numpy(), label)
+        again = PrefillSession(gp)
+        again.run()
+        torch.cuda.synchronize()
+        _same_io(paged.io, again.io, label + " rerun")
+        print(f"[{label}] paged = per-sequence layout, rerun identical", flush=True)
+        del paged, flat, again
+        torch.cuda.empty_cache()
+
