@@ -105,17 +105,17 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
   const int H = a.H;
   const int h0 = hg * kHW + 16 * w;  // this wavefront's first head
 
-  // The position, entry count and window base are requested first (vector
-  // loads: see vload_same).  The first tile's rows are usually cache entries
-  // whose addresses need none of them, so its DMAs go out before they return
-  // (checked below, reissued in the rare case).  (Unconditional loads: an
-  // absent optional array is replaced by a valid dummy address and the value
+  // The position, entry count and window base (scalar loads) are requested
+  // first.  The first tile's rows are usually cache entries whose addresses
+  // need none of them, so its DMAs go out before they return (checked
+  // below, reissued in the rare case).  (Unconditional loads: an absent
+  // optional array is replaced by a valid dummy address and the value
   // discarded, so the three loads are in flight together instead of one
   // branch and wait each.)
   const int64_t* dummy64 = reinterpret_cast<const int64_t*>(a.kv);
-  const int64_t t_ld = vload_same(a.q_pos ? a.q_pos + qrow : dummy64);
-  const int64_t w_ld = vload_same(a.win_pos0 ? a.win_pos0 + b : dummy64);
-  const int32_t cnt_ld = vload_same(SP ? a.topk_cnt + qrow : a.n_entries + b);
+  const int64_t t_ld = (a.q_pos ? a.q_pos + qrow : dummy64)[0];
+  const int64_t w_ld = (a.win_pos0 ? a.win_pos0 + b : dummy64)[0];
+  const int32_t cnt = SP ? a.topk_cnt[qrow] : a.n_entries[b];
   // row range of the split: with the fold inside, the first fold_nsplit
   // splits (the ones that fold) take fold_rows rows each, the rest
   // rows_per_split, so that the fold's time is balanced by fewer rows
@@ -164,10 +164,10 @@ __global__ __launch_bounds__(256, 1) void attend_mfma_kernel(AttendArgs a, int n
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(q + 32 * ks);
   }
-  // (the compiler waits for the three loads here)
-  const int32_t cnt = sgpr32(cnt_ld);
-  const int64_t t = a.q_pos ? sgpr64(t_ld) : a.q_pos0 + qrow % a.Tq;
-  const int64_t wpos0 = a.win_pos0 ? sgpr64(w_ld) : a.win_pos0_const;
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm0);  // the scalars
+  __asm__ __volatile__("" ::"s"(t_ld), "s"(w_ld), "s"(cnt));
+  const int64_t t = a.q_pos ? t_ld : a.q_pos0 + qrow % a.Tq;
+  const int64_t wpos0 = a.win_pos0 ? w_ld : a.win_pos0_const;
   const int64_t lim = vis_limit(t, a.m, a.vis);
   const int64_t have = (int64_t)cnt + a.n_add;
   int64_t n_c = lim < have ? lim : have;
@@ -719,20 +719,30 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
   const int H = a.H;
   const float* pml = reinterpret_cast<const float*>(a.ws);
   const uint16_t* po = reinterpret_cast<const uint16_t*>(pml + (size_t)a.B * a.Tq * n_split * H * 2);
+  const float z2 = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+  // fold_mode: the query's own token and the step's new entry (if any) as
+  // two more rows, weights exp2(s_own - M) and exp2(s_new - M)
   const int b = qrow / a.Tq;
-  // Every load is issued before the first wait (the addresses depend on
-  // nothing loaded): the fold's outputs, this wavefront's splits' rows, the
-  // splits' statistics, the sink and the fold's entry row.
-  // The fold slices' shares of q . new entry and q . token, lane = slice
-  // (summed below in the same lane order on every run)
+  const int frow = a.fold_mode ? a.fold_row[b] : 0;
+  // the fold slices' shares of q . new entry and q . token, lane = slice,
+  // summed in the same lane order on every run
   float2 fsv = float2{0.f, 0.f};
-  uint4 nrow = uint4{0, 0, 0, 0}, xrow = nrow;
   if (a.fold_mode) {
     const int nf = (a.c + a.fold_cs - 1) / a.fold_cs;
     if (l < nf) fsv = *reinterpret_cast<const float2*>(a.fold_s + 2 * (((size_t)b * H + h) * kFoldSlots + l));
+    fsv.x = wave_sum(fsv.x);
+    fsv.y = wave_sum(fsv.y);
+  }
+  const float s_new = frow > 0 ? fsv.x * (a.scale * kLog2e) : -INFINITY;
+  const float s_own = a.fold_mode ? fsv.y * (a.scale * kLog2e) : -INFINITY;
+  // (fixed addresses: every load is issued at once)
+  uint4 nrow = uint4{0, 0, 0, 0}, xrow = nrow;
+  if (a.fold_mode) {
     nrow = *reinterpret_cast<const uint4*>(a.fold_new + (size_t)b * kC + 8 * l);
     xrow = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.fold.x_new) + (size_t)b * kC + 8 * l);
   }
+  // this wavefront's splits' rows, then the statistics: every load is in
+  // flight before the first wait
   uint4 raw[kMergeU];
 #pragma unroll
   for (int u = 0; u < kMergeU; ++u) {
@@ -750,24 +760,6 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttendArgs a, int n_s
     ms = v.x;
     Ls = v.y;
   }
-  // (the sink and the fold's row: vector loads, relaxed atomics so that
-  // they are not turned into scalar loads, whose wait would also wait for
-  // them before the other loads go out; an absent array is replaced by a
-  // valid dummy address and the value discarded)
-  const float* dummy = reinterpret_cast<const float*>(a.ws);
-  const float sink_ld = __hip_atomic_load(a.sink ? a.sink + h : dummy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  // fold_mode: the query's own token and the step's new entry (if any) as
-  // two more rows, weights exp2(s_own - M) and exp2(s_new - M)
-  const int frow_ld = __hip_atomic_load(a.fold_mode ? a.fold_row + b : reinterpret_cast<const int32_t*>(dummy),
-                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  const float z2 = a.sink ? sink_ld * kLog2e : -INFINITY;
-  const int frow = a.fold_mode ? frow_ld : 0;
-  if (a.fold_mode) {
-    fsv.x = wave_sum(fsv.x);
-    fsv.y = wave_sum(fsv.y);
-  }
-  const float s_new = frow > 0 ? fsv.x * (a.scale * kLog2e) : -INFINITY;
-  const float s_own = a.fold_mode ? fsv.y * (a.scale * kLog2e) : -INFINITY;
   const float M = fmaxf(fmaxf(fmaxf(wave_max(ms), z2), s_new), s_own);
   const float wgt = (ms == -INFINITY || Ls == 0.f) ? 0.f : __builtin_amdgcn_exp2f(ms - M) * Ls;
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};

@@ -187,21 +187,6 @@ CSA_DEV void lds_sync() {
 // across.  (An LDS-scoped release fence would also wait for the in-flight
 // DMAs, since they write LDS.)  DMA'd data is published by waiting for its
 // vmcnt explicitly before this barrier.
-// A load of a value every lane reads at one address, kept a vector load (a
-// relaxed atomic is never made a scalar load): a scalar load's wait also
-// waits for the kernel-argument loads issued after it, so memory loads that
-// must not hold up the first loads of a kernel go this way.
-template <class T>
-CSA_DEV T vload_same(const T* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-// a wavefront-uniform value held in VGPRs, into SGPRs
-CSA_DEV int32_t sgpr32(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
-CSA_DEV int64_t sgpr64(int64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uint64_t)v);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
 constexpr int kWaitLgkm0 = 0xC07F;  // gfx9 s_waitcnt: vmcnt 63, expcnt 7, lgkmcnt 0
 CSA_DEV void lds_barrier() {
   __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
