@@ -373,6 +373,35 @@ def measure(cases, steps, warmup, rotate, prefill, profile=True, use_graph=False
     return out
 
 
+def hbm_reference(nbytes=1 << 30, reps=5):
+    """What plain streaming kernels reach on this GPU, timed in the same run
+    (events around torch's own kernels; median of `reps`): a device-to-device
+    copy (read + write bytes) and a sum reduction (read bytes).  Context for
+    the roofline fractions, which stay against the published 8 TB/s."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    out = {}
+    for name, fn, moved in (("device_copy_gbs", lambda: y.copy_(x), 2 * nbytes),
+                            ("sum_read_gbs", lambda: x.sum(), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        out[name] = round(moved / (ts[len(ts) // 2] / 1e3) / 1e9, 1)
+    out["bytes"] = nbytes
+    del x, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -474,6 +503,14 @@ def main():
             del r2, c2
             torch.cuda.empty_cache()
 
+    ref = hbm_reference()
+    log(f"plain streaming kernels here: copy {ref['device_copy_gbs']} GB/s, sum {ref['sum_read_gbs']} GB/s")
+    if not prefill:
+        # the step's and the layers' algorithmic bytes against what a plain
+        # copy reaches on this GPU (the roofline fractions above stay
+        # against the published peak)
+        ref["step_frac_of_copy"] = round(step_roof["achieved_gbs"] / ref["device_copy_gbs"], 4)
+
     cpu = None
     if not args.no_cpu:
         log("timing the oracle on a bounded sample ...")
@@ -485,7 +522,7 @@ def main():
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded; shapes of the pages' Flash/Pro configurations)",
            "config": cfg, "roofline": roofline, "step_roofline": step_roof, "cpu_baseline": cpu,
-           "layer_times": layers, "kernels": kernels, "other_workloads": extra}
+           "layer_times": layers, "kernels": kernels, "other_workloads": extra, "hbm_reference": ref}
     print(json.dumps(out), flush=True)
 
 
