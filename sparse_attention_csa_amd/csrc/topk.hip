@@ -39,6 +39,7 @@ constexpr int kCT = 256;   // collect workgroup
 constexpr int kRT = 1024;  // resolve / row workgroup
 constexpr int kSpecL = 16;  // fused resolve: list entries per workgroup loaded with the counts
 constexpr int kSpecU = 4;   // ... by this many loads per thread (n_wg * kSpecL <= kSpecU * kRT)
+constexpr int kRowU = 16;   // row mode: scores per thread and batch (loads in flight together)
 constexpr int kCollectPer = kTopkCollectSlice / kCT;  // 16 keys per thread
 
 CSA_DEV uint32_t bin_of(uint32_t key) { return key >> kTopkShift; }
@@ -619,23 +620,46 @@ __global__ __launch_bounds__(kRT) void topk_rowsel_kernel(IndexArgs a, TopkWs ws
     L.misc[49] = 0;
   }
   __syncthreads();
-  for (int s = tid; s < nv; s += kRT) atomicAdd(&L.hist[bin_of(f32_key(sc[s]))], 1);
+  // The row is read in batches of kRowU scores per thread, all of a batch's
+  // loads in flight before its first use (one load, wait and LDS atomic per
+  // score would make each score a global round trip).
+  for (int s0 = 0; s0 < nv; s0 += kRowU * kRT) {
+    float v[kRowU];
+#pragma unroll
+    for (int u = 0; u < kRowU; ++u) {
+      const int s = s0 + tid + kRT * u;
+      v[u] = s < nv ? sc[s] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kRowU; ++u)
+      if (s0 + tid + kRT * u < nv) atomicAdd(&L.hist[bin_of(f32_key(v[u]))], 1);
+  }
   __syncthreads();
   int b1, above;
   find_bin<kRT>(L.hist, k, L.misc + 8, L.misc + 40, &b1, &above);
   // certain winners to win[], candidates to ckey/cid (counted past the cap)
-  for (int s = tid; s < nv; s += kRT) {
-    const uint32_t key = f32_key(sc[s]);
-    const int bin = (int)bin_of(key);
-    if (bin > b1) {
-      const int o = atomicAdd(&L.misc[48], 1);
-      if (o < kTopkMaxK) L.win[o] = s;
+  for (int s0 = 0; s0 < nv; s0 += kRowU * kRT) {
+    float v[kRowU];
+#pragma unroll
+    for (int u = 0; u < kRowU; ++u) {
+      const int s = s0 + tid + kRT * u;
+      v[u] = s < nv ? sc[s] : 0.f;
     }
-    if (bin == b1) {
-      const int o = atomicAdd(&L.misc[49], 1);
-      if (o < kTopkCandCap) {
-        L.ckey[o] = key;
-        L.cid[o] = s;
+#pragma unroll
+    for (int u = 0; u < kRowU; ++u) {
+      const int s = s0 + tid + kRT * u;
+      const uint32_t key = f32_key(v[u]);
+      const int bin = (int)bin_of(key);
+      if (s < nv && bin > b1) {
+        const int o = atomicAdd(&L.misc[48], 1);
+        if (o < kTopkMaxK) L.win[o] = s;
+      }
+      if (s < nv && bin == b1) {
+        const int o = atomicAdd(&L.misc[49], 1);
+        if (o < kTopkCandCap) {
+          L.ckey[o] = key;
+          L.cid[o] = s;
+        }
       }
     }
   }
