@@ -566,13 +566,17 @@ __global__ __launch_bounds__(kRT) void topk_fused_resolve_kernel(IndexArgs a, To
         __syncthreads();
       }
       const int n_sel = min(L.misc[50], want);
-      for (int i = tid; i < tot_s; i += kRT) {
-        const int id = L.win[i];
-        out[i + lower_bound_i(sel, n_sel, id)] = id;
-      }
-      for (int j = tid; j < n_sel; j += kRT) {
-        const int id = sel[j];
-        out[j + lower_bound_i(L.win, tot_s, id)] = id;
+      // every id at its rank in its own list plus its rank in the other
+      // (both lists ascending): one binary search per id, the two lists'
+      // ids spread over the threads together
+      for (int f = tid; f < tot_s + n_sel; f += kRT) {
+        if (f < tot_s) {
+          const int id = L.win[f];
+          out[f + lower_bound_i(sel, n_sel, id)] = id;
+        } else {
+          const int id = sel[f - tot_s];
+          out[f - tot_s + lower_bound_i(L.win, tot_s, id)] = id;
+        }
       }
       for (int i = tot_s + n_sel + tid; i < k; i += kRT) out[i] = -1;
       if (tid == 0) a.topk_cnt[row] = tot_s + n_sel;
