@@ -40,6 +40,7 @@ constexpr int kRT = 1024;  // resolve / row workgroup
 constexpr int kSpecL = 16;  // fused resolve: list entries per workgroup loaded with the counts
 constexpr int kSpecU = 4;   // ... by this many loads per thread (n_wg * kSpecL <= kSpecU * kRT)
 constexpr int kRowU = 16;   // row mode: scores per thread and batch (loads in flight together)
+constexpr int kSampleBlk = 16;  // row mode: 256-score blocks sampled for the threshold guess
 constexpr int kCollectPer = kTopkCollectSlice / kCT;  // 16 keys per thread
 
 CSA_DEV uint32_t bin_of(uint32_t key) { return key >> kTopkShift; }
@@ -624,24 +625,44 @@ __global__ __launch_bounds__(kRT) void topk_rowsel_kernel(IndexArgs a, TopkWs ws
     L.misc[49] = 0;
   }
   __syncthreads();
-  // The row is read in batches of kRowU scores per thread, all of a batch's
-  // loads in flight before its first use (one load, wait and LDS atomic per
-  // score would make each score a global round trip).
-  for (int s0 = 0; s0 < nv; s0 += kRowU * kRT) {
-    float v[kRowU];
+  // A guess of the threshold bin from a sample: kSampleBlk blocks of 256
+  // consecutive scores spread over the row (their sample's k_s-th largest,
+  // k_s a wide margin above the k-th largest's expected count).  The row is
+  // then read once: every score into the histogram, and the keys in bins at
+  // or above the guess stashed with their ids.  When the row's threshold
+  // bin b1 is at or above the guess and the stash did not overflow, the
+  // winners (bin > b1) and candidates (bin == b1) are all in the stash;
+  // otherwise the row is read a second time for them.
+  int lo_bin = 0;
+  {
+    float v[kSampleBlk * 256 / kRT];
 #pragma unroll
-    for (int u = 0; u < kRowU; ++u) {
-      const int s = s0 + tid + kRT * u;
+    for (int u = 0; u < kSampleBlk * 256 / kRT; ++u) {
+      const int q = tid + kRT * u, blk = q / 256;
+      const int s = (int)((int64_t)nv * blk / kSampleBlk) + q % 256;
       v[u] = s < nv ? sc[s] : 0.f;
     }
 #pragma unroll
-    for (int u = 0; u < kRowU; ++u)
-      if (s0 + tid + kRT * u < nv) atomicAdd(&L.hist[bin_of(f32_key(v[u]))], 1);
+    for (int u = 0; u < kSampleBlk * 256 / kRT; ++u) {
+      const int q = tid + kRT * u, blk = q / 256;
+      const int s = (int)((int64_t)nv * blk / kSampleBlk) + q % 256;
+      if (s < nv) atomicAdd(&L.hist[bin_of(f32_key(v[u]))], 1);
+    }
+    if (tid == 0) {
+      L.misc[40] = 0;  // (no bin found: stash everything)
+      L.misc[41] = 0;
+    }
+    __syncthreads();
+    const int n_samp = nv < kSampleBlk * 256 ? nv : kSampleBlk * 256;
+    const int k_s = (int)(2 * (int64_t)k * n_samp / nv) + 64;
+    int ab;
+    if (k_s < n_samp) find_bin<kRT>(L.hist, k_s, L.misc + 8, L.misc + 40, &lo_bin, &ab);
+    for (int i = tid; i < kTopkBins; i += kRT) L.hist[i] = 0;
+    __syncthreads();
   }
-  __syncthreads();
-  int b1, above;
-  find_bin<kRT>(L.hist, k, L.misc + 8, L.misc + 40, &b1, &above);
-  // certain winners to win[], candidates to ckey/cid (counted past the cap)
+  // The row in batches of kRowU scores per thread, all of a batch's loads in
+  // flight before its first use (one load, wait and LDS atomic per score
+  // would make each score a global round trip).
   for (int s0 = 0; s0 < nv; s0 += kRowU * kRT) {
     float v[kRowU];
 #pragma unroll
@@ -654,15 +675,75 @@ __global__ __launch_bounds__(kRT) void topk_rowsel_kernel(IndexArgs a, TopkWs ws
       const int s = s0 + tid + kRT * u;
       const uint32_t key = f32_key(v[u]);
       const int bin = (int)bin_of(key);
-      if (s < nv && bin > b1) {
-        const int o = atomicAdd(&L.misc[48], 1);
-        if (o < kTopkMaxK) L.win[o] = s;
+      if (s < nv) {
+        atomicAdd(&L.hist[bin], 1);
+        if (bin >= lo_bin) {
+          const int o = atomicAdd(&L.misc[49], 1);
+          if (o < kTopkCandCap) {
+            L.ckey[o] = key;
+            L.cid[o] = s;
+          }
+        }
       }
-      if (s < nv && bin == b1) {
+    }
+  }
+  __syncthreads();
+  const int n_st = L.misc[49];
+  int b1, above;
+  find_bin<kRT>(L.hist, k, L.misc + 8, L.misc + 40, &b1, &above);
+  if (b1 >= lo_bin && n_st <= kTopkCandCap) {
+    // certain winners to win[], candidates to the front of ckey/cid
+    constexpr int kStU = kTopkCandCap / kRT;
+    uint32_t key[kStU];
+    int id[kStU];
+#pragma unroll
+    for (int u = 0; u < kStU; ++u) {
+      const int i = tid + kRT * u;
+      key[u] = i < n_st ? L.ckey[i] : 0u;
+      id[u] = i < n_st ? L.cid[i] : -1;
+    }
+    __syncthreads();
+    if (tid == 0) L.misc[49] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kStU; ++u) {
+      const int bin = (int)bin_of(key[u]);
+      if (id[u] >= 0 && bin > b1) {
+        const int o = atomicAdd(&L.misc[48], 1);
+        if (o < kTopkMaxK) L.win[o] = id[u];
+      }
+      if (id[u] >= 0 && bin == b1) {
         const int o = atomicAdd(&L.misc[49], 1);
-        if (o < kTopkCandCap) {
-          L.ckey[o] = key;
-          L.cid[o] = s;
+        L.ckey[o] = key[u];
+        L.cid[o] = id[u];
+      }
+    }
+  } else {
+    // the guess missed: certain winners and candidates from a second read
+    if (tid == 0) L.misc[49] = 0;
+    __syncthreads();
+    for (int s0 = 0; s0 < nv; s0 += kRowU * kRT) {
+      float v[kRowU];
+#pragma unroll
+      for (int u = 0; u < kRowU; ++u) {
+        const int s = s0 + tid + kRT * u;
+        v[u] = s < nv ? sc[s] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kRowU; ++u) {
+        const int s = s0 + tid + kRT * u;
+        const uint32_t key = f32_key(v[u]);
+        const int bin = (int)bin_of(key);
+        if (s < nv && bin > b1) {
+          const int o = atomicAdd(&L.misc[48], 1);
+          if (o < kTopkMaxK) L.win[o] = s;
+        }
+        if (s < nv && bin == b1) {
+          const int o = atomicAdd(&L.misc[49], 1);
+          if (o < kTopkCandCap) {
+            L.ckey[o] = key;
+            L.cid[o] = s;
+          }
         }
       }
     }

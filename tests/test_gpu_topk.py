@@ -118,3 +118,47 @@ def test_row_mode_many_queries(gpu_lib):
     pos = (4 * 4000 + np.arange(Tq) * 9)[None, :].astype(np.int64)
     kb, qb, ids, cnt = _run(keys, q, w, 256, [E], pos, rows_tq=Tq)
     _check(kb, qb, w, 256, [E], pos, ids, cnt)
+
+
+def _designed_rows(values, Tq=72):
+    """Row-mode inputs whose index scores are exactly ``values`` (every row
+    the same): one nonzero key coordinate, unit queries, head weights 1/64,
+    so each score is max(0, value) summed exactly over the 64 heads."""
+    E = values.shape[0]
+    keys = np.zeros((1, E, D), np.float32)
+    keys[0, :, 0] = values
+    q = np.zeros((1, Tq, 64, D), np.float32)
+    q[..., 0] = 1.0
+    w = np.full((1, Tq, 64), 1.0 / 64, np.float32)
+    pos = (4 * E + np.arange(Tq))[None, :].astype(np.int64)
+    return keys, q, w, pos
+
+
+def test_row_mode_threshold_guess_missed(gpu_lib):
+    """Row mode guesses the threshold bin from 16 sampled blocks of 256
+    scores and reads the row once; here 400 high scores (< k) all sit in the
+    sampled blocks, so the guess lies above the row's threshold bin and the
+    selection must take its second read of the row."""
+    rng = np.random.default_rng(41)
+    E, k = 20000, 512
+    vals = rng.uniform(0.01, 1.0, E).astype(np.float32)
+    starts = [E * b // 16 for b in range(16)]
+    hi = np.concatenate([np.arange(s, s + 25) for s in starts])  # 400 positions inside the sample
+    vals[hi] = 10.0
+    keys, q, w, pos = _designed_rows(vals)
+    kb, qb, ids, cnt = _run(keys, q, w, k, [E], pos, rows_tq=q.shape[1])
+    _check(kb, qb, w, k, [E], pos, ids, cnt)
+    assert np.all(np.isin(hi, ids[0, 0]))
+
+
+def test_row_mode_stash_overflow(gpu_lib):
+    """Row mode with one dominant score value (most of the row in the
+    threshold bin): the stash of keys at or above the guessed bin overflows
+    and the selection falls back to its second read (ties to lower ids)."""
+    rng = np.random.default_rng(42)
+    E, k = 20000, 512
+    vals = np.full(E, 0.5, np.float32)
+    vals[rng.choice(E, 300, replace=False)] = 0.75
+    keys, q, w, pos = _designed_rows(vals)
+    kb, qb, ids, cnt = _run(keys, q, w, k, [E], pos, rows_tq=q.shape[1])
+    _check(kb, qb, w, k, [E], pos, ids, cnt)
