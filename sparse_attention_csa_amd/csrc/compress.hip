@@ -233,7 +233,63 @@ static void launch_compress_to(const CompressArgs& a, dim3 grid, dim3 block, hip
     CSA_LAUNCH("compress_chunk", (compress_chunk_kernel<T, mx4>), grid, block, 0, s, a);
 }
 
+// Long one-branch blocks (HCA, m' >= 32 sources per entry) with plain f32 /
+// bf16 output: grid (T/m, B, c/64).  A workgroup folds 64 coordinates of
+// one entry; wavefront g takes sources g, g + 4, ... of each coordinate with
+// its own online softmax state (source loads in batches in flight), and the
+// four states merge through LDS in wavefront order.  (The whole-entry
+// kernel above walks all m sources of a coordinate in one thread: with
+// m = 128 that chain of dependent updates set its time.)
+constexpr int kSliceC = 64;
+template <typename T, typename TO>
+__global__ __launch_bounds__(256) void compress_slices_kernel(CompressArgs a) {
+  const int i = blockIdx.x, b = blockIdx.y, tid = threadIdx.x, g = tid >> 6;
+  const int c = a.c, m = a.m, lw = a.logit_width;
+  const int r = blockIdx.z * kSliceC + (tid & 63);
+  const size_t sc = a.seq_stride ? a.seq_stride : (size_t)a.T * c;
+  const size_t sz = a.seq_stride ? a.seq_stride : (size_t)a.T * lw;
+  const T* ca = cptr<T>(a.ca) + (size_t)b * sc + (size_t)m * i * c + r;
+  const T* za = cptr<T>(a.za) + (size_t)b * sz + (size_t)m * i * lw + (lw == 1 ? 0 : r);
+  __shared__ Soft s_part[4][kSliceC];
+  Soft sf{-INFINITY, 0.f, 0.f};
+  constexpr int kB = 8;  // sources per batch and wavefront
+  for (int j0 = g; j0 < m; j0 += 4 * kB) {
+    float lgs[kB], vs[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      int j = j0 + 4 * u;
+      j = j < m ? j : m - 1;  // (past the last source: re-read it, dropped)
+      lgs[u] = ld(za, (size_t)j * lw) + (a.bias_a ? a.bias_a[(size_t)j * c + r] : 0.f);
+      vs[u] = ld(ca, (size_t)j * c);
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u)
+      if (j0 + 4 * u < m) soft_push(sf, lgs[u], vs[u]);
+  }
+  s_part[g][tid & 63] = sf;
+  __syncthreads();
+  if (g != 0) return;
+  Soft acc = s_part[0][tid];
+#pragma unroll
+  for (int v = 1; v < 4; ++v) acc = soft_merge(acc, s_part[v][tid]);
+  const size_t erow = page_row(a.pg, b, a.first + i, a.E_cap);
+  st(reinterpret_cast<TO*>(a.out), erow * c + r, acc.acc / acc.l);
+}
+
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
+  if (!a.seq_pos0 && !a.score_w && !a.cb && !a.nr.on && a.m >= 32 && a.c % kSliceC == 0 &&
+      (a.out_dtype == F32 || a.out_dtype == BF16)) {
+    dim3 grid(a.T / a.m, a.B, a.c / kSliceC), block(256);
+    if (a.dtype == F32 && a.out_dtype == F32)
+      CSA_LAUNCH("compress_chunk", (compress_slices_kernel<float, float>), grid, block, 0, s, a);
+    else if (a.dtype == F32)
+      CSA_LAUNCH("compress_chunk", (compress_slices_kernel<float, bf16>), grid, block, 0, s, a);
+    else if (a.out_dtype == F32)
+      CSA_LAUNCH("compress_chunk", (compress_slices_kernel<bf16, float>), grid, block, 0, s, a);
+    else
+      CSA_LAUNCH("compress_chunk", (compress_slices_kernel<bf16, bf16>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   // (variable-length chunks: a chunk of T tokens ends at most ceil(T/m) blocks)
   dim3 grid(a.seq_pos0 ? (a.T + a.m - 1) / a.m : a.T / a.m, a.B), block(256);
   if (a.dtype == F32)
