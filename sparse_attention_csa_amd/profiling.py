@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "attend_generic": ["attend.hip", "common.h", "kernels.h"],
     "fold_append": ["compress.hip", "common.h", "kernels.h", "fold.h"],
     "compress_chunk": ["compress.hip", "common.h", "kernels.h", "fold.h"],
+    "compress_slices": ["compress.hip", "common.h", "kernels.h", "fold.h"],
     "prefill_state": ["compress.hip", "common.h", "kernels.h", "fold.h"],
     "prep_rows": ["compress.hip", "common.h", "kernels.h", "fold.h"],
 }
