@@ -220,3 +220,40 @@ def test_prefill_is_deterministic(gpu_lib):
             res.append(_bits_of(sess.io, ("out", "lse", "topk_idx", "topk_cnt")))
         for n in res[0]:
             assert np.array_equal(res[0][n], res[1][n]), f"prefill {g['kind']}: {n} differs"
+
+
+@pytest.mark.parametrize("m,in_dt,out_dt,lw,bias", [(128, "bf16", "bf16", "c", True), (128, "f32", "f32", "c", False),
+                                                    (32, "bf16", "f32", "1", True), (64, "f32", "bf16", "1", False)])
+def test_compress_long_blocks(gpu_lib, m, in_dt, out_dt, lw, bias):
+    """csa_compress of long one-branch blocks (the HCA shape; the sliced
+    compressor, four wavefronts splitting each coordinate's sources): f32 /
+    bf16 inputs and outputs, per-coordinate or scalar logits, with and
+    without positional biases, written at an offset into a larger cache,
+    against the oracle's fold of the same stored inputs."""
+    from sparse_attention_csa_amd import _lib as L
+    rng = np.random.default_rng(61 + m)
+    B, c, n_ent, first, E_cap = 2, 512, 6, 3, 12
+    T = m * n_ent
+    zw = c if lw == "c" else 1
+    ca = rng.standard_normal((B, T, c)).astype(np.float32)
+    za = (2.0 * rng.standard_normal((B, T, zw))).astype(np.float32)
+    if in_dt == "bf16":
+        ca_s, za_s = workloads.gen.bf16_bits(ca), workloads.gen.bf16_bits(za)
+        d_ca, d_za = _dev_bf16(ca_s), _dev_bf16(za_s)
+        ca = np.stack([Stored(ca_s[b], "bf16").all() for b in range(B)])
+        za = np.stack([Stored(za_s[b], "bf16").all() for b in range(B)])
+    else:
+        d_ca, d_za = torch.from_numpy(ca).cuda(), torch.from_numpy(za).cuda()
+    ba = rng.standard_normal((m, c)).astype(np.float32) if bias else None
+    odt = torch.bfloat16 if out_dt == "bf16" else torch.float32
+    out = torch.zeros((B, E_cap, c), dtype=odt, device="cuda")
+    L.csa_compress(d_ca, d_za, m, bias_a=torch.from_numpy(ba).cuda() if bias else None, out=out,
+                   out_first_entry=first)
+    torch.cuda.synchronize()
+    got = out.to(torch.float64).cpu().numpy()
+    for b in range(B):
+        ref = OC.compress(ca[b], za[b], m, ba)
+        g = got[b, first:first + n_ent]
+        err = np.abs(g - ref).max(axis=1) / np.abs(ref).max(axis=1)
+        assert err.max() <= (1e-5 if out_dt == "f32" else 2.0 ** -8), f"b={b}: row errors {err}"
+        assert np.all(got[b, :first] == 0) and np.all(got[b, first + n_ent:] == 0)
